@@ -1,0 +1,20 @@
+"""Shared pytest setup: the `gpu` marker and the repository on sys.path."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built libmuon.so")
+
+
+@pytest.fixture(scope="session")
+def golden_dir():
+    return GOLDEN

@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here compares the oracle with itself: every check is a closed form,
+an invariant, a textbook routine (SVD polar factor), brute force over all
+bit patterns, or a value worked by hand (tests/golden).  The planted-mistake
+tests at the end break one oracle function at a time and show that some pin
+then fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.muon_oracle as O
+from workloads import CUBIC, QUINTIC, random_matrix
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _orthonormal(n, k, seed):
+    q, _ = np.linalg.qr(random_matrix((n, k), [77, seed]))
+    return q
+
+
+def scalar_map(x, coeffs, steps):
+    a, b, c = coeffs
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+# ---------------------------------------------------------------------------
+# P-1: closed form.  NS is an odd matrix polynomial X q(X^T X), so with
+# X = Q1 diag(s) Q2^T the output is Q1 diag(phi(s / ||s||_2)) Q2^T where phi is
+# the steps-fold scalar map x -> a x + b x^3 + c x^5.
+# ---------------------------------------------------------------------------
+
+def check_closed_form(shape, coeffs, steps, sigma_seed=0, rank=None):
+    r, c = shape
+    k = min(r, c) if rank is None else rank
+    Q1, Q2 = _orthonormal(r, k, 1 + sigma_seed), _orthonormal(c, k, 2 + sigma_seed)
+    sig = np.logspace(-3, 0, k)[::-1] * (1.0 + 0.1 * np.arange(k))
+    M = (Q1 * sig) @ Q2.T
+    U = O.newton_schulz(M, *coeffs, steps)
+    phi = scalar_map(sig / np.linalg.norm(sig), coeffs, steps)
+    expect = (Q1 * phi) @ Q2.T
+    err = np.linalg.norm(U - expect) / max(np.linalg.norm(expect), 1e-300)
+    assert err < 1e-11, f"closed form mismatch {err:.3e} for {shape} {coeffs} steps={steps}"
+
+
+@pytest.mark.parametrize("shape", [(5, 9), (9, 5), (8, 8), (1, 7), (7, 1), (16, 40)])
+@pytest.mark.parametrize("coeffs", [CUBIC, QUINTIC, (2.0, -1.5, 0.5)])
+@pytest.mark.parametrize("steps", [0, 1, 5])
+def test_closed_form(shape, coeffs, steps):
+    check_closed_form(shape, coeffs, steps)
+
+
+def test_closed_form_rank_deficient():
+    check_closed_form((10, 14), QUINTIC, 5, rank=4)
+    check_closed_form((14, 10), CUBIC, 3, rank=2)
+
+
+# ---------------------------------------------------------------------------
+# P-2: polar factor.  Cubic (1.5, -0.5, 0) converges to U V^T of the SVD.
+# ---------------------------------------------------------------------------
+
+def check_polar(shape, seed):
+    M = random_matrix(shape, [91, seed])
+    U = O.newton_schulz(M, *CUBIC, 60)
+    u, s, vt = np.linalg.svd(M, full_matrices=False)
+    polar = u @ vt
+    assert np.linalg.norm(U - polar) / np.linalg.norm(polar) < 1e-11
+    k = min(shape)
+    gram = U.T @ U if shape[0] >= shape[1] else U @ U.T
+    assert np.allclose(gram, np.eye(k), atol=1e-11)
+    H = U.T @ M                      # symmetric positive semidefinite factor
+    assert np.allclose(H, H.T, atol=1e-10)
+    assert np.linalg.eigvalsh((H + H.T) / 2).min() > -1e-10
+
+
+@pytest.mark.parametrize("shape", [(2, 2), (3, 5), (5, 3), (8, 8), (16, 24), (24, 16)])
+def test_polar_limit(shape):
+    for seed in range(3):
+        check_polar(shape, seed)
+
+
+# ---------------------------------------------------------------------------
+# P-3: invariants.
+# ---------------------------------------------------------------------------
+
+def test_normalised_spectral_norm_at_most_one():
+    for seed in range(5):
+        M = random_matrix((12, 30), [5, seed], "student_t3")
+        X0 = O.frobenius_normalize(M)
+        assert np.linalg.norm(X0, 2) <= 1.0 + 1e-12
+        assert abs(np.linalg.norm(X0) - 1.0) < 1e-12
+
+
+def test_quintic_singular_value_band():
+    # max of the 5-fold quintic map on [0, 1] (dense grid): bounds every singular value
+    grid = np.linspace(0.0, 1.0, 200001)
+    bound = scalar_map(grid, QUINTIC, 5).max()
+    assert 1.20 < bound < 1.21
+    for seed in range(3):
+        M = random_matrix((20, 48), [6, seed])
+        s = np.linalg.svd(O.newton_schulz(M, *QUINTIC, 5), compute_uv=False)
+        assert s.max() <= bound + 1e-9 and s.min() >= 0.0
+
+
+def test_cubic_is_contractive_and_monotone():
+    M = random_matrix((10, 26), [8, 0])
+    s_in = np.linalg.svd(O.frobenius_normalize(M), compute_uv=False)
+    s_out = np.linalg.svd(O.newton_schulz(M, *CUBIC, 5), compute_uv=False)
+    assert s_out.max() <= 1.0 + 1e-12
+    assert np.all(np.diff(s_out) <= 1e-12)          # same order as the inputs
+    assert np.all(s_out >= s_in - 1e-12)            # the cubic map never shrinks x in [0, 1]
+
+
+def test_equivariances():
+    M = random_matrix((9, 21), [10, 0])
+    U = O.newton_schulz(M, *QUINTIC, 5)
+    assert np.allclose(O.newton_schulz(3.7 * M, *QUINTIC, 5), U, atol=1e-12)
+    assert np.allclose(O.newton_schulz(-M, *QUINTIC, 5), -U, atol=1e-12)
+    assert np.allclose(O.newton_schulz(M.T, *QUINTIC, 5), U.T, atol=1e-12)
+    Q1, Q2 = _orthonormal(9, 9, 30), _orthonormal(21, 21, 31)
+    assert np.allclose(O.newton_schulz(Q1 @ M @ Q2, *QUINTIC, 5), Q1 @ U @ Q2, atol=1e-11)
+
+
+def test_stage_products_are_symmetric():
+    X = random_matrix((7, 19), [11, 0])
+    A = O.gram(X)
+    B = O.poly(A, QUINTIC[1], QUINTIC[2])
+    assert np.array_equal(A, A.T) or np.allclose(A, A.T, atol=1e-14)
+    assert np.allclose(B, B.T, atol=1e-13)
+    # U^T X symmetric for the NS output (odd polynomial of X)
+    U = O.ns_iterate(O.frobenius_normalize(X), *QUINTIC, 3)
+    H = U.T @ X
+    assert np.allclose(H, H.T, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P-4: hand-worked iterations.
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_ns():
+    d = json.load(open(os.path.join(GOLDEN, "ns_hand.json")))
+    for case in d["cases"]:
+        M = np.array(case["M_exact"], dtype=np.float64)
+        U = O.newton_schulz(M, *case["coeffs"], case["steps"])
+        assert np.allclose(U, np.array(case["U"]), rtol=0, atol=1e-12), case["name"]
+
+
+# ---------------------------------------------------------------------------
+# P-5: vote by brute force over every bit pattern.
+# ---------------------------------------------------------------------------
+
+def _enumerated_buffers(M):
+    n = 1 << M
+    j = np.arange(n)
+    bufs = np.stack([O.pack_bits(((j >> k) & 1).astype(bool)) for k in range(M)])
+    expect = np.array([2 * bin(x).count("1") >= M for x in range(n)])
+    return bufs, n, expect
+
+
+@pytest.mark.parametrize("M", list(range(1, 12)) + [15])
+def test_vote_all_patterns(M):
+    bufs, n, expect = _enumerated_buffers(M)
+    got = O.unpack_bits(O.majority_vote(bufs, n), n)
+    assert np.array_equal(got, expect)
+
+
+def test_vote_loop_matches_and_textbook_majority():
+    rng = np.random.default_rng(3)
+    n = 200
+    bits = rng.integers(0, 2, size=(3, n)).astype(bool)
+    bufs = np.stack([O.pack_bits(b) for b in bits])
+    out = O.majority_vote(bufs, n)
+    a, b, c = bits
+    assert np.array_equal(O.unpack_bits(out, n), (a & b) | (a & c) | (b & c))
+    loop = O.majority_vote_loop([[int(w) for w in buf] for buf in bufs], n)
+    assert [int(w) for w in out] == loop
+
+
+def test_vote_properties():
+    rng = np.random.default_rng(4)
+    n, M = 333, 7
+    bits = rng.integers(0, 2, size=(M, n)).astype(bool)
+    bufs = np.stack([O.pack_bits(b) for b in bits])
+    out = O.majority_vote(bufs, n)
+    assert np.array_equal(O.majority_vote(bufs[:1], n), bufs[0])                # M = 1
+    assert np.array_equal(O.majority_vote(np.stack([bufs[2]] * 5), n), bufs[2])  # identical
+    assert np.array_equal(O.majority_vote(bufs[rng.permutation(M)], n), out)     # order-free
+    neg = np.stack([O.pack_bits(~b) for b in bits])                               # odd M
+    assert np.array_equal(O.unpack_bits(O.majority_vote(neg, n), n), ~O.unpack_bits(out, n))
+    # int8 SUM of +-1 signs, then sign with sign(0) = +1
+    s8 = np.where(bits, 1, -1).astype(np.int8).sum(axis=0, dtype=np.int8)
+    assert np.array_equal(O.unpack_bits(out, n), s8 >= 0)
+
+
+def test_vote_golden():
+    d = json.load(open(os.path.join(GOLDEN, "bits_hand.json")))["vote"]
+    bufs = np.array([int(x, 16) for x in d["buffers"]], dtype=np.uint64)[:, None]
+    assert int(O.majority_vote(bufs, d["n"])[0]) == int(d["out_m3"], 16)
+    assert int(O.majority_vote(bufs[:2], d["n"])[0]) == int(d["out_m2"], 16)
+
+
+# ---------------------------------------------------------------------------
+# P-6: sign and packing.
+# ---------------------------------------------------------------------------
+
+def test_pack_golden_and_sizes():
+    d = json.load(open(os.path.join(GOLDEN, "bits_hand.json")))["pack"]
+    U = [1.5, -2.0, 0.0, -0.0, float("nan"), -1e-30, 3.0, -0.5]
+    U += [1.0 if i % 2 == 0 else -1.0 for i in range(8, 64)]
+    U += [-3.0, 2.0, -1.0, -1.0, -1.0, -1.0]
+    words = O.sign_pack(np.array(U))
+    assert [int(w) for w in words] == [int(x, 16) for x in d["words"]]
+    # bf16 storage of the same values packs identically
+    from workloads import store
+    Ub = O.decode(store(np.array(U), "bf16"), "bf16")
+    assert [int(w) for w in O.sign_pack(Ub)] == [int(x, 16) for x in d["words"]]
+    for n in [1, 63, 64, 65, 4096 * 14336 // 1024]:
+        assert O.pack_bits(np.ones(n, bool)).nbytes == 8 * ((n + 63) // 64)
+
+
+def test_pack_roundtrip_loop_and_counts():
+    rng = np.random.default_rng(5)
+    for n in [1, 5, 64, 65, 130, 1000]:
+        U = rng.standard_normal(n)
+        U[rng.integers(0, n, size=max(1, n // 10))] = 0.0
+        bits = O.sign_bits(U)
+        words = O.pack_bits(bits)
+        assert np.array_equal(O.unpack_bits(words, n), U >= 0)
+        assert [int(w) for w in words] == O.pack_bits_loop(list(bits))
+        assert sum(bin(int(w)).count("1") for w in words) == int((U >= 0).sum())
+        pad = O.unpack_bits(words, len(words) * 64)[n:]
+        assert not pad.any()
+
+
+# ---------------------------------------------------------------------------
+# P-7 / P-8 / P-9: update, momentum, norm.
+# ---------------------------------------------------------------------------
+
+def test_update_golden():
+    d = json.load(open(os.path.join(GOLDEN, "bits_hand.json")))
+    f = d["update_f32"]
+    W = np.array(f["W"], dtype=np.float32)
+    out = O.apply_update(W, "f32", np.array([int(f["vote"], 16)], dtype=np.uint64), f["eta"])
+    assert out.tolist() == f["W_new"]
+    b = d["update_bf16"]
+    Wb = np.array([int(x, 16) for x in b["W_bits"]], dtype=np.uint16)
+    out = O.apply_update(Wb, "bf16", np.array([int(b["vote"], 16)], dtype=np.uint64), b["eta"])
+    assert [int(x) for x in out] == [int(x, 16) for x in b["W_new_bits"]]
+
+
+def test_update_properties():
+    rng = np.random.default_rng(6)
+    n = 500
+    W = rng.standard_normal(n).astype(np.float32)
+    vote = O.pack_bits(rng.integers(0, 2, n).astype(bool))
+    assert np.array_equal(O.apply_update(W, "f32", vote, 0.0), W)
+    eta = 0.02
+    new = O.apply_update(W, "f32", vote, eta).astype(np.float64)
+    s = np.where(O.unpack_bits(vote, n), 1.0, -1.0)
+    step = W.astype(np.float64) - new
+    assert np.allclose(step, eta * s, rtol=0, atol=np.spacing(np.abs(W)).max() + 1e-9)
+
+
+def test_momentum_golden_and_special_cases():
+    d = json.load(open(os.path.join(GOLDEN, "bits_hand.json")))["momentum"]
+    f = d["f32"]
+    out = O.momentum(np.array(f["M"], np.float32), "f32", np.array(f["G"], np.float32), "f32",
+                     f["beta"], f["alpha"])
+    assert out.tolist() == f["M_new"]
+    b = d["bf16"]
+    Mb = np.array([int(x, 16) for x in b["M_bits"]], np.uint16)
+    Gb = np.array([int(x, 16) for x in b["G_bits"]], np.uint16)
+    out = O.momentum(Mb, "bf16", Gb, "bf16", b["beta"], b["alpha"])
+    assert [int(x) for x in out] == [int(x, 16) for x in b["M_new_bits"]]
+    rng = np.random.default_rng(7)
+    M = rng.standard_normal(100).astype(np.float32)
+    G = rng.standard_normal(100).astype(np.float32)
+    alpha = float(np.float32(0.05))
+    assert np.array_equal(O.momentum(M, "f32", G, "f32", 0.0, alpha),
+                          (np.float32(alpha) * G).astype(np.float32))
+    assert np.array_equal(O.momentum(M, "f32", G, "f32", 1.0, 0.0), M)
+
+
+def test_norm_golden():
+    d = json.load(open(os.path.join(GOLDEN, "bits_hand.json")))["norm"]
+    M1 = np.array(d["M1"])
+    assert O.sumsq(M1) == d["sumsq1"]
+    assert np.allclose(O.frobenius_normalize(M1), np.array(d["X0_1"]), atol=1e-15)
+    M2 = np.full(d["M2_shape"], d["M2_value"])
+    assert O.sumsq(M2) == d["sumsq2"]
+    assert math.isclose(math.sqrt(O.sumsq(M2)), 1.5 * math.sqrt(6.0), rel_tol=1e-15)
+
+
+def test_special_values_follow_sign_rule():
+    # NaN anywhere makes the norm NaN, every U entry NaN, every sign +1
+    M = random_matrix((4, 6), [12, 0])
+    M[1, 2] = np.nan
+    U = O.newton_schulz(M, *QUINTIC, 2)
+    assert np.isnan(U).all()
+    assert O.sign_bits(U).all()
+    assert O.sign_bits(np.zeros((3, 3))).all()
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each breaks one oracle function; some pin must fail.
+# ---------------------------------------------------------------------------
+
+def _pins_ns():
+    for shape in [(8, 8), (5, 9), (9, 5)]:
+        check_closed_form(shape, QUINTIC, 2)
+        check_closed_form(shape, (2.0, -1.5, 0.5), 1)
+    test_hand_worked_ns()
+
+
+def _pins_bits():
+    test_pack_golden_and_sizes()
+    test_pack_roundtrip_loop_and_counts()
+    for M in [2, 3, 4, 5]:
+        test_vote_all_patterns(M)
+    test_vote_golden()
+    test_update_golden()
+    test_momentum_golden_and_special_cases()
+
+
+MUTANTS = {
+    "poly drops the c term": ("poly", lambda A, b, c: b * A, _pins_ns),
+    "poly flips the sign of b": ("poly", lambda A, b, c: -b * A + c * A @ A, _pins_ns),
+    "apply drops aX": ("apply_poly", lambda B, X, a: B @ X, _pins_ns),
+    "apply multiplies on the right": ("apply_poly", lambda B, X, a: a * X + X @ B, _pins_ns),
+    "gram on the long side": ("gram", lambda X: np.asarray(X).T @ np.asarray(X), _pins_ns),
+    "gram without transpose": ("gram", lambda X: np.asarray(X)[:, :X.shape[0]] @ np.asarray(X)[:, :X.shape[0]], _pins_ns),
+    "normalise by max entry": ("frobenius_normalize", lambda M: M / np.abs(M).max(), _pins_ns),
+    "normalise by squared norm": ("frobenius_normalize", lambda M: M / O.sumsq(M), _pins_ns),
+    "sign(0) := -1": ("sign_bits", lambda U: np.asarray(U) > 0, _pins_bits),
+    "pack MSB first": ("pack_bits", lambda b: np.packbits(
+        np.concatenate([np.asarray(b, bool).ravel(), np.zeros((-len(np.asarray(b).ravel())) % 64, bool)]),
+        bitorder="big").view("<u8").astype(np.uint64), _pins_bits),
+    "vote strict majority": ("majority_vote", lambda w, n: O.pack_bits(
+        2 * np.stack([O.unpack_bits(x, n) for x in np.atleast_2d(w)]).sum(0) > np.atleast_2d(w).shape[0]),
+        _pins_bits),
+    "update adds the step": ("apply_update", lambda W, dt, v, eta: _wrong_update(W, dt, v, eta), _pins_bits),
+    "momentum heavy-ball": ("momentum", lambda M, md, G, gd, beta, alpha: O.round_to_storage(
+        beta * O.decode(M, md) + O.decode(G, gd), md), _pins_bits),
+}
+
+_REAL_APPLY_UPDATE = O.apply_update
+
+
+def _wrong_update(W, dt, v, eta):
+    return _REAL_APPLY_UPDATE(W, dt, v, -eta)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, broken, pins = MUTANTS[name]
+    monkeypatch.setattr(O, attr, broken)
+    with pytest.raises((AssertionError, ValueError)):
+        pins()
