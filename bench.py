@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of one SignMuon worker step on one MI355X.
+
+A step is one worker's momentum EMA with per-matrix norms, Newton-Schulz
+(5 quintic iterations, bf16 MFMA / fp32 accumulation), sign + 1-bit pack,
+then the majority vote over the M workers' packed buffers resident on the GPU
+and the update W <- W - eta * vote.  Default workload: one 4096 x 14336 bf16
+matrix (Llama-3-8B MLP shape), 1% heavy columns, M = 7 workers.
+
+Prints one JSON line.  The timed region records HIP events on the stream
+the kernels run on between every library call, so per-kernel times come from
+the same steps as the headline number.
+
+    python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+METRIC = "Muon steps/sec + NS MFMA TFLOP/s (% bf16 peak) at 4096×14336; pack/vote GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeat-kernel", default=None,
+                    help="profiling aid: after the run, launch one stage N more times "
+                         "(gram|poly|apply|momentum|pack|vote|update|copy:N)")
+    return ap.parse_args()
+
+
+def ns_flops(s: int, l: int, c_nonzero: bool):
+    """Algorithmic flops of one iteration: symmetric Gram, symmetric A*A, B*X."""
+    gram = s * (s + 1) * l
+    poly = s * s * (s + 1) if c_nonzero else 0
+    apply = 2 * s * s * l
+    return gram, poly, apply
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import matrix_aware_optimizer_amd as mao
+    from workloads import WORKLOADS, gen_G, gen_M0, gen_W0
+
+    wl = WORKLOADS[args.workload]
+    if len(set(wl.shapes)) != 1 or len(wl.shapes) != 1:
+        # the instrumented step below drives the stage kernels of one matrix shape
+        raise SystemExit("bench.py times single-matrix workloads (4 or 5); others are parity cases")
+    rows, cols = wl.shapes[0]
+    s, l = min(rows, cols), max(rows, cols)
+    if rows > cols or s % mao.MUON_NS_PAD or l % mao.MUON_NS_PAD:
+        raise SystemExit("bench workload must be wide and pad-free")
+    dev = torch.device("cuda", 0)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    prec = wl.precision
+    a, b, c = wl.coeffs
+
+    def dev_tensor(arr, dt):
+        if dt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(arr).to(dev)
+
+    t0 = time.time()
+    W = dev_tensor(gen_W0(wl), wl.w_dtype)
+    M0 = gen_M0(wl)
+    Ms = [dev_tensor(M0, wl.m_dtype) for _ in range(wl.workers)]
+    Gs = [dev_tensor(gen_G(wl, k, 0), wl.g_dtype) for k in range(wl.workers)]
+    gen_s = time.time() - t0
+
+    n = wl.numel
+    nwords = mao.packed_words(n)
+    offsets = torch.tensor([0, n], dtype=torch.int64, device=dev)
+    sumsq = torch.zeros(1, dtype=torch.float32, device=dev)
+    mom_ws = torch.empty(mao.muon_momentum_workspace_bytes(n, 1), dtype=torch.uint8, device=dev)
+    X = [torch.empty((s, l), dtype=tdt[prec], device=dev) for _ in range(2)]
+    A = torch.empty((s, s), dtype=tdt[prec], device=dev)
+    B = torch.empty((s, s), dtype=tdt[prec], device=dev)
+    bits = torch.zeros((wl.workers, nwords), dtype=torch.int64, device=dev)
+    vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
+
+    def worker(k, ev=None):
+        """a1-a6 for worker k; with `ev`, record an event after every call."""
+        mark = (lambda name: ev.append((name, torch.cuda.Event(enable_timing=True))) or
+                ev[-1][1].record()) if ev is not None else (lambda name: None)
+        mark("start")
+        mao.muon_momentum(Ms[k], Gs[k], wl.beta, wl.alpha, offsets, sumsq, mom_ws)
+        mark("momentum")
+        mao.ns_normalize(Ms[k].view(rows, cols), sumsq, X[0], prec)
+        mark("normalize")
+        cur = 0
+        for _ in range(wl.ns_steps):
+            mao.ns_gram(X[cur], A, prec)
+            mark("gram")
+            if c != 0.0:
+                mao.ns_poly(A, B, b, c, prec)
+                mark("poly")
+            mao.ns_apply(B if c != 0.0 else A, X[cur], X[1 - cur], a, 1.0 if c != 0.0 else b, prec)
+            mark("apply")
+            cur = 1 - cur
+        mao.sign_pack(X[cur], bits[k])
+        mark("pack")
+
+    def tail(ev=None):
+        mao.majority_vote(bits, vote)
+        if ev is not None:
+            ev.append(("vote", torch.cuda.Event(enable_timing=True)))
+            ev[-1][1].record()
+        mao.apply_update(W, vote, wl.eta)
+        if ev is not None:
+            ev.append(("update", torch.cuda.Event(enable_timing=True)))
+            ev[-1][1].record()
+
+    # the other workers' packed signs, resident on the GPU (what an all-gather would deliver)
+    for k in range(1, wl.workers):
+        worker(k)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        worker(0)
+        tail()
+    torch.cuda.synchronize()
+
+    events = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        ev = []
+        worker(0, ev)
+        tail(ev)
+        events.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    # per-kernel times from the events of the timed steps
+    per = {}
+    step_ms = []
+    for ev in events:
+        prev = ev[0][1]
+        for name, e in ev[1:]:
+            per.setdefault(name, []).append(prev.elapsed_time(e))
+            prev = e
+        step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
+    launches = {k: len(v) / args.steps for k, v in per.items()}
+    avg = {k: float(np.mean(v)) for k, v in per.items()}            # ms per launch
+    total = {k: avg[k] * launches[k] for k in avg}                  # ms per step
+
+    ms_per_step = wall * 1e3 / args.steps
+    gram_f, poly_f, apply_f = ns_flops(s, l, c != 0.0)
+    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply") if k in total)
+    ns_flop = wl.ns_steps * (gram_f + poly_f + apply_f)
+    peak = PEAK_BF16_TFLOPS if prec == "bf16" else PEAK_F32_TFLOPS
+    ns_tflops = ns_flop / (ns_ms * 1e-3) / 1e12
+
+    es = {"bf16": 2, "f32": 4}
+    bytes_momentum = n * (2 * es[wl.m_dtype] + es[wl.g_dtype])
+    bytes_pack = n * es[prec] + nwords * 8
+    bytes_vote = (wl.workers + 1) * nwords * 8
+    bytes_update = 2 * n * es[wl.w_dtype] + nwords * 8
+
+    def gbs(nbytes, key):
+        return nbytes / (avg[key] * 1e-3) / 1e9
+
+    kernels = {
+        "momentum": {"ms": avg["momentum"], "GB/s": gbs(bytes_momentum, "momentum")},
+        "normalize": {"ms": avg["normalize"],
+                      "GB/s": gbs(n * (es[wl.m_dtype] + es[prec]), "normalize")},
+        "gram": {"ms": avg["gram"], "TFLOP/s": gram_f / (avg["gram"] * 1e-3) / 1e12},
+        "apply": {"ms": avg["apply"], "TFLOP/s": apply_f / (avg["apply"] * 1e-3) / 1e12},
+        "pack": {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack")},
+        "vote": {"ms": avg["vote"], "GB/s": gbs(bytes_vote, "vote")},
+        "update": {"ms": avg["update"], "GB/s": gbs(bytes_update, "update")},
+    }
+    if "poly" in avg:
+        kernels["poly"] = {"ms": avg["poly"], "TFLOP/s": poly_f / (avg["poly"] * 1e-3) / 1e12}
+    for k in kernels:
+        kernels[k]["launches_per_step"] = launches[k]
+        if "GB/s" in kernels[k]:
+            kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
+        else:
+            kernels[k]["frac_peak"] = kernels[k]["TFLOP/s"] / peak
+
+    dominant = max(total, key=total.get)
+    dom_flops = {"gram": gram_f, "poly": poly_f, "apply": apply_f}.get(dominant)
+    if dom_flops is not None:
+        ach = dom_flops / (avg[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": peak,
+                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                    "per_launch_flops": dom_flops, "avg_launch_ms": avg[dominant]}
+    else:
+        nb = {"momentum": bytes_momentum, "pack": bytes_pack, "vote": bytes_vote,
+              "update": bytes_update}[dominant]
+        ach = gbs(nb, dominant)
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                    "per_launch_bytes": nb, "avg_launch_ms": avg[dominant]}
+
+    result = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prec,
+        "data": "synthetic",
+        "config": {"workload": f"C{wl.cfg}: {wl.name}", "shape": [rows, cols], "workers": wl.workers,
+                   "ns_steps": wl.ns_steps, "coeffs": list(wl.coeffs), "beta": wl.beta,
+                   "eta": wl.eta, "momentum_dtype": wl.m_dtype, "weight_dtype": wl.w_dtype},
+        "ns_tflops": ns_tflops,
+        "ns_frac_bf16_peak": ns_tflops / peak,
+        "orthogonalizations_per_s": 1e3 / ns_ms,
+        "pack_gbs": kernels["pack"]["GB/s"],
+        "vote_gbs": kernels["vote"]["GB/s"],
+        "event_ms_per_step": float(np.median(step_ms)),
+        "kernels": kernels,
+        "roofline": roofline,
+        "input_generation_s": gen_s,
+    }
+
+    if args.repeat_kernel:
+        name, _, cnt = args.repeat_kernel.partition(":")
+        cnt = int(cnt or 10)
+        for _ in range(cnt):
+            if name == "gram":
+                mao.ns_gram(X[0], A, prec)
+            elif name == "poly":
+                mao.ns_poly(A, B, b, c, prec)
+            elif name == "apply":
+                mao.ns_apply(B, X[0], X[1], a, 1.0, prec)
+            elif name == "copy":
+                X[1].copy_(X[0])
+        torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on the host cores: the elementwise stages on the whole matrix
+    and one of the Newton-Schulz iterations, scaled to a full worker step."""
+    import oracle.muon_oracle as O
+    from workloads import gen_G, gen_M0, gen_W0
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rows, cols = wl.shapes[0]
+    W0, M0, G = gen_W0(wl), gen_M0(wl), gen_G(wl, 0, 0)
+    a, b, c = wl.coeffs
+    t0 = time.perf_counter()
+    Mn = O.momentum(M0, wl.m_dtype, G, wl.g_dtype, wl.beta, wl.alpha)
+    Mf = O.decode(Mn, wl.m_dtype).reshape(rows, cols)
+    X = O.frobenius_normalize(Mf)
+    X = X.T if rows > cols else X
+    t_elem0 = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    X1 = O.ns_iterate(X, a, b, c, 1)
+    t_iter = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    words = O.sign_pack(X1)
+    packed = np.stack([words] * wl.workers)
+    vote = O.majority_vote(packed, wl.numel)
+    O.apply_update(W0, wl.w_dtype, vote, wl.eta)
+    t_elem1 = time.perf_counter() - t2
+    est = t_elem0 + t_elem1 + wl.ns_steps * t_iter
+    return {"value": 1.0 / est, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle on the full {rows}x{cols} matrix: momentum, norm, sign/pack, "
+                      f"{wl.workers}-way vote, update, and 1 of {wl.ns_steps} Newton-Schulz "
+                      f"iterations (timed {t_iter:.2f} s), step time = elementwise + "
+                      f"{wl.ns_steps} x iteration = {est:.2f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

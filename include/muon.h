@@ -1,0 +1,198 @@
+/*
+ * muon.h -- C ABI of libmuon: the Muon optimizer step with SignMuon's 1-bit
+ * sign and majority-vote tail, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [SM] "SignMuon: Otimização Distribuída de Muon com Eficiência de
+ *        Comunicação" (gist.science technical summary), section 2
+ *        "Metodologia: Sign-Muon" -- "Mecanismo Central", "Fluxo Algorítmico
+ *        (Distribuído)" steps 1-4 and "Eficiência de Comunicação".
+ *   [MG] "NVIDIA MegatronによるLLM学習高速化へ向けた新世代オプティマイザの高度化",
+ *        paragraphs 「分散モード」 (three matrix products per Newton-Schulz
+ *        iteration) and 「SYRK と融合された all-reduce」 (symmetric rank-k
+ *        products that write the full matrix).
+ *
+ * Conventions shared by every call
+ *   - All matrices are dense, row-major and contiguous.  Dtype codes are
+ *     MUON_F32 (IEEE binary32) and MUON_BF16 (bfloat16, the upper 16 bits of
+ *     binary32).
+ *   - Every tensor argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory, and keeps no state
+ *     between calls.  Scratch memory is passed in as `workspace`, sized by the
+ *     matching *_workspace_bytes query.
+ *   - Device pointers must be 16-byte aligned (MUON_EALIGN otherwise).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     kernels on it and never synchronise; device faults surface at the
+ *     caller's next synchronisation.  Calls on different streams that share
+ *     output or workspace buffers race.
+ *   - Every call returns a status: MUON_OK (0) or a negative MUON_E* code.
+ *     Arguments are validated before anything is enqueued, so on any error
+ *     other than MUON_ELAUNCH nothing was launched.  No exception or abort
+ *     crosses the ABI.
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum muon_dtype { MUON_F32 = 0, MUON_BF16 = 1 };
+
+enum muon_status {
+  MUON_OK = 0,
+  MUON_EINVAL = -1,     /* null pointer, negative or inconsistent size      */
+  MUON_EDTYPE = -2,     /* unsupported dtype / precision code               */
+  MUON_EALIGN = -3,     /* a device pointer is not 16-byte aligned          */
+  MUON_EWORKSPACE = -4, /* workspace missing or smaller than the query says */
+  MUON_ELAUNCH = -5     /* the HIP runtime rejected a kernel launch         */
+};
+
+/* Newton-Schulz working dimensions are padded up to a multiple of this. */
+#define MUON_NS_PAD 256
+/* Largest worker count accepted by the vote calls. */
+#define MUON_MAX_VOTERS 1023
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* muon_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int muon_version(void);
+
+/* ---------------------------------------------------------------------------
+ * a1 -- momentum EMA and per-matrix squared Frobenius norm.
+ *   [SM] "Fluxo Algorítmico" step 1: each worker updates its local momentum.
+ *   The pages print no formula; this computes the EMA
+ *       M[i] <- round_m( beta * M[i] + alpha * G[i] )          (fp32 math)
+ *   in place over a flat parameter set of `numel` entries, with alpha =
+ *   1 - beta for the classical EMA (heavy-ball momentum is beta, alpha = 1).
+ *   If `sumsq_out` is not NULL it also writes, for every matrix j of the set,
+ *       sumsq_out[j] = sum over its entries of (stored new M)^2,
+ *   the squared Frobenius norm the normalisation divides by.  Matrix j covers
+ *   flat entries [seg_offsets[j], seg_offsets[j+1]).
+ *
+ *   M          device, numel entries of m_dtype (F32 or BF16), updated in place
+ *   G          device, numel entries of g_dtype (F32 or BF16), read only
+ *   seg_offsets device int64[nseg+1], 0 = seg_offsets[0] <= ... <= seg_offsets
+ *              [nseg] = numel (only read when sumsq_out != NULL)
+ *   sumsq_out  device float[nseg], or NULL to skip the norms
+ *   workspace  device scratch of muon_momentum_workspace_bytes(numel, nseg)
+ *              bytes (only needed when sumsq_out != NULL)
+ *   The sums are deterministic: identical inputs give bit-identical results.
+ * ------------------------------------------------------------------------- */
+size_t muon_momentum_workspace_bytes(int64_t numel, int nseg);
+int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
+                  const int64_t* seg_offsets, int nseg, float beta, float alpha,
+                  float* sumsq_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a2-a5 -- Newton-Schulz orthogonalisation of a list of momentum matrices.
+ *   [SM] "Mecanismo Central" item 1 and "Fluxo" step 1: the polar direction U
+ *   of the momentum, approximated by the Newton-Schulz iteration.  For every
+ *   problem:
+ *       X0 = M / ||M||_F                 (zero matrix -> U = 0)
+ *       repeat `steps` times:            ([MG] 「分散モード」: three products)
+ *           A = X X^T                    (Gram on the short side; symmetric)
+ *           B = b A + c A A              (skipped when c == 0: B = b A)
+ *           X = a X + B X
+ *       U = X
+ *   (a, b, c) are free, so cubic (1.5, -0.5, 0) and quintic coefficient sets
+ *   share this call.  For a tall matrix (rows > cols) the iteration runs on
+ *   X^T, an exact identity; U is always written in the input's orientation.
+ *   The Gram and the polynomial products are symmetric rank-k products
+ *   ([MG] 「SYRK と融合された all-reduce」): only lower-triangle tiles are
+ *   computed and mirrored into the full matrix.
+ *
+ *   precision  MUON_BF16: bf16 MFMA operands, fp32 accumulation, X, A and B
+ *              held in bf16 between products.  MUON_F32: fp32 throughout.
+ *   problem    M (device, rows x cols of m_dtype), U (device, rows x cols of
+ *              u_dtype, may alias nothing else), sumsq (device float holding
+ *              sum(M^2), e.g. from muon_momentum, or NULL to compute it).
+ *   Problems of equal shape and dtypes whose pointers are evenly spaced are
+ *   batched into one launch per stage.  steps == 0 gives U = X0.
+ * ------------------------------------------------------------------------- */
+typedef struct muon_ns_problem {
+  const void* M;
+  void* U;
+  const float* sumsq;
+  int64_t rows;
+  int64_t cols;
+  int32_t m_dtype;
+  int32_t u_dtype;
+} muon_ns_problem;
+
+size_t ns_workspace_bytes(const muon_ns_problem* probs, int count, int precision);
+int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, float c,
+                     int steps, int precision, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Stage calls of the iteration, on padded short-side working buffers.
+ * s and l are the padded short and long sides (multiples of MUON_NS_PAD);
+ * X is [batch][s][l], A and B are [batch][s][s]; element type is bf16 for
+ * MUON_BF16 and fp32 for MUON_F32.  Padding rows/columns must be zero, and
+ * stay zero through every stage.
+ *
+ * ns_normalize (a2): X0[b] = pad(orient(M[b])) * (1/sqrt(sumsq[b])), with the
+ *   M matrices rows x cols contiguous one after another, orient = transpose
+ *   when rows > cols, and sumsq[b] == 0 giving X0[b] = 0.
+ * ns_gram      (a3): A[b] = X[b] X[b]^T.
+ * ns_poly      (a4): B[b] = b A[b] + c A[b] A[b]   (A symmetric).
+ * ns_apply     (a5): Xout[b] = a X[b] + alpha B[b] X[b]. */
+int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t batch,
+                 const float* sumsq, void* X0, int precision, void* stream);
+int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision,
+            void* stream);
+int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c,
+            int precision, void* stream);
+int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch,
+             float a, float alpha, int precision, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a6 -- entrywise sign and 1-bit packing.
+ *   [SM] "Fluxo" steps 2-3: S = sign(U) in {-1,+1}, packed one bit per entry
+ *   for the all-gather exchange ("Eficiência de Comunicação": 32x smaller than
+ *   fp32).  Bit i (flat row-major index) is 1 iff !(U[i] < 0), i.e. +1 for
+ *   positive, +0.0, -0.0 and NaN.  Layout: word i>>6, bit i&63 (LSB first),
+ *   little-endian 64-bit words; the ceil(numel/64)*64 - numel padding bits of
+ *   the last word are 0.
+ *   U     device, numel entries of u_dtype
+ *   bits  device uint64[ceil(numel/64)]
+ * ------------------------------------------------------------------------- */
+int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a7 -- majority vote over M packed sign buffers.
+ *   [SM] "Mecanismo Central" item 3: S_bar = sign(sum_m S^(m)), an integer sum
+ *   of signs and a local threshold.  With sign(0) := +1 this is: out bit = 1
+ *   iff 2 * (number of buffers with bit 1) >= M.  Bit-exact.
+ *   bits  device uint64[M][nwords] (buffer k at bits + k*nwords)
+ *   out   device uint64[nwords]; padding bits follow the same rule (a padding
+ *         bit 0 in every buffer votes 0 only when M >= 1: 2*0 >= M is false).
+ *   1 <= M <= MUON_MAX_VOTERS.
+ * ------------------------------------------------------------------------- */
+int majority_vote(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * a8 -- update W <- W - eta * S_bar.
+ *   [SM] "Fluxo" step 4.  Per entry: W[i] <- round_w( fp32(W[i]) - s_i*eta )
+ *   with s_i = +1 if vote bit i is 1, else -1; one IEEE fp32 subtraction,
+ *   then round-to-nearest-even to bf16 for bf16 storage.  Bit-exact.
+ *   W          device, numel entries of w_dtype, updated in place
+ *   vote_bits  device uint64[ceil(numel/64)]
+ * ------------------------------------------------------------------------- */
+int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits, float eta,
+                 void* stream);
+
+/* a7 + a8 fused: the vote of M buffers applied straight to W, without
+ * writing the vote bits.  Same result as majority_vote then apply_update. */
+int vote_and_update(void* W, int w_dtype, int64_t numel, const uint64_t* bits, int M,
+                    float eta, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

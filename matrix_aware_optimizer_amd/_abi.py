@@ -1,0 +1,285 @@
+"""ctypes binding of libmuon's C ABI (argument marshalling only).
+
+Every function here has the name of the C entry point it calls, converts
+torch tensors to (device pointer, dtype code, size) and the current HIP
+stream, and raises :class:`MuonError` on a non-zero status.  No arithmetic
+of the method happens in Python, and there is no fallback: if libmuon.so is
+missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch  # imported first so libmuon binds to the HIP runtime torch loaded
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmuon.so")
+
+MUON_F32, MUON_BF16 = 0, 1
+MUON_NS_PAD = 256
+MUON_MAX_VOTERS = 1023
+
+_c_void_p, _c_int, _c_i64, _c_size, _c_float = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                                 ctypes.c_size_t, ctypes.c_float)
+
+
+class MuonError(RuntimeError):
+    """A libmuon call returned a non-zero status."""
+
+    def __init__(self, name: str, status: int, text: str):
+        super().__init__(f"{name} failed with status {status}: {text}")
+        self.status = status
+
+
+class NSProblem(ctypes.Structure):
+    """Mirror of ``struct muon_ns_problem``."""
+
+    _fields_ = [("M", _c_void_p), ("U", _c_void_p), ("sumsq", _c_void_p),
+                ("rows", _c_i64), ("cols", _c_i64), ("m_dtype", ctypes.c_int32),
+                ("u_dtype", ctypes.c_int32)]
+
+
+# (name, restype, argtypes) of every exported symbol declared in include/muon.h
+SIGNATURES = {
+    "muon_status_string": (ctypes.c_char_p, [_c_int]),
+    "muon_version": (_c_int, []),
+    "muon_momentum_workspace_bytes": (_c_size, [_c_i64, _c_int]),
+    "muon_momentum": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_i64, _c_void_p, _c_int,
+                               _c_float, _c_float, _c_void_p, _c_void_p, _c_size, _c_void_p]),
+    "ns_workspace_bytes": (_c_size, [ctypes.POINTER(NSProblem), _c_int, _c_int]),
+    "ns_orthogonalize": (_c_int, [ctypes.POINTER(NSProblem), _c_int, _c_float, _c_float, _c_float,
+                                  _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "ns_normalize": (_c_int, [_c_void_p, _c_int, _c_i64, _c_i64, _c_i64, _c_void_p, _c_void_p,
+                              _c_int, _c_void_p]),
+    "ns_gram": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_int, _c_void_p]),
+    "ns_poly": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_float, _c_float, _c_int,
+                         _c_void_p]),
+    "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_float,
+                          _c_float, _c_int, _c_void_p]),
+    "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
+    "majority_vote": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
+    "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
+    "vote_and_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_int, _c_float,
+                                 _c_void_p]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmuon.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m matrix_aware_optimizer_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().muon_status_string(status).decode()
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise MuonError(name, status, status_string(status))
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MUON_F32
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def precision_code(p: Union[str, int]) -> int:
+    if isinstance(p, int):
+        return p
+    return {"f32": MUON_F32, "fp32": MUON_F32, "float32": MUON_F32,
+            "bf16": MUON_BF16, "bfloat16": MUON_BF16}[p]
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+# a1
+# ---------------------------------------------------------------------------
+
+def muon_momentum_workspace_bytes(numel: int, nseg: int) -> int:
+    return int(lib().muon_momentum_workspace_bytes(numel, nseg))
+
+
+def muon_momentum(M: torch.Tensor, G: torch.Tensor, beta: float, alpha: float,
+                  seg_offsets: Optional[torch.Tensor] = None,
+                  sumsq_out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """``M <- beta*M + alpha*G`` in place; optional per-matrix sum of squares."""
+    if M.numel() != G.numel():
+        raise ValueError("M and G must have the same number of entries")
+    nseg, ws_ptr, ws_bytes = 0, None, 0
+    if sumsq_out is not None:
+        if seg_offsets is None:
+            raise ValueError("seg_offsets is required with sumsq_out")
+        nseg = seg_offsets.numel() - 1
+        need = muon_momentum_workspace_bytes(M.numel(), nseg)
+        workspace = _workspace(need, M, workspace)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check("muon_momentum", lib().muon_momentum(
+        _dev(M, "M"), dtype_code(M), _dev(G, "G"), dtype_code(G), M.numel(),
+        _dev(seg_offsets, "seg_offsets") if sumsq_out is not None else None, nseg,
+        float(beta), float(alpha), _dev(sumsq_out, "sumsq_out"), ws_ptr, ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# a2-a5
+# ---------------------------------------------------------------------------
+
+ProblemLike = Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]
+
+
+def _problems(problems: Sequence[ProblemLike]):
+    arr = (NSProblem * len(problems))()
+    for i, (M, U, sumsq) in enumerate(problems):
+        if M.dim() != 2 or U.shape != M.shape:
+            raise ValueError("each problem needs a 2-D M and a U of the same shape")
+        arr[i].M = _dev(M, "M")
+        arr[i].U = _dev(U, "U")
+        arr[i].sumsq = _dev(sumsq, "sumsq") if sumsq is not None else None
+        arr[i].rows, arr[i].cols = M.shape
+        arr[i].m_dtype = dtype_code(M)
+        arr[i].u_dtype = dtype_code(U)
+    return arr
+
+
+def ns_workspace_bytes(problems: Sequence[ProblemLike], precision="bf16") -> int:
+    arr = _problems(problems)
+    return int(lib().ns_workspace_bytes(arr, len(problems), precision_code(precision)))
+
+
+def ns_orthogonalize(problems: Sequence[ProblemLike], a: float, b: float, c: float, steps: int,
+                     precision="bf16", workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Polar directions of every (M, U, sumsq-or-None) problem, written into U."""
+    if len(problems) == 0:
+        return
+    arr = _problems(problems)
+    prec = precision_code(precision)
+    need = int(lib().ns_workspace_bytes(arr, len(problems), prec))
+    workspace = _workspace(need, problems[0][0], workspace)
+    _check("ns_orthogonalize", lib().ns_orthogonalize(
+        arr, len(problems), float(a), float(b), float(c), int(steps), prec,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def _batch3(t: torch.Tensor) -> Tuple[int, int, int]:
+    if t.dim() == 2:
+        return 1, t.shape[0], t.shape[1]
+    if t.dim() == 3:
+        return t.shape[0], t.shape[1], t.shape[2]
+    raise ValueError("expected a 2-D or 3-D tensor")
+
+
+def ns_normalize(M: torch.Tensor, sumsq: torch.Tensor, X0: torch.Tensor, precision="bf16",
+                 stream=None) -> None:
+    batch, rows, cols = _batch3(M)
+    _check("ns_normalize", lib().ns_normalize(
+        _dev(M, "M"), dtype_code(M), rows, cols, batch, _dev(sumsq, "sumsq"), _dev(X0, "X0"),
+        precision_code(precision), _stream(stream)))
+
+
+def ns_gram(X: torch.Tensor, A: torch.Tensor, precision="bf16", stream=None) -> None:
+    batch, s, l = _batch3(X)
+    _check("ns_gram", lib().ns_gram(_dev(X, "X"), _dev(A, "A"), s, l, batch,
+                                    precision_code(precision), _stream(stream)))
+
+
+def ns_poly(A: torch.Tensor, B: torch.Tensor, b: float, c: float, precision="bf16",
+            stream=None) -> None:
+    batch, s, _ = _batch3(A)
+    _check("ns_poly", lib().ns_poly(_dev(A, "A"), _dev(B, "B"), s, batch, float(b), float(c),
+                                    precision_code(precision), _stream(stream)))
+
+
+def ns_apply(B: torch.Tensor, X: torch.Tensor, Xout: torch.Tensor, a: float, alpha: float = 1.0,
+             precision="bf16", stream=None) -> None:
+    batch, s, l = _batch3(X)
+    _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), s, l, batch,
+                                      float(a), float(alpha), precision_code(precision),
+                                      _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# a6-a8
+# ---------------------------------------------------------------------------
+
+def packed_words(numel: int) -> int:
+    return (numel + 63) // 64
+
+
+def sign_pack(U: torch.Tensor, bits: torch.Tensor, stream=None) -> None:
+    """Pack the signs of U (flat) into ``bits`` (int64/uint64, ceil(numel/64) words)."""
+    if bits.numel() < packed_words(U.numel()) or bits.element_size() != 8:
+        raise ValueError("bits must hold ceil(numel/64) 64-bit words")
+    _check("sign_pack", lib().sign_pack(_dev(U, "U"), dtype_code(U), U.numel(), _dev(bits, "bits"),
+                                        _stream(stream)))
+
+
+def majority_vote(bits: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Vote over the rows of ``bits`` ([M, nwords] 64-bit words) into ``out`` ([nwords])."""
+    if bits.dim() != 2 or bits.element_size() != 8 or out.numel() < bits.shape[1]:
+        raise ValueError("bits must be [M, nwords] 64-bit words and out hold nwords")
+    _check("majority_vote", lib().majority_vote(_dev(bits, "bits"), bits.shape[0], bits.shape[1],
+                                                _dev(out, "out"), _stream(stream)))
+
+
+def apply_update(W: torch.Tensor, vote_bits: torch.Tensor, eta: float, stream=None) -> None:
+    if vote_bits.numel() < packed_words(W.numel()) or vote_bits.element_size() != 8:
+        raise ValueError("vote_bits must hold ceil(numel/64) 64-bit words")
+    _check("apply_update", lib().apply_update(_dev(W, "W"), dtype_code(W), W.numel(),
+                                              _dev(vote_bits, "vote_bits"), float(eta),
+                                              _stream(stream)))
+
+
+def vote_and_update(W: torch.Tensor, bits: torch.Tensor, eta: float, stream=None) -> None:
+    if bits.dim() != 2 or bits.element_size() != 8 or bits.shape[1] != packed_words(W.numel()):
+        raise ValueError("bits must be [M, ceil(numel/64)] 64-bit words")
+    _check("vote_and_update", lib().vote_and_update(_dev(W, "W"), dtype_code(W), W.numel(),
+                                                    _dev(bits, "bits"), bits.shape[0], float(eta),
+                                                    _stream(stream)))
+
+
+def muon_version() -> int:
+    return int(lib().muon_version())

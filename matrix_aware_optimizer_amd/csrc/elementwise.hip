@@ -1,0 +1,544 @@
+// HBM-bound kernels of the step: momentum EMA with per-matrix sum of squares
+// (a1), sign + 1-bit packing (a6), majority vote (a7) and the update (a8).
+//
+// Every kernel streams its operands once with 16-byte vector accesses
+// (8 bf16 or 4 fp32 per access, consecutive lanes on consecutive addresses)
+// and keeps all arithmetic in registers.  Reductions use a fixed order so
+// identical inputs give bit-identical outputs.
+#include "common.h"
+
+namespace muon {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 8-element vector access (16 B for bf16, 2 x 16 B for fp32).
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  __device__ __forceinline__ static void load(const bf16_t* p, float v[8]) {
+    uint4 r = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(bf16_t* p, const float v[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void load(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float v[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// a1: momentum EMA + per-segment sum of squares.
+// A block owns a chunk of kChunk consecutive entries.  The chunk's part inside
+// segment s is the "piece" (block b, segment s); its partial sum goes to
+// partials[b + s], an index that is unique for every non-empty piece.
+// ---------------------------------------------------------------------------
+constexpr int kThreads = 256;
+constexpr int kIters = 4;
+constexpr int64_t kChunk = int64_t(kThreads) * 8 * kIters;  // 8192 entries
+
+struct SegMap {
+  const int64_t* offs;  // device offsets [nseg+1], or null for uniform segments
+  int64_t uniform;      // segment length when offs is null
+  int nseg;
+  __device__ __forceinline__ int64_t at(int s) const {
+    return offs ? offs[s] : int64_t(s) * uniform;
+  }
+};
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < kThreads / kWave; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+template <typename TM, typename TG, bool UPDATE, bool SUMS>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
+                                                           const TG* __restrict__ G,
+                                                           int64_t numel, SegMap seg,
+                                                           float beta, float alpha,
+                                                           double* __restrict__ partials) {
+  const int64_t c0 = int64_t(blockIdx.x) * kChunk;
+  const int64_t c1 = min(numel, c0 + kChunk);
+  float vals[kIters][8];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+    if (e0 + 8 <= c1) {
+      float m[8];
+      Vec8<TM>::load(M + e0, m);
+      if (UPDATE) {
+        float g[8];
+        Vec8<TG>::load(G + e0, g);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m[q] = fmaf(beta, m[q], alpha * g[q]);
+        Vec8<TM>::store(M + e0, m);
+        // the stored value is what the norm must see
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m[q] = to_f32(from_f32<TM>(m[q]));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) vals[it][q] = m[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float m = 0.0f;
+        if (e0 + q < c1) {
+          m = to_f32(M[e0 + q]);
+          if (UPDATE) {
+            const TM st = from_f32<TM>(fmaf(beta, m, alpha * to_f32(G[e0 + q])));
+            M[e0 + q] = st;
+            m = to_f32(st);
+          }
+        }
+        vals[it][q] = m;
+      }
+    }
+  }
+  if (!SUMS) return;
+
+  __shared__ double red[kThreads / kWave];
+  __shared__ int s_first;
+  if (threadIdx.x == 0) {
+    // largest s with offset(s) <= c0; that segment contains entry c0
+    int lo = 0, hi = seg.nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg.at(mid) <= c0) lo = mid; else hi = mid - 1;
+    }
+    s_first = lo;
+  }
+  __syncthreads();
+  for (int s = s_first; s < seg.nseg; ++s) {
+    const int64_t s0 = seg.at(s), s1 = seg.at(s + 1);
+    if (s0 >= c1) break;
+    const int64_t p0 = max(c0, s0), p1 = min(c1, s1);
+    if (p0 >= p1) continue;
+    double acc = 0.0;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const double v = vals[it][q];
+        if (e0 + q >= p0 && e0 + q < p1) acc = fma(v, v, acc);
+      }
+    }
+    const double tot = block_sum(acc, red);
+    if (threadIdx.x == 0) partials[blockIdx.x + s] = tot;
+  }
+}
+
+// One block per segment adds that segment's piece partials in a fixed order.
+__global__ __launch_bounds__(kThreads) void segment_reduce_kernel(const double* __restrict__ partials,
+                                                                 SegMap seg, int64_t nchunks,
+                                                                 float* __restrict__ out) {
+  __shared__ double red[kThreads / kWave];
+  const int s = blockIdx.x;
+  const int64_t s0 = seg.at(s), s1 = seg.at(s + 1);
+  double acc = 0.0;
+  if (s1 > s0 && s0 >= 0) {
+    // clamped so that offsets beyond numel cannot index past the partials
+    const int64_t b0 = s0 / kChunk, b1 = min((s1 - 1) / kChunk, nchunks - 1);
+    for (int64_t b = b0 + threadIdx.x; b <= b1; b += kThreads) acc += partials[b + s];
+  }
+  const double tot = block_sum(acc, red);
+  if (threadIdx.x == 0) out[s] = static_cast<float>(tot);
+}
+
+template <typename TM, typename TG, bool UPDATE>
+int launch_momentum(TM* M, const TG* G, int64_t numel, SegMap seg, float beta, float alpha,
+                    float* sumsq_out, double* partials, hipStream_t stream) {
+  const int64_t nchunks = (numel + kChunk - 1) / kChunk;
+  if (nchunks == 0 && !(sumsq_out && seg.nseg > 0)) return MUON_OK;  // nothing to launch
+  if (nchunks > 0) {
+    if (sumsq_out)
+      momentum_kernel<TM, TG, UPDATE, true><<<dim3(nchunks), dim3(kThreads), 0, stream>>>(
+          M, G, numel, seg, beta, alpha, partials);
+    else
+      momentum_kernel<TM, TG, UPDATE, false><<<dim3(nchunks), dim3(kThreads), 0, stream>>>(
+          M, G, numel, seg, beta, alpha, partials);
+  }
+  if (sumsq_out && seg.nseg > 0)
+    segment_reduce_kernel<<<dim3(seg.nseg), dim3(kThreads), 0, stream>>>(partials, seg, nchunks,
+                                                                          sumsq_out);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// a6: sign + pack.  Each lane turns 8 consecutive entries into one byte of
+// bits; eight neighbouring lanes merge their bytes into one 64-bit word with
+// three shuffles, and every eighth lane stores it.  The test "u < 0" is done
+// on the encoding (sign bit set, magnitude non-zero, not NaN), so it is exact
+// for subnormals whatever the float mode.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nonneg_bit(bf16_t h) {
+  return !(h > 0x8000u && h <= 0xff80u);
+}
+__device__ __forceinline__ uint32_t nonneg_bit(uint32_t u) {
+  return !(u > 0x80000000u && u <= 0xff800000u);
+}
+
+template <typename T> struct SignByte;
+template <> struct SignByte<bf16_t> {
+  __device__ __forceinline__ static uint32_t full(const bf16_t* p) {
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t byte = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      byte |= nonneg_bit(static_cast<bf16_t>(w[i] & 0xffffu)) << (2 * i);
+      byte |= nonneg_bit(static_cast<bf16_t>(w[i] >> 16)) << (2 * i + 1);
+    }
+    return byte;
+  }
+  __device__ __forceinline__ static uint32_t one(const bf16_t* p) { return nonneg_bit(*p); }
+};
+template <> struct SignByte<float> {
+  __device__ __forceinline__ static uint32_t full(const float* p) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t byte = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) byte |= nonneg_bit(w[i]) << i;
+    return byte;
+  }
+  __device__ __forceinline__ static uint32_t one(const float* p) {
+    return nonneg_bit(*reinterpret_cast<const uint32_t*>(p));
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sign_pack_kernel(const T* __restrict__ U, int64_t numel,
+                                                            uint64_t* __restrict__ bits,
+                                                            int64_t nwords) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = t * 8;
+  uint32_t byte = 0;
+  if (e0 + 8 <= numel) {
+    byte = SignByte<T>::full(U + e0);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (e0 + q < numel) byte |= SignByte<T>::one(U + e0 + q) << q;
+  }
+  uint32_t v = byte;
+  v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 1, kWave)) << 8;
+  v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 2, kWave)) << 16;
+  const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 4, kWave));
+  if ((threadIdx.x & 7) == 0) {
+    const int64_t w = e0 >> 6;
+    if (w < nwords) bits[w] = static_cast<uint64_t>(v) | (static_cast<uint64_t>(hi) << 32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a7: majority vote.  A bit-sliced counter (NB planes of 64 bits) adds the M
+// buffers' words; the result is compared with ceil(M/2) plane by plane.
+// ---------------------------------------------------------------------------
+template <int NB, typename W>
+__device__ __forceinline__ void counter_add(W (&cnt)[NB], W x) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const W carry = cnt[i] & x;
+    cnt[i] ^= x;
+    x = carry;
+  }
+}
+
+// bit set where the per-bit count is >= thr (thr < 2^NB)
+template <int NB, typename W>
+__device__ __forceinline__ W counter_ge(const W (&cnt)[NB], int thr) {
+  W gt = 0, eq = ~W(0);
+#pragma unroll
+  for (int i = NB - 1; i >= 0; --i) {
+    if ((thr >> i) & 1) {
+      eq &= cnt[i];
+    } else {
+      gt |= eq & cnt[i];
+      eq &= ~cnt[i];
+    }
+  }
+  return gt | eq;
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads) void vote_kernel(const uint64_t* __restrict__ bits, int M,
+                                                       int64_t nwords, uint64_t* __restrict__ out) {
+  const int64_t w = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (w >= nwords) return;
+  uint64_t cnt[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) cnt[i] = 0;
+  for (int k = 0; k < M; ++k) counter_add<NB>(cnt, bits[int64_t(k) * nwords + w]);
+  out[w] = counter_ge<NB>(cnt, (M + 1) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// a8: update, and the fused vote + update.  A lane updates 8 consecutive
+// weights with one byte of vote bits.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void update8(T* __restrict__ W, int64_t e0, int64_t numel, uint32_t byte,
+                                        float eta) {
+  if (e0 + 8 <= numel) {
+    float v[8];
+    Vec8<T>::load(W + e0, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = ((byte >> q) & 1u) ? v[q] - eta : v[q] + eta;
+    Vec8<T>::store(W + e0, v);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (e0 + q < numel) {
+        const float x = to_f32(W[e0 + q]);
+        W[e0 + q] = from_f32<T>(((byte >> q) & 1u) ? x - eta : x + eta);
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void update_kernel(T* __restrict__ W, int64_t numel,
+                                                         const uint8_t* __restrict__ vote,
+                                                         float eta) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = t * 8;
+  if (e0 >= numel) return;
+  update8<T>(W, e0, numel, vote[t], eta);
+}
+
+template <typename T, int NB>
+__global__ __launch_bounds__(kThreads) void vote_update_kernel(T* __restrict__ W, int64_t numel,
+                                                              const uint8_t* __restrict__ bits,
+                                                              int M, int64_t nbytes, float eta) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = t * 8;
+  if (e0 >= numel) return;
+  uint32_t cnt[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) cnt[i] = 0;
+  for (int k = 0; k < M; ++k) counter_add<NB>(cnt, static_cast<uint32_t>(bits[int64_t(k) * nbytes + t]));
+  update8<T>(W, e0, numel, counter_ge<NB>(cnt, (M + 1) >> 1) & 0xffu, eta);
+}
+
+int planes_for(int M) {
+  int nb = 1;
+  while ((1 << nb) <= M) ++nb;
+  return nb;
+}
+
+template <template <int> class F, typename... Args>
+int dispatch_planes(int nb, Args... args) {
+  switch (nb) {
+    case 1: return F<1>::run(args...);
+    case 2: return F<2>::run(args...);
+    case 3: return F<3>::run(args...);
+    case 4: return F<4>::run(args...);
+    case 5: return F<5>::run(args...);
+    case 6: return F<6>::run(args...);
+    case 7: return F<7>::run(args...);
+    case 8: return F<8>::run(args...);
+    case 9: return F<9>::run(args...);
+    case 10: return F<10>::run(args...);
+    default: return MUON_EINVAL;
+  }
+}
+
+template <int NB> struct VoteLaunch {
+  static int run(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, hipStream_t st) {
+    const int64_t blocks = (nwords + kThreads - 1) / kThreads;
+    vote_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(bits, M, nwords, out);
+    return launch_status();
+  }
+};
+
+template <int NB> struct VoteUpdateLaunch {
+  static int run(void* W, int w_dtype, int64_t numel, const uint64_t* bits, int M, int64_t nwords,
+                 float eta, hipStream_t st) {
+    const int64_t blocks = ((numel + 7) / 8 + kThreads - 1) / kThreads;
+    const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
+    if (w_dtype == MUON_BF16)
+      vote_update_kernel<bf16_t, NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+          static_cast<bf16_t*>(W), numel, b8, M, nwords * 8, eta);
+    else
+      vote_update_kernel<float, NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+          static_cast<float*>(W), numel, b8, M, nwords * 8, eta);
+    return launch_status();
+  }
+};
+
+}  // namespace
+
+// Sum of squares of `count` equal matrices of `len` entries spaced `stride`
+// entries apart (the normalisation's norm when the caller supplies none).
+// partials needs muon_momentum_workspace_bytes(len * count, count) bytes when
+// stride == len, else muon_momentum_workspace_bytes(len, 1) bytes.
+int sumsq_strided(const void* M, int m_dtype, int64_t len, int64_t count, int64_t stride,
+                  float* out, void* partials, hipStream_t stream) {
+  double* part = static_cast<double*>(partials);
+  if (stride == len) {
+    SegMap seg{nullptr, len, static_cast<int>(count)};
+    if (m_dtype == MUON_BF16)
+      return launch_momentum<bf16_t, bf16_t, false>(static_cast<bf16_t*>(const_cast<void*>(M)),
+                                                     nullptr, len * count, seg, 1.f, 0.f, out,
+                                                     part, stream);
+    return launch_momentum<float, float, false>(static_cast<float*>(const_cast<void*>(M)), nullptr,
+                                                len * count, seg, 1.f, 0.f, out, part, stream);
+  }
+  for (int64_t i = 0; i < count; ++i) {
+    SegMap seg{nullptr, len, 1};
+    const size_t es = dtype_size(m_dtype);
+    void* Mi = static_cast<char*>(const_cast<void*>(M)) + i * stride * es;
+    int st;
+    if (m_dtype == MUON_BF16)
+      st = launch_momentum<bf16_t, bf16_t, false>(static_cast<bf16_t*>(Mi), nullptr, len, seg,
+                                                  1.f, 0.f, out + i, part, stream);
+    else
+      st = launch_momentum<float, float, false>(static_cast<float*>(Mi), nullptr, len, seg, 1.f,
+                                                0.f, out + i, part, stream);
+    if (st != MUON_OK) return st;
+  }
+  return MUON_OK;
+}
+
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+size_t muon_momentum_workspace_bytes(int64_t numel, int nseg) {
+  if (numel < 0 || nseg < 0) return 0;
+  const int64_t nchunks = (numel + kChunk - 1) / kChunk;
+  return round_up(static_cast<size_t>(nchunks + nseg + 1) * sizeof(double), 256);
+}
+
+int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
+                  const int64_t* seg_offsets, int nseg, float beta, float alpha, float* sumsq_out,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(m_dtype) || !valid_dtype(g_dtype)) return MUON_EDTYPE;
+  if (numel > 0 && (!M || !G)) return MUON_EINVAL;
+  if (numel > 0 && (!aligned16(M) || !aligned16(G))) return MUON_EALIGN;
+  if (sumsq_out) {
+    if (nseg < 1 || !seg_offsets) return MUON_EINVAL;
+    if (!aligned16(seg_offsets)) return MUON_EALIGN;
+    if (!workspace || ws_bytes < muon_momentum_workspace_bytes(numel, nseg)) return MUON_EWORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SegMap seg{seg_offsets, 0, sumsq_out ? nseg : 0};
+  double* part = static_cast<double*>(workspace);
+  if (m_dtype == MUON_BF16 && g_dtype == MUON_BF16)
+    return launch_momentum<bf16_t, bf16_t, true>(static_cast<bf16_t*>(M), static_cast<const bf16_t*>(G),
+                                                 numel, seg, beta, alpha, sumsq_out, part, st);
+  if (m_dtype == MUON_BF16 && g_dtype == MUON_F32)
+    return launch_momentum<bf16_t, float, true>(static_cast<bf16_t*>(M), static_cast<const float*>(G),
+                                                numel, seg, beta, alpha, sumsq_out, part, st);
+  if (m_dtype == MUON_F32 && g_dtype == MUON_BF16)
+    return launch_momentum<float, bf16_t, true>(static_cast<float*>(M), static_cast<const bf16_t*>(G),
+                                                numel, seg, beta, alpha, sumsq_out, part, st);
+  return launch_momentum<float, float, true>(static_cast<float*>(M), static_cast<const float*>(G),
+                                             numel, seg, beta, alpha, sumsq_out, part, st);
+}
+
+int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(u_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!U || !bits) return MUON_EINVAL;
+  if (!aligned16(U) || !aligned16(bits)) return MUON_EALIGN;
+  const int64_t nwords = (numel + 63) / 64;
+  const int64_t threads = nwords * 8;
+  const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (u_dtype == MUON_BF16)
+    sign_pack_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const bf16_t*>(U),
+                                                                      numel, bits, nwords);
+  else
+    sign_pack_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const float*>(U),
+                                                                     numel, bits, nwords);
+  return launch_status();
+}
+
+int majority_vote(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, void* stream) {
+  if (nwords < 0 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
+  if (nwords == 0) return MUON_OK;
+  if (!bits || !out) return MUON_EINVAL;
+  if (!aligned16(bits) || !aligned16(out)) return MUON_EALIGN;
+  return dispatch_planes<VoteLaunch>(planes_for(M), bits, M, nwords, out,
+                                     static_cast<hipStream_t>(stream));
+}
+
+int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits, float eta,
+                 void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(w_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!W || !vote_bits) return MUON_EINVAL;
+  if (!aligned16(W) || !aligned16(vote_bits)) return MUON_EALIGN;
+  const int64_t blocks = ((numel + 7) / 8 + kThreads - 1) / kThreads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vote_bits);
+  if (w_dtype == MUON_BF16)
+    update_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<bf16_t*>(W), numel,
+                                                                   v8, eta);
+  else
+    update_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<float*>(W), numel, v8,
+                                                                  eta);
+  return launch_status();
+}
+
+int vote_and_update(void* W, int w_dtype, int64_t numel, const uint64_t* bits, int M, float eta,
+                    void* stream) {
+  if (numel < 0 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
+  if (!valid_dtype(w_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!W || !bits) return MUON_EINVAL;
+  if (!aligned16(W) || !aligned16(bits)) return MUON_EALIGN;
+  const int64_t nwords = (numel + 63) / 64;
+  return dispatch_planes<VoteUpdateLaunch>(planes_for(M), W, w_dtype, numel, bits, M, nwords, eta,
+                                           static_cast<hipStream_t>(stream));
+}
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_EINVAL: return "invalid argument (null pointer or bad size)";
+    case MUON_EDTYPE: return "unsupported dtype or precision";
+    case MUON_EALIGN: return "device pointer not 16-byte aligned";
+    case MUON_EWORKSPACE: return "workspace missing or too small";
+    case MUON_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int muon_version(void) { return 100; }
+
+}  // extern "C"

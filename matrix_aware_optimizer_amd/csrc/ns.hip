@@ -1,0 +1,700 @@
+// Newton-Schulz orthogonalisation (a2-a5) on CDNA4 matrix cores.
+//
+// One iteration is three products ("NVIDIA Megatron..." article, paragraph
+// 「分散モード」): A = X X^T, B = b A + c A A, X' = a X + B X.  The first two
+// are symmetric rank-k products (paragraph 「SYRK と融合された all-reduce」):
+// only tiles on or below the diagonal are computed, and each off-diagonal
+// tile is also stored mirrored, so A and B are full symmetric matrices.
+//
+// Working layout: X is [batch][s][l] with s <= l (a tall momentum is
+// transposed once by the normalisation kernel), A and B are [batch][s][s];
+// s and l are padded to multiples of MUON_NS_PAD with zeros, and zeros stay
+// zeros through every product, so the GEMM kernels never test bounds.
+//
+// GEMM kernel: C = alpha * P Q^T (+ beta * Z) where P's rows and Q's rows
+// are contiguous along k ("NT"), or Q is given k-major ("NN", the B X
+// product).  Tiles are staged in LDS as 128-byte rows (64 bf16 / 32 fp32
+// along k) with an XOR swizzle of the 16-byte chunks so that both the tile
+// stores and the MFMA fragment reads are free of bank conflicts; the NN
+// loader transposes 8x8 (bf16) or 4x4 (fp32) blocks in registers so that its
+// LDS tile has the same k-contiguous layout.  bf16 uses
+// v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2f32; both accumulate
+// in fp32.
+#include <math.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+namespace muon {
+
+int sumsq_strided(const void* M, int m_dtype, int64_t len, int64_t count, int64_t stride, float* out,
+                  void* partials, hipStream_t stream);
+
+namespace {
+
+constexpr int kRowBytes = 128;  // one LDS tile row = 128 bytes along k
+
+// ---------------------------------------------------------------------------
+// Matrix-core step for one 16-byte fragment per lane and operand.
+// Lane l supplies row/column (l % 32); lanes 0-31 and 32-63 hold two
+// disjoint k-groups.  A and B use the same k placement, so every k of the
+// chunk is contracted exactly once.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  static constexpr int kElems = 8;   // elements per 16 bytes
+  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  }
+};
+
+// byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
+
+struct GemmArgs {
+  const void* P;  // rows of the left operand, k-contiguous, ld = K
+  const void* Q;  // NT: rows of the right operand (k-contiguous, ld = K); NN: [K][N]
+  const void* Z;  // epilogue addend [M][N] (ld = N), may be null
+  void* C;        // output [M][N] (ld = N)
+  int64_t M, N, K;
+  int64_t strideP, strideQ, strideZ, strideC;  // batch strides (elements)
+  float alpha, beta;                           // C = alpha*acc + beta*Z
+  // EPI_FINAL: write U instead of C, un-padded (s_valid x l_valid of the
+  // working layout) and transposed back when the momentum was tall.
+  void* U;
+  int64_t strideU;
+  int64_t s_valid, l_valid;
+  int u_dtype;
+  int transpose_out;
+};
+
+template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
+struct Gemm {
+  static constexpr int E = Mfma<T>::kElems;
+  static constexpr int BK = kRowBytes / sizeof(T);   // k per LDS tile
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NT = WAVES_M * WAVES_N * kWave;
+  static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 fragments per wave
+  static constexpr int KSTEPS = BK / (2 * E);        // fragment reads per LDS tile
+  // k-contiguous loads: 8 chunks per row
+  static constexpr int A_CHUNKS = BM * 8 / NT;
+  static constexpr int B_CHUNKS = BN * 8 / NT;
+  // NN loads: E x E blocks, (BK/E) x (BN/E) of them
+  static constexpr int NN_BLOCKS = (BK / E) * (BN / E);
+  static constexpr int NN_PER_T = (NN_BLOCKS + NT - 1) / NT;
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
+  static_assert(!SYRK || BM == BN, "symmetric products need square tiles");
+  static constexpr int LDS_BYTES = (BM + BN) * kRowBytes;
+};
+
+template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs g) {
+  using Cfg = Gemm<T, BM, BN, WM, WN, SYRK, NN, EPI>;
+  constexpr int E = Cfg::E, BK = Cfg::BK, NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  char* ldsA = lds;
+  char* ldsB = lds + BM * kRowBytes;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t batch = blockIdx.y;
+
+  // ---- tile coordinates ----
+  int64_t tm, tn;
+  if (SYRK) {
+    // lower triangle: block t -> (ti, tj), ti >= tj
+    const int64_t t = blockIdx.x;
+    int64_t ti = static_cast<int64_t>((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tm = ti;
+    tn = t - ti * (ti + 1) / 2;
+  } else {
+    const int64_t tiles_m = g.M / BM;
+    tm = blockIdx.x % tiles_m;
+    tn = blockIdx.x / tiles_m;
+  }
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const T* P = static_cast<const T*>(g.P) + batch * g.strideP;
+  const T* Q = static_cast<const T*>(g.Q) + batch * g.strideQ;
+
+  // ---- global -> register staging ----
+  u32x4_t ra[Cfg::A_CHUNKS];
+  u32x4_t rb[NN ? Cfg::NN_PER_T * E : Cfg::B_CHUNKS];
+
+  auto load_tiles = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
+      const int c = tid + i * NT;
+      const int row = c >> 3, kc = c & 7;
+      ra[i] = *reinterpret_cast<const u32x4_t*>(P + (m0 + row) * g.K + k0 + kc * E);
+    }
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < Cfg::B_CHUNKS; ++i) {
+        const int c = tid + i * NT;
+        const int row = c >> 3, kc = c & 7;
+        rb[i] = *reinterpret_cast<const u32x4_t*>(Q + (n0 + row) * g.K + k0 + kc * E);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::NN_PER_T; ++i) {
+        const int blk = tid + i * NT;
+        if (blk < Cfg::NN_BLOCKS) {
+          const int nb = blk % (BN / E), kb = blk / (BN / E);
+#pragma unroll
+          for (int r = 0; r < E; ++r)
+            rb[i * E + r] = *reinterpret_cast<const u32x4_t*>(Q + (k0 + kb * E + r) * g.N + n0 + nb * E);
+        }
+      }
+    }
+  };
+
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(ldsA + lds_off(c >> 3, c & 7)) = ra[i];
+    }
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < Cfg::B_CHUNKS; ++i) {
+        const int c = tid + i * NT;
+        *reinterpret_cast<u32x4_t*>(ldsB + lds_off(c >> 3, c & 7)) = rb[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::NN_PER_T; ++i) {
+        const int blk = tid + i * NT;
+        if (blk < Cfg::NN_BLOCKS) {
+          const int nb = blk % (BN / E), kb = blk / (BN / E);
+          const u32x4_t* in = rb + i * E;
+          if (sizeof(T) == 2) {
+            // in[r] holds k = kb*8 + r for n = nb*8 + 0..7 (two per dword);
+            // column e of the 8x8 block becomes the 8 k-values of row n.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int d = e >> 1;
+              u32x4_t o;
+              uint32_t w[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = in[2 * j][d], hi = in[2 * j + 1][d];
+                w[j] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                               : ((lo & 0xffffu) | (hi << 16));
+              }
+              o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+              *reinterpret_cast<u32x4_t*>(ldsB + lds_off(nb * 8 + e, kb)) = o;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              u32x4_t o;
+              o.x = in[0][e]; o.y = in[1][e]; o.z = in[2][e]; o.w = in[3][e];
+              *reinterpret_cast<u32x4_t*>(ldsB + lds_off(nb * 4 + e, kb)) = o;
+            }
+          }
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int wm0 = (wave / Cfg::WAVES_N) * WM;
+  const int wn0 = (wave % Cfg::WAVES_N) * WN;
+  const int frow = lane & 31, fgrp = lane >> 5;
+
+  const int64_t KT = g.K / BK;
+  load_tiles(0);
+  store_tiles();
+  __syncthreads();
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) load_tiles((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
+      const int chunk = ks * 2 + fgrp;
+      u32x4_t fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4_t*>(ldsA + lds_off(wm0 + i * 32 + frow, chunk));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(ldsB + lds_off(wn0 + j * 32 + frow, chunk));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
+    }
+    __syncthreads();
+    if (kt + 1 < KT) {
+      store_tiles();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) +
+  // (v%4), column l%32 of the fragment.
+  T* C = static_cast<T*>(g.C) + batch * g.strideC;
+  const T* Z = static_cast<const T*>(g.Z) + batch * g.strideZ;
+  const bool mirror = SYRK && (tm != tn);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn0 + j * 32 + frow;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row0 = m0 + wm0 + i * 32 + 8 * q + 4 * fgrp;
+        float out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[i][j][4 * q + r] * g.alpha;
+          if (EPI != EPI_STORE) v = fmaf(g.beta, to_f32(Z[(row0 + r) * g.N + col]), v);
+          out[r] = v;
+        }
+        if (EPI == EPI_FINAL) {
+          if (col < g.l_valid) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t row = row0 + r;
+              if (row < g.s_valid) {
+                const int64_t idx = g.transpose_out ? col * g.s_valid + row : row * g.l_valid + col;
+                if (g.u_dtype == MUON_BF16)
+                  static_cast<bf16_t*>(g.U)[batch * g.strideU + idx] = f32_to_bf16(out[r]);
+                else
+                  static_cast<float*>(g.U)[batch * g.strideU + idx] = out[r];
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = from_f32<T>(out[r]);
+          if (mirror) {
+            // the four consecutive rows are four consecutive entries of row `col`
+            T* dst = C + col * g.N + row0;
+            if (sizeof(T) == 2) {
+              const uint32_t w0 = uint32_t(from_f32<bf16_t>(out[0])) | (uint32_t(from_f32<bf16_t>(out[1])) << 16);
+              const uint32_t w1 = uint32_t(from_f32<bf16_t>(out[2])) | (uint32_t(from_f32<bf16_t>(out[3])) << 16);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a2: X0 = pad(orient(M)) * scale, scale = 1/sqrt(sumsq) (0 for a zero matrix).
+// One thread writes 8 consecutive entries of a working row.
+// ---------------------------------------------------------------------------
+template <typename TM, typename TX>
+__global__ __launch_bounds__(256) void normalize_kernel(const TM* __restrict__ M, int64_t strideM,
+                                                       int64_t rows, int64_t cols,
+                                                       const float* __restrict__ sumsq,
+                                                       int64_t stride_sumsq, TX* __restrict__ X,
+                                                       int64_t sp, int64_t lp) {
+  const int64_t b = blockIdx.y;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = lp / 8;
+  if (t >= sp * per_row) return;
+  const int64_t i = t / per_row, j0 = (t % per_row) * 8;
+  const bool tall = rows > cols;
+  const int64_t s = tall ? cols : rows, l = tall ? rows : cols;
+  const double ss = static_cast<double>(sumsq[b * stride_sumsq]);
+  const float scale = ss == 0.0 ? 0.0f : static_cast<float>(1.0 / sqrt(ss));
+  const TM* Mb = M + b * strideM;
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t j = j0 + q;
+    float x = 0.0f;
+    if (i < s && j < l) x = to_f32(tall ? Mb[j * cols + i] : Mb[i * cols + j]) * scale;
+    v[q] = x;
+  }
+  TX* dst = X + b * sp * lp + i * lp + j0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dst[q] = from_f32<TX>(v[q]);
+}
+
+// steps == 0: U = X0 (un-padded, original orientation)
+template <typename TX, typename TU>
+__global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int64_t sp, int64_t lp,
+                                                  int64_t rows, int64_t cols, TU* __restrict__ U,
+                                                  int64_t strideU) {
+  const int64_t b = blockIdx.y;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= rows * cols) return;
+  const int64_t r = t / cols, c = t % cols;
+  const bool tall = rows > cols;
+  const int64_t i = tall ? c : r, j = tall ? r : c;
+  U[b * strideU + t] = from_f32<TU>(to_f32(X[b * sp * lp + i * lp + j]));
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers
+// ---------------------------------------------------------------------------
+constexpr int kBM = 128, kBN = 128, kWM = 64, kWN = 64;
+
+template <typename T, bool SYRK, bool NN, int EPI>
+int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  using Cfg = Gemm<T, kBM, kBN, kWM, kWN, SYRK, NN, EPI>;
+  int64_t blocks;
+  if (SYRK) {
+    const int64_t t = g.M / kBM;
+    blocks = t * (t + 1) / 2;
+  } else {
+    blocks = (g.M / kBM) * (g.N / kBN);
+  }
+  if (blocks == 0 || batch == 0) return MUON_OK;
+  gemm_kernel<T, kBM, kBN, kWM, kWN, SYRK, NN, EPI>
+      <<<dim3(blocks, batch), dim3(Cfg::NT), 0, st>>>(g);
+  return launch_status();
+}
+
+template <typename T>
+int gram_t(const void* X, void* A, int64_t s, int64_t l, int64_t batch, hipStream_t st) {
+  GemmArgs g{};
+  g.P = X; g.Q = X; g.Z = nullptr; g.C = A;
+  g.M = s; g.N = s; g.K = l;
+  g.strideP = g.strideQ = s * l; g.strideC = s * s;
+  g.alpha = 1.0f; g.beta = 0.0f;
+  return launch_gemm<T, true, false, EPI_STORE>(g, batch, st);
+}
+
+template <typename T>
+int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, hipStream_t st) {
+  GemmArgs g{};
+  g.P = A; g.Q = A; g.Z = A; g.C = B;
+  g.M = s; g.N = s; g.K = s;
+  g.strideP = g.strideQ = g.strideZ = g.strideC = s * s;
+  g.alpha = c; g.beta = b;
+  return launch_gemm<T, true, false, EPI_AXPBY>(g, batch, st);
+}
+
+template <typename T>
+int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
+            float alpha, hipStream_t st, const GemmArgs* final_out) {
+  GemmArgs g{};
+  if (final_out) g = *final_out;
+  g.P = B; g.Q = X; g.Z = X; g.C = Xout;
+  g.M = s; g.N = l; g.K = s;
+  g.strideP = s * s; g.strideQ = g.strideZ = g.strideC = s * l;
+  g.alpha = alpha; g.beta = a;
+  if (final_out) return launch_gemm<T, false, true, EPI_FINAL>(g, batch, st);
+  return launch_gemm<T, false, true, EPI_AXPBY>(g, batch, st);
+}
+
+template <typename TM, typename TX>
+int normalize_t(const void* M, int64_t strideM, int64_t rows, int64_t cols, const float* sumsq,
+                int64_t stride_sumsq, void* X, int64_t sp, int64_t lp, int64_t batch, hipStream_t st) {
+  const int64_t threads = sp * (lp / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks == 0 || batch == 0) return MUON_OK;
+  normalize_kernel<TM, TX><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+      static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
+  return launch_status();
+}
+
+int normalize_dispatch(const void* M, int m_dtype, int64_t strideM, int64_t rows, int64_t cols,
+                       const float* sumsq, int64_t stride_sumsq, void* X, int precision, int64_t sp,
+                       int64_t lp, int64_t batch, hipStream_t st) {
+  if (precision == MUON_BF16) {
+    if (m_dtype == MUON_BF16)
+      return normalize_t<bf16_t, bf16_t>(M, strideM, rows, cols, sumsq, stride_sumsq, X, sp, lp, batch, st);
+    return normalize_t<float, bf16_t>(M, strideM, rows, cols, sumsq, stride_sumsq, X, sp, lp, batch, st);
+  }
+  if (m_dtype == MUON_BF16)
+    return normalize_t<bf16_t, float>(M, strideM, rows, cols, sumsq, stride_sumsq, X, sp, lp, batch, st);
+  return normalize_t<float, float>(M, strideM, rows, cols, sumsq, stride_sumsq, X, sp, lp, batch, st);
+}
+
+template <typename TX>
+int emit_t(const void* X, int64_t sp, int64_t lp, int64_t rows, int64_t cols, void* U, int u_dtype,
+           int64_t strideU, int64_t batch, hipStream_t st) {
+  const int64_t blocks = (rows * cols + 255) / 256;
+  if (blocks == 0 || batch == 0) return MUON_OK;
+  if (u_dtype == MUON_BF16)
+    emit_kernel<TX, bf16_t><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+        static_cast<const TX*>(X), sp, lp, rows, cols, static_cast<bf16_t*>(U), strideU);
+  else
+    emit_kernel<TX, float><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+        static_cast<const TX*>(X), sp, lp, rows, cols, static_cast<float*>(U), strideU);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Problem grouping: problems of equal shape and dtypes (in any order) are
+// sorted by the address of M; runs of them whose M, U and sumsq pointers
+// advance by a constant stride become one batched run.
+// ---------------------------------------------------------------------------
+struct Run {
+  int count;
+  const void* M;
+  void* U;
+  const float* sumsq;
+  int64_t rows, cols, sp, lp;
+  int m_dtype, u_dtype;
+  bool has_sumsq;
+  int64_t strideM, strideU, stride_sumsq;  // elements
+};
+
+int64_t pad_to(int64_t x) { return (x + MUON_NS_PAD - 1) / MUON_NS_PAD * MUON_NS_PAD; }
+
+bool same_kind(const muon_ns_problem& a, const muon_ns_problem& b) {
+  return a.rows == b.rows && a.cols == b.cols && a.m_dtype == b.m_dtype && a.u_dtype == b.u_dtype &&
+         (a.sumsq != nullptr) == (b.sumsq != nullptr);
+}
+
+bool kind_less(const muon_ns_problem& a, const muon_ns_problem& b) {
+  if (a.rows != b.rows) return a.rows < b.rows;
+  if (a.cols != b.cols) return a.cols < b.cols;
+  if (a.m_dtype != b.m_dtype) return a.m_dtype < b.m_dtype;
+  if (a.u_dtype != b.u_dtype) return a.u_dtype < b.u_dtype;
+  if ((a.sumsq != nullptr) != (b.sumsq != nullptr)) return a.sumsq == nullptr;
+  return reinterpret_cast<uintptr_t>(a.M) < reinterpret_cast<uintptr_t>(b.M);
+}
+
+int64_t diff_elems(const void* a, const void* b, size_t es) {
+  const int64_t d = reinterpret_cast<const char*>(b) - reinterpret_cast<const char*>(a);
+  if (d <= 0 || d % static_cast<int64_t>(es) != 0) return -1;
+  return d / static_cast<int64_t>(es);
+}
+
+std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
+  std::vector<muon_ns_problem> p(probs, probs + count);
+  std::stable_sort(p.begin(), p.end(), kind_less);
+  std::vector<Run> runs;
+  int i = 0;
+  while (i < count) {
+    Run r{};
+    r.count = 1;
+    r.M = p[i].M; r.U = p[i].U; r.sumsq = p[i].sumsq;
+    r.rows = p[i].rows; r.cols = p[i].cols;
+    r.sp = pad_to(std::min(r.rows, r.cols));
+    r.lp = pad_to(std::max(r.rows, r.cols));
+    r.m_dtype = p[i].m_dtype; r.u_dtype = p[i].u_dtype;
+    r.has_sumsq = p[i].sumsq != nullptr;
+    r.strideM = r.strideU = r.rows * r.cols;
+    r.stride_sumsq = 1;
+    if (i + 1 < count && same_kind(p[i], p[i + 1])) {
+      const int64_t sm = diff_elems(p[i].M, p[i + 1].M, dtype_size(r.m_dtype));
+      const int64_t su = diff_elems(p[i].U, p[i + 1].U, dtype_size(r.u_dtype));
+      const int64_t ss = r.has_sumsq ? diff_elems(p[i].sumsq, p[i + 1].sumsq, sizeof(float)) : 1;
+      if (sm > 0 && su > 0 && ss > 0) {
+        int j = i + 1;
+        while (j < count && same_kind(p[j - 1], p[j]) &&
+               diff_elems(p[j - 1].M, p[j].M, dtype_size(r.m_dtype)) == sm &&
+               diff_elems(p[j - 1].U, p[j].U, dtype_size(r.u_dtype)) == su &&
+               (!r.has_sumsq || diff_elems(p[j - 1].sumsq, p[j].sumsq, sizeof(float)) == ss))
+          ++j;
+        r.count = j - i;
+        r.strideM = sm; r.strideU = su; r.stride_sumsq = ss;
+      }
+    }
+    runs.push_back(r);
+    i += r.count;
+  }
+  return runs;
+}
+
+struct RunLayout {
+  size_t x0, x1, a, b, sumsq, partials, total;
+};
+
+RunLayout layout_of(const Run& r, int precision) {
+  const size_t es = precision == MUON_BF16 ? 2 : 4;
+  const size_t n = static_cast<size_t>(r.count);
+  RunLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
+  L.x0 = take(n * r.sp * r.lp * es);
+  L.x1 = take(n * r.sp * r.lp * es);
+  L.a = take(n * r.sp * r.sp * es);
+  L.b = take(n * r.sp * r.sp * es);
+  L.sumsq = take(r.has_sumsq ? 0 : n * sizeof(float));
+  size_t part = 0;
+  if (!r.has_sumsq) {
+    const int64_t len = r.rows * r.cols;
+    part = r.strideM == len ? muon_momentum_workspace_bytes(len * r.count, r.count)
+                            : muon_momentum_workspace_bytes(len, 1);
+  }
+  L.partials = take(part);
+  L.total = off;
+  return L;
+}
+
+bool valid_problem(const muon_ns_problem& p) {
+  return p.rows > 0 && p.cols > 0 && p.M && p.U;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+size_t ns_workspace_bytes(const muon_ns_problem* probs, int count, int precision) {
+  if (!probs || count <= 0 || (precision != MUON_F32 && precision != MUON_BF16)) return 0;
+  for (int i = 0; i < count; ++i)
+    if (!valid_problem(probs[i])) return 0;
+  size_t need = 0;
+  for (const Run& r : make_runs(probs, count)) need = std::max(need, layout_of(r, precision).total);
+  return need;
+}
+
+int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, float c, int steps,
+                     int precision, void* workspace, size_t ws_bytes, void* stream) {
+  if (count < 0 || steps < 0) return MUON_EINVAL;
+  if (count == 0) return MUON_OK;
+  if (!probs) return MUON_EINVAL;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  for (int i = 0; i < count; ++i) {
+    const muon_ns_problem& p = probs[i];
+    if (!valid_problem(p)) return MUON_EINVAL;
+    if (!valid_dtype(p.m_dtype) || !valid_dtype(p.u_dtype)) return MUON_EDTYPE;
+    if (!aligned16(p.M) || !aligned16(p.U)) return MUON_EALIGN;
+  }
+  const std::vector<Run> runs = make_runs(probs, count);
+  size_t need = 0;
+  for (const Run& r : runs) need = std::max(need, layout_of(r, precision).total);
+  if (!workspace || ws_bytes < need) return MUON_EWORKSPACE;
+  if (!aligned16(workspace)) return MUON_EALIGN;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  for (const Run& r : runs) {
+    const RunLayout L = layout_of(r, precision);
+    const float* sumsq = r.sumsq;
+    int64_t stride_sumsq = r.stride_sumsq;
+    int status;
+    if (!r.has_sumsq) {
+      float* out = reinterpret_cast<float*>(ws + L.sumsq);
+      status = sumsq_strided(r.M, r.m_dtype, r.rows * r.cols, r.count, r.strideM, out,
+                             ws + L.partials, st);
+      if (status != MUON_OK) return status;
+      sumsq = out;
+      stride_sumsq = 1;
+    }
+    void* X[2] = {ws + L.x0, ws + L.x1};
+    void* A = ws + L.a;
+    void* B = ws + L.b;
+    status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
+                                precision, r.sp, r.lp, r.count, st);
+    if (status != MUON_OK) return status;
+    if (steps == 0) {
+      status = precision == MUON_BF16
+                   ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
+                   : emit_t<float>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st);
+      if (status != MUON_OK) return status;
+      continue;
+    }
+    GemmArgs fin{};
+    fin.U = r.U;
+    fin.strideU = r.strideU;
+    fin.s_valid = std::min(r.rows, r.cols);
+    fin.l_valid = std::max(r.rows, r.cols);
+    fin.u_dtype = r.u_dtype;
+    fin.transpose_out = r.rows > r.cols;
+    for (int it = 0; it < steps; ++it) {
+      const void* Xc = X[it & 1];
+      void* Xn = X[(it + 1) & 1];
+      const bool last = it + 1 == steps;
+      if (precision == MUON_BF16) {
+        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st);
+        if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st);
+        if (status == MUON_OK)
+          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a,
+                                   c != 0.0f ? 1.0f : b, st, last ? &fin : nullptr);
+      } else {
+        status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st);
+        if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st);
+        if (status == MUON_OK)
+          status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a,
+                                  c != 0.0f ? 1.0f : b, st, last ? &fin : nullptr);
+      }
+      if (status != MUON_OK) return status;
+    }
+  }
+  return MUON_OK;
+}
+
+static bool stage_dims_ok(int64_t s, int64_t l, int64_t batch) {
+  return s > 0 && l > 0 && batch >= 0 && s % MUON_NS_PAD == 0 && l % MUON_NS_PAD == 0 && s <= l;
+}
+
+int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t batch,
+                 const float* sumsq, void* X0, int precision, void* stream) {
+  if (rows <= 0 || cols <= 0 || batch < 0) return MUON_EINVAL;
+  if (!valid_dtype(m_dtype)) return MUON_EDTYPE;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (batch == 0) return MUON_OK;
+  if (!M || !sumsq || !X0) return MUON_EINVAL;
+  if (!aligned16(M) || !aligned16(X0)) return MUON_EALIGN;
+  const int64_t sp = pad_to(std::min(rows, cols)), lp = pad_to(std::max(rows, cols));
+  return normalize_dispatch(M, m_dtype, rows * cols, rows, cols, sumsq, 1, X0, precision, sp, lp,
+                            batch, static_cast<hipStream_t>(stream));
+}
+
+int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision, void* stream) {
+  if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (batch == 0) return MUON_OK;
+  if (!X || !A) return MUON_EINVAL;
+  if (!aligned16(X) || !aligned16(A)) return MUON_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return precision == MUON_BF16 ? gram_t<bf16_t>(X, A, s, l, batch, st) : gram_t<float>(X, A, s, l, batch, st);
+}
+
+int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c, int precision,
+            void* stream) {
+  if (!stage_dims_ok(s, s, batch)) return MUON_EINVAL;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (batch == 0) return MUON_OK;
+  if (!A || !B) return MUON_EINVAL;
+  if (!aligned16(A) || !aligned16(B)) return MUON_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return precision == MUON_BF16 ? poly_t<bf16_t>(A, B, s, batch, b, c, st) : poly_t<float>(A, B, s, batch, b, c, st);
+}
+
+int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
+             float alpha, int precision, void* stream) {
+  if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (batch == 0) return MUON_OK;
+  if (!B || !X || !Xout) return MUON_EINVAL;
+  if (!aligned16(B) || !aligned16(X) || !aligned16(Xout)) return MUON_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return precision == MUON_BF16 ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, nullptr)
+                                : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+"""Buffers and call order of one SignMuon worker step on a flat parameter set.
+
+This is host-side orchestration only: it owns the device buffers (through
+torch) and calls the C ABI in the order of the "SignMuon: Otimização
+Distribuída de Muon com Eficiência de Comunicação" summary, section 2,
+"Fluxo Algorítmico (Distribuído)": local momentum and polar factor (step 1),
+sign extraction packed to one bit per entry (steps 2-3), then the majority
+vote and the update (step 4).  All arithmetic runs in libmuon's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _abi
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class SignMuonStep:
+    """One worker's step over matrices ``shapes`` stored back to back in flat buffers.
+
+    Parameters are the method's: ``beta``/``alpha`` of the momentum EMA,
+    Newton-Schulz ``coeffs`` (a, b, c) and ``ns_steps``, the NS operand
+    ``precision`` ("bf16" or "f32") and the step size ``eta``.
+    """
+
+    def __init__(self, shapes: Sequence[Tuple[int, int]], m_dtype: str = "bf16",
+                 precision: str = "bf16", coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
+                 beta: float = 0.95, alpha: Optional[float] = None, eta: float = 0.02,
+                 device="cuda"):
+        self.shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.device = torch.device(device)
+        sizes = [r * c for r, c in self.shapes]
+        offs = [0]
+        for n in sizes:
+            offs.append(offs[-1] + n)
+        self.offsets_host = offs
+        self.numel = offs[-1]
+        self.nwords = _abi.packed_words(self.numel)
+        self.m_dtype = m_dtype
+        self.precision = precision
+        self.coeffs = tuple(float(x) for x in coeffs)
+        self.ns_steps = int(ns_steps)
+        self.beta = float(beta)
+        self.alpha = float(1.0 - beta if alpha is None else alpha)
+        self.eta = float(eta)
+        u_dtype = torch.float32 if precision == "f32" else torch.bfloat16
+        self.offsets = torch.tensor(offs, dtype=torch.int64, device=self.device)
+        self.sumsq = torch.zeros(len(self.shapes), dtype=torch.float32, device=self.device)
+        self.U = torch.empty(self.numel, dtype=u_dtype, device=self.device)
+        # workspace sized from the NS problems over a stand-in momentum buffer
+        probe_M = torch.empty(self.numel, dtype=_TORCH_DTYPE[m_dtype], device=self.device)
+        ns_bytes = _abi.ns_workspace_bytes(self._problems(probe_M), self.precision)
+        mom_bytes = _abi.muon_momentum_workspace_bytes(self.numel, len(self.shapes))
+        del probe_M
+        self.ns_workspace = torch.empty(max(ns_bytes, 1), dtype=torch.uint8, device=self.device)
+        self.mom_workspace = torch.empty(max(mom_bytes, 1), dtype=torch.uint8, device=self.device)
+
+    def _problems(self, M: torch.Tensor):
+        probs = []
+        for j, (r, c) in enumerate(self.shapes):
+            lo, hi = self.offsets_host[j], self.offsets_host[j + 1]
+            probs.append((M[lo:hi].view(r, c), self.U[lo:hi].view(r, c), self.sumsq[j:j + 1]))
+        return probs
+
+    def new_bits(self, workers: int = 1) -> torch.Tensor:
+        return torch.zeros((workers, self.nwords), dtype=torch.int64, device=self.device)
+
+    # -- step pieces -------------------------------------------------------
+    def momentum(self, M: torch.Tensor, G: torch.Tensor) -> None:
+        _abi.muon_momentum(M, G, self.beta, self.alpha, self.offsets, self.sumsq, self.mom_workspace)
+
+    def orthogonalize(self, M: torch.Tensor) -> None:
+        a, b, c = self.coeffs
+        _abi.ns_orthogonalize(self._problems(M), a, b, c, self.ns_steps, self.precision,
+                              self.ns_workspace)
+
+    def pack(self, bits_row: torch.Tensor) -> None:
+        _abi.sign_pack(self.U, bits_row)
+
+    def worker(self, M: torch.Tensor, G: torch.Tensor, bits_row: torch.Tensor) -> None:
+        """Steps 1-3 for one worker: momentum, polar direction, packed signs."""
+        self.momentum(M, G)
+        self.orthogonalize(M)
+        self.pack(bits_row)
+
+    def vote_update(self, W: torch.Tensor, bits: torch.Tensor, vote_out: Optional[torch.Tensor] = None,
+                    fused: bool = False) -> None:
+        """Step 4: majority vote over the rows of ``bits`` and ``W <- W - eta * vote``."""
+        if fused:
+            _abi.vote_and_update(W, bits, self.eta)
+            return
+        if vote_out is None:
+            vote_out = torch.empty(self.nwords, dtype=torch.int64, device=self.device)
+        _abi.majority_vote(bits, vote_out)
+        _abi.apply_update(W, vote_out, self.eta)

@@ -1,0 +1,165 @@
+"""Host-side checks of libmuon (no GPU): exports, argument validation, workspace sizing.
+
+Every call here fails validation (or is a pure size query) before the
+library touches the HIP runtime, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import matrix_aware_optimizer_amd as mao
+from matrix_aware_optimizer_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE = 0, -1, -2, -3, -4
+A1, A2, A3 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mao.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in muon.h but not exported"
+    assert sorted(_abi.SIGNATURES) == names
+
+
+def test_status_strings(L):
+    for code in [0, -1, -2, -3, -4, -5]:
+        assert mao.status_string(code)
+    assert mao.status_string(-99) == "unknown status"
+    assert mao.muon_version() >= 100
+
+
+def test_momentum_validation(L):
+    f = L.muon_momentum
+    assert f(None, 1, A2, 1, 100, None, 0, 0.9, 0.1, None, None, 0, None) == EINVAL
+    assert f(A1, 1, A2, 1, -1, None, 0, 0.9, 0.1, None, None, 0, None) == EINVAL
+    assert f(A1, 5, A2, 1, 100, None, 0, 0.9, 0.1, None, None, 0, None) == EDTYPE
+    assert f(MISALIGNED, 1, A2, 1, 100, None, 0, 0.9, 0.1, None, None, 0, None) == EALIGN
+    # norms requested: offsets and workspace are required and sized
+    assert f(A1, 1, A2, 1, 100, None, 1, 0.9, 0.1, A3, None, 0, None) == EINVAL
+    need = L.muon_momentum_workspace_bytes(100, 1)
+    assert need >= 16
+    assert f(A1, 1, A2, 1, 100, A3, 1, 0.9, 0.1, A3, A3, need - 1, None) == EWORKSPACE
+    assert f(A1, 1, A2, 1, 0, None, 0, 0.9, 0.1, None, None, 0, None) == OK   # empty: no launch
+
+
+def test_momentum_workspace_formula(L):
+    # one double per 8192-entry chunk and per segment, plus one, rounded to 256 bytes
+    for numel, nseg in [(1, 1), (8192, 1), (8193, 2), (58720256, 1), (84934656, 48)]:
+        chunks = -(-numel // 8192)
+        expect = -(-(chunks + nseg + 1) * 8 // 256) * 256
+        assert L.muon_momentum_workspace_bytes(numel, nseg) == expect
+
+
+def test_pack_vote_update_validation(L):
+    assert L.sign_pack(A1, 1, -5, A2, None) == EINVAL
+    assert L.sign_pack(A1, 9, 64, A2, None) == EDTYPE
+    assert L.sign_pack(A1, 1, 64, MISALIGNED, None) == EALIGN
+    assert L.sign_pack(None, 1, 64, A2, None) == EINVAL
+    assert L.sign_pack(None, 1, 0, None, None) == OK
+    assert L.majority_vote(A1, 0, 10, A2, None) == EINVAL
+    assert L.majority_vote(A1, 1024, 10, A2, None) == EINVAL
+    assert L.majority_vote(MISALIGNED, 3, 10, A2, None) == EALIGN
+    assert L.apply_update(A1, 3, 10, A2, 0.1, None) == EDTYPE
+    assert L.apply_update(A1, 1, 10, None, 0.1, None) == EINVAL
+    assert L.vote_and_update(A1, 1, 10, A2, 0, 0.1, None) == EINVAL
+    assert L.vote_and_update(A1, 1, 10, MISALIGNED, 3, 0.1, None) == EALIGN
+
+
+def test_stage_validation(L):
+    assert L.ns_gram(A1, A2, 250, 512, 1, 1, None) == EINVAL      # s not padded
+    assert L.ns_gram(A1, A2, 512, 256, 1, 1, None) == EINVAL      # s > l
+    assert L.ns_gram(A1, A2, 256, 512, 1, 7, None) == EDTYPE
+    assert L.ns_poly(A1, MISALIGNED, 256, 1, 1.0, 1.0, 1, None) == EALIGN
+    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None) == EINVAL
+    assert L.ns_normalize(A1, 1, 0, 5, 1, A2, A3, 1, None) == EINVAL
+    assert L.ns_gram(A1, A2, 256, 256, 0, 1, None) == OK           # empty batch: no launch
+
+
+def _problems(specs):
+    arr = (_abi.NSProblem * len(specs))()
+    for i, (M, U, s, r, c, md, ud) in enumerate(specs):
+        arr[i].M, arr[i].U, arr[i].sumsq = M, U, s
+        arr[i].rows, arr[i].cols, arr[i].m_dtype, arr[i].u_dtype = r, c, md, ud
+    return arr
+
+
+def _ns_bytes(count, s, l, es=2, sumsq=True, part=0):
+    def up(x):
+        return -(-x // 256) * 256
+    return 2 * up(count * s * l * es) + 2 * up(count * s * s * es) + (0 if sumsq else up(4 * count)) + up(part)
+
+
+def test_ns_workspace_single_and_padding(L):
+    arr = _problems([(0x10000, 0x20000, 0x30000, 4096, 14336, 1, 1)])
+    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 4096, 14336)
+    arr = _problems([(0x10000, 0x20000, 0x30000, 300, 70, 1, 1)])    # tall, ragged
+    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 256, 512)
+    assert L.ns_workspace_bytes(arr, 1, 0) == _ns_bytes(1, 256, 512, es=4)
+    assert L.ns_workspace_bytes(arr, 0, 1) == 0
+    assert L.ns_workspace_bytes(arr, 1, 9) == 0
+
+
+def test_ns_grouping_batches_evenly_spaced_problems(L):
+    # 12 layers x {768x2304, 768x768, 768x3072, 3072x768} laid out flat, given in layer order
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768)] * 12
+    off, specs = 0, []
+    for j, (r, c) in enumerate(shapes):
+        specs.append((0x100000 + 2 * off, 0x40000000 + 2 * off, 0x80000 + 4 * j, r, c, 1, 1))
+        off += r * c
+    arr = _problems(specs)
+    # the largest run is 12 matrices of 768x3072 (the wide and the tall ones are separate runs)
+    assert L.ns_workspace_bytes(arr, 48, 1) == _ns_bytes(12, 768, 3072)
+    # irregular spacing defeats batching: every problem is its own run
+    specs2 = [(M + (j * j % 7) * 4096 * 0, U, s, r, c, md, ud) for j, (M, U, s, r, c, md, ud) in enumerate(specs)]
+    specs2[1] = (specs2[1][0], specs2[1][1] + 16, specs2[1][2], *specs2[1][3:])
+    arr2 = _problems(specs2)
+    assert L.ns_workspace_bytes(arr2, 48, 1) == _ns_bytes(12, 768, 3072)
+    # without norms the run also holds its sums and partial sums
+    specs3 = [(M, U, None, r, c, md, ud) for (M, U, s, r, c, md, ud) in specs[:1]]
+    part = L.muon_momentum_workspace_bytes(768 * 2304, 1)
+    assert L.ns_workspace_bytes(_problems(specs3), 1, 1) == _ns_bytes(1, 768, 2304, sumsq=False, part=part)
+
+
+def test_ns_orthogonalize_validation(L):
+    arr = _problems([(0x10000, 0x20000, 0x30000, 512, 1024, 1, 1)])
+    need = L.ns_workspace_bytes(arr, 1, 1)
+    f = L.ns_orthogonalize
+    assert f(arr, 1, 1.0, 1.0, 1.0, 5, 1, A3, need - 1, None) == EWORKSPACE
+    assert f(arr, 1, 1.0, 1.0, 1.0, 5, 1, None, need, None) == EWORKSPACE
+    assert f(arr, 1, 1.0, 1.0, 1.0, -1, 1, A3, need, None) == EINVAL
+    assert f(arr, 1, 1.0, 1.0, 1.0, 5, 4, A3, need, None) == EDTYPE
+    bad = _problems([(0x10008, 0x20000, 0x30000, 512, 1024, 1, 1)])
+    assert f(bad, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EALIGN
+    bad = _problems([(0x10000, 0x20000, 0x30000, 0, 1024, 1, 1)])
+    assert f(bad, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    bad = _problems([(0x10000, 0x20000, 0x30000, 8, 8, 1, 3)])
+    assert f(bad, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EDTYPE
+    assert f(arr, 0, 1.0, 1.0, 1.0, 5, 1, None, 0, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    t = torch.zeros(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mao.sign_pack(t, torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        _abi.dtype_code(torch.zeros(2, dtype=torch.float16))

@@ -1,0 +1,189 @@
+"""GPU parity of the Newton-Schulz stages (a2-a5) and of the whole iteration.
+
+Stage tolerances follow from one rounding of the output to the working type
+(bf16: unit roundoff 2^-8 bounds the relative Frobenius error, fp32 2^-23
+plus fp32 accumulation); the whole iteration is gated at 2e-2 (bf16) and
+1e-4 (fp32) relative Frobenius error against the fp64 oracle fed the same
+stored momentum.
+"""
+import numpy as np
+import pytest
+import torch
+
+import matrix_aware_optimizer_amd as mao
+import oracle.muon_oracle as O
+from helpers import from_dev, rel_fro, to_dev
+from workloads import CUBIC, QUINTIC, random_matrix, store
+
+pytestmark = pytest.mark.gpu
+
+TOL_STAGE = {"bf16": 2.0 ** -8, "f32": 2e-6}
+TOL_NS = {"bf16": 2e-2, "f32": 1e-4}
+TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def padded(x, s, l):
+    out = np.zeros((x.shape[0], s, l))
+    out[:, :x.shape[1], :x.shape[2]] = x
+    return out
+
+
+def _stage_X(batch, s, l, sv, lv, prec, seed):
+    X = np.zeros((batch, s, l))
+    X[:, :sv, :lv] = random_matrix((batch, sv, lv), [300, seed]) / np.sqrt(sv * lv)
+    Xs = store(X, prec)
+    return Xs, O.decode(Xs, prec)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("batch,s,l,sv,lv", [(1, 256, 256, 256, 256), (2, 256, 768, 200, 700),
+                                              (1, 512, 1024, 512, 1000), (3, 768, 768, 768, 768)])
+def test_gram(prec, batch, s, l, sv, lv):
+    Xs, X = _stage_X(batch, s, l, sv, lv, prec, 1)
+    A = torch.empty((batch, s, s), dtype=TORCH[prec], device="cuda")
+    mao.ns_gram(to_dev(Xs, prec).view(batch, s, l), A, prec)
+    got = O.decode(from_dev(A), prec).reshape(batch, s, s)
+    for b in range(batch):
+        ref = O.gram(X[b])
+        assert rel_fro(got[b], ref) <= TOL_STAGE[prec]
+        assert rel_fro(got[b], got[b].T) <= TOL_STAGE[prec]                 # symmetric
+        assert not got[b][sv:, :].any() and not got[b][:, sv:].any()     # padding stays zero
+
+
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("coeffs", [QUINTIC, (2.0, -1.5, 0.5)])
+@pytest.mark.parametrize("batch,s,sv", [(1, 256, 256), (2, 512, 300), (1, 1024, 1024)])
+def test_poly(prec, coeffs, batch, s, sv):
+    Xs, X = _stage_X(batch, s, s, sv, sv, prec, 2)
+    A = torch.empty((batch, s, s), dtype=TORCH[prec], device="cuda")
+    mao.ns_gram(to_dev(Xs, prec).view(batch, s, s), A, prec)
+    B = torch.empty_like(A)
+    mao.ns_poly(A, B, coeffs[1], coeffs[2], prec)
+    Ain = O.decode(from_dev(A), prec).reshape(batch, s, s)
+    got = O.decode(from_dev(B), prec).reshape(batch, s, s)
+    for b in range(batch):
+        ref = O.poly(Ain[b], coeffs[1], coeffs[2])
+        assert rel_fro(got[b], ref) <= TOL_STAGE[prec]
+        assert not got[b][sv:, :].any() and not got[b][:, sv:].any()
+
+
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("a,alpha", [(QUINTIC[0], 1.0), (1.5, -0.5)])
+@pytest.mark.parametrize("batch,s,l,sv,lv", [(1, 256, 256, 256, 256), (2, 256, 768, 200, 700),
+                                              (1, 512, 1536, 512, 1536)])
+def test_apply(prec, a, alpha, batch, s, l, sv, lv):
+    Xs, X = _stage_X(batch, s, l, sv, lv, prec, 3)
+    Bm = np.zeros((batch, s, s))
+    R = random_matrix((batch, sv, sv), [301, 0]) / np.sqrt(sv)
+    Bm[:, :sv, :sv] = R + np.transpose(R, (0, 2, 1))
+    Bs = store(Bm, prec)
+    Xd = to_dev(Xs, prec).view(batch, s, l)
+    out = torch.empty_like(Xd)
+    mao.ns_apply(to_dev(Bs, prec).view(batch, s, s), Xd, out, a, alpha, prec)
+    got = O.decode(from_dev(out), prec).reshape(batch, s, l)
+    Bd = O.decode(Bs, prec)
+    for b in range(batch):
+        ref = O.apply_poly(alpha * Bd[b], X[b], a)
+        assert rel_fro(got[b], ref) <= TOL_STAGE[prec]
+        assert not got[b][sv:, :].any() and not got[b][:, lv:].any()
+
+
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+@pytest.mark.parametrize("m_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,batch", [(300, 70, 2), (70, 300, 1), (256, 256, 1), (5, 3, 4)])
+def test_normalize(prec, m_dtype, rows, cols, batch):
+    M = store(random_matrix((batch, rows, cols), [302, rows]), m_dtype)
+    Mf = O.decode(M, m_dtype).reshape(batch, rows, cols)
+    sums = torch.tensor([O.sumsq(Mf[b]) for b in range(batch)], dtype=torch.float32, device="cuda")
+    s, l = min(rows, cols), max(rows, cols)
+    sp, lp = -(-s // 256) * 256, -(-l // 256) * 256
+    X0 = torch.full((batch, sp, lp), 7.0, dtype=TORCH[prec], device="cuda")
+    mao.ns_normalize(to_dev(M, m_dtype).view(batch, rows, cols), sums, X0, prec)
+    got = O.decode(from_dev(X0), prec).reshape(batch, sp, lp)
+    for b in range(batch):
+        ref = O.frobenius_normalize(Mf[b])
+        ref = ref.T if rows > cols else ref
+        assert np.allclose(got[b][:s, :l], ref, rtol=TOL_STAGE[prec], atol=1e-30)
+        assert not got[b][s:, :].any() and not got[b][:, l:].any()
+
+
+def _ns_gpu(M_list, m_dtype, u_dtype, coeffs, steps, prec, with_sums=True):
+    """Run ns_orthogonalize over matrices stored back to back in one flat buffer."""
+    flat = np.concatenate([m.ravel() for m in M_list])
+    Md = to_dev(flat, m_dtype)
+    U = torch.zeros(flat.size, dtype=TORCH[u_dtype], device="cuda")
+    sums = torch.tensor([O.sumsq(O.decode(m, m_dtype)) for m in M_list], dtype=torch.float32,
+                        device="cuda")
+    probs, off = [], 0
+    for j, m in enumerate(M_list):
+        n = m.size
+        probs.append((Md[off:off + n].view(*m.shape), U[off:off + n].view(*m.shape),
+                      sums[j:j + 1] if with_sums else None))
+        off += n
+    mao.ns_orthogonalize(probs, *coeffs, steps, prec)
+    out, off = [], 0
+    Uh = O.decode(from_dev(U), u_dtype)
+    for m in M_list:
+        out.append(Uh[off:off + m.size].reshape(m.shape))
+        off += m.size
+    return out
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (37, 300), (300, 37), (512, 1536), (1536, 512),
+                                   (768, 768), (1, 1), (3, 1000)])
+@pytest.mark.parametrize("prec,coeffs", [("f32", CUBIC), ("bf16", QUINTIC), ("f32", QUINTIC)])
+@pytest.mark.parametrize("steps", [0, 1, 5])
+def test_ns_matches_oracle(shape, prec, coeffs, steps):
+    m_dtype = prec
+    M = store(random_matrix(shape, [303, shape[0], shape[1]]), m_dtype)
+    (U,) = _ns_gpu([M], m_dtype, prec, coeffs, steps, prec)
+    ref = O.newton_schulz(O.decode(M, m_dtype), *coeffs, steps)
+    assert rel_fro(U, ref) <= TOL_NS[prec], rel_fro(U, ref)
+
+
+def test_ns_computes_its_own_norm_and_handles_zero():
+    Ms = [store(random_matrix((200, 520), [304, 0]), "bf16"),
+          store(np.zeros((64, 64)), "bf16"),
+          store(random_matrix((520, 200), [304, 1]) * 1e-3, "bf16")]
+    got = _ns_gpu(Ms, "bf16", "bf16", QUINTIC, 5, "bf16", with_sums=False)
+    assert not got[1].any()
+    for M, U in zip([Ms[0], Ms[2]], [got[0], got[2]]):
+        ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
+        assert rel_fro(U, ref) <= TOL_NS["bf16"]
+
+
+def test_ns_batched_interleaved_shapes():
+    # layer-ordered problems of two shapes: grouped into two batched runs internally
+    shapes = [(256, 768), (768, 256), (256, 256)] * 4
+    Ms = [store(random_matrix(s, [305, j]), "bf16") for j, s in enumerate(shapes)]
+    got = _ns_gpu(Ms, "bf16", "bf16", QUINTIC, 5, "bf16")
+    for M, U in zip(Ms, got):
+        ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
+        assert rel_fro(U, ref) <= TOL_NS["bf16"]
+
+
+def test_ns_mixed_dtypes_fp32_momentum_bf16_ops():
+    M = store(random_matrix((300, 900), [306, 0], "student_t3"), "f32")
+    (U,) = _ns_gpu([M], "f32", "bf16", QUINTIC, 5, "bf16")
+    ref = O.newton_schulz(O.decode(M, "f32"), *QUINTIC, 5)
+    assert rel_fro(U, ref) <= TOL_NS["bf16"]
+
+
+@pytest.mark.parametrize("prec,coeffs,steps", [("f32", CUBIC, 30), ("bf16", QUINTIC, 5)])
+def test_ns_closed_form_spectrum(prec, coeffs, steps):
+    # known spectrum: U = Q1 phi(sigma/||sigma||) Q2^T (closed form of the iteration)
+    r, c = 256, 512
+    Q1, _ = np.linalg.qr(random_matrix((r, r), [307, 0]))
+    Q2, _ = np.linalg.qr(random_matrix((c, r), [307, 1]))
+    sig = np.logspace(-2, 0, r)
+    M = store((Q1 * sig) @ Q2.T, prec)
+    (U,) = _ns_gpu([M], prec, prec, coeffs, steps, prec)
+    x = sig / np.linalg.norm(sig)
+    for _ in range(steps):
+        x = coeffs[0] * x + coeffs[1] * x ** 3 + coeffs[2] * x ** 5
+    expect = (Q1 * x) @ Q2.T
+    # the stored M is a rounded copy of the exact one: in bf16 that rounding moves
+    # small singular values by more than the gate, so only fp32 meets the exact form
+    if prec == "f32":
+        assert rel_fro(U, expect) <= TOL_NS[prec]
+    assert rel_fro(U, O.newton_schulz(O.decode(M, prec), *coeffs, steps)) <= TOL_NS[prec]
