@@ -66,9 +66,11 @@ int muon_version(void);
  * a1 -- momentum EMA and per-matrix squared Frobenius norm.
  *   [SM] "Fluxo Algorítmico" step 1: each worker updates its local momentum.
  *   The pages print no formula; this computes the EMA
- *       M[i] <- round_m( beta * M[i] + alpha * G[i] )          (fp32 math)
+ *       M[i] <- round_m( beta * M[i] + alpha * G[i] )
  *   in place over a flat parameter set of `numel` entries, with alpha =
  *   1 - beta for the classical EMA (heavy-ball momentum is beta, alpha = 1).
+ *   The sum of the two exact products is rounded once in fp64, then to fp32
+ *   and, for bf16 storage, to bf16 (nearest-even each time).
  *   If `sumsq_out` is not NULL it also writes, for every matrix j of the set,
  *       sumsq_out[j] = sum over its entries of (stored new M)^2,
  *   the squared Frobenius norm the normalisation divides by.  Matrix j covers

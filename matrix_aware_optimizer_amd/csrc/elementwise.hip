@@ -65,6 +65,13 @@ struct SegMap {
   }
 };
 
+// beta*m + alpha*g rounded once: both products of fp32 values are exact in
+// fp64, the fp64 fma rounds their sum once, then it is rounded to fp32.
+__device__ __forceinline__ float ema(float beta, float m, float alpha, float g) {
+  return static_cast<float>(fma(static_cast<double>(beta), static_cast<double>(m),
+                                static_cast<double>(alpha) * static_cast<double>(g)));
+}
+
 __device__ __forceinline__ double block_sum(double v, double* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
         float g[8];
         Vec8<TG>::load(G + e0, g);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) m[q] = fmaf(beta, m[q], alpha * g[q]);
+        for (int q = 0; q < 8; ++q) m[q] = ema(beta, m[q], alpha, g[q]);
         Vec8<TM>::store(M + e0, m);
         // the stored value is what the norm must see
 #pragma unroll
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
         if (e0 + q < c1) {
           m = to_f32(M[e0 + q]);
           if (UPDATE) {
-            const TM st = from_f32<TM>(fmaf(beta, m, alpha * to_f32(G[e0 + q])));
+            const TM st = from_f32<TM>(ema(beta, m, alpha, to_f32(G[e0 + q])));
             M[e0 + q] = st;
             m = to_f32(st);
           }

@@ -1,0 +1,652 @@
+// Matrix-core GEMM used by the Newton-Schulz products (gfx950, wave64).
+//
+//   C = alpha * P Q^T (+ beta * Z)          P, Q rows contiguous along k ("NT")
+//   C = alpha * P Q   (+ beta * Z)          Q given k-major: [K][N] ("NN")
+//
+// The symmetric products (the Gram X X^T and A A for symmetric A) run NT
+// with P = Q over the lower-triangle tiles only; every off-diagonal tile is
+// stored twice (at (i,j) and mirrored at (j,i)), so the output is the full
+// symmetric matrix.
+//
+// Structure of one workgroup (BM x BN output tile, (BM/WM) x (BN/WN) waves):
+//  * k advances in LDS tiles of 128 bytes per row (64 bf16 / 32 fp32); two
+//    LDS stages: while the waves multiply stage s, the next k-tile travels
+//    global -> registers, and is written to stage s^1 before the one barrier
+//    of the iteration.
+//  * LDS rows hold 8 chunks of 16 bytes; chunk c of row r sits at slot
+//    c ^ ((r ^ (r >> 3)) & 7), which keeps both the tile stores (8 lanes per
+//    row) and the fragment reads (32 consecutive rows) free of bank
+//    conflicts.
+//  * The NN operand is read as E x E blocks (E = 8 bf16 / 4 fp32 per 16 bytes)
+//    of [k][n] and transposed in registers, so its LDS tile has the same
+//    k-contiguous rows as the NT operands.
+//  * Fragments: lane l holds row (l % 32) and k-group (l / 32) of a 32 x 32
+//    tile; bf16 issues v_mfma_f32_32x32x16_bf16, fp32 four
+//    v_mfma_f32_32x32x2f32, both accumulating in fp32.
+//  * Workgroup ids are spread round-robin over the 8 XCDs by the dispatcher;
+//    they are remapped so each XCD gets a contiguous range of tiles, ordered
+//    in groups of GROUP_M tile rows so that concurrently running tiles share
+//    operand strips in that XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace muon {
+namespace gemm {
+
+constexpr int kRowBytes = 128;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  static constexpr int kElems = 8;  // elements per 16 bytes
+  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  }
+};
+
+// byte offset of 16-byte chunk `chunk` (0..7) of LDS tile row `row`
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
+
+struct GemmArgs {
+  const void* P;  // rows of the left operand, k-contiguous, ld = K
+  const void* Q;  // NT: rows of the right operand (k-contiguous, ld = K); NN: [K][N]
+  const void* Z;  // epilogue addend [M][N] (ld = N), may be null
+  void* C;        // output [M][N] (ld = N)
+  int64_t M, N, K;
+  int64_t strideP, strideQ, strideZ, strideC;  // batch strides (elements)
+  float alpha, beta;                           // C = alpha*acc + beta*Z
+  // EPI_FINAL: write U instead of C, un-padded (s_valid x l_valid of the
+  // working layout) and transposed back when the momentum was tall.
+  void* U;
+  int64_t strideU;
+  int64_t s_valid, l_valid;
+  int u_dtype;
+  int transpose_out;
+};
+
+template <typename T, int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int E = Mfma<T>::kElems;
+  static constexpr int BK = kRowBytes / sizeof(T);  // k per LDS tile
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NT = WAVES_M * WAVES_N * kWave;
+  static constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 fragments per wave
+  static constexpr int KSTEPS = BK / (2 * E);       // fragment reads per LDS tile
+  static constexpr int A_CHUNKS = BM * 8 / NT;      // 16-byte loads per thread
+  static constexpr int B_CHUNKS = BN * 8 / NT;
+  static constexpr int NN_BLOCKS = (BK / E) * (BN / E);
+  static constexpr int NN_PER_T = (NN_BLOCKS + NT - 1) / NT;
+  static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
+};
+
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
+  const int64_t full = nblocks / kXcds * kXcds;
+  if (bid >= full) return bid;
+  return (bid % kXcds) * (full / kXcds) + bid / kXcds;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs g) {
+  using C_ = Tile<T, BM, BN, WM, WN>;
+  constexpr int E = C_::E, BK = C_::BK, NT = C_::NT, FM = C_::FM, FN = C_::FN;
+  static_assert(!SYRK || BM == BN, "symmetric products need square tiles");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t batch = blockIdx.y;
+
+  // ---- tile coordinates ----
+  int64_t tm, tn;
+  if (SYRK) {
+    const int64_t T_ = g.M / BM;
+    const int64_t t = xcd_remap(blockIdx.x, T_ * (T_ + 1) / 2);
+    int64_t ti = static_cast<int64_t>((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tm = ti;
+    tn = t - ti * (ti + 1) / 2;
+  } else {
+    const int64_t TM = g.M / BM, TN = g.N / BN;
+    const int64_t t = xcd_remap(blockIdx.x, TM * TN);
+    const int64_t per_group = int64_t(kGroupM) * TN;
+    const int64_t first_m = (t / per_group) * kGroupM;
+    const int64_t gsize = min(TM - first_m, int64_t(kGroupM));
+    const int64_t r = t % per_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+  }
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const T* P = static_cast<const T*>(g.P) + batch * g.strideP;
+  const T* Q = static_cast<const T*>(g.Q) + batch * g.strideQ;
+
+  // ---- global -> register staging ----
+  u32x4_t ra[C_::A_CHUNKS];
+  u32x4_t rb[NN ? C_::NN_PER_T * E : C_::B_CHUNKS];
+
+  auto load_tiles = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < C_::A_CHUNKS; ++i) {
+      const int c = tid + i * NT;
+      ra[i] = *reinterpret_cast<const u32x4_t*>(P + (m0 + (c >> 3)) * g.K + k0 + (c & 7) * E);
+    }
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < C_::B_CHUNKS; ++i) {
+        const int c = tid + i * NT;
+        rb[i] = *reinterpret_cast<const u32x4_t*>(Q + (n0 + (c >> 3)) * g.K + k0 + (c & 7) * E);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C_::NN_PER_T; ++i) {
+        const int blk = tid + i * NT;
+        if (blk < C_::NN_BLOCKS) {
+          const int nb = blk % (BN / E), kb = blk / (BN / E);
+#pragma unroll
+          for (int r = 0; r < E; ++r)
+            rb[i * E + r] =
+                *reinterpret_cast<const u32x4_t*>(Q + (k0 + kb * E + r) * g.N + n0 + nb * E);
+        }
+      }
+    }
+  };
+
+  auto store_tiles = [&](char* stage) {
+    char* sA = stage;
+    char* sB = stage + BM * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < C_::A_CHUNKS; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(sA + lds_off(c >> 3, c & 7)) = ra[i];
+    }
+    if (!NN) {
+#pragma unroll
+      for (int i = 0; i < C_::B_CHUNKS; ++i) {
+        const int c = tid + i * NT;
+        *reinterpret_cast<u32x4_t*>(sB + lds_off(c >> 3, c & 7)) = rb[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C_::NN_PER_T; ++i) {
+        const int blk = tid + i * NT;
+        if (blk < C_::NN_BLOCKS) {
+          const int nb = blk % (BN / E), kb = blk / (BN / E);
+          const u32x4_t* in = rb + i * E;
+          if (sizeof(T) == 2) {
+            // in[r] holds k = kb*8 + r for n = nb*8 + 0..7 (two per dword);
+            // column e of the 8x8 block becomes the 8 k-values of row n.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int d = e >> 1;
+              uint32_t w[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = in[2 * j][d], hi = in[2 * j + 1][d];
+                w[j] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+              }
+              u32x4_t o;
+              o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+              *reinterpret_cast<u32x4_t*>(sB + lds_off(nb * 8 + e, kb)) = o;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              u32x4_t o;
+              o.x = in[0][e]; o.y = in[1][e]; o.z = in[2][e]; o.w = in[3][e];
+              *reinterpret_cast<u32x4_t*>(sB + lds_off(nb * 4 + e, kb)) = o;
+            }
+          }
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int wm0 = (wave / C_::WAVES_N) * WM;
+  const int wn0 = (wave % C_::WAVES_N) * WN;
+  const int frow = lane & 31, fgrp = lane >> 5;
+
+  const int64_t KT = g.K / BK;
+  load_tiles(0);
+  store_tiles(lds);
+  __syncthreads();
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    char* cur = lds + (kt & 1) * C_::STAGE_BYTES;
+    char* nxt = lds + ((kt + 1) & 1) * C_::STAGE_BYTES;
+    if (kt + 1 < KT) load_tiles((kt + 1) * BK);
+    const char* sA = cur;
+    const char* sB = cur + BM * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < C_::KSTEPS; ++ks) {
+      const int chunk = ks * 2 + fgrp;
+      u32x4_t fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4_t*>(sA + lds_off(wm0 + i * 32 + frow, chunk));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(sB + lds_off(wn0 + j * 32 + frow, chunk));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) store_tiles(nxt);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) +
+  // (v%4), column l%32 of the fragment.
+  T* C = static_cast<T*>(g.C) + batch * g.strideC;
+  const T* Z = static_cast<const T*>(g.Z) + batch * g.strideZ;
+  const bool mirror = SYRK && (tm != tn);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn0 + j * 32 + frow;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row0 = m0 + wm0 + i * 32 + 8 * q + 4 * fgrp;
+        float out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[i][j][4 * q + r] * g.alpha;
+          if (EPI != EPI_STORE) v = fmaf(g.beta, to_f32(Z[(row0 + r) * g.N + col]), v);
+          out[r] = v;
+        }
+        if (EPI == EPI_FINAL) {
+          if (col < g.l_valid) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t row = row0 + r;
+              if (row < g.s_valid) {
+                const int64_t idx = g.transpose_out ? col * g.s_valid + row : row * g.l_valid + col;
+                if (g.u_dtype == MUON_BF16)
+                  static_cast<bf16_t*>(g.U)[batch * g.strideU + idx] = f32_to_bf16(out[r]);
+                else
+                  static_cast<float*>(g.U)[batch * g.strideU + idx] = out[r];
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = from_f32<T>(out[r]);
+          if (mirror) {
+            // the four consecutive rows are four consecutive entries of row `col`
+            T* dst = C + col * g.N + row0;
+            if (sizeof(T) == 2) {
+              const uint32_t w0 = uint32_t(from_f32<bf16_t>(out[0])) | (uint32_t(from_f32<bf16_t>(out[1])) << 16);
+              const uint32_t w1 = uint32_t(from_f32<bf16_t>(out[2])) | (uint32_t(from_f32<bf16_t>(out[3])) << 16);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel with global -> LDS DMA (global_load_lds_dwordx4) and an
+// S-stage LDS ring.  k advances 32 at a time (two 32x32x16 MFMA steps).
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so every access pattern below is
+// free of bank conflicts):
+//  * k-contiguous operand rows (P, and Q for NT): 64 bytes = 4 chunks per
+//    row; chunk c of row r sits at slot c ^ (((r >> 1) ^ (r >> 3)) & 3).
+//  * k-major Q tile for NN ([k][n], n contiguous): rows of 2*BN bytes; chunk
+//    c of row r sits at slot c ^ (2 * (r & 3)).
+// One DMA instruction moves 1 KB (64 lanes x 16 bytes) to consecutive LDS
+// bytes; each lane picks the global chunk whose swizzled slot is its own.
+//
+// NN fragments come from ds_read_tr16_b64: within each 16-lane group, lane i
+// receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4j + i/4 (j = 0..3).  Pointing lane 4j + q at row k0 + j, columns
+// n0 + 4q .. n0 + 4q + 3 hands lane i the four k-values of column n0 + i:
+// two such reads (rows k0.., k0+4..) make one 8-deep MFMA operand.
+//
+// Pipeline per k-step of 32 (iteration `it`, stage it % S resident):
+//   fragments (it, 0) are in registers;  read fragments (it, 1);  MFMA (it, 0);
+//   wait until this wave's DMA for stage it+1 landed; s_barrier (all waves'
+//   DMA landed, and every wave is done reading stage it-1);  DMA stage
+//   it+S-1 into the slot of stage it-1;  read fragments (it+1, 0);  MFMA (it, 1).
+// __syncthreads() is not used inside the loop: its fence would wait for every
+// DMA in flight, including the stages being prefetched.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_, int S_, bool NN_>
+struct DmaTile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int BK = 32;
+  static constexpr int W = (BM / WM) * (BN / WN);
+  static constexpr int NT = W * kWave;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int P_BYTES = BM * 64;
+  static constexpr int Q_BYTES = NN_ ? BK * BN * 2 : BN * 64;
+  static constexpr int STAGE_BYTES = P_BYTES + Q_BYTES;
+  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static constexpr int P_DMA = P_BYTES / 1024 / W;   // DMA instructions per wave and stage
+  static constexpr int Q_DMA = Q_BYTES / 1024 / W;
+  static constexpr int D = P_DMA + Q_DMA;
+  static_assert(P_BYTES % (1024 * W) == 0 && Q_BYTES % (1024 * W) == 0, "DMA split");
+  static_assert(S >= 3 && D * (S - 3) <= 63, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4_t;
+
+__device__ __forceinline__ int krow_off(int r, int c) {  // k-contiguous rows, 64 B
+  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory to LDS bytes [lds_block + 16 * lane).
+// Written as inline asm so the compiler's wait-count pass does not see an LDS
+// write it cannot tell apart from the stage being read (it would then drain
+// every DMA in flight before each fragment read); ordering is explicit here:
+// wait_vm_barrier() is the only consumer-side synchronisation.
+// M0 is reserved by the compiler; these kernels contain no other M0 user (no
+// LDS-DMA builtins, no relative register indexing, no messages -- checked in
+// the generated assembly), so setting it here cannot disturb compiled code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, char* lds_block) {
+  // the block address is wave-uniform; readfirstlane puts it in an SGPR for M0
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_block)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ u32x4_t read_tr_pair(const char* base0, const char* base1) {
+  const lds_bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4_t*)base0);
+  const lds_bf16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4_t*)base1);
+  uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  u32x4_t r;
+  r.x = ua.x; r.y = ua.y; r.z = ub.x; r.w = ub.y;
+  return r;
+}
+
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
+  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
+  constexpr int FM = C_::FM, FN = C_::FN, W = C_::W, BK = C_::BK;
+  static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t batch = blockIdx.y;
+
+  int64_t tm, tn;
+  if (SYRK) {
+    const int64_t T_ = g.M / BM;
+    const int64_t t = xcd_remap(blockIdx.x, T_ * (T_ + 1) / 2);
+    int64_t ti = static_cast<int64_t>((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tm = ti;
+    tn = t - ti * (ti + 1) / 2;
+  } else {
+    const int64_t TM = g.M / BM, TN = g.N / BN;
+    const int64_t t = xcd_remap(blockIdx.x, TM * TN);
+    const int64_t per_group = int64_t(kGroupM) * TN;
+    const int64_t first_m = (t / per_group) * kGroupM;
+    const int64_t gsize = min(TM - first_m, int64_t(kGroupM));
+    const int64_t r = t % per_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+  }
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const bf16_t* P = static_cast<const bf16_t*>(g.P) + batch * g.strideP;
+  const bf16_t* Q = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ;
+
+  // ---- per-lane DMA sources (k offset added per stage) ----
+  // P (and NT Q): block b covers rows 16b..16b+15; lane -> row 16b + lane/4, slot lane%4
+  const bf16_t* p_src[C_::P_DMA];
+  int p_dst[C_::P_DMA];
+#pragma unroll
+  for (int i = 0; i < C_::P_DMA; ++i) {
+    const int b = wave * C_::P_DMA + i;
+    const int r = 16 * b + (lane >> 2);
+    const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    p_src[i] = P + (m0 + r) * g.K + c * 8;
+    p_dst[i] = b * 1024;
+  }
+  const bf16_t* q_src[C_::Q_DMA];
+  int q_dst[C_::Q_DMA];
+#pragma unroll
+  for (int i = 0; i < C_::Q_DMA; ++i) {
+    const int b = wave * C_::Q_DMA + i;
+    if (!NN) {
+      const int r = 16 * b + (lane >> 2);
+      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+      q_src[i] = Q + (n0 + r) * g.K + c * 8;
+    } else {
+      constexpr int ROW_CHUNKS = BN / 8;           // 16-byte chunks per k-row
+      constexpr int ROWS_PER_BLOCK = 64 / ROW_CHUNKS;
+      const int r = ROWS_PER_BLOCK * b + lane / ROW_CHUNKS;
+      const int c = (lane % ROW_CHUNKS) ^ (2 * (r & 3));
+      q_src[i] = Q + int64_t(r) * g.N + n0 + c * 8;
+    }
+    q_dst[i] = C_::P_BYTES + b * 1024;
+  }
+
+  auto issue_stage = [&](int64_t kt) {
+    char* st = lds + (kt % S) * C_::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C_::P_DMA; ++i) dma16(p_src[i] + kt * BK, st + p_dst[i]);
+#pragma unroll
+    for (int i = 0; i < C_::Q_DMA; ++i)
+      dma16(NN ? q_src[i] + kt * BK * g.N : q_src[i] + kt * BK, st + q_dst[i]);
+  };
+
+  const int wm0 = (wave / (BN / WN)) * WM;
+  const int wn0 = (wave % (BN / WN)) * WN;
+  const int frow = lane & 31, fgrp = lane >> 5;
+
+  // fragment addresses (bytes within a stage) for k-step ks of the stage
+  auto read_frags = [&](const char* st, int ks, u32x4_t (&fa)[FM], u32x4_t (&fb)[FN]) {
+    const int chunk = 2 * ks + fgrp;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *reinterpret_cast<const u32x4_t*>(st + krow_off(wm0 + i * 32 + frow, chunk));
+    if (!NN) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(st + C_::P_BYTES + krow_off(wn0 + j * 32 + frow, chunk));
+    } else {
+      const int gi = lane & 15, G = lane >> 4;
+      const int k0 = ks * 16 + 8 * (G >> 1) + (gi >> 2);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn0 + j * 32 + 16 * (G & 1) + 4 * (gi & 3);   // first of 4 columns
+        const int c = col >> 3, half = (col & 7) * 2;                    // chunk, byte in chunk
+        const char* b0 = st + C_::P_BYTES + k0 * (BN * 2) + ((c ^ (2 * (k0 & 3))) << 4) + half;
+        const int k1 = k0 + 4;
+        const char* b1 = st + C_::P_BYTES + k1 * (BN * 2) + ((c ^ (2 * (k1 & 3))) << 4) + half;
+        fb[j] = read_tr_pair(b0, b1);
+      }
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int64_t KT = g.K / BK;
+  // prologue: stages 0 .. S-2 in flight, stage 0 resident
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue_stage(s);
+  if (KT >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
+  else wait_vm_barrier<0>();
+
+  u32x4_t fa[2][FM], fb[2][FN];
+  auto mma_all = [&](const u32x4_t (&a)[FM], const u32x4_t (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mfma<bf16_t>::mma(a[i], b[j], acc[i][j]);
+  };
+  read_frags(lds, 0, fa[0], fb[0]);
+  int64_t it = 0;
+  // steady state (branch-free, so the compiler's LDS wait counts stay exact):
+  // stages it+1 .. it+S-2 are in flight on entry, stage it+S-1 is issued here
+  for (; it < KT - (S - 1); ++it) {
+    read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
+    mma_all(fa[0], fb[0]);
+    wait_vm_barrier<C_::D * (S - 3)>();
+    issue_stage(it + S - 1);
+    read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
+    mma_all(fa[1], fb[1]);
+  }
+  // drain: nothing left to issue
+  for (; it < KT; ++it) {
+    read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
+    mma_all(fa[0], fb[0]);
+    if (it + 1 < KT) {
+      wait_vm_barrier<0>();
+      read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
+    }
+    mma_all(fa[1], fb[1]);
+  }
+
+  // ---- epilogue (same layout rules as gemm_kernel) ----
+  bf16_t* C = static_cast<bf16_t*>(g.C) + batch * g.strideC;
+  const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
+  const bool mirror = SYRK && (tm != tn);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn0 + j * 32 + frow;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row0 = m0 + wm0 + i * 32 + 8 * q + 4 * fgrp;
+        float out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[i][j][4 * q + r] * g.alpha;
+          if (EPI != EPI_STORE) v = fmaf(g.beta, bf16_to_f32(Z[(row0 + r) * g.N + col]), v);
+          out[r] = v;
+        }
+        if (EPI == EPI_FINAL) {
+          if (col < g.l_valid) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t row = row0 + r;
+              if (row < g.s_valid) {
+                const int64_t idx = g.transpose_out ? col * g.s_valid + row : row * g.l_valid + col;
+                if (g.u_dtype == MUON_BF16)
+                  static_cast<bf16_t*>(g.U)[batch * g.strideU + idx] = f32_to_bf16(out[r]);
+                else
+                  static_cast<float*>(g.U)[batch * g.strideU + idx] = out[r];
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = f32_to_bf16(out[r]);
+          if (mirror) {
+            bf16_t* dst = C + col * g.N + row0;
+            const uint32_t w0 = uint32_t(f32_to_bf16(out[0])) | (uint32_t(f32_to_bf16(out[1])) << 16);
+            const uint32_t w1 = uint32_t(f32_to_bf16(out[2])) | (uint32_t(f32_to_bf16(out[3])) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st);
+
+// Number of workgroups of one batch entry.
+template <int BM, int BN, bool SYRK>
+inline int64_t tiles_of(const GemmArgs& g) {
+  if (SYRK) {
+    const int64_t t = g.M / BM;
+    return t * (t + 1) / 2;
+  }
+  return (g.M / BM) * (g.N / BN);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
+int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  using C_ = Tile<T, BM, BN, WM, WN>;
+  const int64_t blocks = tiles_of<BM, BN, SYRK>(g);
+  if (blocks == 0 || batch == 0) return MUON_OK;
+  auto kern = gemm_kernel<T, BM, BN, WM, WN, SYRK, NN, EPI>;
+  static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
+  if (!configured) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C_::LDS_BYTES) != hipSuccess)
+      return MUON_ELAUNCH;
+    configured = true;
+  }
+  kern<<<dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  return launch_status();
+}
+
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
+  const int64_t blocks = tiles_of<BM, BN, SYRK>(g);
+  if (blocks == 0 || batch == 0) return MUON_OK;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
+  static bool configured = false;
+  if (!configured) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C_::LDS_BYTES) != hipSuccess)
+      return MUON_ELAUNCH;
+    configured = true;
+  }
+  kern<<<dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  return launch_status();
+}
+
+}  // namespace gemm
+}  // namespace muon

@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "common.h"
+#include "gemm.h"
 
 namespace muon {
 
@@ -34,282 +35,10 @@ int sumsq_strided(const void* M, int m_dtype, int64_t len, int64_t count, int64_
 
 namespace {
 
-constexpr int kRowBytes = 128;  // one LDS tile row = 128 bytes along k
-
-// ---------------------------------------------------------------------------
-// Matrix-core step for one 16-byte fragment per lane and operand.
-// Lane l supplies row/column (l % 32); lanes 0-31 and 32-63 hold two
-// disjoint k-groups.  A and B use the same k placement, so every k of the
-// chunk is contracted exactly once.
-// ---------------------------------------------------------------------------
-template <typename T> struct Mfma;
-template <> struct Mfma<bf16_t> {
-  static constexpr int kElems = 8;   // elements per 16 bytes
-  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-};
-template <> struct Mfma<float> {
-  static constexpr int kElems = 4;
-  __device__ __forceinline__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
-  }
-};
-
-// byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
-
-struct GemmArgs {
-  const void* P;  // rows of the left operand, k-contiguous, ld = K
-  const void* Q;  // NT: rows of the right operand (k-contiguous, ld = K); NN: [K][N]
-  const void* Z;  // epilogue addend [M][N] (ld = N), may be null
-  void* C;        // output [M][N] (ld = N)
-  int64_t M, N, K;
-  int64_t strideP, strideQ, strideZ, strideC;  // batch strides (elements)
-  float alpha, beta;                           // C = alpha*acc + beta*Z
-  // EPI_FINAL: write U instead of C, un-padded (s_valid x l_valid of the
-  // working layout) and transposed back when the momentum was tall.
-  void* U;
-  int64_t strideU;
-  int64_t s_valid, l_valid;
-  int u_dtype;
-  int transpose_out;
-};
-
-template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
-struct Gemm {
-  static constexpr int E = Mfma<T>::kElems;
-  static constexpr int BK = kRowBytes / sizeof(T);   // k per LDS tile
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int NT = WAVES_M * WAVES_N * kWave;
-  static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 fragments per wave
-  static constexpr int KSTEPS = BK / (2 * E);        // fragment reads per LDS tile
-  // k-contiguous loads: 8 chunks per row
-  static constexpr int A_CHUNKS = BM * 8 / NT;
-  static constexpr int B_CHUNKS = BN * 8 / NT;
-  // NN loads: E x E blocks, (BK/E) x (BN/E) of them
-  static constexpr int NN_BLOCKS = (BK / E) * (BN / E);
-  static constexpr int NN_PER_T = (NN_BLOCKS + NT - 1) / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads mismatch");
-  static_assert(!SYRK || BM == BN, "symmetric products need square tiles");
-  static constexpr int LDS_BYTES = (BM + BN) * kRowBytes;
-};
-
-template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs g) {
-  using Cfg = Gemm<T, BM, BN, WM, WN, SYRK, NN, EPI>;
-  constexpr int E = Cfg::E, BK = Cfg::BK, NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  char* ldsA = lds;
-  char* ldsB = lds + BM * kRowBytes;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t batch = blockIdx.y;
-
-  // ---- tile coordinates ----
-  int64_t tm, tn;
-  if (SYRK) {
-    // lower triangle: block t -> (ti, tj), ti >= tj
-    const int64_t t = blockIdx.x;
-    int64_t ti = static_cast<int64_t>((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    while (ti * (ti + 1) / 2 > t) --ti;
-    tm = ti;
-    tn = t - ti * (ti + 1) / 2;
-  } else {
-    const int64_t tiles_m = g.M / BM;
-    tm = blockIdx.x % tiles_m;
-    tn = blockIdx.x / tiles_m;
-  }
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-
-  const T* P = static_cast<const T*>(g.P) + batch * g.strideP;
-  const T* Q = static_cast<const T*>(g.Q) + batch * g.strideQ;
-
-  // ---- global -> register staging ----
-  u32x4_t ra[Cfg::A_CHUNKS];
-  u32x4_t rb[NN ? Cfg::NN_PER_T * E : Cfg::B_CHUNKS];
-
-  auto load_tiles = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      const int row = c >> 3, kc = c & 7;
-      ra[i] = *reinterpret_cast<const u32x4_t*>(P + (m0 + row) * g.K + k0 + kc * E);
-    }
-    if (!NN) {
-#pragma unroll
-      for (int i = 0; i < Cfg::B_CHUNKS; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 3, kc = c & 7;
-        rb[i] = *reinterpret_cast<const u32x4_t*>(Q + (n0 + row) * g.K + k0 + kc * E);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Cfg::NN_PER_T; ++i) {
-        const int blk = tid + i * NT;
-        if (blk < Cfg::NN_BLOCKS) {
-          const int nb = blk % (BN / E), kb = blk / (BN / E);
-#pragma unroll
-          for (int r = 0; r < E; ++r)
-            rb[i * E + r] = *reinterpret_cast<const u32x4_t*>(Q + (k0 + kb * E + r) * g.N + n0 + nb * E);
-        }
-      }
-    }
-  };
-
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_CHUNKS; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(ldsA + lds_off(c >> 3, c & 7)) = ra[i];
-    }
-    if (!NN) {
-#pragma unroll
-      for (int i = 0; i < Cfg::B_CHUNKS; ++i) {
-        const int c = tid + i * NT;
-        *reinterpret_cast<u32x4_t*>(ldsB + lds_off(c >> 3, c & 7)) = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Cfg::NN_PER_T; ++i) {
-        const int blk = tid + i * NT;
-        if (blk < Cfg::NN_BLOCKS) {
-          const int nb = blk % (BN / E), kb = blk / (BN / E);
-          const u32x4_t* in = rb + i * E;
-          if (sizeof(T) == 2) {
-            // in[r] holds k = kb*8 + r for n = nb*8 + 0..7 (two per dword);
-            // column e of the 8x8 block becomes the 8 k-values of row n.
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int d = e >> 1;
-              u32x4_t o;
-              uint32_t w[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = in[2 * j][d], hi = in[2 * j + 1][d];
-                w[j] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                               : ((lo & 0xffffu) | (hi << 16));
-              }
-              o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
-              *reinterpret_cast<u32x4_t*>(ldsB + lds_off(nb * 8 + e, kb)) = o;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              u32x4_t o;
-              o.x = in[0][e]; o.y = in[1][e]; o.z = in[2][e]; o.w = in[3][e];
-              *reinterpret_cast<u32x4_t*>(ldsB + lds_off(nb * 4 + e, kb)) = o;
-            }
-          }
-        }
-      }
-    }
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int wm0 = (wave / Cfg::WAVES_N) * WM;
-  const int wn0 = (wave % Cfg::WAVES_N) * WN;
-  const int frow = lane & 31, fgrp = lane >> 5;
-
-  const int64_t KT = g.K / BK;
-  load_tiles(0);
-  store_tiles();
-  __syncthreads();
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) load_tiles((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
-      const int chunk = ks * 2 + fgrp;
-      u32x4_t fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4_t*>(ldsA + lds_off(wm0 + i * 32 + frow, chunk));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4_t*>(ldsB + lds_off(wn0 + j * 32 + frow, chunk));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
-    }
-    __syncthreads();
-    if (kt + 1 < KT) {
-      store_tiles();
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue ----
-  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) +
-  // (v%4), column l%32 of the fragment.
-  T* C = static_cast<T*>(g.C) + batch * g.strideC;
-  const T* Z = static_cast<const T*>(g.Z) + batch * g.strideZ;
-  const bool mirror = SYRK && (tm != tn);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn0 + j * 32 + frow;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row0 = m0 + wm0 + i * 32 + 8 * q + 4 * fgrp;
-        float out[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[i][j][4 * q + r] * g.alpha;
-          if (EPI != EPI_STORE) v = fmaf(g.beta, to_f32(Z[(row0 + r) * g.N + col]), v);
-          out[r] = v;
-        }
-        if (EPI == EPI_FINAL) {
-          if (col < g.l_valid) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t row = row0 + r;
-              if (row < g.s_valid) {
-                const int64_t idx = g.transpose_out ? col * g.s_valid + row : row * g.l_valid + col;
-                if (g.u_dtype == MUON_BF16)
-                  static_cast<bf16_t*>(g.U)[batch * g.strideU + idx] = f32_to_bf16(out[r]);
-                else
-                  static_cast<float*>(g.U)[batch * g.strideU + idx] = out[r];
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = from_f32<T>(out[r]);
-          if (mirror) {
-            // the four consecutive rows are four consecutive entries of row `col`
-            T* dst = C + col * g.N + row0;
-            if (sizeof(T) == 2) {
-              const uint32_t w0 = uint32_t(from_f32<bf16_t>(out[0])) | (uint32_t(from_f32<bf16_t>(out[1])) << 16);
-              const uint32_t w1 = uint32_t(from_f32<bf16_t>(out[2])) | (uint32_t(from_f32<bf16_t>(out[3])) << 16);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
-            }
-          }
-        }
-      }
-    }
-  }
-}
+using gemm::EPI_AXPBY;
+using gemm::EPI_FINAL;
+using gemm::EPI_STORE;
+using gemm::GemmArgs;
 
 // ---------------------------------------------------------------------------
 // a2: X0 = pad(orient(M)) * scale, scale = 1/sqrt(sumsq) (0 for a zero matrix).
@@ -361,22 +90,20 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kWM = 64, kWN = 64;
-
+// bf16 products run the DMA-pipelined kernel with a 4-stage LDS ring.  Tile
+// choice (measured on MI355X): 256 x 256 tiles (8 waves of 128 x 64) for the
+// symmetric products and for long contractions (K >= 2048); 128 x 128 tiles
+// (4 waves of 64 x 64) for short ones, where prologue and epilogue weigh more.
+// fp32 products (small, latency-bound workloads) use the register-staged kernel.
 template <typename T, bool SYRK, bool NN, int EPI>
 int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
-  using Cfg = Gemm<T, kBM, kBN, kWM, kWN, SYRK, NN, EPI>;
-  int64_t blocks;
-  if (SYRK) {
-    const int64_t t = g.M / kBM;
-    blocks = t * (t + 1) / 2;
+  const bool big = SYRK || g.K >= 2048;
+  if constexpr (sizeof(T) == 2) {
+    if (big) return gemm::launch_dma<256, 256, 128, 64, 4, SYRK, NN, EPI>(g, batch, st);
+    return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st);
   } else {
-    blocks = (g.M / kBM) * (g.N / kBN);
+    return gemm::launch<T, 128, 128, 64, 64, SYRK, NN, EPI>(g, batch, st);
   }
-  if (blocks == 0 || batch == 0) return MUON_OK;
-  gemm_kernel<T, kBM, kBN, kWM, kWN, SYRK, NN, EPI>
-      <<<dim3(blocks, batch), dim3(Cfg::NT), 0, st>>>(g);
-  return launch_status();
 }
 
 template <typename T>

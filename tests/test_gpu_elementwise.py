@@ -1,7 +1,8 @@
 """GPU parity of the HBM-bound stages against the CPU oracle.
 
-a1 momentum: stored values within 1 ulp of the storage type (fp32 fma vs
-fp64 then one rounding), per-matrix sums of squares within 1e-5 relative;
+a1 momentum: stored values bit-exact (exact products, one fp64 rounding,
+then storage rounding on both sides), per-matrix sums of squares within
+1e-5 relative;
 a6 sign/pack, a7 vote and a8 update: bit-exact.  All through the C ABI.
 """
 import numpy as np
@@ -25,7 +26,7 @@ def _momentum_case(numel, offsets, m_dtype, g_dtype, beta, alpha, seed):
     mao.muon_momentum(Md, Gd, beta, alpha, offs, sums)
     got = from_dev(Md)
     ref = O.momentum(M, m_dtype, G, g_dtype, beta, alpha)
-    assert ulp_distance(got, ref, m_dtype).max(initial=0) <= 1
+    assert ulp_distance(got, ref, m_dtype).max(initial=0) == 0
     ref_s = O.segment_sumsq(O.decode(got, m_dtype), offsets)
     s = from_dev(sums).astype(np.float64)
     assert np.all(np.abs(s - ref_s) <= 1e-5 * np.maximum(ref_s, 1e-30)), (s, ref_s)
