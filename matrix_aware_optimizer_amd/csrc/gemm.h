@@ -36,6 +36,9 @@ namespace gemm {
 
 constexpr int kRowBytes = 128;
 constexpr int kXcds = 8;
+#ifndef MUON_GEMM_INTERLEAVE
+#define MUON_GEMM_INTERLEAVE 1
+#endif
 constexpr int kGroupM = 8;
 
 template <typename T> struct Mfma;
@@ -376,7 +379,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// 16 bytes per lane from global memory to LDS bytes [lds_block + 16 * lane).
+// 16 bytes per lane from global memory to LDS bytes [lds_addr + 16 * lane).
 // Written as inline asm so the compiler's wait-count pass does not see an LDS
 // write it cannot tell apart from the stage being read (it would then drain
 // every DMA in flight before each fragment read); ordering is explicit here:
@@ -386,11 +389,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // the generated assembly), so setting it here cannot disturb compiled code.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, char* lds_block) {
-  // the block address is wave-uniform; readfirstlane puts it in an SGPR for M0
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_block)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -404,21 +405,12 @@ __device__ __forceinline__ u32x4_t read_tr_pair(const char* base0, const char* b
   return r;
 }
 
-template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
-  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
-  constexpr int FM = C_::FM, FN = C_::FN, W = C_::W, BK = C_::BK;
-  static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t batch = blockIdx.y;
-
-  int64_t tm, tn;
+// tile index within one batch entry -> (tile row, tile column): the lower
+// triangle for symmetric products, else groups of kGroupM tile rows walked
+// column by column
+template <int BM, int BN, bool SYRK>
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t t, int64_t& tm, int64_t& tn) {
   if (SYRK) {
-    const int64_t T_ = g.M / BM;
-    const int64_t t = xcd_remap(blockIdx.x, T_ * (T_ + 1) / 2);
     int64_t ti = static_cast<int64_t>((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
     while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
     while (ti * (ti + 1) / 2 > t) --ti;
@@ -426,7 +418,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     tn = t - ti * (ti + 1) / 2;
   } else {
     const int64_t TM = g.M / BM, TN = g.N / BN;
-    const int64_t t = xcd_remap(blockIdx.x, TM * TN);
     const int64_t per_group = int64_t(kGroupM) * TN;
     const int64_t first_m = (t / per_group) * kGroupM;
     const int64_t gsize = min(TM - first_m, int64_t(kGroupM));
@@ -434,55 +425,69 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     tm = first_m + r % gsize;
     tn = r / gsize;
   }
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const bf16_t* P = static_cast<const bf16_t*>(g.P) + batch * g.strideP;
-  const bf16_t* Q = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ;
+}
 
-  // ---- per-lane DMA sources (k offset added per stage) ----
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
+  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
+  constexpr int FM = C_::FM, FN = C_::FN, BK = C_::BK;
+  static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps DMA addresses scalar
+  const int wm0 = (wave / (BN / WN)) * WM;
+  const int wn0 = (wave % (BN / WN)) * WN;
+  const int frow = lane & 31, fgrp = lane >> 5;
+  const int64_t batch = blockIdx.y;
+  const int64_t KT = g.K / BK;
+
+  int64_t tm, tn;
+  const int64_t tiles = SYRK ? (g.M / BM) * (g.M / BM + 1) / 2 : (g.M / BM) * (g.N / BN);
+  tile_coords<BM, BN, SYRK>(g, xcd_remap(blockIdx.x, tiles), tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  // ---- DMA sources: tile origin plus a 32-bit per-lane offset (elements) ----
+  const bf16_t* Pt = static_cast<const bf16_t*>(g.P) + batch * g.strideP + m0 * g.K;
+  const bf16_t* Qt = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ + (NN ? n0 : n0 * g.K);
   // P (and NT Q): block b covers rows 16b..16b+15; lane -> row 16b + lane/4, slot lane%4
-  const bf16_t* p_src[C_::P_DMA];
-  int p_dst[C_::P_DMA];
+  uint32_t p_off[C_::P_DMA], q_off[C_::Q_DMA];
 #pragma unroll
   for (int i = 0; i < C_::P_DMA; ++i) {
-    const int b = wave * C_::P_DMA + i;
-    const int r = 16 * b + (lane >> 2);
+    const int r = 16 * (wave * C_::P_DMA + i) + (lane >> 2);
     const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
-    p_src[i] = P + (m0 + r) * g.K + c * 8;
-    p_dst[i] = b * 1024;
+    p_off[i] = uint32_t(r) * uint32_t(g.K) + c * 8;
   }
-  const bf16_t* q_src[C_::Q_DMA];
-  int q_dst[C_::Q_DMA];
 #pragma unroll
   for (int i = 0; i < C_::Q_DMA; ++i) {
     const int b = wave * C_::Q_DMA + i;
     if (!NN) {
       const int r = 16 * b + (lane >> 2);
       const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
-      q_src[i] = Q + (n0 + r) * g.K + c * 8;
+      q_off[i] = uint32_t(r) * uint32_t(g.K) + c * 8;
     } else {
       constexpr int ROW_CHUNKS = BN / 8;           // 16-byte chunks per k-row
       constexpr int ROWS_PER_BLOCK = 64 / ROW_CHUNKS;
       const int r = ROWS_PER_BLOCK * b + lane / ROW_CHUNKS;
       const int c = (lane % ROW_CHUNKS) ^ (2 * (r & 3));
-      q_src[i] = Q + int64_t(r) * g.N + n0 + c * 8;
+      q_off[i] = uint32_t(r) * uint32_t(g.N) + c * 8;
     }
-    q_dst[i] = C_::P_BYTES + b * 1024;
   }
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
   auto issue_stage = [&](int64_t kt) {
-    char* st = lds + (kt % S) * C_::STAGE_BYTES;
+    const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
+    const bf16_t* pk = Pt + kt * BK;
+    const bf16_t* qk = NN ? Qt + kt * BK * g.N : Qt + kt * BK;
 #pragma unroll
-    for (int i = 0; i < C_::P_DMA; ++i) dma16(p_src[i] + kt * BK, st + p_dst[i]);
+    for (int q = 0; q < C_::P_DMA; ++q) dma16(pk + p_off[q], st + (wave * C_::P_DMA + q) * 1024);
 #pragma unroll
-    for (int i = 0; i < C_::Q_DMA; ++i)
-      dma16(NN ? q_src[i] + kt * BK * g.N : q_src[i] + kt * BK, st + q_dst[i]);
+    for (int q = 0; q < C_::Q_DMA; ++q)
+      dma16(qk + q_off[q], st + C_::P_BYTES + (wave * C_::Q_DMA + q) * 1024);
   };
 
-  const int wm0 = (wave / (BN / WN)) * WM;
-  const int wn0 = (wave % (BN / WN)) * WN;
-  const int frow = lane & 31, fgrp = lane >> 5;
-
-  // fragment addresses (bytes within a stage) for k-step ks of the stage
   auto read_frags = [&](const char* st, int ks, u32x4_t (&fa)[FM], u32x4_t (&fb)[FN]) {
     const int chunk = 2 * ks + fgrp;
 #pragma unroll
@@ -514,15 +519,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int64_t KT = g.K / BK;
-  // prologue: stages 0 .. S-2 in flight, stage 0 resident
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue_stage(s);
-  if (KT >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
-  else wait_vm_barrier<0>();
-
   u32x4_t fa[2][FM], fb[2][FN];
   auto mma_all = [&](const u32x4_t (&a)[FM], const u32x4_t (&b)[FN]) {
 #pragma unroll
@@ -530,6 +526,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
       for (int j = 0; j < FN; ++j) Mfma<bf16_t>::mma(a[i], b[j], acc[i][j]);
   };
+
+  // Ask the scheduler to alternate one LDS fragment read with one MFMA, so
+  // the reads for the next k-step run under the current MFMAs.
+  auto interleave = [&]() {
+    constexpr int NDS = FM + (NN ? 2 * FN : FN), NMF = FM * FN;
+#if MUON_GEMM_INTERLEAVE == 1
+#pragma unroll
+    for (int i = 0; i < (NDS > NMF ? NDS : NMF); ++i) {
+      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#elif MUON_GEMM_INTERLEAVE == 2
+    // two reads per MFMA over the first MFMAs, then MFMAs only, so the last
+    // reads have several MFMAs' time to land before the next k-step uses them
+    static_assert(NDS % 2 == 0, "reads come in pairs");
+    constexpr int PAIRS = NDS / 2;
+#pragma unroll
+    for (int i = 0; i < PAIRS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+#endif
+  };
+
+  // prologue: stages 0 .. S-2 in flight, stage 0 resident
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue_stage(s);
+  if (KT >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
+  else wait_vm_barrier<0>();
   read_frags(lds, 0, fa[0], fb[0]);
   int64_t it = 0;
   // steady state (branch-free, so the compiler's LDS wait counts stay exact):
@@ -537,10 +564,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   for (; it < KT - (S - 1); ++it) {
     read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
+    interleave();
     wait_vm_barrier<C_::D * (S - 3)>();
     issue_stage(it + S - 1);
     read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
     mma_all(fa[1], fb[1]);
+    interleave();
   }
   // drain: nothing left to issue
   for (; it < KT; ++it) {
@@ -553,7 +582,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     mma_all(fa[1], fb[1]);
   }
 
-  // ---- epilogue (same layout rules as gemm_kernel) ----
+  // ---- epilogue ----
+  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) +
+  // (v%4), column l%32 of the fragment.
   bf16_t* C = static_cast<bf16_t*>(g.C) + batch * g.strideC;
   const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
   const bool mirror = SYRK && (tm != tn);
@@ -590,19 +621,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
           for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = f32_to_bf16(out[r]);
           if (mirror) {
-            bf16_t* dst = C + col * g.N + row0;
+            // the four consecutive rows are four consecutive entries of row `col`
             const uint32_t w0 = uint32_t(f32_to_bf16(out[0])) | (uint32_t(f32_to_bf16(out[1])) << 16);
             const uint32_t w1 = uint32_t(f32_to_bf16(out[2])) | (uint32_t(f32_to_bf16(out[3])) << 16);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(C + col * g.N + row0) = make_uint2(w0, w1);
           }
         }
       }
     }
   }
 }
-
-template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
-int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st);
 
 // Number of workgroups of one batch entry.
 template <int BM, int BN, bool SYRK>
@@ -631,20 +659,26 @@ int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
   return launch_status();
 }
 
-template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
-int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st) {
-  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
-  const int64_t blocks = tiles_of<BM, BN, SYRK>(g);
-  if (blocks == 0 || batch == 0) return MUON_OK;
-  auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
-  static bool configured = false;
+template <typename K>
+int set_lds_limit(K kern, int bytes, bool& configured) {
   if (!configured) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C_::LDS_BYTES) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
       return MUON_ELAUNCH;
     configured = true;
   }
-  kern<<<dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  return MUON_OK;
+}
+
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
+  const int64_t tpb = tiles_of<BM, BN, SYRK>(g);
+  if (tpb == 0 || batch == 0) return MUON_OK;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
+  static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
+  if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
+  kern<<<dim3(tpb, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
   return launch_status();
 }
 

@@ -91,15 +91,16 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // Launch helpers
 // ---------------------------------------------------------------------------
 // bf16 products run the DMA-pipelined kernel with a 4-stage LDS ring.  Tile
-// choice (measured on MI355X): 256 x 256 tiles (8 waves of 128 x 64) for the
-// symmetric products and for long contractions (K >= 2048); 128 x 128 tiles
-// (4 waves of 64 x 64) for short ones, where prologue and epilogue weigh more.
-// fp32 products (small, latency-bound workloads) use the register-staged kernel.
+// choice (measured on MI355X): 256 x 256 tiles of 8 waves (64 x 128 each) for
+// the symmetric products and for long contractions (K >= 2048); 128 x 128
+// tiles (4 waves of 64 x 64) for short ones, where prologue and epilogue
+// weigh more.  fp32 products (small, latency-bound workloads) use the
+// register-staged kernel.
 template <typename T, bool SYRK, bool NN, int EPI>
 int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
   const bool big = SYRK || g.K >= 2048;
   if constexpr (sizeof(T) == 2) {
-    if (big) return gemm::launch_dma<256, 256, 128, 64, 4, SYRK, NN, EPI>(g, batch, st);
+    if (big) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st);
     return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st);
   } else {
     return gemm::launch<T, 128, 128, 64, 64, SYRK, NN, EPI>(g, batch, st);

@@ -105,7 +105,8 @@ def _problems(specs):
 def _ns_bytes(count, s, l, es=2, sumsq=True, part=0):
     def up(x):
         return -(-x // 256) * 256
-    return 2 * up(count * s * l * es) + 2 * up(count * s * s * es) + (0 if sumsq else up(4 * count)) + up(part)
+    return (2 * up(count * s * l * es) + 2 * up(count * s * s * es) + (0 if sumsq else up(4 * count))
+            + up(part))
 
 
 def test_ns_workspace_single_and_padding(L):

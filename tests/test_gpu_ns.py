@@ -70,7 +70,7 @@ def test_poly(prec, coeffs, batch, s, sv):
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 @pytest.mark.parametrize("a,alpha", [(QUINTIC[0], 1.0), (1.5, -0.5)])
 @pytest.mark.parametrize("batch,s,l,sv,lv", [(1, 256, 256, 256, 256), (2, 256, 768, 200, 700),
-                                              (1, 512, 1536, 512, 1536)])
+                                              (1, 512, 1536, 512, 1536), (1, 2048, 2560, 2000, 2500)])
 def test_apply(prec, a, alpha, batch, s, l, sv, lv):
     Xs, X = _stage_X(batch, s, l, sv, lv, prec, 3)
     Bm = np.zeros((batch, s, s))
@@ -206,7 +206,7 @@ def test_ns_bf16_ill_conditioned_spectrum_bound():
 
 @pytest.mark.parametrize("kind,batch,s,l", [("gram", 16, 2048, 2048), ("poly", 16, 2048, 2048),
                                              ("apply", 16, 1024, 2048), ("apply", 3, 2048, 2304),
-                                             ("gram", 1, 4096, 4096)])
+                                             ("gram", 1, 4096, 4096), ("apply", 1, 4096, 14336)])
 def test_stages_at_large_tile_sizes(kind, batch, s, l):
     """Stage shapes that take the 256 x 256-tile kernels (symmetric products, or B X with
     a contraction of 2048 or more) next to ones that take the 128 x 128 tiles."""
