@@ -39,6 +39,9 @@ constexpr int kXcds = 8;
 #ifndef MUON_GEMM_INTERLEAVE
 #define MUON_GEMM_INTERLEAVE 1
 #endif
+#ifndef MUON_GEMM_LGKM_SPLIT
+#define MUON_GEMM_LGKM_SPLIT 1
+#endif
 constexpr int kGroupM = 8;
 
 template <typename T> struct Mfma;
@@ -324,12 +327,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 // bf16 kernel with global -> LDS DMA (global_load_lds_dwordx4) and an
 // S-stage LDS ring.  k advances 32 at a time (two 32x32x16 MFMA steps).
 //
-// LDS layouts (16-byte chunks, XOR-swizzled so every access pattern below is
-// free of bank conflicts):
+// LDS layouts (16-byte chunks, XOR-swizzled; both chosen by measuring the
+// SQ_LDS_BANK_CONFLICT counter on MI355X for the exact access patterns below,
+// where they read zero conflicts):
 //  * k-contiguous operand rows (P, and Q for NT): 64 bytes = 4 chunks per
-//    row; chunk c of row r sits at slot c ^ (((r >> 1) ^ (r >> 3)) & 3).
+//    row; chunk c of row r sits at slot c ^ ((r >> 2) & 3).
 //  * k-major Q tile for NN ([k][n], n contiguous): rows of 2*BN bytes; chunk
-//    c of row r sits at slot c ^ (2 * (r & 3)).
+//    c of row r sits at slot c ^ (4 * (r & 3)), so the four rows one
+//    transposing read touches are 64 bytes apart within 256 bytes.
 // One DMA instruction moves 1 KB (64 lanes x 16 bytes) to consecutive LDS
 // bytes; each lane picks the global chunk whose swizzled slot is its own.
 //
@@ -357,7 +362,12 @@ struct DmaTile {
   static constexpr int P_BYTES = BM * 64;
   static constexpr int Q_BYTES = NN_ ? BK * BN * 2 : BN * 64;
   static constexpr int STAGE_BYTES = P_BYTES + Q_BYTES;
-  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  // epilogue staging: per wave one 32-row slab of fp32 accumulators; the row
+  // pitch WN + 8 floats puts the two half-waves' rows 128 bytes apart in the
+  // banks
+  static constexpr int LDW = WN + 8;
+  static constexpr int EPI_BYTES = W * 32 * LDW * 4;
+  static constexpr int LDS_BYTES = (S * STAGE_BYTES > EPI_BYTES) ? S * STAGE_BYTES : EPI_BYTES;
   static constexpr int P_DMA = P_BYTES / 1024 / W;   // DMA instructions per wave and stage
   static constexpr int Q_DMA = Q_BYTES / 1024 / W;
   static constexpr int D = P_DMA + Q_DMA;
@@ -371,7 +381,19 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4_t;
 
 __device__ __forceinline__ int krow_off(int r, int c) {  // k-contiguous rows, 64 B
-  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+// slot of chunk c in row k of the [k][n] tile
+__device__ __forceinline__ int nrow_slot(int c, int k) { return c ^ (4 * (k & 3)); }
+
+// Wait for every LDS read of this wave (s_waitcnt lgkmcnt(0), vmcnt and
+// expcnt left open).  Placed where the reads it covers were issued a whole
+// k-step earlier, it costs nothing and keeps the compiler from placing a
+// conservative wait after the next, freshly issued reads.
+__device__ __forceinline__ void lds_reads_done() {
+#if MUON_GEMM_LGKM_SPLIT
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+#endif
 }
 
 template <int N>
@@ -456,7 +478,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
   for (int i = 0; i < C_::P_DMA; ++i) {
     const int r = 16 * (wave * C_::P_DMA + i) + (lane >> 2);
-    const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     p_off[i] = uint32_t(r) * uint32_t(g.K) + c * 8;
   }
 #pragma unroll
@@ -464,13 +486,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     const int b = wave * C_::Q_DMA + i;
     if (!NN) {
       const int r = 16 * b + (lane >> 2);
-      const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
       q_off[i] = uint32_t(r) * uint32_t(g.K) + c * 8;
     } else {
       constexpr int ROW_CHUNKS = BN / 8;           // 16-byte chunks per k-row
       constexpr int ROWS_PER_BLOCK = 64 / ROW_CHUNKS;
       const int r = ROWS_PER_BLOCK * b + lane / ROW_CHUNKS;
-      const int c = (lane % ROW_CHUNKS) ^ (2 * (r & 3));
+      const int c = nrow_slot(lane % ROW_CHUNKS, r);   // the slot is an involution
       q_off[i] = uint32_t(r) * uint32_t(g.N) + c * 8;
     }
   }
@@ -504,9 +526,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
       for (int j = 0; j < FN; ++j) {
         const int col = wn0 + j * 32 + 16 * (G & 1) + 4 * (gi & 3);   // first of 4 columns
         const int c = col >> 3, half = (col & 7) * 2;                    // chunk, byte in chunk
-        const char* b0 = st + C_::P_BYTES + k0 * (BN * 2) + ((c ^ (2 * (k0 & 3))) << 4) + half;
+        const char* b0 = st + C_::P_BYTES + k0 * (BN * 2) + (nrow_slot(c, k0) << 4) + half;
         const int k1 = k0 + 4;
-        const char* b1 = st + C_::P_BYTES + k1 * (BN * 2) + ((c ^ (2 * (k1 & 3))) << 4) + half;
+        const char* b1 = st + C_::P_BYTES + k1 * (BN * 2) + (nrow_slot(c, k1) << 4) + half;
         fb[j] = read_tr_pair(b0, b1);
       }
     }
@@ -562,11 +584,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // steady state (branch-free, so the compiler's LDS wait counts stay exact):
   // stages it+1 .. it+S-2 are in flight on entry, stage it+S-1 is issued here
   for (; it < KT - (S - 1); ++it) {
+    lds_reads_done();
     read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
     interleave();
     wait_vm_barrier<C_::D * (S - 3)>();
     issue_stage(it + S - 1);
+    lds_reads_done();
     read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
     mma_all(fa[1], fb[1]);
     interleave();
@@ -582,50 +606,94 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     mma_all(fa[1], fb[1]);
   }
 
-  // ---- epilogue ----
+  // ---- epilogue, staged through LDS one 32-row slab at a time ----
   // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) +
-  // (v%4), column l%32 of the fragment.
+  // (v%4), column l%32 of the fragment.  Staging turns the column-per-lane
+  // layout into 4-column chunks per lane, so the addend Z is read with one
+  // 8-byte load per chunk, all issued before any is used, and the outputs
+  // are written as 8-byte chunks; a second pass over the staged values writes
+  // the mirrored tile (symmetric products) or the transposed U (final
+  // iteration of a tall matrix).
   bf16_t* C = static_cast<bf16_t*>(g.C) + batch * g.strideC;
   const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
   const bool mirror = SYRK && (tm != tn);
+  const bool second_pass = mirror || (EPI == EPI_FINAL && g.transpose_out);
+  constexpr int LDW = C_::LDW;
+  constexpr int CPR = WN / 4;                 // 4-column chunks per slab row
+  constexpr int NP = 32 * CPR / 64;           // chunks per lane and slab
+  constexpr int NP2 = WN * 8 / 64;            // transposed chunks per lane and slab
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free
+  float* wl = reinterpret_cast<float*>(lds) + wave * 32 * LDW;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn0 + j * 32 + frow;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row0 = m0 + wm0 + i * 32 + 8 * q + 4 * fgrp;
-        float out[4];
+      for (int v = 0; v < 16; ++v)
+        wl[(8 * (v >> 2) + 4 * fgrp + (v & 3)) * LDW + j * 32 + frow] = acc[i][j][v];
+    const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
+    uint2 zr[NP];
+    if (EPI != EPI_STORE) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[i][j][4 * q + r] * g.alpha;
-          if (EPI != EPI_STORE) v = fmaf(g.beta, bf16_to_f32(Z[(row0 + r) * g.N + col]), v);
-          out[r] = v;
+      for (int p = 0; p < NP; ++p) {
+        const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
+        zr[p] = *reinterpret_cast<const uint2*>(Z + (r0 + row) * g.N + c0 + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
+      float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + 4 * c4);
+      float o[4] = {a.x * g.alpha, a.y * g.alpha, a.z * g.alpha, a.w * g.alpha};
+      if (EPI != EPI_STORE) {
+        o[0] = fmaf(g.beta, __uint_as_float(zr[p].x << 16), o[0]);
+        o[1] = fmaf(g.beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
+        o[2] = fmaf(g.beta, __uint_as_float(zr[p].y << 16), o[2]);
+        o[3] = fmaf(g.beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
+      }
+      const int64_t grow = r0 + row, gcol = c0 + 4 * c4;
+      if (EPI == EPI_FINAL) {
+        if (!g.transpose_out && grow < g.s_valid) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (gcol + t < g.l_valid) {
+              const int64_t idx = batch * g.strideU + grow * g.l_valid + gcol + t;
+              if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx] = f32_to_bf16(o[t]);
+              else static_cast<float*>(g.U)[idx] = o[t];
+            }
+          }
         }
-        if (EPI == EPI_FINAL) {
-          if (col < g.l_valid) {
+      } else {
+        const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+        const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+        *reinterpret_cast<uint2*>(C + grow * g.N + gcol) = make_uint2(w0, w1);
+      }
+      if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (second_pass) {
+      // mirrored / transposed: row c0 + mr receives slab rows 4*c4 .. 4*c4+3
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t row = row0 + r;
-              if (row < g.s_valid) {
-                const int64_t idx = g.transpose_out ? col * g.s_valid + row : row * g.l_valid + col;
-                if (g.u_dtype == MUON_BF16)
-                  static_cast<bf16_t*>(g.U)[batch * g.strideU + idx] = f32_to_bf16(out[r]);
-                else
-                  static_cast<float*>(g.U)[batch * g.strideU + idx] = out[r];
+      for (int p = 0; p < NP2; ++p) {
+        const int q = lane + 64 * p, mr = q / 8, c4 = q % 8;
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDW + mr];
+        const int64_t orow = c0 + mr, ocol = r0 + 4 * c4;
+        if (EPI == EPI_FINAL) {
+          if (orow < g.l_valid) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if (ocol + t < g.s_valid) {
+                const int64_t idx = batch * g.strideU + orow * g.s_valid + ocol + t;
+                if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx] = f32_to_bf16(o[t]);
+                else static_cast<float*>(g.U)[idx] = o[t];
               }
             }
           }
         } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) C[(row0 + r) * g.N + col] = f32_to_bf16(out[r]);
-          if (mirror) {
-            // the four consecutive rows are four consecutive entries of row `col`
-            const uint32_t w0 = uint32_t(f32_to_bf16(out[0])) | (uint32_t(f32_to_bf16(out[1])) << 16);
-            const uint32_t w1 = uint32_t(f32_to_bf16(out[2])) | (uint32_t(f32_to_bf16(out[3])) << 16);
-            *reinterpret_cast<uint2*>(C + col * g.N + row0) = make_uint2(w0, w1);
-          }
+          const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+          const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+          *reinterpret_cast<uint2*>(C + orow * g.N + ocol) = make_uint2(w0, w1);
         }
       }
     }
