@@ -16,6 +16,7 @@ the same steps as the headline number.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -32,6 +33,44 @@ METRIC = "Muon steps/sec + NS MFMA TFLOP/s (% bf16 peak) at 4096×14336; pack/vo
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "matrix_aware_optimizer_amd", "csrc")
+KERNEL_SOURCES = ["common.h", "gemm.h", "ns.hip", "elementwise.hip"]
+TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "signmuon_step_{shape}_hbm_traffic.md")
+
+
+def kernel_sources_digest() -> str:
+    """First 16 hex digits of the sha256 of the kernel sources, in a fixed order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, rows: int, cols: int):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary.
+
+    The summary holds one ``record:`` line per kernel with the calibrated
+    FETCH_SIZE and WRITE_SIZE bytes and the digest of the kernel sources it
+    was taken with.  Returns None when there is no record or the sources
+    have changed since."""
+    path = TRAFFIC_RECORDS.format(shape=f"{rows}x{cols}")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    for line in open(path):
+        if not line.startswith("record:"):
+            continue
+        fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if fields.get("kernel") == kernel and fields.get("sources") == digest:
+            return {"bytes": int(fields["fetch_bytes"]) + int(fields["write_bytes"]),
+                    "fetch_bytes": int(fields["fetch_bytes"]),
+                    "write_bytes": int(fields["write_bytes"]),
+                    "source": os.path.relpath(path, ROOT)}
+    return None
 
 
 def parse():
@@ -203,19 +242,26 @@ def main():
             kernels[k]["frac_peak"] = kernels[k]["TFLOP/s"] / peak
 
     dominant = max(total, key=total.get)
+    counters = recorded_traffic({"pack": "sign_pack", "vote": "majority_vote"}.get(dominant, dominant),
+                                rows, cols)
+    traffic = None if counters is None else counters["bytes"]
     dom_flops = {"gram": gram_f, "poly": poly_f, "apply": apply_f}.get(dominant)
     if dom_flops is not None:
         ach = dom_flops / (avg[dominant] * 1e-3) / 1e12
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": peak,
-                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
                     "per_launch_flops": dom_flops, "avg_launch_ms": avg[dominant]}
     else:
         nb = {"momentum": bytes_momentum, "pack": bytes_pack, "vote": bytes_vote,
               "update": bytes_update}[dominant]
         ach = gbs(nb, dominant)
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                    "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
                     "per_launch_bytes": nb, "avg_launch_ms": avg[dominant]}
+
+    if counters is not None:
+        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
+        roofline["traffic_detail"] = counters
 
     result = {
         "metric": METRIC,
