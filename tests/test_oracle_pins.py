@@ -9,6 +9,7 @@ then fails.
 import json
 import math
 import os
+import struct
 
 import numpy as np
 import pytest
@@ -309,6 +310,73 @@ def test_special_values_follow_sign_rule():
 
 
 # ---------------------------------------------------------------------------
+# The whole step, brute force.  For a rank-1 matrix (one row or one column)
+# X X^T is the scalar ||X||^2, so after Frobenius scaling every iteration maps
+# the single singular value s to a s + b s^3 + c s^5: U = phi(1) * M / ||M||_F
+# exactly.  On a flat set of such matrices the whole SignMuon step (momentum,
+# per-matrix polar direction, signs, packing, vote, update) can then be worked
+# out one entry at a time in plain Python floats.
+# ---------------------------------------------------------------------------
+
+def _f32(x):
+    """Round a Python float to the nearest binary32 value (ties to even)."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _brute_force_step(W, M0, Gs, shapes, beta, alpha, eta, coeffs, steps):
+    phi1 = scalar_map(1.0, coeffs, steps)
+    sizes = [r * c for r, c in shapes]
+    n, workers = sum(sizes), len(Gs)
+    dirs, signs = [], []
+    for G in Gs:
+        m = [_f32(beta * M0[i] + alpha * G[i]) for i in range(n)]
+        U, start = [], 0
+        for size in sizes:
+            seg = m[start:start + size]
+            norm = math.sqrt(sum(v * v for v in seg))
+            U += [0.0 if norm == 0 else phi1 * v / norm for v in seg]
+            start += size
+        dirs.append(U)
+        signs.append([not (u < 0) for u in U])
+    vote = [2 * sum(signs[k][i] for k in range(workers)) >= workers for i in range(n)]
+    W_new = [_f32(W[i] - _f32(eta) * (1.0 if vote[i] else -1.0)) for i in range(n)]
+    return dirs, signs, vote, W_new
+
+
+@pytest.mark.parametrize("coeffs,steps", [(CUBIC, 5), (QUINTIC, 5), ((2.0, -1.5, 0.5), 3)])
+def test_whole_step_on_rank_one_matrices(coeffs, steps):
+    shapes = [(1, 8), (8, 1), (1, 5), (3, 1), (1, 64), (2, 1)]
+    n = sum(r * c for r, c in shapes)
+    workers = 5
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal(n).astype(np.float32)
+    M0 = rng.standard_normal(n).astype(np.float32)
+    Gs = [rng.standard_normal(n).astype(np.float32) for _ in range(workers)]
+    # one matrix whose momentum is exactly zero for worker 1 (U = 0, all signs +1)
+    M0[8:16] = 0.0
+    Gs[1][8:16] = 0.0
+    beta, alpha, eta = float(np.float32(0.95)), float(np.float32(0.05)), float(np.float32(0.02))
+    out = O.signmuon_step(W, "f32", [M0] * workers, "f32", Gs, "f32", shapes, beta, alpha, eta,
+                          *coeffs, steps)
+    dirs, signs, vote, W_new = _brute_force_step(W.tolist(), M0.tolist(), [G.tolist() for G in Gs],
+                                                 shapes, beta, alpha, eta, coeffs, steps)
+    for k in range(workers):
+        assert np.allclose(out["U"][k], dirs[k], rtol=1e-12, atol=1e-15)
+        assert O.unpack_bits(out["packed"][k], n).tolist() == signs[k]
+    assert (np.asarray(out["U"][1][8:16]) == 0).all()
+    assert O.unpack_bits(out["vote"], n).tolist() == vote
+    assert out["W"].tolist() == W_new
+
+
+def test_segment_sums_of_squares():
+    # constant segments: c^2 * size exactly (every value and sum is a small dyadic number)
+    values, sizes = [0.5, -3.0, 0.0, 1.25], [6, 1, 9, 16]
+    M = np.concatenate([np.full(sz, v) for v, sz in zip(values, sizes)])
+    offsets = np.concatenate([[0], np.cumsum(sizes)])
+    assert O.segment_sumsq(M, offsets).tolist() == [v * v * sz for v, sz in zip(values, sizes)]
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each breaks one oracle function; some pin must fail.
 # ---------------------------------------------------------------------------
 
@@ -329,7 +397,16 @@ def _pins_bits():
     test_momentum_golden_and_special_cases()
 
 
+def _pins_step():
+    test_whole_step_on_rank_one_matrices(QUINTIC, 5)
+    test_segment_sums_of_squares()
+
+
 MUTANTS = {
+    "direction ignores matrix boundaries": ("worker_direction", lambda M, md, shapes, offs, a, b, c, steps:
+        O.newton_schulz(O.decode(M, md).reshape(1, -1), a, b, c, steps).ravel(), _pins_step),
+    "segment sums shifted by one entry": ("segment_sumsq", lambda M, offs: np.array(
+        [O.sumsq(np.asarray(M)[lo + 1:hi + 1]) for lo, hi in zip(offs[:-1], offs[1:])]), _pins_step),
     "poly drops the c term": ("poly", lambda A, b, c: b * A, _pins_ns),
     "poly flips the sign of b": ("poly", lambda A, b, c: -b * A + c * A @ A, _pins_ns),
     "apply drops aX": ("apply_poly", lambda B, X, a: B @ X, _pins_ns),
