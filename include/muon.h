@@ -142,15 +142,26 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
  *   when rows > cols, and sumsq[b] == 0 giving X0[b] = 0.
  * ns_gram      (a3): A[b] = X[b] X[b]^T.
  * ns_poly      (a4): B[b] = b A[b] + c A[b] A[b]   (A symmetric).
- * ns_apply     (a5): Xout[b] = a X[b] + alpha B[b] X[b]. */
+ * ns_apply     (a5): Xout[b] = a X[b] + alpha B[b] X[b]  (X is not read as an
+ *   addend when a == 0).
+ * One iteration is ns_gram, ns_poly(b, c), ns_apply(a, alpha = 1), or with
+ * c == 0 ns_gram, ns_apply(a, alpha = b).
+ *
+ * sumsq (device float[batch], or NULL; bf16 only, else MUON_EDTYPE) folds the
+ * Frobenius scaling into the first iteration: given the raw momentum M as X
+ * and sumsq[b] = sum(M[b]^2), ns_gram writes A = M M^T / sumsq and ns_apply
+ * writes (a M + alpha B M) / sqrt(sumsq) (0 when sumsq[b] == 0), which is
+ * the first iteration on X0 = M / ||M||_F without materialising X0.
+ * ns_orthogonalize does this for bf16 momenta that are wide with sides that
+ * are multiples of MUON_NS_PAD. */
 int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t batch,
                  const float* sumsq, void* X0, int precision, void* stream);
 int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision,
-            void* stream);
+            const float* sumsq, void* stream);
 int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c,
             int precision, void* stream);
 int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch,
-             float a, float alpha, int precision, void* stream);
+             float a, float alpha, int precision, const float* sumsq, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6 -- entrywise sign and 1-bit packing.

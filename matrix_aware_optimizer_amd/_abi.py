@@ -53,11 +53,12 @@ SIGNATURES = {
                                   _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
     "ns_normalize": (_c_int, [_c_void_p, _c_int, _c_i64, _c_i64, _c_i64, _c_void_p, _c_void_p,
                               _c_int, _c_void_p]),
-    "ns_gram": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_int, _c_void_p]),
+    "ns_gram": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_int, _c_void_p,
+                         _c_void_p]),
     "ns_poly": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_float, _c_float, _c_int,
                          _c_void_p]),
     "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_float,
-                          _c_float, _c_int, _c_void_p]),
+                          _c_float, _c_int, _c_void_p, _c_void_p]),
     "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "majority_vote": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
@@ -220,25 +221,29 @@ def ns_normalize(M: torch.Tensor, sumsq: torch.Tensor, X0: torch.Tensor, precisi
         precision_code(precision), _stream(stream)))
 
 
-def ns_gram(X: torch.Tensor, A: torch.Tensor, precision="bf16", stream=None) -> None:
+def ns_gram(X: torch.Tensor, A: torch.Tensor, precision="bf16", stream=None,
+            sumsq: Optional[torch.Tensor] = None) -> None:
+    """A = X X^T, or M M^T / sumsq with the raw momentum as X."""
     batch, s, l = _batch3(X)
     _check("ns_gram", lib().ns_gram(_dev(X, "X"), _dev(A, "A"), s, l, batch,
-                                    precision_code(precision), _stream(stream)))
+                                    precision_code(precision), _dev(sumsq, "sumsq"), _stream(stream)))
 
 
 def ns_poly(A: torch.Tensor, B: torch.Tensor, b: float, c: float, precision="bf16",
             stream=None) -> None:
+    """B = b A + c A A."""
     batch, s, _ = _batch3(A)
     _check("ns_poly", lib().ns_poly(_dev(A, "A"), _dev(B, "B"), s, batch, float(b), float(c),
                                     precision_code(precision), _stream(stream)))
 
 
 def ns_apply(B: torch.Tensor, X: torch.Tensor, Xout: torch.Tensor, a: float, alpha: float = 1.0,
-             precision="bf16", stream=None) -> None:
+             precision="bf16", stream=None, sumsq: Optional[torch.Tensor] = None) -> None:
+    """Xout = a X + alpha B X, or (a M + alpha B M) / sqrt(sumsq) with the raw momentum as X."""
     batch, s, l = _batch3(X)
     _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), s, l, batch,
                                       float(a), float(alpha), precision_code(precision),
-                                      _stream(stream)))
+                                      _dev(sumsq, "sumsq"), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -76,7 +76,14 @@ struct GemmArgs {
   void* C;        // output [M][N] (ld = N)
   int64_t M, N, K;
   int64_t strideP, strideQ, strideZ, strideC;  // batch strides (elements)
-  float alpha, beta;                           // C = alpha*acc + beta*Z
+  float alpha, beta;                           // C = alpha*acc + beta*Z (Z unread if beta == 0)
+  // Frobenius scaling folded into the first iteration: with scale_sumsq set,
+  // alpha and beta of batch entry b are multiplied by f(sumsq[b * stride]),
+  // f = 1/ss (scale_mode 1, the Gram of M) or 1/sqrt(ss) (scale_mode 2, the
+  // product with M), and f = 0 for ss == 0
+  const float* scale_sumsq;
+  int64_t stride_sumsq;
+  int scale_mode;
   // EPI_FINAL: write U instead of C, un-padded (s_valid x l_valid of the
   // working layout) and transposed back when the momentum was tall.
   void* U;
@@ -286,7 +293,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float v = acc[i][j][4 * q + r] * g.alpha;
-          if (EPI != EPI_STORE) v = fmaf(g.beta, to_f32(Z[(row0 + r) * g.N + col]), v);
+          if (EPI != EPI_STORE && g.beta != 0.0f) v = fmaf(g.beta, to_f32(Z[(row0 + r) * g.N + col]), v);
           out[r] = v;
         }
         if (EPI == EPI_FINAL) {
@@ -618,6 +625,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
   const bool mirror = SYRK && (tm != tn);
   const bool second_pass = mirror || (EPI == EPI_FINAL && g.transpose_out);
+  const bool use_z = EPI != EPI_STORE && g.beta != 0.0f;
+  float alpha = g.alpha, beta = g.beta;
+  if (g.scale_sumsq != nullptr) {
+    const double ss = static_cast<double>(g.scale_sumsq[batch * g.stride_sumsq]);
+    const float f = ss == 0.0 ? 0.0f : static_cast<float>(g.scale_mode == 1 ? 1.0 / ss : 1.0 / sqrt(ss));
+    alpha *= f;
+    beta *= f;
+  }
   constexpr int LDW = C_::LDW;
   constexpr int CPR = WN / 4;                 // 4-column chunks per slab row
   constexpr int NP = 32 * CPR / 64;           // chunks per lane and slab
@@ -633,7 +648,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         wl[(8 * (v >> 2) + 4 * fgrp + (v & 3)) * LDW + j * 32 + frow] = acc[i][j][v];
     const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
     uint2 zr[NP];
-    if (EPI != EPI_STORE) {
+    if (use_z) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
@@ -644,12 +659,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     for (int p = 0; p < NP; ++p) {
       const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
       float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + 4 * c4);
-      float o[4] = {a.x * g.alpha, a.y * g.alpha, a.z * g.alpha, a.w * g.alpha};
-      if (EPI != EPI_STORE) {
-        o[0] = fmaf(g.beta, __uint_as_float(zr[p].x << 16), o[0]);
-        o[1] = fmaf(g.beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
-        o[2] = fmaf(g.beta, __uint_as_float(zr[p].y << 16), o[2]);
-        o[3] = fmaf(g.beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
+      float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
+      if (use_z) {
+        o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
+        o[1] = fmaf(beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
+        o[2] = fmaf(beta, __uint_as_float(zr[p].y << 16), o[2]);
+        o[3] = fmaf(beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
       }
       const int64_t grow = r0 + row, gcol = c0 + 4 * c4;
       if (EPI == EPI_FINAL) {

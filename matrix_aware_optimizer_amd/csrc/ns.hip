@@ -107,13 +107,24 @@ int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
   }
 }
 
+// Frobenius scaling folded into the first iteration (bf16 only): the raw
+// momentum M stands in for X0 = M / ||M||_F, the Gram is scaled by 1/sumsq
+// and the product with M by 1/sqrt(sumsq).
+struct Fold {
+  const float* sumsq;     // null: X is already normalised
+  int64_t stride_sumsq;
+  int64_t strideX;        // batch stride of X (0: s * l)
+};
+
 template <typename T>
-int gram_t(const void* X, void* A, int64_t s, int64_t l, int64_t batch, hipStream_t st) {
+int gram_t(const void* X, void* A, int64_t s, int64_t l, int64_t batch, hipStream_t st,
+           const Fold& fold = Fold{}) {
   GemmArgs g{};
   g.P = X; g.Q = X; g.Z = nullptr; g.C = A;
   g.M = s; g.N = s; g.K = l;
-  g.strideP = g.strideQ = s * l; g.strideC = s * s;
+  g.strideP = g.strideQ = fold.strideX ? fold.strideX : s * l; g.strideC = s * s;
   g.alpha = 1.0f; g.beta = 0.0f;
+  g.scale_sumsq = fold.sumsq; g.stride_sumsq = fold.stride_sumsq; g.scale_mode = 1;
   return launch_gemm<T, true, false, EPI_STORE>(g, batch, st);
 }
 
@@ -129,13 +140,14 @@ int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, h
 
 template <typename T>
 int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
-            float alpha, hipStream_t st, const GemmArgs* final_out) {
+            float alpha, hipStream_t st, const GemmArgs* final_out, const Fold& fold = Fold{}) {
   GemmArgs g{};
   if (final_out) g = *final_out;
   g.P = B; g.Q = X; g.Z = X; g.C = Xout;
   g.M = s; g.N = l; g.K = s;
-  g.strideP = s * s; g.strideQ = g.strideZ = g.strideC = s * l;
+  g.strideP = s * s; g.strideQ = g.strideZ = fold.strideX ? fold.strideX : s * l; g.strideC = s * l;
   g.alpha = alpha; g.beta = a;
+  g.scale_sumsq = fold.sumsq; g.stride_sumsq = fold.stride_sumsq; g.scale_mode = 2;
   if (final_out) return launch_gemm<T, false, true, EPI_FINAL>(g, batch, st);
   return launch_gemm<T, false, true, EPI_AXPBY>(g, batch, st);
 }
@@ -279,6 +291,13 @@ RunLayout layout_of(const Run& r, int precision) {
   return L;
 }
 
+// bf16 momentum already in the working layout (wide, sides multiples of
+// MUON_NS_PAD, 16-byte aligned rows): no normalisation pass is needed
+bool folds_normalisation(const Run& r, int precision) {
+  return precision == MUON_BF16 && r.m_dtype == MUON_BF16 && r.rows <= r.cols &&
+         r.rows % MUON_NS_PAD == 0 && r.cols % MUON_NS_PAD == 0 && r.strideM % 8 == 0;
+}
+
 bool valid_problem(const muon_ns_problem& p) {
   return p.rows > 0 && p.cols > 0 && p.M && p.U;
 }
@@ -335,9 +354,14 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     void* X[2] = {ws + L.x0, ws + L.x1};
     void* A = ws + L.a;
     void* B = ws + L.b;
-    status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
-                                precision, r.sp, r.lp, r.count, st);
-    if (status != MUON_OK) return status;
+    // a bf16, wide, pad-free momentum is its own (unnormalised) X0: the first
+    // iteration reads M and folds the Frobenius scale into its epilogues
+    const bool fold_norm = folds_normalisation(r, precision) && steps > 0;
+    if (!fold_norm) {
+      status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
+                                  precision, r.sp, r.lp, r.count, st);
+      if (status != MUON_OK) return status;
+    }
     if (steps == 0) {
       status = precision == MUON_BF16
                    ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
@@ -353,21 +377,24 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     fin.u_dtype = r.u_dtype;
     fin.transpose_out = r.rows > r.cols;
     for (int it = 0; it < steps; ++it) {
-      const void* Xc = X[it & 1];
+      const bool first_folded = fold_norm && it == 0;
+      const void* Xc = first_folded ? r.M : X[it & 1];
       void* Xn = X[(it + 1) & 1];
       const bool last = it + 1 == steps;
+      const Fold fold = first_folded ? Fold{sumsq, stride_sumsq, r.strideM} : Fold{};
       if (precision == MUON_BF16) {
-        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st);
+        // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
+        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, fold);
         if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st);
         if (status == MUON_OK)
-          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a,
-                                   c != 0.0f ? 1.0f : b, st, last ? &fin : nullptr);
+          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
+                                   st, last ? &fin : nullptr, fold);
       } else {
         status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st);
         if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st);
         if (status == MUON_OK)
-          status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a,
-                                  c != 0.0f ? 1.0f : b, st, last ? &fin : nullptr);
+          status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
+                                  st, last ? &fin : nullptr);
       }
       if (status != MUON_OK) return status;
     }
@@ -392,14 +419,17 @@ int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t
                             batch, static_cast<hipStream_t>(stream));
 }
 
-int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision, void* stream) {
+int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision,
+            const float* sumsq, void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (sumsq && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!X || !A) return MUON_EINVAL;
   if (!aligned16(X) || !aligned16(A)) return MUON_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? gram_t<bf16_t>(X, A, s, l, batch, st) : gram_t<float>(X, A, s, l, batch, st);
+  return precision == MUON_BF16 ? gram_t<bf16_t>(X, A, s, l, batch, st, Fold{sumsq, 1, 0})
+                                : gram_t<float>(X, A, s, l, batch, st);
 }
 
 int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c, int precision,
@@ -410,18 +440,20 @@ int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c, 
   if (!A || !B) return MUON_EINVAL;
   if (!aligned16(A) || !aligned16(B)) return MUON_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? poly_t<bf16_t>(A, B, s, batch, b, c, st) : poly_t<float>(A, B, s, batch, b, c, st);
+  return precision == MUON_BF16 ? poly_t<bf16_t>(A, B, s, batch, b, c, st)
+                                : poly_t<float>(A, B, s, batch, b, c, st);
 }
 
 int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
-             float alpha, int precision, void* stream) {
+             float alpha, int precision, const float* sumsq, void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  if (sumsq && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!B || !X || !Xout) return MUON_EINVAL;
   if (!aligned16(B) || !aligned16(X) || !aligned16(Xout)) return MUON_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, nullptr)
+  return precision == MUON_BF16 ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, nullptr, Fold{sumsq, 1, 0})
                                 : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, nullptr);
 }
 

@@ -85,13 +85,15 @@ def test_pack_vote_update_validation(L):
 
 
 def test_stage_validation(L):
-    assert L.ns_gram(A1, A2, 250, 512, 1, 1, None) == EINVAL      # s not padded
-    assert L.ns_gram(A1, A2, 512, 256, 1, 1, None) == EINVAL      # s > l
-    assert L.ns_gram(A1, A2, 256, 512, 1, 7, None) == EDTYPE
+    assert L.ns_gram(A1, A2, 250, 512, 1, 1, None, None) == EINVAL      # s not padded
+    assert L.ns_gram(A1, A2, 512, 256, 1, 1, None, None) == EINVAL      # s > l
+    assert L.ns_gram(A1, A2, 256, 512, 1, 7, None, None) == EDTYPE
+    assert L.ns_gram(A1, A2, 256, 512, 1, 0, A3, None) == EDTYPE        # folded scaling: bf16 only
     assert L.ns_poly(A1, MISALIGNED, 256, 1, 1.0, 1.0, 1, None) == EALIGN
-    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None) == EINVAL
+    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None, None) == EINVAL
+    assert L.ns_apply(A1, A2, A3, 256, 256, 1, 1.0, 1.0, 0, A3, None) == EDTYPE
     assert L.ns_normalize(A1, 1, 0, 5, 1, A2, A3, 1, None) == EINVAL
-    assert L.ns_gram(A1, A2, 256, 256, 0, 1, None) == OK           # empty batch: no launch
+    assert L.ns_gram(A1, A2, 256, 256, 0, 1, None, None) == OK           # empty batch: no launch
 
 
 def _problems(specs):

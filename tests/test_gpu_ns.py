@@ -68,7 +68,7 @@ def test_poly(prec, coeffs, batch, s, sv):
 
 
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
-@pytest.mark.parametrize("a,alpha", [(QUINTIC[0], 1.0), (1.5, -0.5)])
+@pytest.mark.parametrize("a,alpha", [(QUINTIC[0], 1.0), (1.5, -0.5), (0.0, 1.0)])
 @pytest.mark.parametrize("batch,s,l,sv,lv", [(1, 256, 256, 256, 256), (2, 256, 768, 200, 700),
                                               (1, 512, 1536, 512, 1536), (1, 2048, 2560, 2000, 2500)])
 def test_apply(prec, a, alpha, batch, s, l, sv, lv):
@@ -131,9 +131,12 @@ def _ns_gpu(M_list, m_dtype, u_dtype, coeffs, steps, prec, with_sums=True):
 
 @pytest.mark.parametrize("shape", [(256, 256), (37, 300), (300, 37), (512, 1536), (1536, 512),
                                    (768, 768), (1, 1), (3, 1000)])
-@pytest.mark.parametrize("prec,coeffs", [("f32", CUBIC), ("bf16", QUINTIC), ("f32", QUINTIC)])
+@pytest.mark.parametrize("prec,coeffs", [("f32", CUBIC), ("bf16", QUINTIC), ("f32", QUINTIC),
+                                         ("bf16", CUBIC)])
 @pytest.mark.parametrize("steps", [0, 1, 5])
 def test_ns_matches_oracle(shape, prec, coeffs, steps):
+    """bf16 wide shapes with sides that are multiples of 256 take the path that folds the
+    Frobenius scaling into the first iteration; the others normalise first."""
     m_dtype = prec
     M = store(random_matrix(shape, [303, shape[0], shape[1]]), m_dtype)
     (U,) = _ns_gpu([M], m_dtype, prec, coeffs, steps, prec)
@@ -144,12 +147,53 @@ def test_ns_matches_oracle(shape, prec, coeffs, steps):
 def test_ns_computes_its_own_norm_and_handles_zero():
     Ms = [store(random_matrix((200, 520), [304, 0]), "bf16"),
           store(np.zeros((64, 64)), "bf16"),
-          store(random_matrix((520, 200), [304, 1]) * 1e-3, "bf16")]
+          store(random_matrix((520, 200), [304, 1]) * 1e-3, "bf16"),
+          store(np.zeros((256, 512)), "bf16"),                          # folded scaling path
+          store(random_matrix((256, 768), [304, 2]) * 1e-3, "bf16")]
     got = _ns_gpu(Ms, "bf16", "bf16", QUINTIC, 5, "bf16", with_sums=False)
-    assert not got[1].any()
-    for M, U in zip([Ms[0], Ms[2]], [got[0], got[2]]):
-        ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
-        assert rel_fro(U, ref) <= TOL_NS["bf16"]
+    assert not got[1].any() and not got[3].any()
+    for j in (0, 2, 4):
+        ref = O.newton_schulz(O.decode(Ms[j], "bf16"), *QUINTIC, 5)
+        assert rel_fro(got[j], ref) <= TOL_NS["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(100, 300), (256, 512)])
+def test_ns_nan_momentum_gives_nan_direction(shape):
+    """A NaN makes the norm NaN and, on both the normalising and the folded path, every
+    entry of U NaN (so every sign +1), as the oracle's arithmetic gives."""
+    M = random_matrix(shape, [313, 0])
+    M[3, 7] = np.nan
+    (U,) = _ns_gpu([store(M, "bf16")], "bf16", "bf16", QUINTIC, 5, "bf16")
+    assert np.isnan(U).all()
+    assert np.isnan(O.newton_schulz(O.decode(store(M, "bf16"), "bf16"), *QUINTIC, 5)).all()
+
+
+@pytest.mark.parametrize("batch,s,l", [(1, 256, 768), (3, 512, 1024)])
+def test_stages_with_folded_scaling(batch, s, l):
+    """ns_gram / ns_apply given the raw momentum and its sums of squares equal the
+    stages on X0 = M / ||M||_F (against the oracle), including a zero matrix."""
+    M = random_matrix((batch, s, l), [314, s]) * 0.3
+    M[-1] = 0.0
+    Ms = store(M, "bf16")
+    Mf = O.decode(Ms, "bf16").reshape(batch, s, l)
+    sums = torch.tensor([O.sumsq(Mf[b]) for b in range(batch)], dtype=torch.float32, device="cuda")
+    Md = to_dev(Ms, "bf16").view(batch, s, l)
+    A = torch.empty((batch, s, s), dtype=torch.bfloat16, device="cuda")
+    mao.ns_gram(Md, A, "bf16", sumsq=sums)
+    R = random_matrix((batch, s, s), [315, 0]) / np.sqrt(s)
+    Bs = store(R + np.transpose(R, (0, 2, 1)), "bf16")
+    out = torch.empty_like(Md)
+    mao.ns_apply(to_dev(Bs, "bf16").view(batch, s, s), Md, out, 1.5, 0.7, "bf16", sumsq=sums)
+    gotA = O.decode(from_dev(A), "bf16").reshape(batch, s, s)
+    gotX = O.decode(from_dev(out), "bf16").reshape(batch, s, l)
+    Bd = O.decode(Bs, "bf16").reshape(batch, s, s)
+    for b in range(batch):
+        X0 = O.frobenius_normalize(Mf[b])
+        if b == batch - 1:
+            assert not gotA[b].any() and not gotX[b].any()
+            continue
+        assert rel_fro(gotA[b], O.gram(X0)) <= TOL_STAGE["bf16"]
+        assert rel_fro(gotX[b], O.apply_poly(0.7 * Bd[b], X0, 1.5)) <= TOL_STAGE["bf16"]
 
 
 def test_ns_batched_interleaved_shapes():
@@ -206,7 +250,8 @@ def test_ns_bf16_ill_conditioned_spectrum_bound():
 
 @pytest.mark.parametrize("kind,batch,s,l", [("gram", 16, 2048, 2048), ("poly", 16, 2048, 2048),
                                              ("apply", 16, 1024, 2048), ("apply", 3, 2048, 2304),
-                                             ("gram", 1, 4096, 4096), ("apply", 1, 4096, 14336)])
+                                             ("gram", 1, 4096, 4096), ("apply", 1, 4096, 14336),
+                                             ("gram", 1, 4096, 14336), ("poly", 1, 4096, 4096)])
 def test_stages_at_large_tile_sizes(kind, batch, s, l):
     """Stage shapes that take the 256 x 256-tile kernels (symmetric products, or B X with
     a contraction of 2048 or more) next to ones that take the 128 x 128 tiles."""
@@ -239,3 +284,27 @@ def test_stages_at_large_tile_sizes(kind, batch, s, l):
         X, Bd = O.decode(Xs, prec), O.decode(Bs, prec)
         for b in check:
             assert rel_fro(got[b], O.apply_poly(Bd[b], X[b], QUINTIC[0])) <= TOL_STAGE[prec]
+
+
+def test_stage_sequence_equals_ns_orthogonalize():
+    """The stage calls bench.py times (gram / poly / apply five times, the first on the
+    raw momentum with the scaling folded in) compute exactly what ns_orthogonalize
+    computes: on a pad-free wide matrix the final X equals U bit for bit."""
+    prec, rows, cols = "bf16", 4096, 14336
+    M = store(random_matrix((rows, cols), [312, 0]), prec)
+    Md = to_dev(M, prec).view(rows, cols)
+    sums = torch.tensor([O.sumsq(O.decode(M, prec))], dtype=torch.float32, device="cuda")
+    U = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    a, b, c = QUINTIC
+    mao.ns_orthogonalize([(Md, U, sums)], a, b, c, 5, prec)
+    X = [torch.empty((1, rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    A = torch.empty((1, rows, rows), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty_like(A)
+    # a bf16 wide pad-free momentum: the first iteration reads M and folds the scaling
+    M3 = Md.view(1, rows, cols)
+    for it in range(5):
+        Xc, ss = (M3, sums) if it == 0 else (X[it % 2], None)
+        mao.ns_gram(Xc, A, prec, sumsq=ss)
+        mao.ns_poly(A, B, b, c, prec)
+        mao.ns_apply(B, Xc, X[(it + 1) % 2], a, 1.0, prec, sumsq=ss)
+    assert np.array_equal(from_dev(X[1]).reshape(rows, cols), from_dev(U))
