@@ -11,42 +11,6 @@ namespace muon {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 8-element vector access (16 B for bf16, 2 x 16 B for fp32).
-// ---------------------------------------------------------------------------
-template <typename T> struct Vec8;
-template <> struct Vec8<bf16_t> {
-  __device__ __forceinline__ static void load(const bf16_t* p, float v[8]) {
-    uint4 r = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  __device__ __forceinline__ static void store(bf16_t* p, const float v[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-};
-template <> struct Vec8<float> {
-  __device__ __forceinline__ static void load(const float* p, float v[8]) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  __device__ __forceinline__ static void store(float* p, const float v[8]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-  }
-};
-
-// ---------------------------------------------------------------------------
 // a1: momentum EMA + per-segment sum of squares.
 // A block owns a chunk of kChunk consecutive entries.  The chunk's part inside
 // segment s is the "piece" (block b, segment s); its partial sum goes to
@@ -93,6 +57,28 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
   const int64_t c0 = int64_t(blockIdx.x) * kChunk;
   const int64_t c1 = min(numel, c0 + kChunk);
   float vals[kIters][8];
+  if (c1 - c0 == kChunk) {
+    // full chunk: every load is issued before any arithmetic
+    float g[kIters][8];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+      Vec8<TM>::load(M + e0, vals[it]);
+      if (UPDATE) Vec8<TG>::load(G + e0, g[it]);
+    }
+    if (UPDATE) {
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vals[it][q] = ema(beta, vals[it][q], alpha, g[it][q]);
+        Vec8<TM>::store(M + e0, vals[it]);
+        // the stored value is what the norm must see
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vals[it][q] = to_f32(from_f32<TM>(vals[it][q]));
+      }
+    }
+  } else {
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
@@ -127,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
       }
     }
   }
+  }
   if (!SUMS) return;
 
   __shared__ double red[kThreads / kWave];
@@ -147,13 +134,20 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
     const int64_t p0 = max(c0, s0), p1 = min(c1, s1);
     if (p0 >= p1) continue;
     double acc = 0.0;
+    if (p0 == c0 && p1 == c1) {   // the chunk lies inside one segment (entries past numel are 0)
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+      for (int it = 0; it < kIters; ++it)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const double v = vals[it][q];
-        if (e0 + q >= p0 && e0 + q < p1) acc = fma(v, v, acc);
+        for (int q = 0; q < 8; ++q) acc = fma(double(vals[it][q]), double(vals[it][q]), acc);
+    } else {
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int64_t e0 = c0 + int64_t(it) * (kThreads * 8) + threadIdx.x * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const double v = vals[it][q];
+          if (e0 + q >= p0 && e0 + q < p1) acc = fma(v, v, acc);
+        }
       }
     }
     const double tot = block_sum(acc, red);
@@ -172,7 +166,19 @@ __global__ __launch_bounds__(kThreads) void segment_reduce_kernel(const double* 
   if (s1 > s0 && s0 >= 0) {
     // clamped so that offsets beyond numel cannot index past the partials
     const int64_t b0 = s0 / kChunk, b1 = min((s1 - 1) / kChunk, nchunks - 1);
-    for (int64_t b = b0 + threadIdx.x; b <= b1; b += kThreads) acc += partials[b + s];
+    // each thread adds its entries b0 + tid, b0 + tid + kThreads, ... in that
+    // order; eight loads are issued before the adds
+    constexpr int kU = 8;
+    for (int64_t b = b0 + threadIdx.x; b <= b1; b += kU * kThreads) {
+      double x[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int64_t i = b + int64_t(j) * kThreads;
+        x[j] = i <= b1 ? partials[i + s] : 0.0;
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) acc += x[j];
+    }
   }
   const double tot = block_sum(acc, red);
   if (threadIdx.x == 0) out[s] = static_cast<float>(tot);
@@ -241,27 +247,44 @@ template <> struct SignByte<float> {
   }
 };
 
+// A block packs kPackGroups groups of kThreads * 8 entries; each lane tests
+// its 8 entries of every group (all loads first), then the groups are merged
+// and stored one after another.
+constexpr int kPackGroups = 4;
+constexpr int64_t kPackBlock = int64_t(kPackGroups) * kThreads * 8;   // entries per block
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sign_pack_kernel(const T* __restrict__ U, int64_t numel,
                                                             uint64_t* __restrict__ bits,
                                                             int64_t nwords) {
-  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t e0 = t * 8;
-  uint32_t byte = 0;
-  if (e0 + 8 <= numel) {
-    byte = SignByte<T>::full(U + e0);
+  const int64_t base = int64_t(blockIdx.x) * kPackBlock + threadIdx.x * 8;
+  uint32_t byte[kPackGroups];
+  if (int64_t(blockIdx.x + 1) * kPackBlock <= numel) {
+#pragma unroll
+    for (int g = 0; g < kPackGroups; ++g) byte[g] = SignByte<T>::full(U + base + g * (kThreads * 8));
   } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (e0 + q < numel) byte |= SignByte<T>::one(U + e0 + q) << q;
+    for (int g = 0; g < kPackGroups; ++g) {
+      const int64_t e0 = base + g * (kThreads * 8);
+      byte[g] = 0;
+      if (e0 + 8 <= numel) {
+        byte[g] = SignByte<T>::full(U + e0);
+      } else {
+        for (int q = 0; q < 8; ++q)
+          if (e0 + q < numel) byte[g] |= SignByte<T>::one(U + e0 + q) << q;
+      }
+    }
   }
-  uint32_t v = byte;
-  v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 1, kWave)) << 8;
-  v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 2, kWave)) << 16;
-  const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 4, kWave));
-  if ((threadIdx.x & 7) == 0) {
-    const int64_t w = e0 >> 6;
-    if (w < nwords) bits[w] = static_cast<uint64_t>(v) | (static_cast<uint64_t>(hi) << 32);
+#pragma unroll
+  for (int g = 0; g < kPackGroups; ++g) {
+    uint32_t v = byte[g];
+    v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 1, kWave)) << 8;
+    v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 2, kWave)) << 16;
+    const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 4, kWave));
+    if ((threadIdx.x & 7) == 0) {
+      const int64_t w = (base + g * (kThreads * 8)) >> 6;
+      if (w < nwords) bits[w] = static_cast<uint64_t>(v) | (static_cast<uint64_t>(hi) << 32);
+    }
   }
 }
 
@@ -295,6 +318,8 @@ __device__ __forceinline__ W counter_ge(const W (&cnt)[NB], int thr) {
   return gt | eq;
 }
 
+// One lane per word; the workers' words are read four at a time so that
+// four loads are in flight before the counter adds.
 template <int NB>
 __global__ __launch_bounds__(kThreads) void vote_kernel(const uint64_t* __restrict__ bits, int M,
                                                        int64_t nwords, uint64_t* __restrict__ out) {
@@ -303,8 +328,44 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(const uint64_t* __restri
   uint64_t cnt[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) cnt[i] = 0;
-  for (int k = 0; k < M; ++k) counter_add<NB>(cnt, bits[int64_t(k) * nwords + w]);
+  int k = 0;
+  for (; k + 4 <= M; k += 4) {
+    uint64_t x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = bits[int64_t(k + j) * nwords + w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) counter_add<NB>(cnt, x[j]);
+  }
+  for (; k < M; ++k) counter_add<NB>(cnt, bits[int64_t(k) * nwords + w]);
   out[w] = counter_ge<NB>(cnt, (M + 1) >> 1);
+}
+
+// Two words per lane (16-byte accesses) when every buffer row is 16-byte
+// aligned (an even word count); same arithmetic per word.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void vote2_kernel(const uint4* __restrict__ bits, int M,
+                                                        int64_t npairs, uint4* __restrict__ out) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= npairs) return;
+  uint64_t c0[NB], c1[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) c0[i] = c1[i] = 0;
+  auto add = [&](const uint4 x) {
+    counter_add<NB>(c0, static_cast<uint64_t>(x.x) | (static_cast<uint64_t>(x.y) << 32));
+    counter_add<NB>(c1, static_cast<uint64_t>(x.z) | (static_cast<uint64_t>(x.w) << 32));
+  };
+  int k = 0;
+  for (; k + 4 <= M; k += 4) {
+    uint4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = bits[int64_t(k + j) * npairs + t];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add(x[j]);
+  }
+  for (; k < M; ++k) add(bits[int64_t(k) * npairs + t]);
+  const uint64_t v0 = counter_ge<NB>(c0, (M + 1) >> 1), v1 = counter_ge<NB>(c1, (M + 1) >> 1);
+  out[t] = make_uint4(static_cast<uint32_t>(v0), static_cast<uint32_t>(v0 >> 32),
+                      static_cast<uint32_t>(v1), static_cast<uint32_t>(v1 >> 32));
 }
 
 // ---------------------------------------------------------------------------
@@ -380,8 +441,15 @@ int dispatch_planes(int nb, Args... args) {
 
 template <int NB> struct VoteLaunch {
   static int run(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, hipStream_t st) {
-    const int64_t blocks = (nwords + kThreads - 1) / kThreads;
-    vote_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(bits, M, nwords, out);
+    if (nwords % 2 == 0) {
+      const int64_t npairs = nwords / 2;
+      const int64_t blocks = (npairs + kThreads - 1) / kThreads;
+      vote2_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(reinterpret_cast<const uint4*>(bits), M,
+                                                                 npairs, reinterpret_cast<uint4*>(out));
+    } else {
+      const int64_t blocks = (nwords + kThreads - 1) / kThreads;
+      vote_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(bits, M, nwords, out);
+    }
     return launch_status();
   }
 };
@@ -482,8 +550,7 @@ int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* s
   if (!U || !bits) return MUON_EINVAL;
   if (!aligned16(U) || !aligned16(bits)) return MUON_EALIGN;
   const int64_t nwords = (numel + 63) / 64;
-  const int64_t threads = nwords * 8;
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  const int64_t blocks = (numel + kPackBlock - 1) / kPackBlock;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (u_dtype == MUON_BF16)
     sign_pack_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const bf16_t*>(U),

@@ -42,35 +42,64 @@ using gemm::GemmArgs;
 
 // ---------------------------------------------------------------------------
 // a2: X0 = pad(orient(M)) * scale, scale = 1/sqrt(sumsq) (0 for a zero matrix).
-// One thread writes 8 consecutive entries of a working row.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float frobenius_scale(const float* sumsq, int64_t b, int64_t stride) {
+  const double ss = static_cast<double>(sumsq[b * stride]);
+  return ss == 0.0 ? 0.0f : static_cast<float>(1.0 / sqrt(ss));
+}
+
+// Wide matrix (rows <= cols): one thread writes 8 consecutive entries of a
+// working row; with `vec` (cols and the batch stride multiples of 8) full
+// groups are read and written as vectors.
 template <typename TM, typename TX>
 __global__ __launch_bounds__(256) void normalize_kernel(const TM* __restrict__ M, int64_t strideM,
                                                        int64_t rows, int64_t cols,
                                                        const float* __restrict__ sumsq,
                                                        int64_t stride_sumsq, TX* __restrict__ X,
-                                                       int64_t sp, int64_t lp) {
+                                                       int64_t sp, int64_t lp, int vec) {
   const int64_t b = blockIdx.y;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t per_row = lp / 8;
   if (t >= sp * per_row) return;
   const int64_t i = t / per_row, j0 = (t % per_row) * 8;
-  const bool tall = rows > cols;
-  const int64_t s = tall ? cols : rows, l = tall ? rows : cols;
-  const double ss = static_cast<double>(sumsq[b * stride_sumsq]);
-  const float scale = ss == 0.0 ? 0.0f : static_cast<float>(1.0 / sqrt(ss));
-  const TM* Mb = M + b * strideM;
-  float v[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int64_t j = j0 + q;
-    float x = 0.0f;
-    if (i < s && j < l) x = to_f32(tall ? Mb[j * cols + i] : Mb[i * cols + j]) * scale;
-    v[q] = x;
-  }
+  const float scale = frobenius_scale(sumsq, b, stride_sumsq);
+  const TM* src = M + b * strideM + i * cols + j0;
   TX* dst = X + b * sp * lp + i * lp + j0;
+  float v[8];
+  if (i < rows && j0 + 8 <= cols && vec) {
+    Vec8<TM>::load(src, v);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dst[q] = from_f32<TX>(v[q]);
+    for (int q = 0; q < 8; ++q) v[q] *= scale;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (i < rows && j0 + q < cols) ? to_f32(src[q]) * scale : 0.0f;
+  }
+  Vec8<TX>::store(dst, v);
+}
+
+// Tall matrix (rows > cols): X0 = M^T, transposed through LDS one 64 x 64 tile
+// at a time so that both the reads (along M's rows) and the writes (along
+// X's rows) are coalesced.
+template <typename TM, typename TX>
+__global__ __launch_bounds__(256) void normalize_tall_kernel(const TM* __restrict__ M, int64_t strideM,
+                                                            int64_t rows, int64_t cols,
+                                                            const float* __restrict__ sumsq,
+                                                            int64_t stride_sumsq, TX* __restrict__ X,
+                                                            int64_t sp, int64_t lp) {
+  __shared__ float tile[64][65];
+  const int64_t b = blockIdx.z;
+  const int64_t i0 = int64_t(blockIdx.y) * 64;   // X rows = M columns
+  const int64_t j0 = int64_t(blockIdx.x) * 64;   // X columns = M rows
+  const float scale = frobenius_scale(sumsq, b, stride_sumsq);
+  const TM* Mb = M + b * strideM;
+  const int c = threadIdx.x & 63;
+  for (int r = threadIdx.x >> 6; r < 64; r += 4) {
+    const int64_t mr = j0 + r, mc = i0 + c;
+    tile[r][c] = (mr < rows && mc < cols) ? to_f32(Mb[mr * cols + mc]) * scale : 0.0f;
+  }
+  __syncthreads();
+  TX* Xb = X + b * sp * lp;
+  for (int r = threadIdx.x >> 6; r < 64; r += 4) Xb[(i0 + r) * lp + j0 + c] = from_f32<TX>(tile[c][r]);
 }
 
 // steps == 0: U = X0 (un-padded, original orientation)
@@ -155,11 +184,17 @@ int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int6
 template <typename TM, typename TX>
 int normalize_t(const void* M, int64_t strideM, int64_t rows, int64_t cols, const float* sumsq,
                 int64_t stride_sumsq, void* X, int64_t sp, int64_t lp, int64_t batch, hipStream_t st) {
-  const int64_t threads = sp * (lp / 8);
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks == 0 || batch == 0) return MUON_OK;
-  normalize_kernel<TM, TX><<<dim3(blocks, batch), dim3(256), 0, st>>>(
-      static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
+  if (sp == 0 || lp == 0 || batch == 0) return MUON_OK;
+  if (rows > cols) {
+    normalize_tall_kernel<TM, TX><<<dim3(lp / 64, sp / 64, batch), dim3(256), 0, st>>>(
+        static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
+  } else {
+    const int64_t blocks = (sp * (lp / 8) + 255) / 256;
+    const int vec = cols % 8 == 0 && strideM % 8 == 0;
+    normalize_kernel<TM, TX><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+        static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp,
+        vec);
+  }
   return launch_status();
 }
 

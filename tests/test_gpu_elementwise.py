@@ -128,7 +128,7 @@ def test_sign_pack_golden(golden_dir):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 15, 16, 31, 100, 1023])
-@pytest.mark.parametrize("nwords", [1, 3, 255, 257, 10001])
+@pytest.mark.parametrize("nwords", [1, 2, 3, 255, 256, 257, 10000, 10001])
 def test_majority_vote(M, nwords):
     rng = np.random.default_rng(M * 7919 + nwords)
     words = rng.integers(0, 2 ** 63, size=(M, nwords), dtype=np.int64).view(np.uint64)

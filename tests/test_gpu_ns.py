@@ -90,7 +90,8 @@ def test_apply(prec, a, alpha, batch, s, l, sv, lv):
 
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 @pytest.mark.parametrize("m_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("rows,cols,batch", [(300, 70, 2), (70, 300, 1), (256, 256, 1), (5, 3, 4)])
+@pytest.mark.parametrize("rows,cols,batch", [(300, 70, 2), (70, 300, 1), (256, 256, 1), (5, 3, 4),
+                                            (200, 520, 2), (3072, 768, 1), (768, 3072, 1)])
 def test_normalize(prec, m_dtype, rows, cols, batch):
     M = store(random_matrix((batch, rows, cols), [302, rows]), m_dtype)
     Mf = O.decode(M, m_dtype).reshape(batch, rows, cols)
