@@ -17,8 +17,8 @@ namespace {
 // partials[b + s], an index that is unique for every non-empty piece.
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;
-constexpr int kIters = 4;
-constexpr int64_t kChunk = int64_t(kThreads) * 8 * kIters;  // 8192 entries
+constexpr int kIters = 2;
+constexpr int64_t kChunk = int64_t(kThreads) * 8 * kIters;  // 4096 entries
 
 struct SegMap {
   const int64_t* offs;  // device offsets [nseg+1], or null for uniform segments
@@ -340,32 +340,54 @@ __global__ __launch_bounds__(kThreads) void vote_kernel(const uint64_t* __restri
   out[w] = counter_ge<NB>(cnt, (M + 1) >> 1);
 }
 
-// Two words per lane (16-byte accesses) when every buffer row is 16-byte
-// aligned (an even word count); same arithmetic per word.
+// Two words per 16-byte access when every buffer row is 16-byte aligned (an
+// even word count); a lane handles kVotePairs such pairs, kThreads pairs
+// apart, so consecutive lanes stay on consecutive addresses.  Same
+// arithmetic per word.
+constexpr int kVotePairs = 1;
+
 template <int NB>
 __global__ __launch_bounds__(kThreads) void vote2_kernel(const uint4* __restrict__ bits, int M,
                                                         int64_t npairs, uint4* __restrict__ out) {
-  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= npairs) return;
-  uint64_t c0[NB], c1[NB];
+  const int64_t t0 = int64_t(blockIdx.x) * (kThreads * kVotePairs) + threadIdx.x;
+  uint64_t c[kVotePairs][2][NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) c0[i] = c1[i] = 0;
-  auto add = [&](const uint4 x) {
-    counter_add<NB>(c0, static_cast<uint64_t>(x.x) | (static_cast<uint64_t>(x.y) << 32));
-    counter_add<NB>(c1, static_cast<uint64_t>(x.z) | (static_cast<uint64_t>(x.w) << 32));
+  for (int p = 0; p < kVotePairs; ++p)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) c[p][0][i] = c[p][1][i] = 0;
+  auto add = [&](int p, const uint4 x) {
+    counter_add<NB>(c[p][0], static_cast<uint64_t>(x.x) | (static_cast<uint64_t>(x.y) << 32));
+    counter_add<NB>(c[p][1], static_cast<uint64_t>(x.z) | (static_cast<uint64_t>(x.w) << 32));
   };
   int k = 0;
   for (; k + 4 <= M; k += 4) {
-    uint4 x[4];
+    uint4 x[4][kVotePairs];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = bits[int64_t(k + j) * npairs + t];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) add(x[j]);
+      for (int p = 0; p < kVotePairs; ++p) {
+        const int64_t t = t0 + int64_t(p) * kThreads;
+        x[j][p] = t < npairs ? bits[int64_t(k + j) * npairs + t] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int p = 0; p < kVotePairs; ++p) add(p, x[j][p]);
   }
-  for (; k < M; ++k) add(bits[int64_t(k) * npairs + t]);
-  const uint64_t v0 = counter_ge<NB>(c0, (M + 1) >> 1), v1 = counter_ge<NB>(c1, (M + 1) >> 1);
-  out[t] = make_uint4(static_cast<uint32_t>(v0), static_cast<uint32_t>(v0 >> 32),
-                      static_cast<uint32_t>(v1), static_cast<uint32_t>(v1 >> 32));
+  for (; k < M; ++k)
+#pragma unroll
+    for (int p = 0; p < kVotePairs; ++p) {
+      const int64_t t = t0 + int64_t(p) * kThreads;
+      add(p, t < npairs ? bits[int64_t(k) * npairs + t] : make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+  for (int p = 0; p < kVotePairs; ++p) {
+    const int64_t t = t0 + int64_t(p) * kThreads;
+    if (t >= npairs) continue;
+    const uint64_t v0 = counter_ge<NB>(c[p][0], (M + 1) >> 1), v1 = counter_ge<NB>(c[p][1], (M + 1) >> 1);
+    out[t] = make_uint4(static_cast<uint32_t>(v0), static_cast<uint32_t>(v0 >> 32),
+                        static_cast<uint32_t>(v1), static_cast<uint32_t>(v1 >> 32));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -443,7 +465,7 @@ template <int NB> struct VoteLaunch {
   static int run(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, hipStream_t st) {
     if (nwords % 2 == 0) {
       const int64_t npairs = nwords / 2;
-      const int64_t blocks = (npairs + kThreads - 1) / kThreads;
+      const int64_t blocks = (npairs + kThreads * kVotePairs - 1) / (kThreads * kVotePairs);
       vote2_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(reinterpret_cast<const uint4*>(bits), M,
                                                                  npairs, reinterpret_cast<uint4*>(out));
     } else {

@@ -62,9 +62,9 @@ def test_momentum_validation(L):
 
 
 def test_momentum_workspace_formula(L):
-    # one double per 8192-entry chunk and per segment, plus one, rounded to 256 bytes
-    for numel, nseg in [(1, 1), (8192, 1), (8193, 2), (58720256, 1), (84934656, 48)]:
-        chunks = -(-numel // 8192)
+    # one double per 4096-entry chunk and per segment, plus one, rounded to 256 bytes
+    for numel, nseg in [(1, 1), (4096, 1), (4097, 2), (58720256, 1), (84934656, 48)]:
+        chunks = -(-numel // 4096)
         expect = -(-(chunks + nseg + 1) * 8 // 256) * 256
         assert L.muon_momentum_workspace_bytes(numel, nseg) == expect
 

@@ -35,7 +35,7 @@ def _momentum_case(numel, offsets, m_dtype, g_dtype, beta, alpha, seed):
 
 @pytest.mark.parametrize("m_dtype,g_dtype", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"),
                                              ("bf16", "f32")])
-@pytest.mark.parametrize("offsets", [[0, 1], [0, 7], [0, 8192], [0, 8193], [0, 100003],
+@pytest.mark.parametrize("offsets", [[0, 1], [0, 7], [0, 4096], [0, 4097], [0, 8192], [0, 8193], [0, 100003],
                                      [0, 0, 5, 5, 8200, 8201, 30000, 30000],
                                      [0] + list(np.cumsum([768 * 2304, 768 * 768, 13, 3072 * 768]))])
 def test_momentum(m_dtype, g_dtype, offsets):
