@@ -172,6 +172,40 @@ def test_vote_all_patterns(M):
     assert np.array_equal(got, expect)
 
 
+# ---------------------------------------------------------------------------
+# int8 exchange: the SUM of +-1 signs followed by sign(sum) is the majority
+# vote ([SM] "Mecanismo Central" item 3), so for every pattern of M signs
+# it must give the same bit as the 1-bit vote; the sum itself is fixed by
+# counting: 2 * count(+1) - M, so |sum| <= M and sum = M (mod 2).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", list(range(1, 12)) + [15])
+def test_int8_vote_all_patterns(M):
+    bufs, n, expect = _enumerated_buffers(M)
+    signs = np.stack([np.where(O.unpack_bits(bufs[k], n), 1, -1).astype(np.int8) for k in range(M)])
+    total = O.sum_int8(signs)
+    plus = np.array([bin(j).count("1") for j in range(n)])
+    assert np.array_equal(total.astype(np.int64), 2 * plus - M)
+    assert np.array_equal(O.unpack_bits(O.threshold_pack(total), n), expect)
+
+
+def test_int8_vote_golden_and_limits():
+    # hand-worked: three workers, four entries
+    U = [np.array([0.5, -1.0, 0.0, -0.0]), np.array([-2.0, -3.0, 1.0, np.nan]),
+         np.array([1.0, 4.0, -1.0, -5.0])]
+    signs = np.stack([O.sign_int8(u) for u in U])
+    assert signs.tolist() == [[1, -1, 1, 1], [-1, -1, 1, 1], [1, 1, -1, -1]]
+    assert O.sum_int8(signs).tolist() == [1, -1, 1, 1]
+    assert O.unpack_bits(O.threshold_pack(O.sum_int8(signs)), 4).tolist() == [True, False, True, True]
+    # 127 workers fit int8; 128 do not
+    assert O.sum_int8(np.ones((127, 3), np.int8)).tolist() == [127, 127, 127]
+    assert O.sum_int8(-np.ones((127, 1), np.int8)).tolist() == [-127]
+    with pytest.raises(ValueError):
+        O.sum_int8(np.ones((128, 1), np.int8))
+    # an even tie (sum 0) votes +1
+    assert O.unpack_bits(O.threshold_pack(np.array([0, -2, 2], np.int8)), 3).tolist() == [True, False, True]
+
+
 def test_vote_loop_matches_and_textbook_majority():
     rng = np.random.default_rng(3)
     n = 200
@@ -402,7 +436,16 @@ def _pins_step():
     test_segment_sums_of_squares()
 
 
+def _pins_int8():
+    for M in [2, 3, 4, 5]:
+        test_int8_vote_all_patterns(M)
+    test_int8_vote_golden_and_limits()
+
+
 MUTANTS = {
+    "int8 sign(0) := -1": ("sign_int8", lambda U: np.where(np.asarray(U).ravel() > 0, 1, -1).astype(np.int8),
+                           _pins_int8),
+    "int8 threshold strict": ("threshold_pack", lambda t: O.pack_bits(np.asarray(t, np.int64) > 0), _pins_int8),
     "direction ignores matrix boundaries": ("worker_direction", lambda M, md, shapes, offs, a, b, c, steps:
         O.newton_schulz(O.decode(M, md).reshape(1, -1), a, b, c, steps).ravel(), _pins_step),
     "segment sums shifted by one entry": ("segment_sumsq", lambda M, offs: np.array(
