@@ -189,6 +189,7 @@ def main():
         tail()
     torch.cuda.synchronize()
 
+    cur_final = wl.ns_steps % 2          # X buffer holding the final direction
     events = []
     t_start = time.perf_counter()
     for _ in range(args.steps):
@@ -296,6 +297,7 @@ def main():
         "roofline": roofline,
         "input_generation_s": gen_s,
     }
+    result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
 
     if args.repeat_kernel:
         name, _, cnt = args.repeat_kernel.partition(":")
@@ -314,6 +316,38 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
+
+
+def int8_exchange(mao, torch, U, wl, n, nwords, dev, reps=10):
+    """The int8 exchange format next to the 1-bit one: sign_int8 of one direction,
+    sum_int8 over the M resident int8 buffers, threshold_pack of the sum; each
+    kernel timed with HIP events on the stream it runs on.  Not part of the step."""
+    M = wl.workers
+    S = torch.empty((M, n), dtype=torch.int8, device=dev)
+    for k in range(M):
+        mao.sign_int8(U, S[k])
+    total = torch.empty(n, dtype=torch.int8, device=dev)
+    vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
+    es = 2 if U.dtype == torch.bfloat16 else 4
+    calls = {
+        "sign_int8": (lambda: mao.sign_int8(U, S[0]), n * (es + 1)),
+        "sum_int8": (lambda: mao.sum_int8(S, total), n * (M + 1)),
+        "threshold_pack": (lambda: mao.threshold_pack(total, vote), n + nwords * 8),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    out["payload_bytes_per_worker"] = {"fp32": 4 * n, "int8": n, "packed_bits": nwords * 8}
+    return out
 
 
 def cpu_baseline(wl):

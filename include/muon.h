@@ -55,6 +55,8 @@ enum muon_status {
 #define MUON_NS_PAD 256
 /* Largest worker count accepted by the vote calls. */
 #define MUON_MAX_VOTERS 1023
+/* most workers whose int8 signs can be summed in int8 */
+#define MUON_INT8_MAX_VOTERS 127
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* muon_status_string(int status);
@@ -203,6 +205,30 @@ int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits,
  * writing the vote bits.  Same result as majority_vote then apply_update. */
 int vote_and_update(void* W, int w_dtype, int64_t numel, const uint64_t* bits, int M,
                     float eta, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The int8 exchange format ([SM] "Mecanismo Central" item 3; "Fluxo" step 3,
+ * the all-reduce variant; "Eficiência de Comunicação": 8 bits per entry,
+ * 4x less than fp32).  Each worker's signs travel as int8 +1/-1, an integer
+ * SUM all-reduce adds them, and each worker thresholds the sum locally.  On
+ * one GPU the M workers' int8 buffers are resident and sum_int8 forms the
+ * sum the all-reduce would deliver.  threshold_pack(sum_int8(sign_int8(U_k)))
+ * equals majority_vote(sign_pack(U_k)) bit for bit.
+ *
+ * sign_int8       S[i] = +1 if !(U[i] < 0) (the rule of sign_pack), else -1.
+ *                 U device, numel entries of u_dtype; S device int8[numel].
+ * sum_int8        out[i] = sum_k S[k*numel + i] for 1 <= M <=
+ *                 MUON_INT8_MAX_VOTERS (the sum fits int8; larger M:
+ *                 MUON_EINVAL).  S device int8[M][numel]; out device int8[numel].
+ * threshold_pack  bit i of bits = 1 iff sum[i] >= 0 (sign(0) := +1), in the
+ *                 layout of sign_pack; padding bits 0.  sum device
+ *                 int8[numel]; bits device uint64[ceil(numel/64)], ready for
+ *                 apply_update.
+ * All pointers 16-byte aligned (MUON_EALIGN).  Bit-exact.
+ * ------------------------------------------------------------------------- */
+int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream);
+int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream);
+int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,4 +10,5 @@ from ._abi import (  # noqa: F401
     ns_gram, ns_normalize, ns_orthogonalize, ns_poly, ns_workspace_bytes, packed_words,
     sign_pack, status_string, vote_and_update,
 )
+from ._abi import MUON_INT8_MAX_VOTERS, sign_int8, sum_int8, threshold_pack  # noqa: F401
 from .signmuon import SignMuonStep  # noqa: F401

@@ -64,6 +64,9 @@ SIGNATURES = {
     "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
     "vote_and_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_int, _c_float,
                                  _c_void_p]),
+    "sign_int8": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
+    "sum_int8": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
+    "threshold_pack": (_c_int, [_c_void_p, _c_i64, _c_void_p, _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -288,3 +291,40 @@ def vote_and_update(W: torch.Tensor, bits: torch.Tensor, eta: float, stream=None
 
 def muon_version() -> int:
     return int(lib().muon_version())
+
+
+# ---------------------------------------------------------------------------
+# int8 exchange format
+# ---------------------------------------------------------------------------
+
+MUON_INT8_MAX_VOTERS = 127
+
+
+def _int8(t: torch.Tensor, name: str) -> int:
+    if t.dtype != torch.int8:
+        raise TypeError(f"{name} must be an int8 tensor")
+    return _dev(t, name)
+
+
+def sign_int8(U: torch.Tensor, S: torch.Tensor, stream=None) -> None:
+    """S[i] = +1 if !(U[i] < 0) else -1 (int8)."""
+    if S.numel() < U.numel():
+        raise ValueError("S needs one int8 per entry of U")
+    _check("sign_int8", lib().sign_int8(_dev(U, "U"), dtype_code(U), U.numel(), _int8(S, "S"),
+                                        _stream(stream)))
+
+
+def sum_int8(S: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out = sum over the rows of S ([M, n] int8), as the SUM all-reduce delivers it."""
+    if S.dim() != 2 or out.numel() < S.shape[1]:
+        raise ValueError("S must be [M, n] and out hold n entries")
+    _check("sum_int8", lib().sum_int8(_int8(S, "S"), S.shape[0], S.shape[1], _int8(out, "out"),
+                                      _stream(stream)))
+
+
+def threshold_pack(total: torch.Tensor, bits: torch.Tensor, stream=None) -> None:
+    """Packed vote bits: bit i = 1 iff total[i] >= 0."""
+    if bits.numel() < packed_words(total.numel()):
+        raise ValueError("bits too small")
+    _check("threshold_pack", lib().threshold_pack(_int8(total, "sum"), total.numel(),
+                                                  _dev(bits, "bits"), _stream(stream)))

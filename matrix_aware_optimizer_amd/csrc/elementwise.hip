@@ -438,6 +438,101 @@ __global__ __launch_bounds__(kThreads) void vote_update_kernel(T* __restrict__ W
   update8<T>(W, e0, numel, counter_ge<NB>(cnt, (M + 1) >> 1) & 0xffu, eta);
 }
 
+// ---------------------------------------------------------------------------
+// int8 exchange format: signs as int8 +-1, their SUM over the workers, and
+// the local threshold of the sum packed to bits.
+// ---------------------------------------------------------------------------
+constexpr int kInt8PerLane = 16;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sign_int8_kernel(const T* __restrict__ U, int64_t numel,
+                                                            int8_t* __restrict__ S) {
+  const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * kInt8PerLane;
+  if (e0 >= numel) return;
+  if (e0 + kInt8PerLane <= numel) {
+    // bit q of the two bytes of entries is 1 for +1; byte = 0x01 (+1) or 0xff (-1)
+    const uint32_t lo = SignByte<T>::full(U + e0), hi = SignByte<T>::full(U + e0 + 8);
+    const uint32_t bitsv = lo | (hi << 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v |= (((bitsv >> (4 * d + b)) & 1u) ? 0x01u : 0xffu) << (8 * b);
+      w[d] = v;
+    }
+    *reinterpret_cast<uint4*>(S + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    for (int q = 0; e0 + q < numel; ++q) S[e0 + q] = SignByte<T>::one(U + e0 + q) ? int8_t(1) : int8_t(-1);
+  }
+}
+
+// per-byte addition modulo 256 of four int8 lanes packed in a word: exact
+// for sums that fit int8
+__device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b) {
+  return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
+}
+__device__ __forceinline__ uint4 add_bytes(uint4 a, uint4 b) {
+  return make_uint4(add_bytes(a.x, b.x), add_bytes(a.y, b.y), add_bytes(a.z, b.z), add_bytes(a.w, b.w));
+}
+
+// rows of 16-byte multiples: 16 sums per lane, rows read four at a time
+__global__ __launch_bounds__(kThreads) void sum_int8_kernel(const uint4* __restrict__ S, int M,
+                                                           int64_t nvec, uint4* __restrict__ out) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= nvec) return;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  int k = 0;
+  for (; k + 4 <= M; k += 4) {
+    uint4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = S[int64_t(k + j) * nvec + t];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = add_bytes(acc, x[j]);
+  }
+  for (; k < M; ++k) acc = add_bytes(acc, S[int64_t(k) * nvec + t]);
+  out[t] = acc;
+}
+
+// any length: one sum per lane
+__global__ __launch_bounds__(kThreads) void sum_int8_bytes_kernel(const int8_t* __restrict__ S, int M,
+                                                                 int64_t numel, int8_t* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= numel) return;
+  int acc = 0;
+  for (int k = 0; k < M; ++k) acc += S[int64_t(k) * numel + i];
+  out[i] = static_cast<int8_t>(acc);
+}
+
+// bit i = 1 iff sum[i] >= 0; 16 sums per lane (one 16-byte load), four lanes
+// per 64-bit word
+__device__ __forceinline__ uint32_t nonneg_nibble(uint32_t x) {   // 4 int8 lanes -> 4 bits
+  const uint32_t sgn = ((x >> 7) & 1u) | ((x >> 14) & 2u) | ((x >> 21) & 4u) | ((x >> 28) & 8u);
+  return ~sgn & 0xfu;
+}
+
+__global__ __launch_bounds__(kThreads) void threshold_pack_kernel(const int8_t* __restrict__ sum,
+                                                                 int64_t numel, uint64_t* __restrict__ bits,
+                                                                 int64_t nwords) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = t * 16;
+  uint32_t v = 0;
+  if (e0 + 16 <= numel) {
+    const uint4 x = *reinterpret_cast<const uint4*>(sum + e0);
+    v = nonneg_nibble(x.x) | (nonneg_nibble(x.y) << 4) | (nonneg_nibble(x.z) << 8) |
+        (nonneg_nibble(x.w) << 12);
+  } else {
+    for (int q = 0; q < 16; ++q)
+      if (e0 + q < numel) v |= (sum[e0 + q] >= 0 ? 1u : 0u) << q;
+  }
+  v |= static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 1, kWave)) << 16;
+  const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 2, kWave));
+  if ((threadIdx.x & 3) == 0) {
+    const int64_t w = e0 >> 6;
+    if (w < nwords) bits[w] = static_cast<uint64_t>(v) | (static_cast<uint64_t>(hi) << 32);
+  }
+}
+
 int planes_for(int M) {
   int nb = 1;
   while ((1 << nb) <= M) ++nb;
@@ -636,5 +731,50 @@ const char* muon_status_string(int status) {
 }
 
 int muon_version(void) { return 100; }
+
+
+int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(u_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!U || !S) return MUON_EINVAL;
+  if (!aligned16(U) || !aligned16(S)) return MUON_EALIGN;
+  const int64_t lanes = (numel + kInt8PerLane - 1) / kInt8PerLane;
+  const int64_t blocks = (lanes + kThreads - 1) / kThreads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (u_dtype == MUON_BF16)
+    sign_int8_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const bf16_t*>(U), numel, S);
+  else
+    sign_int8_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const float*>(U), numel, S);
+  return launch_status();
+}
+
+int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream) {
+  if (numel < 0 || M < 1 || M > MUON_INT8_MAX_VOTERS) return MUON_EINVAL;
+  if (numel == 0) return MUON_OK;
+  if (!S || !out) return MUON_EINVAL;
+  if (!aligned16(S) || !aligned16(out)) return MUON_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (numel % 16 == 0) {
+    const int64_t nvec = numel / 16;
+    sum_int8_kernel<<<dim3((nvec + kThreads - 1) / kThreads), dim3(kThreads), 0, st>>>(
+        reinterpret_cast<const uint4*>(S), M, nvec, reinterpret_cast<uint4*>(out));
+  } else {
+    sum_int8_bytes_kernel<<<dim3((numel + kThreads - 1) / kThreads), dim3(kThreads), 0, st>>>(S, M, numel, out);
+  }
+  return launch_status();
+}
+
+int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (numel == 0) return MUON_OK;
+  if (!sum || !bits) return MUON_EINVAL;
+  if (!aligned16(sum) || !aligned16(bits)) return MUON_EALIGN;
+  const int64_t nwords = (numel + 63) / 64;
+  const int64_t blocks = (nwords * 4 + kThreads - 1) / kThreads;
+  threshold_pack_kernel<<<dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
+      sum, numel, bits, nwords);
+  return launch_status();
+}
 
 }  // extern "C"

@@ -166,3 +166,17 @@ def test_binding_rejects_host_tensors():
         mao.sign_pack(t, torch.zeros(1, dtype=torch.int64))
     with pytest.raises(TypeError):
         _abi.dtype_code(torch.zeros(2, dtype=torch.float16))
+
+
+def test_int8_exchange_validation(L):
+    assert L.sign_int8(A1, 1, -1, A2, None) == EINVAL
+    assert L.sign_int8(A1, 5, 16, A2, None) == EDTYPE
+    assert L.sign_int8(MISALIGNED, 1, 16, A2, None) == EALIGN
+    assert L.sign_int8(None, 1, 0, None, None) == OK
+    assert L.sum_int8(A1, 0, 16, A2, None) == EINVAL
+    assert L.sum_int8(A1, 128, 16, A2, None) == EINVAL          # the int8 sum of 128 signs can overflow
+    assert L.sum_int8(A1, 3, 16, MISALIGNED, None) == EALIGN
+    assert L.threshold_pack(A1, -1, A2, None) == EINVAL
+    assert L.threshold_pack(A1, 10, None, None) == EINVAL
+    assert L.threshold_pack(MISALIGNED, 10, A2, None) == EALIGN
+    assert mao.MUON_INT8_MAX_VOTERS == 127
