@@ -315,6 +315,48 @@ def threshold_pack(total: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Local re-orthogonalisation of the vote.  [SM] Fluxo step 5 (optional): each
+# worker may apply a local polar step to the aggregated sign matrix, at no
+# communication cost.  Reading: per matrix, S_bar (+-1) goes through the same
+# Newton-Schulz iteration as the momentum, and the update becomes
+# W <- W - eta * NS(S_bar).  ||S_bar||_F = sqrt(rows * cols) exactly.
+# ---------------------------------------------------------------------------
+
+
+def unpack_signs(vote_words: np.ndarray, n: int) -> np.ndarray:
+    """The vote as a float64 vector of +1 / -1 (bit 1 -> +1)."""
+    return np.where(unpack_bits(vote_words, n), 1.0, -1.0)
+
+
+def apply_update_dense(W_stored: np.ndarray, w_dtype: str, U_stored: np.ndarray, u_dtype: str,
+                       eta: float) -> np.ndarray:
+    """New stored weights ``round_storage(W - eta * U)``.
+
+    W, eta and U are fp32 values, so eta * U is exact in float64; the float64
+    difference is rounded once, then to float32 (and to bfloat16 for bf16
+    storage)."""
+    W = decode(W_stored, w_dtype).ravel()
+    U = decode(U_stored, u_dtype).ravel()
+    eta64 = float(np.float32(eta))
+    with np.errstate(over="ignore", invalid="ignore"):
+        return round_to_storage(W - eta64 * U, w_dtype).reshape(np.shape(W_stored))
+
+
+def reorthogonalized_direction(vote_words: np.ndarray, shapes: Sequence[Tuple[int, int]],
+                               a: float, b: float, c: float, steps: int) -> np.ndarray:
+    """Flat float64 NS(S_bar) of every matrix of the set."""
+    sizes = [r * cc for r, cc in shapes]
+    n = int(np.sum(sizes))
+    S = unpack_signs(vote_words, n)
+    out = np.empty(n)
+    off = 0
+    for (r, cc), size in zip(shapes, sizes):
+        out[off:off + size] = newton_schulz(S[off:off + size].reshape(r, cc), a, b, c, steps).ravel()
+        off += size
+    return out
+
+
+# ---------------------------------------------------------------------------
 # The whole step for one worker and for M simulated workers.
 # ---------------------------------------------------------------------------
 
@@ -362,4 +404,5 @@ __all__ = [
     "sign_bits", "pack_bits", "unpack_bits", "pack_bits_loop", "sign_pack",
     "majority_vote", "majority_vote_loop", "apply_update", "worker_direction",
     "signmuon_step", "INT8_MAX_VOTERS", "sign_int8", "sum_int8", "threshold_pack",
+    "unpack_signs", "apply_update_dense", "reorthogonalized_direction",
 ]

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle.muon_oracle as O
-from workloads import CUBIC, QUINTIC, random_matrix
+from workloads import CUBIC, QUINTIC, random_matrix, store
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -411,6 +411,45 @@ def test_segment_sums_of_squares():
 
 
 # ---------------------------------------------------------------------------
+# Local re-orthogonalisation of the vote ([SM] Fluxo step 5).  A rank-1 vote
+# matrix S = u v^T (u, v vectors of +-1) has the single singular value
+# ||S||_F = sqrt(rows * cols), so NS(S) = phi(1) * S / sqrt(rows * cols)
+# exactly; the dense update is W - eta * U with one rounding.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("coeffs,steps", [(QUINTIC, 5), (CUBIC, 3)])
+def test_reorthogonalized_direction_on_rank_one_votes(coeffs, steps):
+    shapes = [(4, 6), (5, 3), (1, 7)]
+    rng = np.random.default_rng(41)
+    mats = []
+    for r, c in shapes:
+        u, v = rng.choice([-1.0, 1.0], r), rng.choice([-1.0, 1.0], c)
+        mats.append(np.outer(u, v))
+    flat = np.concatenate([m.ravel() for m in mats])
+    words = O.pack_bits(flat > 0)
+    assert np.array_equal(O.unpack_signs(words, flat.size), flat)
+    got = O.reorthogonalized_direction(words, shapes, *coeffs, steps)
+    phi1 = scalar_map(1.0, coeffs, steps)
+    want = np.concatenate([phi1 * m.ravel() / math.sqrt(m.size) for m in mats])
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+def test_apply_update_dense_values():
+    W = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    U = np.array([0.25, -0.5, 0.0, 1.0], np.float32)
+    eta = float(np.float32(0.02))
+    got = O.apply_update_dense(W, "f32", U, "f32", eta)
+    # each difference worked out in float64 then rounded to float32 once
+    want = np.array([1.0 - eta * 0.25, -2.0 + eta * 0.5, 0.5, 3.0 - eta], np.float64).astype(np.float32)
+    assert got.tolist() == want.tolist()
+    assert np.array_equal(O.apply_update_dense(W, "f32", U, "f32", 0.0), W)
+    # bf16 storage: 1.0 - 0.02 * 0.25 = 0.995 rounds to the bf16 value 0.99609375
+    Wb = store(np.array([1.0]), "bf16")
+    Ub = store(np.array([0.25]), "bf16")
+    assert O.decode(O.apply_update_dense(Wb, "bf16", Ub, "bf16", eta), "bf16").tolist() == [0.99609375]
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each breaks one oracle function; some pin must fail.
 # ---------------------------------------------------------------------------
 
@@ -442,7 +481,16 @@ def _pins_int8():
     test_int8_vote_golden_and_limits()
 
 
+def _pins_reorth():
+    test_reorthogonalized_direction_on_rank_one_votes(QUINTIC, 5)
+    test_apply_update_dense_values()
+
+
 MUTANTS = {
+    "dense update adds": ("apply_update_dense", lambda W, wd, U, ud, eta: O.round_to_storage(
+        O.decode(W, wd).ravel() + float(np.float32(eta)) * O.decode(U, ud).ravel(), wd), _pins_reorth),
+    "unpack signs inverted": ("unpack_signs", lambda w, n: np.where(O.unpack_bits(w, n), -1.0, 1.0),
+                              _pins_reorth),
     "int8 sign(0) := -1": ("sign_int8", lambda U: np.where(np.asarray(U).ravel() > 0, 1, -1).astype(np.int8),
                            _pins_int8),
     "int8 threshold strict": ("threshold_pack", lambda t: O.pack_bits(np.asarray(t, np.int64) > 0), _pins_int8),
