@@ -298,6 +298,7 @@ def main():
         "input_generation_s": gen_s,
     }
     result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
+    result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
 
     if args.repeat_kernel:
         name, _, cnt = args.repeat_kernel.partition(":")
@@ -348,6 +349,39 @@ def int8_exchange(mao, torch, U, wl, n, nwords, dev, reps=10):
         out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
     out["payload_bytes_per_worker"] = {"fp32": 4 * n, "int8": n, "packed_bits": nwords * 8}
     return out
+
+
+def reorth_update(mao, torch, wl, W, vote, dev, reps=3):
+    """The optional local re-orthogonalisation of the vote: unpack_signs, Newton-Schulz
+    of the +-1 matrix, apply_update_dense; timed as a whole and kernel by kernel
+    (HIP events on the stream the kernels run on).  Not part of the step."""
+    step = mao.SignMuonStep(wl.shapes, m_dtype=wl.precision, precision=wl.precision,
+                            coeffs=wl.coeffs, ns_steps=wl.ns_steps, beta=wl.beta, alpha=wl.alpha,
+                            eta=wl.eta, device=dev)
+    Wc = W.clone()
+    step.reorthogonalized_update(Wc, vote)          # allocates its buffers
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    n = step.numel
+    es_u = step.U.element_size()
+    es_w = W.element_size()
+    whole = timed(lambda: step.reorthogonalized_update(Wc, vote))
+    unpack = timed(lambda: mao.unpack_signs(vote, step._sbar))
+    dense = timed(lambda: mao.apply_update_dense(Wc, step.U, wl.eta))
+    gbs_u = (n * es_u + n / 8) / (unpack * 1e-3) / 1e9
+    gbs_d = (n * (2 * es_w + es_u)) / (dense * 1e-3) / 1e9
+    return {"ms": whole,
+            "unpack_signs": {"ms": unpack, "GB/s": gbs_u, "frac_hbm": gbs_u / PEAK_HBM_GBS},
+            "apply_update_dense": {"ms": dense, "GB/s": gbs_d, "frac_hbm": gbs_d / PEAK_HBM_GBS}}
 
 
 def cpu_baseline(wl):

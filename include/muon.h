@@ -230,6 +230,28 @@ int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream
 int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream);
 int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Local re-orthogonalisation of the vote ([SM] "Fluxo" step 5, optional: a
+ * local polar step on the aggregated sign matrix, with no communication).
+ * Per matrix: S_bar (+-1) -> ns_orthogonalize (||S_bar||_F = sqrt(rows*cols))
+ * -> W <- W - eta * NS(S_bar):
+ *     unpack_signs(vote, ...)  ->  ns_orthogonalize(S_bar -> U)  ->
+ *     apply_update_dense(W, U, eta)
+ *
+ * unpack_signs        out[i] = +1 if bit i of bits is 1, else -1, as
+ *                     out_dtype (F32 or BF16; exact).  bits device
+ *                     uint64[ceil(numel/64)]; out device, numel entries.
+ * apply_update_dense  W[i] <- round_w(fp64(W[i]) - fp64(eta) * fp64(U[i])):
+ *                     eta * U is exact in fp64, the difference is rounded
+ *                     once to fp32, then (bf16 storage) to bf16.  W device,
+ *                     numel of w_dtype, in place; U device, numel of u_dtype.
+ *                     Bit-exact.
+ * All pointers 16-byte aligned (MUON_EALIGN).
+ * ------------------------------------------------------------------------- */
+int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, void* stream);
+int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u_dtype, float eta,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,4 +11,5 @@ from ._abi import (  # noqa: F401
     sign_pack, status_string, vote_and_update,
 )
 from ._abi import MUON_INT8_MAX_VOTERS, sign_int8, sum_int8, threshold_pack  # noqa: F401
+from ._abi import apply_update_dense, unpack_signs  # noqa: F401
 from .signmuon import SignMuonStep  # noqa: F401

@@ -67,6 +67,8 @@ SIGNATURES = {
     "sign_int8": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "sum_int8": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "threshold_pack": (_c_int, [_c_void_p, _c_i64, _c_void_p, _c_void_p]),
+    "unpack_signs": (_c_int, [_c_void_p, _c_i64, _c_void_p, _c_int, _c_void_p]),
+    "apply_update_dense": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_int, _c_float, _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -328,3 +330,24 @@ def threshold_pack(total: torch.Tensor, bits: torch.Tensor, stream=None) -> None
         raise ValueError("bits too small")
     _check("threshold_pack", lib().threshold_pack(_int8(total, "sum"), total.numel(),
                                                   _dev(bits, "bits"), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# local re-orthogonalisation of the vote
+# ---------------------------------------------------------------------------
+
+def unpack_signs(vote_bits: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out[i] = +1 if vote bit i is set, else -1 (bf16 or fp32)."""
+    if vote_bits.numel() < packed_words(out.numel()):
+        raise ValueError("vote_bits too small")
+    _check("unpack_signs", lib().unpack_signs(_dev(vote_bits, "vote_bits"), out.numel(), _dev(out, "out"),
+                                              dtype_code(out), _stream(stream)))
+
+
+def apply_update_dense(W: torch.Tensor, U: torch.Tensor, eta: float, stream=None) -> None:
+    """W <- W - eta * U (one rounding in fp64, then to W's type)."""
+    if U.numel() != W.numel():
+        raise ValueError("W and U differ in size")
+    _check("apply_update_dense", lib().apply_update_dense(_dev(W, "W"), dtype_code(W), W.numel(),
+                                                          _dev(U, "U"), dtype_code(U), float(eta),
+                                                          _stream(stream)))

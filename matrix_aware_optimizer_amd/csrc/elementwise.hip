@@ -533,6 +533,54 @@ __global__ __launch_bounds__(kThreads) void threshold_pack_kernel(const int8_t* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Local re-orthogonalisation of the vote: the vote bits as a +-1 matrix, and
+// the dense update W <- W - eta * U.
+// ---------------------------------------------------------------------------
+// 16 entries (two bytes of bits) per lane
+template <typename T>
+__global__ __launch_bounds__(kThreads) void unpack_signs_kernel(const uint8_t* __restrict__ bits,
+                                                               int64_t numel, T* __restrict__ out) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = t * 16;
+  if (e0 >= numel) return;
+  if (e0 + 16 <= numel) {
+    const uint32_t b16 = *reinterpret_cast<const uint16_t*>(bits + 2 * t);
+    float v[2][8];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q >> 3][q & 7] = ((b16 >> q) & 1u) ? 1.0f : -1.0f;
+    Vec8<T>::store(out + e0, v[0]);
+    Vec8<T>::store(out + e0 + 8, v[1]);
+  } else {
+    for (int q = 0; e0 + q < numel; ++q)
+      out[e0 + q] = from_f32<T>(((bits[(e0 + q) >> 3] >> ((e0 + q) & 7)) & 1u) ? 1.0f : -1.0f);
+  }
+}
+
+// W, eta and U are fp32 values: eta * U is exact in fp64, the fp64
+// difference is rounded once, then to fp32 (and bf16 for bf16 storage)
+__device__ __forceinline__ float dense_step(float w, float eta, float u) {
+  return static_cast<float>(static_cast<double>(w) - static_cast<double>(eta) * static_cast<double>(u));
+}
+
+template <typename TW, typename TU>
+__global__ __launch_bounds__(kThreads) void update_dense_kernel(TW* __restrict__ W, int64_t numel,
+                                                               const TU* __restrict__ U, float eta) {
+  const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;
+  if (e0 >= numel) return;
+  if (e0 + 8 <= numel) {
+    float w[8], u[8];
+    Vec8<TW>::load(W + e0, w);
+    Vec8<TU>::load(U + e0, u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = dense_step(w[q], eta, u[q]);
+    Vec8<TW>::store(W + e0, w);
+  } else {
+    for (int q = 0; e0 + q < numel; ++q)
+      W[e0 + q] = from_f32<TW>(dense_step(to_f32(W[e0 + q]), eta, to_f32(U[e0 + q])));
+  }
+}
+
 int planes_for(int M) {
   int nb = 1;
   while ((1 << nb) <= M) ++nb;
@@ -774,6 +822,46 @@ int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* strea
   const int64_t blocks = (nwords * 4 + kThreads - 1) / kThreads;
   threshold_pack_kernel<<<dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
       sum, numel, bits, nwords);
+  return launch_status();
+}
+
+int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(out_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!bits || !out) return MUON_EINVAL;
+  if (!aligned16(bits) || !aligned16(out)) return MUON_EALIGN;
+  const int64_t blocks = ((numel + 15) / 16 + kThreads - 1) / kThreads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
+  if (out_dtype == MUON_BF16)
+    unpack_signs_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(b8, numel, static_cast<bf16_t*>(out));
+  else
+    unpack_signs_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(b8, numel, static_cast<float*>(out));
+  return launch_status();
+}
+
+int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u_dtype, float eta,
+                       void* stream) {
+  if (numel < 0) return MUON_EINVAL;
+  if (!valid_dtype(w_dtype) || !valid_dtype(u_dtype)) return MUON_EDTYPE;
+  if (numel == 0) return MUON_OK;
+  if (!W || !U) return MUON_EINVAL;
+  if (!aligned16(W) || !aligned16(U)) return MUON_EALIGN;
+  const int64_t blocks = ((numel + 7) / 8 + kThreads - 1) / kThreads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (w_dtype == MUON_BF16 && u_dtype == MUON_BF16)
+    update_dense_kernel<bf16_t, bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+        static_cast<bf16_t*>(W), numel, static_cast<const bf16_t*>(U), eta);
+  else if (w_dtype == MUON_BF16)
+    update_dense_kernel<bf16_t, float><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+        static_cast<bf16_t*>(W), numel, static_cast<const float*>(U), eta);
+  else if (u_dtype == MUON_BF16)
+    update_dense_kernel<float, bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+        static_cast<float*>(W), numel, static_cast<const bf16_t*>(U), eta);
+  else
+    update_dense_kernel<float, float><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+        static_cast<float*>(W), numel, static_cast<const float*>(U), eta);
   return launch_status();
 }
 

@@ -5,7 +5,8 @@ torch) and calls the C ABI in the order of the "SignMuon: Otimização
 Distribuída de Muon com Eficiência de Comunicação" summary, section 2,
 "Fluxo Algorítmico (Distribuído)": local momentum and polar factor (step 1),
 sign extraction packed to one bit per entry (steps 2-3), then the majority
-vote and the update (step 4).  All arithmetic runs in libmuon's kernels.
+vote and the update (step 4), optionally with the local re-orthogonalisation
+of the vote (step 5).  All arithmetic runs in libmuon's kernels.
 """
 from __future__ import annotations
 
@@ -87,12 +88,41 @@ class SignMuonStep:
         self.pack(bits_row)
 
     def vote_update(self, W: torch.Tensor, bits: torch.Tensor, vote_out: Optional[torch.Tensor] = None,
-                    fused: bool = False) -> None:
-        """Step 4: majority vote over the rows of ``bits`` and ``W <- W - eta * vote``."""
-        if fused:
+                    fused: bool = False, reorthogonalize: bool = False) -> None:
+        """Step 4: majority vote over the rows of ``bits`` and ``W <- W - eta * vote``.
+
+        With ``reorthogonalize`` the optional step 5 replaces the sign update:
+        ``W <- W - eta * NS(vote)`` per matrix."""
+        if fused and not reorthogonalize:
             _abi.vote_and_update(W, bits, self.eta)
             return
         if vote_out is None:
             vote_out = torch.empty(self.nwords, dtype=torch.int64, device=self.device)
         _abi.majority_vote(bits, vote_out)
-        _abi.apply_update(W, vote_out, self.eta)
+        if reorthogonalize:
+            self.reorthogonalized_update(W, vote_out)
+        else:
+            _abi.apply_update(W, vote_out, self.eta)
+
+    def reorthogonalized_update(self, W: torch.Tensor, vote: torch.Tensor) -> None:
+        """Step 5 of the summary's flow (optional): the vote as a +-1 matrix per
+        weight matrix, orthogonalised locally, then ``W <- W - eta * NS(S_bar)``.
+        The direction is left in ``self.U``."""
+        if getattr(self, "_sbar", None) is None:
+            self._sbar = torch.empty(self.numel, dtype=self.U.dtype, device=self.device)
+            probs = self._sbar_problems()
+            nbytes = _abi.ns_workspace_bytes(probs, self.precision)
+            self._sbar_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        _abi.unpack_signs(vote, self._sbar)
+        a, b, c = self.coeffs
+        _abi.ns_orthogonalize(self._sbar_problems(), a, b, c, self.ns_steps, self.precision,
+                              self._sbar_ws)
+        _abi.apply_update_dense(W, self.U, self.eta)
+
+    def _sbar_problems(self):
+        # the norm of a +-1 matrix is sqrt(rows * cols); the library forms it
+        probs = []
+        for j, (r, c) in enumerate(self.shapes):
+            lo, hi = self.offsets_host[j], self.offsets_host[j + 1]
+            probs.append((self._sbar[lo:hi].view(r, c), self.U[lo:hi].view(r, c), None))
+        return probs

@@ -180,3 +180,14 @@ def test_int8_exchange_validation(L):
     assert L.threshold_pack(A1, 10, None, None) == EINVAL
     assert L.threshold_pack(MISALIGNED, 10, A2, None) == EALIGN
     assert mao.MUON_INT8_MAX_VOTERS == 127
+
+
+def test_reorthogonalisation_validation(L):
+    assert L.unpack_signs(A1, -1, A2, 1, None) == EINVAL
+    assert L.unpack_signs(A1, 10, A2, 4, None) == EDTYPE
+    assert L.unpack_signs(MISALIGNED, 10, A2, 1, None) == EALIGN
+    assert L.unpack_signs(None, 0, None, 1, None) == OK
+    assert L.apply_update_dense(A1, 1, -3, A2, 1, 0.1, None) == EINVAL
+    assert L.apply_update_dense(A1, 1, 10, A2, 7, 0.1, None) == EDTYPE
+    assert L.apply_update_dense(A1, 1, 10, MISALIGNED, 1, 0.1, None) == EALIGN
+    assert L.apply_update_dense(A1, 1, 10, None, 1, 0.1, None) == EINVAL
