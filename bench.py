@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the int8-exchange and re-orthogonalised-update measurements "
+                         "(profiling runs then trace the step's kernels only)")
     ap.add_argument("--repeat-kernel", default=None,
                     help="profiling aid: after the run, launch one stage N more times "
                          "(gram|poly|apply|momentum|pack|vote|update|copy:N)")
@@ -297,8 +300,9 @@ def main():
         "roofline": roofline,
         "input_generation_s": gen_s,
     }
-    result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
-    result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
+    if not args.no_extras:
+        result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
+        result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
 
     if args.repeat_kernel:
         name, _, cnt = args.repeat_kernel.partition(":")
