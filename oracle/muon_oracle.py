@@ -357,6 +357,62 @@ def reorthogonalized_direction(vote_words: np.ndarray, shapes: Sequence[Tuple[in
 
 
 # ---------------------------------------------------------------------------
+# Dion ("대규모 AI 모델 학습을 10배 빠르게: Dion 옵티마이저를 사용한 분산 학습",
+# algorithm steps).  Per weight matrix X (m x n) with momentum M, gradient G
+# and the previous right factor Q (n x r):
+#   B = M + G;  one power iteration warm-started from Q: P = orth(B Q),
+#   R = B^T P;  error feedback M = B - (1 - mu) P R^T;
+#   Q = ColumnNormalize(R);  X = X - eta P Q^T.
+# orth is not spelled out on the page; the reading is the thin QR factor with
+# a non-negative diagonal of R (Gram-Schmidt), where a column whose residual
+# is at most DEPENDENT_TOL of its own norm counts as dependent on the earlier
+# ones and becomes zero.  fp32 storage; arithmetic in float64.
+# ---------------------------------------------------------------------------
+
+DEPENDENT_TOL = 1e-4
+
+
+def orthonormalize_columns(P: np.ndarray) -> np.ndarray:
+    """Columns of P made orthonormal in order (modified Gram-Schmidt, done twice)."""
+    Q = np.array(P, dtype=np.float64, copy=True)
+    r = Q.shape[1]
+    keep = np.ones(r, dtype=bool)
+    for j in range(r):
+        norm0 = np.linalg.norm(Q[:, j])
+        for _ in range(2):                      # a second pass restores orthogonality
+            for i in range(j):
+                if keep[i]:
+                    Q[:, j] -= np.dot(Q[:, i], Q[:, j]) * Q[:, i]
+        nrm = np.linalg.norm(Q[:, j])
+        if nrm <= DEPENDENT_TOL * norm0 or nrm == 0.0:
+            keep[j] = False
+            Q[:, j] = 0.0
+        else:
+            Q[:, j] /= nrm
+    return Q
+
+
+def column_normalize(R: np.ndarray) -> np.ndarray:
+    """Each column divided by its Euclidean norm; a zero column stays zero."""
+    R = np.asarray(R, dtype=np.float64)
+    n = np.linalg.norm(R, axis=0)
+    return np.where(n > 0, R / np.where(n > 0, n, 1.0), 0.0)
+
+
+def dion_step(M: np.ndarray, G: np.ndarray, X: np.ndarray, Q: np.ndarray, mu: float,
+              eta: float) -> dict:
+    """One Dion step on one matrix (fp32 inputs); returns the new stored M, Q, X and P (float64)."""
+    B = round_to_storage(decode(M, "f32") + decode(G, "f32"), "f32").astype(np.float64)
+    P = orthonormalize_columns(B @ np.asarray(Q, np.float64))
+    R = B.T @ P
+    M_new = B - (1.0 - mu) * (P @ R.T)
+    Q_new = column_normalize(R)
+    X_new = decode(X, "f32") - eta * (P @ Q_new.T)
+    return {"B": B, "P": P, "M": round_to_storage(M_new, "f32"), "Q": round_to_storage(Q_new, "f32"),
+            "X": round_to_storage(X_new, "f32")}
+
+
+# ---------------------------------------------------------------------------
 # The whole step for one worker and for M simulated workers.
 # ---------------------------------------------------------------------------
 
@@ -405,4 +461,5 @@ __all__ = [
     "majority_vote", "majority_vote_loop", "apply_update", "worker_direction",
     "signmuon_step", "INT8_MAX_VOTERS", "sign_int8", "sum_int8", "threshold_pack",
     "unpack_signs", "apply_update_dense", "reorthogonalized_direction",
+    "DEPENDENT_TOL", "orthonormalize_columns", "column_normalize", "dion_step",
 ]

@@ -450,6 +450,62 @@ def test_apply_update_dense_values():
 
 
 # ---------------------------------------------------------------------------
+# Dion.  (i) The orthonormalisation is the thin QR factor with a non-negative
+# R diagonal: against numpy's QR (a textbook routine) with its signs fixed.
+# (ii) Closed form: for B = U diag(s) V^T of rank r and a warm start Q = V,
+# the power iteration gives P = U, R = V diag(s), so the error feedback leaves
+# M = mu * B, the new Q is V and the update direction is U V^T.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(6, 3), (40, 8), (9, 9)])
+def test_dion_orthonormalisation_is_qr(shape):
+    P = random_matrix(shape, [60, shape[0]])
+    q, r = np.linalg.qr(P)
+    q = q * np.sign(np.diag(r))                  # R with a non-negative diagonal
+    assert np.allclose(O.orthonormalize_columns(P), q, atol=1e-12)
+    # a column that repeats an earlier one comes out zero
+    P2 = np.concatenate([P[:, :2], P[:, :1]], axis=1)
+    Q2 = O.orthonormalize_columns(P2)
+    assert np.allclose(Q2[:, :2], q[:, :2], atol=1e-12)
+    assert not Q2[:, 2].any()
+    # a zero column stays zero and does not disturb the others
+    P3 = P.copy()
+    P3[:, 1] = 0.0
+    Q3 = O.orthonormalize_columns(P3)
+    assert not Q3[:, 1].any() and np.allclose(np.abs(Q3[:, 0]), np.abs(q[:, 0]), atol=1e-12)
+
+
+def test_dion_column_normalize():
+    R = np.array([[3.0, 0.0, 1.0], [4.0, 0.0, -1.0]])
+    assert np.allclose(O.column_normalize(R), [[0.6, 0.0, 1 / np.sqrt(2)], [0.8, 0.0, -1 / np.sqrt(2)]])
+
+
+@pytest.mark.parametrize("m,n,r", [(12, 20, 3), (30, 10, 4)])
+def test_dion_step_closed_form_on_rank_r(m, n, r):
+    U = np.linalg.qr(random_matrix((m, r), [61, m]))[0]
+    V = np.linalg.qr(random_matrix((n, r), [62, n]))[0]
+    sv = np.array([4.0, 2.0, 1.0, 0.5][:r])
+    B = (U * sv) @ V.T
+    # stored fp32 inputs: G = 0 and M = B exactly representable (scaled to a dyadic grid)
+    B = np.round(B * 2 ** 20) / 2 ** 20
+    M = B.astype(np.float32)
+    Bf = M.astype(np.float64)
+    # recompute the exact factors of the stored (rounded) B
+    u, s_, vt = np.linalg.svd(Bf, full_matrices=False)
+    U, sv, V = u[:, :r], s_[:r], vt[:r].T
+    X = random_matrix((m, n), [63, 0]).astype(np.float32)
+    mu, eta = 0.9, 0.1
+    out = O.dion_step(M, np.zeros_like(M), X, V.astype(np.float32), mu, eta)
+    # the warm start is V rounded to fp32: compare at that precision
+    assert np.allclose(np.abs(out["P"].T @ U), np.eye(r), atol=1e-5)
+    assert np.allclose(out["M"], mu * Bf, rtol=1e-5, atol=1e-6 * np.abs(Bf).max())
+    signs = np.sign(np.diag(out["P"].T @ U))
+    assert np.allclose(out["Q"] * signs, V, atol=1e-5)
+    dX = out["X"].astype(np.float64) - X.astype(np.float64)
+    assert np.allclose(dX, -eta * U @ V.T, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each breaks one oracle function; some pin must fail.
 # ---------------------------------------------------------------------------
 
@@ -486,7 +542,19 @@ def _pins_reorth():
     test_apply_update_dense_values()
 
 
+def _pins_dion():
+    for shape in [(6, 3), (40, 8)]:
+        test_dion_orthonormalisation_is_qr(shape)
+    test_dion_column_normalize()
+    test_dion_step_closed_form_on_rank_r(12, 20, 3)
+
+
 MUTANTS = {
+    "dion feedback with mu": ("dion_step", lambda M, G, X, Q, mu, eta: _real_dion(M, G, X, Q, 1.0 - mu, eta),
+                              _pins_dion),
+    "dion normalises rows": ("column_normalize", lambda R: (np.asarray(R, float).T / np.maximum(
+        np.linalg.norm(np.asarray(R, float), axis=1), 1e-300)).T, _pins_dion),
+    "dion orth without renormalising": ("orthonormalize_columns", lambda P: np.asarray(P, float), _pins_dion),
     "dense update adds": ("apply_update_dense", lambda W, wd, U, ud, eta: O.round_to_storage(
         O.decode(W, wd).ravel() + float(np.float32(eta)) * O.decode(U, ud).ravel(), wd), _pins_reorth),
     "unpack signs inverted": ("unpack_signs", lambda w, n: np.where(O.unpack_bits(w, n), -1.0, 1.0),
@@ -519,6 +587,11 @@ MUTANTS = {
 }
 
 _REAL_APPLY_UPDATE = O.apply_update
+_REAL_DION = O.dion_step
+
+
+def _real_dion(M, G, X, Q, mu, eta):
+    return _REAL_DION(M, G, X, Q, mu, eta)
 
 
 def _wrong_update(W, dt, v, eta):

@@ -100,6 +100,49 @@ WORKLOADS = {
 }
 
 
+# Dion workload: the page's d = 768 layer set (GPT-2-small shapes), fp32 state,
+# ranks d/4, d/8, d/16.  Roles 0 = W0, 2 = G, 4 = the initial right factor Q0.
+ROLE_Q0 = 4
+
+
+@dataclasses.dataclass(frozen=True)
+class DionWorkload:
+    cfg: int
+    name: str
+    shapes: Tuple[Tuple[int, int], ...]
+    rank: int
+    mu: float = 0.95
+    eta: float = 0.02
+    g_scale: float = 0.02
+    w_scale: float = 0.02
+
+    @property
+    def offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum([r * c for r, c in self.shapes])]).astype(np.int64)
+
+    @property
+    def q_offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum([c * self.rank for _, c in self.shapes])]).astype(np.int64)
+
+    @property
+    def numel(self) -> int:
+        return int(self.offsets[-1])
+
+
+DION_WORKLOADS = {
+    r: DionWorkload(100 + r, f"GPT-2-small layer set, fp32, rank {r}", _gpt2_small_shapes(), r)
+    for r in (192, 96, 48)
+}
+
+
+def gen_dion(wl: DionWorkload, step: int = 0) -> dict:
+    """W0 and G (flat, fp32, N(0, scale^2)) and Q0 (flat, fp32, N(0, 1)): seeded inputs."""
+    W0 = store(_draw("normal", wl.numel, [wl.cfg, ROLE_W0, 0, 0]) * wl.w_scale, "f32")
+    G = store(_draw("normal", wl.numel, [wl.cfg, ROLE_G, 0, step]) * wl.g_scale, "f32")
+    Q0 = store(_draw("normal", int(wl.q_offsets[-1]), [wl.cfg, ROLE_Q0, 0, 0]), "f32")
+    return {"W0": W0, "G": G, "Q0": Q0}
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); NaN stays a quiet NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -217,7 +260,7 @@ def random_matrix(shape: Tuple[int, ...], seed: Sequence[int], dist: str = "norm
 
 
 __all__ = [
-    "Workload", "WORKLOADS", "CUBIC", "QUINTIC", "CHUNK", "f32_to_bf16_bits",
+    "Workload", "WORKLOADS", "CUBIC", "QUINTIC", "DionWorkload", "DION_WORKLOADS", "gen_dion", "CHUNK", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "store", "to_f64", "gen_W0", "gen_M0", "gen_G", "heavy_columns",
     "small_workload", "random_matrix",
 ]
