@@ -303,6 +303,7 @@ def main():
     if not args.no_extras:
         result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
         result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
+        result["dion"] = dion_bench(mao, torch, dev)
 
     if args.repeat_kernel:
         name, _, cnt = args.repeat_kernel.partition(":")
@@ -386,6 +387,41 @@ def reorth_update(mao, torch, wl, W, vote, dev, reps=3):
     return {"ms": whole,
             "unpack_signs": {"ms": unpack, "GB/s": gbs_u, "frac_hbm": gbs_u / PEAK_HBM_GBS},
             "apply_update_dense": {"ms": dense, "GB/s": gbs_d, "frac_hbm": gbs_d / PEAK_HBM_GBS}}
+
+
+def dion_bench(mao, torch, dev, reps=5):
+    """One Dion step on the d = 768 layer set (48 fp32 matrices, one batched call per
+    shape) at ranks d/4, d/8, d/16; HIP events on the stream it runs on.  Algorithmic
+    flops per matrix: B Q, B^T P, P R^T, P Q^T (2mnr each) and two Cholesky-QR
+    passes (Gram and P L^-T, 2mr^2 each)."""
+    from workloads import DION_WORKLOADS, gen_dion
+    out = {}
+    for rank in (192, 96, 48):
+        wl = DION_WORKLOADS[rank]
+        inp = gen_dion(wl)
+        offs, qoffs = wl.offsets, wl.q_offsets
+        M = torch.zeros(wl.numel, dtype=torch.float32, device=dev)
+        G = torch.from_numpy(inp["G"]).to(dev)
+        X = torch.from_numpy(inp["W0"]).to(dev)
+        Q = torch.from_numpy(inp["Q0"]).to(dev)
+        probs = [(M[offs[j]:offs[j + 1]].view(r, c), G[offs[j]:offs[j + 1]].view(r, c),
+                  X[offs[j]:offs[j + 1]].view(r, c), Q[qoffs[j]:qoffs[j + 1]].view(c, rank))
+                 for j, (r, c) in enumerate(wl.shapes)]
+        ws = torch.empty(mao.dion_workspace_bytes(probs, rank), dtype=torch.uint8, device=dev)
+        mao.dion_step(probs, rank, wl.mu, wl.eta, ws)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            mao.dion_step(probs, rank, wl.mu, wl.eta, ws)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        flops = sum(8 * r * c * rank + 8 * r * rank * rank for r, c in wl.shapes)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"rank_{rank}"] = {"ms": ms, "TFLOP/s": tf, "frac_fp32_peak": tf / PEAK_F32_TFLOPS,
+                               "workload": wl.name}
+    return out
 
 
 def cpu_baseline(wl):

@@ -252,6 +252,42 @@ int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, 
 int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u_dtype, float eta,
                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Dion (the Dion page's algorithm: low-rank power iteration with error
+ * feedback), fp32.  Per matrix X (rows m x cols n) with momentum M, gradient
+ * G and previous right factor Q (n x rank, row-major):
+ *     B = M + G                      (rounded once to fp32; stored in M)
+ *     P = orth(B Q)                  (m x rank; thin QR factor, R diagonal >= 0)
+ *     R = B^T P                      (n x rank)
+ *     M = B - (1 - mu) P R^T         (error feedback)
+ *     Q = ColumnNormalize(R)         (zero columns stay zero)
+ *     X = X - eta P Q^T
+ * orth: Cholesky-QR applied twice; a column whose residual is at most 1e-4
+ * of its own norm counts as dependent and becomes zero.  The page does not
+ * spell out the orthonormalisation; this is the thin QR factor.
+ *
+ * problem    M, G, X device fp32 m x n (M, X updated in place, G read);
+ *            Q device fp32 n x rank (read as Q_{t-1}, written as Q_t).
+ * rank       1 .. MUON_DION_MAX_RANK (the Gram of P is factored in LDS).
+ * Problems of equal shape whose M, G, X and Q advance by constant strides
+ * (in order of shape and address) run batched.  Pointers 16-byte aligned.
+ * workspace  dion_workspace_bytes(probs, count, rank) bytes.
+ * ------------------------------------------------------------------------- */
+#define MUON_DION_MAX_RANK 192
+
+typedef struct muon_dion_problem {
+  void* M;
+  const void* G;
+  void* X;
+  void* Q;
+  int64_t rows;
+  int64_t cols;
+} muon_dion_problem;
+
+size_t dion_workspace_bytes(const muon_dion_problem* probs, int count, int rank);
+int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, float eta,
+              void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

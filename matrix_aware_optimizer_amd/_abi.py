@@ -69,6 +69,9 @@ SIGNATURES = {
     "threshold_pack": (_c_int, [_c_void_p, _c_i64, _c_void_p, _c_void_p]),
     "unpack_signs": (_c_int, [_c_void_p, _c_i64, _c_void_p, _c_int, _c_void_p]),
     "apply_update_dense": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_int, _c_float, _c_void_p]),
+    "dion_workspace_bytes": (_c_size, [ctypes.c_void_p, _c_int, _c_int]),
+    "dion_step": (_c_int, [ctypes.c_void_p, _c_int, _c_int, _c_float, _c_float, _c_void_p, _c_size,
+                           _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -351,3 +354,46 @@ def apply_update_dense(W: torch.Tensor, U: torch.Tensor, eta: float, stream=None
     _check("apply_update_dense", lib().apply_update_dense(_dev(W, "W"), dtype_code(W), W.numel(),
                                                           _dev(U, "U"), dtype_code(U), float(eta),
                                                           _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Dion
+# ---------------------------------------------------------------------------
+
+MUON_DION_MAX_RANK = 192
+
+
+class DionProblem(ctypes.Structure):
+    _fields_ = [("M", _c_void_p), ("G", _c_void_p), ("X", _c_void_p), ("Q", _c_void_p),
+                ("rows", _c_i64), ("cols", _c_i64)]
+
+
+def _dion_problems(problems):
+    arr = (DionProblem * len(problems))()
+    for i, (M, G, X, Q) in enumerate(problems):
+        for name, t in (("M", M), ("G", G), ("X", X), ("Q", Q)):
+            if t.dtype != torch.float32:
+                raise TypeError(f"Dion tensors are fp32 ({name})")
+        if M.dim() != 2 or G.shape != M.shape or X.shape != M.shape or Q.dim() != 2 or Q.shape[0] != M.shape[1]:
+            raise ValueError("Dion problem shapes: M, G, X m x n and Q n x rank")
+        arr[i].M, arr[i].G, arr[i].X, arr[i].Q = (_dev(M, "M"), _dev(G, "G"), _dev(X, "X"), _dev(Q, "Q"))
+        arr[i].rows, arr[i].cols = M.shape
+    return arr
+
+
+def dion_workspace_bytes(problems, rank: int) -> int:
+    arr = _dion_problems(problems)
+    return int(lib().dion_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(problems), int(rank)))
+
+
+def dion_step(problems, rank: int, mu: float, eta: float, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> None:
+    """One Dion step on every (M, G, X, Q) problem (fp32 tensors; M, X, Q updated in place)."""
+    if not problems:
+        return
+    arr = _dion_problems(problems)
+    nbytes = int(lib().dion_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(problems), int(rank)))
+    ws = _workspace(nbytes, problems[0][0], workspace)
+    _check("dion_step", lib().dion_step(ctypes.cast(arr, ctypes.c_void_p), len(problems), int(rank),
+                                        float(mu), float(eta), _dev(ws, "workspace"),
+                                        ws.numel() * ws.element_size(), _stream(stream)))

@@ -18,7 +18,7 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmuon.so")
-SOURCES = ["elementwise.hip", "ns.hip"]
+SOURCES = ["elementwise.hip", "ns.hip", "dion.hip"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,469 @@
+// Dion step on the GPU (the Dion page's algorithm: a low-rank power iteration
+// with error feedback).  Per weight matrix X (m x n, fp32) with momentum M,
+// gradient G and the previous right factor Q (n x r):
+//
+//   B = M + G                                (in place in M)
+//   P = orth(B Q)                            (thin QR factor, Cholesky-QR twice)
+//   R = B^T P
+//   M = B - (1 - mu) P R^T                   (error feedback)
+//   Q = ColumnNormalize(R)
+//   X = X - eta P Q^T
+//
+// These products are skinny (r <= 192 against m, n of a few thousand) and
+// small, so they run in fp32 on one tiled kernel with arbitrary element
+// strides (the transposes are strides, never copies).  orth(P): the Gram
+// P^T P is factored L L^T in LDS by one workgroup per matrix, L is inverted
+// in place, and P <- P L^-T; the second pass restores orthogonality lost to
+// fp32 rounding.  A column whose Gram-Schmidt residual (the Cholesky pivot)
+// is at most 1e-4 of its own norm counts as dependent and is zeroed.
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+namespace muon {
+namespace {
+
+constexpr int kDionMaxRank = MUON_DION_MAX_RANK;
+constexpr float kDependentTol = 1e-4f;
+
+// ---------------------------------------------------------------------------
+// C[b](i,j) = alpha * sum_k A[b](i,k) B[b](k,j) + beta * Z[b](i,j)
+// A(i,k) = A[b*sA + i*a_i + k*a_k], B(k,j) = B[b*sB + k*b_k + j*b_j];
+// C and Z row-major with their own leading dimensions (Z may alias C).
+// ---------------------------------------------------------------------------
+struct DGemm {
+  const float* A;
+  int64_t sA, a_i, a_k;
+  const float* B;
+  int64_t sB, b_k, b_j;
+  const float* Z;
+  int64_t sZ, ldz;
+  float* C;
+  int64_t sC, ldc;
+  int64_t M, N, K;
+  float alpha, beta;
+};
+
+constexpr int kDT = 64;   // output tile
+constexpr int kDK = 32;   // k per LDS tile
+
+// Split k: with `splits` > 1, blockIdx.z = batch * splits + s covers the
+// k-tiles of range s and writes its raw sums to part[s][b] (M x N row-major);
+// reduce_kernel adds the ranges in order and applies alpha, beta.
+__global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, float* part) {
+  __shared__ __attribute__((aligned(16))) float As[kDK][kDT + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[kDK][kDT + 4];
+  const int64_t b = blockIdx.z / splits;
+  const int sp = blockIdx.z % splits;
+  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* A = g.A + b * g.sA;
+  const float* B = g.B + b * g.sB;
+  const int64_t ktiles = (g.K + kDK - 1) / kDK;
+  const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
+  float acc[4][4] = {};
+  for (int64_t k0 = kt0 * kDK; k0 < kt1 * kDK; k0 += kDK) {
+    // each thread loads 8 elements of each tile, consecutive threads along the
+    // operand's contiguous dimension
+#pragma unroll
+    for (int e4 = 0; e4 < kDK * kDT / 256; ++e4) {
+      const int e = tid + 256 * e4;
+      int i, k;
+      if (g.a_k == 1) { i = e / kDK; k = e % kDK; } else { k = e / kDT; i = e % kDT; }
+      const int64_t gi = i0 + i, gk = k0 + k;
+      As[k][i] = (gi < g.M && gk < g.K) ? A[gi * g.a_i + gk * g.a_k] : 0.0f;
+      int j;
+      if (g.b_j == 1) { k = e / kDT; j = e % kDT; } else { j = e / kDK; k = e % kDK; }
+      const int64_t gj = j0 + j, gk2 = k0 + k;
+      Bs[k][j] = (gj < g.N && gk2 < g.K) ? B[gk2 * g.b_k + gj * g.b_j] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kDK; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
+      const float4 bb = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+    }
+    __syncthreads();
+  }
+  if (splits > 1) {
+    float* Pp = part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gi = i0 + ty * 4 + r;
+      if (gi >= g.M) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t gj = j0 + tx * 4 + c;
+        if (gj < g.N) Pp[gi * g.N + gj] = acc[r][c];
+      }
+    }
+    return;
+  }
+  float* C = g.C + b * g.sC;
+  const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t gi = i0 + ty * 4 + r;
+    if (gi >= g.M) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t gj = j0 + tx * 4 + c;
+      if (gj >= g.N) continue;
+      float v = g.alpha * acc[r][c];
+      if (g.beta != 0.0f) v = fmaf(g.beta, Z[gi * g.ldz + gj], v);
+      C[gi * g.ldc + gj] = v;
+    }
+  }
+}
+
+// C[b](i,j) = alpha * sum_s part[s][b](i,j) + beta * Z[b](i,j), ranges added in order
+__global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const float* __restrict__ part,
+                                                    int64_t batch) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per = g.M * g.N;
+  if (t >= batch * per) return;
+  const int64_t b = t / per, e = t % per, i = e / g.N, j = e % g.N;
+  float sum = 0.0f;
+  for (int s = 0; s < splits; ++s) sum += part[(int64_t(s) * batch + b) * per + e];
+  float v = g.alpha * sum;
+  if (g.beta != 0.0f) v = fmaf(g.beta, g.Z[b * g.sZ + i * g.ldz + j], v);
+  g.C[b * g.sC + i * g.ldc + j] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Linv[b] = L^-1 with G[b] = L L^T (r x r, lower triangle of G read).  One
+// workgroup per matrix; L lives in LDS with row pitch r + 1.  Dependent
+// columns (pivot^2 <= tol^2 * G_jj) get a zero column in L, hence a zero row
+// and column in L^-1.  Inversion in place, last column first:
+// column j of L^-1 below the diagonal = -(1 / l_jj) * Linv22 * l_c.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__ G, int64_t sG,
+                                                      float* __restrict__ Linv, int64_t sL, int r) {
+  extern __shared__ float sm[];
+  const int ld = r + 1;
+  float* L = sm;                 // r * ld
+  float* g0 = sm + r * ld;       // original diagonal
+  float* tmp = g0 + r;           // r
+  const float* Gb = G + int64_t(blockIdx.x) * sG;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < r * r; e += 256) {
+    const int i = e / r, k = e % r;
+    L[i * ld + k] = k <= i ? Gb[i * r + k] : 0.0f;
+  }
+  for (int i = tid; i < r; i += 256) g0[i] = Gb[i * r + i];
+  __syncthreads();
+  // Cholesky, right-looking
+  for (int j = 0; j < r; ++j) {
+    if (tid == 0) {
+      const float d = L[j * ld + j];
+      L[j * ld + j] = (d > 0.0f && d > kDependentTol * kDependentTol * g0[j]) ? sqrtf(d) : 0.0f;
+    }
+    __syncthreads();
+    const float piv = L[j * ld + j];
+    const float inv = piv > 0.0f ? 1.0f / piv : 0.0f;
+    for (int i = j + 1 + tid; i < r; i += 256) L[i * ld + j] *= inv;
+    __syncthreads();
+    // trailing update of the lower triangle, 16 x 16 threads over (row, column)
+    for (int i = j + 1 + (tid >> 4); i < r; i += 16) {
+      const float lij = L[i * ld + j];
+#pragma unroll 4
+      for (int k = j + 1 + (tid & 15); k <= i; k += 16) L[i * ld + k] -= lij * L[k * ld + j];
+    }
+    __syncthreads();
+  }
+  // in-place inverse; one thread per row, its dot product in eight
+  // independent partial sums (added in a fixed order)
+  for (int j = r - 1; j >= 0; --j) {
+    const float piv = L[j * ld + j];
+    const float ajj = piv > 0.0f ? -1.0f / piv : 0.0f;
+    for (int i = j + 1 + tid; i < r; i += 256) {
+      float s8[8] = {};
+      int k = j + 1;
+      for (; k + 8 <= i + 1; k += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s8[u] = fmaf(L[i * ld + k + u], L[(k + u) * ld + j], s8[u]);
+      }
+      for (int u = 0; k <= i; ++k, ++u) s8[u] = fmaf(L[i * ld + k], L[k * ld + j], s8[u]);
+      tmp[i] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    }
+    __syncthreads();
+    for (int i = j + 1 + tid; i < r; i += 256) L[i * ld + j] = ajj * tmp[i];
+    if (tid == 0) L[j * ld + j] = piv > 0.0f ? 1.0f / piv : 0.0f;
+    __syncthreads();
+  }
+  float* Lb = Linv + int64_t(blockIdx.x) * sL;
+  for (int e = tid; e < r * r; e += 256) {
+    const int i = e / r, k = e % r;
+    Lb[e] = k <= i ? L[i * ld + k] : 0.0f;
+  }
+}
+
+// Q[b] = R[b] with every column divided by its norm (zero columns stay
+// zero); R and Q row-major n x r.  A block covers 16 columns of one matrix;
+// 16 row phases accumulate, then add up in a fixed order.
+constexpr int kCnCols = 16, kCnPhases = 16;
+
+__global__ __launch_bounds__(256) void colnorm_kernel(const float* __restrict__ R, int64_t sR,
+                                                     float* __restrict__ Q, int64_t sQ, int64_t n, int r) {
+  __shared__ float part[kCnPhases][kCnCols];
+  const int64_t b = blockIdx.y;
+  const int cl = threadIdx.x % kCnCols, ph = threadIdx.x / kCnCols;
+  const int c = blockIdx.x * kCnCols + cl;
+  const float* Rb = R + b * sR;
+  float s = 0.0f;
+  if (c < r)
+    for (int64_t i = ph; i < n; i += kCnPhases) s = fmaf(Rb[i * r + c], Rb[i * r + c], s);
+  part[ph][cl] = s;
+  __syncthreads();
+  float t = 0.0f;
+  for (int q = 0; q < kCnPhases; ++q) t += part[q][cl];
+  const float nrm = sqrtf(t);
+  const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
+  if (c < r) {
+    float* Qb = Q + b * sQ;
+    for (int64_t i = ph; i < n; i += kCnPhases) Qb[i * r + c] = Rb[i * r + c] * inv;
+  }
+}
+
+// M[b] <- round_fp32(M[b] + G[b]) (the exact sum of two fp32 values rounded
+// once), len entries per matrix
+__global__ __launch_bounds__(256) void add_kernel(float* __restrict__ M, int64_t sM,
+                                                 const float* __restrict__ G, int64_t sG, int64_t len) {
+  const int64_t b = blockIdx.y;
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x);
+  if (i >= len) return;
+  float* m = M + b * sM;
+  m[i] = static_cast<float>(static_cast<double>(m[i]) + static_cast<double>(G[b * sG + i]));
+}
+
+// k ranges per output tile: enough workgroups to cover the chip (about 1024),
+// at least 256 of k per range, at most 16 ranges
+int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const int64_t blocks = ((N + kDT - 1) / kDT) * ((M + kDT - 1) / kDT) * batch;
+  int64_t s = (1024 + blocks - 1) / blocks;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / 256));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
+}
+
+size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const int s = gemm_splits(M, N, K, batch);
+  return s > 1 ? static_cast<size_t>(s) * batch * M * N * 4 : 0;
+}
+
+int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, int64_t sB, int64_t b_k,
+          int64_t b_j, const float* Z, int64_t sZ, int64_t ldz, float* C, int64_t sC, int64_t ldc,
+          int64_t M, int64_t N, int64_t K, float alpha, float beta, int64_t batch, float* part, hipStream_t st) {
+  DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta};
+  const int splits = gemm_splits(M, N, K, batch);
+  const dim3 grid((N + kDT - 1) / kDT, (M + kDT - 1) / kDT, batch * splits);
+  dion_gemm_kernel<<<grid, dim3(256), 0, st>>>(g, splits, part);
+  if (splits > 1) {
+    const int64_t n = batch * M * N;
+    reduce_kernel<<<dim3((n + 255) / 256), dim3(256), 0, st>>>(g, splits, part, batch);
+  }
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Grouping: consecutive problems of one shape whose M, G, X and Q advance by
+// constant strides run batched.
+// ---------------------------------------------------------------------------
+struct DRun {
+  int first, count;
+  int64_t m, n;
+  int64_t sM, sG, sX, sQ;   // batch strides (elements)
+};
+
+int64_t stride_of(const void* a, const void* b) {
+  const int64_t d = reinterpret_cast<const char*>(b) - reinterpret_cast<const char*>(a);
+  return (d > 0 && d % 4 == 0) ? d / 4 : -1;
+}
+
+// problems are taken in order of (rows, cols, address of M), so matrices of
+// one shape interleaved with others (a layer set) still batch
+std::vector<muon_dion_problem> dion_sorted(const muon_dion_problem* probs, int count) {
+  std::vector<muon_dion_problem> p(probs, probs + count);
+  std::stable_sort(p.begin(), p.end(), [](const muon_dion_problem& a, const muon_dion_problem& b) {
+    if (a.rows != b.rows) return a.rows < b.rows;
+    if (a.cols != b.cols) return a.cols < b.cols;
+    return reinterpret_cast<uintptr_t>(a.M) < reinterpret_cast<uintptr_t>(b.M);
+  });
+  return p;
+}
+
+std::vector<DRun> dion_runs(const muon_dion_problem* p, int count) {
+  std::vector<DRun> runs;
+  int i = 0;
+  while (i < count) {
+    DRun r{i, 1, p[i].rows, p[i].cols, 0, 0, 0, 0};   // strides unused for a single problem
+    if (i + 1 < count && p[i + 1].rows == r.m && p[i + 1].cols == r.n) {
+      const int64_t sM = stride_of(p[i].M, p[i + 1].M), sG = stride_of(p[i].G, p[i + 1].G);
+      const int64_t sX = stride_of(p[i].X, p[i + 1].X), sQ = stride_of(p[i].Q, p[i + 1].Q);
+      if (sM > 0 && sG > 0 && sX > 0 && sQ > 0) {
+        int j = i + 1;
+        while (j < count && p[j].rows == r.m && p[j].cols == r.n &&
+               stride_of(p[j - 1].M, p[j].M) == sM && stride_of(p[j - 1].G, p[j].G) == sG &&
+               stride_of(p[j - 1].X, p[j].X) == sX && stride_of(p[j - 1].Q, p[j].Q) == sQ)
+          ++j;
+        r.count = j - i;
+        r.sM = sM; r.sG = sG; r.sX = sX; r.sQ = sQ;
+      }
+    }
+    runs.push_back(r);
+    i += r.count;
+  }
+  return runs;
+}
+
+// Workspace: every run keeps its own P (twice) and R, since the stages run
+// over all runs in turn; the Grams and their inverse factors of all matrices
+// sit in two arrays so one launch factors them all; one split-k partial
+// buffer serves every product.
+struct DLayout {
+  std::vector<size_t> p0, p1, R;
+  size_t gram, linv, part, total;
+};
+
+DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
+  const size_t rk = static_cast<size_t>(rank);
+  DLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
+  size_t part = 0;
+  for (const DRun& r : runs) {
+    const size_t b = static_cast<size_t>(r.count);
+    L.p0.push_back(take(b * r.m * rk * 4));
+    L.p1.push_back(take(b * r.m * rk * 4));
+    L.R.push_back(take(b * r.n * rk * 4));
+    part = std::max({part, gemm_part_bytes(r.m, rank, r.n, r.count), gemm_part_bytes(rank, rank, r.m, r.count),
+                     gemm_part_bytes(r.m, rank, rank, r.count), gemm_part_bytes(r.n, rank, r.m, r.count),
+                     gemm_part_bytes(r.m, r.n, rank, r.count)});
+  }
+  L.gram = take(static_cast<size_t>(count) * rk * rk * 4);
+  L.linv = take(static_cast<size_t>(count) * rk * rk * 4);
+  L.part = take(part);
+  L.total = off;
+  return L;
+}
+
+bool dion_valid(const muon_dion_problem& p) {
+  return p.rows > 0 && p.cols > 0 && p.M && p.G && p.X && p.Q;
+}
+
+int set_chol_lds(int bytes) {
+  static int configured = 0;
+  if (bytes > configured) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(chol_inv_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return MUON_ELAUNCH;
+    configured = bytes;
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+size_t dion_workspace_bytes(const muon_dion_problem* probs, int count, int rank) {
+  if (!probs || count <= 0 || rank < 1 || rank > kDionMaxRank) return 0;
+  for (int i = 0; i < count; ++i)
+    if (!dion_valid(probs[i])) return 0;
+  const std::vector<muon_dion_problem> sorted = dion_sorted(probs, count);
+  return dion_layout(dion_runs(sorted.data(), count), count, rank).total;
+}
+
+int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, float eta, void* workspace,
+              size_t ws_bytes, void* stream) {
+  if (count < 0 || rank < 1 || rank > kDionMaxRank) return MUON_EINVAL;
+  if (count == 0) return MUON_OK;
+  if (!probs) return MUON_EINVAL;
+  for (int i = 0; i < count; ++i) {
+    if (!dion_valid(probs[i])) return MUON_EINVAL;
+    if (!aligned16(probs[i].M) || !aligned16(probs[i].G) || !aligned16(probs[i].X) ||
+        !aligned16(probs[i].Q))
+      return MUON_EALIGN;
+  }
+  const std::vector<muon_dion_problem> sorted = dion_sorted(probs, count);
+  const std::vector<DRun> runs = dion_runs(sorted.data(), count);
+  const DLayout L = dion_layout(runs, count, rank);
+  if (!workspace || ws_bytes < L.total) return MUON_EWORKSPACE;
+  if (!aligned16(workspace)) return MUON_EALIGN;
+  const int lds = ((rank * (rank + 1)) + 2 * rank) * 4;
+  if (set_chol_lds(lds) != MUON_OK) return MUON_ELAUNCH;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t r = rank;
+  float* Gm = reinterpret_cast<float*>(ws + L.gram);
+  float* Li = reinterpret_cast<float*>(ws + L.linv);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  auto Pbuf = [&](size_t k, int which) {
+    return reinterpret_cast<float*>(ws + (which == 0 ? L.p0[k] : L.p1[k]));
+  };
+  int status;
+  // B = M + G in place, and P = B Q
+  for (size_t k = 0; k < runs.size(); ++k) {
+    const DRun& run = runs[k];
+    const muon_dion_problem& p = sorted[run.first];
+    float* M = static_cast<float*>(p.M);
+    const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
+    add_kernel<<<dim3((mn + 255) / 256, b), dim3(256), 0, st>>>(M, run.sM, static_cast<const float*>(p.G),
+                                                               run.sG, mn);
+    if ((status = launch_status()) != MUON_OK) return status;
+    status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
+                   m * r, r, m, r, n, 1.0f, 0.0f, b, part, st);
+    if (status != MUON_OK) return status;
+  }
+  // orth(P), twice: the Grams P^T P of all matrices, one factorisation launch,
+  // then P <- P L^-T
+  for (int pass = 0; pass < 2; ++pass) {
+    for (size_t k = 0; k < runs.size(); ++k) {
+      const DRun& run = runs[k];
+      const float* P = Pbuf(k, pass);
+      status = dgemm(P, run.m * r, 1, r, P, run.m * r, r, 1, nullptr, 0, 0, Gm + run.first * r * r, r * r, r,
+                     r, r, run.m, 1.0f, 0.0f, run.count, part, st);
+      if (status != MUON_OK) return status;
+    }
+    chol_inv_kernel<<<dim3(count), dim3(256), lds, st>>>(Gm, r * r, Li, r * r, rank);
+    if ((status = launch_status()) != MUON_OK) return status;
+    for (size_t k = 0; k < runs.size(); ++k) {
+      const DRun& run = runs[k];
+      status = dgemm(Pbuf(k, pass), run.m * r, r, 1, Li + run.first * r * r, r * r, 1, r, nullptr, 0, 0,
+                     Pbuf(k, 1 - pass), run.m * r, r, run.m, r, r, 1.0f, 0.0f, run.count, part, st);
+      if (status != MUON_OK) return status;
+    }
+  }
+  // R = B^T P, error feedback, Q = ColumnNormalize(R), X update
+  for (size_t k = 0; k < runs.size(); ++k) {
+    const DRun& run = runs[k];
+    const muon_dion_problem& p = sorted[run.first];
+    float* M = static_cast<float*>(p.M);
+    float* X = static_cast<float*>(p.X);
+    float* Q = static_cast<float*>(p.Q);
+    float* R = reinterpret_cast<float*>(ws + L.R[k]);
+    const float* Pf = Pbuf(k, 0);      // two passes: back in buffer 0
+    const int64_t m = run.m, n = run.n, b = run.count;
+    status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, st);
+    if (status != MUON_OK) return status;
+    status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - mu), 1.0f, b,
+                   part, st);
+    if (status != MUON_OK) return status;
+    colnorm_kernel<<<dim3((r + kCnCols - 1) / kCnCols, b), dim3(256), 0, st>>>(R, n * r, Q, run.sQ, n, rank);
+    if ((status = launch_status()) != MUON_OK) return status;
+    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, st);
+    if (status != MUON_OK) return status;
+  }
+  return MUON_OK;
+}
+
+}  // extern "C"

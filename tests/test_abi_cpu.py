@@ -191,3 +191,37 @@ def test_reorthogonalisation_validation(L):
     assert L.apply_update_dense(A1, 1, 10, A2, 7, 0.1, None) == EDTYPE
     assert L.apply_update_dense(A1, 1, 10, MISALIGNED, 1, 0.1, None) == EALIGN
     assert L.apply_update_dense(A1, 1, 10, None, 1, 0.1, None) == EINVAL
+
+
+def test_dion_validation(L):
+    from matrix_aware_optimizer_amd._abi import DionProblem
+    arr = (DionProblem * 1)()
+    arr[0].M, arr[0].G, arr[0].X, arr[0].Q = 0x10000, 0x20000, 0x30000, 0x40000
+    arr[0].rows, arr[0].cols = 768, 3072
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    need = L.dion_workspace_bytes(p, 1, 192)
+    # P twice (m x r) and R (n x r) per run, the Grams and their inverse factors
+    # (r x r per matrix), and one split-k partial buffer: ranges per product =
+    # ceil(1024 / output tiles of 64 x 64), at most K / 256 and 16, at least 1
+    up = lambda x: -(-x // 256) * 256
+
+    def part(M, N, K, b=1):
+        blocks = -(-N // 64) * -(-M // 64) * b
+        sp = max(1, min(-(-1024 // blocks), max(1, K // 256), 16))
+        return sp * b * M * N * 4 if sp > 1 else 0
+
+    m, n, r = 768, 3072, 192
+    parts = max(part(m, r, n), part(r, r, m), part(m, r, r), part(n, r, m), part(m, n, r))
+    assert parts == 12 * m * r * 4                     # B Q: 36 tiles, 12 k ranges of 256
+    assert need == 2 * up(m * r * 4) + up(n * r * 4) + 2 * up(r * r * 4) + up(parts)
+    assert L.dion_workspace_bytes(p, 1, 193) == 0                       # above the LDS limit
+    assert L.dion_step(p, 1, 0, 0.9, 0.1, A3, need, None) == EINVAL
+    assert L.dion_step(p, 1, 193, 0.9, 0.1, A3, need, None) == EINVAL
+    assert L.dion_step(p, 1, 192, 0.9, 0.1, A3, need - 1, None) == EWORKSPACE
+    arr[0].X = 0x30008
+    assert L.dion_step(p, 1, 192, 0.9, 0.1, A3, need, None) == EALIGN
+    arr[0].X = 0x30000
+    arr[0].rows = 0
+    assert L.dion_step(p, 1, 192, 0.9, 0.1, A3, need, None) == EINVAL
+    assert L.dion_step(p, 0, 192, 0.9, 0.1, None, 0, None) == OK
+    assert mao.MUON_DION_MAX_RANK == 192
