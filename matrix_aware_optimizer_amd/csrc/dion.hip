@@ -45,79 +45,119 @@ struct DGemm {
   float alpha, beta;
 };
 
-constexpr int kDT = 64;   // output tile
-constexpr int kDK = 32;   // k per LDS tile
+constexpr int kDT = 64;        // output tile
+constexpr int kDK = 32;        // k per LDS tile
+constexpr int kDPitch = 96;    // LDS row pitch (floats): the two k-rows an MFMA operand read
+                               // touches land 32 banks apart
 
+// One operand tile (64 rows of the output dimension x 32 of k, stored k-major
+// in LDS) per thread: 8 elements.  When the operand is contiguous along k
+// (CK: 4 threads per row, 8 k each) or along the output dimension (4 x 8 per
+// k-row), the 8 elements are two 16-byte loads; a group that leaves the
+// matrix falls back to guarded scalar loads.  `vec` (checked on the host:
+// contiguous dimension stride 1, the other stride and the batch stride
+// multiples of 4, 16-byte aligned base) enables the 16-byte loads.
+struct TileLoad {
+  const float* base;   // this batch entry
+  int64_t s_out, s_k;  // element strides along the output dimension and along k
+  int64_t n_out, K;    // extents
+  bool ck;             // contiguous along k
+  bool vec;
+  __device__ __forceinline__ void fetch(int tid, int64_t o0, int64_t k0, float (&r)[8]) const {
+    int oo, kk;       // first element of this thread's group of 8 (along the contiguous dim)
+    if (ck) { oo = tid >> 2; kk = (tid & 3) * 8; } else { kk = tid >> 3; oo = (tid & 7) * 8; }
+    const int64_t go = o0 + oo, gk = k0 + kk;
+    const float* ptr = base + go * s_out + gk * s_k;
+    const bool full = ck ? (go < n_out && gk + 8 <= K) : (gk < K && go + 8 <= n_out);
+    if (vec && full) {
+      const float4 x = *reinterpret_cast<const float4*>(ptr);
+      const float4 y = *reinterpret_cast<const float4*>(ptr + 4);
+      r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w; r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t o = ck ? go : go + q, k = ck ? gk + q : gk;
+        r[q] = (o < n_out && k < K) ? base[o * s_out + k * s_k] : 0.0f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(int tid, float (&r)[8], float (*T)[kDPitch]) const {
+    int oo, kk;
+    if (ck) { oo = tid >> 2; kk = (tid & 3) * 8; } else { kk = tid >> 3; oo = (tid & 7) * 8; }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (ck) T[kk + q][oo] = r[q];
+      else T[kk][oo + q] = r[q];
+    }
+  }
+};
+
+// The tile is computed on fp32 matrix cores: wave w owns the 32 x 32 quarter
+// (w / 2, w % 2) and issues v_mfma_f32_32x32x2f32 over k, lane l supplying
+// A(row l % 32, k + l / 32) and B(k + l / 32, column l % 32); accumulator
+// value v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+// The next k-tile is fetched into registers while the current one is used.
 // Split k: with `splits` > 1, blockIdx.z = batch * splits + s covers the
 // k-tiles of range s and writes its raw sums to part[s][b] (M x N row-major);
 // reduce_kernel adds the ranges in order and applies alpha, beta.
-__global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, float* part) {
-  __shared__ __attribute__((aligned(16))) float As[kDK][kDT + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[kDK][kDT + 4];
+__global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, float* part, int a_vec, int b_vec) {
+  __shared__ __attribute__((aligned(16))) float As[kDK][kDPitch];
+  __shared__ __attribute__((aligned(16))) float Bs[kDK][kDPitch];
   const int64_t b = blockIdx.z / splits;
   const int sp = blockIdx.z % splits;
   const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const float* A = g.A + b * g.sA;
-  const float* B = g.B + b * g.sB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const TileLoad la{g.A + b * g.sA, g.a_i, g.a_k, g.M, g.K, g.a_k == 1, a_vec != 0};
+  const TileLoad lb{g.B + b * g.sB, g.b_j, g.b_k, g.N, g.K, g.b_k == 1, b_vec != 0};
   const int64_t ktiles = (g.K + kDK - 1) / kDK;
   const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
-  float acc[4][4] = {};
-  for (int64_t k0 = kt0 * kDK; k0 < kt1 * kDK; k0 += kDK) {
-    // each thread loads 8 elements of each tile, consecutive threads along the
-    // operand's contiguous dimension
+  f32x16_t acc;
 #pragma unroll
-    for (int e4 = 0; e4 < kDK * kDT / 256; ++e4) {
-      const int e = tid + 256 * e4;
-      int i, k;
-      if (g.a_k == 1) { i = e / kDK; k = e % kDK; } else { k = e / kDT; i = e % kDT; }
-      const int64_t gi = i0 + i, gk = k0 + k;
-      As[k][i] = (gi < g.M && gk < g.K) ? A[gi * g.a_i + gk * g.a_k] : 0.0f;
-      int j;
-      if (g.b_j == 1) { k = e / kDT; j = e % kDT; } else { j = e / kDK; k = e % kDK; }
-      const int64_t gj = j0 + j, gk2 = k0 + k;
-      Bs[k][j] = (gj < g.N && gk2 < g.K) ? B[gk2 * g.b_k + gj * g.b_j] : 0.0f;
-    }
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  float ra[8], rb[8];
+  if (kt0 < kt1) {
+    la.fetch(tid, i0, kt0 * kDK, ra);
+    lb.fetch(tid, j0, kt0 * kDK, rb);
+  }
+  for (int64_t kt = kt0; kt < kt1; ++kt) {
+    la.store(tid, ra, As);
+    lb.store(tid, rb, Bs);
     __syncthreads();
+    if (kt + 1 < kt1) {
+      la.fetch(tid, i0, (kt + 1) * kDK, ra);
+      lb.fetch(tid, j0, (kt + 1) * kDK, rb);
+    }
 #pragma unroll
-    for (int k = 0; k < kDK; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&As[k][ty * 4]);
-      const float4 bb = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+    for (int k = 0; k < kDK; k += 2) {
+      const float a = As[k + (lane >> 5)][wi + (lane & 31)];
+      const float bb = Bs[k + (lane >> 5)][wj + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  const int64_t col = j0 + wj + (lane & 31);
   if (splits > 1) {
     float* Pp = part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N;
+    if (col < g.N) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t gi = i0 + ty * 4 + r;
-      if (gi >= g.M) continue;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t gj = j0 + tx * 4 + c;
-        if (gj < g.N) Pp[gi * g.N + gj] = acc[r][c];
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < g.M) Pp[row * g.N + col] = acc[v];
       }
     }
     return;
   }
   float* C = g.C + b * g.sC;
   const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+  if (col < g.N) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t gi = i0 + ty * 4 + r;
-    if (gi >= g.M) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t gj = j0 + tx * 4 + c;
-      if (gj >= g.N) continue;
-      float v = g.alpha * acc[r][c];
-      if (g.beta != 0.0f) v = fmaf(g.beta, Z[gi * g.ldz + gj], v);
-      C[gi * g.ldc + gj] = v;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (row >= g.M) continue;
+      float o = g.alpha * acc[v];
+      if (g.beta != 0.0f) o = fmaf(g.beta, Z[row * g.ldz + col], o);
+      C[row * g.ldc + col] = o;
     }
   }
 }
@@ -262,7 +302,13 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
   DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta};
   const int splits = gemm_splits(M, N, K, batch);
   const dim3 grid((N + kDT - 1) / kDT, (M + kDT - 1) / kDT, batch * splits);
-  dion_gemm_kernel<<<grid, dim3(256), 0, st>>>(g, splits, part);
+  // 16-byte operand loads: contiguous dimension stride 1, every other stride a
+  // multiple of 4 floats, aligned base
+  auto vec_ok = [](const float* p, int64_t s_batch, int64_t s_a, int64_t s_b) {
+    return aligned16(p) && (s_a == 1 || s_b == 1) && s_batch % 4 == 0 && (s_a == 1 ? s_b : s_a) % 4 == 0;
+  };
+  const int a_vec = vec_ok(A, sA, a_i, a_k), b_vec = vec_ok(B, sB, b_k, b_j);
+  dion_gemm_kernel<<<grid, dim3(256), 0, st>>>(g, splits, part, a_vec, b_vec);
   if (splits > 1) {
     const int64_t n = batch * M * N;
     reduce_kernel<<<dim3((n + 255) / 256), dim3(256), 0, st>>>(g, splits, part, batch);
