@@ -178,69 +178,219 @@ __global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const 
 
 // ---------------------------------------------------------------------------
 // Linv[b] = L^-1 with G[b] = L L^T (r x r, lower triangle of G read).  One
-// workgroup per matrix; L lives in LDS with row pitch r + 1.  Dependent
-// columns (pivot^2 <= tol^2 * G_jj) get a zero column in L, hence a zero row
-// and column in L^-1.  Inversion in place, last column first:
-// column j of L^-1 below the diagonal = -(1 / l_jj) * Linv22 * l_c.
+// workgroup per matrix, on 16 x 16 blocks in LDS (size padded to a multiple
+// of 16 with an identity block; row pitch rp + 1).  Dependent columns
+// (pivot^2 <= tol^2 * G_jj, G_jj the diagonal of G) get a zero column in L;
+// L^-1 is then the inverse over the independent indices, with zero rows and
+// columns at the dependent ones.
+//
+// Cholesky, left-looking by block column J: the panel (rows >= 16 J) takes
+// the products of the earlier block columns; one wave factors the diagonal
+// block and inverts it in registers (lane i owns row i, other rows reach it
+// through readlane); the rows below are multiplied by the transposed inverse.
+// Inverse: with W_IK = D_I L_IK (D_I the inverse of diagonal block I), block
+// (I, J) of L^-1 is -sum_{J <= K < I} W_IK X_KJ, computed one block diagonal
+// at a time.  X is stored transposed in the upper triangle (D_I^T on the
+// diagonal), so each entry is one dot product of two LDS rows.
 // ---------------------------------------------------------------------------
+constexpr int kCb = 16, kCbMax = kDionMaxRank / kCb;
+
+__device__ __forceinline__ float from_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__ G, int64_t sG,
                                                       float* __restrict__ Linv, int64_t sL, int r) {
   extern __shared__ float sm[];
-  const int ld = r + 1;
-  float* L = sm;                 // r * ld
-  float* g0 = sm + r * ld;       // original diagonal
-  float* tmp = g0 + r;           // r
+  const int nb = (r + kCb - 1) / kCb, rp = nb * kCb, ld = rp + 1;
+  float* S = sm;                 // rp x ld
+  float* g0 = sm + rp * ld;      // diagonal of G
   const float* Gb = G + int64_t(blockIdx.x) * sG;
   const int tid = threadIdx.x;
-  for (int e = tid; e < r * r; e += 256) {
-    const int i = e / r, k = e % r;
-    L[i * ld + k] = k <= i ? Gb[i * r + k] : 0.0f;
-  }
-  for (int i = tid; i < r; i += 256) g0[i] = Gb[i * r + i];
-  __syncthreads();
-  // Cholesky, right-looking
-  for (int j = 0; j < r; ++j) {
-    if (tid == 0) {
-      const float d = L[j * ld + j];
-      L[j * ld + j] = (d > 0.0f && d > kDependentTol * kDependentTol * g0[j]) ? sqrtf(d) : 0.0f;
-    }
-    __syncthreads();
-    const float piv = L[j * ld + j];
-    const float inv = piv > 0.0f ? 1.0f / piv : 0.0f;
-    for (int i = j + 1 + tid; i < r; i += 256) L[i * ld + j] *= inv;
-    __syncthreads();
-    // trailing update of the lower triangle, 16 x 16 threads over (row, column)
-    for (int i = j + 1 + (tid >> 4); i < r; i += 16) {
-      const float lij = L[i * ld + j];
-#pragma unroll 4
-      for (int k = j + 1 + (tid & 15); k <= i; k += 16) L[i * ld + k] -= lij * L[k * ld + j];
-    }
-    __syncthreads();
-  }
-  // in-place inverse; one thread per row, its dot product in eight
-  // independent partial sums (added in a fixed order)
-  for (int j = r - 1; j >= 0; --j) {
-    const float piv = L[j * ld + j];
-    const float ajj = piv > 0.0f ? -1.0f / piv : 0.0f;
-    for (int i = j + 1 + tid; i < r; i += 256) {
-      float s8[8] = {};
-      int k = j + 1;
-      for (; k + 8 <= i + 1; k += 8) {
+  // G (row-major r x r, 16-byte aligned rows when r % 4 == 0) into S, eight
+  // loads in flight per thread; the padding is an identity block
+  if (r % 4 == 0) {
+    const int q = r / 4, n4 = r * q;
+    for (int e0 = 0; e0 < n4; e0 += 256 * 8) {
+      float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s8[u] = fmaf(L[i * ld + k + u], L[(k + u) * ld + j], s8[u]);
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256 + tid;
+        v[u] = reinterpret_cast<const float4*>(Gb)[e < n4 ? e : 0];
       }
-      for (int u = 0; k <= i; ++k, ++u) s8[u] = fmaf(L[i * ld + k], L[k * ld + j], s8[u]);
-      tmp[i] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256 + tid;
+        if (e < n4) {
+          const int i = e / q, k = 4 * (e % q);
+          float* d = S + i * ld + k;
+          d[0] = k <= i ? v[u].x : 0.0f;
+          d[1] = k + 1 <= i ? v[u].y : 0.0f;
+          d[2] = k + 2 <= i ? v[u].z : 0.0f;
+          d[3] = k + 3 <= i ? v[u].w : 0.0f;
+        }
+      }
+    }
+  } else {
+    const int n = r * r;
+    for (int e0 = 0; e0 < n; e0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256 + tid;
+        v[u] = Gb[e < n ? e : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256 + tid;
+        if (e < n) {
+          const int i = e / r, k = e % r;
+          S[i * ld + k] = k <= i ? v[u] : 0.0f;
+        }
+      }
+    }
+  }
+  for (int e = tid; e < rp * rp - r * r; e += 256) {
+    // padding rows r.. (all columns), then columns r.. of rows < r
+    const int pr = (rp - r) * rp;
+    const int i = e < pr ? r + e / rp : (e - pr) / (rp - r), k = e < pr ? e % rp : r + (e - pr) % (rp - r);
+    S[i * ld + k] = i == k ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  for (int i = tid; i < rp; i += 256) g0[i] = S[i * ld + i];   // read before the first factorisation
+
+  for (int J = 0; J < nb; ++J) {
+    const int c0 = J * kCb;
+    if (J > 0 && tid < rp - c0) {
+      // panel: A(i, c0 + k) -= sum_{m < c0} L(i, m) L(c0 + k, m), lower part;
+      // each thread a 4 x 4 tile (rows c0 + 4 tr + u, columns c0 + 4 tc + v)
+      const int i0 = c0 + 4 * (tid >> 2), k0 = c0 + 4 * (tid & 3);
+      float acc[4][4] = {};
+#pragma unroll 4
+      for (int m = 0; m < c0; ++m) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[u] = S[(i0 + u) * ld + m];
+          bv[u] = S[(k0 + u) * ld + m];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (k0 + v <= i0 + u) S[(i0 + u) * ld + k0 + v] -= acc[u][v];
     }
     __syncthreads();
-    for (int i = j + 1 + tid; i < r; i += 256) L[i * ld + j] = ajj * tmp[i];
-    if (tid == 0) L[j * ld + j] = piv > 0.0f ? 1.0f / piv : 0.0f;
+    if (tid < 64) {
+      // diagonal block: factor, then invert; lane i < 16 holds row i
+      const int lane = tid, row = c0 + (lane & (kCb - 1));
+      float a[kCb], x[kCb], acc[kCb];
+#pragma unroll
+      for (int c = 0; c < kCb; ++c) a[c] = S[row * ld + c0 + c];
+      const float g = g0[row];
+      float own_inv = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCb; ++k) {
+        const float d = from_lane(a[k], k);
+        const float piv = (d > 0.0f && d > kDependentTol * kDependentTol * from_lane(g, k)) ? sqrtf(d) : 0.0f;
+        const float inv = piv > 0.0f ? 1.0f / piv : 0.0f;
+        if (lane == k) {
+          a[k] = piv;
+          own_inv = inv;
+        } else {
+          a[k] *= inv;
+        }
+#pragma unroll
+        for (int m = k + 1; m < kCb; ++m) a[m] = fmaf(-a[k], from_lane(a[k], m), a[m]);
+      }
+      // rows of D = L_JJ^-1 in order: D(k, c) = (delta_kc - sum_{m<k} L(k, m) D(m, c)) / l_kk
+#pragma unroll
+      for (int c = 0; c < kCb; ++c) x[c] = acc[c] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCb; ++k) {
+        if (lane == k) {
+#pragma unroll
+          for (int c = 0; c <= k; ++c) x[c] = ((c == k ? 1.0f : 0.0f) - acc[c]) * own_inv;
+        }
+#pragma unroll
+        for (int c = 0; c <= k; ++c) acc[c] = fmaf(a[k], from_lane(x[c], k), acc[c]);
+      }
+      if (lane < kCb) {
+#pragma unroll
+        for (int c = 0; c < kCb; ++c) S[(c0 + c) * ld + c0 + lane] = x[c];   // D^T
+      }
+    }
+    __syncthreads();
+    // rows below: L(i, c0 + k) = sum_{m <= k} A(i, c0 + m) D(k, m)
+    for (int i = c0 + kCb + tid; i < rp; i += 256) {
+      float v[kCb];
+#pragma unroll
+      for (int c = 0; c < kCb; ++c) v[c] = S[i * ld + c0 + c];
+#pragma unroll
+      for (int k = 0; k < kCb; ++k) {
+        float o = 0.0f;
+#pragma unroll
+        for (int m = 0; m <= k; ++m) o = fmaf(v[m], S[(c0 + m) * ld + c0 + k], o);
+        S[i * ld + c0 + k] = o;
+      }
+    }
+    __syncthreads();
+  }
+
+  // W_IK = D_I L_IK for every block left of the diagonal, one column per thread
+  const int nw = kCb * nb * (nb - 1) / 2;
+  for (int w = tid; w < nw; w += 256) {
+    int I = 1;
+    while (kCb * I * (I + 1) / 2 <= w) ++I;
+    const int col = w - kCb * I * (I - 1) / 2, r0 = kCb * I;
+    float v[kCb];
+#pragma unroll
+    for (int m = 0; m < kCb; ++m) v[m] = S[(r0 + m) * ld + col];
+#pragma unroll
+    for (int i = 0; i < kCb; ++i) {
+      float o = 0.0f;
+#pragma unroll
+      for (int m = 0; m <= i; ++m) o = fmaf(S[(r0 + m) * ld + r0 + i], v[m], o);
+      S[(r0 + i) * ld + col] = o;
+    }
+  }
+  __syncthreads();
+  // X_IJ(i, j) = -sum_{16 J <= c < 16 I} S(16 I + i, c) S(16 J + j, c), stored at S(16 J + j, 16 I + i)
+  for (int d = 1; d < nb; ++d) {
+    if (tid < kCb * (nb - d)) {
+      // block (J + d, J), J = tid / 16; each thread a 4 x 4 tile
+      const int J = tid >> 4, I = J + d;
+      const int ia = kCb * I + 4 * ((tid >> 2) & 3), jb = kCb * J + 4 * (tid & 3);
+      float acc[4][4] = {};
+#pragma unroll 4
+      for (int c = kCb * J; c < kCb * I; ++c) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[u] = S[(ia + u) * ld + c];
+          bv[u] = S[(jb + u) * ld + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[(jb + v) * ld + ia + u] = -acc[u][v];
+    }
     __syncthreads();
   }
   float* Lb = Linv + int64_t(blockIdx.x) * sL;
   for (int e = tid; e < r * r; e += 256) {
     const int i = e / r, k = e % r;
-    Lb[e] = k <= i ? L[i * ld + k] : 0.0f;
+    Lb[e] = k <= i ? S[k * ld + i] : 0.0f;
   }
 }
 
@@ -444,7 +594,8 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
   const DLayout L = dion_layout(runs, count, rank);
   if (!workspace || ws_bytes < L.total) return MUON_EWORKSPACE;
   if (!aligned16(workspace)) return MUON_EALIGN;
-  const int lds = ((rank * (rank + 1)) + 2 * rank) * 4;
+  const int rp = (rank + kCb - 1) / kCb * kCb;
+  const int lds = (rp * (rp + 1) + rp) * 4;
   if (set_chol_lds(lds) != MUON_OK) return MUON_ELAUNCH;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
