@@ -81,8 +81,13 @@ def parse():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the int8-exchange and re-orthogonalised-update measurements "
+                    help="skip the extra measurements after the timed steps "
                          "(profiling runs then trace the step's kernels only)")
+    ap.add_argument("--extras", default="cold,int8,reorth,dion,library",
+                    help="comma list of extra measurements to run after the timed steps: "
+                         "cold (elementwise kernels with cold caches), int8 (int8 SUM exchange), "
+                         "reorth (re-orthogonalised update), dion (Dion step), "
+                         "library (vendor GEMM library on the same shapes)")
     ap.add_argument("--repeat-kernel", default=None,
                     help="profiling aid: after the run, launch one stage N more times "
                          "(gram|poly|apply|momentum|pack|vote|update|copy:N)")
@@ -300,12 +305,18 @@ def main():
         "roofline": roofline,
         "input_generation_s": gen_s,
     }
-    if not args.no_extras:
+    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    if "cold" in extras:
         result["kernels_cold"] = cold_elementwise(mao, torch, wl, Ms[0], Gs[0], W, X[cur_final], bits, vote,
                                                   offsets, sumsq, mom_ws, dev)
+    if "int8" in extras:
         result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
+    if "reorth" in extras:
         result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
+    if "dion" in extras:
         result["dion"] = dion_bench(mao, torch, dev)
+    if "library" in extras and prec == "bf16":
+        result["library_reference"] = library_reference(torch, avg, s, l, dev)
 
     if args.repeat_kernel:
         name, _, cnt = args.repeat_kernel.partition(":")
@@ -457,6 +468,46 @@ def dion_bench(mao, torch, dev, reps=5):
         tf = flops / (ms * 1e-3) / 1e12
         out[f"rank_{rank}"] = {"ms": ms, "TFLOP/s": tf, "frac_fp32_peak": tf / PEAK_F32_TFLOPS,
                                "workload": wl.name}
+    return out
+
+
+def library_reference(torch, avg, s, l, dev, reps=10):
+    """Context only, not on the product path: the vendor GEMM library (hipBLASLt,
+    reached through torch.matmul on contiguous bf16 operands) timed on the shapes
+    of the Newton-Schulz products, beside this library's own kernels from the
+    timed steps.  The library computes the Gram in full (dense flops), the
+    kernels here its lower triangle."""
+    g = torch.Generator(device=dev).manual_seed(7)
+    X = torch.randn(s, l, device=dev, generator=g).to(torch.bfloat16)
+    Xt = X.t().contiguous()
+    Bm = torch.randn(s, s, device=dev, generator=g).to(torch.bfloat16)
+    out_sl = torch.empty(s, l, device=dev, dtype=torch.bfloat16)
+    out_ss = torch.empty(s, s, device=dev, dtype=torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    apply_ms = timed(lambda: torch.addmm(X, Bm, X, beta=3.4445, alpha=1.0, out=out_sl))
+    gram_ms = timed(lambda: torch.matmul(X, Xt, out=out_ss))
+    poly_ms = timed(lambda: torch.addmm(Bm, Bm, Bm, beta=-4.775, alpha=2.0315, out=out_ss))
+    dense_apply, dense_gram, dense_poly = 2.0 * s * s * l, 2.0 * s * s * l, 2.0 * s ** 3
+    out = {"library": "hipBLASLt via torch.matmul/addmm (bf16, fp32 accumulation)",
+           "apply_aX_plus_BX": {"library_ms": apply_ms, "library_TFLOP/s": dense_apply / apply_ms / 1e9},
+           "gram_dense_XXt": {"library_ms": gram_ms, "library_TFLOP/s": dense_gram / gram_ms / 1e9},
+           "poly_bA_plus_cAA": {"library_ms": poly_ms, "library_TFLOP/s": dense_poly / poly_ms / 1e9}}
+    for key, ours in (("apply_aX_plus_BX", "apply"), ("gram_dense_XXt", "gram"), ("poly_bA_plus_cAA", "poly")):
+        if ours in avg:
+            out[key]["this_library_ms"] = avg[ours]
+            out[key]["speedup_vs_library"] = out[key]["library_ms"] / avg[ours]
     return out
 
 
