@@ -394,42 +394,90 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
   }
 }
 
-// Q[b] = R[b] with every column divided by its norm (zero columns stay
-// zero); R and Q row-major n x r.  A block covers 16 columns of one matrix;
-// 16 row phases accumulate, then add up in a fixed order.
-constexpr int kCnCols = 16, kCnPhases = 16;
-
-__global__ __launch_bounds__(256) void colnorm_kernel(const float* __restrict__ R, int64_t sR,
-                                                     float* __restrict__ Q, int64_t sQ, int64_t n, int r) {
-  __shared__ float part[kCnPhases][kCnCols];
-  const int64_t b = blockIdx.y;
-  const int cl = threadIdx.x % kCnCols, ph = threadIdx.x / kCnCols;
-  const int c = blockIdx.x * kCnCols + cl;
+// Q[b] = R[b] with every column divided by its norm (zero columns stay zero);
+// R and Q row-major n x r.  Two passes over chunks of `rows_per` rows, one
+// workgroup per (chunk, matrix): colsq_kernel writes each chunk's column sums
+// of squares (thread c owns column c, four interleaved partial sums), and
+// colscale_kernel adds the chunks' sums in chunk order -- the same order in
+// every workgroup -- and scales its chunk.
+__global__ __launch_bounds__(256) void colsq_kernel(const float* __restrict__ R, int64_t sR,
+                                                   float* __restrict__ part, int64_t n, int r,
+                                                   int64_t rows_per, int64_t nch) {
+  const int64_t b = blockIdx.y, ch = blockIdx.x;
+  const int64_t i0 = ch * rows_per, i1 = min(n, i0 + rows_per);
   const float* Rb = R + b * sR;
-  float s = 0.0f;
-  if (c < r)
-    for (int64_t i = ph; i < n; i += kCnPhases) s = fmaf(Rb[i * r + c], Rb[i * r + c], s);
-  part[ph][cl] = s;
+  for (int c = threadIdx.x; c < r; c += 256) {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    int64_t i = i0;
+    for (; i + 4 <= i1; i += 4) {
+      const float v0 = Rb[i * r + c], v1 = Rb[(i + 1) * r + c];
+      const float v2 = Rb[(i + 2) * r + c], v3 = Rb[(i + 3) * r + c];
+      s0 = fmaf(v0, v0, s0);
+      s1 = fmaf(v1, v1, s1);
+      s2 = fmaf(v2, v2, s2);
+      s3 = fmaf(v3, v3, s3);
+    }
+    for (; i < i1; ++i) s0 = fmaf(Rb[i * r + c], Rb[i * r + c], s0);
+    part[(b * nch + ch) * r + c] = (s0 + s1) + (s2 + s3);
+  }
+}
+
+__global__ __launch_bounds__(256) void colscale_kernel(const float* __restrict__ R, int64_t sR,
+                                                      const float* __restrict__ part, float* __restrict__ Q,
+                                                      int64_t sQ, int64_t n, int r, int64_t rows_per,
+                                                      int64_t nch) {
+  __shared__ float inv[kDionMaxRank];
+  const int64_t b = blockIdx.y, ch = blockIdx.x;
+  for (int c = threadIdx.x; c < r; c += 256) {
+    float t = 0.0f;
+    for (int64_t q = 0; q < nch; ++q) t += part[(b * nch + q) * r + c];
+    const float nrm = sqrtf(t);
+    inv[c] = nrm > 0.0f ? 1.0f / nrm : 0.0f;
+  }
   __syncthreads();
-  float t = 0.0f;
-  for (int q = 0; q < kCnPhases; ++q) t += part[q][cl];
-  const float nrm = sqrtf(t);
-  const float inv = nrm > 0.0f ? 1.0f / nrm : 0.0f;
-  if (c < r) {
-    float* Qb = Q + b * sQ;
-    for (int64_t i = ph; i < n; i += kCnPhases) Qb[i * r + c] = Rb[i * r + c] * inv;
+  // thread t: column group t % groups (4 columns when rows are 16-byte
+  // aligned, else 1), rows t / groups, t / groups + 256 / groups, ...
+  const int64_t i0 = ch * rows_per, i1 = min(n, i0 + rows_per);
+  const float* Rb = R + b * sR;
+  float* Qb = Q + b * sQ;
+  const bool vec = r % 4 == 0 && sQ % 4 == 0 && sR % 4 == 0;
+  const int groups = vec ? r / 4 : r, step = 256 / groups;
+  const int t = threadIdx.x, g = t % groups;
+  if (t >= groups * step) return;
+  if (vec) {
+    const float4 w = make_float4(inv[4 * g], inv[4 * g + 1], inv[4 * g + 2], inv[4 * g + 3]);
+    for (int64_t i = i0 + t / groups; i < i1; i += step) {
+      const float4 v = *reinterpret_cast<const float4*>(Rb + i * r + 4 * g);
+      *reinterpret_cast<float4*>(Qb + i * r + 4 * g) = make_float4(v.x * w.x, v.y * w.y, v.z * w.z, v.w * w.w);
+    }
+  } else {
+    for (int64_t i = i0 + t / groups; i < i1; i += step) Qb[i * r + g] = Rb[i * r + g] * inv[g];
   }
 }
 
 // M[b] <- round_fp32(M[b] + G[b]) (the exact sum of two fp32 values rounded
-// once), len entries per matrix
+// once), len entries per matrix; 4 entries per thread when len and the batch
+// strides are multiples of 4 (the bases are 16-byte aligned)
+__device__ __forceinline__ float add_once(float a, float b) {
+  return static_cast<float>(static_cast<double>(a) + static_cast<double>(b));
+}
+
 __global__ __launch_bounds__(256) void add_kernel(float* __restrict__ M, int64_t sM,
-                                                 const float* __restrict__ G, int64_t sG, int64_t len) {
+                                                 const float* __restrict__ G, int64_t sG, int64_t len, int vec) {
   const int64_t b = blockIdx.y;
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x);
-  if (i >= len) return;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   float* m = M + b * sM;
-  m[i] = static_cast<float>(static_cast<double>(m[i]) + static_cast<double>(G[b * sG + i]));
+  const float* g = G + b * sG;
+  if (vec) {
+    if (4 * t >= len) return;
+    float4 x = *reinterpret_cast<const float4*>(m + 4 * t);
+    const float4 y = *reinterpret_cast<const float4*>(g + 4 * t);
+    x = make_float4(add_once(x.x, y.x), add_once(x.y, y.y), add_once(x.z, y.z), add_once(x.w, y.w));
+    *reinterpret_cast<float4*>(m + 4 * t) = x;
+  } else {
+    if (t >= len) return;
+    m[t] = add_once(m[t], g[t]);
+  }
 }
 
 // k ranges per output tile: enough workgroups to cover the chip (about 1024),
@@ -614,8 +662,10 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     const muon_dion_problem& p = sorted[run.first];
     float* M = static_cast<float*>(p.M);
     const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
-    add_kernel<<<dim3((mn + 255) / 256, b), dim3(256), 0, st>>>(M, run.sM, static_cast<const float*>(p.G),
-                                                               run.sG, mn);
+    const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
+    const int64_t threads = vec ? mn / 4 : mn;
+    add_kernel<<<dim3((threads + 255) / 256, b), dim3(256), 0, st>>>(M, run.sM, static_cast<const float*>(p.G),
+                                                                    run.sG, mn, vec);
     if ((status = launch_status()) != MUON_OK) return status;
     status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
                    m * r, r, m, r, n, 1.0f, 0.0f, b, part, st);
@@ -655,7 +705,15 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - mu), 1.0f, b,
                    part, st);
     if (status != MUON_OK) return status;
-    colnorm_kernel<<<dim3((r + kCnCols - 1) / kCnCols, b), dim3(256), 0, st>>>(R, n * r, Q, run.sQ, n, rank);
+    {
+      // chunks of at least 64 rows and at most m chunks, so the partial sums
+      // (b x chunks x r) fit in P's second buffer, free after the two passes
+      const int64_t rows_per = std::max<int64_t>(64, (n + m - 1) / m);
+      const int64_t nch = (n + rows_per - 1) / rows_per;
+      float* cpart = Pbuf(k, 1);
+      colsq_kernel<<<dim3(nch, b), dim3(256), 0, st>>>(R, n * r, cpart, n, rank, rows_per, nch);
+      colscale_kernel<<<dim3(nch, b), dim3(256), 0, st>>>(R, n * r, cpart, Q, run.sQ, n, rank, rows_per, nch);
+    }
     if ((status = launch_status()) != MUON_OK) return status;
     status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, st);
     if (status != MUON_OK) return status;
