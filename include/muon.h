@@ -270,7 +270,12 @@ int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u
  *            Q device fp32 n x rank (read as Q_{t-1}, written as Q_t).
  * rank       1 .. MUON_DION_MAX_RANK (the Gram of P is factored in LDS).
  * Problems of equal shape whose M, G, X and Q advance by constant strides
- * (in order of shape and address) run batched.  Pointers 16-byte aligned.
+ * (in order of shape and address) run batched.  Pointers 16-byte aligned
+ * (MUON_EALIGN).  Limits of the products' launch grids: rows and cols at most
+ * 4,194,240 (65535 tiles of 64), count at most 4095, and under 2^32 tiles of
+ * 64 x 64 (times 48 for the rank-wide products) per product; beyond them
+ * dion_step returns MUON_EINVAL before launching anything and
+ * dion_workspace_bytes returns 0.
  * workspace  dion_workspace_bytes(probs, count, rank) bytes.
  * ------------------------------------------------------------------------- */
 #define MUON_DION_MAX_RANK 192

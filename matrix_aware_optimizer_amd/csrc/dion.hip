@@ -596,8 +596,18 @@ DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
   return L;
 }
 
-bool dion_valid(const muon_dion_problem& p) {
-  return p.rows > 0 && p.cols > 0 && p.M && p.G && p.X && p.Q;
+// Launch limits of the products' tile grids: at most 65535 row tiles of 64
+// (grid y), 16 k ranges times the batch in grid z, and fewer than 2^32
+// workgroups in one launch.  The largest grids are the m x n outputs and the
+// m x rank outputs split 16 ways.
+constexpr int64_t kDionMaxSide = 65535 * kDT, kDionMaxCount = 65535 / 16;
+
+bool dion_valid(const muon_dion_problem& p, int count) {
+  if (!(p.rows > 0 && p.cols > 0 && p.M && p.G && p.X && p.Q)) return false;
+  if (p.rows > kDionMaxSide || p.cols > kDionMaxSide || count > kDionMaxCount) return false;
+  const int64_t tm = (p.rows + kDT - 1) / kDT, tn = (p.cols + kDT - 1) / kDT;
+  return std::max<int64_t>(tn, 48) * tm * count < (int64_t(1) << 32) &&
+         std::max<int64_t>(tm, 48) * tn * count < (int64_t(1) << 32);
 }
 
 int set_chol_lds(int bytes) {
@@ -621,7 +631,7 @@ extern "C" {
 size_t dion_workspace_bytes(const muon_dion_problem* probs, int count, int rank) {
   if (!probs || count <= 0 || rank < 1 || rank > kDionMaxRank) return 0;
   for (int i = 0; i < count; ++i)
-    if (!dion_valid(probs[i])) return 0;
+    if (!dion_valid(probs[i], count)) return 0;
   const std::vector<muon_dion_problem> sorted = dion_sorted(probs, count);
   return dion_layout(dion_runs(sorted.data(), count), count, rank).total;
 }
@@ -632,7 +642,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
   if (count == 0) return MUON_OK;
   if (!probs) return MUON_EINVAL;
   for (int i = 0; i < count; ++i) {
-    if (!dion_valid(probs[i])) return MUON_EINVAL;
+    if (!dion_valid(probs[i], count)) return MUON_EINVAL;
     if (!aligned16(probs[i].M) || !aligned16(probs[i].G) || !aligned16(probs[i].X) ||
         !aligned16(probs[i].Q))
       return MUON_EALIGN;

@@ -215,6 +215,18 @@ def test_dion_validation(L):
     assert parts == 12 * m * r * 4                     # B Q: 36 tiles, 12 k ranges of 256
     assert need == 2 * up(m * r * 4) + up(n * r * 4) + 2 * up(r * r * 4) + up(parts)
     assert L.dion_workspace_bytes(p, 1, 193) == 0                       # above the LDS limit
+    # launch-grid limits: a side above 65535 tiles of 64, more than 4095 problems
+    arr[0].rows = 65535 * 64 + 1
+    assert L.dion_workspace_bytes(p, 1, 8) == 0
+    assert L.dion_step(p, 1, 8, 0.9, 0.1, A3, need, None) == EINVAL
+    arr[0].rows = 768
+    many = (DionProblem * 4096)()
+    for k in range(4096):
+        many[k].M, many[k].G, many[k].X, many[k].Q = 0x10000, 0x20000, 0x30000, 0x40000
+        many[k].rows, many[k].cols = 64, 64
+    pm = ctypes.cast(many, ctypes.c_void_p)
+    assert L.dion_workspace_bytes(pm, 4095, 8) > 0
+    assert L.dion_workspace_bytes(pm, 4096, 8) == 0
     assert L.dion_step(p, 1, 0, 0.9, 0.1, A3, need, None) == EINVAL
     assert L.dion_step(p, 1, 193, 0.9, 0.1, A3, need, None) == EINVAL
     assert L.dion_step(p, 1, 192, 0.9, 0.1, A3, need - 1, None) == EWORKSPACE
