@@ -146,6 +146,8 @@ def main():
     X = [torch.empty((s, l), dtype=tdt[prec], device=dev) for _ in range(2)]
     A = torch.empty((s, s), dtype=tdt[prec], device=dev)
     B = torch.empty((s, s), dtype=tdt[prec], device=dev)
+    # split scratch of the stage calls (zeroed once; every call leaves its counters at zero)
+    stage_ws = mao.new_stage_workspace(s, l, 1, prec, dev)
     fold = prec == "bf16" and wl.m_dtype == "bf16"      # wide and pad-free: checked above
     bits = torch.zeros((wl.workers, nwords), dtype=torch.int64, device=dev)
     vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
@@ -165,13 +167,13 @@ def main():
             # a bf16 wide pad-free momentum is read as is by the first iteration,
             # whose products fold in the Frobenius scaling (as ns_orthogonalize does)
             Xc, ss = (Ms[k].view(1, rows, cols), sumsq) if fold and it == 0 else (X[cur], None)
-            mao.ns_gram(Xc, A, prec, sumsq=ss)
+            mao.ns_gram(Xc, A, prec, sumsq=ss, workspace=stage_ws)
             mark("gram")
             if c != 0.0:
-                mao.ns_poly(A, B, b, c, prec)
+                mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
                 mark("poly")
             mao.ns_apply(B if c != 0.0 else A, Xc, X[1 - cur], a, 1.0 if c != 0.0 else b, prec,
-                         sumsq=ss)
+                         sumsq=ss, workspace=stage_ws)
             mark("apply")
             cur = 1 - cur
         mao.sign_pack(X[cur], bits[k])
@@ -323,11 +325,11 @@ def main():
         cnt = int(cnt or 10)
         for _ in range(cnt):
             if name == "gram":
-                mao.ns_gram(X[0], A, prec)
+                mao.ns_gram(X[0], A, prec, workspace=stage_ws)
             elif name == "poly":
-                mao.ns_poly(A, B, b, c, prec)
+                mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
             elif name == "apply":
-                mao.ns_apply(B, X[0], X[1], a, 1.0, prec)
+                mao.ns_apply(B, X[0], X[1], a, 1.0, prec, workspace=stage_ws)
             elif name == "copy":
                 X[1].copy_(X[0])
         torch.cuda.synchronize()

@@ -117,6 +117,20 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
  *              sum(M^2), e.g. from muon_momentum, or NULL to compute it).
  *   Problems of equal shape and dtypes whose pointers are evenly spaced are
  *   batched into one launch per stage.  steps == 0 gives U = X0.
+ *   workspace  device, at least ns_workspace_bytes(probs, count, precision)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on
+ *              entry do not matter (the call clears what must start at zero)
+ *              and are undefined on return.  Calls that share a workspace must
+ *              not overlap in time.
+ *   Work split: with bf16 operands, a Gram whose contraction is at least
+ *   8192 long and whose n_p^2 units (n_p = s / 256, times the batch) fit one
+ *   round of the device's CUs (at most 256) runs every off-diagonal 256 x 256
+ *   tile as two halves of the contraction and every diagonal tile as one unit
+ *   computing only its lower half, instead of n_p (n_p + 1) / 2 whole tiles.
+ *   The two halves of a tile meet through fp32 partial tiles in the
+ *   workspace, added in either order (two terms: the sum is the same).
+ *   Results therefore depend on the device's CU count only through this
+ *   choice, and are deterministic on one device.
  * ------------------------------------------------------------------------- */
 typedef struct muon_ns_problem {
   const void* M;
@@ -155,15 +169,28 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
  * writes (a M + alpha B M) / sqrt(sumsq) (0 when sumsq[b] == 0), which is
  * the first iteration on X0 = M / ||M||_F without materialising X0.
  * ns_orthogonalize does this for bf16 momenta that are wide with sides that
- * are multiples of MUON_NS_PAD. */
+ * are multiples of MUON_NS_PAD.
+ *
+ * workspace (device, or NULL) lets ns_gram split its work as
+ * ns_orthogonalize does (see above); with NULL it does not split.  ns_poly
+ * and ns_apply take the same workspace (for one call sequence) and currently
+ * never split.  It must hold ns_stage_workspace_bytes(s, l, batch, precision)
+ * bytes (0 when nothing splits: then it is not used), be 16-byte aligned,
+ * and its first 512 bytes must be zero on the first call: they are arrival
+ * counters that every call leaves at zero.  One workspace sized for
+ * (s, l, batch) serves ns_gram(s, l), ns_poly(s) and ns_apply(s, l) on that
+ * batch; calls sharing it must not overlap in time.  Too small:
+ * MUON_EWORKSPACE. */
 int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t batch,
                  const float* sumsq, void* X0, int precision, void* stream);
+size_t ns_stage_workspace_bytes(int64_t s, int64_t l, int64_t batch, int precision);
 int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision,
-            const float* sumsq, void* stream);
+            const float* sumsq, void* workspace, size_t ws_bytes, void* stream);
 int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c,
-            int precision, void* stream);
+            int precision, void* workspace, size_t ws_bytes, void* stream);
 int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch,
-             float a, float alpha, int precision, const float* sumsq, void* stream);
+             float a, float alpha, int precision, const float* sumsq, void* workspace,
+             size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6 -- entrywise sign and 1-bit packing.

@@ -53,12 +53,13 @@ SIGNATURES = {
                                   _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
     "ns_normalize": (_c_int, [_c_void_p, _c_int, _c_i64, _c_i64, _c_i64, _c_void_p, _c_void_p,
                               _c_int, _c_void_p]),
+    "ns_stage_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
     "ns_gram": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_int, _c_void_p,
-                         _c_void_p]),
+                         _c_void_p, _c_size, _c_void_p]),
     "ns_poly": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_float, _c_float, _c_int,
-                         _c_void_p]),
+                         _c_void_p, _c_size, _c_void_p]),
     "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_float,
-                          _c_float, _c_int, _c_void_p, _c_void_p]),
+                          _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
     "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "majority_vote": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
@@ -229,29 +230,56 @@ def ns_normalize(M: torch.Tensor, sumsq: torch.Tensor, X0: torch.Tensor, precisi
         precision_code(precision), _stream(stream)))
 
 
+def ns_stage_workspace_bytes(s: int, l: int, batch: int = 1, precision="bf16") -> int:
+    return int(lib().ns_stage_workspace_bytes(s, l, batch, precision_code(precision)))
+
+
+def new_stage_workspace(s: int, l: int, batch: int = 1, precision="bf16", device=None) -> torch.Tensor:
+    """Zeroed workspace for the stage calls on [batch][s][l] (its counters start at zero)."""
+    n = ns_stage_workspace_bytes(s, l, batch, precision)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def _stage_ws(workspace, split: bool, s: int, l: int, batch: int, precision, like: torch.Tensor):
+    """(pointer, bytes) of the stage workspace: the caller's, a fresh zeroed one, or none."""
+    if not split:
+        return None, 0
+    if workspace is None:
+        workspace = new_stage_workspace(s, l, batch, precision, like.device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def ns_gram(X: torch.Tensor, A: torch.Tensor, precision="bf16", stream=None,
-            sumsq: Optional[torch.Tensor] = None) -> None:
-    """A = X X^T, or M M^T / sumsq with the raw momentum as X."""
+            sumsq: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            split: bool = True) -> None:
+    """A = X X^T, or M M^T / sumsq with the raw momentum as X.  With split
+    (the default) the work is split as ns_orthogonalize splits it, in
+    `workspace` (from new_stage_workspace) or a fresh one."""
     batch, s, l = _batch3(X)
+    ws, nbytes = _stage_ws(workspace, split, s, l, batch, precision, X)
     _check("ns_gram", lib().ns_gram(_dev(X, "X"), _dev(A, "A"), s, l, batch,
-                                    precision_code(precision), _dev(sumsq, "sumsq"), _stream(stream)))
+                                    precision_code(precision), _dev(sumsq, "sumsq"), ws, nbytes,
+                                    _stream(stream)))
 
 
 def ns_poly(A: torch.Tensor, B: torch.Tensor, b: float, c: float, precision="bf16",
-            stream=None) -> None:
+            stream=None, workspace: Optional[torch.Tensor] = None, split: bool = True) -> None:
     """B = b A + c A A."""
     batch, s, _ = _batch3(A)
+    ws, nbytes = _stage_ws(workspace, split, s, s, batch, precision, A)
     _check("ns_poly", lib().ns_poly(_dev(A, "A"), _dev(B, "B"), s, batch, float(b), float(c),
-                                    precision_code(precision), _stream(stream)))
+                                    precision_code(precision), ws, nbytes, _stream(stream)))
 
 
 def ns_apply(B: torch.Tensor, X: torch.Tensor, Xout: torch.Tensor, a: float, alpha: float = 1.0,
-             precision="bf16", stream=None, sumsq: Optional[torch.Tensor] = None) -> None:
+             precision="bf16", stream=None, sumsq: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, split: bool = True) -> None:
     """Xout = a X + alpha B X, or (a M + alpha B M) / sqrt(sumsq) with the raw momentum as X."""
     batch, s, l = _batch3(X)
+    ws, nbytes = _stage_ws(workspace, split, s, l, batch, precision, X)
     _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), s, l, batch,
                                       float(a), float(alpha), precision_code(precision),
-                                      _dev(sumsq, "sumsq"), _stream(stream)))
+                                      _dev(sumsq, "sumsq"), ws, nbytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -29,6 +29,9 @@
 //    operand strips in that XCD's L2.
 #pragma once
 
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 
 namespace muon {
@@ -69,6 +72,14 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 
 enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
 
+// Work units of the bf16 DMA kernel.  SPLIT_NONE: one workgroup per tile.
+// SPLIT_SYRK (long symmetric products whose n_p^2 units fit one round of the
+// CUs, n_p = M / BM): every off-diagonal tile runs as two K halves and every
+// diagonal tile as one unit that computes only its lower half, n_p^2 units of
+// about half a tile each instead of n_p (n_p + 1) / 2 whole tiles, which
+// would leave the other CUs idle.
+enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1 };
+
 struct GemmArgs {
   const void* P;  // rows of the left operand, k-contiguous, ld = K
   const void* Q;  // NT: rows of the right operand (k-contiguous, ld = K); NN: [K][N]
@@ -91,6 +102,12 @@ struct GemmArgs {
   int64_t s_valid, l_valid;
   int u_dtype;
   int transpose_out;
+  // work units (Split): the two halves of a split tile each store an fp32
+  // partial tile; the second to finish (counted by an arrival counter) adds
+  // the other's and runs the epilogue
+  int split_mode;
+  float* partials;       // 2 x (split tiles) x BM x BN fp32
+  int* counters;         // one per split tile: zero on entry, left zero
 };
 
 template <typename T, int BM_, int BN_, int WM_, int WN_>
@@ -456,12 +473,51 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int64_t t, int64_
   }
 }
 
+// The lower half of a 256 x 256 diagonal tile of a symmetric product in
+// 32 x 32 blocks, spread so that every SIMD gets 9 of the 36 blocks (waves
+// w and w + 4 share a SIMD).  Waves 0-3 take the 128 x 128 block below the
+// tile's diagonal as four 64 x 64 quads; waves 4-7 take the lower halves of
+// the two 128 x 128 diagonal blocks, five 32 x 32 blocks each.  P = Q for
+// these tiles, so one LDS operand serves both sides of every product: a
+// wave reads NF fragment rows and multiplies the pairs (IA[b], IB[b]).
+template <int PAT> struct DiagPattern;
+template <> struct DiagPattern<0> {   // quad: rows {a0, a1} x cols {b0, b1}
+  static constexpr int NF = 4, NB = 4;
+  static constexpr int IA[NB] = {0, 0, 1, 1}, IB[NB] = {2, 3, 2, 3};
+};
+template <> struct DiagPattern<1> {   // rows {96, 0, 32, 64}: blocks (3,0) (3,1) (3,2) (3,3) (0,0)
+  static constexpr int NF = 4, NB = 5;
+  static constexpr int IA[NB] = {0, 0, 0, 0, 1}, IB[NB] = {1, 2, 3, 0, 1};
+};
+template <> struct DiagPattern<2> {   // rows {64, 0, 32}: blocks (2,0) (2,1) (2,2) (1,0) (1,1)
+  static constexpr int NF = 3, NB = 5;
+  static constexpr int IA[NB] = {0, 0, 0, 2, 2}, IB[NB] = {1, 2, 0, 1, 2};
+};
+
+// Epilogue scalars of batch entry `batch`: C = alpha * acc + beta * Z, with the
+// folded Frobenius scale (1/sumsq for the Gram of M, 1/sqrt(sumsq) for the
+// product with M, 0 for a zero matrix)
+__device__ __forceinline__ void epilogue_scale(const GemmArgs& g, int64_t batch, float& alpha, float& beta) {
+  alpha = g.alpha;
+  beta = g.beta;
+  if (g.scale_sumsq != nullptr) {
+    const double ss = static_cast<double>(g.scale_sumsq[batch * g.stride_sumsq]);
+    const float f = ss == 0.0 ? 0.0f : static_cast<float>(g.scale_mode == 1 ? 1.0 / ss : 1.0 / sqrt(ss));
+    alpha *= f;
+    beta *= f;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   constexpr int FM = C_::FM, FN = C_::FN, BK = C_::BK;
   static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
+  // split units exist only in the 256 x 256-tile Gram (the one long symmetric
+  // product); the other instantiations carry none of their code
+  constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
+  __shared__ int split_arrival;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -472,14 +528,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   const int64_t batch = blockIdx.y;
   const int64_t KT = g.K / BK;
 
+  // ---- work unit: a whole tile, one K half of a tile, or a diagonal lower half ----
   int64_t tm, tn;
+  int64_t kb = 0, ke = KT;      // k-tiles of this unit
+  int64_t sidx = -1;            // split tile index (K halves only)
+  int half = 0;
+  bool diag_half = false;
   const int64_t tiles = SYRK ? (g.M / BM) * (g.M / BM + 1) / 2 : (g.M / BM) * (g.N / BN);
-  tile_coords<BM, BN, SYRK>(g, xcd_remap(blockIdx.x, tiles), tm, tn);
+  if (SPLITS && g.split_mode == SPLIT_SYRK) {
+    // n_p^2 units per batch entry: tile row i holds units [i^2, (i+1)^2): the two
+    // K halves of tiles (i, 0..i-1), then the lower half of diagonal tile (i, i)
+    const int64_t np = g.M / BM;
+    const int64_t v = xcd_remap(blockIdx.x, np * np);
+    int64_t i = static_cast<int64_t>(sqrt(double(v)));
+    while (i * i > v) --i;
+    while ((i + 1) * (i + 1) <= v) ++i;
+    const int64_t w = v - i * i;
+    tm = i;
+    if (w == 2 * i) {
+      tn = i;
+      diag_half = true;
+    } else {
+      tn = w >> 1;
+      half = static_cast<int>(w & 1);
+      sidx = batch * (np * (np - 1) / 2) + i * (i - 1) / 2 + tn;
+    }
+  } else {
+    tile_coords<BM, BN, SYRK>(g, xcd_remap(blockIdx.x, tiles), tm, tn);
+  }
+  if (sidx >= 0) {
+    kb = half ? KT / 2 : 0;
+    ke = half ? KT : KT / 2;
+  }
+  // the decode is uniform across the workgroup: keep it in scalar registers so
+  // the k loop bound and the tile addresses stay scalar
+  tm = __builtin_amdgcn_readfirstlane(static_cast<int>(tm));
+  tn = __builtin_amdgcn_readfirstlane(static_cast<int>(tn));
+  kb = __builtin_amdgcn_readfirstlane(static_cast<int>(kb));
+  ke = __builtin_amdgcn_readfirstlane(static_cast<int>(ke));
+  sidx = __builtin_amdgcn_readfirstlane(static_cast<int>(sidx));
+  half = __builtin_amdgcn_readfirstlane(half);
+  diag_half = __builtin_amdgcn_readfirstlane(static_cast<int>(diag_half)) != 0;
+  const int64_t nk = ke - kb;
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   // ---- DMA sources: tile origin plus a 32-bit per-lane offset (elements) ----
-  const bf16_t* Pt = static_cast<const bf16_t*>(g.P) + batch * g.strideP + m0 * g.K;
-  const bf16_t* Qt = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ + (NN ? n0 : n0 * g.K);
+  const bf16_t* Pt = static_cast<const bf16_t*>(g.P) + batch * g.strideP + m0 * g.K + kb * BK;
+  const bf16_t* Qt = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ +
+                     (NN ? n0 + kb * BK * g.N : n0 * g.K + kb * BK);
   // P (and NT Q): block b covers rows 16b..16b+15; lane -> row 16b + lane/4, slot lane%4
   uint32_t p_off[C_::P_DMA], q_off[C_::Q_DMA];
 #pragma unroll
@@ -506,16 +602,151 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
-  auto issue_stage = [&](int64_t kt) {
+  auto issue_p = [&](int64_t kt) {
     const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
     const bf16_t* pk = Pt + kt * BK;
-    const bf16_t* qk = NN ? Qt + kt * BK * g.N : Qt + kt * BK;
 #pragma unroll
     for (int q = 0; q < C_::P_DMA; ++q) dma16(pk + p_off[q], st + (wave * C_::P_DMA + q) * 1024);
+  };
+  auto issue_stage = [&](int64_t kt) {
+    issue_p(kt);
+    const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
+    const bf16_t* qk = NN ? Qt + kt * BK * g.N : Qt + kt * BK;
 #pragma unroll
     for (int q = 0; q < C_::Q_DMA; ++q)
       dma16(qk + q_off[q], st + C_::P_BYTES + (wave * C_::Q_DMA + q) * 1024);
   };
+
+  if constexpr (SPLITS) {
+    if (diag_half) {
+      // ---- lower half of a diagonal tile: P = Q, only P is staged ----
+      auto body = [&](auto pat_c) {
+        constexpr int PAT = decltype(pat_c)::value;
+        using DP = DiagPattern<PAT>;
+        constexpr int NF = DP::NF, NB = DP::NB;
+        int rows[NF];   // tile-relative first row of each fragment row-block
+        if constexpr (PAT == 0) {
+          const int qr = wave >> 1, qc = wave & 1;
+          rows[0] = 128 + 64 * qr; rows[1] = 160 + 64 * qr; rows[2] = 64 * qc; rows[3] = 64 * qc + 32;
+        } else {
+          const int base = wave >= 6 ? 128 : 0;
+          if constexpr (PAT == 1) {
+            rows[0] = base + 96; rows[1] = base; rows[2] = base + 32; rows[3] = base + 64;
+          } else {
+            rows[0] = base + 64; rows[1] = base; rows[2] = base + 32;
+          }
+        }
+        f32x16_t dacc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) dacc[b][v] = 0.0f;
+        u32x4_t f[2][NF];
+        auto read = [&](const char* st, int ks, u32x4_t (&fr)[NF]) {
+          const int chunk = 2 * ks + fgrp;
+#pragma unroll
+          for (int r = 0; r < NF; ++r)
+            fr[r] = *reinterpret_cast<const u32x4_t*>(st + krow_off(rows[r] + frow, chunk));
+        };
+        auto mma = [&](const u32x4_t (&fr)[NF]) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) Mfma<bf16_t>::mma(fr[DP::IA[b]], fr[DP::IB[b]], dacc[b]);
+        };
+        auto interleave = [&]() {
+#pragma unroll
+          for (int i = 0; i < (NF > NB ? NF : NB); ++i) {
+            if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < NB) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+        };
+        constexpr int D = C_::P_DMA;
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s)
+          if (s < nk) issue_p(s);
+        if (nk >= S - 1) wait_vm_barrier<D * (S - 2)>();
+        else wait_vm_barrier<0>();
+        read(lds, 0, f[0]);
+        int64_t it = 0;
+        for (; it < nk - (S - 1); ++it) {
+          lds_reads_done();
+          read(lds + (it % S) * C_::STAGE_BYTES, 1, f[1]);
+          mma(f[0]);
+          interleave();
+          wait_vm_barrier<D * (S - 3)>();
+          issue_p(it + S - 1);
+          lds_reads_done();
+          read(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, f[0]);
+          mma(f[1]);
+          interleave();
+        }
+        for (; it < nk; ++it) {
+          read(lds + (it % S) * C_::STAGE_BYTES, 1, f[1]);
+          mma(f[0]);
+          if (it + 1 < nk) {
+            wait_vm_barrier<0>();
+            read(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, f[0]);
+          }
+          mma(f[1]);
+        }
+        // epilogue: each 32 x 32 block through a per-wave LDS slab; off-diagonal
+        // blocks are also stored mirrored
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free
+        const bool use_z = EPI != EPI_STORE && g.beta != 0.0f;
+        float alpha, beta;
+        epilogue_scale(g, batch, alpha, beta);
+        bf16_t* C = static_cast<bf16_t*>(g.C) + batch * g.strideC;
+        const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
+        constexpr int LDB = 36;
+        float* wl = reinterpret_cast<float*>(lds) + wave * 32 * LDB;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int ra = rows[DP::IA[b]], rb = rows[DP::IB[b]];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) wl[(8 * (v >> 2) + 4 * fgrp + (v & 3)) * LDB + frow] = dacc[b][v];
+          uint2 zr[4];
+          if (use_z) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int q = lane + 64 * p, row = q >> 3, c4 = q & 7;
+              zr[p] = *reinterpret_cast<const uint2*>(Z + (m0 + ra + row) * g.N + n0 + rb + 4 * c4);
+            }
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int q = lane + 64 * p, row = q >> 3, c4 = q & 7;
+            const float4 a = *reinterpret_cast<const float4*>(wl + row * LDB + 4 * c4);
+            float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
+            if (use_z) {
+              o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
+              o[1] = fmaf(beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
+              o[2] = fmaf(beta, __uint_as_float(zr[p].y << 16), o[2]);
+              o[3] = fmaf(beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
+            }
+            const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+            const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+            *reinterpret_cast<uint2*>(C + (m0 + ra + row) * g.N + n0 + rb + 4 * c4) = make_uint2(w0, w1);
+            if (ra != rb) *reinterpret_cast<float4*>(wl + row * LDB + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+          if (ra != rb) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int q = lane + 64 * p, mr = q >> 3, c4 = q & 7;
+              float o[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDB + mr];
+              const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+              const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+              *reinterpret_cast<uint2*>(C + (n0 + rb + mr) * g.N + m0 + ra + 4 * c4) = make_uint2(w0, w1);
+            }
+          }
+        }
+      };
+      if (wave < 4) body(std::integral_constant<int, 0>{});
+      else if (wave & 1) body(std::integral_constant<int, 2>{});
+      else body(std::integral_constant<int, 1>{});
+      return;
+    }
+  }
 
   auto read_frags = [&](const char* st, int ks, u32x4_t (&fa)[FM], u32x4_t (&fb)[FN]) {
     const int chunk = 2 * ks + fgrp;
@@ -583,14 +814,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // prologue: stages 0 .. S-2 in flight, stage 0 resident
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue_stage(s);
-  if (KT >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
+    if (s < nk) issue_stage(s);
+  if (nk >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
   else wait_vm_barrier<0>();
   read_frags(lds, 0, fa[0], fb[0]);
   int64_t it = 0;
   // steady state (branch-free, so the compiler's LDS wait counts stay exact):
   // stages it+1 .. it+S-2 are in flight on entry, stage it+S-1 is issued here
-  for (; it < KT - (S - 1); ++it) {
+  for (; it < nk - (S - 1); ++it) {
     lds_reads_done();
     read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
@@ -603,14 +834,64 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     interleave();
   }
   // drain: nothing left to issue
-  for (; it < KT; ++it) {
+  for (; it < nk; ++it) {
     read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
-    if (it + 1 < KT) {
+    if (it + 1 < nk) {
       wait_vm_barrier<0>();
       read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
     }
     mma_all(fa[1], fb[1]);
+  }
+
+  // ---- K halves: both halves store their fp32 partial tile, then count in;
+  // the second to arrive adds the other half (for two terms the sum does not
+  // depend on the order) and runs the epilogue, then clears the counter.
+  // The partials move as device-coherent relaxed atomic stores and loads
+  // (global_store / global_load with sc1: written through, and read past, the
+  // per-XCD L2), so no L2 write-back or invalidation is needed; the
+  // vmcnt(0) wait puts every partial store before the counter increment, and
+  // the loads are issued only after the increment has returned ----
+  if (SPLITS && sidx >= 0) {
+    constexpr int PER_WAVE = FM * FN * 4 * kWave;   // 16-byte pieces per wave
+    typedef unsigned long long u64_t;
+    u64_t* mine = reinterpret_cast<u64_t*>(g.partials + (2 * sidx + half) * int64_t(BM * BN)) +
+                  2 * (wave * PER_WAVE + lane);
+    const u64_t* other = reinterpret_cast<const u64_t*>(g.partials + (2 * sidx + (half ^ 1)) * int64_t(BM * BN)) +
+                         2 * (wave * PER_WAVE + lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int o = 2 * ((i * FN + j) * 4 + q) * kWave;
+          const u64_t lo = (u64_t(__float_as_uint(acc[i][j][4 * q + 1])) << 32) | __float_as_uint(acc[i][j][4 * q]);
+          const u64_t hi = (u64_t(__float_as_uint(acc[i][j][4 * q + 3])) << 32) | __float_as_uint(acc[i][j][4 * q + 2]);
+          __hip_atomic_store(mine + o, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(mine + o + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are done
+    __syncthreads();
+    if (tid == 0)
+      split_arrival = __hip_atomic_fetch_add(g.counters + sidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (split_arrival == 0) return;   // first half in: the other half finishes the tile
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int o = 2 * ((i * FN + j) * 4 + q) * kWave;
+          const u64_t lo = __hip_atomic_load(other + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const u64_t hi = __hip_atomic_load(other + o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][j][4 * q] += __uint_as_float(static_cast<uint32_t>(lo));
+          acc[i][j][4 * q + 1] += __uint_as_float(static_cast<uint32_t>(lo >> 32));
+          acc[i][j][4 * q + 2] += __uint_as_float(static_cast<uint32_t>(hi));
+          acc[i][j][4 * q + 3] += __uint_as_float(static_cast<uint32_t>(hi >> 32));
+        }
+    if (tid == 0) __hip_atomic_store(g.counters + sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue, staged through LDS one 32-row slab at a time ----
@@ -626,13 +907,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   const bool mirror = SYRK && (tm != tn);
   const bool second_pass = mirror || (EPI == EPI_FINAL && g.transpose_out);
   const bool use_z = EPI != EPI_STORE && g.beta != 0.0f;
-  float alpha = g.alpha, beta = g.beta;
-  if (g.scale_sumsq != nullptr) {
-    const double ss = static_cast<double>(g.scale_sumsq[batch * g.stride_sumsq]);
-    const float f = ss == 0.0 ? 0.0f : static_cast<float>(g.scale_mode == 1 ? 1.0 / ss : 1.0 / sqrt(ss));
-    alpha *= f;
-    beta *= f;
-  }
+  float alpha, beta;
+  epilogue_scale(g, batch, alpha, beta);
   constexpr int LDW = C_::LDW;
   constexpr int CPR = WN / 4;                 // 4-column chunks per slab row
   constexpr int NP = 32 * CPR / 64;           // chunks per lane and slab
@@ -753,15 +1029,90 @@ int set_lds_limit(K kern, int bytes, bool& configured) {
   return MUON_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Split planning (host).  The scratch of a split launch is a fixed block of
+// kSplitCounters int arrival counters, then two fp32 BM x BN partial tiles
+// per split tile.  Every plan has at most kSplitCounters split tiles
+// (SPLIT_SYRK: n_p (n_p - 1) / 2 * batch < n_p^2 * batch / 2 <= 128), so one
+// scratch serves launches of any shape without its counters moving.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSplitMaxUnits = 256;   // SPLIT_SYRK: at most this many units per launch
+// SPLIT_SYRK only for contractions of at least this many 32-wide k-tiles:
+// measured on MI355X, the Gram of 4096 x 14336 (448 k-tiles) gains a fifth
+// while the 4096^3 polynomial product (128 k-tiles) does not gain, the
+// exchange of the halves costing as much as the idle CUs
+constexpr int64_t kSplitMinKTiles = 256;
+constexpr int64_t kSplitCounters = 128;
+constexpr size_t kSplitCounterBytes = kSplitCounters * sizeof(int);
+
+struct SplitPlan {
+  int mode;
+  int64_t units;         // workgroups per batch entry
+  int64_t split_tiles;   // split tiles of the whole launch
+};
+
+struct Scratch {         // caller-provided split scratch (base == nullptr: no splitting)
+  char* base;
+  size_t bytes;
+};
+
+inline size_t split_scratch_bytes(int64_t split_tiles, int bm, int bn) {
+  if (split_tiles <= 0) return 0;
+  return kSplitCounterBytes + static_cast<size_t>(split_tiles) * 2 * bm * bn * sizeof(float);
+}
+
+// cus > 0: the plan for a device with that many CUs (one 256 x 256-tile
+// workgroup per CU).  cus == 0: the largest plan any device can get, which
+// sizes the scratch.
+template <int BM, int BN, bool SYRK>
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t batch, int64_t cus) {
+  const int64_t tiles = SYRK ? (M / BM) * (M / BM + 1) / 2 : (M / BM) * (N / BN);
+  SplitPlan p{SPLIT_NONE, tiles, 0};
+  if (!SYRK || BM != 256 || K / 32 < kSplitMinKTiles || tiles == 0 || batch <= 0) return p;
+  const int64_t np = M / BM;
+  const int64_t limit = cus > 0 ? std::min(cus, kSplitMaxUnits) : kSplitMaxUnits;
+  if (np * np * batch <= limit) p = SplitPlan{SPLIT_SYRK, np * np, np * (np - 1) / 2 * batch};
+  return p;
+}
+
+// compute units of the current device (cached per device)
+inline int64_t device_cus() {
+  static int64_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
-int launch_dma(const GemmArgs& g, int64_t batch, hipStream_t st) {
+int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   const int64_t tpb = tiles_of<BM, BN, SYRK>(g);
   if (tpb == 0 || batch == 0) return MUON_OK;
+  int64_t grid = tpb;
+  g.split_mode = SPLIT_NONE;
+  // only the instantiation that carries the split units may be given a split plan
+  constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;
+  if (SPLITS && sc.base != nullptr) {
+    const int64_t cus = device_cus();
+    const SplitPlan p = cus > 0 ? plan_split<BM, BN, SYRK>(g.M, g.N, g.K, batch, cus)
+                                : SplitPlan{SPLIT_NONE, tpb, 0};
+    if (p.mode != SPLIT_NONE) {
+      if (sc.bytes < split_scratch_bytes(p.split_tiles, BM, BN) || p.split_tiles > kSplitCounters)
+        return MUON_EWORKSPACE;
+      g.split_mode = p.mode;
+      g.counters = reinterpret_cast<int*>(sc.base);
+      g.partials = reinterpret_cast<float*>(sc.base + kSplitCounterBytes);
+      grid = p.units;
+    }
+  }
   auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
   static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
   if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
-  kern<<<dim3(tpb, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  kern<<<dim3(grid, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
   return launch_status();
 }
 

@@ -125,15 +125,38 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // tiles (4 waves of 64 x 64) for short ones, where prologue and epilogue
 // weigh more.  fp32 products (small, latency-bound workloads) use the
 // register-staged kernel.
+//
+// The 256 x 256-tile symmetric products may split their work units
+// (gemm::Split) when given scratch: long contractions whose n_p^2 units fit
+// one round of the CUs.
+constexpr bool big_tiles(bool syrk, int64_t K) { return syrk || K >= 2048; }
+
 template <typename T, bool SYRK, bool NN, int EPI>
-int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st) {
-  const bool big = SYRK || g.K >= 2048;
+int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st, const gemm::Scratch& sc) {
   if constexpr (sizeof(T) == 2) {
-    if (big) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st);
-    return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st);
+    if (big_tiles(SYRK, g.K)) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st, sc);
+    return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st, gemm::Scratch{nullptr, 0});
   } else {
     return gemm::launch<T, 128, 128, 64, 64, SYRK, NN, EPI>(g, batch, st);
   }
+}
+
+// Scratch that the bf16 products of one iteration on [batch][s][l] may use:
+// the Gram's split plan (the polynomial, a contraction of s <= 4096 whenever
+// n_p^2 units fit one round, never splits).
+size_t split_scratch_bound(int64_t s, int64_t l, int64_t batch) {
+  return gemm::split_scratch_bytes(gemm::plan_split<256, 256, true>(s, s, l, batch, 0).split_tiles, 256, 256);
+}
+
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0;
+}
+
+int zero_counters(void* base, int64_t n, hipStream_t st) {
+  if (n <= 0) return MUON_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  zero_ints_kernel<<<dim3(blocks), dim3(256), 0, st>>>(static_cast<int*>(base), n);
+  return launch_status();
 }
 
 // Frobenius scaling folded into the first iteration (bf16 only): the raw
@@ -147,29 +170,31 @@ struct Fold {
 
 template <typename T>
 int gram_t(const void* X, void* A, int64_t s, int64_t l, int64_t batch, hipStream_t st,
-           const Fold& fold = Fold{}) {
+           const gemm::Scratch& sc, const Fold& fold = Fold{}) {
   GemmArgs g{};
   g.P = X; g.Q = X; g.Z = nullptr; g.C = A;
   g.M = s; g.N = s; g.K = l;
   g.strideP = g.strideQ = fold.strideX ? fold.strideX : s * l; g.strideC = s * s;
   g.alpha = 1.0f; g.beta = 0.0f;
   g.scale_sumsq = fold.sumsq; g.stride_sumsq = fold.stride_sumsq; g.scale_mode = 1;
-  return launch_gemm<T, true, false, EPI_STORE>(g, batch, st);
+  return launch_gemm<T, true, false, EPI_STORE>(g, batch, st, sc);
 }
 
 template <typename T>
-int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, hipStream_t st) {
+int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, hipStream_t st,
+           const gemm::Scratch& sc) {
   GemmArgs g{};
   g.P = A; g.Q = A; g.Z = A; g.C = B;
   g.M = s; g.N = s; g.K = s;
   g.strideP = g.strideQ = g.strideZ = g.strideC = s * s;
   g.alpha = c; g.beta = b;
-  return launch_gemm<T, true, false, EPI_AXPBY>(g, batch, st);
+  return launch_gemm<T, true, false, EPI_AXPBY>(g, batch, st, sc);
 }
 
 template <typename T>
 int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
-            float alpha, hipStream_t st, const GemmArgs* final_out, const Fold& fold = Fold{}) {
+            float alpha, hipStream_t st, const gemm::Scratch& sc, const GemmArgs* final_out,
+            const Fold& fold = Fold{}) {
   GemmArgs g{};
   if (final_out) g = *final_out;
   g.P = B; g.Q = X; g.Z = X; g.C = Xout;
@@ -177,8 +202,8 @@ int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int6
   g.strideP = s * s; g.strideQ = g.strideZ = fold.strideX ? fold.strideX : s * l; g.strideC = s * l;
   g.alpha = alpha; g.beta = a;
   g.scale_sumsq = fold.sumsq; g.stride_sumsq = fold.stride_sumsq; g.scale_mode = 2;
-  if (final_out) return launch_gemm<T, false, true, EPI_FINAL>(g, batch, st);
-  return launch_gemm<T, false, true, EPI_AXPBY>(g, batch, st);
+  if (final_out) return launch_gemm<T, false, true, EPI_FINAL>(g, batch, st, sc);
+  return launch_gemm<T, false, true, EPI_AXPBY>(g, batch, st, sc);
 }
 
 template <typename TM, typename TX>
@@ -337,6 +362,26 @@ bool valid_problem(const muon_ns_problem& p) {
   return p.rows > 0 && p.cols > 0 && p.M && p.U;
 }
 
+// The workspace of ns_orthogonalize starts with the split scratch shared by
+// every product of every run (its counters are cleared once per call and
+// each launch leaves them clear), followed by the largest run's buffers.
+struct SplitRegion {
+  size_t bytes;
+};
+
+SplitRegion split_region(const std::vector<Run>& runs, int precision) {
+  SplitRegion R{0};
+  if (precision != MUON_BF16) return R;
+  for (const Run& r : runs) R.bytes = std::max(R.bytes, round_up(split_scratch_bound(r.sp, r.lp, r.count), 256));
+  return R;
+}
+
+size_t runs_bytes(const std::vector<Run>& runs, int precision) {
+  size_t need = 0;
+  for (const Run& r : runs) need = std::max(need, layout_of(r, precision).total);
+  return need;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -348,9 +393,7 @@ size_t ns_workspace_bytes(const muon_ns_problem* probs, int count, int precision
   if (!probs || count <= 0 || (precision != MUON_F32 && precision != MUON_BF16)) return 0;
   for (int i = 0; i < count; ++i)
     if (!valid_problem(probs[i])) return 0;
-  size_t need = 0;
-  for (const Run& r : make_runs(probs, count)) need = std::max(need, layout_of(r, precision).total);
-  return need;
+  return split_region(make_runs(probs, count), precision).bytes + runs_bytes(make_runs(probs, count), precision);
 }
 
 int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, float c, int steps,
@@ -366,13 +409,20 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     if (!aligned16(p.M) || !aligned16(p.U)) return MUON_EALIGN;
   }
   const std::vector<Run> runs = make_runs(probs, count);
-  size_t need = 0;
-  for (const Run& r : runs) need = std::max(need, layout_of(r, precision).total);
+  const SplitRegion split = split_region(runs, precision);
+  const size_t need = split.bytes + runs_bytes(runs, precision);
   if (!workspace || ws_bytes < need) return MUON_EWORKSPACE;
   if (!aligned16(workspace)) return MUON_EALIGN;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+  // bf16 products may split (a symmetric product with one tile row needs no
+  // scratch: its only unit is the diagonal lower half)
+  const gemm::Scratch sc{precision == MUON_BF16 ? static_cast<char*>(workspace) : nullptr, split.bytes};
+  if (steps > 0 && split.bytes) {
+    const int status = zero_counters(workspace, gemm::kSplitCounters, st);
+    if (status != MUON_OK) return status;
+  }
+  char* ws = static_cast<char*>(workspace) + split.bytes;
   for (const Run& r : runs) {
     const RunLayout L = layout_of(r, precision);
     const float* sumsq = r.sumsq;
@@ -419,17 +469,17 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
       const Fold fold = first_folded ? Fold{sumsq, stride_sumsq, r.strideM} : Fold{};
       if (precision == MUON_BF16) {
         // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
-        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, fold);
-        if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st);
+        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, sc, fold);
+        if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st, sc);
         if (status == MUON_OK)
           status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
-                                   st, last ? &fin : nullptr, fold);
+                                   st, sc, last ? &fin : nullptr, fold);
       } else {
-        status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st);
-        if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st);
+        status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st, sc);
+        if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st, sc);
         if (status == MUON_OK)
           status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
-                                  st, last ? &fin : nullptr);
+                                  st, sc, last ? &fin : nullptr);
       }
       if (status != MUON_OK) return status;
     }
@@ -454,42 +504,70 @@ int ns_normalize(const void* M, int m_dtype, int64_t rows, int64_t cols, int64_t
                             batch, static_cast<hipStream_t>(stream));
 }
 
+size_t ns_stage_workspace_bytes(int64_t s, int64_t l, int64_t batch, int precision) {
+  if (!stage_dims_ok(s, l, batch) || precision != MUON_BF16) return 0;
+  return split_scratch_bound(s, l, batch);
+}
+
+// scratch of a stage call: null (no splitting) or at least
+// ns_stage_workspace_bytes, 16-byte aligned
+static int stage_scratch(void* workspace, size_t ws_bytes, int64_t s, int64_t l, int64_t batch,
+                         int precision, gemm::Scratch& sc) {
+  sc = gemm::Scratch{nullptr, 0};
+  if (!workspace || precision != MUON_BF16) return MUON_OK;
+  if (ws_bytes < split_scratch_bound(s, l, batch)) return MUON_EWORKSPACE;
+  if (!aligned16(workspace)) return MUON_EALIGN;
+  sc = gemm::Scratch{static_cast<char*>(workspace), ws_bytes};
+  return MUON_OK;
+}
+
 int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int precision,
-            const float* sumsq, void* stream) {
+            const float* sumsq, void* workspace, size_t ws_bytes, void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
   if (sumsq && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!X || !A) return MUON_EINVAL;
   if (!aligned16(X) || !aligned16(A)) return MUON_EALIGN;
+  gemm::Scratch sc;
+  const int status = stage_scratch(workspace, ws_bytes, s, l, batch, precision, sc);
+  if (status != MUON_OK) return status;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? gram_t<bf16_t>(X, A, s, l, batch, st, Fold{sumsq, 1, 0})
-                                : gram_t<float>(X, A, s, l, batch, st);
+  return precision == MUON_BF16 ? gram_t<bf16_t>(X, A, s, l, batch, st, sc, Fold{sumsq, 1, 0})
+                                : gram_t<float>(X, A, s, l, batch, st, sc);
 }
 
 int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c, int precision,
-            void* stream) {
+            void* workspace, size_t ws_bytes, void* stream) {
   if (!stage_dims_ok(s, s, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!A || !B) return MUON_EINVAL;
   if (!aligned16(A) || !aligned16(B)) return MUON_EALIGN;
+  gemm::Scratch sc;
+  const int status = stage_scratch(workspace, ws_bytes, s, s, batch, precision, sc);
+  if (status != MUON_OK) return status;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? poly_t<bf16_t>(A, B, s, batch, b, c, st)
-                                : poly_t<float>(A, B, s, batch, b, c, st);
+  return precision == MUON_BF16 ? poly_t<bf16_t>(A, B, s, batch, b, c, st, sc)
+                                : poly_t<float>(A, B, s, batch, b, c, st, sc);
 }
 
 int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
-             float alpha, int precision, const float* sumsq, void* stream) {
+             float alpha, int precision, const float* sumsq, void* workspace, size_t ws_bytes,
+             void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
   if (sumsq && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!B || !X || !Xout) return MUON_EINVAL;
   if (!aligned16(B) || !aligned16(X) || !aligned16(Xout)) return MUON_EALIGN;
+  gemm::Scratch sc;
+  const int status = stage_scratch(workspace, ws_bytes, s, l, batch, precision, sc);
+  if (status != MUON_OK) return status;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return precision == MUON_BF16 ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, nullptr, Fold{sumsq, 1, 0})
-                                : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, nullptr);
+  return precision == MUON_BF16
+             ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr, Fold{sumsq, 1, 0})
+             : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr);
 }
 
 }  // extern "C"

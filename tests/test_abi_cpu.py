@@ -85,15 +85,37 @@ def test_pack_vote_update_validation(L):
 
 
 def test_stage_validation(L):
-    assert L.ns_gram(A1, A2, 250, 512, 1, 1, None, None) == EINVAL      # s not padded
-    assert L.ns_gram(A1, A2, 512, 256, 1, 1, None, None) == EINVAL      # s > l
-    assert L.ns_gram(A1, A2, 256, 512, 1, 7, None, None) == EDTYPE
-    assert L.ns_gram(A1, A2, 256, 512, 1, 0, A3, None) == EDTYPE        # folded scaling: bf16 only
-    assert L.ns_poly(A1, MISALIGNED, 256, 1, 1.0, 1.0, 1, None) == EALIGN
-    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None, None) == EINVAL
-    assert L.ns_apply(A1, A2, A3, 256, 256, 1, 1.0, 1.0, 0, A3, None) == EDTYPE
+    assert L.ns_gram(A1, A2, 250, 512, 1, 1, None, None, 0, None) == EINVAL      # s not padded
+    assert L.ns_gram(A1, A2, 512, 256, 1, 1, None, None, 0, None) == EINVAL      # s > l
+    assert L.ns_gram(A1, A2, 256, 512, 1, 7, None, None, 0, None) == EDTYPE
+    assert L.ns_gram(A1, A2, 256, 512, 1, 0, A3, None, 0, None) == EDTYPE        # folded scaling: bf16 only
+    assert L.ns_poly(A1, MISALIGNED, 256, 1, 1.0, 1.0, 1, None, 0, None) == EALIGN
+    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert L.ns_apply(A1, A2, A3, 256, 256, 1, 1.0, 1.0, 0, A3, None, 0, None) == EDTYPE
     assert L.ns_normalize(A1, 1, 0, 5, 1, A2, A3, 1, None) == EINVAL
-    assert L.ns_gram(A1, A2, 256, 256, 0, 1, None, None) == OK           # empty batch: no launch
+    assert L.ns_gram(A1, A2, 256, 256, 0, 1, None, None, 0, None) == OK           # empty batch: no launch
+    # a stage workspace, when given, must be large enough and aligned
+    need = L.ns_stage_workspace_bytes(4096, 14336, 1, 1)
+    assert L.ns_gram(A1, A2, 4096, 14336, 1, 1, None, A3, need - 1, None) == EWORKSPACE
+    assert L.ns_apply(A1, A2, A3, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
+    assert L.ns_gram(A1, A2, 4096, 14336, 1, 1, None, MISALIGNED, need, None) == EALIGN
+
+
+def test_stage_workspace_bytes(L):
+    """Split scratch: 512 bytes of arrival counters, then two fp32 256 x 256 partial
+    tiles per split tile.  Only symmetric products with a contraction of at least
+    8192 whose n_p^2 units (n_p = s / 256) fit one round of 256 CUs split: the Gram
+    of 4096 x 14336 splits its 120 off-diagonal tiles; fp32 never splits."""
+    tile = 2 * 256 * 256 * 4
+    assert L.ns_stage_workspace_bytes(4096, 14336, 1, 1) == 512 + 120 * tile
+    assert L.ns_stage_workspace_bytes(4096, 14336, 1, 0) == 0
+    assert L.ns_stage_workspace_bytes(4096, 4096, 1, 1) == 0                 # contraction too short
+    assert L.ns_stage_workspace_bytes(7168, 18432, 1, 1) == 0                # 28^2 units > 256
+    assert L.ns_stage_workspace_bytes(1024, 8192, 3, 1) == 512 + 18 * tile   # 16 x 3 units
+    assert L.ns_stage_workspace_bytes(1024, 8192, 17, 1) == 0                # 16 x 17 units > 256
+    assert L.ns_stage_workspace_bytes(256, 8192, 5, 1) == 0                  # diagonal units only
+    assert L.ns_stage_workspace_bytes(768, 2304, 12, 1) == 0
+    assert L.ns_stage_workspace_bytes(250, 512, 1, 1) == 0                   # invalid shape
 
 
 def _problems(specs):
@@ -104,16 +126,20 @@ def _problems(specs):
     return arr
 
 
-def _ns_bytes(count, s, l, es=2, sumsq=True, part=0):
+def _ns_bytes(count, s, l, es=2, sumsq=True, part=0, split=0):
+    """Run buffers (two X, A, B, sums, norm partials) after the split scratch: 512
+    bytes of counters and two fp32 256 x 256 partial tiles per split tile."""
     def up(x):
         return -(-x // 256) * 256
-    return (2 * up(count * s * l * es) + 2 * up(count * s * s * es) + (0 if sumsq else up(4 * count))
-            + up(part))
+    scratch = 512 + split * 2 * 256 * 256 * 4 if split else 0
+    return (scratch + 2 * up(count * s * l * es) + 2 * up(count * s * s * es)
+            + (0 if sumsq else up(4 * count)) + up(part))
 
 
 def test_ns_workspace_single_and_padding(L):
     arr = _problems([(0x10000, 0x20000, 0x30000, 4096, 14336, 1, 1)])
-    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 4096, 14336)
+    # split tiles: the Gram's 120 off-diagonal tiles
+    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 4096, 14336, split=120)
     arr = _problems([(0x10000, 0x20000, 0x30000, 300, 70, 1, 1)])    # tall, ragged
     assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 256, 512)
     assert L.ns_workspace_bytes(arr, 1, 0) == _ns_bytes(1, 256, 512, es=4)

@@ -1,0 +1,123 @@
+"""GPU parity of the split work units of the symmetric products.
+
+A symmetric product with a contraction of at least 8192 whose n_p^2 units
+(n_p = s / 256) fit one round of the CUs runs each off-diagonal 256 x 256
+tile as two halves of the contraction, whose fp32 partials meet through the
+workspace, and each diagonal tile as one unit that computes only its lower
+half.  Each case is checked against the fp64 oracle at the stage tolerance
+(one bf16 rounding of the output), against the same call without splitting
+(the halves change only where the fp32 sum is split), for exact symmetry off
+the 32 x 32 diagonal blocks, for zero padding, and for the arrival counters
+being left at zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import matrix_aware_optimizer_amd as mao
+import oracle.muon_oracle as O
+from helpers import from_dev, rel_fro, to_dev
+from workloads import QUINTIC, random_matrix, store
+
+pytestmark = pytest.mark.gpu
+
+TOL_STAGE = 2.0 ** -8
+# split and unsplit sums differ by fp32 reassociation before one bf16 rounding
+TOL_SPLIT_VS_WHOLE = 2.0 ** -9
+
+
+def _counters_clear(ws):
+    return not ws[:512].cpu().numpy().any()
+
+
+def _X(batch, s, l, seed, sv=None, lv=None):
+    sv, lv = sv or s, lv or l
+    X = np.zeros((batch, s, l))
+    X[:, :sv, :lv] = random_matrix((batch, sv, lv), [320, seed]) / np.sqrt(sv * lv)
+    return store(X, "bf16")
+
+
+def _off_diagonal_block_symmetry(A, s):
+    """A equals A^T exactly outside the 32 x 32 blocks on the diagonal (those are
+    computed whole; every other block is stored once and mirrored)."""
+    mask = np.ones((s, s), bool)
+    for k in range(0, s, 32):
+        mask[k:k + 32, k:k + 32] = False
+    return np.array_equal(A[mask], A.T[mask])
+
+
+@pytest.mark.parametrize("batch,s,l,sv,lv", [(1, 512, 8192, 512, 8000), (3, 1024, 8192, 1000, 8192),
+                                              (1, 4096, 8192, 4096, 8192), (12, 768, 8192, 768, 8192),
+                                              (2, 256, 8192, 200, 8192), (1, 4096, 14336, 4096, 14336)])
+def test_gram_split_units(batch, s, l, sv, lv):
+    Xs = _X(batch, s, l, 1, sv, lv)
+    Xd = to_dev(Xs, "bf16").view(batch, s, l)
+    ws = mao.new_stage_workspace(s, l, batch)
+    A = torch.empty((batch, s, s), dtype=torch.bfloat16, device="cuda")
+    A0 = torch.empty_like(A)
+    mao.ns_gram(Xd, A, workspace=ws)
+    mao.ns_gram(Xd, A0, split=False)
+    torch.cuda.synchronize()
+    assert _counters_clear(ws)
+    raw = from_dev(A).reshape(batch, s, s)
+    got = O.decode(raw, "bf16")
+    whole = O.decode(from_dev(A0), "bf16").reshape(batch, s, s)
+    X = O.decode(Xs, "bf16")
+    for b in sorted({0, batch - 1}):
+        ref = O.gram(X[b])
+        assert rel_fro(got[b], ref) <= TOL_STAGE
+        assert rel_fro(got[b], whole[b]) <= TOL_SPLIT_VS_WHOLE
+        assert _off_diagonal_block_symmetry(raw[b], s)
+        assert not got[b][sv:, :].any() and not got[b][:, sv:].any()      # padding stays zero
+
+
+def test_gram_split_with_folded_scaling():
+    """The first iteration's Gram reads the raw momentum and scales by 1/sum(M^2) in
+    both epilogues (the K halves' and the diagonal units')."""
+    s, l = 1024, 8192
+    M = store(random_matrix((1, s, l), [323, 0]), "bf16")
+    Md = to_dev(M, "bf16").view(1, s, l)
+    Mf = O.decode(M, "bf16")
+    sums = torch.tensor([O.sumsq(Mf[0])], dtype=torch.float32, device="cuda")
+    A = torch.empty((1, s, s), dtype=torch.bfloat16, device="cuda")
+    mao.ns_gram(Md, A, sumsq=sums)
+    got = O.decode(from_dev(A), "bf16").reshape(s, s)
+    assert rel_fro(got, O.gram(O.frobenius_normalize(Mf[0]))) <= TOL_STAGE
+
+
+def test_gram_split_zero_matrix():
+    s, l = 512, 8192
+    Md = torch.zeros((1, s, l), dtype=torch.bfloat16, device="cuda")
+    A = torch.full((1, s, s), 3.0, dtype=torch.bfloat16, device="cuda")
+    mao.ns_gram(Md, A, sumsq=torch.zeros(1, dtype=torch.float32, device="cuda"))
+    assert not from_dev(A).any()
+
+
+def test_split_calls_are_repeatable_on_one_workspace():
+    """Three Gram calls on one workspace (each leaves the counters at zero) give
+    identical bits."""
+    s, l = 4096, 8192
+    Xd = to_dev(_X(1, s, l, 4), "bf16").view(1, s, l)
+    ws = mao.new_stage_workspace(s, l, 1)
+    outs = []
+    for _ in range(3):
+        A = torch.empty((1, s, s), dtype=torch.bfloat16, device="cuda")
+        mao.ns_gram(Xd, A, workspace=ws)
+        outs.append(from_dev(A))
+    torch.cuda.synchronize()
+    assert _counters_clear(ws)
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+
+
+@pytest.mark.parametrize("shape", [(1024, 8192), (8192, 1024)])
+def test_ns_with_split_gram_matches_oracle(shape):
+    """Whole iteration whose Grams split (4^2 units): wide (scaling folded into the first
+    iteration) and tall (normalised and transposed first, U transposed back)."""
+    M = store(random_matrix(shape, [322, shape[0]]), "bf16")
+    Md = to_dev(M, "bf16").view(*shape)
+    U = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    sums = torch.tensor([O.sumsq(O.decode(M, "bf16"))], dtype=torch.float32, device="cuda")
+    mao.ns_orthogonalize([(Md, U, sums)], *QUINTIC, 5, "bf16")
+    ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
+    assert rel_fro(O.decode(from_dev(U), "bf16"), ref) <= 2e-2
