@@ -155,33 +155,44 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(TM* __restrict__ M,
   }
 }
 
-// One block per segment adds that segment's piece partials in a fixed order.
-__global__ __launch_bounds__(kThreads) void segment_reduce_kernel(const double* __restrict__ partials,
-                                                                 SegMap seg, int64_t nchunks,
-                                                                 float* __restrict__ out) {
-  __shared__ double red[kThreads / kWave];
+// One block of kReduceThreads per segment adds that segment's piece partials
+// in a fixed order: thread t adds entries b0 + t, b0 + t + kReduceThreads, ...
+// in that order, with kReduceLoads loads in flight, then the block sum runs
+// in a fixed butterfly order.  A segment of one 4096 x 14336 matrix has 14336
+// partials: one pass of loads per thread.
+constexpr int kReduceThreads = 1024;
+constexpr int kReduceLoads = 16;
+
+__global__ __launch_bounds__(kReduceThreads) void segment_reduce_kernel(const double* __restrict__ partials,
+                                                                       SegMap seg, int64_t nchunks,
+                                                                       float* __restrict__ out) {
+  __shared__ double red[kReduceThreads / kWave];
   const int s = blockIdx.x;
   const int64_t s0 = seg.at(s), s1 = seg.at(s + 1);
   double acc = 0.0;
   if (s1 > s0 && s0 >= 0) {
     // clamped so that offsets beyond numel cannot index past the partials
     const int64_t b0 = s0 / kChunk, b1 = min((s1 - 1) / kChunk, nchunks - 1);
-    // each thread adds its entries b0 + tid, b0 + tid + kThreads, ... in that
-    // order; eight loads are issued before the adds
-    constexpr int kU = 8;
-    for (int64_t b = b0 + threadIdx.x; b <= b1; b += kU * kThreads) {
-      double x[kU];
+    for (int64_t b = b0 + threadIdx.x; b <= b1; b += int64_t(kReduceLoads) * kReduceThreads) {
+      double x[kReduceLoads];
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const int64_t i = b + int64_t(j) * kThreads;
+      for (int j = 0; j < kReduceLoads; ++j) {
+        const int64_t i = b + int64_t(j) * kReduceThreads;
         x[j] = i <= b1 ? partials[i + s] : 0.0;
       }
 #pragma unroll
-      for (int j = 0; j < kU; ++j) acc += x[j];
+      for (int j = 0; j < kReduceLoads; ++j) acc += x[j];
     }
   }
-  const double tot = block_sum(acc, red);
-  if (threadIdx.x == 0) out[s] = static_cast<float>(tot);
+  acc = wave_sum(acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kReduceThreads / kWave; ++i) t += red[i];
+    out[s] = static_cast<float>(t);
+  }
 }
 
 template <typename TM, typename TG, bool UPDATE>
@@ -198,7 +209,7 @@ int launch_momentum(TM* M, const TG* G, int64_t numel, SegMap seg, float beta, f
           M, G, numel, seg, beta, alpha, partials);
   }
   if (sumsq_out && seg.nseg > 0)
-    segment_reduce_kernel<<<dim3(seg.nseg), dim3(kThreads), 0, stream>>>(partials, seg, nchunks,
+    segment_reduce_kernel<<<dim3(seg.nseg), dim3(kReduceThreads), 0, stream>>>(partials, seg, nchunks,
                                                                           sumsq_out);
   return launch_status();
 }

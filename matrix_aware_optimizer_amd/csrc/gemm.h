@@ -105,6 +105,11 @@ struct GemmArgs {
   // work units (Split): the two halves of a split tile each store an fp32
   // partial tile; the second to finish (counted by an arrival counter) adds
   // the other's and runs the epilogue
+  // Row stride (elements) of Q for NN, Z and C; 0 means N.  A launch may
+  // cover columns [col0, col0 + N) of a wider output: its Q, Z and C point at
+  // column col0, and col0 places the columns of U (EPI_FINAL).
+  int64_t ld;
+  int64_t col0;
   int split_mode;
   float* partials;       // 2 x (split tiles) x BM x BN fp32
   int* counters;         // one per split tile: zero on entry, left zero
@@ -575,7 +580,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // ---- DMA sources: tile origin plus a 32-bit per-lane offset (elements) ----
   const bf16_t* Pt = static_cast<const bf16_t*>(g.P) + batch * g.strideP + m0 * g.K + kb * BK;
   const bf16_t* Qt = static_cast<const bf16_t*>(g.Q) + batch * g.strideQ +
-                     (NN ? n0 + kb * BK * g.N : n0 * g.K + kb * BK);
+                     (NN ? n0 + kb * BK * g.ld : n0 * g.K + kb * BK);
   // P (and NT Q): block b covers rows 16b..16b+15; lane -> row 16b + lane/4, slot lane%4
   uint32_t p_off[C_::P_DMA], q_off[C_::Q_DMA];
 #pragma unroll
@@ -596,7 +601,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
       constexpr int ROWS_PER_BLOCK = 64 / ROW_CHUNKS;
       const int r = ROWS_PER_BLOCK * b + lane / ROW_CHUNKS;
       const int c = nrow_slot(lane % ROW_CHUNKS, r);   // the slot is an involution
-      q_off[i] = uint32_t(r) * uint32_t(g.N) + c * 8;
+      q_off[i] = uint32_t(r) * uint32_t(g.ld) + c * 8;
     }
   }
   const uint32_t lds_base =
@@ -611,7 +616,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   auto issue_stage = [&](int64_t kt) {
     issue_p(kt);
     const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
-    const bf16_t* qk = NN ? Qt + kt * BK * g.N : Qt + kt * BK;
+    const bf16_t* qk = NN ? Qt + kt * BK * g.ld : Qt + kt * BK;
 #pragma unroll
     for (int q = 0; q < C_::Q_DMA; ++q)
       dma16(qk + q_off[q], st + C_::P_BYTES + (wave * C_::Q_DMA + q) * 1024);
@@ -708,7 +713,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               const int q = lane + 64 * p, row = q >> 3, c4 = q & 7;
-              zr[p] = *reinterpret_cast<const uint2*>(Z + (m0 + ra + row) * g.N + n0 + rb + 4 * c4);
+              zr[p] = *reinterpret_cast<const uint2*>(Z + (m0 + ra + row) * g.ld + n0 + rb + 4 * c4);
             }
           }
 #pragma unroll
@@ -724,7 +729,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
             }
             const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
             const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
-            *reinterpret_cast<uint2*>(C + (m0 + ra + row) * g.N + n0 + rb + 4 * c4) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(C + (m0 + ra + row) * g.ld + n0 + rb + 4 * c4) = make_uint2(w0, w1);
             if (ra != rb) *reinterpret_cast<float4*>(wl + row * LDB + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
           }
           if (ra != rb) {
@@ -736,7 +741,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
               for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDB + mr];
               const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
               const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
-              *reinterpret_cast<uint2*>(C + (n0 + rb + mr) * g.N + m0 + ra + 4 * c4) = make_uint2(w0, w1);
+              *reinterpret_cast<uint2*>(C + (n0 + rb + mr) * g.ld + m0 + ra + 4 * c4) = make_uint2(w0, w1);
             }
           }
         }
@@ -928,7 +933,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
-        zr[p] = *reinterpret_cast<const uint2*>(Z + (r0 + row) * g.N + c0 + 4 * c4);
+        zr[p] = *reinterpret_cast<const uint2*>(Z + (r0 + row) * g.ld + c0 + 4 * c4);
       }
     }
 #pragma unroll
@@ -947,8 +952,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         if (!g.transpose_out && grow < g.s_valid) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            if (gcol + t < g.l_valid) {
-              const int64_t idx = batch * g.strideU + grow * g.l_valid + gcol + t;
+            if (g.col0 + gcol + t < g.l_valid) {
+              const int64_t idx = batch * g.strideU + grow * g.l_valid + g.col0 + gcol + t;
               if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx] = f32_to_bf16(o[t]);
               else static_cast<float*>(g.U)[idx] = o[t];
             }
@@ -957,7 +962,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
       } else {
         const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
         const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
-        *reinterpret_cast<uint2*>(C + grow * g.N + gcol) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(C + grow * g.ld + gcol) = make_uint2(w0, w1);
       }
       if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
     }
@@ -971,11 +976,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDW + mr];
         const int64_t orow = c0 + mr, ocol = r0 + 4 * c4;
         if (EPI == EPI_FINAL) {
-          if (orow < g.l_valid) {
+          if (g.col0 + orow < g.l_valid) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               if (ocol + t < g.s_valid) {
-                const int64_t idx = batch * g.strideU + orow * g.s_valid + ocol + t;
+                const int64_t idx = batch * g.strideU + (g.col0 + orow) * g.s_valid + ocol + t;
                 if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx] = f32_to_bf16(o[t]);
                 else static_cast<float*>(g.U)[idx] = o[t];
               }
@@ -984,7 +989,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         } else {
           const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
           const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
-          *reinterpret_cast<uint2*>(C + orow * g.N + ocol) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(C + orow * g.ld + ocol) = make_uint2(w0, w1);
         }
       }
     }
@@ -1093,6 +1098,7 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
   const int64_t tpb = tiles_of<BM, BN, SYRK>(g);
   if (tpb == 0 || batch == 0) return MUON_OK;
   int64_t grid = tpb;
+  if (g.ld == 0) g.ld = g.N;
   g.split_mode = SPLIT_NONE;
   // only the instantiation that carries the split units may be given a split plan
   constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;

@@ -131,9 +131,43 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // one round of the CUs.
 constexpr bool big_tiles(bool syrk, int64_t K) { return syrk || K >= 2048; }
 
+// B X on 256 x 256 tiles: when the last round of tiles would leave at least
+// half of the CUs idle and those tiles form whole column strips, the strips
+// run as a second launch of 128 x 256 tiles (twice the tiles at half the work
+// each), so that round fills the CUs.  4096 x 14336: 768 tiles (three
+// rounds of 256 CUs), then 256 tiles of 128 x 256 over the last 2048 columns.
+template <int EPI>
+int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
+  const gemm::Scratch none{nullptr, 0};
+  const int64_t TM = g.M / 256, TN = g.N / 256, T = TM * TN;
+  const int64_t cus = batch == 1 ? gemm::device_cus() : 0;
+  int64_t ct = 0;   // 256-column strips in the second launch
+  if (cus > 0 && TM > 0) {
+    const int64_t r = T % cus;
+    if (r > 0 && 2 * r <= cus && r % TM == 0 && r / TM < TN) ct = r / TM;
+  }
+  if (ct == 0) return gemm::launch_dma<256, 256, 64, 128, 4, false, true, EPI>(g, batch, st, none);
+  const int64_t n1 = (TN - ct) * 256;
+  GemmArgs g1 = g;
+  g1.ld = g.N;
+  g1.N = n1;
+  int status = gemm::launch_dma<256, 256, 64, 128, 4, false, true, EPI>(g1, batch, st, none);
+  if (status != MUON_OK) return status;
+  GemmArgs g2 = g;
+  g2.ld = g.N;
+  g2.N = ct * 256;
+  g2.col0 = n1;
+  g2.Q = static_cast<const bf16_t*>(g.Q) + n1;
+  if (g.Z) g2.Z = static_cast<const bf16_t*>(g.Z) + n1;
+  g2.C = static_cast<bf16_t*>(g.C) + n1;
+  return gemm::launch_dma<128, 256, 64, 64, 4, false, true, EPI>(g2, batch, st, none);
+}
+
 template <typename T, bool SYRK, bool NN, int EPI>
 int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st, const gemm::Scratch& sc) {
   if constexpr (sizeof(T) == 2) {
+    if constexpr (NN && !SYRK)
+      if (big_tiles(SYRK, g.K)) return launch_apply_big<EPI>(g, batch, st);
     if (big_tiles(SYRK, g.K)) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st, sc);
     return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st, gemm::Scratch{nullptr, 0});
   } else {

@@ -1,4 +1,5 @@
-"""GPU parity of the split work units of the symmetric products.
+"""GPU parity of the work units that fill the CUs: split symmetric products and
+the B X product's last round as column strips.
 
 A symmetric product with a contraction of at least 8192 whose n_p^2 units
 (n_p = s / 256) fit one round of the CUs runs each off-diagonal 256 x 256
@@ -121,3 +122,39 @@ def test_ns_with_split_gram_matches_oracle(shape):
     mao.ns_orthogonalize([(Md, U, sums)], *QUINTIC, 5, "bf16")
     ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
     assert rel_fro(O.decode(from_dev(U), "bf16"), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("s,l", [(4096, 14336), (4096, 5120)])
+def test_apply_last_round_as_column_strips(s, l):
+    """B X on 256 x 256 tiles whose last round would leave half of the 256 CUs idle
+    runs that round's column strips as 128 x 256 tiles: 4096 x 14336 has 896 tiles,
+    the last 128 (2048 columns) become 256; 4096 x 5120 has 320, the last 64 become
+    128.  Both launches write one output; checked against the fp64 product."""
+    Xs = _X(1, s, l, 3)
+    R = random_matrix((1, s, s), [321, 0]) / np.sqrt(s)
+    Bs = store(R + np.transpose(R, (0, 2, 1)), "bf16")
+    Xd = to_dev(Xs, "bf16").view(1, s, l)
+    out = torch.empty_like(Xd)
+    mao.ns_apply(to_dev(Bs, "bf16").view(1, s, s), Xd, out, QUINTIC[0], 1.0)
+    got = O.decode(from_dev(out), "bf16").reshape(s, l)
+    ref = O.apply_poly(O.decode(Bs, "bf16")[0], O.decode(Xs, "bf16")[0], QUINTIC[0])
+    assert rel_fro(got, ref) <= TOL_STAGE
+    # the strips of the second launch are checked on their own
+    assert rel_fro(got[:, -1024:], ref[:, -1024:]) <= TOL_STAGE
+
+
+@pytest.mark.parametrize("shape", [(4096, 5120), (5120, 4096)])
+def test_ns_final_iteration_through_column_strips(shape):
+    """One iteration on 4096 x 5120 (wide, scaling folded in) and 5120 x 4096 (tall:
+    the final epilogue writes U transposed): the last 1024 working columns are
+    produced by the 128 x 256-tile launch, whose U rows or columns sit at an offset."""
+    M = store(random_matrix(shape, [324, shape[0]]), "bf16")
+    Md = to_dev(M, "bf16").view(*shape)
+    U = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    mao.ns_orthogonalize([(Md, U, None)], *QUINTIC, 1, "bf16")
+    got = O.decode(from_dev(U), "bf16")
+    ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 1)
+    # the Newton-Schulz gate (a misplaced strip would give an error of order one)
+    assert rel_fro(got, ref) <= 2e-2
+    tail = (slice(None), slice(-1024, None)) if shape[0] < shape[1] else (slice(-1024, None), slice(None))
+    assert rel_fro(got[tail], ref[tail]) <= 2e-2
