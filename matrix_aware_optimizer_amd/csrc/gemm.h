@@ -499,6 +499,16 @@ template <> struct DiagPattern<2> {   // rows {64, 0, 32}: blocks (2,0) (2,1) (2
   static constexpr int IA[NB] = {0, 0, 0, 2, 2}, IB[NB] = {1, 2, 0, 1, 2};
 };
 
+// Column of slab element (row, col) in the epilogue's LDS slab: the column is
+// XOR-swizzled by the row's group of four (bits 3 and up), which keeps 4-column
+// groups contiguous for 16-byte accesses and spreads the transposed reads
+// (four rows 4c..4c+3 at one column, eight columns per instruction) over the
+// banks.  MASK = 7 for slabs of 64 or more columns, 3 for 32.
+template <int MASK>
+__device__ __forceinline__ int slab_col(int row, int col) {
+  return col ^ (((row >> 2) & MASK) << 3);
+}
+
 // Epilogue scalars of batch entry `batch`: C = alpha * acc + beta * Z, with the
 // folded Frobenius scale (1/sumsq for the Gram of M, 1/sqrt(sumsq) for the
 // product with M, 0 for a zero matrix)
@@ -518,11 +528,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   constexpr int FM = C_::FM, FN = C_::FN, BK = C_::BK;
   static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
+  static_assert(WN >= 64, "the epilogue slab swizzle (slab_col<7>) needs 64 or more columns per wave");
   // split units exist only in the 256 x 256-tile Gram (the one long symmetric
   // product); the other instantiations carry none of their code
   constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  __shared__ int split_arrival;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -707,7 +717,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         for (int b = 0; b < NB; ++b) {
           const int ra = rows[DP::IA[b]], rb = rows[DP::IB[b]];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) wl[(8 * (v >> 2) + 4 * fgrp + (v & 3)) * LDB + frow] = dacc[b][v];
+          for (int v = 0; v < 16; ++v) {
+            const int row = 8 * (v >> 2) + 4 * fgrp + (v & 3);
+            wl[row * LDB + slab_col<3>(row, frow)] = dacc[b][v];
+          }
           uint2 zr[4];
           if (use_z) {
 #pragma unroll
@@ -719,7 +732,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const int q = lane + 64 * p, row = q >> 3, c4 = q & 7;
-            const float4 a = *reinterpret_cast<const float4*>(wl + row * LDB + 4 * c4);
+            const float4 a = *reinterpret_cast<const float4*>(wl + row * LDB + slab_col<3>(row, 4 * c4));
             float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
             if (use_z) {
               o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
@@ -730,7 +743,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
             const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
             const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
             *reinterpret_cast<uint2*>(C + (m0 + ra + row) * g.ld + n0 + rb + 4 * c4) = make_uint2(w0, w1);
-            if (ra != rb) *reinterpret_cast<float4*>(wl + row * LDB + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
+            if (ra != rb) *reinterpret_cast<float4*>(wl + row * LDB + slab_col<3>(row, 4 * c4)) = make_float4(o[0], o[1], o[2], o[3]);
           }
           if (ra != rb) {
 #pragma unroll
@@ -738,7 +751,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
               const int q = lane + 64 * p, mr = q >> 3, c4 = q & 7;
               float o[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDB + mr];
+              for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDB + slab_col<3>(4 * c4 + t, mr)];
               const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
               const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
               *reinterpret_cast<uint2*>(C + (n0 + rb + mr) * g.ld + m0 + ra + 4 * c4) = make_uint2(w0, w1);
@@ -857,7 +870,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // per-XCD L2), so no L2 write-back or invalidation is needed; the
   // vmcnt(0) wait puts every partial store before the counter increment, and
   // the loads are issued only after the increment has returned ----
-  if (SPLITS && sidx >= 0) {
+  if constexpr (SPLITS) if (sidx >= 0) {
+    __shared__ int split_arrival;   // only this instantiation holds it: the others may use all 160 KB
     constexpr int PER_WAVE = FM * FN * 4 * kWave;   // 16-byte pieces per wave
     typedef unsigned long long u64_t;
     u64_t* mine = reinterpret_cast<u64_t*>(g.partials + (2 * sidx + half) * int64_t(BM * BN)) +
@@ -926,7 +940,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        wl[(8 * (v >> 2) + 4 * fgrp + (v & 3)) * LDW + j * 32 + frow] = acc[i][j][v];
+        {
+          const int row = 8 * (v >> 2) + 4 * fgrp + (v & 3);
+          wl[row * LDW + slab_col<7>(row, j * 32 + frow)] = acc[i][j][v];
+        }
     const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
     uint2 zr[NP];
     if (use_z) {
@@ -939,7 +956,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
-      float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + 4 * c4);
+      float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + slab_col<7>(row, 4 * c4));
       float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
       if (use_z) {
         o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
@@ -964,7 +981,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
         *reinterpret_cast<uint2*>(C + grow * g.ld + gcol) = make_uint2(w0, w1);
       }
-      if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + 4 * c4) = make_float4(o[0], o[1], o[2], o[3]);
+      if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + slab_col<7>(row, 4 * c4)) = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (second_pass) {
       // mirrored / transposed: row c0 + mr receives slab rows 4*c4 .. 4*c4+3
@@ -973,7 +990,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         const int q = lane + 64 * p, mr = q / 8, c4 = q % 8;
         float o[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDW + mr];
+        for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDW + slab_col<7>(4 * c4 + t, mr)];
         const int64_t orow = c0 + mr, ocol = r0 + 4 * c4;
         if (EPI == EPI_FINAL) {
           if (g.col0 + orow < g.l_valid) {
