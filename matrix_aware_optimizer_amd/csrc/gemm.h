@@ -617,15 +617,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
-  auto issue_p = [&](int64_t kt) {
-    const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
+  // stages live at byte offsets 0, STAGE_BYTES, ..., (S-1) STAGE_BYTES of the
+  // ring; the loops advance offsets incrementally (no modulo by S per k-step)
+  auto ring_next = [](uint32_t o) {
+    o += C_::STAGE_BYTES;
+    return o == uint32_t(S * C_::STAGE_BYTES) ? 0u : o;
+  };
+  auto issue_p = [&](int64_t kt, uint32_t off) {
+    const uint32_t st = lds_base + off;
     const bf16_t* pk = Pt + kt * BK;
 #pragma unroll
     for (int q = 0; q < C_::P_DMA; ++q) dma16(pk + p_off[q], st + (wave * C_::P_DMA + q) * 1024);
   };
-  auto issue_stage = [&](int64_t kt) {
-    issue_p(kt);
-    const uint32_t st = lds_base + uint32_t(kt % S) * C_::STAGE_BYTES;
+  auto issue_stage = [&](int64_t kt, uint32_t off) {
+    issue_p(kt, off);
+    const uint32_t st = lds_base + off;
     const bf16_t* qk = NN ? Qt + kt * BK * g.ld : Qt + kt * BK;
 #pragma unroll
     for (int q = 0; q < C_::Q_DMA; ++q)
@@ -677,31 +683,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         constexpr int D = C_::P_DMA;
 #pragma unroll
         for (int s = 0; s < S - 1; ++s)
-          if (s < nk) issue_p(s);
+          if (s < nk) issue_p(s, uint32_t(s) * C_::STAGE_BYTES);
         if (nk >= S - 1) wait_vm_barrier<D * (S - 2)>();
         else wait_vm_barrier<0>();
         read(lds, 0, f[0]);
         int64_t it = 0;
+        uint32_t o_cur = 0, o_iss = uint32_t(S - 1) * C_::STAGE_BYTES;
         for (; it < nk - (S - 1); ++it) {
+          const uint32_t o_nxt = ring_next(o_cur);
           lds_reads_done();
-          read(lds + (it % S) * C_::STAGE_BYTES, 1, f[1]);
+          read(lds + o_cur, 1, f[1]);
           mma(f[0]);
           interleave();
           wait_vm_barrier<D * (S - 3)>();
-          issue_p(it + S - 1);
+          issue_p(it + S - 1, o_iss);
           lds_reads_done();
-          read(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, f[0]);
+          read(lds + o_nxt, 0, f[0]);
           mma(f[1]);
           interleave();
+          o_cur = o_nxt;
+          o_iss = ring_next(o_iss);
         }
         for (; it < nk; ++it) {
-          read(lds + (it % S) * C_::STAGE_BYTES, 1, f[1]);
+          const uint32_t o_nxt = ring_next(o_cur);
+          read(lds + o_cur, 1, f[1]);
           mma(f[0]);
           if (it + 1 < nk) {
             wait_vm_barrier<0>();
-            read(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, f[0]);
+            read(lds + o_nxt, 0, f[0]);
           }
           mma(f[1]);
+          o_cur = o_nxt;
         }
         // epilogue: each 32 x 32 block through a per-wave LDS slab; off-diagonal
         // blocks are also stored mirrored
@@ -832,34 +844,40 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // prologue: stages 0 .. S-2 in flight, stage 0 resident
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue_stage(s);
+    if (s < nk) issue_stage(s, uint32_t(s) * C_::STAGE_BYTES);
   if (nk >= S - 1) wait_vm_barrier<C_::D * (S - 2)>();
   else wait_vm_barrier<0>();
   read_frags(lds, 0, fa[0], fb[0]);
   int64_t it = 0;
+  uint32_t o_cur = 0, o_iss = uint32_t(S - 1) * C_::STAGE_BYTES;   // stages it and it + S - 1
   // steady state (branch-free, so the compiler's LDS wait counts stay exact):
   // stages it+1 .. it+S-2 are in flight on entry, stage it+S-1 is issued here
   for (; it < nk - (S - 1); ++it) {
+    const uint32_t o_nxt = ring_next(o_cur);
     lds_reads_done();
-    read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
+    read_frags(lds + o_cur, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
     interleave();
     wait_vm_barrier<C_::D * (S - 3)>();
-    issue_stage(it + S - 1);
+    issue_stage(it + S - 1, o_iss);
     lds_reads_done();
-    read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
+    read_frags(lds + o_nxt, 0, fa[0], fb[0]);
     mma_all(fa[1], fb[1]);
     interleave();
+    o_cur = o_nxt;
+    o_iss = ring_next(o_iss);
   }
   // drain: nothing left to issue
   for (; it < nk; ++it) {
-    read_frags(lds + (it % S) * C_::STAGE_BYTES, 1, fa[1], fb[1]);
+    const uint32_t o_nxt = ring_next(o_cur);
+    read_frags(lds + o_cur, 1, fa[1], fb[1]);
     mma_all(fa[0], fb[0]);
     if (it + 1 < nk) {
       wait_vm_barrier<0>();
-      read_frags(lds + ((it + 1) % S) * C_::STAGE_BYTES, 0, fa[0], fb[0]);
+      read_frags(lds + o_nxt, 0, fa[0], fb[0]);
     }
     mma_all(fa[1], fb[1]);
+    o_cur = o_nxt;
   }
 
   // ---- K halves: both halves store their fp32 partial tile, then count in;
