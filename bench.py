@@ -2,7 +2,8 @@
 """Throughput of one SignMuon worker step on one MI355X.
 
 A step is one worker's momentum EMA with per-matrix norms, Newton-Schulz
-(5 quintic iterations, bf16 MFMA / fp32 accumulation), sign + 1-bit pack,
+(5 quintic iterations, bf16 MFMA / fp32 accumulation), sign + 1-bit pack
+(written by the last product's epilogue),
 then the majority vote over the M workers' packed buffers resident on the GPU
 and the update W <- W - eta * vote.  Default workload: one 4096 x 14336 bf16
 matrix (Llama-3-8B MLP shape), 1% heavy columns, M = 7 workers.
@@ -80,6 +81,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused-pack", action="store_true",
+                    help="pack the signs with sign_pack after the last product instead of in it")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra measurements after the timed steps "
                          "(profiling runs then trace the step's kernels only)")
@@ -149,6 +152,7 @@ def main():
     # split scratch of the stage calls (zeroed once; every call leaves its counters at zero)
     stage_ws = mao.new_stage_workspace(s, l, 1, prec, dev)
     fold = prec == "bf16" and wl.m_dtype == "bf16"      # wide and pad-free: checked above
+    fuse_signs = prec == "bf16" and wl.ns_steps > 0 and not args.unfused_pack
     bits = torch.zeros((wl.workers, nwords), dtype=torch.int64, device=dev)
     vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
 
@@ -172,12 +176,19 @@ def main():
             if c != 0.0:
                 mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
                 mark("poly")
-            mao.ns_apply(B if c != 0.0 else A, Xc, X[1 - cur], a, 1.0 if c != 0.0 else b, prec,
-                         sumsq=ss, workspace=stage_ws)
-            mark("apply")
+            Bm, alpha = (B, 1.0) if c != 0.0 else (A, b)
+            if fuse_signs and it + 1 == wl.ns_steps:
+                # the last product packs the signs of its values (nothing else of
+                # the direction is needed by the vote)
+                mao.ns_apply_signs(Bm, Xc, None, bits[k], a, alpha, prec, sumsq=ss, workspace=stage_ws)
+                mark("apply_signs")
+            else:
+                mao.ns_apply(Bm, Xc, X[1 - cur], a, alpha, prec, sumsq=ss, workspace=stage_ws)
+                mark("apply")
             cur = 1 - cur
-        mao.sign_pack(X[cur], bits[k])
-        mark("pack")
+        if not fuse_signs or wl.ns_steps == 0:
+            mao.sign_pack(X[cur], bits[k])
+            mark("pack")
 
     def tail(ev=None):
         mao.majority_vote(bits, vote)
@@ -225,7 +236,7 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     gram_f, poly_f, apply_f = ns_flops(s, l, c != 0.0)
-    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply") if k in total)
+    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply", "apply_signs") if k in total)
     ns_flop = wl.ns_steps * (gram_f + poly_f + apply_f)
     peak = PEAK_BF16_TFLOPS if prec == "bf16" else PEAK_F32_TFLOPS
     ns_tflops = ns_flop / (ns_ms * 1e-3) / 1e12
@@ -243,7 +254,6 @@ def main():
         "momentum": {"ms": avg["momentum"], "GB/s": gbs(bytes_momentum, "momentum")},
         "gram": {"ms": avg["gram"], "TFLOP/s": gram_f / (avg["gram"] * 1e-3) / 1e12},
         "apply": {"ms": avg["apply"], "TFLOP/s": apply_f / (avg["apply"] * 1e-3) / 1e12},
-        "pack": {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack")},
         "vote": {"ms": avg["vote"], "GB/s": gbs(bytes_vote, "vote")},
         "update": {"ms": avg["update"], "GB/s": gbs(bytes_update, "update")},
     }
@@ -252,6 +262,25 @@ def main():
                                 "GB/s": gbs(n * (es[wl.m_dtype] + es[prec]), "normalize")}
     if "poly" in avg:
         kernels["poly"] = {"ms": avg["poly"], "TFLOP/s": poly_f / (avg["poly"] * 1e-3) / 1e12}
+    if "apply_signs" in avg:
+        kernels["apply_signs"] = {"ms": avg["apply_signs"],
+                                  "TFLOP/s": apply_f / (avg["apply_signs"] * 1e-3) / 1e12}
+    if "pack" in avg:
+        kernels["pack"] = {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack")}
+    else:
+        # fused into the last product in the step; the standalone kernel (the
+        # path of tall or fp32 problems) is timed here on the same buffers
+        for _ in range(3):
+            mao.sign_pack(X[0], bits[0])
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(20):
+            mao.sign_pack(X[0], bits[0])
+        p1.record()
+        torch.cuda.synchronize()
+        avg["pack"] = p0.elapsed_time(p1) / 20
+        launches["pack"] = 0.0
+        kernels["pack"] = {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack"), "fused_in_step": True}
     for k in kernels:
         kernels[k]["launches_per_step"] = launches[k]
         if "GB/s" in kernels[k]:

@@ -114,7 +114,14 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
  *              held in bf16 between products.  MUON_F32: fp32 throughout.
  *   problem    M (device, rows x cols of m_dtype), U (device, rows x cols of
  *              u_dtype, may alias nothing else), sumsq (device float holding
- *              sum(M^2), e.g. from muon_momentum, or NULL to compute it).
+ *              sum(M^2), e.g. from muon_momentum, or NULL to compute it),
+ *              bits (device, 8-byte aligned, or NULL): the packed signs of U
+ *              in sign_pack's layout (ceil(rows * cols / 64) words), i.e.
+ *              a6 of [SM] "Fluxo" step 2 on this problem's U.  With bf16
+ *              precision, steps > 0, rows <= cols and cols % 64 == 0 the
+ *              signs come from the last product's epilogue and U may be NULL
+ *              (then only the signs are written); otherwise U is required and
+ *              the signs are packed from it after the iteration.
  *   Problems of equal shape and dtypes whose pointers are evenly spaced are
  *   batched into one launch per stage.  steps == 0 gives U = X0.
  *   workspace  device, at least ns_workspace_bytes(probs, count, precision)
@@ -140,6 +147,7 @@ typedef struct muon_ns_problem {
   int64_t cols;
   int32_t m_dtype;
   int32_t u_dtype;
+  uint64_t* bits;
 } muon_ns_problem;
 
 size_t ns_workspace_bytes(const muon_ns_problem* probs, int count, int precision);
@@ -191,6 +199,17 @@ int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c,
 int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch,
              float a, float alpha, int precision, const float* sumsq, void* workspace,
              size_t ws_bytes, void* stream);
+
+/* ns_apply_signs (a5 + a6): ns_apply with MUON_BF16 precision (else
+ *   MUON_EDTYPE) that also writes the packed signs of Xout, as sign_pack
+ *   would pack the stored bf16 values: bits (device, 8-byte aligned) is
+ *   [batch][s * l / 64] words, entry b holding Xout[b] (s x l row-major) with
+ *   bit i of the flat index in word i >> 6, bit i & 63.  Xout may be NULL:
+ *   then only the signs are written (the last iteration of SignMuon needs
+ *   nothing else).  Other arguments, errors and the workspace as ns_apply. */
+int ns_apply_signs(const void* B, const void* X, void* Xout, uint64_t* bits, int64_t s, int64_t l,
+                   int64_t batch, float a, float alpha, int precision, const float* sumsq,
+                   void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6 -- entrywise sign and 1-bit packing.

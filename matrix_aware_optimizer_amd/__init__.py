@@ -12,6 +12,6 @@ from ._abi import (  # noqa: F401
 )
 from ._abi import MUON_INT8_MAX_VOTERS, sign_int8, sum_int8, threshold_pack  # noqa: F401
 from ._abi import apply_update_dense, unpack_signs  # noqa: F401
-from ._abi import new_stage_workspace, ns_stage_workspace_bytes  # noqa: F401
+from ._abi import new_stage_workspace, ns_apply_signs, ns_stage_workspace_bytes  # noqa: F401
 from ._abi import MUON_DION_MAX_RANK, dion_step, dion_workspace_bytes  # noqa: F401
 from .signmuon import SignMuonStep  # noqa: F401

@@ -38,7 +38,7 @@ class NSProblem(ctypes.Structure):
 
     _fields_ = [("M", _c_void_p), ("U", _c_void_p), ("sumsq", _c_void_p),
                 ("rows", _c_i64), ("cols", _c_i64), ("m_dtype", ctypes.c_int32),
-                ("u_dtype", ctypes.c_int32)]
+                ("u_dtype", ctypes.c_int32), ("bits", _c_void_p)]
 
 
 # (name, restype, argtypes) of every exported symbol declared in include/muon.h
@@ -60,6 +60,8 @@ SIGNATURES = {
                          _c_void_p, _c_size, _c_void_p]),
     "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_float,
                           _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
+    "ns_apply_signs": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64,
+                                _c_float, _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
     "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "majority_vote": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
@@ -176,20 +178,27 @@ def muon_momentum(M: torch.Tensor, G: torch.Tensor, beta: float, alpha: float,
 # a2-a5
 # ---------------------------------------------------------------------------
 
-ProblemLike = Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]
+# (M, U, sumsq) or (M, U, sumsq, bits); U may be None when bits are given and
+# the signs are fused (bf16, wide, cols % 64 == 0, steps > 0)
+ProblemLike = Tuple[torch.Tensor, ...]
 
 
 def _problems(problems: Sequence[ProblemLike]):
     arr = (NSProblem * len(problems))()
-    for i, (M, U, sumsq) in enumerate(problems):
-        if M.dim() != 2 or U.shape != M.shape:
+    for i, prob in enumerate(problems):
+        M, U, sumsq = prob[:3]
+        bits = prob[3] if len(prob) > 3 else None
+        if M.dim() != 2 or (U is not None and U.shape != M.shape):
             raise ValueError("each problem needs a 2-D M and a U of the same shape")
+        if bits is not None and (bits.element_size() != 8 or bits.numel() < packed_words(M.numel())):
+            raise ValueError("bits must hold ceil(rows * cols / 64) 64-bit words")
         arr[i].M = _dev(M, "M")
         arr[i].U = _dev(U, "U")
         arr[i].sumsq = _dev(sumsq, "sumsq") if sumsq is not None else None
+        arr[i].bits = _dev(bits, "bits")
         arr[i].rows, arr[i].cols = M.shape
         arr[i].m_dtype = dtype_code(M)
-        arr[i].u_dtype = dtype_code(U)
+        arr[i].u_dtype = dtype_code(U) if U is not None else dtype_code(M)
     return arr
 
 
@@ -280,6 +289,21 @@ def ns_apply(B: torch.Tensor, X: torch.Tensor, Xout: torch.Tensor, a: float, alp
     _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), s, l, batch,
                                       float(a), float(alpha), precision_code(precision),
                                       _dev(sumsq, "sumsq"), ws, nbytes, _stream(stream)))
+
+
+def ns_apply_signs(B: torch.Tensor, X: torch.Tensor, Xout: Optional[torch.Tensor], bits: torch.Tensor,
+                   a: float, alpha: float = 1.0, precision="bf16", stream=None,
+                   sumsq: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   split: bool = True) -> None:
+    """ns_apply that also packs the signs of Xout into ``bits`` ([batch][s*l/64] words);
+    with Xout None only the signs are written."""
+    batch, s, l = _batch3(X)
+    if bits.element_size() != 8 or bits.numel() < batch * (s * l // 64):
+        raise ValueError("bits must hold batch * s * l / 64 64-bit words")
+    ws, nbytes = _stage_ws(workspace, split, s, l, batch, precision, X)
+    _check("ns_apply_signs", lib().ns_apply_signs(
+        _dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), _dev(bits, "bits"), s, l, batch, float(a),
+        float(alpha), precision_code(precision), _dev(sumsq, "sumsq"), ws, nbytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -110,6 +111,14 @@ struct GemmArgs {
   // column col0, and col0 places the columns of U (EPI_FINAL).
   int64_t ld;
   int64_t col0;
+  // Optional packed signs of the stored output (non-symmetric products): bit
+  // (r, c) of a bits_rows x bits_cols row-major matrix (bits_cols a multiple
+  // of 64) is bit (r * bits_cols + c) % 64 of word (r * bits_cols + c) / 64,
+  // batch entries stride_bits words apart.  For EPI_FINAL the matrix is U
+  // (not transposed), else the launch's full output.  C (EPI_AXPBY) or U
+  // (EPI_FINAL) may then be null, and only the signs are written.
+  uint64_t* bits;
+  int64_t bits_rows, bits_cols, stride_bits;
   int split_mode;
   float* partials;       // 2 x (split tiles) x BM x BN fp32
   int* counters;         // one per split tile: zero on entry, left zero
@@ -498,6 +507,28 @@ template <> struct DiagPattern<2> {   // rows {64, 0, 32}: blocks (2,0) (2,1) (2
   static constexpr int NF = 3, NB = 5;
   static constexpr int IA[NB] = {0, 0, 0, 2, 2}, IB[NB] = {1, 2, 0, 1, 2};
 };
+
+// Sign bit of a stored value: 1 iff !(u < 0) on its encoding (+0, -0 and NaN
+// give 1), the rule of the 1-bit packing.
+__device__ __forceinline__ uint32_t nonneg_bf16(bf16_t h) { return !(h > 0x8000u && h <= 0xff80u); }
+__device__ __forceinline__ uint32_t nonneg_f32(uint32_t u) { return !(u > 0x80000000u && u <= 0xff800000u); }
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of lane i - SH of the same 16-lane DPP row, 0 where that lane lies
+// before the row's first lane.
+template <int SH>
+__device__ __forceinline__ uint32_t row_shr_or(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x110 | SH, 0xf, 0xf, true));
+}
 
 // Column of slab element (row, col) in the epilogue's LDS slab: the column is
 // XOR-swizzled by the row's group of four (bits 3 and up), which keeps 4-column
@@ -952,8 +983,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   constexpr int NP2 = WN * 8 / 64;            // transposed chunks per lane and slab
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free
   float* wl = reinterpret_cast<float*>(lds) + wave * 32 * LDW;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  // one 32-row slab per accumulator row block; expanded at compile time (the
+  // unroller gives up on bodies this large, and the accumulators must keep
+  // constant indices to stay in registers)
+  auto slab = [&](auto I_) __attribute__((always_inline)) {
+    constexpr int i = decltype(I_)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -983,8 +1017,30 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         o[3] = fmaf(beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
       }
       const int64_t grow = r0 + row, gcol = c0 + 4 * c4;
+      if constexpr (!SYRK && WN % 64 == 0) if (g.bits != nullptr) {
+        // sign bits of the stored values (bit 1 iff !(u < 0) on the stored
+        // encoding, as sign_pack tests it).  A 16-lane DPP row holds 64
+        // consecutive columns of one row, 4 per lane: each lane places its
+        // nibble in the word's low or high half, an OR-scan over the row
+        // (shifts 1, 2, 4, 8) gathers the word in the row's last lane.
+        const bool f32_out = EPI == EPI_FINAL && g.u_dtype == MUON_F32;
+        uint32_t nib = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          nib |= (f32_out ? nonneg_f32(__float_as_uint(o[t])) : nonneg_bf16(f32_to_bf16(o[t]))) << t;
+        const int rl = lane & 15;
+        uint32_t lo = rl < 8 ? nib << (4 * rl) : 0u;
+        uint32_t hi = rl < 8 ? 0u : nib << (4 * (rl - 8));
+        lo |= row_shr_or<1>(lo); hi |= row_shr_or<1>(hi);
+        lo |= row_shr_or<2>(lo); hi |= row_shr_or<2>(hi);
+        lo |= row_shr_or<4>(lo); hi |= row_shr_or<4>(hi);
+        lo |= row_shr_or<8>(lo); hi |= row_shr_or<8>(hi);
+        if (rl == 15 && grow < g.bits_rows && g.col0 + gcol < g.bits_cols)
+          *reinterpret_cast<uint2*>(g.bits + batch * g.stride_bits + (grow * g.bits_cols + g.col0 + gcol) / 64) =
+              make_uint2(lo, hi);
+      }
       if (EPI == EPI_FINAL) {
-        if (!g.transpose_out && grow < g.s_valid) {
+        if (g.U != nullptr && !g.transpose_out && grow < g.s_valid) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             if (g.col0 + gcol + t < g.l_valid) {
@@ -994,7 +1050,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
             }
           }
         }
-      } else {
+      } else if (SYRK || g.C != nullptr) {
         const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
         const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
         *reinterpret_cast<uint2*>(C + grow * g.ld + gcol) = make_uint2(w0, w1);
@@ -1011,7 +1067,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         for (int t = 0; t < 4; ++t) o[t] = wl[(4 * c4 + t) * LDW + slab_col<7>(4 * c4 + t, mr)];
         const int64_t orow = c0 + mr, ocol = r0 + 4 * c4;
         if (EPI == EPI_FINAL) {
-          if (g.col0 + orow < g.l_valid) {
+          if (g.U != nullptr && g.col0 + orow < g.l_valid) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               if (ocol + t < g.s_valid) {
@@ -1028,7 +1084,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
         }
       }
     }
-  }
+  };
+  static_for<FM>(slab);
 }
 
 // Number of workgroups of one batch entry.
@@ -1046,6 +1103,7 @@ int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
   using C_ = Tile<T, BM, BN, WM, WN>;
   const int64_t blocks = tiles_of<BM, BN, SYRK>(g);
   if (blocks == 0 || batch == 0) return MUON_OK;
+  if (g.bits != nullptr) return MUON_EINVAL;   // sign bits: DMA kernel only
   auto kern = gemm_kernel<T, BM, BN, WM, WN, SYRK, NN, EPI>;
   static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
   if (!configured) {
@@ -1132,6 +1190,8 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   const int64_t tpb = tiles_of<BM, BN, SYRK>(g);
   if (tpb == 0 || batch == 0) return MUON_OK;
+  // sign bits come from 16-lane groups that each hold 64 columns of one row
+  if (g.bits != nullptr && (SYRK || WN % 64 != 0 || g.bits_cols % 64 != 0)) return MUON_EINVAL;
   int64_t grid = tpb;
   if (g.ld == 0) g.ld = g.N;
   g.split_mode = SPLIT_NONE;

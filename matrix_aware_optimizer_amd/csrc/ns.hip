@@ -159,7 +159,7 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   g2.col0 = n1;
   g2.Q = static_cast<const bf16_t*>(g.Q) + n1;
   if (g.Z) g2.Z = static_cast<const bf16_t*>(g.Z) + n1;
-  g2.C = static_cast<bf16_t*>(g.C) + n1;
+  if (g.C) g2.C = static_cast<bf16_t*>(g.C) + n1;
   return gemm::launch_dma<128, 256, 64, 64, 4, false, true, EPI>(g2, batch, st, none);
 }
 
@@ -228,9 +228,15 @@ int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, h
 template <typename T>
 int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
             float alpha, hipStream_t st, const gemm::Scratch& sc, const GemmArgs* final_out,
-            const Fold& fold = Fold{}) {
+            const Fold& fold = Fold{}, const GemmArgs* signs = nullptr) {
   GemmArgs g{};
   if (final_out) g = *final_out;
+  if (signs) {
+    g.bits = signs->bits;
+    g.bits_rows = signs->bits_rows;
+    g.bits_cols = signs->bits_cols;
+    g.stride_bits = signs->stride_bits;
+  }
   g.P = B; g.Q = X; g.Z = X; g.C = Xout;
   g.M = s; g.N = l; g.K = s;
   g.strideP = s * s; g.strideQ = g.strideZ = fold.strideX ? fold.strideX : s * l; g.strideC = s * l;
@@ -292,19 +298,22 @@ int emit_t(const void* X, int64_t sp, int64_t lp, int64_t rows, int64_t cols, vo
 struct Run {
   int count;
   const void* M;
-  void* U;
+  void* U;                 // null: only the signs are written
   const float* sumsq;
+  uint64_t* bits;          // packed signs of U, or null
   int64_t rows, cols, sp, lp;
   int m_dtype, u_dtype;
   bool has_sumsq;
   int64_t strideM, strideU, stride_sumsq;  // elements
+  int64_t stride_bits;                     // words
 };
 
 int64_t pad_to(int64_t x) { return (x + MUON_NS_PAD - 1) / MUON_NS_PAD * MUON_NS_PAD; }
 
 bool same_kind(const muon_ns_problem& a, const muon_ns_problem& b) {
   return a.rows == b.rows && a.cols == b.cols && a.m_dtype == b.m_dtype && a.u_dtype == b.u_dtype &&
-         (a.sumsq != nullptr) == (b.sumsq != nullptr);
+         (a.sumsq != nullptr) == (b.sumsq != nullptr) && (a.U != nullptr) == (b.U != nullptr) &&
+         (a.bits != nullptr) == (b.bits != nullptr);
 }
 
 bool kind_less(const muon_ns_problem& a, const muon_ns_problem& b) {
@@ -313,6 +322,8 @@ bool kind_less(const muon_ns_problem& a, const muon_ns_problem& b) {
   if (a.m_dtype != b.m_dtype) return a.m_dtype < b.m_dtype;
   if (a.u_dtype != b.u_dtype) return a.u_dtype < b.u_dtype;
   if ((a.sumsq != nullptr) != (b.sumsq != nullptr)) return a.sumsq == nullptr;
+  if ((a.U != nullptr) != (b.U != nullptr)) return a.U == nullptr;
+  if ((a.bits != nullptr) != (b.bits != nullptr)) return a.bits == nullptr;
   return reinterpret_cast<uintptr_t>(a.M) < reinterpret_cast<uintptr_t>(b.M);
 }
 
@@ -320,6 +331,13 @@ int64_t diff_elems(const void* a, const void* b, size_t es) {
   const int64_t d = reinterpret_cast<const char*>(b) - reinterpret_cast<const char*>(a);
   if (d <= 0 || d % static_cast<int64_t>(es) != 0) return -1;
   return d / static_cast<int64_t>(es);
+}
+
+// stride of an optional pointer: both null gives 0 (no stride needed)
+int64_t diff_opt(const void* a, const void* b, size_t es) {
+  if (!a && !b) return 0;
+  if (!a || !b) return -1;
+  return diff_elems(a, b, es);
 }
 
 std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
@@ -330,7 +348,7 @@ std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
   while (i < count) {
     Run r{};
     r.count = 1;
-    r.M = p[i].M; r.U = p[i].U; r.sumsq = p[i].sumsq;
+    r.M = p[i].M; r.U = p[i].U; r.sumsq = p[i].sumsq; r.bits = p[i].bits;
     r.rows = p[i].rows; r.cols = p[i].cols;
     r.sp = pad_to(std::min(r.rows, r.cols));
     r.lp = pad_to(std::max(r.rows, r.cols));
@@ -338,19 +356,23 @@ std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
     r.has_sumsq = p[i].sumsq != nullptr;
     r.strideM = r.strideU = r.rows * r.cols;
     r.stride_sumsq = 1;
+    r.stride_bits = (r.rows * r.cols + 63) / 64;
     if (i + 1 < count && same_kind(p[i], p[i + 1])) {
       const int64_t sm = diff_elems(p[i].M, p[i + 1].M, dtype_size(r.m_dtype));
-      const int64_t su = diff_elems(p[i].U, p[i + 1].U, dtype_size(r.u_dtype));
+      const int64_t su = diff_opt(p[i].U, p[i + 1].U, dtype_size(r.u_dtype));
       const int64_t ss = r.has_sumsq ? diff_elems(p[i].sumsq, p[i + 1].sumsq, sizeof(float)) : 1;
-      if (sm > 0 && su > 0 && ss > 0) {
+      const int64_t sb = diff_opt(p[i].bits, p[i + 1].bits, sizeof(uint64_t));
+      if (sm > 0 && su >= 0 && ss > 0 && sb >= 0) {
         int j = i + 1;
         while (j < count && same_kind(p[j - 1], p[j]) &&
                diff_elems(p[j - 1].M, p[j].M, dtype_size(r.m_dtype)) == sm &&
-               diff_elems(p[j - 1].U, p[j].U, dtype_size(r.u_dtype)) == su &&
-               (!r.has_sumsq || diff_elems(p[j - 1].sumsq, p[j].sumsq, sizeof(float)) == ss))
+               diff_opt(p[j - 1].U, p[j].U, dtype_size(r.u_dtype)) == su &&
+               (!r.has_sumsq || diff_elems(p[j - 1].sumsq, p[j].sumsq, sizeof(float)) == ss) &&
+               diff_opt(p[j - 1].bits, p[j].bits, sizeof(uint64_t)) == sb)
           ++j;
         r.count = j - i;
         r.strideM = sm; r.strideU = su; r.stride_sumsq = ss;
+        if (sb > 0) r.stride_bits = sb;
       }
     }
     runs.push_back(r);
@@ -392,8 +414,14 @@ bool folds_normalisation(const Run& r, int precision) {
          r.rows % MUON_NS_PAD == 0 && r.cols % MUON_NS_PAD == 0 && r.strideM % 8 == 0;
 }
 
+// signs from the last product's epilogue: bf16 products, U not transposed,
+// whole 64-bit words per row of U
+bool fuses_signs(int64_t rows, int64_t cols, int precision, int steps) {
+  return precision == MUON_BF16 && steps > 0 && rows <= cols && cols % 64 == 0;
+}
+
 bool valid_problem(const muon_ns_problem& p) {
-  return p.rows > 0 && p.cols > 0 && p.M && p.U;
+  return p.rows > 0 && p.cols > 0 && p.M && (p.U || p.bits);
 }
 
 // The workspace of ns_orthogonalize starts with the split scratch shared by
@@ -408,6 +436,19 @@ SplitRegion split_region(const std::vector<Run>& runs, int precision) {
   if (precision != MUON_BF16) return R;
   for (const Run& r : runs) R.bytes = std::max(R.bytes, round_up(split_scratch_bound(r.sp, r.lp, r.count), 256));
   return R;
+}
+
+// packed signs of every U of a run whose signs were not fused into its last
+// product (one sign_pack per problem: U entries need not be contiguous)
+int pack_run_signs(const Run& r, hipStream_t st) {
+  if (!r.bits) return MUON_OK;
+  const size_t es = dtype_size(r.u_dtype);
+  for (int k = 0; k < r.count; ++k) {
+    const int status = sign_pack(static_cast<const char*>(r.U) + k * r.strideU * es, r.u_dtype,
+                                 r.rows * r.cols, r.bits + k * r.stride_bits, st);
+    if (status != MUON_OK) return status;
+  }
+  return MUON_OK;
 }
 
 size_t runs_bytes(const std::vector<Run>& runs, int precision) {
@@ -440,7 +481,9 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     const muon_ns_problem& p = probs[i];
     if (!valid_problem(p)) return MUON_EINVAL;
     if (!valid_dtype(p.m_dtype) || !valid_dtype(p.u_dtype)) return MUON_EDTYPE;
-    if (!aligned16(p.M) || !aligned16(p.U)) return MUON_EALIGN;
+    if (!p.U && !fuses_signs(p.rows, p.cols, precision, steps)) return MUON_EINVAL;
+    if (!aligned16(p.M) || (p.U && !aligned16(p.U))) return MUON_EALIGN;
+    if (reinterpret_cast<uintptr_t>(p.bits) % 8 != 0) return MUON_EALIGN;
   }
   const std::vector<Run> runs = make_runs(probs, count);
   const SplitRegion split = split_region(runs, precision);
@@ -485,6 +528,7 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
       status = precision == MUON_BF16
                    ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
                    : emit_t<float>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st);
+      if (status == MUON_OK) status = pack_run_signs(r, st);
       if (status != MUON_OK) return status;
       continue;
     }
@@ -495,6 +539,13 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     fin.l_valid = std::max(r.rows, r.cols);
     fin.u_dtype = r.u_dtype;
     fin.transpose_out = r.rows > r.cols;
+    const bool fused_signs = r.bits && fuses_signs(r.rows, r.cols, precision, steps);
+    if (fused_signs) {
+      fin.bits = r.bits;
+      fin.bits_rows = r.rows;
+      fin.bits_cols = r.cols;
+      fin.stride_bits = r.stride_bits;
+    }
     for (int it = 0; it < steps; ++it) {
       const bool first_folded = fold_norm && it == 0;
       const void* Xc = first_folded ? r.M : X[it & 1];
@@ -515,6 +566,10 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
           status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
                                   st, sc, last ? &fin : nullptr);
       }
+      if (status != MUON_OK) return status;
+    }
+    if (!fused_signs) {
+      status = pack_run_signs(r, st);
       if (status != MUON_OK) return status;
     }
   }
@@ -602,6 +657,27 @@ int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int
   return precision == MUON_BF16
              ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr, Fold{sumsq, 1, 0})
              : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr);
+}
+
+int ns_apply_signs(const void* B, const void* X, void* Xout, uint64_t* bits, int64_t s, int64_t l,
+                   int64_t batch, float a, float alpha, int precision, const float* sumsq,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
+  if (precision != MUON_BF16) return MUON_EDTYPE;
+  if (batch == 0) return MUON_OK;
+  if (!B || !X || !bits) return MUON_EINVAL;
+  if (!aligned16(B) || !aligned16(X) || (Xout && !aligned16(Xout))) return MUON_EALIGN;
+  if (reinterpret_cast<uintptr_t>(bits) % 8 != 0) return MUON_EALIGN;
+  gemm::Scratch sc;
+  const int status = stage_scratch(workspace, ws_bytes, s, l, batch, precision, sc);
+  if (status != MUON_OK) return status;
+  GemmArgs signs{};
+  signs.bits = bits;
+  signs.bits_rows = s;
+  signs.bits_cols = l;
+  signs.stride_bits = s * l / 64;
+  return apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, static_cast<hipStream_t>(stream), sc, nullptr,
+                         Fold{sumsq, 1, 0}, &signs);
 }
 
 }  // extern "C"

@@ -39,6 +39,9 @@ class SignMuonStep:
             offs.append(offs[-1] + n)
         self.offsets_host = offs
         self.numel = offs[-1]
+        # every matrix's signs start on a word boundary: ns_orthogonalize can
+        # write them per matrix (from the last product's epilogue where it can)
+        self.signs_per_matrix = all(o % 64 == 0 for o in offs[:-1])
         self.nwords = _abi.packed_words(self.numel)
         self.m_dtype = m_dtype
         self.precision = precision
@@ -59,11 +62,14 @@ class SignMuonStep:
         self.ns_workspace = torch.empty(max(ns_bytes, 1), dtype=torch.uint8, device=self.device)
         self.mom_workspace = torch.empty(max(mom_bytes, 1), dtype=torch.uint8, device=self.device)
 
-    def _problems(self, M: torch.Tensor):
+    def _problems(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None):
         probs = []
         for j, (r, c) in enumerate(self.shapes):
             lo, hi = self.offsets_host[j], self.offsets_host[j + 1]
-            probs.append((M[lo:hi].view(r, c), self.U[lo:hi].view(r, c), self.sumsq[j:j + 1]))
+            prob = (M[lo:hi].view(r, c), self.U[lo:hi].view(r, c), self.sumsq[j:j + 1])
+            if bits_row is not None:
+                prob += (bits_row[lo // 64:(hi + 63) // 64],)
+            probs.append(prob)
         return probs
 
     def new_bits(self, workers: int = 1) -> torch.Tensor:
@@ -73,9 +79,11 @@ class SignMuonStep:
     def momentum(self, M: torch.Tensor, G: torch.Tensor) -> None:
         _abi.muon_momentum(M, G, self.beta, self.alpha, self.offsets, self.sumsq, self.mom_workspace)
 
-    def orthogonalize(self, M: torch.Tensor) -> None:
+    def orthogonalize(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None) -> None:
+        """Polar directions into ``self.U``; with ``bits_row`` also their packed
+        signs (requires ``signs_per_matrix``)."""
         a, b, c = self.coeffs
-        _abi.ns_orthogonalize(self._problems(M), a, b, c, self.ns_steps, self.precision,
+        _abi.ns_orthogonalize(self._problems(M, bits_row), a, b, c, self.ns_steps, self.precision,
                               self.ns_workspace)
 
     def pack(self, bits_row: torch.Tensor) -> None:
@@ -84,8 +92,11 @@ class SignMuonStep:
     def worker(self, M: torch.Tensor, G: torch.Tensor, bits_row: torch.Tensor) -> None:
         """Steps 1-3 for one worker: momentum, polar direction, packed signs."""
         self.momentum(M, G)
-        self.orthogonalize(M)
-        self.pack(bits_row)
+        if self.signs_per_matrix:
+            self.orthogonalize(M, bits_row)
+        else:
+            self.orthogonalize(M)
+            self.pack(bits_row)
 
     def vote_update(self, W: torch.Tensor, bits: torch.Tensor, vote_out: Optional[torch.Tensor] = None,
                     fused: bool = False, reorthogonalize: bool = False) -> None:

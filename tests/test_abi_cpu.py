@@ -120,9 +120,11 @@ def test_stage_workspace_bytes(L):
 
 def _problems(specs):
     arr = (_abi.NSProblem * len(specs))()
-    for i, (M, U, s, r, c, md, ud) in enumerate(specs):
+    for i, spec in enumerate(specs):
+        M, U, s, r, c, md, ud = spec[:7]
         arr[i].M, arr[i].U, arr[i].sumsq = M, U, s
         arr[i].rows, arr[i].cols, arr[i].m_dtype, arr[i].u_dtype = r, c, md, ud
+        arr[i].bits = spec[7] if len(spec) > 7 else None
     return arr
 
 
@@ -183,6 +185,55 @@ def test_ns_orthogonalize_validation(L):
     bad = _problems([(0x10000, 0x20000, 0x30000, 8, 8, 1, 3)])
     assert f(bad, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EDTYPE
     assert f(arr, 0, 1.0, 1.0, 1.0, 5, 1, None, 0, None) == OK
+
+
+def test_ns_orthogonalize_sign_bits_validation(L):
+    """U may be NULL only where the signs come from the last product's epilogue:
+    bf16 precision, steps > 0, rows <= cols and cols % 64 == 0."""
+    f = L.ns_orthogonalize
+    ok = _problems([(0x10000, None, 0x30000, 512, 1024, 1, 1, 0x40000)])
+    need = L.ns_workspace_bytes(ok, 1, 1)
+    assert need == _ns_bytes(1, 512, 1024)                     # the signs need no workspace
+    assert f(ok, 1, 1.0, 1.0, 1.0, 5, 1, A3, need - 1, None) == EWORKSPACE   # passes validation
+    assert f(ok, 1, 1.0, 1.0, 1.0, 5, 0, A3, need, None) == EINVAL           # f32: not fused, U needed
+    assert f(ok, 1, 1.0, 1.0, 1.0, 0, 1, A3, need, None) == EINVAL           # steps == 0: U needed
+    tall = _problems([(0x10000, None, 0x30000, 1024, 512, 1, 1, 0x40000)])
+    assert f(tall, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    ragged = _problems([(0x10000, None, 0x30000, 512, 1000, 1, 1, 0x40000)])
+    assert f(ragged, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    neither = _problems([(0x10000, None, 0x30000, 512, 1024, 1, 1)])
+    assert L.ns_workspace_bytes(neither, 1, 1) == 0
+    assert f(neither, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    misaligned = _problems([(0x10000, 0x20000, 0x30000, 512, 1024, 1, 1, 0x40004)])
+    assert f(misaligned, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EALIGN
+
+
+def test_ns_grouping_with_sign_bits(L):
+    """Problems with evenly spaced bits (and U, or no U) still form one run;
+    bits that break the spacing split it."""
+    specs = []
+    for j in range(12):
+        off = j * 768 * 3072
+        specs.append((0x100000 + 2 * off, None, 0x80000 + 4 * j, 768, 3072, 1, 1, 0x8000000 + off // 8))
+    assert L.ns_workspace_bytes(_problems(specs), 12, 1) == _ns_bytes(12, 768, 3072)
+    with_u = [(M, 0x40000000 + 2 * j * 768 * 3072, *rest) for j, (M, _, *rest) in enumerate(specs)]
+    assert L.ns_workspace_bytes(_problems(with_u), 12, 1) == _ns_bytes(12, 768, 3072)
+    broken = list(specs)
+    broken[6] = (*broken[6][:7], broken[6][7] + 8)
+    assert L.ns_workspace_bytes(_problems(broken), 12, 1) == _ns_bytes(6, 768, 3072)
+
+
+def test_ns_apply_signs_validation(L):
+    f = L.ns_apply_signs
+    assert f(A1, A2, None, A3, 256, 512, 1, 1.0, 1.0, 0, None, None, 0, None) == EDTYPE   # bf16 only
+    assert f(A1, A2, None, None, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(None, A2, None, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(A1, A2, None, ctypes.c_void_p(0x30004), 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
+    assert f(A1, A2, MISALIGNED, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
+    assert f(A1, A2, None, A3, 250, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(A1, A2, None, A3, 256, 512, 0, 1.0, 1.0, 1, None, None, 0, None) == OK      # empty batch
+    need = L.ns_stage_workspace_bytes(4096, 14336, 1, 1)
+    assert f(A1, A2, None, A3, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
 
 
 def test_binding_rejects_host_tensors():
