@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused-pack", action="store_true",
                     help="pack the signs with sign_pack after the last product instead of in it")
+    ap.add_argument("--unfused-tail", action="store_true",
+                    help="run majority_vote and apply_update as two calls instead of vote_and_update")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra measurements after the timed steps "
                          "(profiling runs then trace the step's kernels only)")
@@ -153,6 +155,7 @@ def main():
     stage_ws = mao.new_stage_workspace(s, l, 1, prec, dev)
     fold = prec == "bf16" and wl.m_dtype == "bf16"      # wide and pad-free: checked above
     fuse_signs = prec == "bf16" and wl.ns_steps > 0 and not args.unfused_pack
+    fuse_tail = not args.unfused_tail
     bits = torch.zeros((wl.workers, nwords), dtype=torch.int64, device=dev)
     vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
 
@@ -191,14 +194,19 @@ def main():
             mark("pack")
 
     def tail(ev=None):
-        mao.majority_vote(bits, vote)
-        if ev is not None:
-            ev.append(("vote", torch.cuda.Event(enable_timing=True)))
-            ev[-1][1].record()
-        mao.apply_update(W, vote, wl.eta)
-        if ev is not None:
-            ev.append(("update", torch.cuda.Event(enable_timing=True)))
-            ev[-1][1].record()
+        def mark(name):
+            if ev is not None:
+                ev.append((name, torch.cuda.Event(enable_timing=True)))
+                ev[-1][1].record()
+        if fuse_tail:
+            # a7 + a8 in one pass: the vote is never written (nothing else reads it)
+            mao.vote_and_update(W, bits, wl.eta)
+            mark("vote_update")
+        else:
+            mao.majority_vote(bits, vote)
+            mark("vote")
+            mao.apply_update(W, vote, wl.eta)
+            mark("update")
 
     # the other workers' packed signs, resident on the GPU (what an all-gather would deliver)
     for k in range(1, wl.workers):
@@ -254,9 +262,33 @@ def main():
         "momentum": {"ms": avg["momentum"], "GB/s": gbs(bytes_momentum, "momentum")},
         "gram": {"ms": avg["gram"], "TFLOP/s": gram_f / (avg["gram"] * 1e-3) / 1e12},
         "apply": {"ms": avg["apply"], "TFLOP/s": apply_f / (avg["apply"] * 1e-3) / 1e12},
-        "vote": {"ms": avg["vote"], "GB/s": gbs(bytes_vote, "vote")},
-        "update": {"ms": avg["update"], "GB/s": gbs(bytes_update, "update")},
     }
+
+    def standalone(fn, reps=20):
+        """Average time of `reps` back-to-back calls (after 3 untimed), for a
+        kernel the step runs fused into another."""
+        for _ in range(3):
+            fn()
+        t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0_.record()
+        for _ in range(reps):
+            fn()
+        t1_.record()
+        torch.cuda.synchronize()
+        return t0_.elapsed_time(t1_) / reps
+
+    bytes_vote_update = 2 * n * es[wl.w_dtype] + wl.workers * nwords * 8
+    if "vote_update" in avg:
+        kernels["vote_update"] = {"ms": avg["vote_update"], "GB/s": gbs(bytes_vote_update, "vote_update")}
+    for key, fn, nb in (("vote", lambda: mao.majority_vote(bits, vote), bytes_vote),
+                        ("update", lambda: mao.apply_update(W, vote, wl.eta), bytes_update)):
+        if key in avg:
+            kernels[key] = {"ms": avg[key], "GB/s": gbs(nb, key)}
+        else:
+            # fused into vote_and_update in the step; timed on its own here
+            avg[key] = standalone(fn)
+            launches[key] = 0.0
+            kernels[key] = {"ms": avg[key], "GB/s": gbs(nb, key), "fused_in_step": True}
     if "normalize" in avg:
         kernels["normalize"] = {"ms": avg["normalize"],
                                 "GB/s": gbs(n * (es[wl.m_dtype] + es[prec]), "normalize")}
@@ -270,15 +302,7 @@ def main():
     else:
         # fused into the last product in the step; the standalone kernel (the
         # path of tall or fp32 problems) is timed here on the same buffers
-        for _ in range(3):
-            mao.sign_pack(X[0], bits[0])
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        p0.record()
-        for _ in range(20):
-            mao.sign_pack(X[0], bits[0])
-        p1.record()
-        torch.cuda.synchronize()
-        avg["pack"] = p0.elapsed_time(p1) / 20
+        avg["pack"] = standalone(lambda: mao.sign_pack(X[0], bits[0]))
         launches["pack"] = 0.0
         kernels["pack"] = {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack"), "fused_in_step": True}
     for k in kernels:
@@ -300,7 +324,7 @@ def main():
                     "per_launch_flops": dom_flops, "avg_launch_ms": avg[dominant]}
     else:
         nb = {"momentum": bytes_momentum, "pack": bytes_pack, "vote": bytes_vote,
-              "update": bytes_update}[dominant]
+              "update": bytes_update, "vote_update": bytes_vote_update}[dominant]
         ach = gbs(nb, dominant)
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
@@ -383,6 +407,8 @@ def cold_elementwise(mao, torch, wl, M, G, W, U, bits, vote, offsets, sumsq, mom
         "pack": (lambda: mao.sign_pack(U, bits[0]), n * es[wl.precision] + nwords * 8),
         "vote": (lambda: mao.majority_vote(bits, vote), (wl.workers + 1) * nwords * 8),
         "update": (lambda: mao.apply_update(W, vote, wl.eta), 2 * n * es[wl.w_dtype] + nwords * 8),
+        "vote_update": (lambda: mao.vote_and_update(W, bits, wl.eta),
+                        2 * n * es[wl.w_dtype] + wl.workers * nwords * 8),
     }
     out = {}
     for name, (fn, nbytes) in calls.items():
