@@ -22,11 +22,14 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 }
 
 // float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+// Round to nearest even; a NaN keeps its sign and top payload bits and is
+// made quiet.  Written as a select, not a branch: in a wave's epilogue a
+// branch per conversion costs an exec-mask save and restore each time.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return static_cast<bf16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 template <typename T> struct Elem;

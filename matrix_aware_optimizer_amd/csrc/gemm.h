@@ -981,6 +981,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   constexpr int CPR = WN / 4;                 // 4-column chunks per slab row
   constexpr int NP = 32 * CPR / 64;           // chunks per lane and slab
   constexpr int NP2 = WN * 8 / 64;            // transposed chunks per lane and slab
+  // The addend of slab i + 1 is loaded while slab i is staged and written
+  // (double-buffered registers), and slab 0's before the barrier below, so
+  // its latency is not paid once per slab.
+  constexpr int RPP = 64 / CPR;               // slab rows per chunk index
+  static_assert(64 % CPR == 0, "a lane keeps its column across chunks");
+  const int rb = lane / CPR, cc = lane % CPR;
+  // EPI_FINAL: 4-entry chunks of U are whole and aligned when its row length is
+  // a multiple of 4 (all chunk columns are multiples of 4)
+  const bool u_vec = EPI == EPI_FINAL && g.l_valid % 4 == 0;
+  uint2 zbuf[2][NP];
+  auto load_z = [&](int i, uint2 (&dst)[NP]) __attribute__((always_inline)) {
+    const bf16_t* zrow = Z + (m0 + wm0 + i * 32 + rb) * g.ld + n0 + wn0 + 4 * cc;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) dst[p] = *reinterpret_cast<const uint2*>(zrow + int64_t(p * RPP) * g.ld);
+  };
+  if (use_z) load_z(0, zbuf[0]);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free
   float* wl = reinterpret_cast<float*>(lds) + wave * 32 * LDW;
   // one 32-row slab per accumulator row block; expanded at compile time (the
@@ -997,65 +1013,86 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
           wl[row * LDW + slab_col<7>(row, j * 32 + frow)] = acc[i][j][v];
         }
     const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
-    uint2 zr[NP];
-    if (use_z) {
+    if constexpr (i + 1 < FM)
+      if (use_z) load_z(i + 1, zbuf[(i + 1) & 1]);
+    const uint2 (&zr)[NP] = zbuf[i & 1];
+    // chunk p of a lane: slab row rb + p * RPP, columns 4 cc .. 4 cc + 3 (the
+    // column does not depend on p, so addresses advance by a uniform stride)
+    const int64_t gcol = c0 + 4 * cc;
+    bf16_t* crow = C + (r0 + rb) * g.ld + gcol;
+    auto pass1 = [&](auto SG_) __attribute__((always_inline)) {
+      constexpr bool SG = decltype(SG_)::value;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
-        zr[p] = *reinterpret_cast<const uint2*>(Z + (r0 + row) * g.ld + c0 + 4 * c4);
-      }
-    }
+        const int row = rb + p * RPP;
+        float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + slab_col<7>(row, 4 * cc));
+        float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
+        if (use_z) {
+          o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
+          o[1] = fmaf(beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
+          o[2] = fmaf(beta, __uint_as_float(zr[p].y << 16), o[2]);
+          o[3] = fmaf(beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
+        }
+        const int64_t grow = r0 + row;
+        if constexpr (SG) {
+          // sign bits of the stored values (bit 1 iff !(u < 0) on the stored
+          // encoding, as sign_pack tests it).  A 16-lane DPP row holds 64
+          // consecutive columns of one row, 4 per lane: each lane places its
+          // nibble in the word's low or high half, an OR-scan over the row
+          // (shifts 1, 2, 4, 8) gathers the word in the row's last lane.
+          const bool f32_out = EPI == EPI_FINAL && g.u_dtype == MUON_F32;
+          uint32_t nib = 0;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int q = lane + 64 * p, row = q / CPR, c4 = q % CPR;
-      float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + slab_col<7>(row, 4 * c4));
-      float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
-      if (use_z) {
-        o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
-        o[1] = fmaf(beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
-        o[2] = fmaf(beta, __uint_as_float(zr[p].y << 16), o[2]);
-        o[3] = fmaf(beta, __uint_as_float(zr[p].y & 0xffff0000u), o[3]);
-      }
-      const int64_t grow = r0 + row, gcol = c0 + 4 * c4;
-      if constexpr (!SYRK && WN % 64 == 0) if (g.bits != nullptr) {
-        // sign bits of the stored values (bit 1 iff !(u < 0) on the stored
-        // encoding, as sign_pack tests it).  A 16-lane DPP row holds 64
-        // consecutive columns of one row, 4 per lane: each lane places its
-        // nibble in the word's low or high half, an OR-scan over the row
-        // (shifts 1, 2, 4, 8) gathers the word in the row's last lane.
-        const bool f32_out = EPI == EPI_FINAL && g.u_dtype == MUON_F32;
-        uint32_t nib = 0;
+          for (int t = 0; t < 4; ++t)
+            nib |= (f32_out ? nonneg_f32(__float_as_uint(o[t])) : nonneg_bf16(f32_to_bf16(o[t]))) << t;
+          const int rl = lane & 15;
+          uint32_t lo = rl < 8 ? nib << (4 * rl) : 0u;
+          uint32_t hi = rl < 8 ? 0u : nib << (4 * (rl - 8));
+          lo |= row_shr_or<1>(lo); hi |= row_shr_or<1>(hi);
+          lo |= row_shr_or<2>(lo); hi |= row_shr_or<2>(hi);
+          lo |= row_shr_or<4>(lo); hi |= row_shr_or<4>(hi);
+          lo |= row_shr_or<8>(lo); hi |= row_shr_or<8>(hi);
+          if (rl == 15 && grow < g.bits_rows && g.col0 + gcol < g.bits_cols)
+            *reinterpret_cast<uint2*>(g.bits + batch * g.stride_bits + (grow * g.bits_cols + g.col0 + gcol) / 64) =
+                make_uint2(lo, hi);
+        }
+        if (EPI == EPI_FINAL) {
+          if (g.U != nullptr && !g.transpose_out && grow < g.s_valid) {
+            const int64_t idx = batch * g.strideU + grow * g.l_valid + g.col0 + gcol;
+            if (u_vec) {
+              // whole chunk inside U, 8- (bf16) or 16-byte (fp32) aligned
+              if (g.col0 + gcol < g.l_valid) {
+                if (g.u_dtype == MUON_BF16) {
+                  const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+                  const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+                  *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.U) + idx) = make_uint2(w0, w1);
+                } else {
+                  *reinterpret_cast<float4*>(static_cast<float*>(g.U) + idx) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+              }
+            } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          nib |= (f32_out ? nonneg_f32(__float_as_uint(o[t])) : nonneg_bf16(f32_to_bf16(o[t]))) << t;
-        const int rl = lane & 15;
-        uint32_t lo = rl < 8 ? nib << (4 * rl) : 0u;
-        uint32_t hi = rl < 8 ? 0u : nib << (4 * (rl - 8));
-        lo |= row_shr_or<1>(lo); hi |= row_shr_or<1>(hi);
-        lo |= row_shr_or<2>(lo); hi |= row_shr_or<2>(hi);
-        lo |= row_shr_or<4>(lo); hi |= row_shr_or<4>(hi);
-        lo |= row_shr_or<8>(lo); hi |= row_shr_or<8>(hi);
-        if (rl == 15 && grow < g.bits_rows && g.col0 + gcol < g.bits_cols)
-          *reinterpret_cast<uint2*>(g.bits + batch * g.stride_bits + (grow * g.bits_cols + g.col0 + gcol) / 64) =
-              make_uint2(lo, hi);
-      }
-      if (EPI == EPI_FINAL) {
-        if (g.U != nullptr && !g.transpose_out && grow < g.s_valid) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (g.col0 + gcol + t < g.l_valid) {
-              const int64_t idx = batch * g.strideU + grow * g.l_valid + g.col0 + gcol + t;
-              if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx] = f32_to_bf16(o[t]);
-              else static_cast<float*>(g.U)[idx] = o[t];
+              for (int t = 0; t < 4; ++t) {
+                if (g.col0 + gcol + t < g.l_valid) {
+                  if (g.u_dtype == MUON_BF16) static_cast<bf16_t*>(g.U)[idx + t] = f32_to_bf16(o[t]);
+                  else static_cast<float*>(g.U)[idx + t] = o[t];
+                }
+              }
             }
           }
+        } else if (SYRK || g.C != nullptr) {
+          const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+          const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+          *reinterpret_cast<uint2*>(crow + int64_t(p * RPP) * g.ld) = make_uint2(w0, w1);
         }
-      } else if (SYRK || g.C != nullptr) {
-        const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
-        const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
-        *reinterpret_cast<uint2*>(C + grow * g.ld + gcol) = make_uint2(w0, w1);
+        if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + slab_col<7>(row, 4 * cc)) = make_float4(o[0], o[1], o[2], o[3]);
       }
-      if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + slab_col<7>(row, 4 * c4)) = make_float4(o[0], o[1], o[2], o[3]);
+    };
+    if constexpr (!SYRK && WN % 64 == 0) {
+      if (g.bits != nullptr) pass1(std::true_type{});
+      else pass1(std::false_type{});
+    } else {
+      pass1(std::false_type{});
     }
     if (second_pass) {
       // mirrored / transposed: row c0 + mr receives slab rows 4*c4 .. 4*c4+3
