@@ -554,8 +554,11 @@ __device__ __forceinline__ void epilogue_scale(const GemmArgs& g, int64_t batch,
   }
 }
 
+// One work unit (workgroup `bid` of the launch's unit list) of a product; the
+// kernels below are thin wrappers, so that one launch can hold units of two
+// tile shapes.
 template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t bid, char* lds) {
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   constexpr int FM = C_::FM, FN = C_::FN, BK = C_::BK;
   static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
@@ -563,7 +566,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   // split units exist only in the 256 x 256-tile Gram (the one long symmetric
   // product); the other instantiations carry none of their code
   constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -585,7 +587,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
     // n_p^2 units per batch entry: tile row i holds units [i^2, (i+1)^2): the two
     // K halves of tiles (i, 0..i-1), then the lower half of diagonal tile (i, i)
     const int64_t np = g.M / BM;
-    const int64_t v = xcd_remap(blockIdx.x, np * np);
+    const int64_t v = xcd_remap(bid, np * np);
     int64_t i = static_cast<int64_t>(sqrt(double(v)));
     while (i * i > v) --i;
     while ((i + 1) * (i + 1) <= v) ++i;
@@ -600,7 +602,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
       sidx = batch * (np * (np - 1) / 2) + i * (i - 1) / 2 + tn;
     }
   } else {
-    tile_coords<BM, BN, SYRK>(g, xcd_remap(blockIdx.x, tiles), tm, tn);
+    tile_coords<BM, BN, SYRK>(g, xcd_remap(bid, tiles), tm, tn);
   }
   if (sidx >= 0) {
     kb = half ? KT / 2 : 0;
@@ -1125,6 +1127,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(Ge
   static_for<FM>(slab);
 }
 
+template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_dma_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  gemm_dma_unit<BM, BN, WM, WN, S, SYRK, NN, EPI>(g, blockIdx.x, lds);
+}
+
+// B X whose last round runs as 128 x 256 column strips, in one launch:
+// workgroups [0, n1) take the 256 x 256 tiles of g1, the others the strips
+// of g2, so a CU starts its strip as soon as its last whole tile is done
+// instead of after the slowest tile of the chip and a second launch.  n1 is a
+// multiple of the XCD count, so both parts keep their XCD-grouped tile order.
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_apply_mixed_kernel(GemmArgs g1, GemmArgs g2, int64_t n1) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int64_t b = blockIdx.x;
+  if (b < n1) gemm_dma_unit<256, 256, 64, 128, 4, false, true, EPI>(g1, b, lds);
+  else gemm_dma_unit<128, 256, 64, 64, 4, false, true, EPI>(g2, b - n1, lds);
+}
+
 // Number of workgroups of one batch entry.
 template <int BM, int BN, bool SYRK>
 inline int64_t tiles_of(const GemmArgs& g) {
@@ -1251,6 +1272,24 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
   static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
   if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(grid, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  return launch_status();
+}
+
+// The mixed launch above: g1 covers the first n1 = tiles of 256 x 256, g2 the
+// strips; both already carry their row stride, column offset and pointers.
+template <int EPI>
+int launch_apply_mixed(GemmArgs g1, GemmArgs g2, hipStream_t st) {
+  using A_ = DmaTile<256, 256, 64, 128, 4, true>;
+  using B_ = DmaTile<128, 256, 64, 64, 4, true>;
+  const int64_t n1 = tiles_of<256, 256, false>(g1), n2 = tiles_of<128, 256, false>(g2);
+  if (n1 % kXcds != 0) return MUON_EINVAL;
+  if (g1.bits != nullptr && (g1.bits_cols % 64 != 0 || g2.bits_cols % 64 != 0)) return MUON_EINVAL;
+  g1.split_mode = g2.split_mode = SPLIT_NONE;
+  constexpr int lds_bytes = A_::LDS_BYTES > B_::LDS_BYTES ? A_::LDS_BYTES : B_::LDS_BYTES;
+  auto kern = gemm_apply_mixed_kernel<EPI>;
+  static bool configured = false;
+  if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
+  kern<<<dim3(n1 + n2, 1), dim3(512), lds_bytes, st>>>(g1, g2, n1);
   return launch_status();
 }
 

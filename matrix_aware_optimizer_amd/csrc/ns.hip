@@ -141,7 +141,7 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   const gemm::Scratch none{nullptr, 0};
   const int64_t TM = g.M / 256, TN = g.N / 256, T = TM * TN;
   const int64_t cus = batch == 1 ? gemm::device_cus() : 0;
-  int64_t ct = 0;   // 256-column strips in the second launch
+  int64_t ct = 0;   // 256-column strips run as 128 x 256 tiles
   if (cus > 0 && TM > 0) {
     const int64_t r = T % cus;
     if (r > 0 && 2 * r <= cus && r % TM == 0 && r / TM < TN) ct = r / TM;
@@ -151,8 +151,6 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   GemmArgs g1 = g;
   g1.ld = g.N;
   g1.N = n1;
-  int status = gemm::launch_dma<256, 256, 64, 128, 4, false, true, EPI>(g1, batch, st, none);
-  if (status != MUON_OK) return status;
   GemmArgs g2 = g;
   g2.ld = g.N;
   g2.N = ct * 256;
@@ -160,6 +158,11 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   g2.Q = static_cast<const bf16_t*>(g.Q) + n1;
   if (g.Z) g2.Z = static_cast<const bf16_t*>(g.Z) + n1;
   if (g.C) g2.C = static_cast<bf16_t*>(g.C) + n1;
+  // one launch when the whole-tile count keeps the XCD grouping (batch is 1 here)
+  const int64_t whole = TM * (TN - ct);
+  if (whole > 0 && whole % gemm::kXcds == 0) return gemm::launch_apply_mixed<EPI>(g1, g2, st);
+  int status = gemm::launch_dma<256, 256, 64, 128, 4, false, true, EPI>(g1, batch, st, none);
+  if (status != MUON_OK) return status;
   return gemm::launch_dma<128, 256, 64, 64, 4, false, true, EPI>(g2, batch, st, none);
 }
 
