@@ -79,7 +79,7 @@ enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
 // diagonal tile as one unit that computes only its lower half, n_p^2 units of
 // about half a tile each instead of n_p (n_p + 1) / 2 whole tiles, which
 // would leave the other CUs idle.
-enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1 };
+enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2 };
 
 struct GemmArgs {
   const void* P;  // rows of the left operand, k-contiguous, ld = K
@@ -561,11 +561,16 @@ template <int BM, int BN, int WM, int WN, int S, bool SYRK, bool NN, int EPI>
 __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t bid, char* lds) {
   using C_ = DmaTile<BM, BN, WM, WN, S, NN>;
   constexpr int FM = C_::FM, FN = C_::FN, BK = C_::BK;
-  static_assert(!SYRK || (BM == BN && !NN), "symmetric products are NT with square tiles");
+  // symmetric products: square tiles, or (HALVES) the column halves of the
+  // off-diagonal square tiles of a BM-tiled lower triangle
+  constexpr bool HALVES = SYRK && BN * 2 == BM;
+  static_assert(!SYRK || ((BM == BN || HALVES) && !NN), "symmetric products are NT with square or half tiles");
   static_assert(WN >= 64, "the epilogue slab swizzle (slab_col<7>) needs 64 or more columns per wave");
   // split units exist only in the 256 x 256-tile Gram (the one long symmetric
   // product); the other instantiations carry none of their code
   constexpr bool SPLITS = SYRK && EPI == EPI_STORE && BM == 256 && C_::W == 8;
+  // lower-half diagonal units (the split Gram's, and SPLIT_DIAG launches)
+  constexpr bool DIAGS = SYRK && BM == 256 && BN == 256 && C_::W == 8;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -601,6 +606,22 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
       half = static_cast<int>(w & 1);
       sidx = batch * (np * (np - 1) / 2) + i * (i - 1) / 2 + tn;
     }
+  } else if (DIAGS && g.split_mode == SPLIT_DIAG) {
+    // unit v: the lower half of diagonal tile v
+    tm = tn = xcd_remap(bid, g.M / BM);
+    diag_half = true;
+  } else if (HALVES) {
+    // n_p (n_p - 1) units per batch entry: unit v is column half v & 1 of
+    // off-diagonal tile t = v >> 1 = i (i - 1) / 2 + j (row i, column j < i);
+    // both halves of a tile are neighbours in the XCD-grouped order
+    const int64_t np = g.M / BM;
+    const int64_t v = xcd_remap(bid, np * (np - 1));
+    const int64_t t = v >> 1;
+    int64_t i = static_cast<int64_t>((1.0 + sqrt(1.0 + 8.0 * double(t))) * 0.5);
+    while (i * (i - 1) / 2 > t) --i;
+    while ((i + 1) * i / 2 <= t) ++i;
+    tm = i;
+    tn = 2 * (t - i * (i - 1) / 2) + (v & 1);   // in units of BN columns
   } else {
     tile_coords<BM, BN, SYRK>(g, xcd_remap(bid, tiles), tm, tn);
   }
@@ -671,7 +692,7 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
       dma16(qk + q_off[q], st + C_::P_BYTES + (wave * C_::Q_DMA + q) * 1024);
   };
 
-  if constexpr (SPLITS) {
+  if constexpr (DIAGS) {
     if (diag_half) {
       // ---- lower half of a diagonal tile: P = Q, only P is staged ----
       auto body = [&](auto pat_c) {
@@ -974,7 +995,7 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
   // iteration of a tall matrix).
   bf16_t* C = static_cast<bf16_t*>(g.C) + batch * g.strideC;
   const bf16_t* Z = static_cast<const bf16_t*>(g.Z) + batch * g.strideZ;
-  const bool mirror = SYRK && (tm != tn);
+  const bool mirror = SYRK && (HALVES || tm != tn);
   const bool second_pass = mirror || (EPI == EPI_FINAL && g.transpose_out);
   const bool use_z = EPI != EPI_STORE && g.beta != 0.0f;
   float alpha, beta;
@@ -1146,6 +1167,18 @@ __global__ __launch_bounds__(512) void gemm_apply_mixed_kernel(GemmArgs g1, Gemm
   else gemm_dma_unit<128, 256, 64, 64, 4, false, true, EPI>(g2, b - n1, lds);
 }
 
+// A symmetric product as n_p^2 units per batch entry (n_p = M / 256), one
+// round when they fit the CUs: workgroups [0, n1 = n_p (n_p - 1)) take the
+// column halves (256 x 128) of the off-diagonal 256 x 256 tiles, the other
+// n_p the lower halves of the diagonal tiles.  No unit depends on another.
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_syrk_halves_kernel(GemmArgs gh, GemmArgs gd, int64_t n1) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int64_t b = blockIdx.x;
+  if (b < n1) gemm_dma_unit<256, 128, 64, 64, 4, true, false, EPI>(gh, b, lds);
+  else gemm_dma_unit<256, 256, 64, 128, 4, true, false, EPI>(gd, b - n1, lds);
+}
+
 // Number of workgroups of one batch entry.
 template <int BM, int BN, bool SYRK>
 inline int64_t tiles_of(const GemmArgs& g) {
@@ -1290,6 +1323,27 @@ int launch_apply_mixed(GemmArgs g1, GemmArgs g2, hipStream_t st) {
   static bool configured = false;
   if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(n1 + n2, 1), dim3(512), lds_bytes, st>>>(g1, g2, n1);
+  return launch_status();
+}
+
+// The halves launch above for g (a symmetric product on 256 x 256 tiles,
+// M a multiple of 512).
+template <int EPI>
+int launch_syrk_halves(GemmArgs g, int64_t batch, hipStream_t st) {
+  using H_ = DmaTile<256, 128, 64, 64, 4, false>;
+  using D_ = DmaTile<256, 256, 64, 128, 4, false>;
+  const int64_t np = g.M / 256;
+  if (np < 2 || g.M % 256 != 0 || g.N != g.M || batch == 0) return MUON_EINVAL;
+  if (g.ld == 0) g.ld = g.N;
+  GemmArgs gh = g, gd = g;
+  gh.split_mode = SPLIT_NONE;
+  gd.split_mode = SPLIT_DIAG;
+  const int64_t n1 = np * (np - 1);
+  constexpr int lds_bytes = H_::LDS_BYTES > D_::LDS_BYTES ? H_::LDS_BYTES : D_::LDS_BYTES;
+  auto kern = gemm_syrk_halves_kernel<EPI>;
+  static bool configured = false;
+  if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
+  kern<<<dim3(n1 + np, batch), dim3(512), lds_bytes, st>>>(gh, gd, n1);
   return launch_status();
 }
 

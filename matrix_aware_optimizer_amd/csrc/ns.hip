@@ -166,11 +166,21 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   return gemm::launch_dma<128, 256, 64, 64, 4, false, true, EPI>(g2, batch, st, none);
 }
 
+// bf16 symmetric product with the addend (the polynomial) as column halves
+// and diagonal lower halves: when its n_p^2 units per batch entry fit one
+// round of the CUs (4096: 256 units for 256 CUs, against 136 whole tiles).
+bool syrk_halves_fit(const GemmArgs& g, int64_t batch) {
+  const int64_t np = g.M / 256, cus = gemm::device_cus();
+  return np >= 2 && g.M % 256 == 0 && cus > 0 && np * np * batch <= cus;
+}
+
 template <typename T, bool SYRK, bool NN, int EPI>
 int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st, const gemm::Scratch& sc) {
   if constexpr (sizeof(T) == 2) {
     if constexpr (NN && !SYRK)
       if (big_tiles(SYRK, g.K)) return launch_apply_big<EPI>(g, batch, st);
+    if constexpr (SYRK && EPI == EPI_AXPBY)
+      if (syrk_halves_fit(g, batch)) return gemm::launch_syrk_halves<EPI>(g, batch, st);
     if (big_tiles(SYRK, g.K)) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st, sc);
     return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st, gemm::Scratch{nullptr, 0});
   } else {

@@ -158,3 +158,29 @@ def test_ns_final_iteration_through_column_strips(shape):
     assert rel_fro(got, ref) <= 2e-2
     tail = (slice(None), slice(-1024, None)) if shape[0] < shape[1] else (slice(-1024, None), slice(None))
     assert rel_fro(got[tail], ref[tail]) <= 2e-2
+
+
+@pytest.mark.parametrize("batch,s,sv", [(1, 4096, 4096), (3, 1024, 1000), (12, 768, 768), (1, 512, 512),
+                                        (2, 2048, 2048), (1, 256, 256)])
+def test_poly_column_halves_and_diagonal_units(batch, s, sv):
+    """B = b A + c A^2 as n_p^2 units per matrix when they fit one round of the CUs:
+    the two 256 x 128 column halves of every off-diagonal 256 x 256 tile (stored
+    and mirrored) and the lower half of every diagonal tile.  4096: 240 + 16 units
+    for 256 CUs; 1024 x 3 and 768 x 12 batched; 256 has no off-diagonal tile (one
+    whole tile).  Checked against the fp64 product at the stage tolerance, for
+    exact symmetry off the 32 x 32 diagonal blocks, and for zero padding."""
+    R = np.zeros((batch, s, s))
+    R[:, :sv, :sv] = random_matrix((batch, sv, sv), [325, s]) / np.sqrt(sv)
+    As = store(R + np.transpose(R, (0, 2, 1)), "bf16")
+    Ad = to_dev(As, "bf16").view(batch, s, s)
+    B = torch.full((batch, s, s), 7.0, dtype=torch.bfloat16, device="cuda")
+    b, c = QUINTIC[1], QUINTIC[2]
+    mao.ns_poly(Ad, B, b, c)
+    raw = from_dev(B).reshape(batch, s, s)
+    got = O.decode(raw, "bf16")
+    A = O.decode(As, "bf16")
+    for k in sorted({0, batch - 1}):
+        ref = O.poly(A[k], b, c)
+        assert rel_fro(got[k], ref) <= TOL_STAGE
+        assert _off_diagonal_block_symmetry(raw[k], s)
+        assert not got[k][sv:, :].any() and not got[k][:, sv:].any()
