@@ -134,10 +134,14 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
  *   round of the device's CUs (at most 256) runs every off-diagonal 256 x 256
  *   tile as two halves of the contraction and every diagonal tile as one unit
  *   computing only its lower half, instead of n_p (n_p + 1) / 2 whole tiles.
- *   The two halves of a tile meet through fp32 partial tiles in the
- *   workspace, added in either order (two terms: the sum is the same).
- *   Results therefore depend on the device's CU count only through this
- *   choice, and are deterministic on one device.
+ *   The half that finishes first leaves its fp32 partial tile in the
+ *   workspace; the other adds it (two terms: the sum does not depend on
+ *   which half came first).  The polynomial product B = bA + cA^2 (which
+ *   needs no workspace) runs, when its n_p^2 units per matrix fit one round
+ *   of the CUs, as the two 256 x 128 column halves of every off-diagonal tile
+ *   plus the lower half of every diagonal tile.  Results therefore depend on
+ *   the device's CU count only through these choices, and are deterministic
+ *   on one device.
  * ------------------------------------------------------------------------- */
 typedef struct muon_ns_problem {
   const void* M;

@@ -80,6 +80,10 @@ enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
 // about half a tile each instead of n_p (n_p + 1) / 2 whole tiles, which
 // would leave the other CUs idle.
 enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2 };
+// bound on the polls of the second K half waiting for the first one's partial
+// (each poll sleeps ~128 cycles; the first half never needs more than
+// microseconds, the bound only keeps a wait from outliving its cause)
+constexpr int kSplitSpinLimit = 1 << 22;
 
 struct GemmArgs {
   const void* P;  // rows of the left operand, k-contiguous, ld = K
@@ -120,7 +124,7 @@ struct GemmArgs {
   uint64_t* bits;
   int64_t bits_rows, bits_cols, stride_bits;
   int split_mode;
-  float* partials;       // 2 x (split tiles) x BM x BN fp32
+  float* partials;       // (split tiles) x BM x BN fp32: the first-arriving half's
   int* counters;         // one per split tile: zero on entry, left zero
 };
 
@@ -943,31 +947,50 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
   // vmcnt(0) wait puts every partial store before the counter increment, and
   // the loads are issued only after the increment has returned ----
   if constexpr (SPLITS) if (sidx >= 0) {
+    // The tile's arrival counter (zero on entry): each half adds 1 when its
+    // k-loop is done.  The first to arrive stores its fp32 partial tile as
+    // device-coherent relaxed atomic stores (global_store sc1, written
+    // through past the per-XCD L2), waits for them (vmcnt(0)), adds 2 and
+    // leaves; the count then reaches 4 once both have arrived and the partial
+    // is in memory.  The second waits for 4, reads the partial with coherent
+    // loads, adds it (two terms: the order does not change the sum), clears
+    // the counter and runs the epilogue.  The first half depends on no other
+    // workgroup after its loop, so the wait ends; it is also bounded.
     __shared__ int split_arrival;   // only this instantiation holds it: the others may use all 160 KB
     constexpr int PER_WAVE = FM * FN * 4 * kWave;   // 16-byte pieces per wave
     typedef unsigned long long u64_t;
-    u64_t* mine = reinterpret_cast<u64_t*>(g.partials + (2 * sidx + half) * int64_t(BM * BN)) +
-                  2 * (wave * PER_WAVE + lane);
-    const u64_t* other = reinterpret_cast<const u64_t*>(g.partials + (2 * sidx + (half ^ 1)) * int64_t(BM * BN)) +
-                         2 * (wave * PER_WAVE + lane);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int o = 2 * ((i * FN + j) * 4 + q) * kWave;
-          const u64_t lo = (u64_t(__float_as_uint(acc[i][j][4 * q + 1])) << 32) | __float_as_uint(acc[i][j][4 * q]);
-          const u64_t hi = (u64_t(__float_as_uint(acc[i][j][4 * q + 3])) << 32) | __float_as_uint(acc[i][j][4 * q + 2]);
-          __hip_atomic_store(mine + o, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(mine + o + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are done
-    __syncthreads();
+    u64_t* part = reinterpret_cast<u64_t*>(g.partials + sidx * int64_t(BM * BN)) + 2 * (wave * PER_WAVE + lane);
     if (tid == 0)
       split_arrival = __hip_atomic_fetch_add(g.counters + sidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (split_arrival == 0) return;   // first half in: the other half finishes the tile
+    if (split_arrival == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int o = 2 * ((i * FN + j) * 4 + q) * kWave;
+            const u64_t lo = (u64_t(__float_as_uint(acc[i][j][4 * q + 1])) << 32) | __float_as_uint(acc[i][j][4 * q]);
+            const u64_t hi = (u64_t(__float_as_uint(acc[i][j][4 * q + 3])) << 32) | __float_as_uint(acc[i][j][4 * q + 2]);
+            __hip_atomic_store(part + o, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + o + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are done
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(g.counters + sidx, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;   // the other half finishes the tile
+    }
+    if (tid == 0) {
+      for (int spin = 0; spin < kSplitSpinLimit; ++spin) {
+        // an agent-scope atomic load observes the agent-scope adds to the
+        // same word (the compiler emits a coherent sc1 load, and turns an
+        // add of zero into the same load)
+        if (__hip_atomic_load(g.counters + sidx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -975,8 +998,8 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int o = 2 * ((i * FN + j) * 4 + q) * kWave;
-          const u64_t lo = __hip_atomic_load(other + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const u64_t hi = __hip_atomic_load(other + o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const u64_t lo = __hip_atomic_load(part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const u64_t hi = __hip_atomic_load(part + o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           acc[i][j][4 * q] += __uint_as_float(static_cast<uint32_t>(lo));
           acc[i][j][4 * q + 1] += __uint_as_float(static_cast<uint32_t>(lo >> 32));
           acc[i][j][4 * q + 2] += __uint_as_float(static_cast<uint32_t>(hi));
@@ -1220,8 +1243,8 @@ int set_lds_limit(K kern, int bytes, bool& configured) {
 
 // ---------------------------------------------------------------------------
 // Split planning (host).  The scratch of a split launch is a fixed block of
-// kSplitCounters int arrival counters, then two fp32 BM x BN partial tiles
-// per split tile.  Every plan has at most kSplitCounters split tiles
+// kSplitCounters int arrival counters, then one fp32 BM x BN partial tile
+// per split tile (written by the first K half to finish).  Every plan has at most kSplitCounters split tiles
 // (SPLIT_SYRK: n_p (n_p - 1) / 2 * batch < n_p^2 * batch / 2 <= 128), so one
 // scratch serves launches of any shape without its counters moving.
 // ---------------------------------------------------------------------------
@@ -1247,7 +1270,7 @@ struct Scratch {         // caller-provided split scratch (base == nullptr: no s
 
 inline size_t split_scratch_bytes(int64_t split_tiles, int bm, int bn) {
   if (split_tiles <= 0) return 0;
-  return kSplitCounterBytes + static_cast<size_t>(split_tiles) * 2 * bm * bn * sizeof(float);
+  return kSplitCounterBytes + static_cast<size_t>(split_tiles) * bm * bn * sizeof(float);
 }
 
 // cus > 0: the plan for a device with that many CUs (one 256 x 256-tile

@@ -102,11 +102,11 @@ def test_stage_validation(L):
 
 
 def test_stage_workspace_bytes(L):
-    """Split scratch: 512 bytes of arrival counters, then two fp32 256 x 256 partial
-    tiles per split tile.  Only symmetric products with a contraction of at least
+    """Split scratch: 512 bytes of arrival counters, then one fp32 256 x 256 partial
+    tile per split tile.  Only symmetric products with a contraction of at least
     8192 whose n_p^2 units (n_p = s / 256) fit one round of 256 CUs split: the Gram
     of 4096 x 14336 splits its 120 off-diagonal tiles; fp32 never splits."""
-    tile = 2 * 256 * 256 * 4
+    tile = 256 * 256 * 4
     assert L.ns_stage_workspace_bytes(4096, 14336, 1, 1) == 512 + 120 * tile
     assert L.ns_stage_workspace_bytes(4096, 14336, 1, 0) == 0
     assert L.ns_stage_workspace_bytes(4096, 4096, 1, 1) == 0                 # contraction too short
@@ -130,10 +130,10 @@ def _problems(specs):
 
 def _ns_bytes(count, s, l, es=2, sumsq=True, part=0, split=0):
     """Run buffers (two X, A, B, sums, norm partials) after the split scratch: 512
-    bytes of counters and two fp32 256 x 256 partial tiles per split tile."""
+    bytes of counters and one fp32 256 x 256 partial tile per split tile."""
     def up(x):
         return -(-x // 256) * 256
-    scratch = 512 + split * 2 * 256 * 256 * 4 if split else 0
+    scratch = 512 + split * 256 * 256 * 4 if split else 0
     return (scratch + 2 * up(count * s * l * es) + 2 * up(count * s * s * es)
             + (0 if sumsq else up(4 * count)) + up(part))
 
