@@ -88,11 +88,12 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra measurements after the timed steps "
                          "(profiling runs then trace the step's kernels only)")
-    ap.add_argument("--extras", default="cold,int8,reorth,dion,library",
+    ap.add_argument("--extras", default="cold,int8,reorth,dion,library,configs",
                     help="comma list of extra measurements to run after the timed steps: "
                          "cold (elementwise kernels with cold caches), int8 (int8 SUM exchange), "
                          "reorth (re-orthogonalised update), dion (Dion step), "
-                         "library (vendor GEMM library on the same shapes)")
+                         "library (vendor GEMM library on the same shapes), "
+                         "configs (ns_orthogonalize on the other workloads' matrix sets)")
     ap.add_argument("--repeat-kernel", default=None,
                     help="profiling aid: after the run, launch one stage N more times "
                          "(gram|poly|apply|momentum|pack|vote|update|copy:N)")
@@ -370,6 +371,8 @@ def main():
         result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
     if "dion" in extras:
         result["dion"] = dion_bench(mao, torch, dev)
+    if "configs" in extras:
+        result["ns_configs"] = ns_configs(mao, torch, dev)
     if "library" in extras and prec == "bf16":
         result["library_reference"] = library_reference(torch, avg, s, l, dev)
 
@@ -525,6 +528,47 @@ def dion_bench(mao, torch, dev, reps=5):
         tf = flops / (ms * 1e-3) / 1e12
         out[f"rank_{rank}"] = {"ms": ms, "TFLOP/s": tf, "frac_fp32_peak": tf / PEAK_F32_TFLOPS,
                                "workload": wl.name}
+    return out
+
+
+def ns_configs(mao, torch, dev, reps=5):
+    """ns_orthogonalize alone on the other workloads' matrix sets, as one call per
+    set (the library batches equal shapes): the GPT-2-small layer set (48
+    matrices, 4 shapes), 128 batched 1024 x 1024, and 7168 x 18432 (fp32 momentum),
+    5 quintic steps, norms computed by the call.  Seeded normal inputs; HIP
+    events on the stream the call runs on."""
+    from workloads import WORKLOADS
+    out = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    for cfg in (2, 3, 5):
+        wl = WORKLOADS[cfg]
+        offs = wl.offsets
+        M = torch.randn(wl.numel, generator=gen, device=dev).to(tdt[wl.m_dtype])
+        U = torch.empty(wl.numel, dtype=tdt[wl.precision], device=dev)
+        probs = [(M[offs[j]:offs[j + 1]].view(r, c), U[offs[j]:offs[j + 1]].view(r, c), None)
+                 for j, (r, c) in enumerate(wl.shapes)]
+        ws = torch.empty(max(mao.ns_workspace_bytes(probs, wl.precision), 1), dtype=torch.uint8, device=dev)
+        a, b, c = wl.coeffs
+        mao.ns_orthogonalize(probs, a, b, c, wl.ns_steps, wl.precision, ws)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            mao.ns_orthogonalize(probs, a, b, c, wl.ns_steps, wl.precision, ws)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        flops = 0
+        for r, cc in wl.shapes:
+            g_, p_, ap_ = ns_flops(min(r, cc), max(r, cc), c != 0.0)
+            flops += wl.ns_steps * (g_ + p_ + ap_)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"C{cfg}"] = {"workload": wl.name, "matrices": len(wl.shapes), "ms_per_call": ms,
+                          "orthogonalizations_per_s": len(wl.shapes) / (ms * 1e-3),
+                          "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+        del M, U, ws
     return out
 
 

@@ -166,9 +166,11 @@ def test_poly_column_halves_and_diagonal_units(batch, s, sv):
     """B = b A + c A^2 as n_p^2 units per matrix when they fit one round of the CUs:
     the two 256 x 128 column halves of every off-diagonal 256 x 256 tile (stored
     and mirrored) and the lower half of every diagonal tile.  4096: 240 + 16 units
-    for 256 CUs; 1024 x 3 and 768 x 12 batched; 256 has no off-diagonal tile (one
-    whole tile).  Checked against the fp64 product at the stage tolerance, for
-    exact symmetry off the 32 x 32 diagonal blocks, and for zero padding."""
+    for 256 CUs; 1024 x 3 and 2048 x 2 batched.  768 x 12 and 512 (side below
+    1024 and a short contraction) run 128 x 128 tiles instead, and 256 one tile;
+    all are checked the same way: against the fp64 product at the stage
+    tolerance, for exact symmetry off the 32 x 32 diagonal blocks, and for zero
+    padding."""
     R = np.zeros((batch, s, s))
     R[:, :sv, :sv] = random_matrix((batch, sv, sv), [325, s]) / np.sqrt(sv)
     As = store(R + np.transpose(R, (0, 2, 1)), "bf16")
