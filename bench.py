@@ -535,8 +535,9 @@ def ns_configs(mao, torch, dev, reps=5):
     """ns_orthogonalize alone on the other workloads' matrix sets, as one call per
     set (the library batches equal shapes): the GPT-2-small layer set (48
     matrices, 4 shapes), 128 batched 1024 x 1024, and 7168 x 18432 (fp32 momentum),
-    5 quintic steps, norms computed by the call.  Seeded normal inputs; HIP
-    events on the stream the call runs on."""
+    5 quintic steps.  The per-matrix sums of squares are passed in, as the
+    optimizer step passes muon_momentum's (computed once here, before timing).
+    Seeded normal inputs; HIP events on the stream the call runs on."""
     from workloads import WORKLOADS
     out = {}
     gen = torch.Generator(device=dev)
@@ -547,7 +548,13 @@ def ns_configs(mao, torch, dev, reps=5):
         offs = wl.offsets
         M = torch.randn(wl.numel, generator=gen, device=dev).to(tdt[wl.m_dtype])
         U = torch.empty(wl.numel, dtype=tdt[wl.precision], device=dev)
-        probs = [(M[offs[j]:offs[j + 1]].view(r, c), U[offs[j]:offs[j + 1]].view(r, c), None)
+        offs_d = torch.from_numpy(offs).to(dev)
+        sums = torch.zeros(len(wl.shapes), dtype=torch.float32, device=dev)
+        mws = torch.empty(mao.muon_momentum_workspace_bytes(wl.numel, len(wl.shapes)), dtype=torch.uint8,
+                          device=dev)
+        # beta = 1, alpha = 0 leaves M as it is and writes its sums of squares
+        mao.muon_momentum(M, M, 1.0, 0.0, offs_d, sums, mws)
+        probs = [(M[offs[j]:offs[j + 1]].view(r, c), U[offs[j]:offs[j + 1]].view(r, c), sums[j:j + 1])
                  for j, (r, c) in enumerate(wl.shapes)]
         ws = torch.empty(max(mao.ns_workspace_bytes(probs, wl.precision), 1), dtype=torch.uint8, device=dev)
         a, b, c = wl.coeffs

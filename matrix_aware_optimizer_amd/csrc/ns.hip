@@ -121,18 +121,19 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // ---------------------------------------------------------------------------
 // bf16 products run the DMA-pipelined kernel with a 4-stage LDS ring.  Tile
 // choice (measured on MI355X with the batched workloads' matrix sets): 256 x
-// 256 tiles of 8 waves (64 x 128 each) for B X with K >= 1024 and for the
-// symmetric products unless both the side and the contraction are short
-// (side < 1024 and K < 2048, e.g. 768 x 768 matrices); 128 x 128 tiles (4
-// waves of 64 x 64) otherwise, where prologue and epilogue weigh more than
-// the smaller tiles' lower reuse.  128 x 1024^2: 4.96 -> 4.36 ms per
-// orthogonalisation call; GPT-2-small layer set: 3.02 -> 2.91 ms.  fp32
-// products (small, latency-bound workloads) use the register-staged kernel.
+// 256 tiles of 8 waves (64 x 128 each) for B X with K >= 1024 and for
+// symmetric products with a side of at least 1024 (or a contraction long
+// enough to split, K >= 8192); 128 x 128 tiles (4 waves of 64 x 64)
+// otherwise: there a 256 x 256 grid leaves most CUs idle (a 768 side: 6 tiles
+// per matrix) and prologue and epilogue weigh more than the smaller tiles'
+// lower reuse.  128 x 1024^2: 4.96 -> 4.36 ms per orthogonalisation call;
+// GPT-2-small layer set: 3.02 -> 2.30 ms.  fp32 products (small,
+// latency-bound workloads) use the register-staged kernel.
 //
 // The 256 x 256-tile symmetric products may split their work units
 // (gemm::Split) when given scratch: long contractions whose n_p^2 units fit
 // one round of the CUs.
-constexpr bool big_tiles(bool syrk, int64_t K, int64_t M) { return syrk ? (K >= 2048 || M >= 1024) : K >= 1024; }
+constexpr bool big_tiles(bool syrk, int64_t K, int64_t M) { return syrk ? (M >= 1024 || K >= 8192) : K >= 1024; }
 
 // B X on 256 x 256 tiles: when the last round of tiles would leave at least
 // half of the CUs idle and those tiles form whole column strips, the strips
