@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void sum_int8_kernel(const uint4* __restr
   for (int k = 0; k < M; k += kVoteChunk) {
     uint4 x[kVoteChunk];
 #pragma unroll
-    for (int j = 0; j < kVoteChunk; ++j) x[j] = k + j < M ? S[int64_t(k + j) * nvec + t] : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kVoteChunk; ++j) x[j] = k + j < M ? load_stream(S + int64_t(k + j) * nvec + t) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < kVoteChunk; ++j) acc = add_bytes(acc, x[j]);
   }
@@ -606,19 +606,27 @@ __global__ __launch_bounds__(kThreads) void threshold_pack_kernel(const int8_t* 
 // the dense update W <- W - eta * U.
 // ---------------------------------------------------------------------------
 // 16 entries (two bytes of bits) per lane
+constexpr int kUnpackPerLane = 8;   // entries (vote bits) per lane: 8, 16 or 32 (8 measured fastest)
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void unpack_signs_kernel(const uint8_t* __restrict__ bits,
                                                                int64_t numel, T* __restrict__ out) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t e0 = t * 16;
+  const int64_t e0 = t * kUnpackPerLane;
   if (e0 >= numel) return;
-  if (e0 + 16 <= numel) {
-    const uint32_t b16 = *reinterpret_cast<const uint16_t*>(bits + 2 * t);
-    float v[2][8];
+  if (e0 + kUnpackPerLane <= numel) {
+    // one load of the lane's kUnpackPerLane vote bits, then groups of 8 outputs
+    uint32_t bw;
+    if constexpr (kUnpackPerLane == 8) bw = bits[t];
+    else if constexpr (kUnpackPerLane == 16) bw = *reinterpret_cast<const uint16_t*>(bits + 2 * t);
+    else bw = *reinterpret_cast<const uint32_t*>(bits + 4 * t);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q >> 3][q & 7] = ((b16 >> q) & 1u) ? 1.0f : -1.0f;
-    Vec8<T>::store(out + e0, v[0]);
-    Vec8<T>::store(out + e0 + 8, v[1]);
+    for (int g = 0; g < kUnpackPerLane / 8; ++g) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = ((bw >> (8 * g + q)) & 1u) ? 1.0f : -1.0f;
+      Vec8<T>::store(out + e0 + 8 * g, v);
+    }
   } else {
     for (int q = 0; e0 + q < numel; ++q)
       out[e0 + q] = from_f32<T>(((bits[(e0 + q) >> 3] >> ((e0 + q) & 7)) & 1u) ? 1.0f : -1.0f);
@@ -899,7 +907,7 @@ int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, 
   if (numel == 0) return MUON_OK;
   if (!bits || !out) return MUON_EINVAL;
   if (!aligned16(bits) || !aligned16(out)) return MUON_EALIGN;
-  const int64_t blocks = ((numel + 15) / 16 + kThreads - 1) / kThreads;
+  const int64_t blocks = ((numel + kUnpackPerLane - 1) / kUnpackPerLane + kThreads - 1) / kThreads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
   if (out_dtype == MUON_BF16)
