@@ -111,7 +111,7 @@ def ns_flops(s: int, l: int, c_nonzero: bool):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the step has no multi-GPU path; use --gpus 1"}))
         sys.exit(2)
 
     import torch
