@@ -129,3 +129,35 @@ def test_ns_signs_agree_with_oracle_direction():
     assert clear.mean() > 0.5
     assert np.array_equal(got[clear], O.sign_bits(ref)[clear])
     assert rel_fro(O.decode(from_dev(U), "bf16"), ref) <= 2e-2
+
+
+def test_apply_signs_non_finite_and_no_addend():
+    """Signs of stored non-finite values follow sign_pack's rule (NaN gives 1, -inf
+    gives 0), and a = 0 (no addend read) packs the same way."""
+    batch, s, l = 1, 1024, 4096
+    B, X = _stage_inputs(batch, s, l, 77)
+    Xh = from_dev(X).reshape(s, l).copy()
+    Xh[5, :] = 0x7FC0            # NaN row: NaN wherever B[:, 5] is non-zero
+    Xh[9, 100:200] = 0xFF80      # -inf entries
+    Xh[17, 300:400] = 0x7F80     # +inf entries
+    Xd = to_dev(Xh, "bf16").view(1, s, l)
+    for a in (QUINTIC[0], 0.0):
+        ref = torch.empty_like(Xd)
+        mao.ns_apply(B, Xd, ref, a, 1.0)
+        bits = _words(s * l // 64)
+        mao.ns_apply_signs(B, Xd, None, bits, a, 1.0)
+        want = O.sign_pack(O.decode(from_dev(ref), "bf16"))
+        assert np.array_equal(from_dev(bits), want), f"a = {a}"
+
+
+def test_ns_orthogonalize_signs_cubic():
+    """c = 0 (cubic coefficients): the last product is a X + b A X, packed in place."""
+    from workloads import CUBIC
+    shapes = [(1024, 2048)]
+    sizes = [r * c for r, c in shapes]
+    Mh = store(random_matrix((sizes[0],), [335, 0]), "bf16")
+    Md = to_dev(Mh, "bf16")
+    U = torch.empty(sizes[0], dtype=torch.bfloat16, device="cuda")
+    bits = _words(sizes[0] // 64)
+    mao.ns_orthogonalize([(Md.view(*shapes[0]), U.view(*shapes[0]), None, bits)], *CUBIC, 5, "bf16")
+    assert np.array_equal(from_dev(bits), O.sign_pack(O.decode(from_dev(U), "bf16")))
