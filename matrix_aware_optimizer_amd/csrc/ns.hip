@@ -123,11 +123,12 @@ __global__ __launch_bounds__(256) void emit_kernel(const TX* __restrict__ X, int
 // choice (measured on MI355X with the batched workloads' matrix sets): 256 x
 // 256 tiles of 8 waves (64 x 128 each) for B X with K >= 1024 and for
 // symmetric products with a side of at least 1024 (or a contraction long
-// enough to split, K >= 8192); 128 x 128 tiles (4 waves of 64 x 64)
+// enough to split, K >= 8192); 128 x 128 tiles (8 waves of 32 x 64)
 // otherwise: there a 256 x 256 grid leaves most CUs idle (a 768 side: 6 tiles
 // per matrix) and prologue and epilogue weigh more than the smaller tiles'
 // lower reuse.  128 x 1024^2: 4.96 -> 4.36 ms per orthogonalisation call;
-// GPT-2-small layer set: 3.02 -> 2.30 ms.  fp32 products (small,
+// GPT-2-small layer set: 3.02 -> 2.30 ms, and 2.26 ms with the 128 x 128
+// tiles on 8 waves instead of 4.  fp32 products (small,
 // latency-bound workloads) use the register-staged kernel.
 //
 // The 256 x 256-tile symmetric products may split their work units
@@ -186,7 +187,8 @@ int launch_gemm(const GemmArgs& g, int64_t batch, hipStream_t st, const gemm::Sc
     if constexpr (SYRK && EPI == EPI_AXPBY)
       if (big_tiles(SYRK, g.K, g.M) && syrk_halves_fit(g, batch)) return gemm::launch_syrk_halves<EPI>(g, batch, st);
     if (big_tiles(SYRK, g.K, g.M)) return gemm::launch_dma<256, 256, 64, 128, 4, SYRK, NN, EPI>(g, batch, st, sc);
-    return gemm::launch_dma<128, 128, 64, 64, 4, SYRK, NN, EPI>(g, batch, st, gemm::Scratch{nullptr, 0});
+    // 8 waves of 32 x 64: two per SIMD, and two workgroups per CU (74 KB of LDS each)
+    return gemm::launch_dma<128, 128, 32, 64, 4, SYRK, NN, EPI>(g, batch, st, gemm::Scratch{nullptr, 0});
   } else {
     return gemm::launch<T, 128, 128, 64, 64, SYRK, NN, EPI>(g, batch, st);
   }
