@@ -17,9 +17,12 @@
  *     MUON_F32 (IEEE binary32) and MUON_BF16 (bfloat16, the upper 16 bits of
  *     binary32).
  *   - Every tensor argument is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or retains memory, and keeps no state
- *     between calls.  Scratch memory is passed in as `workspace`, sized by the
- *     matching *_workspace_bytes query.
+ *     library never allocates, frees or retains memory.  Between calls it
+ *     keeps only per-device facts set once: each device's CU count and the
+ *     dynamic LDS limits of its kernels (kernel attributes).  These are
+ *     atomics, so host threads may call concurrently (on separate streams
+ *     and buffers).  Scratch memory is passed in as `workspace`, sized by
+ *     the matching *_workspace_bytes query.
  *   - Device pointers must be 16-byte aligned (MUON_EALIGN otherwise).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     kernels on it and never synchronise; device faults surface at the

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "muon.h"
 
 namespace muon {
@@ -16,6 +18,21 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Host-side one-time set-up is tracked per device (ordinals 0..63) with
+// atomics, so host threads may call concurrently and each device gets its own
+// kernel attributes.  A device past 63 simply repeats the set-up every call.
+constexpr int kMaxTrackedDevices = 64;
+
+inline int current_device() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+// Bit of `dev` in a per-device set, or 0 when the ordinal is not tracked.
+inline uint64_t device_bit(int dev) {
+  return dev >= 0 && dev < kMaxTrackedDevices ? uint64_t(1) << dev : 0;
+}
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

@@ -610,13 +610,21 @@ bool dion_valid(const muon_dion_problem& p, int count) {
          std::max<int64_t>(tm, 48) * tn * count < (int64_t(1) << 32);
 }
 
+// The LDS limit of the factorisation kernel, raised per device to the largest
+// request so far (a raced update only repeats the attribute call).
 int set_chol_lds(int bytes) {
-  static int configured = 0;
-  if (bytes > configured) {
+  static std::atomic<int> configured[kMaxTrackedDevices];   // bytes set, per device
+  const int dev = current_device();
+  const bool tracked = dev >= 0 && dev < kMaxTrackedDevices;
+  if (!tracked || bytes > configured[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(chol_inv_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
       return MUON_ELAUNCH;
-    configured = bytes;
+    if (tracked) {
+      int cur = configured[dev].load(std::memory_order_relaxed);
+      while (bytes > cur && !configured[dev].compare_exchange_weak(cur, bytes, std::memory_order_release)) {
+      }
+    }
   }
   return MUON_OK;
 }

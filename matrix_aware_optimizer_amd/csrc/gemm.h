@@ -1212,6 +1212,21 @@ inline int64_t tiles_of(const GemmArgs& g) {
   return (g.M / BM) * (g.N / BN);
 }
 
+// The dynamic LDS limit is an attribute of the kernel on the current device:
+// set it once per device (`configured` holds one bit per device).  Setting it
+// twice is harmless, so threads that race here only repeat the call.
+template <typename K>
+int set_lds_limit(K kern, int bytes, std::atomic<uint64_t>& configured) {
+  const uint64_t bit = device_bit(current_device());
+  if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return MUON_ELAUNCH;
+    configured.fetch_or(bit, std::memory_order_release);
+  }
+  return MUON_OK;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, bool SYRK, bool NN, int EPI>
 int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
   using C_ = Tile<T, BM, BN, WM, WN>;
@@ -1219,26 +1234,10 @@ int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
   if (blocks == 0 || batch == 0) return MUON_OK;
   if (g.bits != nullptr) return MUON_EINVAL;   // sign bits: DMA kernel only
   auto kern = gemm_kernel<T, BM, BN, WM, WN, SYRK, NN, EPI>;
-  static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
-  if (!configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C_::LDS_BYTES) != hipSuccess)
-      return MUON_ELAUNCH;
-    configured = true;
-  }
+  static std::atomic<uint64_t> configured{0};   // devices with the LDS limit set
+  if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
   return launch_status();
-}
-
-template <typename K>
-int set_lds_limit(K kern, int bytes, bool& configured) {
-  if (!configured) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return MUON_ELAUNCH;
-    configured = true;
-  }
-  return MUON_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -1289,13 +1288,16 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int64_t batch, int64_t cus
 
 // compute units of the current device (cached per device)
 inline int64_t device_cus() {
-  static int64_t cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  static std::atomic<int> cache[kMaxTrackedDevices];   // 0 = not yet queried
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  if (dev < kMaxTrackedDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cache[dev] = n;
+  if (dev < kMaxTrackedDevices && n > 0) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1325,7 +1327,7 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
     }
   }
   auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
-  static bool configured = false;  // the dynamic LDS limit is a per-kernel attribute
+  static std::atomic<uint64_t> configured{0};   // devices with the LDS limit set
   if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(grid, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
   return launch_status();
@@ -1343,7 +1345,7 @@ int launch_apply_mixed(GemmArgs g1, GemmArgs g2, hipStream_t st) {
   g1.split_mode = g2.split_mode = SPLIT_NONE;
   constexpr int lds_bytes = A_::LDS_BYTES > B_::LDS_BYTES ? A_::LDS_BYTES : B_::LDS_BYTES;
   auto kern = gemm_apply_mixed_kernel<EPI>;
-  static bool configured = false;
+  static std::atomic<uint64_t> configured{0};
   if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(n1 + n2, 1), dim3(512), lds_bytes, st>>>(g1, g2, n1);
   return launch_status();
@@ -1364,7 +1366,7 @@ int launch_syrk_halves(GemmArgs g, int64_t batch, hipStream_t st) {
   const int64_t n1 = np * (np - 1);
   constexpr int lds_bytes = H_::LDS_BYTES > D_::LDS_BYTES ? H_::LDS_BYTES : D_::LDS_BYTES;
   auto kern = gemm_syrk_halves_kernel<EPI>;
-  static bool configured = false;
+  static std::atomic<uint64_t> configured{0};
   if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
   kern<<<dim3(n1 + np, batch), dim3(512), lds_bytes, st>>>(gh, gd, n1);
   return launch_status();
