@@ -60,6 +60,11 @@ enum muon_status {
 #define MUON_MAX_VOTERS 1023
 /* most workers whose int8 signs can be summed in int8 */
 #define MUON_INT8_MAX_VOTERS 127
+/* Largest element count (numel) the elementwise calls accept, and 64 times
+ * the largest nwords of majority_vote: 2^38, more than any one device's
+ * memory holds even at one byte per entry, and small enough that every
+ * launch grid stays within its 32-bit limit.  Larger: MUON_EINVAL. */
+#define MUON_MAX_NUMEL (INT64_C(1) << 38)
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* muon_status_string(int status);

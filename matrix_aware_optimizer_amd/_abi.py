@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libmuon.so")
 MUON_F32, MUON_BF16 = 0, 1
 MUON_NS_PAD = 256
 MUON_MAX_VOTERS = 1023
+MUON_MAX_NUMEL = 1 << 38   # largest element count of the elementwise calls
 
 _c_void_p, _c_int, _c_i64, _c_size, _c_float = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                                  ctypes.c_size_t, ctypes.c_float)

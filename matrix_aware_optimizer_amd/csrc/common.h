@@ -110,6 +110,8 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// An element count the elementwise calls accept (0 .. MUON_MAX_NUMEL).
+inline bool numel_ok(int64_t n) { return n >= 0 && n <= MUON_MAX_NUMEL; }
 inline bool valid_dtype(int d) { return d == MUON_F32 || d == MUON_BF16; }
 inline size_t dtype_size(int d) { return d == MUON_F32 ? 4 : 2; }
 inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }

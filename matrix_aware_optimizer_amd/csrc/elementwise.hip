@@ -751,7 +751,7 @@ using namespace muon;
 extern "C" {
 
 size_t muon_momentum_workspace_bytes(int64_t numel, int nseg) {
-  if (numel < 0 || nseg < 0) return 0;
+  if (!numel_ok(numel) || nseg < 0) return 0;
   const int64_t nchunks = (numel + kChunk - 1) / kChunk;
   return round_up(static_cast<size_t>(nchunks + nseg + 1) * sizeof(double), 256);
 }
@@ -759,7 +759,7 @@ size_t muon_momentum_workspace_bytes(int64_t numel, int nseg) {
 int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
                   const int64_t* seg_offsets, int nseg, float beta, float alpha, float* sumsq_out,
                   void* workspace, size_t ws_bytes, void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(m_dtype) || !valid_dtype(g_dtype)) return MUON_EDTYPE;
   if (numel > 0 && (!M || !G)) return MUON_EINVAL;
   if (numel > 0 && (!aligned16(M) || !aligned16(G))) return MUON_EALIGN;
@@ -785,7 +785,7 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
 }
 
 int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(u_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!U || !bits) return MUON_EINVAL;
@@ -803,7 +803,7 @@ int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* s
 }
 
 int majority_vote(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, void* stream) {
-  if (nwords < 0 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
+  if (nwords < 0 || nwords > MUON_MAX_NUMEL / 64 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
   if (nwords == 0) return MUON_OK;
   if (!bits || !out) return MUON_EINVAL;
   if (!aligned16(bits) || !aligned16(out)) return MUON_EALIGN;
@@ -813,7 +813,7 @@ int majority_vote(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, vo
 
 int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits, float eta,
                  void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(w_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!W || !vote_bits) return MUON_EINVAL;
@@ -832,7 +832,7 @@ int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits,
 
 int vote_and_update(void* W, int w_dtype, int64_t numel, const uint64_t* bits, int M, float eta,
                     void* stream) {
-  if (numel < 0 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
+  if (!numel_ok(numel) || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;
   if (!valid_dtype(w_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!W || !bits) return MUON_EINVAL;
@@ -858,7 +858,7 @@ int muon_version(void) { return 100; }
 
 
 int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(u_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!U || !S) return MUON_EINVAL;
@@ -874,7 +874,7 @@ int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream
 }
 
 int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream) {
-  if (numel < 0 || M < 1 || M > MUON_INT8_MAX_VOTERS) return MUON_EINVAL;
+  if (!numel_ok(numel) || M < 1 || M > MUON_INT8_MAX_VOTERS) return MUON_EINVAL;
   if (numel == 0) return MUON_OK;
   if (!S || !out) return MUON_EINVAL;
   if (!aligned16(S) || !aligned16(out)) return MUON_EALIGN;
@@ -890,7 +890,7 @@ int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream) {
 }
 
 int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (numel == 0) return MUON_OK;
   if (!sum || !bits) return MUON_EINVAL;
   if (!aligned16(sum) || !aligned16(bits)) return MUON_EALIGN;
@@ -902,7 +902,7 @@ int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* strea
 }
 
 int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(out_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!bits || !out) return MUON_EINVAL;
@@ -919,7 +919,7 @@ int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, 
 
 int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u_dtype, float eta,
                        void* stream) {
-  if (numel < 0) return MUON_EINVAL;
+  if (!numel_ok(numel)) return MUON_EINVAL;
   if (!valid_dtype(w_dtype) || !valid_dtype(u_dtype)) return MUON_EDTYPE;
   if (numel == 0) return MUON_OK;
   if (!W || !U) return MUON_EINVAL;

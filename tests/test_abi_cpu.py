@@ -245,6 +245,32 @@ def test_binding_rejects_host_tensors():
         _abi.dtype_code(torch.zeros(2, dtype=torch.float16))
 
 
+def test_element_count_limit(L):
+    """Counts above MUON_MAX_NUMEL (2^38) are rejected before anything launches,
+    so no launch grid can exceed its 32-bit limit; the limit itself passes
+    validation (the calls below then fail only on their null pointers)."""
+    text = open(HEADER).read()
+    assert re.search(r"#define MUON_MAX_NUMEL \(INT64_C\(1\) << 38\)", text)
+    big = mao.MUON_MAX_NUMEL + 1
+    assert mao.MUON_MAX_NUMEL == 1 << 38
+    assert L.muon_momentum_workspace_bytes(big, 1) == 0
+    assert L.muon_momentum_workspace_bytes(mao.MUON_MAX_NUMEL, 1) > 0
+    assert L.muon_momentum(A1, 1, A2, 1, big, None, 0, 0.9, 0.1, None, None, 0, None) == EINVAL
+    assert L.sign_pack(A1, 1, big, A2, None) == EINVAL
+    assert L.majority_vote(A1, 3, big // 64 + 1, A2, None) == EINVAL
+    assert L.majority_vote(None, 3, mao.MUON_MAX_NUMEL // 64, A2, None) == EINVAL   # null, not size
+    assert L.apply_update(A1, 1, big, A2, 0.1, None) == EINVAL
+    assert L.vote_and_update(A1, 1, big, A2, 3, 0.1, None) == EINVAL
+    assert L.sign_int8(A1, 1, big, A2, None) == EINVAL
+    assert L.sum_int8(A1, 3, big, A2, None) == EINVAL
+    assert L.threshold_pack(A1, big, A2, None) == EINVAL
+    assert L.unpack_signs(A1, big, A2, 1, None) == EINVAL
+    assert L.apply_update_dense(A1, 1, big, A2, 1, 0.1, None) == EINVAL
+    # at the limit the size check passes and the misaligned pointer is what fails
+    assert L.sign_pack(MISALIGNED, 1, mao.MUON_MAX_NUMEL, A2, None) == EALIGN
+    assert L.apply_update_dense(A1, 1, mao.MUON_MAX_NUMEL, MISALIGNED, 1, 0.1, None) == EALIGN
+
+
 def test_int8_exchange_validation(L):
     assert L.sign_int8(A1, 1, -1, A2, None) == EINVAL
     assert L.sign_int8(A1, 5, 16, A2, None) == EDTYPE
