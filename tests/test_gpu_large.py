@@ -78,3 +78,33 @@ def test_int8_sum_and_threshold_past_2_31():
         want_sum = O.sum_int8(S[:, sl].cpu().numpy())
         assert np.array_equal(total[sl].cpu().numpy(), want_sum), (w0, w1)
         assert np.array_equal(from_dev(bits[w0:w1]), O.threshold_pack(want_sum)), (w0, w1)
+
+
+def test_momentum_past_2_31():
+    """a1 on N bf16 entries in two segments that meet 320 entries before 2^31.
+    The state is compared with the oracle on the windows. Each segment's
+    sum of squares is compared with an fp64 reduction of the stored state:
+    a property that holds at any size, because the oracle's one-by-one sum
+    over 2^31 entries is too slow to run here (relative 1e-5, as at small
+    sizes)."""
+    beta, alpha = float(np.float32(0.95)), float(np.float32(0.05))   # the fp32 values the call receives
+    M = _bf16_normal(N, 5)
+    G = _bf16_normal(N, 6)
+    before = {w: (from_dev(_entries(M, *w)).copy(), from_dev(_entries(G, *w)).copy()) for w in WINDOWS}
+    cut = 2 ** 31 - 320
+    offs = torch.tensor([0, cut, N], dtype=torch.int64, device="cuda")
+    sums = torch.zeros(2, dtype=torch.float32, device="cuda")
+    mao.muon_momentum(M, G, beta, alpha, offs, sums)
+    for w in WINDOWS:
+        want = O.momentum(before[w][0], "bf16", before[w][1], "bf16", beta, alpha)
+        assert np.array_equal(from_dev(_entries(M, *w)), want), w
+    ref = [0.0, 0.0]
+    chunk = 1 << 28
+    for i in range(0, N, chunk):
+        j = min(i + chunk, N)
+        for k, (lo, hi) in enumerate([(0, cut), (cut, N)]):
+            a, b = max(i, lo), min(j, hi)
+            if a < b:
+                ref[k] += float((M[a:b].double() ** 2).sum())
+    got = sums.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - np.array(ref)) <= 1e-5 * np.array(ref)), (got, ref)
