@@ -348,7 +348,7 @@ def main():
         "vs_baseline": None,
         "dtype": prec,
         "data": "synthetic",
-        "config": {"workload": f"C{wl.cfg}: {wl.name}", "shape": [rows, cols], "workers": wl.workers,
+        "config": {"workload": wl.name, "shape": [rows, cols], "workers": wl.workers,
                    "ns_steps": wl.ns_steps, "coeffs": list(wl.coeffs), "beta": wl.beta,
                    "eta": wl.eta, "momentum_dtype": wl.m_dtype, "weight_dtype": wl.w_dtype},
         "ns_tflops": ns_tflops,
@@ -572,7 +572,7 @@ def ns_configs(mao, torch, dev, reps=5):
             g_, p_, ap_ = ns_flops(min(r, cc), max(r, cc), c != 0.0)
             flops += wl.ns_steps * (g_ + p_ + ap_)
         tf = flops / (ms * 1e-3) / 1e12
-        out[f"C{cfg}"] = {"workload": wl.name, "matrices": len(wl.shapes), "ms_per_call": ms,
+        out[wl.name] = {"workload": wl.name, "matrices": len(wl.shapes), "ms_per_call": ms,
                           "orthogonalizations_per_s": len(wl.shapes) / (ms * 1e-3),
                           "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
         del M, U, ws

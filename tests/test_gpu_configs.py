@@ -183,7 +183,7 @@ def test_c1_fp32_256_cubic():
     assert np.array_equal(first["vote"], O.majority_vote(first["bits"], wl.numel))
     oracle_U = {k: direction_on(wl, first, k, [0]) for k in range(wl.workers)}
     agreement = sign_agreement(first, oracle_U, entries_of(first, [0]))
-    report("C1", agreement)
+    report(wl.name, agreement)
     assert agreement[0] <= 1e-3 and agreement[2] <= 1e-3
     check_second_step(wl, second, [0])
 
@@ -200,7 +200,7 @@ def test_c2_gpt2_small_layer_set():
     check_vote_update(wl, first)
     oracle_U = {k: direction_on(wl, first, k, sample) for k in range(wl.workers)}
     agreement = sign_agreement(first, oracle_U, entries_of(first, sample))
-    report("C2", agreement)
+    report(wl.name, agreement)
     assert agreement[1] <= 1e-3 and agreement[3] <= 1e-3
     check_second_step(wl, second, sample)
 
@@ -214,7 +214,7 @@ def test_c3_batched_1024_sign_pack():
     check_ns(wl, first, 0, sample)
     agreement = sign_agreement(first, {0: direction_on(wl, first, 0, sample)},
                                entries_of(first, sample))
-    report("C3", agreement)
+    report(wl.name, agreement)
     assert agreement[1] <= 1e-3
     check_second_step(wl, second, [0, 127])
 
@@ -233,7 +233,7 @@ def test_c4_llama_mlp_4096x14336():
         print(f"  worker {k}: NS error {err:.3e}")
         assert err <= TOL_NS["bf16"]
     agreement = sign_agreement(first, oracle_U, np.arange(wl.numel))
-    report("C4", agreement)
+    report(wl.name, agreement)
     assert agreement[1] <= 1e-3 and agreement[3] <= 1e-3
     del oracle_U
     check_second_step(wl, second, [0], nsample=200_000)
@@ -247,7 +247,7 @@ def test_c5_dense_ffn_7168x18432():
     check_vote_update(wl, first, nsample=200_000)
     refs = check_ns(wl, first, 0, [0])
     agreement = sign_agreement(first, {0: refs[0]}, np.arange(wl.numel))
-    report("C5 worker 0", agreement)
+    report(wl.name + ", worker 0", agreement)
     assert agreement[1] <= 1e-3
     del refs
     check_second_step(wl, second, [0], nsample=200_000)
