@@ -2,15 +2,20 @@
 """Throughput of one SignMuon worker step on one MI355X.
 
 A step is one worker's momentum EMA with per-matrix norms, Newton-Schulz
-(5 quintic iterations, bf16 MFMA / fp32 accumulation), sign + 1-bit pack
-(written by the last product's epilogue),
-then the majority vote over the M workers' packed buffers resident on the GPU
-and the update W <- W - eta * vote.  Default workload: one 4096 x 14336 bf16
-matrix (Llama-3-8B MLP shape), 1% heavy columns, M = 7 workers.
+(5 iterations, bf16 MFMA operands / fp32 accumulation; fp32 for the 256 x 256
+workload), sign + 1-bit pack (written by the last product's epilogue where the
+matrix allows it), then the majority vote over the M workers' packed buffers
+resident on the GPU and the update W <- W - eta * vote.  The headline workload
+is one 4096 x 14336 bf16 matrix (Llama-3-8B MLP shape), 1% heavy columns,
+M = 7 workers.
 
-Prints one JSON line.  The timed region records HIP events on the stream
-the kernels run on between every library call, so per-kernel times come from
-the same steps as the headline number.
+The headline times the shipped calls (SignMuonStep: muon_momentum,
+ns_orthogonalize, vote_and_update) with HIP events between them.  The same step
+driven through the stage calls (ns_gram / ns_poly / ns_apply, the kernels
+ns_orthogonalize launches) gives per-kernel times and the roofline.  Then the
+full step of the four other workloads, the elementwise kernels with cold
+caches (the pack and vote GB/s reported at the top level), the extra rows, and
+the CPU oracle timed on the host.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
 """
@@ -74,29 +79,52 @@ def recorded_traffic(kernel: str, rows: int, cols: int):
     return None
 
 
+MFMA_RECORDS = os.path.join(ROOT, "profiles", "signmuon_step_{shape}_mfma_counters.md")
+
+
+def recorded_mfma(kernel: str, rows: int, cols: int):
+    """MFMA busy fraction, sustained clock and L2 hit rate of ``kernel`` from the
+    committed rocprofv3 counter summary (``record:`` lines), or None when there is
+    none for the current kernel sources."""
+    path = MFMA_RECORDS.format(shape=f"{rows}x{cols}")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    for line in open(path):
+        if not line.startswith("record:"):
+            continue
+        fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if fields.get("kernel") == kernel and fields.get("sources") == digest:
+            out = {k: float(v) for k, v in fields.items() if k not in ("kernel", "sources")}
+            out["source"] = os.path.relpath(path, ROOT)
+            return out
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps of each of the other workloads (the 7168 x 18432 one: half)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--unfused-pack", action="store_true",
-                    help="pack the signs with sign_pack after the last product instead of in it")
     ap.add_argument("--unfused-tail", action="store_true",
                     help="run majority_vote and apply_update as two calls instead of vote_and_update")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the extra measurements after the timed steps "
+                    help="skip every measurement after the headline step "
                          "(profiling runs then trace the step's kernels only)")
-    ap.add_argument("--extras", default="cold,int8,reorth,dion,library,configs",
-                    help="comma list of extra measurements to run after the timed steps: "
-                         "cold (elementwise kernels with cold caches), int8 (int8 SUM exchange), "
-                         "reorth (re-orthogonalised update), dion (Dion step), "
-                         "library (vendor GEMM library on the same shapes), "
-                         "configs (ns_orthogonalize on the other workloads' matrix sets)")
+    ap.add_argument("--extras", default="stages,configs,cold,int8,reorth,dion,library",
+                    help="comma list of measurements after the headline step: "
+                         "stages (the same step as stage calls, with HIP events between kernels: "
+                         "per-kernel times and the roofline), configs (the full step of the other "
+                         "workloads), cold (elementwise kernels with cold caches), int8 (int8 SUM "
+                         "exchange), reorth (re-orthogonalised update), dion (Dion step), "
+                         "library (vendor GEMM library on the same shapes)")
     ap.add_argument("--repeat-kernel", default=None,
                     help="profiling aid: after the run, launch one stage N more times "
-                         "(gram|poly|apply|momentum|pack|vote|update|copy:N)")
+                         "(gram|poly|apply|copy:N)")
     return ap.parse_args()
 
 
@@ -108,284 +136,393 @@ def ns_flops(s: int, l: int, c_nonzero: bool):
     return gram, poly, apply
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU: the step has no multi-GPU path; use --gpus 1"}))
-        sys.exit(2)
+def ns_work(wl):
+    """(algorithmic flops, algorithmic HBM bytes if every intermediate streams
+    through memory) of the Newton-Schulz iteration over all of the workload's
+    matrices.  Bytes per iteration: X read by the Gram, A written and read, B
+    written and read, X read and X' written by the product, in the operand type."""
+    es = 2 if wl.precision == "bf16" else 4
+    flops = nbytes = 0
+    for r, c in wl.shapes:
+        s, l = min(r, c), max(r, c)
+        g, p, a = ns_flops(s, l, wl.coeffs[2] != 0.0)
+        flops += wl.ns_steps * (g + p + a)
+        sq = 4 * s * s if wl.coeffs[2] != 0.0 else 2 * s * s
+        nbytes += wl.ns_steps * es * (3 * s * l + sq)
+    return flops, nbytes
 
-    import torch
 
-    import matrix_aware_optimizer_amd as mao
-    from workloads import WORKLOADS, gen_G, gen_M0, gen_W0
+ES = {"bf16": 2, "f32": 4}
 
-    wl = WORKLOADS[args.workload]
-    if len(set(wl.shapes)) != 1 or len(wl.shapes) != 1:
-        # the instrumented step below drives the stage kernels of one matrix shape
-        raise SystemExit("bench.py times single-matrix workloads (4 or 5); others are parity cases")
-    rows, cols = wl.shapes[0]
-    s, l = min(rows, cols), max(rows, cols)
-    if rows > cols or s % mao.MUON_NS_PAD or l % mao.MUON_NS_PAD:
-        raise SystemExit("bench workload must be wide and pad-free")
-    dev = torch.device("cuda", 0)
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
-    prec = wl.precision
-    a, b, c = wl.coeffs
+
+def elementwise_bytes(wl):
+    """Algorithmic bytes of the HBM-bound stages of one step (whole parameter set)."""
+    n = wl.numel
+    nwords = (n + 63) // 64
+    out = {"momentum": n * (2 * ES[wl.m_dtype] + ES[wl.g_dtype]),
+           "pack": n * ES[wl.precision] + nwords * 8,
+           "vote": (wl.workers + 1) * nwords * 8}
+    if wl.w_dtype is not None:
+        out["update"] = 2 * n * ES[wl.w_dtype] + nwords * 8
+        out["vote_update"] = 2 * n * ES[wl.w_dtype] + wl.workers * nwords * 8
+    return out
+
+
+class Events:
+    """HIP events recorded on the current stream (the one every call here runs on)
+    after each named call of one step."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.marks.append((name, ev))
+
+
+def per_call_ms(events_list):
+    """{name: [ms per step]} summed over the calls of that name in each step, plus
+    {name: launches per step}."""
+    per, counts = {}, {}
+    for ev in events_list:
+        prev = ev.marks[0][1]
+        step = {}
+        for name, e in ev.marks[1:]:
+            step[name] = step.get(name, 0.0) + prev.elapsed_time(e)
+            counts[name] = counts.get(name, 0) + 1
+            prev = e
+        for k, v in step.items():
+            per.setdefault(k, []).append(v)
+    return per, {k: v / len(events_list) for k, v in counts.items()}
+
+
+def make_inputs(torch, wl, dev):
+    """W0, M0 and worker 0's G on the device, from the seeded host generators."""
+    from workloads import gen_G, gen_M0, gen_W0
 
     def dev_tensor(arr, dt):
         if dt == "bf16":
             return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(arr).to(dev)
 
+    W0 = gen_W0(wl)
+    return {"W": None if W0 is None else dev_tensor(W0, wl.w_dtype),
+            "M0": dev_tensor(gen_M0(wl), wl.m_dtype),
+            "G0": dev_tensor(gen_G(wl, 0, 0), wl.g_dtype),
+            "G": lambda k: dev_tensor(gen_G(wl, k, 0), wl.g_dtype)}
+
+
+def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
+    """Time the shipped step: SignMuonStep's calls for worker 0 (muon_momentum, then
+    ns_orthogonalize writing the packed signs, plus sign_pack where the signs are not
+    fused), then the vote over the M resident buffers and the update
+    (vote_and_update), HIP events between the calls.  The other M - 1 workers' packed
+    signs are made once beforehand by the same calls on their own gradients."""
     t0 = time.time()
-    W = dev_tensor(gen_W0(wl), wl.w_dtype)
-    M0 = gen_M0(wl)
-    Ms = [dev_tensor(M0, wl.m_dtype) for _ in range(wl.workers)]
-    Gs = [dev_tensor(gen_G(wl, k, 0), wl.g_dtype) for k in range(wl.workers)]
+    inp = make_inputs(torch, wl, dev)
+    step = mao.SignMuonStep(wl.shapes, m_dtype=wl.m_dtype, precision=wl.precision,
+                            coeffs=wl.coeffs, ns_steps=wl.ns_steps, beta=wl.beta, alpha=wl.alpha,
+                            eta=wl.eta, device=dev)
+    bits = step.new_bits(wl.workers)
+    for k in range(1, wl.workers):
+        Mk = inp["M0"].clone()
+        Gk = inp["G"](k)
+        step.worker(Mk, Gk, bits[k])
+        del Mk, Gk
+    M, G, W = inp["M0"].clone(), inp["G0"], inp["W"]
     gen_s = time.time() - t0
+    vote = torch.zeros(step.nwords, dtype=torch.int64, device=dev)
 
-    n = wl.numel
-    nwords = mao.packed_words(n)
-    offsets = torch.tensor([0, n], dtype=torch.int64, device=dev)
-    sumsq = torch.zeros(1, dtype=torch.float32, device=dev)
-    mom_ws = torch.empty(mao.muon_momentum_workspace_bytes(n, 1), dtype=torch.uint8, device=dev)
-    X = [torch.empty((s, l), dtype=tdt[prec], device=dev) for _ in range(2)]
-    A = torch.empty((s, s), dtype=tdt[prec], device=dev)
-    B = torch.empty((s, s), dtype=tdt[prec], device=dev)
-    # split scratch of the stage calls (zeroed once; every call leaves its counters at zero)
-    stage_ws = mao.new_stage_workspace(s, l, 1, prec, dev)
-    fold = prec == "bf16" and wl.m_dtype == "bf16"      # wide and pad-free: checked above
-    fuse_signs = prec == "bf16" and wl.ns_steps > 0 and not args.unfused_pack
-    fuse_tail = not args.unfused_tail
-    bits = torch.zeros((wl.workers, nwords), dtype=torch.int64, device=dev)
-    vote = torch.zeros(nwords, dtype=torch.int64, device=dev)
-
-    def worker(k, ev=None):
-        """a1-a6 for worker k; with `ev`, record an event after every call."""
-        mark = (lambda name: ev.append((name, torch.cuda.Event(enable_timing=True))) or
-                ev[-1][1].record()) if ev is not None else (lambda name: None)
+    def one(ev=None):
+        mark = ev.mark if ev is not None else (lambda name: None)
         mark("start")
-        mao.muon_momentum(Ms[k], Gs[k], wl.beta, wl.alpha, offsets, sumsq, mom_ws)
+        step.momentum(M, G)
+        mark("momentum")
+        if step.signs_per_matrix:
+            step.orthogonalize(M, bits[0])
+            mark("ns")
+        else:
+            step.orthogonalize(M)
+            mark("ns")
+            step.pack(bits[0])
+            mark("pack")
+        if W is not None and wl.workers > 0:
+            if fuse_tail:
+                step.vote_update(W, bits, fused=True)
+                mark("vote_update")
+            else:
+                step.vote_update(W, bits, vote_out=vote)
+                mark("vote_and_update_unfused")
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    step.check()                 # a split product that gave up would make the timing meaningless
+    evs = []
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        ev = Events(torch)
+        one(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step.check()
+    per, launches = per_call_ms(evs)
+    med = {k: float(np.median(v)) for k, v in per.items()}
+    step_ev = [ev.marks[0][1].elapsed_time(ev.marks[-1][1]) for ev in evs]
+    ms = wall * 1e3 / steps
+    flops, ns_bytes = ns_work(wl)
+    eb = elementwise_bytes(wl)
+    peak = PEAK_BF16_TFLOPS if wl.precision == "bf16" else PEAK_F32_TFLOPS
+    ns_ms = med["ns"]
+    tf = flops / (ns_ms * 1e-3) / 1e12
+    hbm_floor_ms = ns_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    mfma_floor_ms = flops / (peak * 1e12) * 1e3
+    out = {"workload": wl.name, "matrices": len(wl.shapes), "workers": wl.workers,
+           "steps": steps, "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+           "event_ms_per_step": float(np.median(step_ev)),
+           "calls_ms": med,
+           "ns": {"ms": ns_ms, "TFLOP/s": tf, "frac_peak": tf / peak,
+                  "peak": "bf16 MFMA" if wl.precision == "bf16" else "fp32 MFMA",
+                  "orthogonalizations_per_s": len(wl.shapes) / (ns_ms * 1e-3),
+                  "algorithmic_flops": flops,
+                  # both floors: the MFMA one, and the HBM one if X, A and B all
+                  # streamed through memory between the products
+                  "mfma_floor_ms": mfma_floor_ms, "hbm_floor_ms": hbm_floor_ms,
+                  "frac_of_floor": max(mfma_floor_ms, hbm_floor_ms) / ns_ms},
+           "input_generation_s": gen_s}
+    gb = {}
+    gb["momentum"] = eb["momentum"] / (med["momentum"] * 1e-3) / 1e9
+    if "pack" in med:
+        gb["pack"] = eb["pack"] / (med["pack"] * 1e-3) / 1e9
+    if "vote_update" in med:
+        gb["vote_update"] = eb["vote_update"] / (med["vote_update"] * 1e-3) / 1e9
+    out["elementwise"] = {k: {"ms": med[k], "GB/s": v, "frac_hbm": v / PEAK_HBM_GBS} for k, v in gb.items()}
+    out["_objects"] = {"step": step, "M": M, "G": G, "W": W, "bits": bits, "vote": vote}
+    return out
+
+
+def stage_sequence(mao, torch, wl, dev, objs, steps, warmup):
+    """The headline step with Newton-Schulz driven through the stage calls (ns_gram,
+    ns_poly, ns_apply, and ns_apply_signs for the last product: the kernels and
+    arguments ns_orthogonalize launches, bit-identical by test), with HIP events
+    between every kernel on the stream they run on: per-kernel times of the timed
+    steps and the roofline of the dominant kernel."""
+    rows, cols = wl.shapes[0]
+    s, l = min(rows, cols), max(rows, cols)
+    prec = wl.precision
+    a, b, c = wl.coeffs
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[prec]
+    step, M, G, W, bits = objs["step"], objs["M"], objs["G"], objs["W"], objs["bits"]
+    X = [torch.empty((1, s, l), dtype=tdt, device=dev) for _ in range(2)]
+    Xlo = torch.empty((1, s, l), dtype=tdt, device=dev)
+    A = torch.empty((1, s, s), dtype=tdt, device=dev)
+    B = torch.empty((1, s, s), dtype=tdt, device=dev)
+    stage_ws = mao.new_stage_workspace(s, l, 1, prec, dev)
+    fold = prec == "bf16" and wl.m_dtype == "bf16"
+    kres = mao.ns_residual_iterations(rows, cols, a, b, c, wl.ns_steps, prec)
+
+    def one(ev=None):
+        mark = ev.mark if ev is not None else (lambda name: None)
+        mark("start")
+        step.momentum(M, G)
         mark("momentum")
         if not fold:
-            mao.ns_normalize(Ms[k].view(rows, cols), sumsq, X[0], prec)
+            mao.ns_normalize(M.view(1, rows, cols), step.sumsq, X[0], prec)
             mark("normalize")
         cur = 0
         for it in range(wl.ns_steps):
-            # a bf16 wide pad-free momentum is read as is by the first iteration,
-            # whose products fold in the Frobenius scaling (as ns_orthogonalize does)
-            Xc, ss = (Ms[k].view(1, rows, cols), sumsq) if fold and it == 0 else (X[cur], None)
+            Xc, ss = (M.view(1, rows, cols), step.sumsq) if fold and it == 0 else (X[cur], None)
+            lo_in = Xlo if 1 <= it <= kres else None
+            lo_out = Xlo if it < kres and it + 1 < wl.ns_steps else None
             mao.ns_gram(Xc, A, prec, sumsq=ss, workspace=stage_ws)
             mark("gram")
             if c != 0.0:
                 mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
                 mark("poly")
             Bm, alpha = (B, 1.0) if c != 0.0 else (A, b)
-            if fuse_signs and it + 1 == wl.ns_steps:
-                # the last product packs the signs of its values (nothing else of
-                # the direction is needed by the vote)
-                mao.ns_apply_signs(Bm, Xc, None, bits[k], a, alpha, prec, sumsq=ss, workspace=stage_ws)
+            if it + 1 == wl.ns_steps:
+                mao.ns_apply_signs(Bm, Xc, None, bits[0], a, alpha, prec, sumsq=ss, workspace=stage_ws,
+                                   X_lo=lo_in)
                 mark("apply_signs")
             else:
-                mao.ns_apply(Bm, Xc, X[1 - cur], a, alpha, prec, sumsq=ss, workspace=stage_ws)
+                mao.ns_apply(Bm, Xc, X[1 - cur], a, alpha, prec, sumsq=ss, workspace=stage_ws,
+                             X_lo=lo_in, Xout_lo=lo_out)
                 mark("apply")
             cur = 1 - cur
-        if not fuse_signs or wl.ns_steps == 0:
-            mao.sign_pack(X[cur], bits[k])
-            mark("pack")
+        step.vote_update(W, bits, fused=True)
+        mark("vote_update")
 
-    def tail(ev=None):
-        def mark(name):
-            if ev is not None:
-                ev.append((name, torch.cuda.Event(enable_timing=True)))
-                ev[-1][1].record()
-        if fuse_tail:
-            # a7 + a8 in one pass: the vote is never written (nothing else reads it)
-            mao.vote_and_update(W, bits, wl.eta)
-            mark("vote_update")
-        else:
-            mao.majority_vote(bits, vote)
-            mark("vote")
-            mao.apply_update(W, vote, wl.eta)
-            mark("update")
-
-    # the other workers' packed signs, resident on the GPU (what an all-gather would deliver)
-    for k in range(1, wl.workers):
-        worker(k)
+    for _ in range(warmup):
+        one()
     torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        worker(0)
-        tail()
-    torch.cuda.synchronize()
-
-    cur_final = wl.ns_steps % 2          # X buffer holding the final direction
-    events = []
+    evs = []
     t_start = time.perf_counter()
-    for _ in range(args.steps):
-        ev = []
-        worker(0, ev)
-        tail(ev)
-        events.append(ev)
+    for _ in range(steps):
+        ev = Events(torch)
+        one(ev)
+        evs.append(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-
-    # per-kernel times from the events of the timed steps
-    per = {}
-    step_ms = []
-    for ev in events:
-        prev = ev[0][1]
-        for name, e in ev[1:]:
-            per.setdefault(name, []).append(prev.elapsed_time(e))
-            prev = e
-        step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
-    launches = {k: len(v) / args.steps for k, v in per.items()}
-    avg = {k: float(np.mean(v)) for k, v in per.items()}            # ms per launch
-    total = {k: avg[k] * launches[k] for k in avg}                  # ms per step
-
-    ms_per_step = wall * 1e3 / args.steps
+    mao.ns_workspace_status(stage_ws)
+    per, launches = per_call_ms(evs)
+    # per launch: the step's total for a name over its launches per step
+    avg = {k: float(np.mean(v)) / launches[k] for k, v in per.items()}
+    total = {k: float(np.mean(v)) for k, v in per.items()}
     gram_f, poly_f, apply_f = ns_flops(s, l, c != 0.0)
-    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply", "apply_signs") if k in total)
-    ns_flop = wl.ns_steps * (gram_f + poly_f + apply_f)
     peak = PEAK_BF16_TFLOPS if prec == "bf16" else PEAK_F32_TFLOPS
-    ns_tflops = ns_flop / (ns_ms * 1e-3) / 1e12
-
-    es = {"bf16": 2, "f32": 4}
-    bytes_momentum = n * (2 * es[wl.m_dtype] + es[wl.g_dtype])
-    bytes_pack = n * es[prec] + nwords * 8
-    bytes_vote = (wl.workers + 1) * nwords * 8
-    bytes_update = 2 * n * es[wl.w_dtype] + nwords * 8
-
-    def gbs(nbytes, key):
-        return nbytes / (avg[key] * 1e-3) / 1e9
-
-    kernels = {
-        "momentum": {"ms": avg["momentum"], "GB/s": gbs(bytes_momentum, "momentum")},
-        "gram": {"ms": avg["gram"], "TFLOP/s": gram_f / (avg["gram"] * 1e-3) / 1e12},
-        "apply": {"ms": avg["apply"], "TFLOP/s": apply_f / (avg["apply"] * 1e-3) / 1e12},
-    }
-
-    def standalone(fn, reps=20):
-        """Average time of `reps` back-to-back calls (after 3 untimed), for a
-        kernel the step runs fused into another."""
-        for _ in range(3):
-            fn()
-        t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0_.record()
-        for _ in range(reps):
-            fn()
-        t1_.record()
-        torch.cuda.synchronize()
-        return t0_.elapsed_time(t1_) / reps
-
-    bytes_vote_update = 2 * n * es[wl.w_dtype] + wl.workers * nwords * 8
-    if "vote_update" in avg:
-        kernels["vote_update"] = {"ms": avg["vote_update"], "GB/s": gbs(bytes_vote_update, "vote_update")}
-    for key, fn, nb in (("vote", lambda: mao.majority_vote(bits, vote), bytes_vote),
-                        ("update", lambda: mao.apply_update(W, vote, wl.eta), bytes_update)):
-        if key in avg:
-            kernels[key] = {"ms": avg[key], "GB/s": gbs(nb, key)}
-        else:
-            # fused into vote_and_update in the step; timed on its own here
-            avg[key] = standalone(fn)
-            launches[key] = 0.0
-            kernels[key] = {"ms": avg[key], "GB/s": gbs(nb, key), "fused_in_step": True}
+    eb = elementwise_bytes(wl)
+    kernels = {}
+    for k, fl in (("gram", gram_f), ("poly", poly_f), ("apply", apply_f), ("apply_signs", apply_f)):
+        if k in avg:
+            tf = fl / (avg[k] * 1e-3) / 1e12
+            kernels[k] = {"ms": avg[k], "TFLOP/s": tf, "frac_peak": tf / peak, "launches_per_step": launches[k]}
+    for k in ("momentum", "vote_update"):
+        gbs = eb[k] / (avg[k] * 1e-3) / 1e9
+        kernels[k] = {"ms": avg[k], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "launches_per_step": launches[k]}
     if "normalize" in avg:
-        kernels["normalize"] = {"ms": avg["normalize"],
-                                "GB/s": gbs(n * (es[wl.m_dtype] + es[prec]), "normalize")}
-    if "poly" in avg:
-        kernels["poly"] = {"ms": avg["poly"], "TFLOP/s": poly_f / (avg["poly"] * 1e-3) / 1e12}
-    if "apply_signs" in avg:
-        kernels["apply_signs"] = {"ms": avg["apply_signs"],
-                                  "TFLOP/s": apply_f / (avg["apply_signs"] * 1e-3) / 1e12}
-    if "pack" in avg:
-        kernels["pack"] = {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack")}
-    else:
-        # fused into the last product in the step; the standalone kernel (the
-        # path of tall or fp32 problems) is timed here on the same buffers
-        avg["pack"] = standalone(lambda: mao.sign_pack(X[0], bits[0]))
-        launches["pack"] = 0.0
-        kernels["pack"] = {"ms": avg["pack"], "GB/s": gbs(bytes_pack, "pack"), "fused_in_step": True}
-    for k in kernels:
-        kernels[k]["launches_per_step"] = launches[k]
-        if "GB/s" in kernels[k]:
-            kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
-        else:
-            kernels[k]["frac_peak"] = kernels[k]["TFLOP/s"] / peak
+        gbs = wl.numel * (ES[wl.m_dtype] + ES[prec]) / (avg["normalize"] * 1e-3) / 1e9
+        kernels["normalize"] = {"ms": avg["normalize"], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply", "apply_signs") if k in total)
+    flops, _ = ns_work(wl)
+    return {"ms_per_step": wall * 1e3 / steps, "ns_ms": ns_ms,
+            "ns_TFLOP/s": flops / (ns_ms * 1e-3) / 1e12, "kernels": kernels, "total_ms": total,
+            "_buffers": {"X": X, "A": A, "B": B, "stage_ws": stage_ws}}
 
+
+def roofline_of(kernels, total, rows, cols, wl):
+    """Roofline of the kernel with the most time per step (from the stage sequence)."""
     dominant = max(total, key=total.get)
-    counters = recorded_traffic({"pack": "sign_pack", "vote": "majority_vote"}.get(dominant, dominant),
-                                rows, cols)
-    traffic = None if counters is None else counters["bytes"]
-    dom_flops = {"gram": gram_f, "poly": poly_f, "apply": apply_f}.get(dominant)
-    if dom_flops is not None:
-        ach = dom_flops / (avg[dominant] * 1e-3) / 1e12
-        roofline = {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": peak,
-                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": traffic,
-                    "per_launch_flops": dom_flops, "avg_launch_ms": avg[dominant]}
+    peak = PEAK_BF16_TFLOPS if wl.precision == "bf16" else PEAK_F32_TFLOPS
+    k = kernels[dominant]
+    counters = recorded_traffic(dominant, rows, cols)
+    if "TFLOP/s" in k:
+        s, l = min(rows, cols), max(rows, cols)
+        fl = dict(zip(("gram", "poly", "apply"), ns_flops(s, l, wl.coeffs[2] != 0.0)))
+        fl["apply_signs"] = fl["apply"]
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": k["TFLOP/s"], "peak": peak,
+                "unit": "TFLOP/s", "frac": k["TFLOP/s"] / peak,
+                "traffic": None if counters is None else counters["bytes"],
+                "per_launch_flops": fl[dominant], "avg_launch_ms": k["ms"]}
     else:
-        nb = {"momentum": bytes_momentum, "pack": bytes_pack, "vote": bytes_vote,
-              "update": bytes_update, "vote_update": bytes_vote_update}[dominant]
-        ach = gbs(nb, dominant)
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
-                    "per_launch_bytes": nb, "avg_launch_ms": avg[dominant]}
-
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": k["GB/s"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": k["GB/s"] / PEAK_HBM_GBS,
+                "traffic": None if counters is None else counters["bytes"], "avg_launch_ms": k["ms"]}
     if counters is not None:
-        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
-        roofline["traffic_detail"] = counters
+        roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
+        roof["traffic_detail"] = counters
+    util = recorded_mfma(dominant, rows, cols)
+    if util is not None:
+        roof["mfma_counters"] = util
+    return roof
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures one GPU: every GPU box of this setup has one, "
+                                   "and the step's exchange between GPUs is not built; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import matrix_aware_optimizer_amd as mao
+    from workloads import WORKLOADS
+
+    dev = torch.device("cuda", 0)
+    wl = WORKLOADS[args.workload]
+    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+
+    head = product_step(mao, torch, wl, dev, args.steps, args.warmup, fuse_tail=not args.unfused_tail)
+    objs = head.pop("_objects")
+    rows, cols = wl.shapes[0]
+    peak = PEAK_BF16_TFLOPS if wl.precision == "bf16" else PEAK_F32_TFLOPS
     result = {
         "metric": METRIC,
-        "value": 1e3 / ms_per_step,
+        "value": head["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": prec,
+        "dtype": wl.precision,
         "data": "synthetic",
-        "config": {"workload": wl.name, "shape": [rows, cols], "workers": wl.workers,
-                   "ns_steps": wl.ns_steps, "coeffs": list(wl.coeffs), "beta": wl.beta,
-                   "eta": wl.eta, "momentum_dtype": wl.m_dtype, "weight_dtype": wl.w_dtype},
-        "ns_tflops": ns_tflops,
-        "ns_frac_bf16_peak": ns_tflops / peak,
-        "orthogonalizations_per_s": 1e3 / ns_ms,
-        "pack_gbs": kernels["pack"]["GB/s"],
-        "vote_gbs": kernels["vote"]["GB/s"],
-        "event_ms_per_step": float(np.median(step_ms)),
-        "kernels": kernels,
-        "roofline": roofline,
-        "input_generation_s": gen_s,
+        "config": {"workload": wl.name, "shapes": sorted(set(wl.shapes)), "matrices": len(wl.shapes),
+                   "workers": wl.workers, "ns_steps": wl.ns_steps, "coeffs": list(wl.coeffs),
+                   "beta": wl.beta, "eta": wl.eta, "momentum_dtype": wl.m_dtype,
+                   "weight_dtype": wl.w_dtype, "path": "SignMuonStep (product calls)"},
+        "ns_tflops": head["ns"]["TFLOP/s"],
+        "ns_frac_bf16_peak": head["ns"]["TFLOP/s"] / PEAK_BF16_TFLOPS,
+        "orthogonalizations_per_s": head["ns"]["orthogonalizations_per_s"],
+        "step": head,
     }
-    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    single = len(wl.shapes) == 1 and rows <= cols and rows % mao.MUON_NS_PAD == 0 \
+        and cols % mao.MUON_NS_PAD == 0 and wl.w_dtype is not None
+    stages = None
+    if "stages" in extras and single:
+        stages = stage_sequence(mao, torch, wl, dev, objs, args.steps, args.warmup)
+        bufs = stages.pop("_buffers")
+        result["stage_sequence"] = stages
+        result["kernels"] = stages["kernels"]
+        result["roofline"] = roofline_of(stages["kernels"], stages["total_ms"], rows, cols, wl)
+    else:
+        # no per-kernel events: the whole orthogonalisation against the MFMA peak
+        result["roofline"] = {"kernel": "ns_orthogonalize (all launches)", "bound": "mfma",
+                              "achieved": head["ns"]["TFLOP/s"], "peak": peak, "unit": "TFLOP/s",
+                              "frac": head["ns"]["frac_peak"], "traffic": None}
+
     if "cold" in extras:
-        result["kernels_cold"] = cold_elementwise(mao, torch, wl, Ms[0], Gs[0], W, X[cur_final], bits, vote,
-                                                  offsets, sumsq, mom_ws, dev)
-    if "int8" in extras:
-        result["int8_exchange"] = int8_exchange(mao, torch, X[cur_final], wl, n, nwords, dev)
-    if "reorth" in extras:
+        cold = cold_elementwise(mao, torch, wl, objs, dev)
+        result["kernels_cold"] = cold
+        result["pack_gbs"] = cold["pack"]["GB/s"]
+        result["vote_gbs"] = cold["vote"]["GB/s"]
+    if "configs" in extras:
+        cfgs = {}
+        del objs
+        for cfg in (1, 2, 3, 4, 5):
+            if cfg == args.workload:
+                continue
+            other = WORKLOADS[cfg]
+            n_steps = max(2, args.config_steps // (2 if cfg == 5 else 1))
+            r = product_step(mao, torch, other, dev, n_steps, 2)
+            r.pop("_objects")
+            cfgs[other.name] = r
+            torch.cuda.empty_cache()
+        cfgs[wl.name] = {k: v for k, v in head.items()}
+        result["configs"] = cfgs
+        objs = None
+    if "int8" in extras and stages is not None:
+        result["int8_exchange"] = int8_exchange(mao, torch, bufs["X"][0], wl, wl.numel,
+                                                mao.packed_words(wl.numel), dev)
+    if "reorth" in extras and single:
+        vote = torch.zeros(mao.packed_words(wl.numel), dtype=torch.int64, device=dev)
+        W = make_inputs(torch, wl, dev)["W"]
+        bits = torch.randint(-2 ** 62, 2 ** 62, (1, vote.numel()), dtype=torch.int64, device=dev)
+        mao.majority_vote(bits, vote)
         result["reorthogonalized_update"] = reorth_update(mao, torch, wl, W, vote, dev)
     if "dion" in extras:
         result["dion"] = dion_bench(mao, torch, dev)
-    if "configs" in extras:
-        result["ns_configs"] = ns_configs(mao, torch, dev)
-    if "library" in extras and prec == "bf16":
-        result["library_reference"] = library_reference(torch, avg, s, l, dev)
+    if "library" in extras and stages is not None and wl.precision == "bf16":
+        avg = {k: v["ms"] for k, v in stages["kernels"].items()}
+        result["library_reference"] = library_reference(torch, avg, min(rows, cols), max(rows, cols), dev)
 
-    if args.repeat_kernel:
+    if args.repeat_kernel and stages is not None:
         name, _, cnt = args.repeat_kernel.partition(":")
         cnt = int(cnt or 10)
+        a, b, c = wl.coeffs
+        X, A, B, stage_ws = bufs["X"], bufs["A"], bufs["B"], bufs["stage_ws"]
         for _ in range(cnt):
             if name == "gram":
-                mao.ns_gram(X[0], A, prec, workspace=stage_ws)
+                mao.ns_gram(X[0], A, wl.precision, workspace=stage_ws)
             elif name == "poly":
-                mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
+                mao.ns_poly(A, B, b, c, wl.precision, workspace=stage_ws)
             elif name == "apply":
-                mao.ns_apply(B, X[0], X[1], a, 1.0, prec, workspace=stage_ws)
+                mao.ns_apply(B, X[0], X[1], a, 1.0, wl.precision, workspace=stage_ws)
             elif name == "copy":
                 X[1].copy_(X[0])
         torch.cuda.synchronize()
@@ -395,26 +532,28 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cold_elementwise(mao, torch, wl, M, G, W, U, bits, vote, offsets, sumsq, mom_ws, dev, reps=5):
+def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
     """The HBM-bound kernels with cold caches: before each timed call a 1 GiB buffer
     is read (a sum over it), which replaces the 256 MB Infinity Cache's contents with
     clean lines, so every operand comes from HBM and no write-back of someone else's
     data is charged to the kernel.  HIP events bracket the call alone, on the stream
-    it runs on."""
+    it runs on; the median of ``reps`` calls."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)        # 1 GiB
-    n, nwords = wl.numel, mao.packed_words(wl.numel)
-    es = {"bf16": 2, "f32": 4}
+    step, M, G, W, bits, vote = (objs[k] for k in ("step", "M", "G", "W", "bits", "vote"))
+    U = step.U
+    U.copy_(M.to(U.dtype))                  # a direction-like operand for the standalone pack
+    eb = elementwise_bytes(wl)
     calls = {
-        "momentum": (lambda: mao.muon_momentum(M, G, wl.beta, wl.alpha, offsets, sumsq, mom_ws),
-                     n * (2 * es[wl.m_dtype] + es[wl.g_dtype])),
-        "pack": (lambda: mao.sign_pack(U, bits[0]), n * es[wl.precision] + nwords * 8),
-        "vote": (lambda: mao.majority_vote(bits, vote), (wl.workers + 1) * nwords * 8),
-        "update": (lambda: mao.apply_update(W, vote, wl.eta), 2 * n * es[wl.w_dtype] + nwords * 8),
-        "vote_update": (lambda: mao.vote_and_update(W, bits, wl.eta),
-                        2 * n * es[wl.w_dtype] + wl.workers * nwords * 8),
+        "momentum": (lambda: step.momentum(M, G), eb["momentum"]),
+        "pack": (lambda: mao.sign_pack(U, bits[0]), eb["pack"]),
+        "vote": (lambda: mao.majority_vote(bits, vote), eb["vote"]),
     }
+    if W is not None:
+        calls["update"] = (lambda: mao.apply_update(W, vote, wl.eta), eb["update"])
+        calls["vote_update"] = (lambda: mao.vote_and_update(W, bits, wl.eta), eb["vote_update"])
     out = {}
     for name, (fn, nbytes) in calls.items():
+        fn()
         times = []
         for _ in range(reps):
             flush.sum()
@@ -531,54 +670,6 @@ def dion_bench(mao, torch, dev, reps=5):
     return out
 
 
-def ns_configs(mao, torch, dev, reps=5):
-    """ns_orthogonalize alone on the other workloads' matrix sets, as one call per
-    set (the library batches equal shapes): the GPT-2-small layer set (48
-    matrices, 4 shapes), 128 batched 1024 x 1024, and 7168 x 18432 (fp32 momentum),
-    5 quintic steps.  The per-matrix sums of squares are passed in, as the
-    optimizer step passes muon_momentum's (computed once here, before timing).
-    Seeded normal inputs; HIP events on the stream the call runs on."""
-    from workloads import WORKLOADS
-    out = {}
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1234)
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
-    for cfg in (2, 3, 5):
-        wl = WORKLOADS[cfg]
-        offs = wl.offsets
-        M = torch.randn(wl.numel, generator=gen, device=dev).to(tdt[wl.m_dtype])
-        U = torch.empty(wl.numel, dtype=tdt[wl.precision], device=dev)
-        offs_d = torch.from_numpy(offs).to(dev)
-        sums = torch.zeros(len(wl.shapes), dtype=torch.float32, device=dev)
-        mws = torch.empty(mao.muon_momentum_workspace_bytes(wl.numel, len(wl.shapes)), dtype=torch.uint8,
-                          device=dev)
-        # beta = 1, alpha = 0 leaves M as it is and writes its sums of squares
-        mao.muon_momentum(M, M, 1.0, 0.0, offs_d, sums, mws)
-        probs = [(M[offs[j]:offs[j + 1]].view(r, c), U[offs[j]:offs[j + 1]].view(r, c), sums[j:j + 1])
-                 for j, (r, c) in enumerate(wl.shapes)]
-        ws = torch.empty(max(mao.ns_workspace_bytes(probs, wl.precision), 1), dtype=torch.uint8, device=dev)
-        a, b, c = wl.coeffs
-        mao.ns_orthogonalize(probs, a, b, c, wl.ns_steps, wl.precision, ws)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(reps):
-            mao.ns_orthogonalize(probs, a, b, c, wl.ns_steps, wl.precision, ws)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / reps
-        flops = 0
-        for r, cc in wl.shapes:
-            g_, p_, ap_ = ns_flops(min(r, cc), max(r, cc), c != 0.0)
-            flops += wl.ns_steps * (g_ + p_ + ap_)
-        tf = flops / (ms * 1e-3) / 1e12
-        out[wl.name] = {"workload": wl.name, "matrices": len(wl.shapes), "ms_per_call": ms,
-                          "orthogonalizations_per_s": len(wl.shapes) / (ms * 1e-3),
-                          "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
-        del M, U, ws
-    return out
-
-
 def library_reference(torch, avg, s, l, dev, reps=10):
     """Context only, not on the product path: the vendor GEMM library (hipBLASLt,
     reached through torch.matmul on contiguous bf16 operands) timed on the shapes
@@ -619,9 +710,36 @@ def library_reference(torch, avg, s, l, dev, reps=10):
     return out
 
 
+def _numpy_f32_step(wl, W0, M0, G, others):
+    """The same worker step in numpy float32 (the CPU baseline comparable in
+    precision to the GPU's fp32 accumulation; not the oracle): EMA, Frobenius
+    scaling, the iteration on the short side, sign and packing (numpy.packbits,
+    little bit order), the vote over the M packed buffers and the update."""
+    rows, cols = wl.shapes[0]
+    a, b, c = (np.float32(x) for x in wl.coeffs)
+    to32 = (lambda x, dt: (x.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else x)
+    Mn = np.float32(wl.beta) * to32(M0, wl.m_dtype) + np.float32(wl.alpha) * to32(G, wl.g_dtype)
+    X = Mn.reshape(rows, cols)
+    X = (X.T if rows > cols else X) / np.float32(np.sqrt(np.sum(Mn.astype(np.float64) ** 2)))
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    for _ in range(wl.ns_steps):
+        A = X @ X.T
+        Bm = b * A + c * (A @ A)
+        X = a * X + Bm @ X
+    U = X.T if rows > cols else X
+    mine = np.packbits(~(U.ravel() < 0), bitorder="little")
+    buffers = np.stack([mine] + [others] * (wl.workers - 1))
+    counts = np.unpackbits(buffers, axis=1, bitorder="little")[:, :wl.numel].sum(0, dtype=np.int32)
+    vote = 2 * counts >= wl.workers
+    return to32(W0, wl.w_dtype) - np.float32(wl.eta) * np.where(vote, np.float32(1), np.float32(-1))
+
+
 def cpu_baseline(wl):
-    """The fp64 oracle on the host cores: the elementwise stages on the whole matrix
-    and one of the Newton-Schulz iterations, scaled to a full worker step."""
+    """The fp64 oracle on the host cores, one whole worker step on the headline
+    workload, measured (nothing extrapolated): momentum, Newton-Schulz with all its
+    iterations, sign and packing, the vote over M packed buffers (worker 0's and M - 1
+    copies of it: the vote costs the same whatever the bits), the update.  Beside it
+    the same step in numpy float32 (not the oracle)."""
     import oracle.muon_oracle as O
     from workloads import gen_G, gen_M0, gen_W0
 
@@ -632,29 +750,34 @@ def cpu_baseline(wl):
         threads = len(os.sched_getaffinity(0))
     rows, cols = wl.shapes[0]
     W0, M0, G = gen_W0(wl), gen_M0(wl), gen_G(wl, 0, 0)
-    a, b, c = wl.coeffs
     t0 = time.perf_counter()
     Mn = O.momentum(M0, wl.m_dtype, G, wl.g_dtype, wl.beta, wl.alpha)
-    Mf = O.decode(Mn, wl.m_dtype).reshape(rows, cols)
-    X = O.frobenius_normalize(Mf)
-    X = X.T if rows > cols else X
-    t_elem0 = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    X1 = O.ns_iterate(X, a, b, c, 1)
-    t_iter = time.perf_counter() - t1
-    t2 = time.perf_counter()
-    words = O.sign_pack(X1)
-    packed = np.stack([words] * wl.workers)
-    vote = O.majority_vote(packed, wl.numel)
+    U = O.newton_schulz(O.decode(Mn, wl.m_dtype).reshape(rows, cols), *wl.coeffs, wl.ns_steps)
+    words = O.sign_pack(U.ravel())
+    vote = O.majority_vote(np.stack([words] * wl.workers), wl.numel)
     O.apply_update(W0, wl.w_dtype, vote, wl.eta)
-    t_elem1 = time.perf_counter() - t2
-    est = t_elem0 + t_elem1 + wl.ns_steps * t_iter
-    return {"value": 1.0 / est, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle on the full {rows}x{cols} matrix: momentum, norm, sign/pack, "
-                      f"{wl.workers}-way vote, update, and 1 of {wl.ns_steps} Newton-Schulz "
-                      f"iterations (timed {t_iter:.2f} s), step time = elementwise + "
-                      f"{wl.ns_steps} x iteration = {est:.2f} s",
-            "cpu": platform.processor() or platform.machine()}
+    t_oracle = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    _numpy_f32_step(wl, W0, M0, G, np.packbits(np.ones(wl.numel, bool), bitorder="little"))
+    t_f32 = time.perf_counter() - t1
+    return {"value": 1.0 / t_oracle, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one whole fp64 oracle worker step on the full {rows}x{cols} workload "
+                      f"({wl.ns_steps} Newton-Schulz iterations, {wl.workers}-way vote over copies of "
+                      f"worker 0's bits, update): {t_oracle:.2f} s measured",
+            "numpy_f32": {"value": 1.0 / t_f32, "unit": "steps/s", "seconds": t_f32,
+                          "sample": "the same step in numpy float32 (not the oracle)"},
+            "cpu": platform.processor() or platform.machine(),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 if __name__ == "__main__":

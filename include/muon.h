@@ -51,7 +51,10 @@ enum muon_status {
   MUON_EDTYPE = -2,     /* unsupported dtype / precision code               */
   MUON_EALIGN = -3,     /* a device pointer is not 16-byte aligned          */
   MUON_EWORKSPACE = -4, /* workspace missing or smaller than the query says */
-  MUON_ELAUNCH = -5     /* the HIP runtime rejected a kernel launch         */
+  MUON_ELAUNCH = -5,    /* the HIP runtime rejected a kernel launch         */
+  MUON_ESPLIT = -6      /* (ns_workspace_status) a split product's second
+                           half gave up waiting for the first half's partial
+                           tile; that tile of the output was not written     */
 };
 
 /* Newton-Schulz working dimensions are padded up to a multiple of this. */
@@ -119,7 +122,13 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
  *   computed and mirrored into the full matrix.
  *
  *   precision  MUON_BF16: bf16 MFMA operands, fp32 accumulation, X, A and B
- *              held in bf16 between products.  MUON_F32: fp32 throughout.
+ *              held in bf16 between products; the outputs X_1 .. X_k of the
+ *              first k iterations also keep their bf16 rounding residual,
+ *              which the next iteration adds to its a X term (X + residual
+ *              holds X to about 16 significant bits): rounding X costs the
+ *              most accuracy while the singular values are still small.  k
+ *              is ns_residual_iterations(rows, cols, a, b, c, steps, ...).
+ *              MUON_F32: fp32 throughout.
  *   problem    M (device, rows x cols of m_dtype), U (device, rows x cols of
  *              u_dtype, may alias nothing else), sumsq (device float holding
  *              sum(M^2), e.g. from muon_momentum, or NULL to compute it),
@@ -149,7 +158,10 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
  *   of the CUs, as the two 256 x 128 column halves of every off-diagonal tile
  *   plus the lower half of every diagonal tile.  Results therefore depend on
  *   the device's CU count only through these choices, and are deterministic
- *   on one device.
+ *   on one device.  The second half's wait for the first is bounded
+ *   (muon_set_split_wait_limit); a wait that runs out leaves its tile
+ *   unwritten and sets an error word in the workspace, which
+ *   ns_workspace_status reports.
  * ------------------------------------------------------------------------- */
 typedef struct muon_ns_problem {
   const void* M;
@@ -167,6 +179,45 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
                      int steps, int precision, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* ns_residual_iterations -- the k above: how many leading iterations of
+ *   ns_orthogonalize keep the bf16 residual of their output, for a rows x cols
+ *   problem with these coefficients and steps.  With the residual, the
+ *   rounding error of X reaches the next iterate through the slope of B X
+ *   alone, p'(x) - a, instead of the slope p'(x) of the scalar map
+ *   p(x) = a x + b x^3 + c x^5, which pays while p'(x) >= a / 2.  k counts
+ *   the iterates p(x0), p(p(x0)), ... of x0 = 1/sqrt(min(rows, cols)) (the
+ *   typical normalised singular value of a well-conditioned matrix) that
+ *   stay below the first x > 0 with p'(x) <= a / 2, at most steps - 1.
+ *   Quintic (3.4445, -4.7750, 2.0315), 5 steps: 0 below a short side of 87,
+ *   1 up to 1020, 2 from 1021.  Returns k >= 0 (0 for MUON_F32, or a <= 0),
+ *   or MUON_EINVAL / MUON_EDTYPE. */
+int ns_residual_iterations(int64_t rows, int64_t cols, float a, float b, float c, int steps,
+                           int precision);
+
+/* ns_workspace_status -- did a split product give up?
+ *   Enqueues a copy of the workspace's error word to the host on `stream`,
+ *   synchronises `stream`, and returns MUON_ESPLIT if a split product that
+ *   used this workspace gave up waiting for its other half since the word
+ *   was last cleared, else MUON_OK.  ns_orthogonalize clears the word (and
+ *   the arrival counters) at the start of every call, so after it the status
+ *   describes that call; a stage-call workspace keeps the word until the
+ *   caller zeroes its first 1024 bytes again, which it must do after
+ *   MUON_ESPLIT (an abandoned tile leaves its counter set).
+ *   workspace  device, a workspace of ns_orthogonalize or of the stage calls
+ *              (at least 1024 bytes, else MUON_EINVAL; 16-byte aligned).
+ *   Copy or synchronisation failures return MUON_ELAUNCH.
+ *
+ * muon_set_split_wait_limit / muon_get_split_wait_limit -- the number of
+ *   polls (each about 128 cycles) a split product's second half makes for
+ *   its partner before it gives up; process-wide, read at each launch.
+ *   Default 2^22 (seconds: far beyond the microseconds the partner needs,
+ *   which depends on no other workgroup).  polls >= 0, else MUON_EINVAL.
+ *   0 makes every split second half give up at once: a way to exercise the
+ *   error path with every kernel still exiting normally. */
+int ns_workspace_status(const void* workspace, size_t ws_bytes, void* stream);
+int muon_set_split_wait_limit(int polls);
+int muon_get_split_wait_limit(void);
+
 /* Stage calls of the iteration, on padded short-side working buffers.
  * s and l are the padded short and long sides (multiples of MUON_NS_PAD);
  * X is [batch][s][l], A and B are [batch][s][s]; element type is bf16 for
@@ -179,7 +230,12 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
  * ns_gram      (a3): A[b] = X[b] X[b]^T.
  * ns_poly      (a4): B[b] = b A[b] + c A[b] A[b]   (A symmetric).
  * ns_apply     (a5): Xout[b] = a X[b] + alpha B[b] X[b]  (X is not read as an
- *   addend when a == 0).
+ *   addend when a == 0).  bf16 residuals (MUON_BF16 only, else MUON_EDTYPE;
+ *   each may be NULL): with X_lo ([batch][s][l] bf16) the addend is
+ *   a (X + X_lo); Xout_lo receives bf16(v - bf16(v)) for each stored value
+ *   v of Xout, so that Xout + Xout_lo holds v to about 16 significant bits.
+ *   X_lo and Xout_lo may be the same buffer (each entry is read before it is
+ *   rewritten, by the same lane); neither may alias X or Xout.
  * One iteration is ns_gram, ns_poly(b, c), ns_apply(a, alpha = 1), or with
  * c == 0 ns_gram, ns_apply(a, alpha = b).
  *
@@ -196,8 +252,9 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
  * and ns_apply take the same workspace (for one call sequence) and currently
  * never split.  It must hold ns_stage_workspace_bytes(s, l, batch, precision)
  * bytes (0 when nothing splits: then it is not used), be 16-byte aligned,
- * and its first 512 bytes must be zero on the first call: they are arrival
- * counters that every call leaves at zero.  One workspace sized for
+ * and its first 1024 bytes must be zero on the first call: they are arrival
+ * counters that every successful call leaves at zero, and the error word of
+ * ns_workspace_status.  One workspace sized for
  * (s, l, batch) serves ns_gram(s, l), ns_poly(s) and ns_apply(s, l) on that
  * batch; calls sharing it must not overlap in time.  Too small:
  * MUON_EWORKSPACE. */
@@ -208,9 +265,9 @@ int ns_gram(const void* X, void* A, int64_t s, int64_t l, int64_t batch, int pre
             const float* sumsq, void* workspace, size_t ws_bytes, void* stream);
 int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c,
             int precision, void* workspace, size_t ws_bytes, void* stream);
-int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch,
-             float a, float alpha, int precision, const float* sumsq, void* workspace,
-             size_t ws_bytes, void* stream);
+int ns_apply(const void* B, const void* X, const void* X_lo, void* Xout, void* Xout_lo, int64_t s,
+             int64_t l, int64_t batch, float a, float alpha, int precision, const float* sumsq,
+             void* workspace, size_t ws_bytes, void* stream);
 
 /* ns_apply_signs (a5 + a6): ns_apply with MUON_BF16 precision (else
  *   MUON_EDTYPE) that also writes the packed signs of Xout, as sign_pack
@@ -218,10 +275,11 @@ int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int
  *   [batch][s * l / 64] words, entry b holding Xout[b] (s x l row-major) with
  *   bit i of the flat index in word i >> 6, bit i & 63.  Xout may be NULL:
  *   then only the signs are written (the last iteration of SignMuon needs
- *   nothing else).  Other arguments, errors and the workspace as ns_apply. */
-int ns_apply_signs(const void* B, const void* X, void* Xout, uint64_t* bits, int64_t s, int64_t l,
-                   int64_t batch, float a, float alpha, int precision, const float* sumsq,
-                   void* workspace, size_t ws_bytes, void* stream);
+ *   nothing else).  X_lo (or NULL) as in ns_apply; no residual is written.
+ *   Other arguments, errors and the workspace as ns_apply. */
+int ns_apply_signs(const void* B, const void* X, const void* X_lo, void* Xout, uint64_t* bits,
+                   int64_t s, int64_t l, int64_t batch, float a, float alpha, int precision,
+                   const float* sumsq, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a6 -- entrywise sign and 1-bit packing.

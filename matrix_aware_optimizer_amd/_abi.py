@@ -59,10 +59,15 @@ SIGNATURES = {
                          _c_void_p, _c_size, _c_void_p]),
     "ns_poly": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_float, _c_float, _c_int,
                          _c_void_p, _c_size, _c_void_p]),
-    "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64, _c_float,
-                          _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
-    "ns_apply_signs": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64,
-                                _c_float, _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
+    "ns_apply": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64, _c_i64,
+                          _c_float, _c_float, _c_int, _c_void_p, _c_void_p, _c_size, _c_void_p]),
+    "ns_apply_signs": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_i64, _c_i64,
+                                _c_i64, _c_float, _c_float, _c_int, _c_void_p, _c_void_p, _c_size,
+                                _c_void_p]),
+    "ns_workspace_status": (_c_int, [_c_void_p, _c_size, _c_void_p]),
+    "ns_residual_iterations": (_c_int, [_c_i64, _c_i64, _c_float, _c_float, _c_float, _c_int, _c_int]),
+    "muon_set_split_wait_limit": (_c_int, [_c_int]),
+    "muon_get_split_wait_limit": (_c_int, []),
     "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "majority_vote": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
     "apply_update": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_float, _c_void_p]),
@@ -283,19 +288,23 @@ def ns_poly(A: torch.Tensor, B: torch.Tensor, b: float, c: float, precision="bf1
 
 def ns_apply(B: torch.Tensor, X: torch.Tensor, Xout: torch.Tensor, a: float, alpha: float = 1.0,
              precision="bf16", stream=None, sumsq: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, split: bool = True) -> None:
-    """Xout = a X + alpha B X, or (a M + alpha B M) / sqrt(sumsq) with the raw momentum as X."""
+             workspace: Optional[torch.Tensor] = None, split: bool = True,
+             X_lo: Optional[torch.Tensor] = None, Xout_lo: Optional[torch.Tensor] = None) -> None:
+    """Xout = a X + alpha B X, or (a M + alpha B M) / sqrt(sumsq) with the raw momentum as X.
+    With ``X_lo`` the addend is a (X + X_lo); ``Xout_lo`` receives the bf16 rounding
+    residual of Xout (bf16 only; the two may be one tensor)."""
     batch, s, l = _batch3(X)
     ws, nbytes = _stage_ws(workspace, split, s, l, batch, precision, X)
-    _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), s, l, batch,
-                                      float(a), float(alpha), precision_code(precision),
-                                      _dev(sumsq, "sumsq"), ws, nbytes, _stream(stream)))
+    _check("ns_apply", lib().ns_apply(_dev(B, "B"), _dev(X, "X"), _dev(X_lo, "X_lo"), _dev(Xout, "Xout"),
+                                      _dev(Xout_lo, "Xout_lo"), s, l, batch, float(a), float(alpha),
+                                      precision_code(precision), _dev(sumsq, "sumsq"), ws, nbytes,
+                                      _stream(stream)))
 
 
 def ns_apply_signs(B: torch.Tensor, X: torch.Tensor, Xout: Optional[torch.Tensor], bits: torch.Tensor,
                    a: float, alpha: float = 1.0, precision="bf16", stream=None,
                    sumsq: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   split: bool = True) -> None:
+                   split: bool = True, X_lo: Optional[torch.Tensor] = None) -> None:
     """ns_apply that also packs the signs of Xout into ``bits`` ([batch][s*l/64] words);
     with Xout None only the signs are written."""
     batch, s, l = _batch3(X)
@@ -303,8 +312,34 @@ def ns_apply_signs(B: torch.Tensor, X: torch.Tensor, Xout: Optional[torch.Tensor
         raise ValueError("bits must hold batch * s * l / 64 64-bit words")
     ws, nbytes = _stage_ws(workspace, split, s, l, batch, precision, X)
     _check("ns_apply_signs", lib().ns_apply_signs(
-        _dev(B, "B"), _dev(X, "X"), _dev(Xout, "Xout"), _dev(bits, "bits"), s, l, batch, float(a),
-        float(alpha), precision_code(precision), _dev(sumsq, "sumsq"), ws, nbytes, _stream(stream)))
+        _dev(B, "B"), _dev(X, "X"), _dev(X_lo, "X_lo"), _dev(Xout, "Xout"), _dev(bits, "bits"), s, l,
+        batch, float(a), float(alpha), precision_code(precision), _dev(sumsq, "sumsq"), ws, nbytes,
+        _stream(stream)))
+
+
+def ns_workspace_status(workspace: torch.Tensor, stream=None) -> None:
+    """Synchronise ``stream`` and raise MuonError (MUON_ESPLIT) if a split product that
+    used ``workspace`` gave up waiting for its other half (its tile was not written)."""
+    _check("ns_workspace_status", lib().ns_workspace_status(
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def ns_residual_iterations(rows: int, cols: int, a: float, b: float, c: float, steps: int,
+                           precision="bf16") -> int:
+    """How many leading iterations of ns_orthogonalize keep the bf16 residual of their output."""
+    k = int(lib().ns_residual_iterations(rows, cols, float(a), float(b), float(c), int(steps),
+                                         precision_code(precision)))
+    if k < 0:
+        _check("ns_residual_iterations", k)
+    return k
+
+
+def set_split_wait_limit(polls: int) -> int:
+    """Set the polls a split product's second half waits for the first (process-wide);
+    returns the previous limit."""
+    prev = int(lib().muon_get_split_wait_limit())
+    _check("muon_set_split_wait_limit", lib().muon_set_split_wait_limit(int(polls)))
+    return prev
 
 
 # ---------------------------------------------------------------------------

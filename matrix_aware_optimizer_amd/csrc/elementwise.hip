@@ -850,11 +850,13 @@ const char* muon_status_string(int status) {
     case MUON_EALIGN: return "device pointer not 16-byte aligned";
     case MUON_EWORKSPACE: return "workspace missing or too small";
     case MUON_ELAUNCH: return "kernel launch failed";
+    case MUON_ESPLIT:
+      return "a split product's second half gave up waiting for the first: its tile was not written";
     default: return "unknown status";
   }
 }
 
-int muon_version(void) { return 100; }
+int muon_version(void) { return 200; }
 
 
 int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream) {

@@ -80,9 +80,11 @@ enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
 // about half a tile each instead of n_p (n_p + 1) / 2 whole tiles, which
 // would leave the other CUs idle.
 enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2 };
-// bound on the polls of the second K half waiting for the first one's partial
-// (each poll sleeps ~128 cycles; the first half never needs more than
-// microseconds, the bound only keeps a wait from outliving its cause)
+// default bound on the polls of the second K half waiting for the first
+// one's partial (each poll sleeps ~128 cycles; the first half never needs
+// more than microseconds, the bound only keeps a wait from outliving its
+// cause).  A wait that runs out sets the scratch's error word and leaves the
+// tile unwritten; the host reads the word back (ns_workspace_status).
 constexpr int kSplitSpinLimit = 1 << 22;
 
 struct GemmArgs {
@@ -90,6 +92,13 @@ struct GemmArgs {
   const void* Q;  // NT: rows of the right operand (k-contiguous, ld = K); NN: [K][N]
   const void* Z;  // epilogue addend [M][N] (ld = N), may be null
   void* C;        // output [M][N] (ld = N)
+  // bf16 residuals (B X products only): the addend is Z + Zl when Zl is set,
+  // and Cl receives C's rounding residual bf16(v - bf16(v)), so that C + Cl
+  // carries v to about 16 significant bits.  Same layout as Z and C.  Each
+  // entry of Zl is read by the lane that writes the same entry of Cl, so Zl
+  // and Cl may be one buffer.
+  const void* Zl;
+  void* Cl;
   int64_t M, N, K;
   int64_t strideP, strideQ, strideZ, strideC;  // batch strides (elements)
   float alpha, beta;                           // C = alpha*acc + beta*Z (Z unread if beta == 0)
@@ -126,6 +135,8 @@ struct GemmArgs {
   int split_mode;
   float* partials;       // (split tiles) x BM x BN fp32: the first-arriving half's
   int* counters;         // one per split tile: zero on entry, left zero
+  int* split_error;      // set to 1 by a second half whose wait ran out
+  int spin_limit;        // polls of that wait
 };
 
 template <typename T, int BM_, int BN_, int WM_, int WN_>
@@ -981,16 +992,25 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
       if (tid == 0) __hip_atomic_fetch_add(g.counters + sidx, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;   // the other half finishes the tile
     }
+    __shared__ int split_ready;
     if (tid == 0) {
-      for (int spin = 0; spin < kSplitSpinLimit; ++spin) {
+      int ready = 0;
+      for (int spin = 0; spin < g.spin_limit; ++spin) {
         // an agent-scope atomic load observes the agent-scope adds to the
         // same word (the compiler emits a coherent sc1 load, and turns an
         // add of zero into the same load)
-        if (__hip_atomic_load(g.counters + sidx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+        if (__hip_atomic_load(g.counters + sidx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) {
+          ready = 1;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
+      split_ready = ready;
+      // the wait ran out: report it and leave the tile (and its counter) alone
+      if (!ready) __hip_atomic_store(g.split_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    if (!split_ready) return;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1021,6 +1041,11 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
   const bool mirror = SYRK && (HALVES || tm != tn);
   const bool second_pass = mirror || (EPI == EPI_FINAL && g.transpose_out);
   const bool use_z = EPI != EPI_STORE && g.beta != 0.0f;
+  // B X products: the addend's residual, and the output's residual
+  const bool use_zl = !SYRK && use_z && g.Zl != nullptr;
+  const bool write_cl = !SYRK && EPI == EPI_AXPBY && g.Cl != nullptr;
+  const bf16_t* Zl = static_cast<const bf16_t*>(g.Zl) + batch * g.strideZ;
+  bf16_t* Cl = static_cast<bf16_t*>(g.Cl) + batch * g.strideC;
   float alpha, beta;
   epilogue_scale(g, batch, alpha, beta);
   constexpr int LDW = C_::LDW;
@@ -1050,6 +1075,20 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
   // constant indices to stay in registers)
   auto slab = [&](auto I_) __attribute__((always_inline)) {
     constexpr int i = decltype(I_)::value;
+    const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
+    // chunk p of a lane: slab row rb + p * RPP, columns 4 cc .. 4 cc + 3 (the
+    // column does not depend on p, so addresses advance by a uniform stride)
+    const int64_t gcol = c0 + 4 * cc;
+    // the addend's residual (only some iterations carry one): loaded per slab,
+    // issued before the accumulators go to LDS so that store hides its latency
+    uint2 zl[NP];
+    if constexpr (!SYRK) {
+      if (use_zl) {
+        const bf16_t* zlrow = Zl + (r0 + rb) * g.ld + gcol;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) zl[p] = *reinterpret_cast<const uint2*>(zlrow + int64_t(p * RPP) * g.ld);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1058,14 +1097,11 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
           const int row = 8 * (v >> 2) + 4 * fgrp + (v & 3);
           wl[row * LDW + slab_col<7>(row, j * 32 + frow)] = acc[i][j][v];
         }
-    const int64_t r0 = m0 + wm0 + i * 32, c0 = n0 + wn0;
     if constexpr (i + 1 < FM)
       if (use_z) load_z(i + 1, zbuf[(i + 1) & 1]);
     const uint2 (&zr)[NP] = zbuf[i & 1];
-    // chunk p of a lane: slab row rb + p * RPP, columns 4 cc .. 4 cc + 3 (the
-    // column does not depend on p, so addresses advance by a uniform stride)
-    const int64_t gcol = c0 + 4 * cc;
     bf16_t* crow = C + (r0 + rb) * g.ld + gcol;
+    bf16_t* clrow = Cl + (r0 + rb) * g.ld + gcol;
     auto pass1 = [&](auto SG_) __attribute__((always_inline)) {
       constexpr bool SG = decltype(SG_)::value;
 #pragma unroll
@@ -1073,6 +1109,14 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
         const int row = rb + p * RPP;
         float4 a = *reinterpret_cast<const float4*>(wl + row * LDW + slab_col<7>(row, 4 * cc));
         float o[4] = {a.x * alpha, a.y * alpha, a.z * alpha, a.w * alpha};
+        if constexpr (!SYRK) {
+          if (use_zl) {
+            o[0] = fmaf(beta, __uint_as_float(zl[p].x << 16), o[0]);
+            o[1] = fmaf(beta, __uint_as_float(zl[p].x & 0xffff0000u), o[1]);
+            o[2] = fmaf(beta, __uint_as_float(zl[p].y << 16), o[2]);
+            o[3] = fmaf(beta, __uint_as_float(zl[p].y & 0xffff0000u), o[3]);
+          }
+        }
         if (use_z) {
           o[0] = fmaf(beta, __uint_as_float(zr[p].x << 16), o[0]);
           o[1] = fmaf(beta, __uint_as_float(zr[p].x & 0xffff0000u), o[1]);
@@ -1127,9 +1171,22 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
             }
           }
         } else if (SYRK || g.C != nullptr) {
-          const uint32_t w0 = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
-          const uint32_t w1 = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+          bf16_t h[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) h[t] = f32_to_bf16(o[t]);
+          const uint32_t w0 = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+          const uint32_t w1 = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
           *reinterpret_cast<uint2*>(crow + int64_t(p * RPP) * g.ld) = make_uint2(w0, w1);
+          if constexpr (!SYRK) {
+            if (write_cl) {
+              bf16_t r[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) r[t] = f32_to_bf16(o[t] - bf16_to_f32(h[t]));
+              const uint32_t l0 = uint32_t(r[0]) | (uint32_t(r[1]) << 16);
+              const uint32_t l1 = uint32_t(r[2]) | (uint32_t(r[3]) << 16);
+              *reinterpret_cast<uint2*>(clrow + int64_t(p * RPP) * g.ld) = make_uint2(l0, l1);
+            }
+          }
         }
         if (second_pass) *reinterpret_cast<float4*>(wl + row * LDW + slab_col<7>(row, 4 * cc)) = make_float4(o[0], o[1], o[2], o[3]);
       }
@@ -1254,7 +1311,18 @@ constexpr int64_t kSplitMaxUnits = 256;   // SPLIT_SYRK: at most this many units
 // exchange of the halves costing as much as the idle CUs
 constexpr int64_t kSplitMinKTiles = 256;
 constexpr int64_t kSplitCounters = 128;
-constexpr size_t kSplitCounterBytes = kSplitCounters * sizeof(int);
+// the counter block: kSplitCounters arrival counters, then the error word
+// (int index kSplitCounters), padded to 1 KB
+constexpr int64_t kSplitWords = kSplitCounters + 1;
+constexpr size_t kSplitCounterBytes = 1024;
+static_assert(kSplitWords * sizeof(int) <= kSplitCounterBytes, "counter block");
+
+// polls of a split wait, set for the process (tests lower it to drive the
+// give-up path with every kernel still exiting normally)
+inline std::atomic<int>& split_spin_limit() {
+  static std::atomic<int> limit{kSplitSpinLimit};
+  return limit;
+}
 
 struct SplitPlan {
   int mode;
@@ -1322,6 +1390,8 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
         return MUON_EWORKSPACE;
       g.split_mode = p.mode;
       g.counters = reinterpret_cast<int*>(sc.base);
+      g.split_error = g.counters + kSplitCounters;
+      g.spin_limit = split_spin_limit().load(std::memory_order_relaxed);
       g.partials = reinterpret_cast<float*>(sc.base + kSplitCounterBytes);
       grid = p.units;
     }

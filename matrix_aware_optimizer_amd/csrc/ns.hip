@@ -23,6 +23,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "common.h"
@@ -163,6 +164,8 @@ int launch_apply_big(const GemmArgs& g, int64_t batch, hipStream_t st) {
   g2.Q = static_cast<const bf16_t*>(g.Q) + n1;
   if (g.Z) g2.Z = static_cast<const bf16_t*>(g.Z) + n1;
   if (g.C) g2.C = static_cast<bf16_t*>(g.C) + n1;
+  if (g.Zl) g2.Zl = static_cast<const bf16_t*>(g.Zl) + n1;
+  if (g.Cl) g2.Cl = static_cast<bf16_t*>(g.Cl) + n1;
   // one launch when the whole-tile count keeps the XCD grouping (batch is 1 here)
   const int64_t whole = TM * (TN - ct);
   if (whole > 0 && whole % gemm::kXcds == 0) return gemm::launch_apply_mixed<EPI>(g1, g2, st);
@@ -244,10 +247,14 @@ int poly_t(const void* A, void* B, int64_t s, int64_t batch, float b, float c, h
   return launch_gemm<T, true, false, EPI_AXPBY>(g, batch, st, sc);
 }
 
+// Residual of X (bf16 products): X_lo_in, when set, is added to the addend
+// a X; X_lo_out, when set, receives the rounding residual of the stored X'
+// (not with final_out).  They may be one buffer.
 template <typename T>
 int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
             float alpha, hipStream_t st, const gemm::Scratch& sc, const GemmArgs* final_out,
-            const Fold& fold = Fold{}, const GemmArgs* signs = nullptr) {
+            const Fold& fold = Fold{}, const GemmArgs* signs = nullptr, const void* X_lo_in = nullptr,
+            void* X_lo_out = nullptr) {
   GemmArgs g{};
   if (final_out) g = *final_out;
   if (signs) {
@@ -257,6 +264,8 @@ int apply_t(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int6
     g.stride_bits = signs->stride_bits;
   }
   g.P = B; g.Q = X; g.Z = X; g.C = Xout;
+  g.Zl = X_lo_in;
+  g.Cl = final_out ? nullptr : X_lo_out;
   g.M = s; g.N = l; g.K = s;
   g.strideP = s * s; g.strideQ = g.strideZ = fold.strideX ? fold.strideX : s * l; g.strideC = s * l;
   g.alpha = alpha; g.beta = a;
@@ -401,7 +410,7 @@ std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
 }
 
 struct RunLayout {
-  size_t x0, x1, a, b, sumsq, partials, total;
+  size_t x0, x1, xl, a, b, sumsq, partials, total;
 };
 
 RunLayout layout_of(const Run& r, int precision) {
@@ -412,6 +421,7 @@ RunLayout layout_of(const Run& r, int precision) {
   auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
   L.x0 = take(n * r.sp * r.lp * es);
   L.x1 = take(n * r.sp * r.lp * es);
+  L.xl = take(precision == MUON_BF16 ? n * r.sp * r.lp * es : 0);
   L.a = take(n * r.sp * r.sp * es);
   L.b = take(n * r.sp * r.sp * es);
   L.sumsq = take(r.has_sumsq ? 0 : n * sizeof(float));
@@ -433,6 +443,44 @@ bool folds_normalisation(const Run& r, int precision) {
          r.rows % MUON_NS_PAD == 0 && r.cols % MUON_NS_PAD == 0 && r.strideM % 8 == 0;
 }
 
+// bf16 products: the outputs X_1 .. X_k of the first k iterations keep a bf16
+// residual beside X (X + X_lo holds X to about 16 significant bits), which the
+// next iteration adds to its addend a X.  Rounding X costs the most while the
+// singular values are small: there the iteration grows them about a-fold,
+// noise included, and the noise that rounding puts on the small directions is
+// large next to them.  With the residual, the rounding error of X enters the
+// next iterate through the slope of B X alone, p'(x) - a, instead of the whole
+// slope p'(x) of x -> p(x) = a x + b x^3 + c x^5; that pays while p'(x) stays
+// above a / 2, and costs once the singular values near the point where the
+// iteration flattens out (for the quintic p'(x) falls to a / 2 at x = 0.365).
+// k is chosen from the shape and the coefficients: the typical normalised
+// singular value of a well-conditioned s-row matrix, 1/sqrt(s), is iterated
+// through p while it stays below the first x > 0 with p'(x) <= a / 2.
+// Quintic, 5 steps: k = 0 for s < 87 (37 x 300: 1.84e-2 plain, 2.02e-2 with
+// two residuals), 1 up to s = 1020, 2 from 1021; cubic: 4 (all but the last).
+int residual_iterations(int64_t s, float a, float b, float c, int steps) {
+  if (!(a > 0.0f) || steps < 2 || s < 1) return 0;
+  const double A = a, B = b, C = c;
+  auto p = [&](double x) { return x * (A + x * x * (B + C * x * x)); };
+  auto slope = [&](double x) { return A + x * x * (3.0 * B + 5.0 * C * x * x); };
+  double xstar = HUGE_VAL;
+  for (int i = 1; i <= 4000; ++i) {
+    const double x = 1e-3 * i;
+    if (slope(x) <= 0.5 * A) {
+      xstar = x;
+      break;
+    }
+  }
+  double x = 1.0 / std::sqrt(static_cast<double>(s));
+  int k = 0;
+  while (k < steps - 1) {
+    x = p(x);
+    if (!(x > 0.0 && x < xstar)) break;
+    ++k;
+  }
+  return k;
+}
+
 // signs from the last product's epilogue: bf16 products, U not transposed,
 // whole 64-bit words per row of U
 bool fuses_signs(int64_t rows, int64_t cols, int precision, int steps) {
@@ -451,7 +499,9 @@ struct SplitRegion {
 };
 
 SplitRegion split_region(const std::vector<Run>& runs, int precision) {
-  SplitRegion R{0};
+  // the counter block (with the error word ns_workspace_status reads) is
+  // always there, also when nothing splits
+  SplitRegion R{gemm::kSplitCounterBytes};
   if (precision != MUON_BF16) return R;
   for (const Run& r : runs) R.bytes = std::max(R.bytes, round_up(split_scratch_bound(r.sp, r.lp, r.count), 256));
   return R;
@@ -514,8 +564,9 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
   // bf16 products may split (a symmetric product with one tile row needs no
   // scratch: its only unit is the diagonal lower half)
   const gemm::Scratch sc{precision == MUON_BF16 ? static_cast<char*>(workspace) : nullptr, split.bytes};
-  if (steps > 0 && split.bytes) {
-    const int status = zero_counters(workspace, gemm::kSplitCounters, st);
+  {
+    // arrival counters and the error word start at zero on every call
+    const int status = zero_counters(workspace, gemm::kSplitWords, st);
     if (status != MUON_OK) return status;
   }
   char* ws = static_cast<char*>(workspace) + split.bytes;
@@ -565,6 +616,7 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
       fin.bits_cols = r.cols;
       fin.stride_bits = r.stride_bits;
     }
+    const int kres = precision == MUON_BF16 ? residual_iterations(std::min(r.rows, r.cols), a, b, c, steps) : 0;
     for (int it = 0; it < steps; ++it) {
       const bool first_folded = fold_norm && it == 0;
       const void* Xc = first_folded ? r.M : X[it & 1];
@@ -575,9 +627,14 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
         // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
         status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, sc, fold);
         if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st, sc);
+        // the residual buffer is read and rewritten in place (entry by entry, by one lane)
+        void* Xlo = ws + L.xl;
+        const bool lo_in = it >= 1 && it <= kres;
+        const bool lo_out = it < kres && !last;
         if (status == MUON_OK)
           status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
-                                   st, sc, last ? &fin : nullptr, fold);
+                                   st, sc, last ? &fin : nullptr, fold, nullptr, lo_in ? Xlo : nullptr,
+                                   lo_out ? Xlo : nullptr);
       } else {
         status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st, sc);
         if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st, sc);
@@ -594,6 +651,31 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
   }
   return MUON_OK;
 }
+
+int ns_workspace_status(const void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || ws_bytes < gemm::kSplitCounterBytes) return MUON_EINVAL;
+  if (!aligned16(workspace)) return MUON_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int word = 0;
+  const char* src = static_cast<const char*>(workspace) + gemm::kSplitCounters * sizeof(int);
+  if (hipMemcpyAsync(&word, src, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return MUON_ELAUNCH;
+  if (hipStreamSynchronize(st) != hipSuccess) return MUON_ELAUNCH;
+  return word != 0 ? MUON_ESPLIT : MUON_OK;
+}
+
+int ns_residual_iterations(int64_t rows, int64_t cols, float a, float b, float c, int steps, int precision) {
+  if (rows <= 0 || cols <= 0 || steps < 0) return MUON_EINVAL;
+  if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
+  return precision == MUON_BF16 ? residual_iterations(std::min(rows, cols), a, b, c, steps) : 0;
+}
+
+int muon_set_split_wait_limit(int polls) {
+  if (polls < 0) return MUON_EINVAL;
+  gemm::split_spin_limit().store(polls, std::memory_order_relaxed);
+  return MUON_OK;
+}
+
+int muon_get_split_wait_limit(void) { return gemm::split_spin_limit().load(std::memory_order_relaxed); }
 
 static bool stage_dims_ok(int64_t s, int64_t l, int64_t batch) {
   return s > 0 && l > 0 && batch >= 0 && s % MUON_NS_PAD == 0 && l % MUON_NS_PAD == 0 && s <= l;
@@ -660,32 +742,35 @@ int ns_poly(const void* A, void* B, int64_t s, int64_t batch, float b, float c, 
                                 : poly_t<float>(A, B, s, batch, b, c, st, sc);
 }
 
-int ns_apply(const void* B, const void* X, void* Xout, int64_t s, int64_t l, int64_t batch, float a,
-             float alpha, int precision, const float* sumsq, void* workspace, size_t ws_bytes,
-             void* stream) {
+int ns_apply(const void* B, const void* X, const void* X_lo, void* Xout, void* Xout_lo, int64_t s,
+             int64_t l, int64_t batch, float a, float alpha, int precision, const float* sumsq,
+             void* workspace, size_t ws_bytes, void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
-  if (sumsq && precision != MUON_BF16) return MUON_EDTYPE;
+  if ((sumsq || X_lo || Xout_lo) && precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!B || !X || !Xout) return MUON_EINVAL;
   if (!aligned16(B) || !aligned16(X) || !aligned16(Xout)) return MUON_EALIGN;
+  if ((X_lo && !aligned16(X_lo)) || (Xout_lo && !aligned16(Xout_lo))) return MUON_EALIGN;
   gemm::Scratch sc;
   const int status = stage_scratch(workspace, ws_bytes, s, l, batch, precision, sc);
   if (status != MUON_OK) return status;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return precision == MUON_BF16
-             ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr, Fold{sumsq, 1, 0})
+             ? apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr, Fold{sumsq, 1, 0},
+                               nullptr, X_lo, Xout_lo)
              : apply_t<float>(B, X, Xout, s, l, batch, a, alpha, st, sc, nullptr);
 }
 
-int ns_apply_signs(const void* B, const void* X, void* Xout, uint64_t* bits, int64_t s, int64_t l,
-                   int64_t batch, float a, float alpha, int precision, const float* sumsq,
+int ns_apply_signs(const void* B, const void* X, const void* X_lo, void* Xout, uint64_t* bits, int64_t s,
+                   int64_t l, int64_t batch, float a, float alpha, int precision, const float* sumsq,
                    void* workspace, size_t ws_bytes, void* stream) {
   if (!stage_dims_ok(s, l, batch)) return MUON_EINVAL;
   if (precision != MUON_BF16) return MUON_EDTYPE;
   if (batch == 0) return MUON_OK;
   if (!B || !X || !bits) return MUON_EINVAL;
   if (!aligned16(B) || !aligned16(X) || (Xout && !aligned16(Xout))) return MUON_EALIGN;
+  if (X_lo && !aligned16(X_lo)) return MUON_EALIGN;
   if (reinterpret_cast<uintptr_t>(bits) % 8 != 0) return MUON_EALIGN;
   gemm::Scratch sc;
   const int status = stage_scratch(workspace, ws_bytes, s, l, batch, precision, sc);
@@ -696,7 +781,7 @@ int ns_apply_signs(const void* B, const void* X, void* Xout, uint64_t* bits, int
   signs.bits_cols = l;
   signs.stride_bits = s * l / 64;
   return apply_t<bf16_t>(B, X, Xout, s, l, batch, a, alpha, static_cast<hipStream_t>(stream), sc, nullptr,
-                         Fold{sumsq, 1, 0}, &signs);
+                         Fold{sumsq, 1, 0}, &signs, X_lo, nullptr);
 }
 
 }  // extern "C"

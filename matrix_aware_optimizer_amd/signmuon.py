@@ -25,12 +25,19 @@ class SignMuonStep:
     Parameters are the method's: ``beta``/``alpha`` of the momentum EMA,
     Newton-Schulz ``coeffs`` (a, b, c) and ``ns_steps``, the NS operand
     ``precision`` ("bf16" or "f32") and the step size ``eta``.
+
+    The exchange needs only the packed signs of the polar directions.  Where
+    the last Newton-Schulz product packs them itself (bf16 products on a wide
+    matrix whose row length is a multiple of 64, every matrix starting on a
+    64-bit word), the direction is not written unless ``keep_direction``;
+    ``self.U`` then holds the directions of the other matrices only.  With
+    ``keep_direction`` every direction is written to ``self.U``.
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int]], m_dtype: str = "bf16",
                  precision: str = "bf16", coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
                  beta: float = 0.95, alpha: Optional[float] = None, eta: float = 0.02,
-                 device="cuda"):
+                 device="cuda", keep_direction: bool = False):
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.device = torch.device(device)
         sizes = [r * c for r, c in self.shapes]
@@ -50,6 +57,7 @@ class SignMuonStep:
         self.beta = float(beta)
         self.alpha = float(1.0 - beta if alpha is None else alpha)
         self.eta = float(eta)
+        self.keep_direction = bool(keep_direction)
         u_dtype = torch.float32 if precision == "f32" else torch.bfloat16
         self.offsets = torch.tensor(offs, dtype=torch.int64, device=self.device)
         self.sumsq = torch.zeros(len(self.shapes), dtype=torch.float32, device=self.device)
@@ -62,11 +70,19 @@ class SignMuonStep:
         self.ns_workspace = torch.empty(max(ns_bytes, 1), dtype=torch.uint8, device=self.device)
         self.mom_workspace = torch.empty(max(mom_bytes, 1), dtype=torch.uint8, device=self.device)
 
+    def signs_fused(self, j: int) -> bool:
+        """Whether matrix j's packed signs come from its last product (rule of ns_orthogonalize)."""
+        r, c = self.shapes[j]
+        return (self.signs_per_matrix and self.precision == "bf16" and self.ns_steps > 0
+                and r <= c and c % 64 == 0)
+
     def _problems(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None):
         probs = []
         for j, (r, c) in enumerate(self.shapes):
             lo, hi = self.offsets_host[j], self.offsets_host[j + 1]
-            prob = (M[lo:hi].view(r, c), self.U[lo:hi].view(r, c), self.sumsq[j:j + 1])
+            signs_only = bits_row is not None and self.signs_fused(j) and not self.keep_direction
+            U = None if signs_only else self.U[lo:hi].view(r, c)
+            prob = (M[lo:hi].view(r, c), U, self.sumsq[j:j + 1])
             if bits_row is not None:
                 prob += (bits_row[lo // 64:(hi + 63) // 64],)
             probs.append(prob)
@@ -80,14 +96,19 @@ class SignMuonStep:
         _abi.muon_momentum(M, G, self.beta, self.alpha, self.offsets, self.sumsq, self.mom_workspace)
 
     def orthogonalize(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None) -> None:
-        """Polar directions into ``self.U``; with ``bits_row`` also their packed
-        signs (requires ``signs_per_matrix``)."""
+        """Polar directions into ``self.U`` (see ``keep_direction``); with ``bits_row``
+        also their packed signs (requires ``signs_per_matrix``)."""
         a, b, c = self.coeffs
         _abi.ns_orthogonalize(self._problems(M, bits_row), a, b, c, self.ns_steps, self.precision,
                               self.ns_workspace)
 
     def pack(self, bits_row: torch.Tensor) -> None:
         _abi.sign_pack(self.U, bits_row)
+
+    def check(self) -> None:
+        """Synchronise the current stream and raise if a split product of the last
+        orthogonalisation gave up waiting for its other half (its output is invalid)."""
+        _abi.ns_workspace_status(self.ns_workspace)
 
     def worker(self, M: torch.Tensor, G: torch.Tensor, bits_row: torch.Tensor) -> None:
         """Steps 1-3 for one worker: momentum, polar direction, packed signs."""

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_status_strings(L):
-    for code in [0, -1, -2, -3, -4, -5]:
+    for code in [0, -1, -2, -3, -4, -5, -6]:
         assert mao.status_string(code)
     assert mao.status_string(-99) == "unknown status"
     assert mao.muon_version() >= 100
@@ -90,28 +90,33 @@ def test_stage_validation(L):
     assert L.ns_gram(A1, A2, 256, 512, 1, 7, None, None, 0, None) == EDTYPE
     assert L.ns_gram(A1, A2, 256, 512, 1, 0, A3, None, 0, None) == EDTYPE        # folded scaling: bf16 only
     assert L.ns_poly(A1, MISALIGNED, 256, 1, 1.0, 1.0, 1, None, 0, None) == EALIGN
-    assert L.ns_apply(A1, A2, None, 256, 256, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
-    assert L.ns_apply(A1, A2, A3, 256, 256, 1, 1.0, 1.0, 0, A3, None, 0, None) == EDTYPE
+    assert L.ns_apply(A1, A2, None, None, None, 256, 256, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert L.ns_apply(A1, A2, None, A3, None, 256, 256, 1, 1.0, 1.0, 0, A3, None, 0, None) == EDTYPE
+    # bf16 residuals: bf16 only, 16-byte aligned
+    assert L.ns_apply(A1, A2, A1, A3, None, 256, 256, 1, 1.0, 1.0, 0, None, None, 0, None) == EDTYPE
+    assert L.ns_apply(A1, A2, None, A3, A1, 256, 256, 1, 1.0, 1.0, 0, None, None, 0, None) == EDTYPE
+    assert L.ns_apply(A1, A2, MISALIGNED, A3, None, 256, 256, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
+    assert L.ns_apply(A1, A2, None, A3, MISALIGNED, 256, 256, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
     assert L.ns_normalize(A1, 1, 0, 5, 1, A2, A3, 1, None) == EINVAL
     assert L.ns_gram(A1, A2, 256, 256, 0, 1, None, None, 0, None) == OK           # empty batch: no launch
     # a stage workspace, when given, must be large enough and aligned
     need = L.ns_stage_workspace_bytes(4096, 14336, 1, 1)
     assert L.ns_gram(A1, A2, 4096, 14336, 1, 1, None, A3, need - 1, None) == EWORKSPACE
-    assert L.ns_apply(A1, A2, A3, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
+    assert L.ns_apply(A1, A2, None, A3, None, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
     assert L.ns_gram(A1, A2, 4096, 14336, 1, 1, None, MISALIGNED, need, None) == EALIGN
 
 
 def test_stage_workspace_bytes(L):
-    """Split scratch: 512 bytes of arrival counters, then one fp32 256 x 256 partial
+    """Split scratch: 1024 bytes of arrival counters and the error word, then one fp32 256 x 256 partial
     tile per split tile.  Only symmetric products with a contraction of at least
     8192 whose n_p^2 units (n_p = s / 256) fit one round of 256 CUs split: the Gram
     of 4096 x 14336 splits its 120 off-diagonal tiles; fp32 never splits."""
     tile = 256 * 256 * 4
-    assert L.ns_stage_workspace_bytes(4096, 14336, 1, 1) == 512 + 120 * tile
+    assert L.ns_stage_workspace_bytes(4096, 14336, 1, 1) == 1024 + 120 * tile
     assert L.ns_stage_workspace_bytes(4096, 14336, 1, 0) == 0
     assert L.ns_stage_workspace_bytes(4096, 4096, 1, 1) == 0                 # contraction too short
     assert L.ns_stage_workspace_bytes(7168, 18432, 1, 1) == 0                # 28^2 units > 256
-    assert L.ns_stage_workspace_bytes(1024, 8192, 3, 1) == 512 + 18 * tile   # 16 x 3 units
+    assert L.ns_stage_workspace_bytes(1024, 8192, 3, 1) == 1024 + 18 * tile  # 16 x 3 units
     assert L.ns_stage_workspace_bytes(1024, 8192, 17, 1) == 0                # 16 x 17 units > 256
     assert L.ns_stage_workspace_bytes(256, 8192, 5, 1) == 0                  # diagonal units only
     assert L.ns_stage_workspace_bytes(768, 2304, 12, 1) == 0
@@ -129,12 +134,14 @@ def _problems(specs):
 
 
 def _ns_bytes(count, s, l, es=2, sumsq=True, part=0, split=0):
-    """Run buffers (two X, A, B, sums, norm partials) after the split scratch: 512
-    bytes of counters and one fp32 256 x 256 partial tile per split tile."""
+    """Run buffers (two X, the bf16 residual of X, A, B, sums, norm partials) after
+    the split scratch: 1024 bytes of counters and error word (always there), then
+    one fp32 256 x 256 partial tile per split tile."""
     def up(x):
         return -(-x // 256) * 256
-    scratch = 512 + split * 256 * 256 * 4 if split else 0
-    return (scratch + 2 * up(count * s * l * es) + 2 * up(count * s * s * es)
+    scratch = 1024 + split * 256 * 256 * 4
+    residual = up(count * s * l * es) if es == 2 else 0
+    return (scratch + 2 * up(count * s * l * es) + residual + 2 * up(count * s * s * es)
             + (0 if sumsq else up(4 * count)) + up(part))
 
 
@@ -225,15 +232,32 @@ def test_ns_grouping_with_sign_bits(L):
 
 def test_ns_apply_signs_validation(L):
     f = L.ns_apply_signs
-    assert f(A1, A2, None, A3, 256, 512, 1, 1.0, 1.0, 0, None, None, 0, None) == EDTYPE   # bf16 only
-    assert f(A1, A2, None, None, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
-    assert f(None, A2, None, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
-    assert f(A1, A2, None, ctypes.c_void_p(0x30004), 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
-    assert f(A1, A2, MISALIGNED, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
-    assert f(A1, A2, None, A3, 250, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
-    assert f(A1, A2, None, A3, 256, 512, 0, 1.0, 1.0, 1, None, None, 0, None) == OK      # empty batch
+    assert f(A1, A2, None, None, A3, 256, 512, 1, 1.0, 1.0, 0, None, None, 0, None) == EDTYPE   # bf16 only
+    assert f(A1, A2, None, None, None, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(None, A2, None, None, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(A1, A2, None, None, ctypes.c_void_p(0x30004), 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
+    assert f(A1, A2, None, MISALIGNED, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
+    assert f(A1, A2, None, None, A3, 250, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EINVAL
+    assert f(A1, A2, None, None, A3, 256, 512, 0, 1.0, 1.0, 1, None, None, 0, None) == OK      # empty batch
+    assert f(A1, A2, MISALIGNED, None, A3, 256, 512, 1, 1.0, 1.0, 1, None, None, 0, None) == EALIGN
     need = L.ns_stage_workspace_bytes(4096, 14336, 1, 1)
-    assert f(A1, A2, None, A3, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
+    assert f(A1, A2, None, None, A3, 4096, 14336, 1, 1.0, 1.0, 1, None, A1, need - 1, None) == EWORKSPACE
+
+
+def test_split_status_and_wait_limit_validation(L):
+    """ns_workspace_status needs a workspace holding the 1 KB counter block; the
+    split wait limit is a non-negative poll count, readable back."""
+    assert L.ns_workspace_status(None, 4096, None) == EINVAL
+    assert L.ns_workspace_status(A1, 1023, None) == EINVAL
+    assert L.ns_workspace_status(MISALIGNED, 4096, None) == EALIGN
+    prev = L.muon_get_split_wait_limit()
+    assert prev == 1 << 22
+    assert L.muon_set_split_wait_limit(-1) == EINVAL
+    assert L.muon_get_split_wait_limit() == prev
+    assert L.muon_set_split_wait_limit(7) == OK
+    assert L.muon_get_split_wait_limit() == 7
+    assert mao.set_split_wait_limit(prev) == 7
+    assert L.muon_get_split_wait_limit() == prev
 
 
 def test_binding_rejects_host_tensors():
@@ -340,3 +364,22 @@ def test_dion_validation(L):
     assert L.dion_step(p, 1, 192, 0.9, 0.1, A3, need, None) == EINVAL
     assert L.dion_step(p, 0, 192, 0.9, 0.1, None, 0, None) == OK
     assert mao.MUON_DION_MAX_RANK == 192
+
+
+def test_residual_iterations_rule(L):
+    """The leading iterations that keep their bf16 residual: while the typical
+    normalised singular value of a well-conditioned matrix, 1/sqrt(short side),
+    iterated through p(x) = a x + b x^3 + c x^5, stays below the first x with
+    p'(x) <= a / 2 (0.365 for the quintic, 0.708 for the cubic); at most steps - 1."""
+    q, cu = (3.4445, -4.775, 2.0315), (1.5, -0.5, 0.0)
+    f = mao.ns_residual_iterations
+    assert [f(s, 4 * s, *q, 5) for s in (1, 3, 37, 86, 87, 256, 768, 1020, 1021, 4096, 7168)] == \
+        [0, 0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
+    assert f(14336, 4096, *q, 5) == 2                    # the short side decides
+    assert f(256, 512, *cu, 5) == 4 and f(256, 512, *cu, 3) == 2 and f(256, 512, *q, 1) == 0
+    assert f(3, 1000, *cu, 5) == 0                       # p(1/sqrt 3) is past 0.708 at once
+    assert f(4096, 4096, *q, 5, "f32") == 0               # fp32 products keep no residual
+    assert f(4096, 4096, 0.0, 1.0, 1.0, 5) == 0           # no a X term
+    assert L.ns_residual_iterations(0, 5, 1.0, 1.0, 1.0, 5, 1) == EINVAL
+    assert L.ns_residual_iterations(5, 5, 1.0, 1.0, 1.0, -1, 1) == EINVAL
+    assert L.ns_residual_iterations(5, 5, 1.0, 1.0, 1.0, 5, 3) == EDTYPE

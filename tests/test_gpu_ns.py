@@ -215,8 +215,13 @@ def test_ns_mixed_dtypes_fp32_momentum_bf16_ops():
 
 
 @pytest.mark.parametrize("prec,coeffs,steps,lo", [("f32", CUBIC, 30, -2.0), ("f32", QUINTIC, 5, -2.0),
-                                                  ("bf16", QUINTIC, 5, -1.0)])
+                                                  ("bf16", QUINTIC, 5, -1.0), ("bf16", QUINTIC, 5, -2.0),
+                                                  ("bf16", CUBIC, 5, -2.0)])
 def test_ns_closed_form_spectrum(prec, coeffs, steps, lo):
+    """Singular values spread over one and two decades.  In bf16 the first
+    iteration's output keeps its rounding residual here (short side 256; the small
+    directions grow about 3.4x per iteration together with any noise picked up while
+    small); without it two decades measured 2.55e-2."""
     # known spectrum: U = Q1 phi(sigma/||sigma||) Q2^T (closed form of the iteration)
     r, c = 256, 512
     Q1, _ = np.linalg.qr(random_matrix((r, r), [307, 0]))
@@ -235,18 +240,56 @@ def test_ns_closed_form_spectrum(prec, coeffs, steps, lo):
     assert rel_fro(U, O.newton_schulz(O.decode(M, prec), *coeffs, steps)) <= TOL_NS[prec]
 
 
-def test_ns_bf16_ill_conditioned_spectrum_bound():
-    """Characterisation, not the gate: with singular values spread over two decades
-    the bf16 copy of X taken between iterations costs accuracy (the small directions
-    are amplified about 3.4x per iteration together with their rounding noise).
-    The measured error is 2.55e-2; a float64 emulation of the same rounding points
-    gives the same figure, so it is the scheme's, not the kernels'."""
-    r, c = 256, 512
-    Q1, _ = np.linalg.qr(random_matrix((r, r), [307, 0]))
-    Q2, _ = np.linalg.qr(random_matrix((c, r), [307, 1]))
-    M = store((Q1 * np.logspace(-2, 0, r)) @ Q2.T, "bf16")
-    (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, 5, "bf16")
-    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)) <= 3e-2
+@pytest.mark.parametrize("steps", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [(1024, 2048), (2048, 1024), (768, 2304), (1000, 1000)])
+def test_ns_few_steps_with_residuals(steps, shape):
+    """Two residual iterations (short side 1024: wide, and tall with its final
+    transposed write) and one (768, and the ragged 1000): step counts where the
+    last product reads a residual (2, 3) or not (1, 4)."""
+    r, c = shape
+    Q1, _ = np.linalg.qr(random_matrix((r, min(r, c)), [316, r]))
+    Q2, _ = np.linalg.qr(random_matrix((c, min(r, c)), [316, c]))
+    M = store((Q1 * np.logspace(-2, 0, min(r, c))) @ Q2.T, "bf16")
+    (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, steps, "bf16")
+    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, steps)) <= TOL_NS["bf16"]
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("batch,s,l", [(1, 4096, 14336), (2, 768, 2304), (1, 1024, 4096)])
+def test_apply_residuals(in_place, batch, s, l):
+    """ns_apply with the addend's residual X_lo and the output's residual: Xout + Xout_lo
+    equals a (X + X_lo) + B X to fp32 accumulation (the residual keeps about 16
+    significant bits), Xout_lo is within half a bf16 unit of Xout, and zero residuals
+    reproduce the plain product.  4096 x 14336 takes the one-launch whole-tile and
+    column-strip path; in place, X_lo and Xout_lo are one buffer."""
+    Xs = store(random_matrix((batch, s, l), [317, s]) / np.sqrt(s * l), "bf16")
+    Ls = store(random_matrix((batch, s, l), [318, s]) / np.sqrt(s * l) * 2.0 ** -9, "bf16")
+    R = random_matrix((batch, s, s), [319, s]) / np.sqrt(s)
+    Bs = store(R + np.transpose(R, (0, 2, 1)), "bf16")
+    Xd, Ld = to_dev(Xs, "bf16").view(batch, s, l), to_dev(Ls, "bf16").view(batch, s, l)
+    Bd = to_dev(Bs, "bf16").view(batch, s, s)
+    a = QUINTIC[0]
+    out = torch.empty_like(Xd)
+    lo_out = Ld if in_place else torch.empty_like(Xd)
+    mao.ns_apply(Bd, Xd, out, a, 1.0, X_lo=Ld, Xout_lo=lo_out)
+    hi = O.decode(from_dev(out), "bf16").reshape(batch, s, l)
+    lo = O.decode(from_dev(lo_out), "bf16").reshape(batch, s, l)
+    X = O.decode(Xs, "bf16").reshape(batch, s, l)
+    Lx = O.decode(Ls, "bf16").reshape(batch, s, l)
+    B = O.decode(Bs, "bf16").reshape(batch, s, s)
+    for b in (0, batch - 1):
+        ref = O.apply_poly(B[b], X[b], a) + a * Lx[b]
+        # bf16 alone would be about 1e-3 off; the pair is off by the residual's own
+        # rounding and the fp32 accumulation
+        assert rel_fro(hi[b] + lo[b], ref) <= 3e-5
+        assert np.all(np.abs(lo[b]) <= 2.0 ** -8 * np.abs(hi[b]))
+    # zero residuals: the plain product's values
+    zeros = torch.zeros_like(Xd)
+    plain = torch.empty_like(Xd)
+    mao.ns_apply(Bd, Xd, plain, a, 1.0)
+    with_zero = torch.empty_like(Xd)
+    mao.ns_apply(Bd, Xd, with_zero, a, 1.0, X_lo=zeros, Xout_lo=zeros)
+    assert np.array_equal(O.decode(from_dev(plain), "bf16"), O.decode(from_dev(with_zero), "bf16"))
 
 
 @pytest.mark.parametrize("kind,batch,s,l", [("gram", 16, 2048, 2048), ("poly", 16, 2048, 2048),
@@ -301,11 +344,16 @@ def test_stage_sequence_equals_ns_orthogonalize():
     X = [torch.empty((1, rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     A = torch.empty((1, rows, rows), dtype=torch.bfloat16, device="cuda")
     B = torch.empty_like(A)
-    # a bf16 wide pad-free momentum: the first iteration reads M and folds the scaling
+    # a bf16 wide pad-free momentum: the first iteration reads M and folds the scaling;
+    # the outputs of the first two iterations keep their residual, read by the next
     M3 = Md.view(1, rows, cols)
+    Xlo = torch.empty_like(X[0])
+    k = mao.ns_residual_iterations(rows, cols, a, b, c, 5, prec)
+    assert k == 2
     for it in range(5):
         Xc, ss = (M3, sums) if it == 0 else (X[it % 2], None)
         mao.ns_gram(Xc, A, prec, sumsq=ss)
         mao.ns_poly(A, B, b, c, prec)
-        mao.ns_apply(B, Xc, X[(it + 1) % 2], a, 1.0, prec, sumsq=ss)
+        mao.ns_apply(B, Xc, X[(it + 1) % 2], a, 1.0, prec, sumsq=ss,
+                     X_lo=Xlo if 1 <= it <= k else None, Xout_lo=Xlo if it < k and it < 4 else None)
     assert np.array_equal(from_dev(X[1]).reshape(rows, cols), from_dev(U))

@@ -28,7 +28,7 @@ TOL_SPLIT_VS_WHOLE = 2.0 ** -9
 
 
 def _counters_clear(ws):
-    return not ws[:512].cpu().numpy().any()
+    return not ws[:1024].cpu().numpy().any()
 
 
 def _X(batch, s, l, seed, sv=None, lv=None):
@@ -186,3 +186,51 @@ def test_poly_column_halves_and_diagonal_units(batch, s, sv):
         assert rel_fro(got[k], ref) <= TOL_STAGE
         assert _off_diagonal_block_symmetry(raw[k], s)
         assert not got[k][sv:, :].any() and not got[k][:, sv:].any()
+
+
+def test_split_wait_that_runs_out_is_reported():
+    """A second K half that gives up waiting (forced from the host: a wait limit of 0
+    polls, so every kernel still exits normally) leaves its tile unwritten and sets
+    the workspace's error word, which ns_workspace_status reports; a fresh workspace
+    and the default limit give the normal result and status again.  ns_orthogonalize
+    clears the word at the start of each call."""
+    batch, s, l = 1, 1024, 8192
+    Xd = to_dev(_X(batch, s, l, 9), "bf16").view(batch, s, l)
+    good = torch.empty((batch, s, s), dtype=torch.bfloat16, device="cuda")
+    mao.ns_gram(Xd, good, split=False)
+    sentinel = torch.full_like(good, 7.0)
+    ws = mao.new_stage_workspace(s, l, batch)
+    prev = mao.set_split_wait_limit(0)
+    try:
+        mao.ns_gram(Xd, sentinel, workspace=ws)
+    finally:
+        mao.set_split_wait_limit(prev)
+    with pytest.raises(mao.MuonError) as err:
+        mao.ns_workspace_status(ws)
+    assert err.value.status == -6
+    got = from_dev(sentinel).reshape(s, s)
+    assert (got == from_dev(torch.full((1,), 7.0, dtype=torch.bfloat16))[0]).any()   # tiles left unwritten
+    ws2 = mao.new_stage_workspace(s, l, batch)
+    A = torch.empty_like(good)
+    mao.ns_gram(Xd, A, workspace=ws2)
+    mao.ns_workspace_status(ws2)
+    assert _counters_clear(ws2)
+    assert rel_fro(O.decode(from_dev(A), "bf16"), O.decode(from_dev(good), "bf16")) <= TOL_SPLIT_VS_WHOLE
+
+    # the whole iteration at a splitting shape: the status of each call
+    rows, cols = 1024, 8192
+    M = to_dev(store(random_matrix((rows, cols), [321, 0]), "bf16"), "bf16").view(rows, cols)
+    U = torch.empty_like(M)
+    probs = [(M, U, None)]
+    wsn = torch.empty(mao.ns_workspace_bytes(probs), dtype=torch.uint8, device="cuda")
+    prev = mao.set_split_wait_limit(0)
+    try:
+        mao.ns_orthogonalize(probs, *QUINTIC, 5, "bf16", workspace=wsn)
+    finally:
+        mao.set_split_wait_limit(prev)
+    with pytest.raises(mao.MuonError):
+        mao.ns_workspace_status(wsn)
+    mao.ns_orthogonalize(probs, *QUINTIC, 5, "bf16", workspace=wsn)
+    mao.ns_workspace_status(wsn)
+    ref = O.newton_schulz(O.decode(from_dev(M), "bf16").reshape(rows, cols), *QUINTIC, 5)
+    assert rel_fro(O.decode(from_dev(U), "bf16").reshape(rows, cols), ref) <= 2e-2
