@@ -18,8 +18,9 @@
  *     binary32).
  *   - Every tensor argument is a DEVICE pointer owned by the caller; the
  *     library never allocates, frees or retains memory.  Between calls it
- *     keeps only per-device facts set once: each device's CU count and the
- *     dynamic LDS limits of its kernels (kernel attributes).  These are
+ *     keeps only per-device facts set once: each device's CU count, the
+ *     dynamic LDS limits of its kernels (kernel attributes) and the address
+ *     of its fixed 4 MiB scratch array (used by muon_momentum_noalloc only).  These are
  *     atomics, so host threads may call concurrently (on separate streams
  *     and buffers).  Scratch memory is passed in as `workspace`, sized by
  *     the matching *_workspace_bytes query.
@@ -52,9 +53,11 @@ enum muon_status {
   MUON_EALIGN = -3,     /* a device pointer is not 16-byte aligned          */
   MUON_EWORKSPACE = -4, /* workspace missing or smaller than the query says */
   MUON_ELAUNCH = -5,    /* the HIP runtime rejected a kernel launch         */
-  MUON_ESPLIT = -6      /* (ns_workspace_status) a split product's second
+  MUON_ESPLIT = -6,     /* (ns_workspace_status) a split product's second
                            half gave up waiting for the first half's partial
                            tile; that tile of the output was not written     */
+  MUON_ESCRATCH = -7    /* (muon_momentum_noalloc) the problem needs more
+                           scratch than the library's fixed array holds     */
 };
 
 /* Newton-Schulz working dimensions are padded up to a multiple of this. */
@@ -102,6 +105,27 @@ size_t muon_momentum_workspace_bytes(int64_t numel, int nseg);
 int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
                   const int64_t* seg_offsets, int nseg, float beta, float alpha,
                   float* sumsq_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* muon_momentum_noalloc -- muon_momentum without a workspace argument, for
+ *   callers that cannot allocate device memory: code under HIP graph capture,
+ *   tight serving or training loops, harnesses that forbid allocation.  It
+ *   computes exactly what muon_momentum computes (same kernels, bit-identical
+ *   results) and allocates nothing: the norms' partial sums go to a fixed
+ *   4 MiB array in the library's device memory, one per device, held from the
+ *   device's first call until the process ends (its address is looked up
+ *   once per device on that first call).
+ *   Limit: muon_momentum_workspace_bytes(numel, nseg) <= 4 MiB, i.e. about
+ *   (524287 - nseg) * 4096 entries (2.1e9); larger problems return
+ *   MUON_ESCRATCH before anything is launched.  Without sumsq_out the array
+ *   is not used and there is no limit beyond MUON_MAX_NUMEL.
+ *   Every call on one device shares that device's array (the last call's
+ *   values stay in it; each call writes every partial it reads, so nothing
+ *   needs clearing): calls that overlap in time on one device -- on two
+ *   streams, or from two host threads -- race and must be ordered by the
+ *   caller.  Other arguments and errors as muon_momentum. */
+int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
+                          const int64_t* seg_offsets, int nseg, float beta, float alpha,
+                          float* sumsq_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * a2-a5 -- Newton-Schulz orthogonalisation of a list of momentum matrices.

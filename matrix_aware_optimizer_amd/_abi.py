@@ -49,6 +49,8 @@ SIGNATURES = {
     "muon_momentum_workspace_bytes": (_c_size, [_c_i64, _c_int]),
     "muon_momentum": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_i64, _c_void_p, _c_int,
                                _c_float, _c_float, _c_void_p, _c_void_p, _c_size, _c_void_p]),
+    "muon_momentum_noalloc": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_i64, _c_void_p, _c_int,
+                                       _c_float, _c_float, _c_void_p, _c_void_p]),
     "ns_workspace_bytes": (_c_size, [ctypes.POINTER(NSProblem), _c_int, _c_int]),
     "ns_orthogonalize": (_c_int, [ctypes.POINTER(NSProblem), _c_int, _c_float, _c_float, _c_float,
                                   _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
@@ -178,6 +180,25 @@ def muon_momentum(M: torch.Tensor, G: torch.Tensor, beta: float, alpha: float,
         _dev(M, "M"), dtype_code(M), _dev(G, "G"), dtype_code(G), M.numel(),
         _dev(seg_offsets, "seg_offsets") if sumsq_out is not None else None, nseg,
         float(beta), float(alpha), _dev(sumsq_out, "sumsq_out"), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def muon_momentum_noalloc(M: torch.Tensor, G: torch.Tensor, beta: float, alpha: float,
+                          seg_offsets: Optional[torch.Tensor] = None,
+                          sumsq_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """muon_momentum without a workspace: the library's fixed per-device scratch holds
+    the partial sums (nothing is allocated here or in the library).  Calls that overlap
+    on one device race."""
+    if M.numel() != G.numel():
+        raise ValueError("M and G must have the same number of entries")
+    nseg = 0
+    if sumsq_out is not None:
+        if seg_offsets is None:
+            raise ValueError("seg_offsets is required with sumsq_out")
+        nseg = seg_offsets.numel() - 1
+    _check("muon_momentum_noalloc", lib().muon_momentum_noalloc(
+        _dev(M, "M"), dtype_code(M), _dev(G, "G"), dtype_code(G), M.numel(),
+        _dev(seg_offsets, "seg_offsets") if sumsq_out is not None else None, nseg,
+        float(beta), float(alpha), _dev(sumsq_out, "sumsq_out"), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -746,6 +746,43 @@ int sumsq_strided(const void* M, int m_dtype, int64_t len, int64_t count, int64_
 
 }  // namespace muon
 
+// ---------------------------------------------------------------------------
+// Fixed scratch of muon_momentum_noalloc: the per-piece partial sums of the
+// norms (the buffer muon_momentum takes as its workspace), 4 MiB on every
+// device the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it only names the symbol):
+// it passes the device address looked up once per device below.
+// ---------------------------------------------------------------------------
+static constexpr int64_t kScratchDoubles = int64_t(1) << 19;
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+namespace muon {
+namespace {
+
+// Device address of the current device's copy of `scratch`, looked up with
+// that device current on its first use and kept per device (ordinals past the
+// tracked range look it up on every call).
+int scratch_address(double** out) {
+  static std::atomic<uintptr_t> cache[kMaxTrackedDevices];
+  const int dev = current_device();
+  if (dev < 0) return MUON_ELAUNCH;
+  if (dev < kMaxTrackedDevices) {
+    const uintptr_t cached = cache[dev].load(std::memory_order_acquire);
+    if (cached != 0) {
+      *out = reinterpret_cast<double*>(cached);
+      return MUON_OK;
+    }
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MUON_ELAUNCH;
+  if (dev < kMaxTrackedDevices) cache[dev].store(reinterpret_cast<uintptr_t>(ptr), std::memory_order_release);
+  *out = static_cast<double*>(ptr);
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
 using namespace muon;
 
 extern "C" {
@@ -782,6 +819,27 @@ int muon_momentum(void* M, int m_dtype, const void* G, int g_dtype, int64_t nume
                                                 numel, seg, beta, alpha, sumsq_out, part, st);
   return launch_momentum<float, float, true>(static_cast<float*>(M), static_cast<const float*>(G),
                                              numel, seg, beta, alpha, sumsq_out, part, st);
+}
+
+int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int64_t numel,
+                          const int64_t* seg_offsets, int nseg, float beta, float alpha,
+                          float* sumsq_out, void* stream) {
+  if (!numel_ok(numel)) return MUON_EINVAL;
+  if (!valid_dtype(m_dtype) || !valid_dtype(g_dtype)) return MUON_EDTYPE;
+  if (numel > 0 && (!M || !G)) return MUON_EINVAL;
+  if (numel > 0 && (!aligned16(M) || !aligned16(G))) return MUON_EALIGN;
+  double* part = nullptr;
+  if (sumsq_out) {
+    if (nseg < 1 || !seg_offsets) return MUON_EINVAL;
+    if (!aligned16(seg_offsets)) return MUON_EALIGN;
+    if (muon_momentum_workspace_bytes(numel, nseg) > size_t(kScratchDoubles) * sizeof(double))
+      return MUON_ESCRATCH;
+    const int status = scratch_address(&part);
+    if (status != MUON_OK) return status;
+  }
+  // the partials need no clearing: the reduction reads only pieces this call wrote
+  return muon_momentum(M, m_dtype, G, g_dtype, numel, seg_offsets, nseg, beta, alpha, sumsq_out, part,
+                       size_t(kScratchDoubles) * sizeof(double), stream);
 }
 
 int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* stream) {
@@ -852,6 +910,8 @@ const char* muon_status_string(int status) {
     case MUON_ELAUNCH: return "kernel launch failed";
     case MUON_ESPLIT:
       return "a split product's second half gave up waiting for the first: its tile was not written";
+    case MUON_ESCRATCH:
+      return "the problem needs more than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

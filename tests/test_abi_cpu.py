@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_status_strings(L):
-    for code in [0, -1, -2, -3, -4, -5, -6]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         assert mao.status_string(code)
     assert mao.status_string(-99) == "unknown status"
     assert mao.muon_version() >= 100
@@ -383,3 +383,27 @@ def test_residual_iterations_rule(L):
     assert L.ns_residual_iterations(0, 5, 1.0, 1.0, 1.0, 5, 1) == EINVAL
     assert L.ns_residual_iterations(5, 5, 1.0, 1.0, 1.0, -1, 1) == EINVAL
     assert L.ns_residual_iterations(5, 5, 1.0, 1.0, 1.0, 5, 3) == EDTYPE
+
+
+def test_noalloc_momentum_validation(L):
+    """The allocation-free momentum rejects, before launching anything, what its fixed
+    4 MiB scratch cannot hold (workspace_bytes(numel, nseg) > 4 MiB) and the same bad
+    arguments as muon_momentum."""
+    f = L.muon_momentum_noalloc
+    ESCRATCH = -7
+    assert mao.status_string(ESCRATCH) != "unknown status"
+    cap = 1 << 22
+    big = (cap // 8) * 4096                       # nchunks alone fills the array
+    assert L.muon_momentum_workspace_bytes(big, 1) > cap
+    assert f(A1, 1, A2, 1, big, A3, 1, 0.9, 0.1, A3, None) == ESCRATCH
+    fits = ((cap // 8) - 1 - 48) * 4096            # the largest set of 48 matrices that fits
+    assert L.muon_momentum_workspace_bytes(fits, 48) == cap
+    assert L.muon_momentum_workspace_bytes(fits + 1, 48) > cap
+    assert f(A1, 1, A2, 1, fits + 1, A3, 48, 0.9, 0.1, A3, None) == ESCRATCH
+    assert f(None, 1, A2, 1, 100, None, 0, 0.9, 0.1, None, None) == EINVAL
+    assert f(A1, 5, A2, 1, 100, None, 0, 0.9, 0.1, None, None) == EDTYPE
+    assert f(MISALIGNED, 1, A2, 1, 100, None, 0, 0.9, 0.1, None, None) == EALIGN
+    assert f(A1, 1, A2, 1, 100, None, 1, 0.9, 0.1, A3, None) == EINVAL        # sums need offsets
+    assert f(A1, 1, A2, 1, 100, MISALIGNED, 1, 0.9, 0.1, A3, None) == EALIGN
+    assert f(A1, 1, A2, 1, (1 << 38) + 1, None, 0, 0.9, 0.1, None, None) == EINVAL
+    assert f(A1, 1, A2, 1, 0, None, 0, 0.9, 0.1, None, None) == OK            # empty: no launch
