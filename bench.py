@@ -169,17 +169,41 @@ def elementwise_bytes(wl):
 
 
 class Events:
-    """HIP events recorded on the current stream (the one every call here runs on)
-    after each named call of one step."""
+    """HIP events on the current stream (the one every call here runs on).
 
-    def __init__(self, torch):
+    ``mark(name)`` records an event after a named call (the step's timeline, gaps
+    between kernels included).  ``kernel(name)`` hands a pair of events to the
+    library for the next kernel it launches (muon_time_next_launch): they are
+    recorded by that launch at the kernel's own start and end, so their interval is
+    the kernel's duration, the figure rocprofv3's kernel trace also reports."""
+
+    def __init__(self, torch, mao=None):
         self.torch = torch
+        self.mao = mao
         self.marks = []
+        self.kernels = []
 
     def mark(self, name):
         ev = self.torch.cuda.Event(enable_timing=True)
         ev.record()
         self.marks.append((name, ev))
+
+    def kernel(self, name):
+        e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()            # creates the HIP events; the launch records them again
+        self.mao.time_next_launch(e0, e1)
+        self.kernels.append((name, e0, e1))
+
+
+def per_kernel_ms(events_list):
+    """{name: [ms per launch]} from the launch-bound event pairs, and launches per step."""
+    per, counts = {}, {}
+    for ev in events_list:
+        for name, e0, e1 in ev.kernels:
+            per.setdefault(name, []).append(e0.elapsed_time(e1))
+            counts[name] = counts.get(name, 0) + 1
+    return per, {k: v / len(events_list) for k, v in counts.items()}
 
 
 def per_call_ms(events_list):
@@ -237,7 +261,9 @@ def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
 
     def one(ev=None):
         mark = ev.mark if ev is not None else (lambda name: None)
+        kern = ev.kernel if ev is not None else (lambda name: None)
         mark("start")
+        kern("momentum")
         step.momentum(M, G)
         mark("momentum")
         if step.signs_per_matrix:
@@ -246,10 +272,12 @@ def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
         else:
             step.orthogonalize(M)
             mark("ns")
+            kern("pack")
             step.pack(bits[0])
             mark("pack")
         if W is not None and wl.workers > 0:
             if fuse_tail:
+                kern("vote_update")
                 step.vote_update(W, bits, fused=True)
                 mark("vote_update")
             else:
@@ -263,7 +291,7 @@ def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
     evs = []
     t_start = time.perf_counter()
     for _ in range(steps):
-        ev = Events(torch)
+        ev = Events(torch, mao)
         one(ev)
         evs.append(ev)
     torch.cuda.synchronize()
@@ -271,6 +299,8 @@ def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
     step.check()
     per, launches = per_call_ms(evs)
     med = {k: float(np.median(v)) for k, v in per.items()}
+    kper, _ = per_kernel_ms(evs)
+    kmed = {k: float(np.median(v)) for k, v in kper.items()}
     step_ev = [ev.marks[0][1].elapsed_time(ev.marks[-1][1]) for ev in evs]
     ms = wall * 1e3 / steps
     flops, ns_bytes = ns_work(wl)
@@ -293,13 +323,11 @@ def product_step(mao, torch, wl, dev, steps, warmup, fuse_tail=True):
                   "mfma_floor_ms": mfma_floor_ms, "hbm_floor_ms": hbm_floor_ms,
                   "frac_of_floor": max(mfma_floor_ms, hbm_floor_ms) / ns_ms},
            "input_generation_s": gen_s}
-    gb = {}
-    gb["momentum"] = eb["momentum"] / (med["momentum"] * 1e-3) / 1e9
-    if "pack" in med:
-        gb["pack"] = eb["pack"] / (med["pack"] * 1e-3) / 1e9
-    if "vote_update" in med:
-        gb["vote_update"] = eb["vote_update"] / (med["vote_update"] * 1e-3) / 1e9
-    out["elementwise"] = {k: {"ms": med[k], "GB/s": v, "frac_hbm": v / PEAK_HBM_GBS} for k, v in gb.items()}
+    # elementwise kernels: the kernel's own duration (launch-bound events); the
+    # momentum call also runs the short per-matrix reduction of the norms
+    gb = {k: eb[k] / (kmed[k] * 1e-3) / 1e9 for k in ("momentum", "pack", "vote_update") if k in kmed}
+    out["elementwise"] = {k: {"ms": kmed[k], "GB/s": v, "frac_hbm": v / PEAK_HBM_GBS, "call_ms": med[k]}
+                          for k, v in gb.items()}
     out["_objects"] = {"step": step, "M": M, "G": G, "W": W, "bits": bits, "vote": vote}
     return out
 
@@ -326,10 +354,13 @@ def stage_sequence(mao, torch, wl, dev, objs, steps, warmup):
 
     def one(ev=None):
         mark = ev.mark if ev is not None else (lambda name: None)
+        kern = ev.kernel if ev is not None else (lambda name: None)
         mark("start")
+        kern("momentum")
         step.momentum(M, G)
         mark("momentum")
         if not fold:
+            kern("normalize")
             mao.ns_normalize(M.view(1, rows, cols), step.sumsq, X[0], prec)
             mark("normalize")
         cur = 0
@@ -337,21 +368,27 @@ def stage_sequence(mao, torch, wl, dev, objs, steps, warmup):
             Xc, ss = (M.view(1, rows, cols), step.sumsq) if fold and it == 0 else (X[cur], None)
             lo_in = Xlo if 1 <= it <= kres else None
             lo_out = Xlo if it < kres and it + 1 < wl.ns_steps else None
+            kern("gram")
             mao.ns_gram(Xc, A, prec, sumsq=ss, workspace=stage_ws)
             mark("gram")
             if c != 0.0:
+                kern("poly")
                 mao.ns_poly(A, B, b, c, prec, workspace=stage_ws)
                 mark("poly")
             Bm, alpha = (B, 1.0) if c != 0.0 else (A, b)
             if it + 1 == wl.ns_steps:
+                kern("apply_signs")
                 mao.ns_apply_signs(Bm, Xc, None, bits[0], a, alpha, prec, sumsq=ss, workspace=stage_ws,
                                    X_lo=lo_in)
                 mark("apply_signs")
             else:
+                # the products that also read or write the residual of X are timed apart
+                kern("apply" if lo_in is None and lo_out is None else "apply_residual")
                 mao.ns_apply(Bm, Xc, X[1 - cur], a, alpha, prec, sumsq=ss, workspace=stage_ws,
                              X_lo=lo_in, Xout_lo=lo_out)
                 mark("apply")
             cur = 1 - cur
+        kern("vote_update")
         step.vote_update(W, bits, fused=True)
         mark("vote_update")
 
@@ -361,21 +398,22 @@ def stage_sequence(mao, torch, wl, dev, objs, steps, warmup):
     evs = []
     t_start = time.perf_counter()
     for _ in range(steps):
-        ev = Events(torch)
+        ev = Events(torch, mao)
         one(ev)
         evs.append(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     mao.ns_workspace_status(stage_ws)
-    per, launches = per_call_ms(evs)
-    # per launch: the step's total for a name over its launches per step
-    avg = {k: float(np.mean(v)) / launches[k] for k, v in per.items()}
-    total = {k: float(np.mean(v)) for k, v in per.items()}
+    per, launches = per_kernel_ms(evs)
+    # per launch: the kernel's own duration, averaged over the timed steps' launches
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    total = {k: avg[k] * launches[k] for k in avg}
     gram_f, poly_f, apply_f = ns_flops(s, l, c != 0.0)
     peak = PEAK_BF16_TFLOPS if prec == "bf16" else PEAK_F32_TFLOPS
     eb = elementwise_bytes(wl)
     kernels = {}
-    for k, fl in (("gram", gram_f), ("poly", poly_f), ("apply", apply_f), ("apply_signs", apply_f)):
+    for k, fl in (("gram", gram_f), ("poly", poly_f), ("apply", apply_f), ("apply_residual", apply_f),
+                  ("apply_signs", apply_f)):
         if k in avg:
             tf = fl / (avg[k] * 1e-3) / 1e12
             kernels[k] = {"ms": avg[k], "TFLOP/s": tf, "frac_peak": tf / peak, "launches_per_step": launches[k]}
@@ -385,31 +423,42 @@ def stage_sequence(mao, torch, wl, dev, objs, steps, warmup):
     if "normalize" in avg:
         gbs = wl.numel * (ES[wl.m_dtype] + ES[prec]) / (avg["normalize"] * 1e-3) / 1e9
         kernels["normalize"] = {"ms": avg["normalize"], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
-    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply", "apply_signs") if k in total)
+    ns_ms = sum(total[k] for k in ("normalize", "gram", "poly", "apply", "apply_residual", "apply_signs")
+                if k in total)
     flops, _ = ns_work(wl)
-    return {"ms_per_step": wall * 1e3 / steps, "ns_ms": ns_ms,
-            "ns_TFLOP/s": flops / (ns_ms * 1e-3) / 1e12, "kernels": kernels, "total_ms": total,
+    return {"ms_per_step": wall * 1e3 / steps, "ns_kernel_ms": ns_ms,
+            "ns_kernel_TFLOP/s": flops / (ns_ms * 1e-3) / 1e12, "residual_iterations": kres,
+            "kernels": kernels, "total_ms": total,
             "_buffers": {"X": X, "A": A, "B": B, "stage_ws": stage_ws}}
 
 
 def roofline_of(kernels, total, rows, cols, wl):
-    """Roofline of the kernel with the most time per step (from the stage sequence)."""
-    dominant = max(total, key=total.get)
+    """Roofline of the kernel function with the most time per step (from the stage
+    sequence).  The B X product is one kernel whatever its epilogue writes (the
+    direction, its residual, or only the packed signs), so its launches are taken
+    together, as rocprofv3 averages them under one kernel name."""
+    groups = {"apply": ("apply", "apply_residual", "apply_signs"), "gram": ("gram",), "poly": ("poly",),
+              "momentum": ("momentum",), "vote_update": ("vote_update",), "normalize": ("normalize",)}
+    tot = {g: sum(total.get(k, 0.0) for k in ks) for g, ks in groups.items()}
+    dominant = max(tot, key=tot.get)
+    launches = sum(kernels[k]["launches_per_step"] for k in groups[dominant] if k in kernels)
+    ms = tot[dominant] / launches
     peak = PEAK_BF16_TFLOPS if wl.precision == "bf16" else PEAK_F32_TFLOPS
-    k = kernels[dominant]
     counters = recorded_traffic(dominant, rows, cols)
-    if "TFLOP/s" in k:
-        s, l = min(rows, cols), max(rows, cols)
-        fl = dict(zip(("gram", "poly", "apply"), ns_flops(s, l, wl.coeffs[2] != 0.0)))
-        fl["apply_signs"] = fl["apply"]
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": k["TFLOP/s"], "peak": peak,
-                "unit": "TFLOP/s", "frac": k["TFLOP/s"] / peak,
-                "traffic": None if counters is None else counters["bytes"],
-                "per_launch_flops": fl[dominant], "avg_launch_ms": k["ms"]}
+    s, l = min(rows, cols), max(rows, cols)
+    fl = dict(zip(("gram", "poly", "apply"), ns_flops(s, l, wl.coeffs[2] != 0.0)))
+    if dominant in fl:
+        ach = fl[dominant] / (ms * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": None if counters is None else counters["bytes"],
+                "per_launch_flops": fl[dominant], "avg_launch_ms": ms, "launches_per_step": launches}
     else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": k["GB/s"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": k["GB/s"] / PEAK_HBM_GBS,
-                "traffic": None if counters is None else counters["bytes"], "avg_launch_ms": k["ms"]}
+        nb = elementwise_bytes(wl)[dominant]
+        ach = nb / (ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": None if counters is None else counters["bytes"],
+                "per_launch_bytes": nb, "avg_launch_ms": ms, "launches_per_step": launches}
+    roof["timing"] = "HIP events recorded by each launch at the kernel's start and end"
     if counters is not None:
         roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
         roof["traffic_detail"] = counters
@@ -536,8 +585,10 @@ def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
     """The HBM-bound kernels with cold caches: before each timed call a 1 GiB buffer
     is read (a sum over it), which replaces the 256 MB Infinity Cache's contents with
     clean lines, so every operand comes from HBM and no write-back of someone else's
-    data is charged to the kernel.  HIP events bracket the call alone, on the stream
-    it runs on; the median of ``reps`` calls."""
+    data is charged to the kernel.  The kernel's duration comes from HIP events its
+    launch records at its start and end (on the stream it runs on); the median of
+    ``reps`` calls.  The momentum call's short norm reduction is not in the timed
+    kernel."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)        # 1 GiB
     step, M, G, W, bits, vote = (objs[k] for k in ("step", "M", "G", "W", "bits", "vote"))
     U = step.U
@@ -554,18 +605,22 @@ def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
     out = {}
     for name, (fn, nbytes) in calls.items():
         fn()
-        times = []
+        times, calls_ms = [], []
         for _ in range(reps):
             flush.sum()
-            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            start.record()
+            ev = Events(torch, mao)
+            ev.mark("start")
+            ev.kernel(name)
             fn()
-            end.record()
+            ev.mark("end")
             torch.cuda.synchronize()
-            times.append(start.elapsed_time(end))
+            times.append(ev.kernels[0][1].elapsed_time(ev.kernels[0][2]))
+            calls_ms.append(ev.marks[0][1].elapsed_time(ev.marks[1][1]))
         ms = float(np.median(times))
         gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        # call_ms: events around the host call, dispatch gaps included
+        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                     "call_ms": float(np.median(calls_ms))}
     del flush
     return out
 

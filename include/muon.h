@@ -78,6 +78,15 @@ const char* muon_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int muon_version(void);
 
+/* muon_time_next_launch -- measurement aid.  The next kernel that the calling
+ * host thread launches through this library records `start_event` as it
+ * starts and `stop_event` as it ends (hipEvent_t handles created by the
+ * caller, either may be NULL), on the stream of that call, so that
+ * hipEventElapsedTime gives the kernel's own duration without the gaps
+ * around it; then the request is forgotten.  For a call that launches
+ * several kernels only the first is timed.  Always MUON_OK. */
+int muon_time_next_launch(void* start_event, void* stop_event);
+
 /* ---------------------------------------------------------------------------
  * a1 -- momentum EMA and per-matrix squared Frobenius norm.
  *   [SM] "Fluxo Algorítmico" step 1: each worker updates its local momentum.

@@ -46,6 +46,7 @@ class NSProblem(ctypes.Structure):
 SIGNATURES = {
     "muon_status_string": (ctypes.c_char_p, [_c_int]),
     "muon_version": (_c_int, []),
+    "muon_time_next_launch": (_c_int, [_c_void_p, _c_void_p]),
     "muon_momentum_workspace_bytes": (_c_size, [_c_i64, _c_int]),
     "muon_momentum": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_i64, _c_void_p, _c_int,
                                _c_float, _c_float, _c_void_p, _c_void_p, _c_size, _c_void_p]),
@@ -405,6 +406,22 @@ def vote_and_update(W: torch.Tensor, bits: torch.Tensor, eta: float, stream=None
 
 def muon_version() -> int:
     return int(lib().muon_version())
+
+
+def time_next_launch(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:
+    """Make the next kernel this thread launches through the library record ``start`` and
+    ``stop`` (torch timing events) at its own start and end.  Each event must have been
+    recorded once already (torch creates the underlying HIP event on its first record)."""
+    handles = []
+    for ev in (start, stop):
+        if ev is None:
+            handles.append(None)
+            continue
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("record the event once before passing it (the HIP event is created lazily)")
+        handles.append(h)
+    _check("muon_time_next_launch", lib().muon_time_next_launch(handles[0], handles[1]))
 
 
 # ---------------------------------------------------------------------------

@@ -1,6 +1,7 @@
 // Shared device helpers for libmuon (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -115,6 +116,32 @@ inline bool numel_ok(int64_t n) { return n >= 0 && n <= MUON_MAX_NUMEL; }
 inline bool valid_dtype(int d) { return d == MUON_F32 || d == MUON_BF16; }
 inline size_t dtype_size(int d) { return d == MUON_F32 ? 4 : 2; }
 inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// Timing events for the next kernel this host thread launches through the
+// library (set by muon_time_next_launch): that launch records them at the
+// kernel's start and end (hipExtLaunchKernelGGL), then they are forgotten.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& pending_launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
+// Every kernel of the library is launched here.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                          Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  LaunchEvents& pending = pending_launch_events();
+  if (pending.start != nullptr || pending.stop != nullptr) {
+    const LaunchEvents ev = pending;
+    pending = LaunchEvents{};
+    hipExtLaunchKernelGGL(kern, grid, block, lds, st, ev.start, ev.stop, 0, static_cast<KArgs>(args)...);
+  } else {
+    kern<<<grid, block, lds, st>>>(static_cast<KArgs>(args)...);
+  }
+}
 
 inline int launch_status() {
   hipError_t e = hipGetLastError();

@@ -506,10 +506,10 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
     return aligned16(p) && (s_a == 1 || s_b == 1) && s_batch % 4 == 0 && (s_a == 1 ? s_b : s_a) % 4 == 0;
   };
   const int a_vec = vec_ok(A, sA, a_i, a_k), b_vec = vec_ok(B, sB, b_k, b_j);
-  dion_gemm_kernel<<<grid, dim3(256), 0, st>>>(g, splits, part, a_vec, b_vec);
+  launch_kernel(dion_gemm_kernel, grid, dim3(256), 0, st, g, splits, part, a_vec, b_vec);
   if (splits > 1) {
     const int64_t n = batch * M * N;
-    reduce_kernel<<<dim3((n + 255) / 256), dim3(256), 0, st>>>(g, splits, part, batch);
+    launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
   }
   return launch_status();
 }
@@ -682,7 +682,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
     const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
     const int64_t threads = vec ? mn / 4 : mn;
-    add_kernel<<<dim3((threads + 255) / 256, b), dim3(256), 0, st>>>(M, run.sM, static_cast<const float*>(p.G),
+    launch_kernel(add_kernel, dim3((threads + 255) / 256, b), dim3(256), 0, st, M, run.sM, static_cast<const float*>(p.G),
                                                                     run.sG, mn, vec);
     if ((status = launch_status()) != MUON_OK) return status;
     status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
@@ -699,7 +699,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
                      r, r, run.m, 1.0f, 0.0f, run.count, part, st);
       if (status != MUON_OK) return status;
     }
-    chol_inv_kernel<<<dim3(count), dim3(256), lds, st>>>(Gm, r * r, Li, r * r, rank);
+    launch_kernel(chol_inv_kernel, dim3(count), dim3(256), lds, st, Gm, r * r, Li, r * r, rank);
     if ((status = launch_status()) != MUON_OK) return status;
     for (size_t k = 0; k < runs.size(); ++k) {
       const DRun& run = runs[k];
@@ -729,8 +729,8 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
       const int64_t rows_per = std::max<int64_t>(64, (n + m - 1) / m);
       const int64_t nch = (n + rows_per - 1) / rows_per;
       float* cpart = Pbuf(k, 1);
-      colsq_kernel<<<dim3(nch, b), dim3(256), 0, st>>>(R, n * r, cpart, n, rank, rows_per, nch);
-      colscale_kernel<<<dim3(nch, b), dim3(256), 0, st>>>(R, n * r, cpart, Q, run.sQ, n, rank, rows_per, nch);
+      launch_kernel(colsq_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, n, rank, rows_per, nch);
+      launch_kernel(colscale_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, Q, run.sQ, n, rank, rows_per, nch);
     }
     if ((status = launch_status()) != MUON_OK) return status;
     status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, st);

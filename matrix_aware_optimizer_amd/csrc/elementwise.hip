@@ -202,14 +202,14 @@ int launch_momentum(TM* M, const TG* G, int64_t numel, SegMap seg, float beta, f
   if (nchunks == 0 && !(sumsq_out && seg.nseg > 0)) return MUON_OK;  // nothing to launch
   if (nchunks > 0) {
     if (sumsq_out)
-      momentum_kernel<TM, TG, UPDATE, true><<<dim3(nchunks), dim3(kThreads), 0, stream>>>(
+      launch_kernel(momentum_kernel<TM, TG, UPDATE, true>, dim3(nchunks), dim3(kThreads), 0, stream, 
           M, G, numel, seg, beta, alpha, partials);
     else
-      momentum_kernel<TM, TG, UPDATE, false><<<dim3(nchunks), dim3(kThreads), 0, stream>>>(
+      launch_kernel(momentum_kernel<TM, TG, UPDATE, false>, dim3(nchunks), dim3(kThreads), 0, stream, 
           M, G, numel, seg, beta, alpha, partials);
   }
   if (sumsq_out && seg.nseg > 0)
-    segment_reduce_kernel<<<dim3(seg.nseg), dim3(kReduceThreads), 0, stream>>>(partials, seg, nchunks,
+    launch_kernel(segment_reduce_kernel, dim3(seg.nseg), dim3(kReduceThreads), 0, stream, partials, seg, nchunks,
                                                                           sumsq_out);
   return launch_status();
 }
@@ -685,11 +685,11 @@ template <int NB> struct VoteLaunch {
     if (nwords % 2 == 0) {
       const int64_t npairs = nwords / 2;
       const int64_t blocks = (npairs + kThreads * kVotePairs - 1) / (kThreads * kVotePairs);
-      vote2_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(reinterpret_cast<const uint4*>(bits), M,
+      launch_kernel(vote2_kernel<NB>, dim3(blocks), dim3(kThreads), 0, st, reinterpret_cast<const uint4*>(bits), M,
                                                                  npairs, reinterpret_cast<uint4*>(out));
     } else {
       const int64_t blocks = (nwords + kThreads - 1) / kThreads;
-      vote_kernel<NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(bits, M, nwords, out);
+      launch_kernel(vote_kernel<NB>, dim3(blocks), dim3(kThreads), 0, st, bits, M, nwords, out);
     }
     return launch_status();
   }
@@ -701,10 +701,10 @@ template <int NB> struct VoteUpdateLaunch {
     const int64_t blocks = ((numel + 7) / 8 + kThreads - 1) / kThreads;
     const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
     if (w_dtype == MUON_BF16)
-      vote_update_kernel<bf16_t, NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+      launch_kernel(vote_update_kernel<bf16_t, NB>, dim3(blocks), dim3(kThreads), 0, st, 
           static_cast<bf16_t*>(W), numel, b8, M, nwords * 8, eta);
     else
-      vote_update_kernel<float, NB><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+      launch_kernel(vote_update_kernel<float, NB>, dim3(blocks), dim3(kThreads), 0, st, 
           static_cast<float*>(W), numel, b8, M, nwords * 8, eta);
     return launch_status();
   }
@@ -852,10 +852,10 @@ int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* s
   const int64_t blocks = (numel + kPackBlock - 1) / kPackBlock;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (u_dtype == MUON_BF16)
-    sign_pack_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const bf16_t*>(U),
+    launch_kernel(sign_pack_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const bf16_t*>(U),
                                                                       numel, bits, nwords);
   else
-    sign_pack_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const float*>(U),
+    launch_kernel(sign_pack_kernel<float>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const float*>(U),
                                                                      numel, bits, nwords);
   return launch_status();
 }
@@ -880,10 +880,10 @@ int apply_update(void* W, int w_dtype, int64_t numel, const uint64_t* vote_bits,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vote_bits);
   if (w_dtype == MUON_BF16)
-    update_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<bf16_t*>(W), numel,
+    launch_kernel(update_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, st, static_cast<bf16_t*>(W), numel,
                                                                    v8, eta);
   else
-    update_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<float*>(W), numel, v8,
+    launch_kernel(update_kernel<float>, dim3(blocks), dim3(kThreads), 0, st, static_cast<float*>(W), numel, v8,
                                                                   eta);
   return launch_status();
 }
@@ -918,6 +918,11 @@ const char* muon_status_string(int status) {
 
 int muon_version(void) { return 200; }
 
+int muon_time_next_launch(void* start_event, void* stop_event) {
+  pending_launch_events() = LaunchEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return MUON_OK;
+}
+
 
 int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream) {
   if (!numel_ok(numel)) return MUON_EINVAL;
@@ -929,9 +934,9 @@ int sign_int8(const void* U, int u_dtype, int64_t numel, int8_t* S, void* stream
   const int64_t blocks = (lanes + kThreads - 1) / kThreads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (u_dtype == MUON_BF16)
-    sign_int8_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const bf16_t*>(U), numel, S);
+    launch_kernel(sign_int8_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const bf16_t*>(U), numel, S);
   else
-    sign_int8_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(static_cast<const float*>(U), numel, S);
+    launch_kernel(sign_int8_kernel<float>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const float*>(U), numel, S);
   return launch_status();
 }
 
@@ -943,10 +948,10 @@ int sum_int8(const int8_t* S, int M, int64_t numel, int8_t* out, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (numel % 16 == 0) {
     const int64_t nvec = numel / 16;
-    sum_int8_kernel<<<dim3((nvec + kThreads - 1) / kThreads), dim3(kThreads), 0, st>>>(
+    launch_kernel(sum_int8_kernel, dim3((nvec + kThreads - 1) / kThreads), dim3(kThreads), 0, st, 
         reinterpret_cast<const uint4*>(S), M, nvec, reinterpret_cast<uint4*>(out));
   } else {
-    sum_int8_bytes_kernel<<<dim3((numel + kThreads - 1) / kThreads), dim3(kThreads), 0, st>>>(S, M, numel, out);
+    launch_kernel(sum_int8_bytes_kernel, dim3((numel + kThreads - 1) / kThreads), dim3(kThreads), 0, st, S, M, numel, out);
   }
   return launch_status();
 }
@@ -958,7 +963,7 @@ int threshold_pack(const int8_t* sum, int64_t numel, uint64_t* bits, void* strea
   if (!aligned16(sum) || !aligned16(bits)) return MUON_EALIGN;
   const int64_t nwords = (numel + 63) / 64;
   const int64_t blocks = (nwords * 4 + kThreads - 1) / kThreads;
-  threshold_pack_kernel<<<dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
+  launch_kernel(threshold_pack_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), 
       sum, numel, bits, nwords);
   return launch_status();
 }
@@ -973,9 +978,9 @@ int unpack_signs(const uint64_t* bits, int64_t numel, void* out, int out_dtype, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bits);
   if (out_dtype == MUON_BF16)
-    unpack_signs_kernel<bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(b8, numel, static_cast<bf16_t*>(out));
+    launch_kernel(unpack_signs_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, st, b8, numel, static_cast<bf16_t*>(out));
   else
-    unpack_signs_kernel<float><<<dim3(blocks), dim3(kThreads), 0, st>>>(b8, numel, static_cast<float*>(out));
+    launch_kernel(unpack_signs_kernel<float>, dim3(blocks), dim3(kThreads), 0, st, b8, numel, static_cast<float*>(out));
   return launch_status();
 }
 
@@ -989,16 +994,16 @@ int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u
   const int64_t blocks = ((numel + 7) / 8 + kThreads - 1) / kThreads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (w_dtype == MUON_BF16 && u_dtype == MUON_BF16)
-    update_dense_kernel<bf16_t, bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+    launch_kernel(update_dense_kernel<bf16_t, bf16_t>, dim3(blocks), dim3(kThreads), 0, st, 
         static_cast<bf16_t*>(W), numel, static_cast<const bf16_t*>(U), eta);
   else if (w_dtype == MUON_BF16)
-    update_dense_kernel<bf16_t, float><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+    launch_kernel(update_dense_kernel<bf16_t, float>, dim3(blocks), dim3(kThreads), 0, st, 
         static_cast<bf16_t*>(W), numel, static_cast<const float*>(U), eta);
   else if (u_dtype == MUON_BF16)
-    update_dense_kernel<float, bf16_t><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+    launch_kernel(update_dense_kernel<float, bf16_t>, dim3(blocks), dim3(kThreads), 0, st, 
         static_cast<float*>(W), numel, static_cast<const bf16_t*>(U), eta);
   else
-    update_dense_kernel<float, float><<<dim3(blocks), dim3(kThreads), 0, st>>>(
+    launch_kernel(update_dense_kernel<float, float>, dim3(blocks), dim3(kThreads), 0, st, 
         static_cast<float*>(W), numel, static_cast<const float*>(U), eta);
   return launch_status();
 }

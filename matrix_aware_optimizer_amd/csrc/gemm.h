@@ -1293,7 +1293,7 @@ int launch(const GemmArgs& g, int64_t batch, hipStream_t st) {
   auto kern = gemm_kernel<T, BM, BN, WM, WN, SYRK, NN, EPI>;
   static std::atomic<uint64_t> configured{0};   // devices with the LDS limit set
   if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
-  kern<<<dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  launch_kernel(kern, dim3(blocks, batch), dim3(C_::NT), C_::LDS_BYTES, st, g);
   return launch_status();
 }
 
@@ -1399,7 +1399,7 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
   auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
   static std::atomic<uint64_t> configured{0};   // devices with the LDS limit set
   if (set_lds_limit(kern, C_::LDS_BYTES, configured) != MUON_OK) return MUON_ELAUNCH;
-  kern<<<dim3(grid, batch), dim3(C_::NT), C_::LDS_BYTES, st>>>(g);
+  launch_kernel(kern, dim3(grid, batch), dim3(C_::NT), C_::LDS_BYTES, st, g);
   return launch_status();
 }
 
@@ -1417,7 +1417,7 @@ int launch_apply_mixed(GemmArgs g1, GemmArgs g2, hipStream_t st) {
   auto kern = gemm_apply_mixed_kernel<EPI>;
   static std::atomic<uint64_t> configured{0};
   if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
-  kern<<<dim3(n1 + n2, 1), dim3(512), lds_bytes, st>>>(g1, g2, n1);
+  launch_kernel(kern, dim3(n1 + n2, 1), dim3(512), lds_bytes, st, g1, g2, n1);
   return launch_status();
 }
 
@@ -1438,7 +1438,7 @@ int launch_syrk_halves(GemmArgs g, int64_t batch, hipStream_t st) {
   auto kern = gemm_syrk_halves_kernel<EPI>;
   static std::atomic<uint64_t> configured{0};
   if (set_lds_limit(kern, lds_bytes, configured) != MUON_OK) return MUON_ELAUNCH;
-  kern<<<dim3(n1 + np, batch), dim3(512), lds_bytes, st>>>(gh, gd, n1);
+  launch_kernel(kern, dim3(n1 + np, batch), dim3(512), lds_bytes, st, gh, gd, n1);
   return launch_status();
 }
 

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int
 int zero_counters(void* base, int64_t n, hipStream_t st) {
   if (n <= 0) return MUON_OK;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
-  zero_ints_kernel<<<dim3(blocks), dim3(256), 0, st>>>(static_cast<int*>(base), n);
+  launch_kernel(zero_ints_kernel, dim3(blocks), dim3(256), 0, st, static_cast<int*>(base), n);
   return launch_status();
 }
 
@@ -279,12 +279,12 @@ int normalize_t(const void* M, int64_t strideM, int64_t rows, int64_t cols, cons
                 int64_t stride_sumsq, void* X, int64_t sp, int64_t lp, int64_t batch, hipStream_t st) {
   if (sp == 0 || lp == 0 || batch == 0) return MUON_OK;
   if (rows > cols) {
-    normalize_tall_kernel<TM, TX><<<dim3(lp / 64, sp / 64, batch), dim3(256), 0, st>>>(
+    launch_kernel(normalize_tall_kernel<TM, TX>, dim3(lp / 64, sp / 64, batch), dim3(256), 0, st, 
         static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
   } else {
     const int64_t blocks = (sp * (lp / 8) + 255) / 256;
     const int vec = cols % 8 == 0 && strideM % 8 == 0;
-    normalize_kernel<TM, TX><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+    launch_kernel(normalize_kernel<TM, TX>, dim3(blocks, batch), dim3(256), 0, st, 
         static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp,
         vec);
   }
@@ -310,10 +310,10 @@ int emit_t(const void* X, int64_t sp, int64_t lp, int64_t rows, int64_t cols, vo
   const int64_t blocks = (rows * cols + 255) / 256;
   if (blocks == 0 || batch == 0) return MUON_OK;
   if (u_dtype == MUON_BF16)
-    emit_kernel<TX, bf16_t><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+    launch_kernel(emit_kernel<TX, bf16_t>, dim3(blocks, batch), dim3(256), 0, st, 
         static_cast<const TX*>(X), sp, lp, rows, cols, static_cast<bf16_t*>(U), strideU);
   else
-    emit_kernel<TX, float><<<dim3(blocks, batch), dim3(256), 0, st>>>(
+    launch_kernel(emit_kernel<TX, float>, dim3(blocks, batch), dim3(256), 0, st, 
         static_cast<const TX*>(X), sp, lp, rows, cols, static_cast<float*>(U), strideU);
   return launch_status();
 }
@@ -631,10 +631,13 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
         void* Xlo = ws + L.xl;
         const bool lo_in = it >= 1 && it <= kres;
         const bool lo_out = it < kres && !last;
+        // signs only (no direction wanted): the last product is the kernel of the
+        // other iterations with no output but the packed signs
+        const bool signs_only = last && r.U == nullptr;
         if (status == MUON_OK)
-          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
-                                   st, sc, last ? &fin : nullptr, fold, nullptr, lo_in ? Xlo : nullptr,
-                                   lo_out ? Xlo : nullptr);
+          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, signs_only ? nullptr : Xn, r.sp, r.lp, r.count, a,
+                                   c != 0.0f ? 1.0f : b, st, sc, last && !signs_only ? &fin : nullptr, fold,
+                                   signs_only ? &fin : nullptr, lo_in ? Xlo : nullptr, lo_out ? Xlo : nullptr);
       } else {
         status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st, sc);
         if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st, sc);
