@@ -207,6 +207,18 @@ def test_ns_batched_interleaved_shapes():
         assert rel_fro(U, ref) <= TOL_NS["bf16"]
 
 
+def test_ns_many_runs_in_one_call():
+    """Six shapes (one tall, one with rows that are not a multiple of the padding), two
+    matrices each in layer order: six batched runs of two in one call, one after the
+    other through the same workspace.  Every direction against the oracle."""
+    shapes = [(256, 256), (256, 512), (200, 768), (256, 1024), (256, 1280), (768, 256)] * 2
+    Ms = [store(random_matrix(s, [322, j]), "bf16") for j, s in enumerate(shapes)]
+    got = _ns_gpu(Ms, "bf16", "bf16", QUINTIC, 5, "bf16")
+    for M, U in zip(Ms, got):
+        ref = O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)
+        assert rel_fro(U, ref) <= TOL_NS["bf16"]
+
+
 def test_ns_mixed_dtypes_fp32_momentum_bf16_ops():
     M = store(random_matrix((300, 900), [306, 0], "student_t3"), "f32")
     (U,) = _ns_gpu([M], "f32", "bf16", QUINTIC, 5, "bf16")
