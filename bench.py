@@ -602,6 +602,14 @@ def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
     if W is not None:
         calls["update"] = (lambda: mao.apply_update(W, vote, wl.eta), eb["update"])
         calls["vote_update"] = (lambda: mao.vote_and_update(W, bits, wl.eta), eb["vote_update"])
+    # reference: a device-to-device copy moving as many bytes as the vote, and as the
+    # pack (half read, half written); its kernel is the runtime's, so only the call
+    # bracket is timed here and its own duration is read from the kernel trace
+    refs = {}
+    for name in ("vote", "pack"):
+        half = eb[name] // 2
+        src, dst = torch.empty(half, dtype=torch.uint8, device=dev), torch.empty(half, dtype=torch.uint8, device=dev)
+        refs["copy_like_" + name] = ((lambda d=dst, s_=src: d.copy_(s_)), eb[name])
     out = {}
     for name, (fn, nbytes) in calls.items():
         fn()
@@ -621,7 +629,19 @@ def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
         # call_ms: events around the host call, dispatch gaps included
         out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
                      "call_ms": float(np.median(calls_ms))}
-    del flush
+    for name, (fn, nbytes) in refs.items():
+        fn()
+        calls_ms = []
+        for _ in range(reps):
+            flush.sum()
+            ev = Events(torch, mao)
+            ev.mark("start")
+            fn()
+            ev.mark("end")
+            torch.cuda.synchronize()
+            calls_ms.append(ev.marks[0][1].elapsed_time(ev.marks[1][1]))
+        out[name] = {"bytes": nbytes, "call_ms": float(np.median(calls_ms))}
+    del flush, refs
     return out
 
 
