@@ -161,6 +161,10 @@ int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int6
  *              holds X to about 16 significant bits): rounding X costs the
  *              most accuracy while the singular values are still small.  k
  *              is ns_residual_iterations(rows, cols, a, b, c, steps, ...).
+ *              A problem whose short side is below ns_bf16_min_side() (96)
+ *              runs on the fp32 products instead: at such sizes the bf16
+ *              rounding of B alone can exceed 2e-2 relative error, and the
+ *              products take microseconds either way.
  *              MUON_F32: fp32 throughout.
  *   problem    M (device, rows x cols of m_dtype), U (device, rows x cols of
  *              u_dtype, may alias nothing else), sumsq (device float holding
@@ -168,8 +172,9 @@ int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int6
  *              bits (device, 8-byte aligned, or NULL): the packed signs of U
  *              in sign_pack's layout (ceil(rows * cols / 64) words), i.e.
  *              a6 of [SM] "Fluxo" step 2 on this problem's U.  With bf16
- *              precision, steps > 0, rows <= cols and cols % 64 == 0 the
- *              signs come from the last product's epilogue and U may be NULL
+ *              precision, steps > 0, ns_bf16_min_side() <= rows <= cols and
+ *              cols % 64 == 0 the signs come from the last product's
+ *              epilogue and U may be NULL
  *              (then only the signs are written); otherwise U is required and
  *              the signs are packed from it after the iteration.
  *   Problems of equal shape and dtypes whose pointers are evenly spaced are
@@ -217,15 +222,22 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
  *   problem with these coefficients and steps.  With the residual, the
  *   rounding error of X reaches the next iterate through the slope of B X
  *   alone, p'(x) - a, instead of the slope p'(x) of the scalar map
- *   p(x) = a x + b x^3 + c x^5, which pays while p'(x) >= a / 2.  k counts
- *   the iterates p(x0), p(p(x0)), ... of x0 = 1/sqrt(min(rows, cols)) (the
- *   typical normalised singular value of a well-conditioned matrix) that
- *   stay below the first x > 0 with p'(x) <= a / 2, at most steps - 1.
- *   Quintic (3.4445, -4.7750, 2.0315), 5 steps: 0 below a short side of 87,
- *   1 up to 1020, 2 from 1021.  Returns k >= 0 (0 for MUON_F32, or a <= 0),
- *   or MUON_EINVAL / MUON_EDTYPE. */
+ *   p(x) = a x + b x^3 + c x^5, which pays while p'(x) >= a / 2.  k is the
+ *   larger of steps - 2 (directions far below the typical singular value of
+ *   an ill-conditioned momentum keep growing for most iterations) and the
+ *   number of iterates p(x0), p(p(x0)), ... of x0 = 1/sqrt(min(rows, cols))
+ *   (the typical normalised singular value of a well-conditioned matrix) that
+ *   stay below the first x > 0 with p'(x) <= a / 2; at most steps - 1.
+ *   Quintic (3.4445, -4.7750, 2.0315), 5 steps: 3; cubic (1.5, -0.5, 0): 4.
+ *   Returns k >= 0 (0 for MUON_F32, for a short side below
+ *   ns_bf16_min_side(), or a <= 0), or MUON_EINVAL / MUON_EDTYPE. */
 int ns_residual_iterations(int64_t rows, int64_t cols, float a, float b, float c, int steps,
                            int precision);
+
+/* ns_bf16_min_side -- the shortest short side that ns_orthogonalize runs on
+ *   bf16 products when asked for MUON_BF16 (96); smaller problems run on the
+ *   fp32 products (see precision above).  No arguments, no errors. */
+int ns_bf16_min_side(void);
 
 /* ns_workspace_status -- did a split product give up?
  *   Enqueues a copy of the workspace's error word to the host on `stream`,

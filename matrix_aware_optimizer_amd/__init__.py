@@ -14,6 +14,6 @@ from ._abi import MUON_INT8_MAX_VOTERS, sign_int8, sum_int8, threshold_pack  # n
 from ._abi import apply_update_dense, unpack_signs  # noqa: F401
 from ._abi import new_stage_workspace, ns_apply_signs, ns_stage_workspace_bytes  # noqa: F401
 from ._abi import MUON_DION_MAX_RANK, dion_step, dion_workspace_bytes  # noqa: F401
-from ._abi import ns_residual_iterations, ns_workspace_status, set_split_wait_limit  # noqa: F401
+from ._abi import ns_bf16_min_side, ns_residual_iterations, ns_workspace_status, set_split_wait_limit  # noqa: F401
 from ._abi import muon_momentum_noalloc, time_next_launch  # noqa: F401
 from .signmuon import SignMuonStep  # noqa: F401

@@ -69,6 +69,7 @@ SIGNATURES = {
                                 _c_void_p]),
     "ns_workspace_status": (_c_int, [_c_void_p, _c_size, _c_void_p]),
     "ns_residual_iterations": (_c_int, [_c_i64, _c_i64, _c_float, _c_float, _c_float, _c_int, _c_int]),
+    "ns_bf16_min_side": (_c_int, []),
     "muon_set_split_wait_limit": (_c_int, [_c_int]),
     "muon_get_split_wait_limit": (_c_int, []),
     "sign_pack": (_c_int, [_c_void_p, _c_int, _c_i64, _c_void_p, _c_void_p]),
@@ -354,6 +355,12 @@ def ns_residual_iterations(rows: int, cols: int, a: float, b: float, c: float, s
     if k < 0:
         _check("ns_residual_iterations", k)
     return k
+
+
+def ns_bf16_min_side() -> int:
+    """The shortest short side that ns_orthogonalize runs on bf16 products (smaller
+    problems asked for bf16 run on the fp32 products)."""
+    return int(lib().ns_bf16_min_side())
 
 
 def set_split_wait_limit(polls: int) -> int:

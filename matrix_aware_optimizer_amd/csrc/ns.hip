@@ -409,11 +409,24 @@ std::vector<Run> make_runs(const muon_ns_problem* probs, int count) {
   return runs;
 }
 
+// bf16 products need a short side of at least kBf16MinSide.  Below it the
+// rounding of B = bA + cA^2 alone puts 1.8e-2 to 2.4e-2 of relative error on a
+// Gaussian 37 x 300 or 16 x 128 momentum (with or without residuals), so such
+// problems run on the fp32 products; at these sizes they take microseconds
+// either way.  From 96 up, Gaussian inputs stay at or below 1.4e-2.
+constexpr int64_t kBf16MinSide = 96;
+
+// the precision a problem's products actually run in
+int run_precision(int64_t rows, int64_t cols, int precision) {
+  return precision == MUON_BF16 && std::min(rows, cols) < kBf16MinSide ? MUON_F32 : precision;
+}
+
 struct RunLayout {
   size_t x0, x1, xl, a, b, sumsq, partials, total;
 };
 
-RunLayout layout_of(const Run& r, int precision) {
+RunLayout layout_of(const Run& r, int requested) {
+  const int precision = run_precision(r.rows, r.cols, requested);
   const size_t es = precision == MUON_BF16 ? 2 : 4;
   const size_t n = static_cast<size_t>(r.count);
   RunLayout L{};
@@ -451,13 +464,20 @@ bool folds_normalisation(const Run& r, int precision) {
 // large next to them.  With the residual, the rounding error of X enters the
 // next iterate through the slope of B X alone, p'(x) - a, instead of the whole
 // slope p'(x) of x -> p(x) = a x + b x^3 + c x^5; that pays while p'(x) stays
-// above a / 2, and costs once the singular values near the point where the
-// iteration flattens out (for the quintic p'(x) falls to a / 2 at x = 0.365).
-// k is chosen from the shape and the coefficients: the typical normalised
-// singular value of a well-conditioned s-row matrix, 1/sqrt(s), is iterated
-// through p while it stays below the first x > 0 with p'(x) <= a / 2.
-// Quintic, 5 steps: k = 0 for s < 87 (37 x 300: 1.84e-2 plain, 2.02e-2 with
-// two residuals), 1 up to s = 1020, 2 from 1021; cubic: 4 (all but the last).
+// above a / 2, and costs a little once the singular values near the point
+// where the iteration flattens out (for the quintic p'(x) falls to a / 2 at
+// x = 0.365).
+// k is the larger of two counts.  The first follows the typical normalised
+// singular value of a well-conditioned s-row matrix, 1/sqrt(s), through p
+// while it stays below the first x > 0 with p'(x) <= a / 2.  The second is
+// steps - 2: an ill-conditioned momentum has directions far below the typical
+// value that keep growing for most of the iterations.  Measured against the
+// fp64 iteration (bf16 stage calls, short sides 768 to 4096), three residuals
+// hold spectra over three decades, a rank-s/8 matrix plus noise of 1e-2 or
+// 1e-3, and a two-level spectrum at 5.5e-3 to 9.9e-3, where two residuals
+// reach 2.8e-2 and one 8.6e-2; on Gaussian and heavy-tailed inputs three cost
+// at most 15% over two (7.8e-3 to 1.1e-2).  Quintic, 5 steps: k = 3; cubic:
+// 4 (all but the last).
 int residual_iterations(int64_t s, float a, float b, float c, int steps) {
   if (!(a > 0.0f) || steps < 2 || s < 1) return 0;
   const double A = a, B = b, C = c;
@@ -478,13 +498,13 @@ int residual_iterations(int64_t s, float a, float b, float c, int steps) {
     if (!(x > 0.0 && x < xstar)) break;
     ++k;
   }
-  return k;
+  return std::max(k, steps - 2);
 }
 
 // signs from the last product's epilogue: bf16 products, U not transposed,
 // whole 64-bit words per row of U
 bool fuses_signs(int64_t rows, int64_t cols, int precision, int steps) {
-  return precision == MUON_BF16 && steps > 0 && rows <= cols && cols % 64 == 0;
+  return run_precision(rows, cols, precision) == MUON_BF16 && steps > 0 && rows <= cols && cols % 64 == 0;
 }
 
 bool valid_problem(const muon_ns_problem& p) {
@@ -503,7 +523,9 @@ SplitRegion split_region(const std::vector<Run>& runs, int precision) {
   // always there, also when nothing splits
   SplitRegion R{gemm::kSplitCounterBytes};
   if (precision != MUON_BF16) return R;
-  for (const Run& r : runs) R.bytes = std::max(R.bytes, round_up(split_scratch_bound(r.sp, r.lp, r.count), 256));
+  for (const Run& r : runs)
+    if (run_precision(r.rows, r.cols, precision) == MUON_BF16)
+      R.bytes = std::max(R.bytes, round_up(split_scratch_bound(r.sp, r.lp, r.count), 256));
   return R;
 }
 
@@ -572,6 +594,7 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
   char* ws = static_cast<char*>(workspace) + split.bytes;
   for (const Run& r : runs) {
     const RunLayout L = layout_of(r, precision);
+    const int prec = run_precision(r.rows, r.cols, precision);
     const float* sumsq = r.sumsq;
     int64_t stride_sumsq = r.stride_sumsq;
     int status;
@@ -588,14 +611,14 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     void* B = ws + L.b;
     // a bf16, wide, pad-free momentum is its own (unnormalised) X0: the first
     // iteration reads M and folds the Frobenius scale into its epilogues
-    const bool fold_norm = folds_normalisation(r, precision) && steps > 0;
+    const bool fold_norm = folds_normalisation(r, prec) && steps > 0;
     if (!fold_norm) {
       status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
-                                  precision, r.sp, r.lp, r.count, st);
+                                  prec, r.sp, r.lp, r.count, st);
       if (status != MUON_OK) return status;
     }
     if (steps == 0) {
-      status = precision == MUON_BF16
+      status = prec == MUON_BF16
                    ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
                    : emit_t<float>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st);
       if (status == MUON_OK) status = pack_run_signs(r, st);
@@ -616,14 +639,14 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
       fin.bits_cols = r.cols;
       fin.stride_bits = r.stride_bits;
     }
-    const int kres = precision == MUON_BF16 ? residual_iterations(std::min(r.rows, r.cols), a, b, c, steps) : 0;
+    const int kres = prec == MUON_BF16 ? residual_iterations(std::min(r.rows, r.cols), a, b, c, steps) : 0;
     for (int it = 0; it < steps; ++it) {
       const bool first_folded = fold_norm && it == 0;
       const void* Xc = first_folded ? r.M : X[it & 1];
       void* Xn = X[(it + 1) & 1];
       const bool last = it + 1 == steps;
       const Fold fold = first_folded ? Fold{sumsq, stride_sumsq, r.strideM} : Fold{};
-      if (precision == MUON_BF16) {
+      if (prec == MUON_BF16) {
         // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
         status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, sc, fold);
         if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st, sc);
@@ -666,10 +689,13 @@ int ns_workspace_status(const void* workspace, size_t ws_bytes, void* stream) {
   return word != 0 ? MUON_ESPLIT : MUON_OK;
 }
 
+int ns_bf16_min_side(void) { return static_cast<int>(kBf16MinSide); }
+
 int ns_residual_iterations(int64_t rows, int64_t cols, float a, float b, float c, int steps, int precision) {
   if (rows <= 0 || cols <= 0 || steps < 0) return MUON_EINVAL;
   if (precision != MUON_F32 && precision != MUON_BF16) return MUON_EDTYPE;
-  return precision == MUON_BF16 ? residual_iterations(std::min(rows, cols), a, b, c, steps) : 0;
+  return run_precision(rows, cols, precision) == MUON_BF16 ? residual_iterations(std::min(rows, cols), a, b, c, steps)
+                                                            : 0;
 }
 
 int muon_set_split_wait_limit(int polls) {

@@ -71,10 +71,11 @@ class SignMuonStep:
         self.mom_workspace = torch.empty(max(mom_bytes, 1), dtype=torch.uint8, device=self.device)
 
     def signs_fused(self, j: int) -> bool:
-        """Whether matrix j's packed signs come from its last product (rule of ns_orthogonalize)."""
+        """Whether matrix j's packed signs come from its last product (rule of
+        ns_orthogonalize: bf16 products, which need a short side of at least 96)."""
         r, c = self.shapes[j]
         return (self.signs_per_matrix and self.precision == "bf16" and self.ns_steps > 0
-                and r <= c and c % 64 == 0)
+                and r <= c and c % 64 == 0 and r >= _abi.ns_bf16_min_side())
 
     def _problems(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None):
         probs = []

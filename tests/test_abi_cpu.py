@@ -150,8 +150,12 @@ def test_ns_workspace_single_and_padding(L):
     # split tiles: the Gram's 120 off-diagonal tiles
     assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 4096, 14336, split=120)
     arr = _problems([(0x10000, 0x20000, 0x30000, 300, 70, 1, 1)])    # tall, ragged
-    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 256, 512)
+    # a short side below 96 runs on the fp32 products, also when bf16 is asked for
+    assert L.ns_bf16_min_side() == 96
+    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 256, 512, es=4)
     assert L.ns_workspace_bytes(arr, 1, 0) == _ns_bytes(1, 256, 512, es=4)
+    arr = _problems([(0x10000, 0x20000, 0x30000, 300, 96, 1, 1)])    # tall, ragged, bf16 products
+    assert L.ns_workspace_bytes(arr, 1, 1) == _ns_bytes(1, 256, 512)
     assert L.ns_workspace_bytes(arr, 0, 1) == 0
     assert L.ns_workspace_bytes(arr, 1, 9) == 0
 
@@ -196,7 +200,8 @@ def test_ns_orthogonalize_validation(L):
 
 def test_ns_orthogonalize_sign_bits_validation(L):
     """U may be NULL only where the signs come from the last product's epilogue:
-    bf16 precision, steps > 0, rows <= cols and cols % 64 == 0."""
+    bf16 products (bf16 precision and a short side of at least 96), steps > 0,
+    rows <= cols and cols % 64 == 0."""
     f = L.ns_orthogonalize
     ok = _problems([(0x10000, None, 0x30000, 512, 1024, 1, 1, 0x40000)])
     need = L.ns_workspace_bytes(ok, 1, 1)
@@ -208,6 +213,10 @@ def test_ns_orthogonalize_sign_bits_validation(L):
     assert f(tall, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
     ragged = _problems([(0x10000, None, 0x30000, 512, 1000, 1, 1, 0x40000)])
     assert f(ragged, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    small = _problems([(0x10000, None, 0x30000, 95, 1024, 1, 1, 0x40000)])    # fp32 products
+    assert f(small, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
+    smallest_bf16 = _problems([(0x10000, None, 0x30000, 96, 1024, 1, 1, 0x40000)])
+    assert f(smallest_bf16, 1, 1.0, 1.0, 1.0, 5, 1, A3, 16, None) == EWORKSPACE
     neither = _problems([(0x10000, None, 0x30000, 512, 1024, 1, 1)])
     assert L.ns_workspace_bytes(neither, 1, 1) == 0
     assert f(neither, 1, 1.0, 1.0, 1.0, 5, 1, A3, need, None) == EINVAL
@@ -367,17 +376,22 @@ def test_dion_validation(L):
 
 
 def test_residual_iterations_rule(L):
-    """The leading iterations that keep their bf16 residual: while the typical
-    normalised singular value of a well-conditioned matrix, 1/sqrt(short side),
-    iterated through p(x) = a x + b x^3 + c x^5, stays below the first x with
-    p'(x) <= a / 2 (0.365 for the quintic, 0.708 for the cubic); at most steps - 1."""
+    """The leading iterations that keep their bf16 residual: the larger of (1) how
+    long the typical normalised singular value of a well-conditioned matrix,
+    1/sqrt(short side), iterated through p(x) = a x + b x^3 + c x^5, stays below
+    the first x with p'(x) <= a / 2 (0.365 for the quintic, 0.708 for the cubic),
+    and (2) steps - 2; at most steps - 1.  Short sides under 96 run on fp32
+    products, which keep no residual."""
     q, cu = (3.4445, -4.775, 2.0315), (1.5, -0.5, 0.0)
     f = mao.ns_residual_iterations
-    assert [f(s, 4 * s, *q, 5) for s in (1, 3, 37, 86, 87, 256, 768, 1020, 1021, 4096, 7168)] == \
-        [0, 0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
-    assert f(14336, 4096, *q, 5) == 2                    # the short side decides
+    assert [f(s, 4 * s, *q, 5) for s in (1, 3, 37, 86, 87, 95, 96, 256, 768, 1020, 1021, 4096, 7168)] == \
+        [0, 0, 0, 0, 0, 0, 3, 3, 3, 3, 3, 3, 3]
+    assert f(14336, 4096, *q, 5) == 3                    # the short side decides
+    assert f(95, 4096, *q, 5) == 0 and f(4096, 95, *q, 5) == 0
     assert f(256, 512, *cu, 5) == 4 and f(256, 512, *cu, 3) == 2 and f(256, 512, *q, 1) == 0
-    assert f(3, 1000, *cu, 5) == 0                       # p(1/sqrt 3) is past 0.708 at once
+    assert f(256, 512, *q, 2) == 1                       # the typical value: p(1/16) = 0.21 < 0.365
+    assert f(4096, 8192, *q, 3) == 2                     # capped at steps - 1
+    assert f(96, 1000, *cu, 5) == 4
     assert f(4096, 4096, *q, 5, "f32") == 0               # fp32 products keep no residual
     assert f(4096, 4096, 0.0, 1.0, 1.0, 5) == 0           # no a X term
     assert L.ns_residual_iterations(0, 5, 1.0, 1.0, 1.0, 5, 1) == EINVAL

@@ -230,10 +230,10 @@ def test_ns_mixed_dtypes_fp32_momentum_bf16_ops():
                                                   ("bf16", QUINTIC, 5, -1.0), ("bf16", QUINTIC, 5, -2.0),
                                                   ("bf16", CUBIC, 5, -2.0)])
 def test_ns_closed_form_spectrum(prec, coeffs, steps, lo):
-    """Singular values spread over one and two decades.  In bf16 the first
-    iteration's output keeps its rounding residual here (short side 256; the small
-    directions grow about 3.4x per iteration together with any noise picked up while
-    small); without it two decades measured 2.55e-2."""
+    """Singular values spread over one and two decades.  In bf16 the outputs of the
+    first three iterations keep their rounding residual (the small directions grow
+    about 3.4x per iteration together with any noise picked up while small); without
+    it two decades measured 2.03e-2 to 2.55e-2."""
     # known spectrum: U = Q1 phi(sigma/||sigma||) Q2^T (closed form of the iteration)
     r, c = 256, 512
     Q1, _ = np.linalg.qr(random_matrix((r, r), [307, 0]))
@@ -255,8 +255,8 @@ def test_ns_closed_form_spectrum(prec, coeffs, steps, lo):
 @pytest.mark.parametrize("steps", [1, 2, 3, 4])
 @pytest.mark.parametrize("shape", [(1024, 2048), (2048, 1024), (768, 2304), (1000, 1000)])
 def test_ns_few_steps_with_residuals(steps, shape):
-    """Two residual iterations (short side 1024: wide, and tall with its final
-    transposed write) and one (768, and the ragged 1000): step counts where the
+    """Fewer steps than five (residual iterations: 0, 1, 2, 2 for 1, 2, 3, 4 steps),
+    wide, tall with its final transposed write, and ragged: step counts where the
     last product reads a residual (2, 3) or not (1, 4)."""
     r, c = shape
     Q1, _ = np.linalg.qr(random_matrix((r, min(r, c)), [316, r]))
@@ -264,6 +264,63 @@ def test_ns_few_steps_with_residuals(steps, shape):
     M = store((Q1 * np.logspace(-2, 0, min(r, c))) @ Q2.T, "bf16")
     (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, steps, "bf16")
     assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, steps)) <= TOL_NS["bf16"]
+
+
+def _spectrum_matrix(r, c, sig, seed):
+    Q1, _ = np.linalg.qr(random_matrix((r, r), [seed, 0]))
+    Q2, _ = np.linalg.qr(random_matrix((c, r), [seed, 1]))
+    return (Q1 * sig) @ Q2.T
+
+
+HARD_SPECTRA = {
+    "three_decades": lambda s: np.logspace(-3, 0, s),
+    "rank_s_over_8_plus_1e-3": lambda s: np.r_[np.ones(s // 8), 1e-3 * np.ones(s - s // 8)],
+    "rank_s_over_8_plus_1e-2": lambda s: np.r_[np.ones(s // 8), 1e-2 * np.ones(s - s // 8)],
+    "two_levels_30x_apart": lambda s: np.r_[np.ones(s // 2), 0.03 * np.ones(s - s // 2)],
+}
+
+
+@pytest.mark.parametrize("kind", sorted(HARD_SPECTRA))
+@pytest.mark.parametrize("shape", [(768, 2304), (1024, 4096)])
+def test_ns_bf16_hard_spectra(kind, shape):
+    """Ill-conditioned momenta against the bf16 gate through ns_orthogonalize: three
+    residual iterations (quintic, five steps) measured 5.5e-3 to 9.9e-3 on these,
+    where two reached 2.2e-2 and one 8.6e-2."""
+    r, c = shape
+    M = store(_spectrum_matrix(r, c, HARD_SPECTRA[kind](r), 330 + r), "bf16")
+    (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, 5, "bf16")
+    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)) <= TOL_NS["bf16"]
+
+
+def test_ns_bf16_hard_spectrum_llama_mlp_shape():
+    """A rank-512 momentum plus noise 1e-3 times smaller at 4096 x 14336 (two residual
+    iterations measured 2.75e-2 here, three 7.7e-3)."""
+    r, c = 4096, 14336
+    M = store(_spectrum_matrix(r, c, HARD_SPECTRA["rank_s_over_8_plus_1e-3"](r), 331), "bf16")
+    (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, 5, "bf16")
+    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)) <= TOL_NS["bf16"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("shape", [(16, 128), (37, 300), (300, 37), (95, 760)])
+def test_ns_small_bf16_problems_run_on_fp32_products(shape, seed):
+    """Short sides below ns_bf16_min_side() (96) run on the fp32 products when bf16 is
+    asked for: bf16 products measured 1.8e-2 to 2.4e-2 on such Gaussian momenta.  With
+    an fp32 direction the result meets the fp32 bar against the oracle."""
+    assert mao.ns_bf16_min_side() == 96
+    M = store(random_matrix(shape, [332, seed]), "bf16")
+    (U,) = _ns_gpu([M], "bf16", "f32", QUINTIC, 5, "bf16")
+    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)) <= TOL_NS["f32"]
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("shape", [(96, 768), (128, 1024)])
+def test_ns_smallest_bf16_products(shape, seed):
+    """The smallest short sides on bf16 products, Gaussian momenta (measured at most
+    1.4e-2 in emulation of the kernels' rounding)."""
+    M = store(random_matrix(shape, [333, seed]), "bf16")
+    (U,) = _ns_gpu([M], "bf16", "bf16", QUINTIC, 5, "bf16")
+    assert rel_fro(U, O.newton_schulz(O.decode(M, "bf16"), *QUINTIC, 5)) <= TOL_NS["bf16"]
 
 
 @pytest.mark.parametrize("in_place", [False, True])
@@ -357,11 +414,11 @@ def test_stage_sequence_equals_ns_orthogonalize():
     A = torch.empty((1, rows, rows), dtype=torch.bfloat16, device="cuda")
     B = torch.empty_like(A)
     # a bf16 wide pad-free momentum: the first iteration reads M and folds the scaling;
-    # the outputs of the first two iterations keep their residual, read by the next
+    # the outputs of the first three iterations keep their residual, read by the next
     M3 = Md.view(1, rows, cols)
     Xlo = torch.empty_like(X[0])
     k = mao.ns_residual_iterations(rows, cols, a, b, c, 5, prec)
-    assert k == 2
+    assert k == 3
     for it in range(5):
         Xc, ss = (M3, sums) if it == 0 else (X[it % 2], None)
         mao.ns_gram(Xc, A, prec, sumsq=ss)

@@ -97,6 +97,7 @@ def _ns_case(shapes, u_dtype="bf16", precision="bf16", steps=5, keep_u=True, see
     ([(768, 2304)] * 3 + [(768, 768)], "bf16", "bf16", 5),     # batched run + a square one
     ([(4096, 1024)], "bf16", "bf16", 5),                       # tall: packed from U
     ([(512, 1000)], "bf16", "bf16", 5),                        # rows not whole words: packed from U
+    ([(64, 1024)], "bf16", "bf16", 5),                         # short side below 96: fp32 products
     ([(512, 1024)], "f32", "f32", 3),                          # fp32 products: packed from U
     ([(512, 1024), (1024, 512)], "bf16", "bf16", 0),           # no iteration: packed from U
 ])
