@@ -151,12 +151,22 @@ __global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, flo
   float* C = g.C + b * g.sC;
   const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
   if (col < g.N) {
+    // all 16 addend values are loaded before the first store: Z may be C
+    // itself (the in-place updates), and a lane reads only the entries it
+    // writes, so no store can change a value another lane still has to read.
+    // Interleaved, each load would wait for the store before it.
+    float z[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      z[v] = (g.beta != 0.0f && row < g.M) ? Z[row * g.ldz + col] : 0.0f;
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (row >= g.M) continue;
       float o = g.alpha * acc[v];
-      if (g.beta != 0.0f) o = fmaf(g.beta, Z[row * g.ldz + col], o);
+      if (g.beta != 0.0f) o = fmaf(g.beta, z[v], o);
       C[row * g.ldc + col] = o;
     }
   }

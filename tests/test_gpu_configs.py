@@ -109,6 +109,7 @@ def check_ns(wl, res, k, matrices):
         assert err <= TOL_NS[wl.precision], f"NS error {err:.3e} on matrix {j} of worker {k}"
         refs[j] = ref.ravel()
     print(f"  worker {k}: worst NS error over {len(refs)} matrices {worst:.3e}")
+    NS_WORST[wl.name] = max(NS_WORST.get(wl.name, 0.0), worst)
     return refs
 
 
@@ -158,18 +159,26 @@ def entries_of(res, matrices):
     return np.concatenate([np.arange(offs[j], offs[j + 1]) for j in matrices])
 
 
-def report(name, agreement):
-    """Print the four rates; with MUON_RECORD_DIR set, also append them as a JSON line
-    to sign_agreement.jsonl there (the record kept with the measurements)."""
+# worst Newton-Schulz error against the oracle seen so far, per workload name
+NS_WORST = {}
+
+
+def report(name, agreement, wl=None):
+    """Print the four rates; with MUON_RECORD_DIR set, also append them (and the
+    worst NS error checked so far on ``wl``) as a JSON line to sign_agreement.jsonl
+    there (the record kept with the measurements)."""
     raw_w, dec_w, raw_v, dec_v = (float(x) for x in agreement)
     print(f"  {name} sign disagreement: worker raw {raw_w:.2e} decided {dec_w:.2e}; "
           f"vote raw {raw_v:.2e} decided {dec_v:.2e}")
     out = os.environ.get("MUON_RECORD_DIR")
     if out:
         os.makedirs(out, exist_ok=True)
+        rec = {"workload": name, "worker_raw": raw_w, "worker_decided": dec_w,
+               "vote_raw": raw_v, "vote_decided": dec_v}
+        if wl is not None and wl.name in NS_WORST:
+            rec["ns_error_worst"] = NS_WORST[wl.name]
         with open(os.path.join(out, "sign_agreement.jsonl"), "a") as f:
-            f.write(json.dumps({"workload": name, "worker_raw": raw_w, "worker_decided": dec_w,
-                                "vote_raw": raw_v, "vote_decided": dec_v}) + "\n")
+            f.write(json.dumps(rec) + "\n")
 
 
 def check_second_step(wl, res, matrices):
@@ -190,7 +199,7 @@ def test_c1_fp32_256_cubic():
     assert np.array_equal(first["vote"], O.majority_vote(first["bits"], wl.numel))
     oracle_U = {k: direction_on(wl, first, k, [0]) for k in range(wl.workers)}
     agreement = sign_agreement(first, oracle_U, entries_of(first, [0]))
-    report(wl.name, agreement)
+    report(wl.name, agreement, wl)
     assert agreement[0] <= 1e-3 and agreement[2] <= 1e-3
     check_second_step(wl, second, [0])
 
@@ -207,7 +216,7 @@ def test_c2_gpt2_small_layer_set():
     check_vote_update(wl, first)
     oracle_U = {k: direction_on(wl, first, k, sample) for k in range(wl.workers)}
     agreement = sign_agreement(first, oracle_U, entries_of(first, sample))
-    report(wl.name, agreement)
+    report(wl.name, agreement, wl)
     assert agreement[1] <= 1e-3 and agreement[3] <= 1e-3
     check_second_step(wl, second, sample)
 
@@ -221,7 +230,7 @@ def test_c3_batched_1024_sign_pack():
     check_ns(wl, first, 0, sample)
     agreement = sign_agreement(first, {0: direction_on(wl, first, 0, sample)},
                                entries_of(first, sample))
-    report(wl.name, agreement)
+    report(wl.name, agreement, wl)
     assert agreement[1] <= 1e-3
     check_second_step(wl, second, [0, 127])
 
@@ -238,9 +247,10 @@ def test_c4_llama_mlp_4096x14336():
     for k in range(wl.workers):
         err = rel_fro(first["U"][k], oracle_U[k])
         print(f"  worker {k}: NS error {err:.3e}")
+        NS_WORST[wl.name] = max(NS_WORST.get(wl.name, 0.0), err)
         assert err <= TOL_NS["bf16"]
     agreement = sign_agreement(first, oracle_U, np.arange(wl.numel))
-    report(wl.name, agreement)
+    report(wl.name, agreement, wl)
     assert agreement[1] <= 1e-3 and agreement[3] <= 1e-3
     del oracle_U
     check_second_step(wl, second, [0])
@@ -254,7 +264,7 @@ def test_c5_dense_ffn_7168x18432():
     check_vote_update(wl, first)
     refs = {k: check_ns(wl, first, k, [0])[0] for k in (0, 1)}
     agreement = sign_agreement(first, refs, np.arange(wl.numel))
-    report(wl.name + ", workers 0 and 1", agreement)
+    report(wl.name + ", workers 0 and 1", agreement, wl)
     assert agreement[1] <= 1e-3
     del refs
     check_second_step(wl, second, [0])
