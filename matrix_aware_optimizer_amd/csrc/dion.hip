@@ -172,6 +172,176 @@ __global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, flo
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same product with its operands staged by global -> LDS DMA
+// (global_load_lds_dwordx4: 16 bytes per lane straight into LDS, no register
+// round trip) in an S-stage ring, so S - 1 k-tiles are in flight while one is
+// multiplied.  Used when both operands allow 16-byte chunks: stride 1 along
+// one dimension, the other strides multiples of 4 floats, 16-byte aligned
+// base, and the chunked extent (k for a k-contiguous operand, the output
+// dimension otherwise) a multiple of 4.
+//
+// An operand tile (64 of the output dimension x 32 of k, 8 KB) is 512 chunks;
+// DMA instruction i of wave w fills chunks [64 (2 w + i), +64), one per lane.
+//  * k-contiguous operand ("ck"): LDS rows of 32 k (128 bytes) per output
+//    index o, chunk c (k = 4c .. 4c + 3) of row o at slot c ^ (o & 7).  A
+//    lane reads 4 k-values of one row with ds_read_b128; the 8 lanes of a
+//    read group touch 8 different slots, so all 32 banks.
+//  * output-contiguous operand ("co"): LDS rows of 64 o (256 bytes) per k,
+//    unswizzled; a half-wave reads 32 consecutive floats of one row.
+// k-values are paired across the two half-waves of v_mfma_f32_32x32x2f32 as
+// (k, k + 4) within each 8-deep group, so a ck lane's ds_read_b128 feeds 4
+// MFMAs; a co lane reads the matching row for each MFMA.
+// Chunks past the contraction (k >= K) load from a 1 KB page of zeros in the
+// workspace, so both operands are zero there and the tail adds nothing;
+// chunks past the output dimension load a clamped valid chunk, whose products
+// land only in rows or columns that are never stored.
+// The waits are explicit: each wave issues exactly 4 DMA instructions per
+// k-tile (dummies from the zero page after the last tile), so s_waitcnt
+// vmcnt(4 (S - 2)) means its chunks of the oldest stage have landed, and the
+// s_barrier after it means every wave's have.
+// ---------------------------------------------------------------------------
+constexpr int kDmaTileBytes = kDT * kDK * 4;   // one operand tile: 8 KB
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global memory to LDS bytes [lds_addr + 16 lane).  M0
+// is set here and used by nothing else in the kernel (no other LDS-DMA, no
+// relative register indexing, no messages).
+__device__ __forceinline__ void dion_dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void dion_wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+struct DmaOperand {
+  const float* base;     // this batch entry
+  int64_t s_out, s_k;    // element strides along the output dimension and along k
+  int64_t n_out, K;
+  // global address of the chunk that LDS chunk slot p of the tile at (o0, k0) holds
+  template <bool CK>
+  __device__ __forceinline__ const float* chunk(int p, int64_t o0, int64_t k0, const float* zero, int lane) const {
+    int64_t o, k;
+    if constexpr (CK) {
+      const int row = p >> 3, c = (p & 7) ^ (row & 7);
+      o = o0 + row;
+      k = k0 + 4 * c;
+      if (o >= n_out) o = n_out - 1;
+    } else {
+      k = k0 + (p >> 4);
+      o = o0 + 4 * (p & 15);
+      if (o >= n_out) o = n_out - 4;
+    }
+    return k < K ? base + o * s_out + k * s_k : zero + 4 * lane;
+  }
+};
+
+template <int S, bool ACK, bool BCK>
+__global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits, float* part, const float* zero) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int64_t b = blockIdx.z / splits;
+  const int sp = blockIdx.z % splits;
+  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const int half = lane >> 5, l32 = lane & 31;
+  const DmaOperand oa{g.A + b * g.sA, g.a_i, g.a_k, g.M, g.K};
+  const DmaOperand ob{g.B + b * g.sB, g.b_j, g.b_k, g.N, g.K};
+  const int64_t ktiles = (g.K + kDK - 1) / kDK;
+  const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
+  const int nk = static_cast<int>(kt1 - kt0);
+  const uint32_t lds0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
+  // stage s: A tile at s * 16 KB, B tile 8 KB after it
+  auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
+    const int64_t k0 = kt * kDK;
+    const uint32_t sa = lds0 + stage * 2 * kDmaTileBytes, sb = sa + kDmaTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot0 = 64 * (2 * wave + i);
+      // beyond the last k-tile: dummies from the zero page (k0 >= K)
+      dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, lane), sa + 16 * slot0);
+      dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, lane), sb + 16 * slot0);
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s, kt0 + s);
+  for (int it = 0; it < nk; ++it) {
+    dion_wait_vm_barrier<4 * (S - 2)>();
+    issue((it + S - 1) % S, kt0 + it + S - 1);
+    const char* ta = dsm + (it % S) * 2 * kDmaTileBytes;
+    const char* tb = ta + kDmaTileBytes;
+#pragma unroll
+    for (int gk = 0; gk < 4; ++gk) {
+      float av[4], bv[4];
+      if constexpr (ACK) {
+        const int row = wi + l32, c = 2 * gk + half;
+        const float4 v = *reinterpret_cast<const float4*>(ta + row * 128 + ((c ^ (row & 7)) << 4));
+        av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          av[j] = *reinterpret_cast<const float*>(ta + ((8 * gk + j + 4 * half) * kDT + wi + l32) * 4);
+      }
+      if constexpr (BCK) {
+        const int row = wj + l32, c = 2 * gk + half;
+        const float4 v = *reinterpret_cast<const float4*>(tb + row * 128 + ((c ^ (row & 7)) << 4));
+        bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bv[j] = *reinterpret_cast<const float*>(tb + ((8 * gk + j + 4 * half) * kDT + wj + l32) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the dummy stages have landed
+  const int64_t col = j0 + wj + l32;
+  if (splits > 1) {
+    float* Pp = part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N;
+    if (col < g.N) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (row < g.M) Pp[row * g.N + col] = acc[v];
+      }
+    }
+    return;
+  }
+  float* C = g.C + b * g.sC;
+  const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+  if (col < g.N) {
+    float z[16];   // every addend value before the first store (Z may be C)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+      z[v] = (g.beta != 0.0f && row < g.M) ? Z[row * g.ldz + col] : 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (row >= g.M) continue;
+      float o = g.alpha * acc[v];
+      if (g.beta != 0.0f) o = fmaf(g.beta, z[v], o);
+      C[row * g.ldc + col] = o;
+    }
+  }
+}
+
+// the zero page the DMA kernel's tail chunks read (1 KB)
+constexpr int kZeroPageFloats = 256;
+__global__ __launch_bounds__(256) void zero_page_kernel(float* z) { z[threadIdx.x] = 0.0f; }
+
 // C[b](i,j) = alpha * sum_s part[s][b](i,j) + beta * Z[b](i,j), ranges added in order
 __global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const float* __restrict__ part,
                                                     int64_t batch) {
@@ -271,29 +441,33 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
 
   for (int J = 0; J < nb; ++J) {
     const int c0 = J * kCb;
-    if (J > 0 && tid < rp - c0) {
-      // panel: A(i, c0 + k) -= sum_{m < c0} L(i, m) L(c0 + k, m), lower part;
-      // each thread a 4 x 4 tile (rows c0 + 4 tr + u, columns c0 + 4 tc + v)
-      const int i0 = c0 + 4 * (tid >> 2), k0 = c0 + 4 * (tid & 3);
-      float acc[4][4] = {};
-#pragma unroll 4
-      for (int m = 0; m < c0; ++m) {
-        float av[4], bv[4];
+    if (J > 0) {
+      // panel: A(i, c0 + k) -= sum_{m < c0} L(i, m) L(c0 + k, m), lower part,
+      // on fp32 matrix cores: wave w takes the 16-row blocks J + w, J + w + 4,
+      // ...; v_mfma_f32_16x16x4f32 with lane l supplying L(16 ib + l % 16,
+      // m + l / 16) and L(c0 + l % 16, m + l / 16), and holding result rows
+      // 4 (l / 16) .. + 3 of column l % 16
+      const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+      for (int ib = J + wave; ib < nb; ib += 4) {
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float* ar = S + (kCb * ib + li) * ld + lk;
+        const float* br = S + (c0 + li) * ld + lk;
+        for (int m = 0; m < c0; m += kCb) {   // c0 is a multiple of 16: four MFMAs per pass
+          float a4[4], b4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[u] = S[(i0 + u) * ld + m];
-          bv[u] = S[(k0 + u) * ld + m];
+          for (int q = 0; q < 4; ++q) {
+            a4[q] = ar[m + 4 * q];
+            b4[q] = br[m + 4 * q];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+        for (int v = 0; v < 4; ++v) {
+          const int row = kCb * ib + 4 * lk + v;
+          if (ib > J || li <= 4 * lk + v) S[row * ld + c0 + li] -= acc[v];
+        }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (k0 + v <= i0 + u) S[(i0 + u) * ld + k0 + v] -= acc[u][v];
     }
     __syncthreads();
     if (tid < 64) {
@@ -372,28 +546,27 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
   __syncthreads();
   // X_IJ(i, j) = -sum_{16 J <= c < 16 I} S(16 I + i, c) S(16 J + j, c), stored at S(16 J + j, 16 I + i)
   for (int d = 1; d < nb; ++d) {
-    if (tid < kCb * (nb - d)) {
-      // block (J + d, J), J = tid / 16; each thread a 4 x 4 tile
-      const int J = tid >> 4, I = J + d;
-      const int ia = kCb * I + 4 * ((tid >> 2) & 3), jb = kCb * J + 4 * (tid & 3);
-      float acc[4][4] = {};
-#pragma unroll 4
-      for (int c = kCb * J; c < kCb * I; ++c) {
-        float av[4], bv[4];
+    // block (J + d, J) on fp32 matrix cores, one wave per block (J = w, w + 4,
+    // ...): lane l supplies S(16 I + l % 16, c + l / 16) and S(16 J + l % 16,
+    // c + l / 16) and holds rows 4 (l / 16) .. + 3 of column l % 16
+    const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+    for (int J = wave; J < nb - d; J += 4) {
+      const int I = J + d;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float* ar = S + (kCb * I + li) * ld + lk;
+      const float* br = S + (kCb * J + li) * ld + lk;
+      for (int c = kCb * J; c < kCb * I; c += kCb) {   // four MFMAs per pass
+        float a4[4], b4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[u] = S[(ia + u) * ld + c];
-          bv[u] = S[(jb + u) * ld + c];
+        for (int q = 0; q < 4; ++q) {
+          a4[q] = ar[c + 4 * q];
+          b4[q] = br[c + 4 * q];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) S[(jb + v) * ld + ia + u] = -acc[u][v];
+      for (int v = 0; v < 4; ++v) S[(kCb * J + li) * ld + kCb * I + 4 * lk + v] = -acc[v];
     }
     __syncthreads();
   }
@@ -504,19 +677,49 @@ size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
   return s > 1 ? static_cast<size_t>(s) * batch * M * N * 4 : 0;
 }
 
+#ifndef MUON_DION_STAGES
+#define MUON_DION_STAGES 2
+#endif
+constexpr int kDionStages = MUON_DION_STAGES;   // DMA ring depth (16 KB per stage)
+
+// an operand the DMA kernel can stage: 16-byte chunks along its contiguous
+// dimension (k when s_k == 1, else the output dimension), whole chunks only
+bool dma_operand_ok(const float* p, int64_t s_batch, int64_t s_out, int64_t s_k, int64_t n_out, int64_t K) {
+  if (!aligned16(p) || s_batch % 4 != 0) return false;
+  if (s_k == 1) return s_out % 4 == 0 && K % 4 == 0;
+  return s_out == 1 && s_k % 4 == 0 && n_out % 4 == 0;
+}
+
+template <bool ACK, bool BCK>
+void launch_dma(const DGemm& g, dim3 grid, int splits, float* part, const float* zero, hipStream_t st) {
+  launch_kernel(dion_gemm_dma_kernel<kDionStages, ACK, BCK>, grid, dim3(256), kDionStages * 2 * kDmaTileBytes, st, g,
+                splits, part, zero);
+}
+
+// zero: the workspace's zero page (NULL keeps every product on the
+// register-staged kernel)
 int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, int64_t sB, int64_t b_k,
           int64_t b_j, const float* Z, int64_t sZ, int64_t ldz, float* C, int64_t sC, int64_t ldc,
-          int64_t M, int64_t N, int64_t K, float alpha, float beta, int64_t batch, float* part, hipStream_t st) {
+          int64_t M, int64_t N, int64_t K, float alpha, float beta, int64_t batch, float* part,
+          const float* zero, hipStream_t st) {
   DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta};
   const int splits = gemm_splits(M, N, K, batch);
   const dim3 grid((N + kDT - 1) / kDT, (M + kDT - 1) / kDT, batch * splits);
-  // 16-byte operand loads: contiguous dimension stride 1, every other stride a
-  // multiple of 4 floats, aligned base
-  auto vec_ok = [](const float* p, int64_t s_batch, int64_t s_a, int64_t s_b) {
-    return aligned16(p) && (s_a == 1 || s_b == 1) && s_batch % 4 == 0 && (s_a == 1 ? s_b : s_a) % 4 == 0;
-  };
-  const int a_vec = vec_ok(A, sA, a_i, a_k), b_vec = vec_ok(B, sB, b_k, b_j);
-  launch_kernel(dion_gemm_kernel, grid, dim3(256), 0, st, g, splits, part, a_vec, b_vec);
+  if (zero && dma_operand_ok(A, sA, a_i, a_k, M, K) && dma_operand_ok(B, sB, b_j, b_k, N, K)) {
+    const bool ack = a_k == 1, bck = b_k == 1;
+    if (ack && bck) launch_dma<true, true>(g, grid, splits, part, zero, st);
+    else if (ack) launch_dma<true, false>(g, grid, splits, part, zero, st);
+    else if (bck) launch_dma<false, true>(g, grid, splits, part, zero, st);
+    else launch_dma<false, false>(g, grid, splits, part, zero, st);
+  } else {
+    // 16-byte operand loads: contiguous dimension stride 1, every other stride a
+    // multiple of 4 floats, aligned base
+    auto vec_ok = [](const float* p, int64_t s_batch, int64_t s_a, int64_t s_b) {
+      return aligned16(p) && (s_a == 1 || s_b == 1) && s_batch % 4 == 0 && (s_a == 1 ? s_b : s_a) % 4 == 0;
+    };
+    const int a_vec = vec_ok(A, sA, a_i, a_k), b_vec = vec_ok(B, sB, b_k, b_j);
+    launch_kernel(dion_gemm_kernel, grid, dim3(256), 0, st, g, splits, part, a_vec, b_vec);
+  }
   if (splits > 1) {
     const int64_t n = batch * M * N;
     launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
@@ -581,7 +784,7 @@ std::vector<DRun> dion_runs(const muon_dion_problem* p, int count) {
 // buffer serves every product.
 struct DLayout {
   std::vector<size_t> p0, p1, R;
-  size_t gram, linv, part, total;
+  size_t gram, linv, part, zero, total;
 };
 
 DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
@@ -602,6 +805,7 @@ DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
   L.gram = take(static_cast<size_t>(count) * rk * rk * 4);
   L.linv = take(static_cast<size_t>(count) * rk * rk * 4);
   L.part = take(part);
+  L.zero = take(kZeroPageFloats * sizeof(float));
   L.total = off;
   return L;
 }
@@ -680,10 +884,20 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
   float* Gm = reinterpret_cast<float*>(ws + L.gram);
   float* Li = reinterpret_cast<float*>(ws + L.linv);
   float* part = reinterpret_cast<float*>(ws + L.part);
+#ifndef MUON_DION_DMA
+#define MUON_DION_DMA 1
+#endif
+  // the DMA products' zero page, cleared on every call (the workspace's
+  // contents on entry do not matter)
+  float* zp = MUON_DION_DMA ? reinterpret_cast<float*>(ws + L.zero) : nullptr;
   auto Pbuf = [&](size_t k, int which) {
     return reinterpret_cast<float*>(ws + (which == 0 ? L.p0[k] : L.p1[k]));
   };
   int status;
+  if (zp) {
+    launch_kernel(zero_page_kernel, dim3(1), dim3(kZeroPageFloats), 0, st, zp);
+    if ((status = launch_status()) != MUON_OK) return status;
+  }
   // B = M + G in place, and P = B Q
   for (size_t k = 0; k < runs.size(); ++k) {
     const DRun& run = runs[k];
@@ -696,7 +910,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
                                                                     run.sG, mn, vec);
     if ((status = launch_status()) != MUON_OK) return status;
     status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
-                   m * r, r, m, r, n, 1.0f, 0.0f, b, part, st);
+                   m * r, r, m, r, n, 1.0f, 0.0f, b, part, zp, st);
     if (status != MUON_OK) return status;
   }
   // orth(P), twice: the Grams P^T P of all matrices, one factorisation launch,
@@ -706,7 +920,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
       const DRun& run = runs[k];
       const float* P = Pbuf(k, pass);
       status = dgemm(P, run.m * r, 1, r, P, run.m * r, r, 1, nullptr, 0, 0, Gm + run.first * r * r, r * r, r,
-                     r, r, run.m, 1.0f, 0.0f, run.count, part, st);
+                     r, r, run.m, 1.0f, 0.0f, run.count, part, zp, st);
       if (status != MUON_OK) return status;
     }
     launch_kernel(chol_inv_kernel, dim3(count), dim3(256), lds, st, Gm, r * r, Li, r * r, rank);
@@ -714,7 +928,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     for (size_t k = 0; k < runs.size(); ++k) {
       const DRun& run = runs[k];
       status = dgemm(Pbuf(k, pass), run.m * r, r, 1, Li + run.first * r * r, r * r, 1, r, nullptr, 0, 0,
-                     Pbuf(k, 1 - pass), run.m * r, r, run.m, r, r, 1.0f, 0.0f, run.count, part, st);
+                     Pbuf(k, 1 - pass), run.m * r, r, run.m, r, r, 1.0f, 0.0f, run.count, part, zp, st);
       if (status != MUON_OK) return status;
     }
   }
@@ -728,10 +942,10 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     float* R = reinterpret_cast<float*>(ws + L.R[k]);
     const float* Pf = Pbuf(k, 0);      // two passes: back in buffer 0
     const int64_t m = run.m, n = run.n, b = run.count;
-    status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, st);
+    status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, zp, st);
     if (status != MUON_OK) return status;
     status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - mu), 1.0f, b,
-                   part, st);
+                   part, zp, st);
     if (status != MUON_OK) return status;
     {
       // chunks of at least 64 rows and at most m chunks, so the partial sums
@@ -743,7 +957,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
       launch_kernel(colscale_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, Q, run.sQ, n, rank, rows_per, nch);
     }
     if ((status = launch_status()) != MUON_OK) return status;
-    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, st);
+    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, zp, st);
     if (status != MUON_OK) return status;
   }
   return MUON_OK;
