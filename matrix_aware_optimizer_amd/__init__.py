@@ -5,7 +5,7 @@ C ABI, declared in ``include/muon.h``); this package is its ctypes binding
 plus host-side orchestration.  PyTorch provides device memory and streams.
 """
 from ._abi import (  # noqa: F401
-    MUON_BF16, MUON_F32, MUON_MAX_NUMEL, MUON_MAX_VOTERS, MUON_NS_PAD, MuonError, apply_update, lib,
+    MUON_BF16, MUON_F32, MUON_MAX_NUMEL, MUON_MAX_VOTERS, MUON_NS_PAD, MuonError, PreparedNS, apply_update, lib,
     majority_vote, muon_momentum, muon_momentum_workspace_bytes, muon_version, ns_apply,
     ns_gram, ns_normalize, ns_orthogonalize, ns_poly, ns_workspace_bytes, packed_words,
     sign_pack, status_string, vote_and_update,

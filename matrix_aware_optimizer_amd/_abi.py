@@ -252,6 +252,35 @@ def ns_orthogonalize(problems: Sequence[ProblemLike], a: float, b: float, c: flo
         _stream(stream)))
 
 
+class PreparedNS:
+    """One ns_orthogonalize call whose problem array is marshalled once.
+
+    For a caller that orthogonalises the same device buffers every step (a
+    parameter set's momentum, directions and sign words): building the ctypes
+    array of a layer set costs the host hundreds of microseconds, long enough
+    to leave the GPU idle between the momentum and the first product.  Calling
+    the object only enqueues the work, on ``stream`` (default: the current one)."""
+
+    def __init__(self, problems: Sequence[ProblemLike], a: float, b: float, c: float, steps: int,
+                 precision="bf16", workspace: Optional[torch.Tensor] = None):
+        if len(problems) == 0:
+            raise ValueError("no problems")
+        self._problems = list(problems)     # keeps the tensors alive
+        self._arr = _problems(self._problems)
+        self._n = len(self._problems)
+        prec = precision_code(precision)
+        self._args = (float(a), float(b), float(c), int(steps), prec)
+        need = int(lib().ns_workspace_bytes(self._arr, self._n, prec))
+        self.workspace = _workspace(need, self._problems[0][0], workspace)
+        self._ws = (_dev(self.workspace, "workspace"), self.workspace.numel() * self.workspace.element_size())
+        if self._ws[1] < need:
+            raise ValueError(f"workspace holds {self._ws[1]} bytes, the call needs {need}")
+
+    def __call__(self, stream=None) -> None:
+        _check("ns_orthogonalize", lib().ns_orthogonalize(self._arr, self._n, *self._args, *self._ws,
+                                                          _stream(stream)))
+
+
 def _batch3(t: torch.Tensor) -> Tuple[int, int, int]:
     if t.dim() == 2:
         return 1, t.shape[0], t.shape[1]

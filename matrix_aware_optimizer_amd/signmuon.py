@@ -69,6 +69,7 @@ class SignMuonStep:
         del probe_M
         self.ns_workspace = torch.empty(max(ns_bytes, 1), dtype=torch.uint8, device=self.device)
         self.mom_workspace = torch.empty(max(mom_bytes, 1), dtype=torch.uint8, device=self.device)
+        self._prepared = {}   # marshalled orthogonalisation calls (see orthogonalize)
 
     def signs_fused(self, j: int) -> bool:
         """Whether matrix j's packed signs come from its last product (rule of
@@ -99,9 +100,18 @@ class SignMuonStep:
     def orthogonalize(self, M: torch.Tensor, bits_row: Optional[torch.Tensor] = None) -> None:
         """Polar directions into ``self.U`` (see ``keep_direction``); with ``bits_row``
         also their packed signs (requires ``signs_per_matrix``)."""
-        a, b, c = self.coeffs
-        _abi.ns_orthogonalize(self._problems(M, bits_row), a, b, c, self.ns_steps, self.precision,
-                              self.ns_workspace)
+        # the marshalled call is kept per (momentum, sign words) buffer pair
+        key = (M.data_ptr(), M.numel(), bits_row.data_ptr() if bits_row is not None else None,
+               self.keep_direction)
+        call = self._prepared.get(key)
+        if call is None:
+            a, b, c = self.coeffs
+            call = _abi.PreparedNS(self._problems(M, bits_row), a, b, c, self.ns_steps, self.precision,
+                                   self.ns_workspace)
+            if len(self._prepared) >= 64:
+                self._prepared.clear()
+            self._prepared[key] = call
+        call()
 
     def pack(self, bits_row: torch.Tensor) -> None:
         _abi.sign_pack(self.U, bits_row)

@@ -118,6 +118,30 @@ def test_ns_orthogonalize_signs_only():
     assert np.array_equal(from_dev(with_u), from_dev(only))
 
 
+def test_prepared_call_matches_direct_calls():
+    """PreparedNS (the problem array marshalled once) gives the same words as
+    ns_orthogonalize, on two calls in a row and after the momentum changes in place
+    (the norms are computed by the call itself here).  SignMuonStep keeps one such
+    call per buffer pair; its second step is checked in the workload tests."""
+    shapes = [(768, 2304)] * 2 + [(768, 768), (3072, 768)]
+    Mh, offs, U, direct = _ns_case(shapes, seed=9)
+    _, _, _, direct2 = _ns_case(shapes, seed=10)
+    M1 = to_dev(Mh, "bf16")
+    U2 = torch.zeros_like(M1)
+    bits = torch.zeros(direct.numel(), dtype=torch.int64, device="cuda")
+    probs = [(M1[offs[j]:offs[j + 1]].view(*shp), U2[offs[j]:offs[j + 1]].view(*shp), None,
+              bits[offs[j] // 64:(offs[j + 1] + 63) // 64]) for j, shp in enumerate(shapes)]
+    call = mao.PreparedNS(probs, *QUINTIC, 5, "bf16")
+    for _ in range(2):
+        bits.zero_()
+        call()
+        assert np.array_equal(from_dev(bits), from_dev(direct))
+    Mh2, _, _, _ = _ns_case(shapes, seed=10)
+    M1.copy_(to_dev(Mh2, "bf16"))
+    call()
+    assert np.array_equal(from_dev(bits), from_dev(direct2))
+
+
 def test_ns_signs_agree_with_oracle_direction():
     """Against the fp64 oracle's direction: signs agree wherever the oracle's entry is
     clear of the bf16 iteration's error (|U| above a quarter of its RMS, more than ten
