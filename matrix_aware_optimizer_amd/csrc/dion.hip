@@ -242,7 +242,7 @@ struct DmaOperand {
   }
 };
 
-template <int S, bool ACK, bool BCK>
+template <int S, bool ACK, bool BCK, bool ZPRE>
 __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits, float* part, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int64_t b = blockIdx.z / splits;
@@ -275,6 +275,21 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s, kt0 + s);
+  // ZPRE (an addend and no split): the addend is read before the contraction,
+  // so its latency overlaps the k-loop (the m x n updates have a short k and a
+  // full tile of addend each).  Z may be C itself: every lane reads only the
+  // entries it writes, and reads them all before its first store.
+  const int64_t col = j0 + wj + l32;
+  const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+  float z[16];
+  auto load_z = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+      z[v] = (g.beta != 0.0f && row < g.M && col < g.N) ? Z[row * g.ldz + col] : 0.0f;
+    }
+  };
+  if constexpr (ZPRE) load_z();
   for (int it = 0; it < nk; ++it) {
     dion_wait_vm_barrier<4 * (S - 2)>();
     issue((it + S - 1) % S, kt0 + it + S - 1);
@@ -306,7 +321,6 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the dummy stages have landed
-  const int64_t col = j0 + wj + l32;
   if (splits > 1) {
     float* Pp = part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N;
     if (col < g.N) {
@@ -319,14 +333,8 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
     return;
   }
   float* C = g.C + b * g.sC;
-  const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+  if constexpr (!ZPRE) load_z();
   if (col < g.N) {
-    float z[16];   // every addend value before the first store (Z may be C)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
-      z[v] = (g.beta != 0.0f && row < g.M) ? Z[row * g.ldz + col] : 0.0f;
-    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -692,8 +700,16 @@ bool dma_operand_ok(const float* p, int64_t s_batch, int64_t s_out, int64_t s_k,
 
 template <bool ACK, bool BCK>
 void launch_dma(const DGemm& g, dim3 grid, int splits, float* part, const float* zero, hipStream_t st) {
-  launch_kernel(dion_gemm_dma_kernel<kDionStages, ACK, BCK>, grid, dim3(256), kDionStages * 2 * kDmaTileBytes, st, g,
-                splits, part, zero);
+  const uint32_t lds = kDionStages * 2 * kDmaTileBytes;
+  // only k-contiguous operands with an addend (the m x n updates) read it first
+  if constexpr (ACK && BCK) {
+    if (splits == 1 && g.beta != 0.0f) {
+      launch_kernel(dion_gemm_dma_kernel<kDionStages, true, true, true>, grid, dim3(256), lds, st, g, splits, part,
+                    zero);
+      return;
+    }
+  }
+  launch_kernel(dion_gemm_dma_kernel<kDionStages, ACK, BCK, false>, grid, dim3(256), lds, st, g, splits, part, zero);
 }
 
 // zero: the workspace's zero page (NULL keeps every product on the
