@@ -78,8 +78,16 @@ enum Epi { EPI_STORE = 0, EPI_AXPBY = 1, EPI_FINAL = 2 };
 // CUs, n_p = M / BM): every off-diagonal tile runs as two K halves and every
 // diagonal tile as one unit that computes only its lower half, n_p^2 units of
 // about half a tile each instead of n_p (n_p + 1) / 2 whole tiles, which
-// would leave the other CUs idle.
-enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2 };
+// would leave the other CUs idle.  SPLIT_DIAG: unit v is the lower half of
+// diagonal tile v.  SPLIT_TRI (symmetric products over several rounds of the
+// CUs): the n_p (n_p - 1) / 2 off-diagonal tiles whole, row by row, then the n_p
+// diagonal tiles as lower halves, so no unit computes the upper half of a
+// diagonal tile (the same unit count as whole tiles, less work).
+enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2, SPLIT_TRI = 3 };
+#ifndef MUON_SYRK_TRI
+#define MUON_SYRK_TRI 1
+#endif
+constexpr bool kSyrkTri = MUON_SYRK_TRI != 0;
 // default bound on the polls of the second K half waiting for the first
 // one's partial (each poll sleeps ~128 cycles; the first half never needs
 // more than microseconds, the bound only keeps a wait from outliving its
@@ -628,6 +636,20 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
     // unit v: the lower half of diagonal tile v
     tm = tn = bid;
     diag_half = true;
+  } else if (DIAGS && g.split_mode == SPLIT_TRI) {
+    // units [0, n_p (n_p - 1) / 2): off-diagonal tile (i, j), j < i, row by row;
+    // then the lower half of diagonal tile v - n_p (n_p - 1) / 2
+    const int64_t np = g.M / BM, noff = np * (np - 1) / 2;
+    if (bid < noff) {
+      int64_t i = static_cast<int64_t>((1.0 + sqrt(1.0 + 8.0 * double(bid))) * 0.5);
+      while (i * (i - 1) / 2 > bid) --i;
+      while ((i + 1) * i / 2 <= bid) ++i;
+      tm = i;
+      tn = bid - i * (i - 1) / 2;
+    } else {
+      tm = tn = bid - noff;
+      diag_half = true;
+    }
   } else if (HALVES) {
     // n_p (n_p - 1) units per batch entry: unit v is column half v & 1 of
     // off-diagonal tile t = v >> 1 = i (i - 1) / 2 + j (row i, column j < i);
@@ -1417,6 +1439,12 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
       g.partials = reinterpret_cast<float*>(sc.base + kSplitCounterBytes);
       grid = p.units;
     }
+  }
+  // several rounds of whole symmetric tiles: diagonal tiles as lower halves
+  constexpr bool DIAGS = SYRK && BM == 256 && BN == 256 && C_::W == 8;
+  if (DIAGS && kSyrkTri && g.split_mode == SPLIT_NONE && g.M / BM >= 2) {
+    const int64_t cus = device_cus();
+    if (cus > 0 && tpb * batch > cus) g.split_mode = SPLIT_TRI;
   }
   auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SYRK, NN, EPI>;
   static std::atomic<uint64_t> configured{0};   // devices with the LDS limit set
