@@ -80,8 +80,11 @@ __global__ __launch_bounds__(256) void normalize_kernel(const TM* __restrict__ M
 
 // Tall matrix (rows > cols): X0 = M^T, transposed through LDS one 64 x 64 tile
 // at a time so that both the reads (along M's rows) and the writes (along
-// X's rows) are coalesced.
-template <typename TM, typename TX>
+// X's rows) are coalesced.  With VEC (cols and strideM multiples of 8, M
+// 16-byte aligned) every lane moves 8 consecutive entries per access: M in
+// whole 8-entry groups, each inside or outside the matrix; X's rows are
+// padded to multiples of 256, so its 8-entry groups are always whole.
+template <typename TM, typename TX, bool VEC>
 __global__ __launch_bounds__(256) void normalize_tall_kernel(const TM* __restrict__ M, int64_t strideM,
                                                             int64_t rows, int64_t cols,
                                                             const float* __restrict__ sumsq,
@@ -93,14 +96,42 @@ __global__ __launch_bounds__(256) void normalize_tall_kernel(const TM* __restric
   const int64_t j0 = int64_t(blockIdx.x) * 64;   // X columns = M rows
   const float scale = frobenius_scale(sumsq, b, stride_sumsq);
   const TM* Mb = M + b * strideM;
-  const int c = threadIdx.x & 63;
-  for (int r = threadIdx.x >> 6; r < 64; r += 4) {
-    const int64_t mr = j0 + r, mc = i0 + c;
-    tile[r][c] = (mr < rows && mc < cols) ? to_f32(Mb[mr * cols + mc]) * scale : 0.0f;
-  }
-  __syncthreads();
   TX* Xb = X + b * sp * lp;
-  for (int r = threadIdx.x >> 6; r < 64; r += 4) Xb[(i0 + r) * lp + j0 + c] = from_f32<TX>(tile[c][r]);
+  if constexpr (VEC) {
+    // thread t: row t / 8 (+ 32) of the tile, entries 8 (t % 8) .. + 7
+    const int q = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + 32 * h;
+      const int64_t mr = j0 + r, mc = i0 + 8 * q;
+      float v[8];
+      if (mr < rows && mc < cols) {
+        Vec8<TM>::load(Mb + mr * cols + mc, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[r][8 * q + e] = v[e] * scale;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + 32 * h;   // X row i0 + r, columns j0 + 8 q .. + 7
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[8 * q + e][r];
+      Vec8<TX>::store(Xb + (i0 + r) * lp + j0 + 8 * q, v);
+    }
+  } else {
+    const int c = threadIdx.x & 63;
+    for (int r = threadIdx.x >> 6; r < 64; r += 4) {
+      const int64_t mr = j0 + r, mc = i0 + c;
+      tile[r][c] = (mr < rows && mc < cols) ? to_f32(Mb[mr * cols + mc]) * scale : 0.0f;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x >> 6; r < 64; r += 4) Xb[(i0 + r) * lp + j0 + c] = from_f32<TX>(tile[c][r]);
+  }
 }
 
 // steps == 0: U = X0 (un-padded, original orientation)
@@ -279,8 +310,10 @@ int normalize_t(const void* M, int64_t strideM, int64_t rows, int64_t cols, cons
                 int64_t stride_sumsq, void* X, int64_t sp, int64_t lp, int64_t batch, hipStream_t st) {
   if (sp == 0 || lp == 0 || batch == 0) return MUON_OK;
   if (rows > cols) {
-    launch_kernel(normalize_tall_kernel<TM, TX>, dim3(lp / 64, sp / 64, batch), dim3(256), 0, st, 
-        static_cast<const TM*>(M), strideM, rows, cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
+    const bool vec = cols % 8 == 0 && strideM % 8 == 0 && aligned16(M);
+    auto kern = vec ? normalize_tall_kernel<TM, TX, true> : normalize_tall_kernel<TM, TX, false>;
+    launch_kernel(kern, dim3(lp / 64, sp / 64, batch), dim3(256), 0, st, static_cast<const TM*>(M), strideM, rows,
+                  cols, sumsq, stride_sumsq, static_cast<TX*>(X), sp, lp);
   } else {
     const int64_t blocks = (sp * (lp / 8) + 255) / 256;
     const int vec = cols % 8 == 0 && strideM % 8 == 0;
@@ -530,10 +563,15 @@ SplitRegion split_region(const std::vector<Run>& runs, int precision) {
 }
 
 // packed signs of every U of a run whose signs were not fused into its last
-// product (one sign_pack per problem: U entries need not be contiguous)
+// product: one sign_pack over the whole run when its directions lie back to
+// back and each starts a fresh 64-bit word with its words back to back too
+// (the words are then those of the concatenation), else one per problem
 int pack_run_signs(const Run& r, hipStream_t st) {
   if (!r.bits) return MUON_OK;
   const size_t es = dtype_size(r.u_dtype);
+  const int64_t n = r.rows * r.cols;
+  if (r.count > 1 && r.strideU == n && n % 64 == 0 && r.stride_bits == n / 64)
+    return sign_pack(r.U, r.u_dtype, n * r.count, r.bits, st);
   for (int k = 0; k < r.count; ++k) {
     const int status = sign_pack(static_cast<const char*>(r.U) + k * r.strideU * es, r.u_dtype,
                                  r.rows * r.cols, r.bits + k * r.stride_bits, st);
