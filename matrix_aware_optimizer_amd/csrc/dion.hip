@@ -192,16 +192,19 @@ __global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, flo
 // k-values are paired across the two half-waves of v_mfma_f32_32x32x2f32 as
 // (k, k + 4) within each 8-deep group, so a ck lane's ds_read_b128 feeds 4
 // MFMAs; a co lane reads the matching row for each MFMA.
-// Chunks past the contraction (k >= K) load from a 1 KB page of zeros in the
-// workspace, so both operands are zero there and the tail adds nothing;
-// chunks past the output dimension load a clamped valid chunk, whose products
-// land only in rows or columns that are never stored.
+// Chunks past the contraction (k >= K) load from a 16 KB page of zeros in the
+// workspace (spread over it by slot and workgroup), so both operands are zero
+// there and the tail adds nothing; chunks past the output dimension load a
+// clamped valid chunk, whose products land only in rows or columns that are
+// never stored.
 // The waits are explicit: each wave issues exactly 4 DMA instructions per
-// k-tile (dummies from the zero page after the last tile), so s_waitcnt
-// vmcnt(4 (S - 2)) means its chunks of the oldest stage have landed, and the
-// s_barrier after it means every wave's have.
+// k-tile, so while S - 2 younger stages are in flight s_waitcnt vmcnt(4 (S -
+// 2)) means its chunks of the oldest stage have landed, and the s_barrier
+// after it means every wave's have; the last S - 1 iterations issue nothing
+// and wait for everything.
 // ---------------------------------------------------------------------------
 constexpr int kDmaTileBytes = kDT * kDK * 4;   // one operand tile: 8 KB
+constexpr int kZeroPageFloats = 4096;          // the workspace's page of zeros: 16 KB
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -226,7 +229,7 @@ struct DmaOperand {
   int64_t n_out, K;
   // global address of the chunk that LDS chunk slot p of the tile at (o0, k0) holds
   template <bool CK>
-  __device__ __forceinline__ const float* chunk(int p, int64_t o0, int64_t k0, const float* zero, int lane) const {
+  __device__ __forceinline__ const float* chunk(int p, int64_t o0, int64_t k0, const float* zero, int zspread) const {
     int64_t o, k;
     if constexpr (CK) {
       const int row = p >> 3, c = (p & 7) ^ (row & 7);
@@ -238,7 +241,10 @@ struct DmaOperand {
       o = o0 + 4 * (p & 15);
       if (o >= n_out) o = n_out - 4;
     }
-    return k < K ? base + o * s_out + k * s_k : zero + 4 * lane;
+    // past the contraction: a chunk of the zero page, spread over its 16 KB by
+    // slot and workgroup so that the tail reads of many workgroups do not all
+    // land on the same few cache lines
+    return k < K ? base + o * s_out + k * s_k : zero + 4 * ((p + 67 * zspread) & (kZeroPageFloats / 4 - 1));
   }
 };
 
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   const int nk = static_cast<int>(kt1 - kt0);
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
+  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
   // stage s: A tile at s * 16 KB, B tile 8 KB after it
   auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
     const int64_t k0 = kt * kDK;
@@ -266,15 +273,18 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
     for (int i = 0; i < 2; ++i) {
       const int slot0 = 64 * (2 * wave + i);
       // beyond the last k-tile: dummies from the zero page (k0 >= K)
-      dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, lane), sa + 16 * slot0);
-      dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, lane), sb + 16 * slot0);
+      dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
+      dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, zspread + 1), sb + 16 * slot0);
     }
   };
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  // the first S - 1 stages (those past the range are not issued; the waits
+  // below count only issued ones)
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s, kt0 + s);
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, kt0 + s);
   // ZPRE (an addend and no split): the addend is read before the contraction,
   // so its latency overlaps the k-loop (the m x n updates have a short k and a
   // full tile of addend each).  Z may be C itself: every lane reads only the
@@ -291,8 +301,14 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   };
   if constexpr (ZPRE) load_z();
   for (int it = 0; it < nk; ++it) {
-    dion_wait_vm_barrier<4 * (S - 2)>();
-    issue((it + S - 1) % S, kt0 + it + S - 1);
+    // steady state: S - 2 younger stages are in flight behind the one needed;
+    // in the last S - 1 iterations nothing is issued any more, so wait for all
+    if (it + S - 1 < nk) {
+      dion_wait_vm_barrier<4 * (S - 2)>();
+      issue((it + S - 1) % S, kt0 + it + S - 1);
+    } else {
+      dion_wait_vm_barrier<0>();
+    }
     const char* ta = dsm + (it % S) * 2 * kDmaTileBytes;
     const char* tb = ta + kDmaTileBytes;
 #pragma unroll
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
       for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the dummy stages have landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every stage has landed
   if (splits > 1) {
     float* Pp = part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N;
     if (col < g.N) {
@@ -346,9 +362,8 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   }
 }
 
-// the zero page the DMA kernel's tail chunks read (1 KB)
-constexpr int kZeroPageFloats = 256;
-__global__ __launch_bounds__(256) void zero_page_kernel(float* z) { z[threadIdx.x] = 0.0f; }
+// the zero page the DMA kernel's tail chunks read (16 KB)
+__global__ __launch_bounds__(256) void zero_page_kernel(float* z) { z[blockIdx.x * 256 + threadIdx.x] = 0.0f; }
 
 // C[b](i,j) = alpha * sum_s part[s][b](i,j) + beta * Z[b](i,j), ranges added in order
 __global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const float* __restrict__ part,
@@ -911,7 +926,7 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
   };
   int status;
   if (zp) {
-    launch_kernel(zero_page_kernel, dim3(1), dim3(kZeroPageFloats), 0, st, zp);
+    launch_kernel(zero_page_kernel, dim3(kZeroPageFloats / 256), dim3(256), 0, st, zp);
     if ((status = launch_status()) != MUON_OK) return status;
   }
   // B = M + G in place, and P = B Q

@@ -337,7 +337,7 @@ def test_dion_validation(L):
     p = ctypes.cast(arr, ctypes.c_void_p)
     need = L.dion_workspace_bytes(p, 1, 192)
     # P twice (m x r) and R (n x r) per run, the Grams and their inverse factors
-    # (r x r per matrix), one split-k partial buffer, and the 1 KB page of zeros
+    # (r x r per matrix), one split-k partial buffer, and the 16 KB page of zeros
     # the DMA-staged products read past the contraction: ranges per product =
     # ceil(1024 / output tiles of 64 x 64), at most K / 256 and 16, at least 1
     up = lambda x: -(-x // 256) * 256
@@ -350,7 +350,7 @@ def test_dion_validation(L):
     m, n, r = 768, 3072, 192
     parts = max(part(m, r, n), part(r, r, m), part(m, r, r), part(n, r, m), part(m, n, r))
     assert parts == 12 * m * r * 4                     # B Q: 36 tiles, 12 k ranges of 256
-    assert need == 2 * up(m * r * 4) + up(n * r * 4) + 2 * up(r * r * 4) + up(parts) + 1024
+    assert need == 2 * up(m * r * 4) + up(n * r * 4) + 2 * up(r * r * 4) + up(parts) + 16384
     assert L.dion_workspace_bytes(p, 1, 193) == 0                       # above the LDS limit
     # launch-grid limits: a side above 65535 tiles of 64, more than 4095 problems
     arr[0].rows = 65535 * 64 + 1
