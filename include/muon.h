@@ -178,12 +178,23 @@ int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int6
  *              (then only the signs are written); otherwise U is required and
  *              the signs are packed from it after the iteration.
  *   Problems of equal shape and dtypes whose pointers are evenly spaced are
- *   batched into one launch per stage.  steps == 0 gives U = X0.
+ *   batched into one launch per stage (a run).  steps == 0 gives U = X0.
+ *   Streams: with two or more runs, the runs are shared out (largest first,
+ *   onto the lighter side) between `stream` and a second stream the library
+ *   creates once per device (default priority, not synchronising with the
+ *   null stream).  The second side starts after the work already enqueued on
+ *   `stream` (an event recorded there) and `stream` waits for it before any
+ *   later work (an event recorded on the second stream), so to the caller
+ *   the call behaves like work on `stream` alone.  The events are the calling
+ *   host thread's own; host threads share the second stream.  If the stream
+ *   or the events cannot be created, every run goes on `stream`.
  *   workspace  device, at least ns_workspace_bytes(probs, count, precision)
  *              bytes, 16-byte aligned, owned by the caller; its contents on
  *              entry do not matter (the call clears what must start at zero)
  *              and are undefined on return.  Calls that share a workspace must
- *              not overlap in time.
+ *              not overlap in time.  With two streams it holds the split
+ *              scratch and run buffers of each side (the first side's sized
+ *              for every run).
  *   Work split: with bf16 operands, a Gram whose contraction is at least
  *   8192 long and whose n_p^2 units (n_p = s / 256, times the batch) fit one
  *   round of the device's CUs (at most 256) runs every off-diagonal 256 x 256
@@ -194,9 +205,12 @@ int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int6
  *   which half came first).  The polynomial product B = bA + cA^2 (which
  *   needs no workspace) runs, when its n_p^2 units per matrix fit one round
  *   of the CUs, as the two 256 x 128 column halves of every off-diagonal tile
- *   plus the lower half of every diagonal tile.  Results therefore depend on
- *   the device's CU count only through these choices, and are deterministic
- *   on one device.  The second half's wait for the first is bounded
+ *   plus the lower half of every diagonal tile.  A symmetric product on
+ *   256 x 256 tiles that neither splits nor fits one round runs its
+ *   off-diagonal tiles whole and its diagonal tiles as lower halves (same
+ *   results: every element's contraction order is unchanged).  Results
+ *   therefore depend on the device's CU count only through these choices,
+ *   and are deterministic on one device.  The second half's wait for the first is bounded
  *   (muon_set_split_wait_limit); a wait that runs out leaves its tile
  *   unwritten and sets an error word in the workspace, which
  *   ns_workspace_status reports.

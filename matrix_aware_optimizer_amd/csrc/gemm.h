@@ -1377,6 +1377,7 @@ struct SplitPlan {
 struct Scratch {         // caller-provided split scratch (base == nullptr: no splitting)
   char* base;
   size_t bytes;
+  int* error = nullptr;  // the error word a wait that runs out sets (null: the one after base's counters)
 };
 
 inline size_t split_scratch_bytes(int64_t split_tiles, int bm, int bn) {
@@ -1434,7 +1435,7 @@ int launch_dma(GemmArgs g, int64_t batch, hipStream_t st, const Scratch& sc) {
         return MUON_EWORKSPACE;
       g.split_mode = p.mode;
       g.counters = reinterpret_cast<int*>(sc.base);
-      g.split_error = g.counters + kSplitCounters;
+      g.split_error = sc.error != nullptr ? sc.error : g.counters + kSplitCounters;
       g.spin_limit = split_spin_limit().load(std::memory_order_relaxed);
       g.partials = reinterpret_cast<float*>(sc.base + kSplitCounterBytes);
       grid = p.units;

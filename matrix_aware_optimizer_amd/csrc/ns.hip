@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -586,6 +587,192 @@ size_t runs_bytes(const std::vector<Run>& runs, int precision) {
   return need;
 }
 
+// One run of equal-shape problems: normalisation (unless folded), `steps`
+// iterations, and the signs; `ws` holds the run's buffers (layout_of), `sc`
+// the split scratch of the lane it runs on.
+int run_one(const Run& r, char* ws, const gemm::Scratch& sc, int precision, float a, float b, float c, int steps,
+            hipStream_t st) {
+  const RunLayout L = layout_of(r, precision);
+  const int prec = run_precision(r.rows, r.cols, precision);
+  const float* sumsq = r.sumsq;
+  int64_t stride_sumsq = r.stride_sumsq;
+  int status;
+  if (!r.has_sumsq) {
+    float* out = reinterpret_cast<float*>(ws + L.sumsq);
+    status = sumsq_strided(r.M, r.m_dtype, r.rows * r.cols, r.count, r.strideM, out,
+                           ws + L.partials, st);
+    if (status != MUON_OK) return status;
+    sumsq = out;
+    stride_sumsq = 1;
+  }
+  void* X[2] = {ws + L.x0, ws + L.x1};
+  void* A = ws + L.a;
+  void* B = ws + L.b;
+  // a bf16, wide, pad-free momentum is its own (unnormalised) X0: the first
+  // iteration reads M and folds the Frobenius scale into its epilogues
+  const bool fold_norm = folds_normalisation(r, prec) && steps > 0;
+  if (!fold_norm) {
+    status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
+                                prec, r.sp, r.lp, r.count, st);
+    if (status != MUON_OK) return status;
+  }
+  if (steps == 0) {
+    status = prec == MUON_BF16
+                 ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
+                 : emit_t<float>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st);
+    if (status == MUON_OK) status = pack_run_signs(r, st);
+    if (status != MUON_OK) return status;
+    return MUON_OK;
+  }
+  GemmArgs fin{};
+  fin.U = r.U;
+  fin.strideU = r.strideU;
+  fin.s_valid = std::min(r.rows, r.cols);
+  fin.l_valid = std::max(r.rows, r.cols);
+  fin.u_dtype = r.u_dtype;
+  fin.transpose_out = r.rows > r.cols;
+  const bool fused_signs = r.bits && fuses_signs(r.rows, r.cols, precision, steps);
+  if (fused_signs) {
+    fin.bits = r.bits;
+    fin.bits_rows = r.rows;
+    fin.bits_cols = r.cols;
+    fin.stride_bits = r.stride_bits;
+  }
+  const int kres = prec == MUON_BF16 ? residual_iterations(std::min(r.rows, r.cols), a, b, c, steps) : 0;
+  for (int it = 0; it < steps; ++it) {
+    const bool first_folded = fold_norm && it == 0;
+    const void* Xc = first_folded ? r.M : X[it & 1];
+    void* Xn = X[(it + 1) & 1];
+    const bool last = it + 1 == steps;
+    const Fold fold = first_folded ? Fold{sumsq, stride_sumsq, r.strideM} : Fold{};
+    if (prec == MUON_BF16) {
+      // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
+      status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, sc, fold);
+      if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st, sc);
+      // the residual buffer is read and rewritten in place (entry by entry, by one lane)
+      void* Xlo = ws + L.xl;
+      const bool lo_in = it >= 1 && it <= kres;
+      const bool lo_out = it < kres && !last;
+      // signs only (no direction wanted): the last product is the kernel of the
+      // other iterations with no output but the packed signs
+      const bool signs_only = last && r.U == nullptr;
+      if (status == MUON_OK)
+        status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, signs_only ? nullptr : Xn, r.sp, r.lp, r.count, a,
+                                 c != 0.0f ? 1.0f : b, st, sc, last && !signs_only ? &fin : nullptr, fold,
+                                 signs_only ? &fin : nullptr, lo_in ? Xlo : nullptr, lo_out ? Xlo : nullptr);
+    } else {
+      status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st, sc);
+      if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st, sc);
+      if (status == MUON_OK)
+        status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
+                                st, sc, last ? &fin : nullptr);
+    }
+    if (status != MUON_OK) return status;
+  }
+  if (!fused_signs) {
+    status = pack_run_signs(r, st);
+    if (status != MUON_OK) return status;
+  }
+  return MUON_OK;
+}
+
+// Runs of different shapes (a layer set) go to two lanes, the caller's stream
+// and a second stream of the library's, forked from and joined back into the
+// caller's stream with events: the small launches of one run then fill the
+// CUs that another run's tails and ramps leave idle.  Measured on the
+// GPT-2-small set (four runs on two streams): 2.15 -> 2.0 ms.  Each lane has
+// its own run buffers and split scratch; lane 0's are sized for every run, so
+// all runs can also go to lane 0 alone (when the second stream or the events
+// cannot be had).
+#ifndef MUON_NS_LANES
+#define MUON_NS_LANES 2
+#endif
+constexpr int kNsLanes = MUON_NS_LANES;
+
+// relative cost of a run (its products' multiply-adds per iteration)
+double run_cost(const Run& r) {
+  const double s = static_cast<double>(r.sp), l = static_cast<double>(r.lp);
+  return static_cast<double>(r.count) * (s * s * l + s * s * s + 2.0 * s * s * l);
+}
+
+struct LanePlan {
+  int lanes = 1;
+  std::vector<int> lane;          // lane of each run
+  size_t split[2] = {0, 0};       // split scratch of each lane (counters first)
+  size_t bufs[2] = {0, 0};        // run buffers of each lane
+  size_t total() const { return split[0] + split[1] + bufs[0] + bufs[1]; }
+};
+
+// Workspace: [split scratch 0][split scratch 1][run buffers 0][run buffers 1].
+// Runs are placed largest first on the lane with less work so far.
+LanePlan plan_lanes(const std::vector<Run>& runs, int precision) {
+  LanePlan P;
+  P.lane.assign(runs.size(), 0);
+  P.split[0] = split_region(runs, precision).bytes;
+  P.bufs[0] = runs_bytes(runs, precision);
+  if (kNsLanes < 2 || runs.size() < 2) return P;
+  std::vector<size_t> order(runs.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t x, size_t y) { return run_cost(runs[x]) > run_cost(runs[y]); });
+  double load[2] = {0.0, 0.0};
+  std::vector<Run> second;
+  for (size_t i : order) {
+    const int l = load[1] < load[0] ? 1 : 0;
+    P.lane[i] = l;
+    load[l] += run_cost(runs[i]);
+  }
+  for (size_t i = 0; i < runs.size(); ++i)
+    if (P.lane[i] == 1) second.push_back(runs[i]);
+  if (second.empty()) return P;
+  P.lanes = 2;
+  P.split[1] = split_region(second, precision).bytes;
+  P.bufs[1] = runs_bytes(second, precision);
+  return P;
+}
+
+// The library's second stream on the current device (default priority, not
+// synchronising with the null stream), created on first use; null if it
+// cannot be created.  Host threads share it; each call orders its own work
+// with its own events.
+hipStream_t lane_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[kMaxTrackedDevices] = {};
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxTrackedDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = st;
+  }
+  return streams[dev];
+}
+
+// The fork and join events of this host thread on the current device,
+// created on first use and kept (a wait takes the event's last record at the
+// time it is enqueued, so reusing them call after call is safe).
+bool fork_join_events(hipEvent_t& fork, hipEvent_t& join) {
+  struct Pair {
+    hipEvent_t fork = nullptr, join = nullptr;
+  };
+  static thread_local Pair pairs[kMaxTrackedDevices];
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxTrackedDevices) return false;
+  Pair& e = pairs[dev];
+  if (e.fork == nullptr && hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess) {
+    e.fork = nullptr;
+    return false;
+  }
+  if (e.join == nullptr && hipEventCreateWithFlags(&e.join, hipEventDisableTiming) != hipSuccess) {
+    e.join = nullptr;
+    return false;
+  }
+  fork = e.fork;
+  join = e.join;
+  return true;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -597,7 +784,7 @@ size_t ns_workspace_bytes(const muon_ns_problem* probs, int count, int precision
   if (!probs || count <= 0 || (precision != MUON_F32 && precision != MUON_BF16)) return 0;
   for (int i = 0; i < count; ++i)
     if (!valid_problem(probs[i])) return 0;
-  return split_region(make_runs(probs, count), precision).bytes + runs_bytes(make_runs(probs, count), precision);
+  return plan_lanes(make_runs(probs, count), precision).total();
 }
 
 int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, float c, int steps,
@@ -615,105 +802,40 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
     if (reinterpret_cast<uintptr_t>(p.bits) % 8 != 0) return MUON_EALIGN;
   }
   const std::vector<Run> runs = make_runs(probs, count);
-  const SplitRegion split = split_region(runs, precision);
-  const size_t need = split.bytes + runs_bytes(runs, precision);
-  if (!workspace || ws_bytes < need) return MUON_EWORKSPACE;
+  const LanePlan P = plan_lanes(runs, precision);
+  if (!workspace || ws_bytes < P.total()) return MUON_EWORKSPACE;
   if (!aligned16(workspace)) return MUON_EALIGN;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
   // bf16 products may split (a symmetric product with one tile row needs no
-  // scratch: its only unit is the diagonal lower half)
-  const gemm::Scratch sc{precision == MUON_BF16 ? static_cast<char*>(workspace) : nullptr, split.bytes};
+  // scratch: its only unit is the diagonal lower half).  Both lanes report a
+  // wait that runs out in lane 0's error word, the one ns_workspace_status reads.
+  int* error_word = reinterpret_cast<int*>(base) + gemm::kSplitCounters;
+  const bool bf16 = precision == MUON_BF16;
+  const gemm::Scratch sc[2] = {gemm::Scratch{bf16 ? base : nullptr, P.split[0]},
+                               gemm::Scratch{bf16 ? base + P.split[0] : nullptr, P.split[1], error_word}};
+  char* bufs[2] = {base + P.split[0] + P.split[1], base + P.split[0] + P.split[1] + P.bufs[0]};
   {
     // arrival counters and the error word start at zero on every call
-    const int status = zero_counters(workspace, gemm::kSplitWords, st);
+    int status = zero_counters(base, gemm::kSplitWords, st);
+    if (status == MUON_OK && P.lanes == 2) status = zero_counters(base + P.split[0], gemm::kSplitWords, st);
     if (status != MUON_OK) return status;
   }
-  char* ws = static_cast<char*>(workspace) + split.bytes;
-  for (const Run& r : runs) {
-    const RunLayout L = layout_of(r, precision);
-    const int prec = run_precision(r.rows, r.cols, precision);
-    const float* sumsq = r.sumsq;
-    int64_t stride_sumsq = r.stride_sumsq;
-    int status;
-    if (!r.has_sumsq) {
-      float* out = reinterpret_cast<float*>(ws + L.sumsq);
-      status = sumsq_strided(r.M, r.m_dtype, r.rows * r.cols, r.count, r.strideM, out,
-                             ws + L.partials, st);
-      if (status != MUON_OK) return status;
-      sumsq = out;
-      stride_sumsq = 1;
-    }
-    void* X[2] = {ws + L.x0, ws + L.x1};
-    void* A = ws + L.a;
-    void* B = ws + L.b;
-    // a bf16, wide, pad-free momentum is its own (unnormalised) X0: the first
-    // iteration reads M and folds the Frobenius scale into its epilogues
-    const bool fold_norm = folds_normalisation(r, prec) && steps > 0;
-    if (!fold_norm) {
-      status = normalize_dispatch(r.M, r.m_dtype, r.strideM, r.rows, r.cols, sumsq, stride_sumsq, X[0],
-                                  prec, r.sp, r.lp, r.count, st);
-      if (status != MUON_OK) return status;
-    }
-    if (steps == 0) {
-      status = prec == MUON_BF16
-                   ? emit_t<bf16_t>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st)
-                   : emit_t<float>(X[0], r.sp, r.lp, r.rows, r.cols, r.U, r.u_dtype, r.strideU, r.count, st);
-      if (status == MUON_OK) status = pack_run_signs(r, st);
-      if (status != MUON_OK) return status;
-      continue;
-    }
-    GemmArgs fin{};
-    fin.U = r.U;
-    fin.strideU = r.strideU;
-    fin.s_valid = std::min(r.rows, r.cols);
-    fin.l_valid = std::max(r.rows, r.cols);
-    fin.u_dtype = r.u_dtype;
-    fin.transpose_out = r.rows > r.cols;
-    const bool fused_signs = r.bits && fuses_signs(r.rows, r.cols, precision, steps);
-    if (fused_signs) {
-      fin.bits = r.bits;
-      fin.bits_rows = r.rows;
-      fin.bits_cols = r.cols;
-      fin.stride_bits = r.stride_bits;
-    }
-    const int kres = prec == MUON_BF16 ? residual_iterations(std::min(r.rows, r.cols), a, b, c, steps) : 0;
-    for (int it = 0; it < steps; ++it) {
-      const bool first_folded = fold_norm && it == 0;
-      const void* Xc = first_folded ? r.M : X[it & 1];
-      void* Xn = X[(it + 1) & 1];
-      const bool last = it + 1 == steps;
-      const Fold fold = first_folded ? Fold{sumsq, stride_sumsq, r.strideM} : Fold{};
-      if (prec == MUON_BF16) {
-        // c != 0: X' = a X + (bA + cA^2) X;  c == 0: X' = a X + b A X
-        status = gram_t<bf16_t>(Xc, A, r.sp, r.lp, r.count, st, sc, fold);
-        if (status == MUON_OK && c != 0.0f) status = poly_t<bf16_t>(A, B, r.sp, r.count, b, c, st, sc);
-        // the residual buffer is read and rewritten in place (entry by entry, by one lane)
-        void* Xlo = ws + L.xl;
-        const bool lo_in = it >= 1 && it <= kres;
-        const bool lo_out = it < kres && !last;
-        // signs only (no direction wanted): the last product is the kernel of the
-        // other iterations with no output but the packed signs
-        const bool signs_only = last && r.U == nullptr;
-        if (status == MUON_OK)
-          status = apply_t<bf16_t>(c != 0.0f ? B : A, Xc, signs_only ? nullptr : Xn, r.sp, r.lp, r.count, a,
-                                   c != 0.0f ? 1.0f : b, st, sc, last && !signs_only ? &fin : nullptr, fold,
-                                   signs_only ? &fin : nullptr, lo_in ? Xlo : nullptr, lo_out ? Xlo : nullptr);
-      } else {
-        status = gram_t<float>(Xc, A, r.sp, r.lp, r.count, st, sc);
-        if (status == MUON_OK && c != 0.0f) status = poly_t<float>(A, B, r.sp, r.count, b, c, st, sc);
-        if (status == MUON_OK)
-          status = apply_t<float>(c != 0.0f ? B : A, Xc, Xn, r.sp, r.lp, r.count, a, c != 0.0f ? 1.0f : b,
-                                  st, sc, last ? &fin : nullptr);
-      }
-      if (status != MUON_OK) return status;
-    }
-    if (!fused_signs) {
-      status = pack_run_signs(r, st);
-      if (status != MUON_OK) return status;
-    }
+  hipStream_t lane1 = P.lanes == 2 ? lane_stream() : nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (lane1 != nullptr && (!fork_join_events(fork, join) || hipEventRecord(fork, st) != hipSuccess ||
+                           hipStreamWaitEvent(lane1, fork, 0) != hipSuccess))
+    lane1 = nullptr;   // every run on the caller's stream
+  int status = MUON_OK;
+  for (size_t i = 0; i < runs.size() && status == MUON_OK; ++i) {
+    const int l = lane1 != nullptr ? P.lane[i] : 0;
+    status = run_one(runs[i], bufs[l], sc[l], precision, a, b, c, steps, l == 1 ? lane1 : st);
   }
-  return MUON_OK;
+  if (lane1 != nullptr && (hipEventRecord(join, lane1) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess) &&
+      status == MUON_OK)
+    status = MUON_ELAUNCH;
+  return status;
 }
 
 int ns_workspace_status(const void* workspace, size_t ws_bytes, void* stream) {

@@ -168,13 +168,16 @@ def test_ns_grouping_batches_evenly_spaced_problems(L):
         specs.append((0x100000 + 2 * off, 0x40000000 + 2 * off, 0x80000 + 4 * j, r, c, 1, 1))
         off += r * c
     arr = _problems(specs)
-    # the largest run is 12 matrices of 768x3072 (the wide and the tall ones are separate runs)
-    assert L.ns_workspace_bytes(arr, 48, 1) == _ns_bytes(12, 768, 3072)
+    # four runs (the wide and the tall 768 x 3072 ones are separate runs) on two lanes,
+    # largest first onto the lane with less work: lane 0 gets 768x3072 and 768x2304,
+    # lane 1 3072x768 and 768x768.  Each lane has its own counters and run buffers,
+    # lane 0's sized for every run (the largest: 12 matrices of 768x3072)
+    assert L.ns_workspace_bytes(arr, 48, 1) == 2 * _ns_bytes(12, 768, 3072)
     # irregular spacing defeats batching: every problem is its own run
     specs2 = [(M + (j * j % 7) * 4096 * 0, U, s, r, c, md, ud) for j, (M, U, s, r, c, md, ud) in enumerate(specs)]
     specs2[1] = (specs2[1][0], specs2[1][1] + 16, specs2[1][2], *specs2[1][3:])
     arr2 = _problems(specs2)
-    assert L.ns_workspace_bytes(arr2, 48, 1) == _ns_bytes(12, 768, 3072)
+    assert L.ns_workspace_bytes(arr2, 48, 1) == 2 * _ns_bytes(12, 768, 3072)   # five runs, lane 1 gets 3072x768
     # without norms the run also holds its sums and partial sums
     specs3 = [(M, U, None, r, c, md, ud) for (M, U, s, r, c, md, ud) in specs[:1]]
     part = L.muon_momentum_workspace_bytes(768 * 2304, 1)
@@ -236,7 +239,9 @@ def test_ns_grouping_with_sign_bits(L):
     assert L.ns_workspace_bytes(_problems(with_u), 12, 1) == _ns_bytes(12, 768, 3072)
     broken = list(specs)
     broken[6] = (*broken[6][:7], broken[6][7] + 8)
-    assert L.ns_workspace_bytes(_problems(broken), 12, 1) == _ns_bytes(6, 768, 3072)
+    # runs of 6, 2 (the shifted words and the next) and 4 problems on two lanes: 6 on lane 0,
+    # 4 and 2 on lane 1
+    assert L.ns_workspace_bytes(_problems(broken), 12, 1) == _ns_bytes(6, 768, 3072) + _ns_bytes(4, 768, 3072)
 
 
 def test_ns_apply_signs_validation(L):

@@ -18,8 +18,10 @@ from workloads import QUINTIC, random_matrix, store
 
 pytestmark = pytest.mark.gpu
 
-# small tiles; a split Gram with 256 x 256 apply tiles; a batched pair; a tall one
-SHAPES = [[(768, 2304)], [(2048, 8192)], [(512, 1536), (512, 1536)], [(2048, 512)]]
+# small tiles; a split Gram with 256 x 256 apply tiles; a batched pair; a tall one;
+# three shapes (runs on the library's two lanes, whose second stream the threads share)
+SHAPES = [[(768, 2304)], [(2048, 8192)], [(512, 1536), (512, 1536)], [(2048, 512)],
+          [(768, 2304), (768, 768), (1024, 2048)]]
 
 
 def _case(k, shapes):
