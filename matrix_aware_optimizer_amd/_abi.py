@@ -302,9 +302,11 @@ def ns_stage_workspace_bytes(s: int, l: int, batch: int = 1, precision="bf16") -
 
 
 def new_stage_workspace(s: int, l: int, batch: int = 1, precision="bf16", device=None) -> torch.Tensor:
-    """Zeroed workspace for the stage calls on [batch][s][l] (its counters start at zero)."""
+    """Zeroed workspace for the stage calls on [batch][s][l] (its counters start at zero).
+    At least the 1024-byte counter block, so that ns_workspace_status can read its
+    error word also when nothing splits."""
     n = ns_stage_workspace_bytes(s, l, batch, precision)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(max(n, 1024), dtype=torch.uint8, device=device or "cuda")
 
 
 def _stage_ws(workspace, split: bool, s: int, l: int, batch: int, precision, like: torch.Tensor):

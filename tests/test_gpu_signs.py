@@ -142,11 +142,14 @@ def test_prepared_call_matches_direct_calls():
     assert np.array_equal(from_dev(bits), from_dev(direct2))
 
 
-def test_runs_on_two_lanes_match_one_call_per_run():
+@pytest.mark.parametrize("steps", [5, 0])
+def test_runs_on_two_lanes_match_one_call_per_run(steps):
     """A call with runs of several shapes (spread over the library's two streams)
-    writes exactly what separate calls, one run each, write: directions and words."""
-    shapes = [(768, 2304)] * 3 + [(768, 768)] * 2 + [(1024, 2048)] * 2 + [(3072, 768)] * 2
-    Mh, offs, U, bits = _ns_case(shapes, seed=11)
+    writes exactly what separate calls, one run each, write: directions and words.
+    Among them a short side under 96 (fp32 products) and a tall run."""
+    shapes = ([(768, 2304)] * 3 + [(768, 768)] * 2 + [(1024, 2048)] * 2 + [(3072, 768)] * 2
+              + [(64, 1024)] * 2)
+    Mh, offs, U, bits = _ns_case(shapes, steps=steps, seed=11)
     Md = to_dev(Mh, "bf16")
     U2 = torch.empty_like(U)
     bits2 = torch.zeros_like(bits)
@@ -156,7 +159,7 @@ def test_runs_on_two_lanes_match_one_call_per_run():
         groups.setdefault((r, c), []).append((Md[lo:hi].view(r, c), U2[lo:hi].view(r, c), None,
                                               bits2[lo // 64:(hi + 63) // 64]))
     for probs in groups.values():
-        mao.ns_orthogonalize(probs, *QUINTIC, 5, "bf16")
+        mao.ns_orthogonalize(probs, *QUINTIC, steps, "bf16")
     assert np.array_equal(from_dev(U), from_dev(U2))
     assert np.array_equal(from_dev(bits), from_dev(bits2))
 
