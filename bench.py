@@ -471,8 +471,8 @@ def roofline_of(kernels, total, rows, cols, wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU: every GPU box of this setup has one, "
-                                   "and the step's exchange between GPUs is not built; use --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: the exchange of packed signs between GPUs "
+                                   "is not built, so only --gpus 1 is measured"}))
         sys.exit(2)
 
     import torch
