@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "muon.h"
 
@@ -146,6 +147,48 @@ inline void launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, uint32_
 inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MUON_OK : MUON_ELAUNCH;
+}
+
+// The library's second stream on the current device (default priority, not
+// synchronising with the null stream), created on first use; null if it
+// cannot be created.  Host threads share it; each call orders its own work
+// with its own events.
+inline hipStream_t lane_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[kMaxTrackedDevices] = {};
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxTrackedDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = st;
+  }
+  return streams[dev];
+}
+
+// The fork and join events of this host thread on the current device,
+// created on first use and kept (a wait takes the event's last record at the
+// time it is enqueued, so reusing them call after call is safe).
+inline bool fork_join_events(hipEvent_t& fork, hipEvent_t& join) {
+  struct Pair {
+    hipEvent_t fork = nullptr, join = nullptr;
+  };
+  static thread_local Pair pairs[kMaxTrackedDevices];
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxTrackedDevices) return false;
+  Pair& e = pairs[dev];
+  if (e.fork == nullptr && hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess) {
+    e.fork = nullptr;
+    return false;
+  }
+  if (e.join == nullptr && hipEventCreateWithFlags(&e.join, hipEventDisableTiming) != hipSuccess) {
+    e.join = nullptr;
+    return false;
+  }
+  fork = e.fork;
+  join = e.join;
+  return true;
 }
 
 }  // namespace muon

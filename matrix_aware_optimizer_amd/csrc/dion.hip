@@ -809,33 +809,80 @@ std::vector<DRun> dion_runs(const muon_dion_problem* p, int count) {
   return runs;
 }
 
+// Two lanes: the caller's stream and the library's second stream, forked from
+// and joined back into the caller's with events.  Runs are placed largest
+// first on the lane with less work so far, and each lane takes the stages
+// below over its own runs.  The launches that leave most CUs idle (the
+// factorisation's one workgroup per matrix, the r x r Grams, the split-k
+// reductions, the column norms) then run beside the other lane's products.
+#ifndef MUON_DION_LANES
+#define MUON_DION_LANES 2
+#endif
+constexpr int kDionLanes = MUON_DION_LANES;
+
 // Workspace: every run keeps its own P (twice) and R, since the stages run
-// over all runs in turn; the Grams and their inverse factors of all matrices
-// sit in two arrays so one launch factors them all; one split-k partial
-// buffer serves every product.
+// over all runs of a lane in turn; the Grams and their inverse factors sit in
+// two arrays, lane 0's matrices first, so each lane factors its matrices in
+// one launch; each lane has a split-k partial buffer for its products (lane
+// 0's is sized for every run, so all runs can also go to lane 0 alone, when
+// the second stream or the events cannot be had).
 struct DLayout {
   std::vector<size_t> p0, p1, R;
-  size_t gram, linv, part, zero, total;
+  std::vector<int> lane;        // lane of each run
+  std::vector<int64_t> slot;    // first matrix of each run in the Gram and factor arrays
+  int64_t lane_mats[2] = {0, 0};
+  int lanes = 1;
+  size_t gram = 0, linv = 0, part[2] = {0, 0}, zero = 0, total = 0;
 };
+
+size_t run_part_bytes(const DRun& r, int rank) {
+  return std::max({gemm_part_bytes(r.m, rank, r.n, r.count), gemm_part_bytes(rank, rank, r.m, r.count),
+                   gemm_part_bytes(r.m, rank, rank, r.count), gemm_part_bytes(r.n, rank, r.m, r.count),
+                   gemm_part_bytes(r.m, r.n, rank, r.count)});
+}
 
 DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
   const size_t rk = static_cast<size_t>(rank);
   DLayout L{};
+  L.lane.assign(runs.size(), 0);
+  if (kDionLanes >= 2 && runs.size() >= 2) {
+    // every product of a run moves or multiplies in proportion to its m n
+    std::vector<size_t> order(runs.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    auto cost = [&](size_t i) { return static_cast<double>(runs[i].count) * runs[i].m * runs[i].n; };
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return cost(x) > cost(y); });
+    double load[2] = {0.0, 0.0};
+    for (size_t i : order) {
+      const int l = load[1] < load[0] ? 1 : 0;
+      L.lane[i] = l;
+      load[l] += cost(i);
+    }
+    L.lanes = load[1] > 0.0 ? 2 : 1;
+  }
+  L.slot.assign(runs.size(), 0);
+  for (int l = 0; l < 2; ++l)
+    for (size_t k = 0; k < runs.size(); ++k)
+      if (L.lane[k] == l) {
+        L.slot[k] = L.lane_mats[0] + L.lane_mats[1];
+        L.lane_mats[l] += runs[k].count;
+      }
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
-  size_t part = 0;
-  for (const DRun& r : runs) {
+  size_t part[2] = {0, 0};
+  for (size_t k = 0; k < runs.size(); ++k) {
+    const DRun& r = runs[k];
     const size_t b = static_cast<size_t>(r.count);
     L.p0.push_back(take(b * r.m * rk * 4));
     L.p1.push_back(take(b * r.m * rk * 4));
     L.R.push_back(take(b * r.n * rk * 4));
-    part = std::max({part, gemm_part_bytes(r.m, rank, r.n, r.count), gemm_part_bytes(rank, rank, r.m, r.count),
-                     gemm_part_bytes(r.m, rank, rank, r.count), gemm_part_bytes(r.n, rank, r.m, r.count),
-                     gemm_part_bytes(r.m, r.n, rank, r.count)});
+    const size_t pb = run_part_bytes(r, rank);
+    part[0] = std::max(part[0], pb);
+    if (L.lane[k] == 1) part[1] = std::max(part[1], pb);
   }
   L.gram = take(static_cast<size_t>(count) * rk * rk * 4);
   L.linv = take(static_cast<size_t>(count) * rk * rk * 4);
-  L.part = take(part);
+  L.part[0] = take(part[0]);
+  L.part[1] = take(part[1]);
   L.zero = take(kZeroPageFloats * sizeof(float));
   L.total = off;
   return L;
@@ -870,6 +917,111 @@ int set_chol_lds(int bytes) {
       while (bytes > cur && !configured[dev].compare_exchange_weak(cur, bytes, std::memory_order_release)) {
       }
     }
+  }
+  return MUON_OK;
+}
+
+// One call's state shared by both lanes.
+struct DionCall {
+  const std::vector<DRun>* runs;
+  const std::vector<muon_dion_problem>* sorted;
+  const DLayout* L;
+  char* ws;
+  int rank, chol_lds;
+  float mu, eta;
+  const float* zero;   // the DMA products' zero page (null: register-staged products)
+};
+
+// Stage `stage` of Dion's step for the runs `ids` of one lane, on stream st:
+//   0     B = M + G in place, and P = B Q
+//   1-3   first orthonormalisation pass: the Grams P^T P, their factorisation
+//         (one launch over the lane's nmat matrices from slot0), P <- P L^-T
+//   4-6   the second pass, back into P's first buffer
+//   7     R = B^T P, error feedback, Q = ColumnNormalize(R), X update
+constexpr int kDionStagesPerCall = 8;
+
+int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float* part, int64_t slot0,
+               int64_t nmat, hipStream_t st) {
+  const DLayout& L = *C.L;
+  const int64_t r = C.rank;
+  float* Gm = reinterpret_cast<float*>(C.ws + L.gram);
+  float* Li = reinterpret_cast<float*>(C.ws + L.linv);
+  auto Pbuf = [&](size_t k, int which) {
+    return reinterpret_cast<float*>(C.ws + (which == 0 ? L.p0[k] : L.p1[k]));
+  };
+  const float* zp = C.zero;
+  int status = MUON_OK;
+  if (stage == 0) {
+    for (int k : ids) {
+      const DRun& run = (*C.runs)[k];
+      const muon_dion_problem& p = (*C.sorted)[run.first];
+      float* M = static_cast<float*>(p.M);
+      const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
+      const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
+      const int64_t threads = vec ? mn / 4 : mn;
+      launch_kernel(add_kernel, dim3((threads + 255) / 256, b), dim3(256), 0, st, M, run.sM,
+                    static_cast<const float*>(p.G), run.sG, mn, vec);
+      if ((status = launch_status()) != MUON_OK) return status;
+      status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
+                     m * r, r, m, r, n, 1.0f, 0.0f, b, part, zp, st);
+      if (status != MUON_OK) return status;
+    }
+    return MUON_OK;
+  }
+  if (stage <= 6) {
+    const int pass = (stage - 1) / 3, step = (stage - 1) % 3;
+    if (step == 0) {
+      for (int k : ids) {
+        const DRun& run = (*C.runs)[k];
+        const float* P = Pbuf(k, pass);
+        status = dgemm(P, run.m * r, 1, r, P, run.m * r, r, 1, nullptr, 0, 0, Gm + L.slot[k] * r * r, r * r, r,
+                       r, r, run.m, 1.0f, 0.0f, run.count, part, zp, st);
+        if (status != MUON_OK) return status;
+      }
+    } else if (step == 1) {
+      if (nmat > 0) {
+        launch_kernel(chol_inv_kernel, dim3(nmat), dim3(256), C.chol_lds, st, Gm + slot0 * r * r, r * r,
+                      Li + slot0 * r * r, r * r, C.rank);
+        status = launch_status();
+      }
+    } else {
+      for (int k : ids) {
+        const DRun& run = (*C.runs)[k];
+        status = dgemm(Pbuf(k, pass), run.m * r, r, 1, Li + L.slot[k] * r * r, r * r, 1, r, nullptr, 0, 0,
+                       Pbuf(k, 1 - pass), run.m * r, r, run.m, r, r, 1.0f, 0.0f, run.count, part, zp, st);
+        if (status != MUON_OK) return status;
+      }
+    }
+    return status;
+  }
+  for (int k : ids) {
+    const DRun& run = (*C.runs)[k];
+    const muon_dion_problem& p = (*C.sorted)[run.first];
+    float* M = static_cast<float*>(p.M);
+    float* X = static_cast<float*>(p.X);
+    float* Q = static_cast<float*>(p.Q);
+    float* R = reinterpret_cast<float*>(C.ws + L.R[k]);
+    const float* Pf = Pbuf(k, 0);      // two passes: back in buffer 0
+    const int64_t m = run.m, n = run.n, b = run.count;
+    status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, zp, st);
+    if (status != MUON_OK) return status;
+    status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - C.mu), 1.0f, b,
+                   part, zp, st);
+    if (status != MUON_OK) return status;
+    {
+      // chunks of at least 64 rows and at most m chunks, so the partial sums
+      // (b x chunks x r) fit in P's second buffer, free after the two passes
+      const int64_t rows_per = std::max<int64_t>(64, (n + m - 1) / m);
+      const int64_t nch = (n + rows_per - 1) / rows_per;
+      float* cpart = Pbuf(k, 1);
+      launch_kernel(colsq_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, n, C.rank, rows_per, nch);
+      launch_kernel(colscale_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, Q, run.sQ, n, C.rank,
+                    rows_per, nch);
+    }
+    if ((status = launch_status()) != MUON_OK) return status;
+    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -C.eta, 1.0f, b, part,
+                   zp, st);
+    if (status != MUON_OK) return status;
   }
   return MUON_OK;
 }
@@ -911,87 +1063,39 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const int64_t r = rank;
-  float* Gm = reinterpret_cast<float*>(ws + L.gram);
-  float* Li = reinterpret_cast<float*>(ws + L.linv);
-  float* part = reinterpret_cast<float*>(ws + L.part);
 #ifndef MUON_DION_DMA
 #define MUON_DION_DMA 1
 #endif
   // the DMA products' zero page, cleared on every call (the workspace's
   // contents on entry do not matter)
   float* zp = MUON_DION_DMA ? reinterpret_cast<float*>(ws + L.zero) : nullptr;
-  auto Pbuf = [&](size_t k, int which) {
-    return reinterpret_cast<float*>(ws + (which == 0 ? L.p0[k] : L.p1[k]));
-  };
-  int status;
   if (zp) {
     launch_kernel(zero_page_kernel, dim3(kZeroPageFloats / 256), dim3(256), 0, st, zp);
-    if ((status = launch_status()) != MUON_OK) return status;
-  }
-  // B = M + G in place, and P = B Q
-  for (size_t k = 0; k < runs.size(); ++k) {
-    const DRun& run = runs[k];
-    const muon_dion_problem& p = sorted[run.first];
-    float* M = static_cast<float*>(p.M);
-    const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
-    const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
-    const int64_t threads = vec ? mn / 4 : mn;
-    launch_kernel(add_kernel, dim3((threads + 255) / 256, b), dim3(256), 0, st, M, run.sM, static_cast<const float*>(p.G),
-                                                                    run.sG, mn, vec);
-    if ((status = launch_status()) != MUON_OK) return status;
-    status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
-                   m * r, r, m, r, n, 1.0f, 0.0f, b, part, zp, st);
+    const int status = launch_status();
     if (status != MUON_OK) return status;
   }
-  // orth(P), twice: the Grams P^T P of all matrices, one factorisation launch,
-  // then P <- P L^-T
-  for (int pass = 0; pass < 2; ++pass) {
-    for (size_t k = 0; k < runs.size(); ++k) {
-      const DRun& run = runs[k];
-      const float* P = Pbuf(k, pass);
-      status = dgemm(P, run.m * r, 1, r, P, run.m * r, r, 1, nullptr, 0, 0, Gm + run.first * r * r, r * r, r,
-                     r, r, run.m, 1.0f, 0.0f, run.count, part, zp, st);
-      if (status != MUON_OK) return status;
-    }
-    launch_kernel(chol_inv_kernel, dim3(count), dim3(256), lds, st, Gm, r * r, Li, r * r, rank);
-    if ((status = launch_status()) != MUON_OK) return status;
-    for (size_t k = 0; k < runs.size(); ++k) {
-      const DRun& run = runs[k];
-      status = dgemm(Pbuf(k, pass), run.m * r, r, 1, Li + run.first * r * r, r * r, 1, r, nullptr, 0, 0,
-                     Pbuf(k, 1 - pass), run.m * r, r, run.m, r, r, 1.0f, 0.0f, run.count, part, zp, st);
-      if (status != MUON_OK) return status;
-    }
+  const DionCall C{&runs, &sorted, &L, ws, rank, lds, mu, eta, zp};
+  float* part[2] = {reinterpret_cast<float*>(ws + L.part[0]), reinterpret_cast<float*>(ws + L.part[1])};
+  hipStream_t lane1 = L.lanes == 2 ? lane_stream() : nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (lane1 != nullptr && (!fork_join_events(fork, join) || hipEventRecord(fork, st) != hipSuccess ||
+                           hipStreamWaitEvent(lane1, fork, 0) != hipSuccess))
+    lane1 = nullptr;   // every run on the caller's stream
+  std::vector<int> ids[2];
+  for (int l = 0; l < 2; ++l)
+    for (size_t k = 0; k < runs.size(); ++k)
+      if (L.lane[k] == l) ids[lane1 != nullptr ? l : 0].push_back(static_cast<int>(k));
+  const int64_t mats[2] = {lane1 != nullptr ? L.lane_mats[0] : count, lane1 != nullptr ? L.lane_mats[1] : 0};
+  // the lanes' launches are enqueued stage by stage, so both start at once
+  int status = MUON_OK;
+  for (int stage = 0; stage < kDionStagesPerCall && status == MUON_OK; ++stage) {
+    status = dion_stage(C, stage, ids[0], part[0], 0, mats[0], st);
+    if (status == MUON_OK && lane1 != nullptr) status = dion_stage(C, stage, ids[1], part[1], mats[0], mats[1], lane1);
   }
-  // R = B^T P, error feedback, Q = ColumnNormalize(R), X update
-  for (size_t k = 0; k < runs.size(); ++k) {
-    const DRun& run = runs[k];
-    const muon_dion_problem& p = sorted[run.first];
-    float* M = static_cast<float*>(p.M);
-    float* X = static_cast<float*>(p.X);
-    float* Q = static_cast<float*>(p.Q);
-    float* R = reinterpret_cast<float*>(ws + L.R[k]);
-    const float* Pf = Pbuf(k, 0);      // two passes: back in buffer 0
-    const int64_t m = run.m, n = run.n, b = run.count;
-    status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, zp, st);
-    if (status != MUON_OK) return status;
-    status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - mu), 1.0f, b,
-                   part, zp, st);
-    if (status != MUON_OK) return status;
-    {
-      // chunks of at least 64 rows and at most m chunks, so the partial sums
-      // (b x chunks x r) fit in P's second buffer, free after the two passes
-      const int64_t rows_per = std::max<int64_t>(64, (n + m - 1) / m);
-      const int64_t nch = (n + rows_per - 1) / rows_per;
-      float* cpart = Pbuf(k, 1);
-      launch_kernel(colsq_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, n, rank, rows_per, nch);
-      launch_kernel(colscale_kernel, dim3(nch, b), dim3(256), 0, st, R, n * r, cpart, Q, run.sQ, n, rank, rows_per, nch);
-    }
-    if ((status = launch_status()) != MUON_OK) return status;
-    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -eta, 1.0f, b, part, zp, st);
-    if (status != MUON_OK) return status;
-  }
-  return MUON_OK;
+  if (lane1 != nullptr && (hipEventRecord(join, lane1) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess) &&
+      status == MUON_OK)
+    status = MUON_ELAUNCH;
+  return status;
 }
 
 }  // extern "C"

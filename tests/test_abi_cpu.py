@@ -380,6 +380,21 @@ def test_dion_validation(L):
     assert L.dion_step(p, 0, 192, 0.9, 0.1, None, 0, None) == OK
     assert mao.MUON_DION_MAX_RANK == 192
 
+    # two shapes: the larger run on the caller's stream, the other on the
+    # library's second stream, which gets a split-k buffer of its own (the
+    # first lane's is sized for both runs)
+    two = (DionProblem * 2)()
+    for k, (rows, cols) in enumerate([(768, 3072), (256, 512)]):
+        two[k].M, two[k].G, two[k].X, two[k].Q = 0x100000 * (k + 1), 0x200000 * (k + 1), 0x300000 * (k + 1), 0x400000 * (k + 1)
+        two[k].rows, two[k].cols = rows, cols
+    parts_of = lambda M_, N_: max(part(M_, r, N_), part(r, r, M_), part(M_, r, r), part(N_, r, M_), part(M_, N_, r))
+    p2 = ctypes.cast(two, ctypes.c_void_p)
+    runs = [(768, 3072), (256, 512)]
+    bufs = sum(2 * up(mm * r * 4) + up(nn * r * 4) for mm, nn in runs)
+    expect = bufs + 2 * up(2 * r * r * 4) + up(max(parts_of(*x) for x in runs)) + up(parts_of(256, 512)) + 16384
+    assert parts_of(256, 512) > 0
+    assert L.dion_workspace_bytes(p2, 2, 192) == expect
+
 
 def test_residual_iterations_rule(L):
     """The leading iterations that keep their bf16 residual: the larger of (1) how

@@ -115,3 +115,41 @@ def test_dion_layer_set(rank):
                              inp["W0"][sl].reshape(r_, c_), inp["Q0"][ql].reshape(c_, rank),
                              (Mh[sl].reshape(r_, c_), Qh[ql].reshape(c_, rank), Xh[sl].reshape(r_, c_)),
                              wl.mu, wl.eta)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("rank", [96, 48])
+def test_dion_lanes_match_one_call_per_shape(rank):
+    """The layer set's four shapes share two streams in one call; every run's
+    products, factorisations and column norms are the same kernels on the same
+    data as in a call that holds that run alone (one stream), so the two agree
+    bit for bit.  Two steps, so the second starts from the first's state."""
+    wl = DION_WORKLOADS[48]
+    inp = gen_dion(wl)
+    offs = wl.offsets
+    qn = [c_ * rank for _, c_ in wl.shapes]
+    qoffs = np.concatenate([[0], np.cumsum(qn)])
+    Q0 = random_matrix((int(qoffs[-1]),), [612, rank]).astype(np.float32)
+
+    def state():
+        return (torch.zeros(wl.numel, dtype=torch.float32, device="cuda"), dev(inp["W0"]), dev(Q0))
+
+    def probs_of(M, G, X, Q, js):
+        out = []
+        for j in js:
+            r_, c_ = wl.shapes[j]
+            out.append((M[offs[j]:offs[j + 1]].view(r_, c_), G[offs[j]:offs[j + 1]].view(r_, c_),
+                        X[offs[j]:offs[j + 1]].view(r_, c_), Q[qoffs[j]:qoffs[j + 1]].view(c_, rank)))
+        return out
+
+    G = dev(inp["G"])
+    one, per = state(), state()
+    shapes = sorted(set(wl.shapes))
+    for _ in range(2):
+        mao.dion_step(probs_of(*one[:1], G, *one[1:], range(len(wl.shapes))), rank, wl.mu, wl.eta)
+        for sh in shapes:
+            js = [j for j, s in enumerate(wl.shapes) if s == sh]
+            mao.dion_step(probs_of(*per[:1], G, *per[1:], js), rank, wl.mu, wl.eta)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("M", "X", "Q"), one, per):
+        assert torch.equal(a, b), f"{name} differs between one call and one call per shape"
