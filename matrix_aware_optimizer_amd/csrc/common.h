@@ -149,45 +149,50 @@ inline int launch_status() {
   return e == hipSuccess ? MUON_OK : MUON_ELAUNCH;
 }
 
-// The library's second stream on the current device (default priority, not
-// synchronising with the null stream), created on first use; null if it
-// cannot be created.  Host threads share it; each call orders its own work
-// with its own events.
-inline hipStream_t lane_stream() {
+// The library's own streams on the current device (default priority, not
+// synchronising with the null stream; stream i for i < kLibStreams), created
+// on first use; null if one cannot be created.  Host threads share them; each
+// call orders its own work with its own events.
+constexpr int kLibStreams = 3;
+inline hipStream_t lane_stream(int i = 0) {
   static std::mutex mu;
-  static hipStream_t streams[kMaxTrackedDevices] = {};
+  static hipStream_t streams[kMaxTrackedDevices][kLibStreams] = {};
   const int dev = current_device();
-  if (dev < 0 || dev >= kMaxTrackedDevices) return nullptr;
+  if (dev < 0 || dev >= kMaxTrackedDevices || i < 0 || i >= kLibStreams) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
-  if (streams[dev] == nullptr) {
+  if (streams[dev][i] == nullptr) {
     hipStream_t st = nullptr;
     if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    streams[dev] = st;
+    streams[dev][i] = st;
   }
-  return streams[dev];
+  return streams[dev][i];
 }
 
-// The fork and join events of this host thread on the current device,
-// created on first use and kept (a wait takes the event's last record at the
-// time it is enqueued, so reusing them call after call is safe).
-inline bool fork_join_events(hipEvent_t& fork, hipEvent_t& join) {
-  struct Pair {
-    hipEvent_t fork = nullptr, join = nullptr;
-  };
-  static thread_local Pair pairs[kMaxTrackedDevices];
+// n events of this host thread on the current device (n <= kLibStreams + 1:
+// a fork and one join per library stream), created on first use and kept (a
+// wait takes the event's last record at the time it is enqueued, so reusing
+// them call after call is safe).
+inline bool lane_events(hipEvent_t* ev, int n) {
+  static thread_local hipEvent_t events[kMaxTrackedDevices][kLibStreams + 1] = {};
   const int dev = current_device();
-  if (dev < 0 || dev >= kMaxTrackedDevices) return false;
-  Pair& e = pairs[dev];
-  if (e.fork == nullptr && hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess) {
-    e.fork = nullptr;
-    return false;
+  if (dev < 0 || dev >= kMaxTrackedDevices || n < 0 || n > kLibStreams + 1) return false;
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t& e = events[dev][i];
+    if (e == nullptr && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      e = nullptr;
+      return false;
+    }
+    ev[i] = e;
   }
-  if (e.join == nullptr && hipEventCreateWithFlags(&e.join, hipEventDisableTiming) != hipSuccess) {
-    e.join = nullptr;
-    return false;
-  }
-  fork = e.fork;
-  join = e.join;
+  return true;
+}
+
+// The fork and join events of one second stream.
+inline bool fork_join_events(hipEvent_t& fork, hipEvent_t& join) {
+  hipEvent_t ev[2];
+  if (!lane_events(ev, 2)) return false;
+  fork = ev[0];
+  join = ev[1];
   return true;
 }
 

@@ -809,30 +809,32 @@ std::vector<DRun> dion_runs(const muon_dion_problem* p, int count) {
   return runs;
 }
 
-// Two lanes: the caller's stream and the library's second stream, forked from
-// and joined back into the caller's with events.  Runs are placed largest
-// first on the lane with less work so far, and each lane takes the stages
-// below over its own runs.  The launches that leave most CUs idle (the
-// factorisation's one workgroup per matrix, the r x r Grams, the split-k
-// reductions, the column norms) then run beside the other lane's products.
+// Lanes: the caller's stream and up to three of the library's streams,
+// forked from and joined back into the caller's with events, one lane per run
+// up to that count.  Runs are placed largest first on the lane with the least
+// work so far, and each lane takes the stages below over its own runs.  The
+// launches that leave most CUs idle (the factorisation's one workgroup per
+// matrix, the r x r Grams, the split-k reductions, the column norms) then run
+// beside the other lanes' products.
 #ifndef MUON_DION_LANES
-#define MUON_DION_LANES 2
+#define MUON_DION_LANES 4
 #endif
 constexpr int kDionLanes = MUON_DION_LANES;
+static_assert(kDionLanes >= 1 && kDionLanes <= kLibStreams + 1, "one library stream per extra lane");
 
 // Workspace: every run keeps its own P (twice) and R, since the stages run
 // over all runs of a lane in turn; the Grams and their inverse factors sit in
-// two arrays, lane 0's matrices first, so each lane factors its matrices in
-// one launch; each lane has a split-k partial buffer for its products (lane
-// 0's is sized for every run, so all runs can also go to lane 0 alone, when
-// the second stream or the events cannot be had).
+// two arrays, lane by lane, so each lane factors its matrices in one launch;
+// each lane has a split-k partial buffer for its products (lane 0's is sized
+// for every run, so all runs can also go to lane 0 alone, when a stream or
+// the events cannot be had).
 struct DLayout {
   std::vector<size_t> p0, p1, R;
   std::vector<int> lane;        // lane of each run
   std::vector<int64_t> slot;    // first matrix of each run in the Gram and factor arrays
-  int64_t lane_mats[2] = {0, 0};
+  int64_t lane_mats[kDionLanes] = {};
   int lanes = 1;
-  size_t gram = 0, linv = 0, part[2] = {0, 0}, zero = 0, total = 0;
+  size_t gram = 0, linv = 0, part[kDionLanes] = {}, zero = 0, total = 0;
 };
 
 size_t run_part_bytes(const DRun& r, int rank) {
@@ -845,30 +847,34 @@ DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
   const size_t rk = static_cast<size_t>(rank);
   DLayout L{};
   L.lane.assign(runs.size(), 0);
-  if (kDionLanes >= 2 && runs.size() >= 2) {
+  L.lanes = static_cast<int>(std::min<size_t>(kDionLanes, runs.size()));
+  if (L.lanes > 1) {
     // every product of a run moves or multiplies in proportion to its m n
     std::vector<size_t> order(runs.size());
     for (size_t i = 0; i < order.size(); ++i) order[i] = i;
     auto cost = [&](size_t i) { return static_cast<double>(runs[i].count) * runs[i].m * runs[i].n; };
     std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return cost(x) > cost(y); });
-    double load[2] = {0.0, 0.0};
+    double load[kDionLanes] = {};
     for (size_t i : order) {
-      const int l = load[1] < load[0] ? 1 : 0;
+      int l = 0;
+      for (int j = 1; j < L.lanes; ++j)
+        if (load[j] < load[l]) l = j;
       L.lane[i] = l;
       load[l] += cost(i);
     }
-    L.lanes = load[1] > 0.0 ? 2 : 1;
   }
   L.slot.assign(runs.size(), 0);
-  for (int l = 0; l < 2; ++l)
+  int64_t slots = 0;
+  for (int l = 0; l < L.lanes; ++l)
     for (size_t k = 0; k < runs.size(); ++k)
       if (L.lane[k] == l) {
-        L.slot[k] = L.lane_mats[0] + L.lane_mats[1];
+        L.slot[k] = slots;
+        slots += runs[k].count;
         L.lane_mats[l] += runs[k].count;
       }
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
-  size_t part[2] = {0, 0};
+  size_t part[kDionLanes] = {};
   for (size_t k = 0; k < runs.size(); ++k) {
     const DRun& r = runs[k];
     const size_t b = static_cast<size_t>(r.count);
@@ -877,12 +883,11 @@ DLayout dion_layout(const std::vector<DRun>& runs, int count, int rank) {
     L.R.push_back(take(b * r.n * rk * 4));
     const size_t pb = run_part_bytes(r, rank);
     part[0] = std::max(part[0], pb);
-    if (L.lane[k] == 1) part[1] = std::max(part[1], pb);
+    if (L.lane[k] > 0) part[L.lane[k]] = std::max(part[L.lane[k]], pb);
   }
   L.gram = take(static_cast<size_t>(count) * rk * rk * 4);
   L.linv = take(static_cast<size_t>(count) * rk * rk * 4);
-  L.part[0] = take(part[0]);
-  L.part[1] = take(part[1]);
+  for (int l = 0; l < kDionLanes; ++l) L.part[l] = take(part[l]);
   L.zero = take(kZeroPageFloats * sizeof(float));
   L.total = off;
   return L;
@@ -1075,26 +1080,38 @@ int dion_step(const muon_dion_problem* probs, int count, int rank, float mu, flo
     if (status != MUON_OK) return status;
   }
   const DionCall C{&runs, &sorted, &L, ws, rank, lds, mu, eta, zp};
-  float* part[2] = {reinterpret_cast<float*>(ws + L.part[0]), reinterpret_cast<float*>(ws + L.part[1])};
-  hipStream_t lane1 = L.lanes == 2 ? lane_stream() : nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (lane1 != nullptr && (!fork_join_events(fork, join) || hipEventRecord(fork, st) != hipSuccess ||
-                           hipStreamWaitEvent(lane1, fork, 0) != hipSuccess))
-    lane1 = nullptr;   // every run on the caller's stream
-  std::vector<int> ids[2];
-  for (int l = 0; l < 2; ++l)
+  // the lanes' streams, forked from the caller's; with any of them or the
+  // events missing, every run goes to the caller's stream
+  int lanes = L.lanes;
+  hipStream_t lane_st[kDionLanes] = {st};
+  hipEvent_t ev[kDionLanes] = {};   // the fork, then the joins of lanes 1 ..
+  for (int l = 1; l < lanes; ++l)
+    if ((lane_st[l] = lane_stream(l - 1)) == nullptr) lanes = 1;
+  if (lanes > 1 && (!lane_events(ev, lanes) || hipEventRecord(ev[0], st) != hipSuccess)) lanes = 1;
+  int forked = 1;   // lanes 1 .. forked - 1 wait on the fork (and are joined below)
+  for (int l = 1; l < lanes; ++l, ++forked)
+    if (hipStreamWaitEvent(lane_st[l], ev[0], 0) != hipSuccess) break;
+  if (forked < lanes) lanes = 1;
+  std::vector<int> ids[kDionLanes];
+  int64_t mats[kDionLanes] = {}, slot0[kDionLanes] = {};
+  for (int l = 0; l < L.lanes; ++l)   // lane by lane: the order of the Gram slots
     for (size_t k = 0; k < runs.size(); ++k)
-      if (L.lane[k] == l) ids[lane1 != nullptr ? l : 0].push_back(static_cast<int>(k));
-  const int64_t mats[2] = {lane1 != nullptr ? L.lane_mats[0] : count, lane1 != nullptr ? L.lane_mats[1] : 0};
-  // the lanes' launches are enqueued stage by stage, so both start at once
-  int status = MUON_OK;
-  for (int stage = 0; stage < kDionStagesPerCall && status == MUON_OK; ++stage) {
-    status = dion_stage(C, stage, ids[0], part[0], 0, mats[0], st);
-    if (status == MUON_OK && lane1 != nullptr) status = dion_stage(C, stage, ids[1], part[1], mats[0], mats[1], lane1);
+      if (L.lane[k] == l) ids[lanes > 1 ? l : 0].push_back(static_cast<int>(k));
+  if (lanes > 1) {
+    for (int l = 0; l < lanes; ++l) mats[l] = L.lane_mats[l];
+    for (int l = 1; l < lanes; ++l) slot0[l] = slot0[l - 1] + mats[l - 1];
+  } else {
+    mats[0] = count;
   }
-  if (lane1 != nullptr && (hipEventRecord(join, lane1) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess) &&
-      status == MUON_OK)
-    status = MUON_ELAUNCH;
+  // the lanes' launches are enqueued stage by stage, so all start at once
+  int status = MUON_OK;
+  for (int stage = 0; stage < kDionStagesPerCall && status == MUON_OK; ++stage)
+    for (int l = 0; l < lanes && status == MUON_OK; ++l)
+      status = dion_stage(C, stage, ids[l], reinterpret_cast<float*>(ws + L.part[l]), slot0[l], mats[l], lane_st[l]);
+  for (int l = 1; l < forked; ++l)
+    if ((hipEventRecord(ev[l], lane_st[l]) != hipSuccess || hipStreamWaitEvent(st, ev[l], 0) != hipSuccess) &&
+        status == MUON_OK)
+      status = MUON_ELAUNCH;
   return status;
 }
 
