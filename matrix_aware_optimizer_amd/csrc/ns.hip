@@ -675,18 +675,21 @@ int run_one(const Run& r, char* ws, const gemm::Scratch& sc, int precision, floa
   return MUON_OK;
 }
 
-// Runs of different shapes (a layer set) go to two lanes, the caller's stream
-// and a second stream of the library's, forked from and joined back into the
+// Runs of different shapes (a layer set) go to lanes, the caller's stream and
+// up to three streams of the library's, forked from and joined back into the
 // caller's stream with events: the small launches of one run then fill the
 // CUs that another run's tails and ramps leave idle.  Measured on the
-// GPT-2-small set (four runs on two streams): 2.15 -> 2.0 ms.  Each lane has
+// GPT-2-small set (four runs on two streams): 2.15 -> 2.0 ms; on three and four
+// streams it ran 2% and 5% slower than on two (these products fill the CUs
+// better than Dion's, and more runs at once share the caches).  Each lane has
 // its own run buffers and split scratch; lane 0's are sized for every run, so
-// all runs can also go to lane 0 alone (when the second stream or the events
-// cannot be had).
+// all runs can also go to lane 0 alone (when a stream or the events cannot be
+// had).
 #ifndef MUON_NS_LANES
 #define MUON_NS_LANES 2
 #endif
 constexpr int kNsLanes = MUON_NS_LANES;
+static_assert(kNsLanes >= 1 && kNsLanes <= kLibStreams + 1, "one library stream per extra lane");
 
 // relative cost of a run (its products' multiply-adds per iteration)
 double run_cost(const Run& r) {
@@ -696,37 +699,53 @@ double run_cost(const Run& r) {
 
 struct LanePlan {
   int lanes = 1;
-  std::vector<int> lane;          // lane of each run
-  size_t split[2] = {0, 0};       // split scratch of each lane (counters first)
-  size_t bufs[2] = {0, 0};        // run buffers of each lane
-  size_t total() const { return split[0] + split[1] + bufs[0] + bufs[1]; }
+  std::vector<int> lane;                // lane of each run
+  size_t split[kNsLanes] = {};          // split scratch of each lane (counters first)
+  size_t bufs[kNsLanes] = {};           // run buffers of each lane
+  size_t split_off(int l) const {
+    size_t o = 0;
+    for (int i = 0; i < l; ++i) o += split[i];
+    return o;
+  }
+  size_t bufs_off(int l) const {
+    size_t o = split_off(kNsLanes);
+    for (int i = 0; i < l; ++i) o += bufs[i];
+    return o;
+  }
+  size_t total() const { return bufs_off(kNsLanes); }
 };
 
-// Workspace: [split scratch 0][split scratch 1][run buffers 0][run buffers 1].
-// Runs are placed largest first on the lane with less work so far.
+// Workspace: [split scratch 0][split scratch 1] .. [run buffers 0][run buffers 1] ..
+// Runs are placed largest first on the lane with the least work so far.
 LanePlan plan_lanes(const std::vector<Run>& runs, int precision) {
   LanePlan P;
   P.lane.assign(runs.size(), 0);
   P.split[0] = split_region(runs, precision).bytes;
   P.bufs[0] = runs_bytes(runs, precision);
-  if (kNsLanes < 2 || runs.size() < 2) return P;
+  P.lanes = static_cast<int>(std::min<size_t>(kNsLanes, runs.size()));
+  if (P.lanes < 2) {
+    P.lanes = 1;
+    return P;
+  }
   std::vector<size_t> order(runs.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(),
                    [&](size_t x, size_t y) { return run_cost(runs[x]) > run_cost(runs[y]); });
-  double load[2] = {0.0, 0.0};
-  std::vector<Run> second;
+  double load[kNsLanes] = {};
   for (size_t i : order) {
-    const int l = load[1] < load[0] ? 1 : 0;
+    int l = 0;
+    for (int j = 1; j < P.lanes; ++j)
+      if (load[j] < load[l]) l = j;
     P.lane[i] = l;
     load[l] += run_cost(runs[i]);
   }
-  for (size_t i = 0; i < runs.size(); ++i)
-    if (P.lane[i] == 1) second.push_back(runs[i]);
-  if (second.empty()) return P;
-  P.lanes = 2;
-  P.split[1] = split_region(second, precision).bytes;
-  P.bufs[1] = runs_bytes(second, precision);
+  for (int l = 1; l < P.lanes; ++l) {
+    std::vector<Run> mine;
+    for (size_t i = 0; i < runs.size(); ++i)
+      if (P.lane[i] == l) mine.push_back(runs[i]);
+    P.split[l] = split_region(mine, precision).bytes;
+    P.bufs[l] = runs_bytes(mine, precision);
+  }
   return P;
 }
 
@@ -766,32 +785,42 @@ int ns_orthogonalize(const muon_ns_problem* probs, int count, float a, float b, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   // bf16 products may split (a symmetric product with one tile row needs no
-  // scratch: its only unit is the diagonal lower half).  Both lanes report a
+  // scratch: its only unit is the diagonal lower half).  Every lane reports a
   // wait that runs out in lane 0's error word, the one ns_workspace_status reads.
   int* error_word = reinterpret_cast<int*>(base) + gemm::kSplitCounters;
   const bool bf16 = precision == MUON_BF16;
-  const gemm::Scratch sc[2] = {gemm::Scratch{bf16 ? base : nullptr, P.split[0]},
-                               gemm::Scratch{bf16 ? base + P.split[0] : nullptr, P.split[1], error_word}};
-  char* bufs[2] = {base + P.split[0] + P.split[1], base + P.split[0] + P.split[1] + P.bufs[0]};
-  {
-    // arrival counters and the error word start at zero on every call
-    int status = zero_counters(base, gemm::kSplitWords, st);
-    if (status == MUON_OK && P.lanes == 2) status = zero_counters(base + P.split[0], gemm::kSplitWords, st);
+  gemm::Scratch sc[kNsLanes];
+  char* bufs[kNsLanes];
+  for (int l = 0; l < kNsLanes; ++l) {
+    sc[l] = gemm::Scratch{bf16 ? base + P.split_off(l) : nullptr, P.split[l], l > 0 ? error_word : nullptr};
+    bufs[l] = base + P.bufs_off(l);
+  }
+  // arrival counters and the error word start at zero on every call
+  for (int l = 0; l < P.lanes; ++l) {
+    const int status = zero_counters(base + P.split_off(l), gemm::kSplitWords, st);
     if (status != MUON_OK) return status;
   }
-  hipStream_t lane1 = P.lanes == 2 ? lane_stream() : nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (lane1 != nullptr && (!fork_join_events(fork, join) || hipEventRecord(fork, st) != hipSuccess ||
-                           hipStreamWaitEvent(lane1, fork, 0) != hipSuccess))
-    lane1 = nullptr;   // every run on the caller's stream
+  // the lanes' streams, forked from the caller's; with any of them or the
+  // events missing, every run goes to the caller's stream
+  int lanes = P.lanes;
+  hipStream_t lane_st[kNsLanes] = {st};
+  hipEvent_t ev[kNsLanes] = {};   // the fork, then the joins of lanes 1 ..
+  for (int l = 1; l < lanes; ++l)
+    if ((lane_st[l] = lane_stream(l - 1)) == nullptr) lanes = 1;
+  if (lanes > 1 && (!lane_events(ev, lanes) || hipEventRecord(ev[0], st) != hipSuccess)) lanes = 1;
+  int forked = 1;   // lanes 1 .. forked - 1 wait on the fork (and are joined below)
+  for (int l = 1; l < lanes; ++l, ++forked)
+    if (hipStreamWaitEvent(lane_st[l], ev[0], 0) != hipSuccess) break;
+  if (forked < lanes) lanes = 1;
   int status = MUON_OK;
   for (size_t i = 0; i < runs.size() && status == MUON_OK; ++i) {
-    const int l = lane1 != nullptr ? P.lane[i] : 0;
-    status = run_one(runs[i], bufs[l], sc[l], precision, a, b, c, steps, l == 1 ? lane1 : st);
+    const int l = lanes > 1 ? P.lane[i] : 0;
+    status = run_one(runs[i], bufs[l], sc[l], precision, a, b, c, steps, lane_st[l]);
   }
-  if (lane1 != nullptr && (hipEventRecord(join, lane1) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess) &&
-      status == MUON_OK)
-    status = MUON_ELAUNCH;
+  for (int l = 1; l < forked; ++l)
+    if ((hipEventRecord(ev[l], lane_st[l]) != hipSuccess || hipStreamWaitEvent(st, ev[l], 0) != hipSuccess) &&
+        status == MUON_OK)
+      status = MUON_ELAUNCH;
   return status;
 }
 
