@@ -180,14 +180,15 @@ int muon_momentum_noalloc(void* M, int m_dtype, const void* G, int g_dtype, int6
  *   Problems of equal shape and dtypes whose pointers are evenly spaced are
  *   batched into one launch per stage (a run).  steps == 0 gives U = X0.
  *   Streams: with two or more runs, the runs are shared out (largest first,
- *   onto the lighter side) between `stream` and a second stream the library
- *   creates once per device (default priority, not synchronising with the
- *   null stream).  The second side starts after the work already enqueued on
- *   `stream` (an event recorded there) and `stream` waits for it before any
- *   later work (an event recorded on the second stream), so to the caller
- *   the call behaves like work on `stream` alone.  The events are the calling
- *   host thread's own; host threads share the second stream.  If the stream
- *   or the events cannot be created, every run goes on `stream`.
+ *   onto the lighter side) between `stream` and a second stream, the first of
+ *   the three the library creates once per device (default priority, not
+ *   synchronising with the null stream).  The second side starts after the
+ *   work already enqueued on `stream` (an event recorded there) and `stream`
+ *   waits for it before any later work (an event recorded on the second
+ *   stream), so to the caller the call behaves like work on `stream` alone.
+ *   The events are the calling host thread's own; host threads share the
+ *   library's streams.  If a stream or the events cannot be created, every
+ *   run goes on `stream`.
  *   workspace  device, at least ns_workspace_bytes(probs, count, precision)
  *              bytes, 16-byte aligned, owned by the caller; its contents on
  *              entry do not matter (the call clears what must start at zero)
@@ -451,7 +452,17 @@ int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u
  * 64 x 64 (times 48 for the rank-wide products) per product; beyond them
  * dion_step returns MUON_EINVAL before launching anything and
  * dion_workspace_bytes returns 0.
- * workspace  dion_workspace_bytes(probs, count, rank) bytes.
+ * Streams: the runs (one per shape) are shared out, largest first onto the
+ * side with the least work, between `stream` and up to three streams of the
+ * library's (one side per run, at most four), forked from `stream` with an
+ * event and joined back into it, as in ns_orthogonalize: to the caller the
+ * call behaves like work on `stream` alone, and every run computes what it
+ * computes in a call of its own.
+ * workspace  dion_workspace_bytes(probs, count, rank) bytes, 16-byte aligned,
+ *            owned by the caller; contents on entry do not matter.  It holds
+ *            each run's P and R, the Grams and their inverse factors, a
+ *            split-k buffer per side and a 16 KB page of zeros.  Calls that
+ *            share a workspace must not overlap in time.
  * ------------------------------------------------------------------------- */
 #define MUON_DION_MAX_RANK 192
 
