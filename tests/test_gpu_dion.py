@@ -153,3 +153,44 @@ def test_dion_lanes_match_one_call_per_shape(rank):
     torch.cuda.synchronize()
     for name, a, b in zip(("M", "X", "Q"), one, per):
         assert torch.equal(a, b), f"{name} differs between one call and one call per shape"
+
+
+@pytest.mark.parametrize("rank", [16, 44])
+def test_dion_more_runs_than_streams(rank):
+    """Six shapes (six runs) in one call share four streams, so some streams
+    take two runs and factor both runs' matrices in one launch; the result
+    equals one call per shape bit for bit, and sampled matrices match the
+    oracle."""
+    shapes = [(64, 128), (64, 128), (96, 64), (96, 64), (96, 64), (128, 256), (48, 72), (48, 72), (200, 100),
+              (256, 96)]
+    sizes = [r_ * c_ for r_, c_ in shapes]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    qoffs = np.concatenate([[0], np.cumsum([c_ * rank for _, c_ in shapes])])
+    G = (random_matrix((int(offs[-1]),), [613, rank]) * 0.02).astype(np.float32)
+    X0 = (random_matrix((int(offs[-1]),), [614, rank]) * 0.02).astype(np.float32)
+    Q0 = random_matrix((int(qoffs[-1]),), [615, rank]).astype(np.float32)
+
+    def state():
+        return torch.zeros(int(offs[-1]), dtype=torch.float32, device="cuda"), dev(X0), dev(Q0)
+
+    def probs_of(M, Gd, X, Q, js):
+        return [(M[offs[j]:offs[j + 1]].view(*shapes[j]), Gd[offs[j]:offs[j + 1]].view(*shapes[j]),
+                 X[offs[j]:offs[j + 1]].view(*shapes[j]), Q[qoffs[j]:qoffs[j + 1]].view(shapes[j][1], rank))
+                for j in js]
+
+    Gd = dev(G)
+    one, per = state(), state()
+    mao.dion_step(probs_of(one[0], Gd, one[1], one[2], range(len(shapes))), rank, 0.95, 0.02)
+    for sh in sorted(set(shapes)):
+        js = [j for j, s in enumerate(shapes) if s == sh]
+        mao.dion_step(probs_of(per[0], Gd, per[1], per[2], js), rank, 0.95, 0.02)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("M", "X", "Q"), one, per):
+        assert torch.equal(a, b), f"{name} differs between one call and one call per shape"
+    Mh, Xh, Qh = (t.cpu().numpy() for t in one)
+    for j in (0, 4, 5, 7, 9):
+        r_, c_ = shapes[j]
+        sl, ql = slice(offs[j], offs[j + 1]), slice(qoffs[j], qoffs[j + 1])
+        check_against_oracle(np.zeros((r_, c_), np.float32), G[sl].reshape(r_, c_), X0[sl].reshape(r_, c_),
+                             Q0[ql].reshape(c_, rank),
+                             (Mh[sl].reshape(r_, c_), Qh[ql].reshape(c_, rank), Xh[sl].reshape(r_, c_)), 0.95, 0.02)
