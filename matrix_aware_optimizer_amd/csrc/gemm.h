@@ -88,6 +88,10 @@ enum Split { SPLIT_NONE = 0, SPLIT_SYRK = 1, SPLIT_DIAG = 2, SPLIT_TRI = 3 };
 #define MUON_SYRK_TRI 1
 #endif
 constexpr bool kSyrkTri = MUON_SYRK_TRI != 0;
+#ifndef MUON_SYRK_HALF_ORDER
+#define MUON_SYRK_HALF_ORDER 1
+#endif
+constexpr bool kSyrkHalfOrder = MUON_SYRK_HALF_ORDER != 0;
 // default bound on the polls of the second K half waiting for the first
 // one's partial (each poll sleeps ~128 cycles; the first half never needs
 // more than microseconds, the bound only keeps a wait from outliving its
@@ -531,6 +535,29 @@ template <> struct DiagPattern<2> {   // rows {64, 0, 32}: blocks (2,0) (2,1) (2
   static constexpr int IA[NB] = {0, 0, 0, 2, 2}, IB[NB] = {1, 2, 0, 1, 2};
 };
 
+// Off-diagonal tile t (0 <= t < n_p (n_p - 1) / 2) of a lower triangle of n_p
+// tile rows, in the order of the split Gram's units: blocks of 8 tile columns,
+// and within a block row by row (rows i > j).  The XCD-grouped launch hands
+// each XCD 32 consecutive units, all of one K half: a column block then
+// reads its few row panels (the block's columns and the rows it spans) over
+// one K range in step, and the XCD's L2 serves the repeats.  Modelled per
+// XCD at 4096 (16 tile rows): 77% of the panel reads are repeats, against 62%
+// for tile rows with both halves side by side.
+__device__ __forceinline__ void syrk_offdiag_tile(int64_t np, int64_t t, int64_t& ti, int64_t& tj) {
+  for (int64_t j0 = 0;; j0 += 8) {
+    const int64_t j1 = min(j0 + 8, np - 1);   // columns [j0, j1) of this block
+    for (int64_t i = j0 + 1; i < np; ++i) {
+      const int64_t c = min(i, j1) - j0;      // tiles of row i in the block
+      if (t < c) {
+        ti = i;
+        tj = j0 + t;
+        return;
+      }
+      t -= c;
+    }
+  }
+}
+
 // Sign bit of a stored value: 1 iff !(u < 0) on its encoding (+0, -0 and NaN
 // give 1), the rule of the 1-bit packing.
 __device__ __forceinline__ uint32_t nonneg_bf16(bf16_t h) { return !(h > 0x8000u && h <= 0xff80u); }
@@ -614,7 +641,22 @@ __device__ __forceinline__ void gemm_dma_unit(const GemmArgs& g, const int64_t b
   int half = 0;
   bool diag_half = false;
   const int64_t tiles = SYRK ? (g.M / BM) * (g.M / BM + 1) / 2 : (g.M / BM) * (g.N / BN);
-  if (SPLITS && g.split_mode == SPLIT_SYRK) {
+  if (SPLITS && g.split_mode == SPLIT_SYRK && kSyrkHalfOrder) {
+    // n_p^2 units per batch entry: the first K halves of the T = n_p (n_p - 1) / 2
+    // off-diagonal tiles, then their second halves, then the lower halves of
+    // the n_p diagonal tiles (syrk_offdiag_tile gives the tile order)
+    const int64_t np = g.M / BM, T = np * (np - 1) / 2;
+    const int64_t v = bid;
+    if (v < 2 * T) {
+      half = v >= T ? 1 : 0;
+      const int64_t t = v - half * T;
+      syrk_offdiag_tile(np, t, tm, tn);
+      sidx = batch * T + t;
+    } else {
+      tm = tn = v - 2 * T;
+      diag_half = true;
+    }
+  } else if (SPLITS && g.split_mode == SPLIT_SYRK) {
     // n_p^2 units per batch entry: tile row i holds units [i^2, (i+1)^2): the two
     // K halves of tiles (i, 0..i-1), then the lower half of diagonal tile (i, i)
     const int64_t np = g.M / BM;
