@@ -402,7 +402,12 @@ __device__ __forceinline__ float from_lane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__ G, int64_t sG,
+#ifndef MUON_CHOL_THREADS
+#define MUON_CHOL_THREADS 512
+#endif
+constexpr int kCholThreads = MUON_CHOL_THREADS;   // threads of the factorisation's workgroup
+constexpr int kCholWaves = kCholThreads / 64;
+__global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __restrict__ G, int64_t sG,
                                                       float* __restrict__ Linv, int64_t sL, int r) {
   extern __shared__ float sm[];
   const int nb = (r + kCb - 1) / kCb, rp = nb * kCb, ld = rp + 1;
@@ -414,16 +419,16 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
   // loads in flight per thread; the padding is an identity block
   if (r % 4 == 0) {
     const int q = r / 4, n4 = r * q;
-    for (int e0 = 0; e0 < n4; e0 += 256 * 8) {
+    for (int e0 = 0; e0 < n4; e0 += kCholThreads * 8) {
       float4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
+        const int e = e0 + u * kCholThreads + tid;
         v[u] = reinterpret_cast<const float4*>(Gb)[e < n4 ? e : 0];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
+        const int e = e0 + u * kCholThreads + tid;
         if (e < n4) {
           const int i = e / q, k = 4 * (e % q);
           float* d = S + i * ld + k;
@@ -436,16 +441,16 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
     }
   } else {
     const int n = r * r;
-    for (int e0 = 0; e0 < n; e0 += 256 * 8) {
+    for (int e0 = 0; e0 < n; e0 += kCholThreads * 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
+        const int e = e0 + u * kCholThreads + tid;
         v[u] = Gb[e < n ? e : 0];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * 256 + tid;
+        const int e = e0 + u * kCholThreads + tid;
         if (e < n) {
           const int i = e / r, k = e % r;
           S[i * ld + k] = k <= i ? v[u] : 0.0f;
@@ -453,25 +458,25 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
       }
     }
   }
-  for (int e = tid; e < rp * rp - r * r; e += 256) {
+  for (int e = tid; e < rp * rp - r * r; e += kCholThreads) {
     // padding rows r.. (all columns), then columns r.. of rows < r
     const int pr = (rp - r) * rp;
     const int i = e < pr ? r + e / rp : (e - pr) / (rp - r), k = e < pr ? e % rp : r + (e - pr) % (rp - r);
     S[i * ld + k] = i == k ? 1.0f : 0.0f;
   }
   __syncthreads();
-  for (int i = tid; i < rp; i += 256) g0[i] = S[i * ld + i];   // read before the first factorisation
+  for (int i = tid; i < rp; i += kCholThreads) g0[i] = S[i * ld + i];   // read before the first factorisation
 
   for (int J = 0; J < nb; ++J) {
     const int c0 = J * kCb;
     if (J > 0) {
       // panel: A(i, c0 + k) -= sum_{m < c0} L(i, m) L(c0 + k, m), lower part,
-      // on fp32 matrix cores: wave w takes the 16-row blocks J + w, J + w + 4,
-      // ...; v_mfma_f32_16x16x4f32 with lane l supplying L(16 ib + l % 16,
+      // on fp32 matrix cores: wave w takes the 16-row blocks J + w, J + w + W,
+      // ... (W waves); v_mfma_f32_16x16x4f32 with lane l supplying L(16 ib + l % 16,
       // m + l / 16) and L(c0 + l % 16, m + l / 16), and holding result rows
       // 4 (l / 16) .. + 3 of column l % 16
       const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
-      for (int ib = J + wave; ib < nb; ib += 4) {
+      for (int ib = J + wave; ib < nb; ib += kCholWaves) {
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         const float* ar = S + (kCb * ib + li) * ld + lk;
         const float* br = S + (c0 + li) * ld + lk;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
     }
     __syncthreads();
     // rows below: L(i, c0 + k) = sum_{m <= k} A(i, c0 + m) D(k, m)
-    for (int i = c0 + kCb + tid; i < rp; i += 256) {
+    for (int i = c0 + kCb + tid; i < rp; i += kCholThreads) {
       float v[kCb];
 #pragma unroll
       for (int c = 0; c < kCb; ++c) v[c] = S[i * ld + c0 + c];
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
 
   // W_IK = D_I L_IK for every block left of the diagonal, one column per thread
   const int nw = kCb * nb * (nb - 1) / 2;
-  for (int w = tid; w < nw; w += 256) {
+  for (int w = tid; w < nw; w += kCholThreads) {
     int I = 1;
     while (kCb * I * (I + 1) / 2 <= w) ++I;
     const int col = w - kCb * I * (I - 1) / 2, r0 = kCb * I;
@@ -569,11 +574,11 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
   __syncthreads();
   // X_IJ(i, j) = -sum_{16 J <= c < 16 I} S(16 I + i, c) S(16 J + j, c), stored at S(16 J + j, 16 I + i)
   for (int d = 1; d < nb; ++d) {
-    // block (J + d, J) on fp32 matrix cores, one wave per block (J = w, w + 4,
+    // block (J + d, J) on fp32 matrix cores, one wave per block (J = w, w + W,
     // ...): lane l supplies S(16 I + l % 16, c + l / 16) and S(16 J + l % 16,
     // c + l / 16) and holds rows 4 (l / 16) .. + 3 of column l % 16
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
-    for (int J = wave; J < nb - d; J += 4) {
+    for (int J = wave; J < nb - d; J += kCholWaves) {
       const int I = J + d;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
       const float* ar = S + (kCb * I + li) * ld + lk;
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(const float* __restrict__
     __syncthreads();
   }
   float* Lb = Linv + int64_t(blockIdx.x) * sL;
-  for (int e = tid; e < r * r; e += 256) {
+  for (int e = tid; e < r * r; e += kCholThreads) {
     const int i = e / r, k = e % r;
     Lb[e] = k <= i ? S[k * ld + i] : 0.0f;
   }
@@ -985,7 +990,7 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
       }
     } else if (step == 1) {
       if (nmat > 0) {
-        launch_kernel(chol_inv_kernel, dim3(nmat), dim3(256), C.chol_lds, st, Gm + slot0 * r * r, r * r,
+        launch_kernel(chol_inv_kernel, dim3(nmat), dim3(kCholThreads), C.chol_lds, st, Gm + slot0 * r * r, r * r,
                       Li + slot0 * r * r, r * r, C.rank);
         status = launch_status();
       }
