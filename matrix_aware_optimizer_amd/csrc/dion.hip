@@ -362,6 +362,112 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   }
 }
 
+// A 64 x 48 output tile, for an output width N that is a multiple of 48 but
+// not of 64 (rank 48 or 96, where 64-wide tiles would compute a quarter or a
+// third of padding).  Wave w owns rows 16 w .. 16 w + 15 and all 48 columns
+// as three 16 x 16 blocks on v_mfma_f32_16x16x4f32: lane l supplies A(16 w +
+// l % 16, k) and B(k, 16 j + l % 16) for the product's k-slot l / 16 and
+// holds rows 4 (l / 16) .. + 3 of column l % 16.  Operands are staged as in
+// dion_gemm_dma_kernel (the B tile keeps 64 output indices: the last 16 are
+// loaded, clamped at the edge, and not used).  In each 16-deep k group g,
+// k-slot q of product t (t = 0..3) is k = 16 g + 4 q + t, so a k-contiguous
+// lane's 16-byte read feeds four products.
+template <int S, bool ACK, bool BCK>
+__global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int splits, float* part,
+                                                              const float* zero) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int64_t b = blockIdx.z / splits;
+  const int sp = blockIdx.z % splits;
+  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * 48;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, q = lane >> 4;
+  const int arow = 16 * wave + li;   // the tile row this lane supplies
+  const DmaOperand oa{g.A + b * g.sA, g.a_i, g.a_k, g.M, g.K};
+  const DmaOperand ob{g.B + b * g.sB, g.b_j, g.b_k, g.N, g.K};
+  const int64_t ktiles = (g.K + kDK - 1) / kDK;
+  const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
+  const int nk = static_cast<int>(kt1 - kt0);
+  const uint32_t lds0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
+  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
+  auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
+    const int64_t k0 = kt * kDK;
+    const uint32_t sa = lds0 + stage * 2 * kDmaTileBytes, sb = sa + kDmaTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot0 = 64 * (2 * wave + i);
+      dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
+      dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, zspread + 1), sb + 16 * slot0);
+    }
+  };
+  f32x4_t acc[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, kt0 + s);
+  for (int it = 0; it < nk; ++it) {
+    if (it + S - 1 < nk) {
+      dion_wait_vm_barrier<4 * (S - 2)>();
+      issue((it + S - 1) % S, kt0 + it + S - 1);
+    } else {
+      dion_wait_vm_barrier<0>();
+    }
+    const char* ta = dsm + (it % S) * 2 * kDmaTileBytes;
+    const char* tb = ta + kDmaTileBytes;
+#pragma unroll
+    for (int gk = 0; gk < 2; ++gk) {
+      float av[4];
+      if constexpr (ACK) {
+        const int c = 4 * gk + q;
+        const float4 v = *reinterpret_cast<const float4*>(ta + arow * 128 + ((c ^ (arow & 7)) << 4));
+        av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          av[t] = *reinterpret_cast<const float*>(ta + ((16 * gk + 4 * q + t) * kDT + arow) * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int bcol = 16 * j + li;
+        float bv[4];
+        if constexpr (BCK) {
+          const int c = 4 * gk + q;
+          const float4 v = *reinterpret_cast<const float4*>(tb + bcol * 128 + ((c ^ (bcol & 7)) << 4));
+          bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            bv[t] = *reinterpret_cast<const float*>(tb + ((16 * gk + 4 * q + t) * kDT + bcol) * 4);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc[j], 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every stage has landed
+  float* Pp = splits > 1 ? part + (int64_t(sp) * gridDim.z / splits + b) * g.M * g.N : nullptr;
+  float* C = g.C + b * g.sC;
+  const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int64_t col = j0 + 16 * j + li;
+    if (col >= g.N) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = i0 + 16 * wave + 4 * q + v;
+      if (row >= g.M) continue;
+      if (Pp != nullptr) {
+        Pp[row * g.N + col] = acc[j][v];
+      } else {
+        float o = g.alpha * acc[j][v];
+        if (g.beta != 0.0f) o = fmaf(g.beta, Z[row * g.ldz + col], o);
+        C[row * g.ldc + col] = o;
+      }
+    }
+  }
+}
+
 // the zero page the DMA kernel's tail chunks read (16 KB)
 __global__ __launch_bounds__(256) void zero_page_kernel(float* z) { z[blockIdx.x * 256 + threadIdx.x] = 0.0f; }
 
@@ -693,15 +799,21 @@ __global__ __launch_bounds__(256) void add_kernel(float* __restrict__ M, int64_t
 
 // k ranges per output tile: enough workgroups to cover the chip (about 1024),
 // at least 256 of k per range, at most 16 ranges
-int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  const int64_t blocks = ((N + kDT - 1) / kDT) * ((M + kDT - 1) / kDT) * batch;
+// 48-wide output tiles (dion_gemm_dma48_kernel) for widths that are multiples
+// of 48 but not of 64, when the operands can be staged by DMA
+bool use48(int64_t N) { return N % 48 == 0 && N % kDT != 0; }
+
+int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch, bool w48 = false) {
+  const int64_t blocks = (w48 ? N / 48 : (N + kDT - 1) / kDT) * ((M + kDT - 1) / kDT) * batch;
   int64_t s = (1024 + blocks - 1) / blocks;
   s = std::min<int64_t>(s, std::max<int64_t>(1, K / 256));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
 }
 
 size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  const int s = gemm_splits(M, N, K, batch);
+  // the larger of the two tile widths' split counts (the width is chosen per
+  // product, from whether its operands can be staged by DMA)
+  const int s = std::max(gemm_splits(M, N, K, batch), use48(N) ? gemm_splits(M, N, K, batch, true) : 1);
   return s > 1 ? static_cast<size_t>(s) * batch * M * N * 4 : 0;
 }
 
@@ -739,9 +851,26 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
           int64_t M, int64_t N, int64_t K, float alpha, float beta, int64_t batch, float* part,
           const float* zero, hipStream_t st) {
   DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta};
+  const bool dma = zero && dma_operand_ok(A, sA, a_i, a_k, M, K) && dma_operand_ok(B, sB, b_j, b_k, N, K);
+  if (dma && use48(N)) {
+    const int splits = gemm_splits(M, N, K, batch, true);
+    const dim3 grid(N / 48, (M + kDT - 1) / kDT, batch * splits);
+    const uint32_t lds = kDionStages * 2 * kDmaTileBytes;
+    auto go = [&](auto kern) { launch_kernel(kern, grid, dim3(256), lds, st, g, splits, part, zero); };
+    const bool ack = a_k == 1, bck = b_k == 1;
+    if (ack && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true>);
+    else if (ack) go(dion_gemm_dma48_kernel<kDionStages, true, false>);
+    else if (bck) go(dion_gemm_dma48_kernel<kDionStages, false, true>);
+    else go(dion_gemm_dma48_kernel<kDionStages, false, false>);
+    if (splits > 1) {
+      const int64_t n = batch * M * N;
+      launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
+    }
+    return launch_status();
+  }
   const int splits = gemm_splits(M, N, K, batch);
   const dim3 grid((N + kDT - 1) / kDT, (M + kDT - 1) / kDT, batch * splits);
-  if (zero && dma_operand_ok(A, sA, a_i, a_k, M, K) && dma_operand_ok(B, sB, b_j, b_k, N, K)) {
+  if (dma) {
     const bool ack = a_k == 1, bck = b_k == 1;
     if (ack && bck) launch_dma<true, true>(g, grid, splits, part, zero, st);
     else if (ack) launch_dma<true, false>(g, grid, splits, part, zero, st);
