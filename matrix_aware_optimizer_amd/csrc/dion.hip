@@ -468,6 +468,116 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   }
 }
 
+// Both rank-r updates of one step in one pass over the m x n tiles:
+//   M <- M + alpha_m * P R^T   (error feedback, alpha_m = -(1 - mu))
+//   X <- X + alpha_x * P Q^T   (alpha_x = -eta)
+// P (m x r), R and Q (n x r) row-major, every operand k-contiguous.  A
+// workgroup stages P's, R's and Q's tiles side by side in the DMA ring (three
+// 8 KB tiles per stage), reads its tiles of M and X before the contraction,
+// and runs the two products from one P fragment each; each product, and
+// each output value, is computed as by dion_gemm_dma_kernel alone.
+struct DUpdate2 {
+  const float* P;
+  int64_t sP, ldp;
+  const float* R;
+  int64_t sR, ldr;
+  const float* Q;
+  int64_t sQ, ldq;
+  float* M;
+  int64_t sM, ldm;
+  float* X;
+  int64_t sX, ldx;
+  int64_t m, n, r;
+  float alpha_m, alpha_x;
+  float beta;   // 1: the addend's factor, a run-time value as in dion_gemm_dma_kernel, so that
+                // alpha * acc and its sum with the addend round as they do there
+};
+
+template <int S>
+__global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const float* zero) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int64_t b = blockIdx.z;
+  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+  const int half = lane >> 5, l32 = lane & 31;
+  const DmaOperand op{u.P + b * u.sP, u.ldp, 1, u.m, u.r};
+  const DmaOperand orr{u.R + b * u.sR, u.ldr, 1, u.n, u.r};
+  const DmaOperand oq{u.Q + b * u.sQ, u.ldq, 1, u.n, u.r};
+  const int nk = static_cast<int>((u.r + kDK - 1) / kDK);
+  const uint32_t lds0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
+  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
+  // stage s: P's tile, R's 8 KB after it, Q's after that (6 DMA instructions
+  // per wave)
+  auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
+    const int64_t k0 = kt * kDK;
+    const uint32_t sa = lds0 + stage * 3 * kDmaTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int slot0 = 64 * (2 * wave + i);
+      dion_dma16(op.chunk<true>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
+      dion_dma16(orr.chunk<true>(slot0 + lane, j0, k0, zero, zspread + 1), sa + kDmaTileBytes + 16 * slot0);
+      dion_dma16(oq.chunk<true>(slot0 + lane, j0, k0, zero, zspread + 2), sa + 2 * kDmaTileBytes + 16 * slot0);
+    }
+  };
+  f32x16_t am, ax;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) am[v] = ax[v] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  // the addends (this lane's entries of M and X) before the contraction
+  const int64_t col = j0 + wj + l32;
+  float* Mb = u.M + b * u.sM;
+  float* Xb = u.X + b * u.sX;
+  float zm[16], zx[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+    const bool in = row < u.m && col < u.n;
+    zm[v] = in ? Mb[row * u.ldm + col] : 0.0f;
+    zx[v] = in ? Xb[row * u.ldx + col] : 0.0f;
+  }
+  for (int it = 0; it < nk; ++it) {
+    if (it + S - 1 < nk) {
+      dion_wait_vm_barrier<6 * (S - 2)>();
+      issue((it + S - 1) % S, it + S - 1);
+    } else {
+      dion_wait_vm_barrier<0>();
+    }
+    const char* ta = dsm + (it % S) * 3 * kDmaTileBytes;
+    const char* tr = ta + kDmaTileBytes;
+    const char* tq = tr + kDmaTileBytes;
+#pragma unroll
+    for (int gk = 0; gk < 4; ++gk) {
+      const int c = 2 * gk + half;
+      const int ra = wi + l32, rb = wj + l32;
+      const float4 a = *reinterpret_cast<const float4*>(ta + ra * 128 + ((c ^ (ra & 7)) << 4));
+      const float4 br = *reinterpret_cast<const float4*>(tr + rb * 128 + ((c ^ (rb & 7)) << 4));
+      const float4 bq = *reinterpret_cast<const float4*>(tq + rb * 128 + ((c ^ (rb & 7)) << 4));
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, br.x, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, br.y, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, br.z, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, br.w, am, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bq.x, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bq.y, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bq.z, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every stage has landed
+  if (col < u.n) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (row >= u.m) continue;
+      Mb[row * u.ldm + col] = fmaf(u.beta, zm[v], u.alpha_m * am[v]);
+      Xb[row * u.ldx + col] = fmaf(u.beta, zx[v], u.alpha_x * ax[v]);
+    }
+  }
+}
+
 // the zero page the DMA kernel's tail chunks read (16 KB)
 __global__ __launch_bounds__(256) void zero_page_kernel(float* z) { z[blockIdx.x * 256 + threadIdx.x] = 0.0f; }
 
@@ -1144,9 +1254,17 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
     const int64_t m = run.m, n = run.n, b = run.count;
     status = dgemm(M, run.sM, 1, n, Pf, m * r, r, 1, nullptr, 0, 0, R, n * r, r, n, r, m, 1.0f, 0.0f, b, part, zp, st);
     if (status != MUON_OK) return status;
-    status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - C.mu), 1.0f, b,
-                   part, zp, st);
-    if (status != MUON_OK) return status;
+    // the two rank-r updates in one pass when their products would each run
+    // unsplit on the DMA kernel (the error feedback then waits for the column
+    // norms, on which it does not depend)
+    const bool both = zp != nullptr && !use48(n) && gemm_splits(m, n, r, b) == 1 &&
+                      dma_operand_ok(Pf, m * r, r, 1, m, r) && dma_operand_ok(R, n * r, r, 1, n, r) &&
+                      dma_operand_ok(Q, run.sQ, r, 1, n, r);
+    if (!both) {
+      status = dgemm(Pf, m * r, r, 1, R, n * r, 1, r, M, run.sM, n, M, run.sM, n, m, n, r, -(1.0f - C.mu), 1.0f, b,
+                     part, zp, st);
+      if (status != MUON_OK) return status;
+    }
     {
       // chunks of at least 64 rows and at most m chunks, so the partial sums
       // (b x chunks x r) fit in P's second buffer, free after the two passes
@@ -1158,8 +1276,16 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
                     rows_per, nch);
     }
     if ((status = launch_status()) != MUON_OK) return status;
-    status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -C.eta, 1.0f, b, part,
-                   zp, st);
+    if (both) {
+      const DUpdate2 u{Pf, m * r, r, R, n * r, r, Q, run.sQ, r, M, run.sM, n, X, run.sX, n, m, n, r,
+                       -(1.0f - C.mu), -C.eta, 1.0f};
+      launch_kernel(dion_update2_kernel<kDionStages>, dim3((n + kDT - 1) / kDT, (m + kDT - 1) / kDT, b), dim3(256),
+                    kDionStages * 3 * kDmaTileBytes, st, u, zp);
+      status = launch_status();
+    } else {
+      status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -C.eta, 1.0f, b, part,
+                     zp, st);
+    }
     if (status != MUON_OK) return status;
   }
   return MUON_OK;
