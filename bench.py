@@ -578,6 +578,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"]["other_workloads"] = cpu_baseline_configs()
     print(json.dumps(result), flush=True)
 
 
@@ -811,6 +812,68 @@ def _numpy_f32_step(wl, W0, M0, G, others):
     counts = np.unpackbits(buffers, axis=1, bitorder="little")[:, :wl.numel].sum(0, dtype=np.int32)
     vote = 2 * counts >= wl.workers
     return to32(W0, wl.w_dtype) - np.float32(wl.eta) * np.where(vote, np.float32(1), np.float32(-1))
+
+
+def _numpy_f32_set_step(wl, W0, M0, G):
+    """_numpy_f32_step over a set of matrices (each on its short side), for the
+    per-workload CPU timings."""
+    a, b, c = (np.float32(x) for x in wl.coeffs)
+    to32 = (lambda x, dt: (x.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else x)
+    Mn = np.float32(wl.beta) * to32(M0, wl.m_dtype) + np.float32(wl.alpha) * to32(G, wl.g_dtype)
+    U = np.empty_like(Mn)
+    offs = wl.offsets
+    for j, (rows, cols) in enumerate(wl.shapes):
+        X = Mn[offs[j]:offs[j + 1]].reshape(rows, cols)
+        X = np.ascontiguousarray((X.T if rows > cols else X) / np.float32(np.sqrt(np.sum(X.astype(np.float64) ** 2))))
+        for _ in range(wl.ns_steps):
+            A = X @ X.T
+            Bm = b * A + c * (A @ A)
+            X = a * X + Bm @ X
+        U[offs[j]:offs[j + 1]] = (X.T if rows > cols else X).ravel()
+    mine = np.packbits(~(U < 0), bitorder="little")
+    if W0 is None:
+        return mine
+    counts = np.unpackbits(np.stack([mine] * wl.workers), axis=1, bitorder="little")[:, :wl.numel].sum(0, dtype=np.int32)
+    vote = 2 * counts >= wl.workers
+    return to32(W0, wl.w_dtype) - np.float32(wl.eta) * np.where(vote, np.float32(1), np.float32(-1))
+
+
+def _oracle_set_step(wl, W0, M0, G):
+    """One worker step of the fp64 oracle over a workload's matrix set: momentum,
+    Newton-Schulz of every matrix, sign and packing, then (workloads with
+    weights) the vote over M copies of the worker's bits and the update."""
+    import oracle.muon_oracle as O
+    Mn = O.momentum(M0, wl.m_dtype, G, wl.g_dtype, wl.beta, wl.alpha)
+    U = O.worker_direction(Mn, wl.m_dtype, wl.shapes, wl.offsets, *wl.coeffs, wl.ns_steps)
+    words = O.sign_pack(U)
+    if W0 is not None:
+        O.apply_update(W0, wl.w_dtype, O.majority_vote(np.stack([words] * wl.workers), wl.numel), wl.eta)
+
+
+def cpu_baseline_configs(samples=((1, 1), (2, 4), (3, 4))):
+    """fp64 oracle and numpy fp32 worker steps on a bounded sample of the
+    smaller workloads: (workload, k) times one worker step over the set's first k
+    matrices (the GPT-2-small set's first layer, four of the 128 1024^2
+    matrices), each measured once, reported per orthogonalisation so that it
+    compares with the GPU's orthogonalisations per second on the whole set.  The
+    7168x18432 step takes minutes on the host and is not timed."""
+    import dataclasses
+    from workloads import WORKLOADS, gen_G, gen_M0, gen_W0
+    out = {}
+    for cfg, k in samples:
+        full = WORKLOADS[cfg]
+        wl = dataclasses.replace(full, shapes=full.shapes[:k])
+        W0, M0, G = gen_W0(wl), gen_M0(wl), gen_G(wl, 0, 0)
+        t0 = time.perf_counter()
+        _oracle_set_step(wl, W0, M0, G)
+        t_oracle = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        _numpy_f32_set_step(wl, W0, M0, G)
+        t_f32 = time.perf_counter() - t1
+        out[full.name] = {"sample": f"one worker step over the first {k} of the set's {len(full.shapes)} matrices",
+                          "oracle_seconds": t_oracle, "oracle_orthogonalizations_per_s": k / t_oracle,
+                          "numpy_f32_seconds": t_f32, "numpy_f32_orthogonalizations_per_s": k / t_f32}
+    return out
 
 
 def cpu_baseline(wl):
