@@ -754,17 +754,26 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
       }
     }
     __syncthreads();
-    // rows below: L(i, c0 + k) = sum_{m <= k} A(i, c0 + m) D(k, m)
-    for (int i = c0 + kCb + tid; i < rp; i += kCholThreads) {
-      float v[kCb];
+    // rows below: L(i, c0 + k) = sum_m A(i, c0 + m) D(k, m), the block row times
+    // D^T (the diagonal block of S holds D^T, zero above D's diagonal), on fp32
+    // matrix cores: wave w takes the 16-row blocks J + 1 + w, J + 1 + w + W,
+    // ...; lane l supplies A(16 ib + l % 16, c0 + 4 q + l / 16) and D^T(4 q +
+    // l / 16, l % 16) for pass q and holds rows 4 (l / 16) .. + 3 of column
+    // l % 16.  A wave reads its block row before it writes it.
+    {
+      const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+      for (int ib = J + 1 + wave; ib < nb; ib += kCholWaves) {
+        float a4[4], b4[4];
 #pragma unroll
-      for (int c = 0; c < kCb; ++c) v[c] = S[i * ld + c0 + c];
+        for (int q = 0; q < 4; ++q) {
+          a4[q] = S[(kCb * ib + li) * ld + c0 + 4 * q + lk];
+          b4[q] = S[(c0 + 4 * q + lk) * ld + c0 + li];
+        }
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < kCb; ++k) {
-        float o = 0.0f;
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m <= k; ++m) o = fmaf(v[m], S[(c0 + m) * ld + c0 + k], o);
-        S[i * ld + c0 + k] = o;
+        for (int v = 0; v < 4; ++v) S[(kCb * ib + 4 * lk + v) * ld + c0 + li] = acc[v];
       }
     }
     __syncthreads();
