@@ -267,7 +267,10 @@ constexpr int64_t kPackBlock = int64_t(kPackGroups) * kThreads * 8;   // entries
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sign_pack_kernel(const T* __restrict__ U, int64_t numel,
                                                             uint64_t* __restrict__ bits,
-                                                            int64_t nwords) {
+                                                            int64_t nwords, int64_t strideU, int64_t stride_bits) {
+  // grid y: equal problems strideU elements and stride_bits words apart
+  U += int64_t(blockIdx.y) * strideU;
+  bits += int64_t(blockIdx.y) * stride_bits;
   const int64_t base = int64_t(blockIdx.x) * kPackBlock + threadIdx.x * 8;
   uint32_t byte[kPackGroups];
   if (int64_t(blockIdx.x + 1) * kPackBlock <= numel) {
@@ -785,6 +788,33 @@ int scratch_address(double** out) {
 
 using namespace muon;
 
+namespace muon {
+// sign_pack of `count` problems of numel entries each, strideU entries and
+// stride_bits words apart, in one launch (a run of ns_orthogonalize whose
+// signs are packed after the iteration).  Each problem's words are its own:
+// a last partial word holds zeros past numel.  U and every problem's U
+// 16-byte aligned, bits 8-byte aligned; MUON_EALIGN otherwise.
+int sign_pack_runs(const void* U, int u_dtype, int64_t numel, int64_t count, int64_t strideU, uint64_t* bits,
+                   int64_t stride_bits, hipStream_t st) {
+  if (!numel_ok(numel) || count < 0 || count > 65535 || strideU < 0 || stride_bits < 0) return MUON_EINVAL;
+  if (!valid_dtype(u_dtype)) return MUON_EDTYPE;
+  if (numel == 0 || count == 0) return MUON_OK;
+  if (!U || !bits) return MUON_EINVAL;
+  if (!aligned16(U) || (strideU * int64_t(dtype_size(u_dtype))) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(bits) & 7u) != 0)
+    return MUON_EALIGN;
+  const int64_t nwords = (numel + 63) / 64;
+  const int64_t blocks = (numel + kPackBlock - 1) / kPackBlock;
+  if (u_dtype == MUON_BF16)
+    launch_kernel(sign_pack_kernel<bf16_t>, dim3(blocks, count), dim3(kThreads), 0, st,
+                  static_cast<const bf16_t*>(U), numel, bits, nwords, strideU, stride_bits);
+  else
+    launch_kernel(sign_pack_kernel<float>, dim3(blocks, count), dim3(kThreads), 0, st,
+                  static_cast<const float*>(U), numel, bits, nwords, strideU, stride_bits);
+  return launch_status();
+}
+}  // namespace muon
+
 extern "C" {
 
 size_t muon_momentum_workspace_bytes(int64_t numel, int nseg) {
@@ -853,12 +883,13 @@ int sign_pack(const void* U, int u_dtype, int64_t numel, uint64_t* bits, void* s
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (u_dtype == MUON_BF16)
     launch_kernel(sign_pack_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const bf16_t*>(U),
-                                                                      numel, bits, nwords);
+                                                                      numel, bits, nwords, 0, 0);
   else
     launch_kernel(sign_pack_kernel<float>, dim3(blocks), dim3(kThreads), 0, st, static_cast<const float*>(U),
-                                                                     numel, bits, nwords);
+                                                                     numel, bits, nwords, 0, 0);
   return launch_status();
 }
+
 
 int majority_vote(const uint64_t* bits, int M, int64_t nwords, uint64_t* out, void* stream) {
   if (nwords < 0 || nwords > MUON_MAX_NUMEL / 64 || M < 1 || M > MUON_MAX_VOTERS) return MUON_EINVAL;

@@ -31,6 +31,10 @@
 
 namespace muon {
 
+// one launch of sign_pack for evenly spaced equal problems (elementwise.hip)
+int sign_pack_runs(const void* U, int u_dtype, int64_t numel, int64_t count, int64_t strideU, uint64_t* bits,
+                   int64_t stride_bits, hipStream_t st);
+
 int sumsq_strided(const void* M, int m_dtype, int64_t len, int64_t count, int64_t stride, float* out,
                   void* partials, hipStream_t stream);
 
@@ -572,6 +576,9 @@ int pack_run_signs(const Run& r, hipStream_t st) {
   const int64_t n = r.rows * r.cols;
   if (r.count > 1 && r.strideU == n && n % 64 == 0 && r.stride_bits == n / 64)
     return sign_pack(r.U, r.u_dtype, n * r.count, r.bits, st);
+  // evenly spaced problems (a layer set's matrices of one shape): one launch
+  if (r.count > 1 && sign_pack_runs(r.U, r.u_dtype, n, r.count, r.strideU, r.bits, r.stride_bits, st) == MUON_OK)
+    return MUON_OK;
   for (int k = 0; k < r.count; ++k) {
     const int status = sign_pack(static_cast<const char*>(r.U) + k * r.strideU * es, r.u_dtype,
                                  r.rows * r.cols, r.bits + k * r.stride_bits, st);
