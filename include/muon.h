@@ -19,10 +19,12 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller; the
  *     library never allocates, frees or retains memory.  Between calls it
  *     keeps only per-device facts set once: each device's CU count, the
- *     dynamic LDS limits of its kernels (kernel attributes) and the address
- *     of its fixed 4 MiB scratch array (used by muon_momentum_noalloc only).  These are
- *     atomics, so host threads may call concurrently (on separate streams
- *     and buffers).  Scratch memory is passed in as `workspace`, sized by
+ *     dynamic LDS limits of its kernels (kernel attributes), the address of
+ *     its fixed 4 MiB scratch array (used by muon_momentum_noalloc only),
+ *     three streams of its own (used by ns_orthogonalize and dion_step, see
+ *     there) and each host thread's fork and join events.  These are set up
+ *     under atomics or a lock, so host threads may call concurrently (on
+ *     separate streams and buffers).  Scratch memory is passed in as `workspace`, sized by
  *     the matching *_workspace_bytes query.
  *   - Device pointers must be 16-byte aligned (MUON_EALIGN otherwise).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
