@@ -1195,7 +1195,8 @@ struct DionCall {
 //   1-3   first orthonormalisation pass: the Grams P^T P, their factorisation
 //         (one launch over the lane's nmat matrices from slot0), P <- P L^-T
 //   4-6   the second pass, back into P's first buffer
-//   7     R = B^T P, error feedback, Q = ColumnNormalize(R), X update
+//   7     R = B^T P, Q = ColumnNormalize(R), then the error feedback and the X
+//         update (one pass over the m x n tiles where both fit the DMA kernel)
 constexpr int kDionStagesPerCall = 8;
 
 int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float* part, int64_t slot0,
