@@ -203,6 +203,29 @@ __global__ __launch_bounds__(256) void dion_gemm_kernel(DGemm g, int splits, flo
 // after it means every wave's have; the last S - 1 iterations issue nothing
 // and wait for everything.
 // ---------------------------------------------------------------------------
+// Tile (x, y, z) of a DMA product's workgroup.  Workgroups go to the 8 XCDs
+// round-robin by their flat index (x fastest); the flat index is remapped so
+// that each XCD takes a contiguous range of tiles, and the tiles that share a
+// row panel of the left operand (consecutive x: B Q's rank-wide row at rank
+// 96 or 192) meet in one XCD's L2 instead of being read from memory by
+// several.
+#ifndef MUON_DION_XCD
+#define MUON_DION_XCD 1
+#endif
+struct DTile {
+  int64_t x, y, z;
+};
+__device__ __forceinline__ DTile dion_tile() {
+  const int64_t X = gridDim.x, Y = gridDim.y;
+  const int64_t n = X * Y * int64_t(gridDim.z);
+  int64_t t = blockIdx.x + X * (blockIdx.y + Y * int64_t(blockIdx.z));
+  if (MUON_DION_XCD) {
+    const int64_t full = n / 8 * 8;
+    if (t < full) t = (t % 8) * (full / 8) + t / 8;
+  }
+  return DTile{t % X, (t / X) % Y, t / (X * Y)};
+}
+
 constexpr int kDmaTileBytes = kDT * kDK * 4;   // one operand tile: 8 KB
 constexpr int kZeroPageFloats = 4096;          // the workspace's page of zeros: 16 KB
 
@@ -251,9 +274,10 @@ struct DmaOperand {
 template <int S, bool ACK, bool BCK, bool ZPRE>
 __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits, float* part, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  const int64_t b = blockIdx.z / splits;
-  const int sp = blockIdx.z % splits;
-  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
+  const DTile T = dion_tile();
+  const int64_t b = T.z / splits;
+  const int sp = static_cast<int>(T.z % splits);
+  const int64_t i0 = T.y * kDT, j0 = T.x * kDT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
   const int half = lane >> 5, l32 = lane & 31;
@@ -264,7 +288,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   const int nk = static_cast<int>(kt1 - kt0);
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
-  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
+  const int zspread = static_cast<int>((T.x + 3 * T.y + 5 * T.z) & 63);
   // stage s: A tile at s * 16 KB, B tile 8 KB after it
   auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
     const int64_t k0 = kt * kDK;
@@ -376,9 +400,10 @@ template <int S, bool ACK, bool BCK>
 __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int splits, float* part,
                                                               const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  const int64_t b = blockIdx.z / splits;
-  const int sp = blockIdx.z % splits;
-  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * 48;
+  const DTile T = dion_tile();
+  const int64_t b = T.z / splits;
+  const int sp = static_cast<int>(T.z % splits);
+  const int64_t i0 = T.y * kDT, j0 = T.x * 48;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q = lane >> 4;
   const int arow = 16 * wave + li;   // the tile row this lane supplies
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   const int nk = static_cast<int>(kt1 - kt0);
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
-  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
+  const int zspread = static_cast<int>((T.x + 3 * T.y + 5 * T.z) & 63);
   auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
     const int64_t k0 = kt * kDK;
     const uint32_t sa = lds0 + stage * 2 * kDmaTileBytes, sb = sa + kDmaTileBytes;
@@ -496,8 +521,9 @@ struct DUpdate2 {
 template <int S>
 __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  const int64_t b = blockIdx.z;
-  const int64_t i0 = int64_t(blockIdx.y) * kDT, j0 = int64_t(blockIdx.x) * kDT;
+  const DTile T = dion_tile();
+  const int64_t b = T.z;
+  const int64_t i0 = T.y * kDT, j0 = T.x * kDT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
   const int half = lane >> 5, l32 = lane & 31;
@@ -507,7 +533,7 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
   const int nk = static_cast<int>((u.r + kDK - 1) / kDK);
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
-  const int zspread = static_cast<int>((blockIdx.x + 3 * blockIdx.y + 5 * blockIdx.z) & 63);
+  const int zspread = static_cast<int>((T.x + 3 * T.y + 5 * T.z) & 63);
   // stage s: P's tile, R's 8 KB after it, Q's after that (6 DMA instructions
   // per wave)
   auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
