@@ -518,7 +518,7 @@ struct DUpdate2 {
                 // alpha * acc and its sum with the addend round as they do there
 };
 
-template <int S>
+template <int S, bool TAIL16>
 __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const DTile T = dion_tile();
@@ -565,18 +565,14 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     zm[v] = in ? Mb[row * u.ldm + col] : 0.0f;
     zx[v] = in ? Xb[row * u.ldx + col] : 0.0f;
   }
-  for (int it = 0; it < nk; ++it) {
-    if (it + S - 1 < nk) {
-      dion_wait_vm_barrier<6 * (S - 2)>();
-      issue((it + S - 1) % S, it + S - 1);
-    } else {
-      dion_wait_vm_barrier<0>();
-    }
+  // the products of k-tile `it` over its first G 8-deep groups
+  auto mma = [&](int it, auto groups) __attribute__((always_inline)) {
+    constexpr int G = decltype(groups)::value;
     const char* ta = dsm + (it % S) * 3 * kDmaTileBytes;
     const char* tr = ta + kDmaTileBytes;
     const char* tq = tr + kDmaTileBytes;
 #pragma unroll
-    for (int gk = 0; gk < 4; ++gk) {
+    for (int gk = 0; gk < G; ++gk) {
       const int c = 2 * gk + half;
       const int ra = wi + l32, rb = wj + l32;
       const float4 a = *reinterpret_cast<const float4*>(ta + ra * 128 + ((c ^ (ra & 7)) << 4));
@@ -590,6 +586,24 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bq.y, ax, 0, 0, 0);
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bq.z, ax, 0, 0, 0);
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
+    }
+  };
+  // TAIL16: the contraction ends 16 into its last k-tile (r = 48, 80, ...),
+  // whose last two 8-deep groups hold only the zero page's zeros
+  const int full = TAIL16 ? nk - 1 : nk;
+  for (int it = 0; it < full; ++it) {
+    if (it + S - 1 < nk) {
+      dion_wait_vm_barrier<6 * (S - 2)>();
+      issue((it + S - 1) % S, it + S - 1);
+    } else {
+      dion_wait_vm_barrier<0>();
+    }
+    mma(it, std::integral_constant<int, 4>{});
+  }
+  if constexpr (TAIL16) {
+    if (full >= 0) {
+      dion_wait_vm_barrier<0>();
+      mma(full, std::integral_constant<int, 2>{});
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every stage has landed
@@ -1315,8 +1329,10 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
     if (both) {
       const DUpdate2 u{Pf, m * r, r, R, n * r, r, Q, run.sQ, r, M, run.sM, n, X, run.sX, n, m, n, r,
                        -(1.0f - C.mu), -C.eta, 1.0f};
-      launch_kernel(dion_update2_kernel<kDionStages>, dim3((n + kDT - 1) / kDT, (m + kDT - 1) / kDT, b), dim3(256),
-                    kDionStages * 3 * kDmaTileBytes, st, u, zp);
+      const dim3 grid((n + kDT - 1) / kDT, (m + kDT - 1) / kDT, b);
+      const uint32_t lds = kDionStages * 3 * kDmaTileBytes;
+      if (r % kDK == 16) launch_kernel(dion_update2_kernel<kDionStages, true>, grid, dim3(256), lds, st, u, zp);
+      else launch_kernel(dion_update2_kernel<kDionStages, false>, grid, dim3(256), lds, st, u, zp);
       status = launch_status();
     } else {
       status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -C.eta, 1.0f, b, part,
