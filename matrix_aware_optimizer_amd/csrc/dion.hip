@@ -43,7 +43,19 @@ struct DGemm {
   int64_t sC, ldc;
   int64_t M, N, K;
   float alpha, beta;
+  // dion_gemm_dma48_kernel only: the left operand is A + A2 (each sum rounded
+  // once to fp32), A2 with A's element strides and batch stride sA2, and the
+  // sum is written to Aout (A's strides and batch stride), whose entries this
+  // product alone reads
+  const float* A2 = nullptr;
+  int64_t sA2 = 0;
+  float* Aout = nullptr;
 };
+
+// the exact sum of two fp32 values rounded once to fp32
+__device__ __forceinline__ float add_once(float a, float b) {
+  return static_cast<float>(static_cast<double>(a) + static_cast<double>(b));
+}
 
 constexpr int kDT = 64;        // output tile
 constexpr int kDK = 32;        // k per LDS tile
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
 // loaded, clamped at the edge, and not used).  In each 16-deep k group g,
 // k-slot q of product t (t = 0..3) is k = 16 g + 4 q + t, so a k-contiguous
 // lane's 16-byte read feeds four products.
-template <int S, bool ACK, bool BCK>
+template <int S, bool ACK, bool BCK, bool ADDA>
 __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int splits, float* part,
                                                               const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
@@ -409,6 +421,9 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   const int arow = 16 * wave + li;   // the tile row this lane supplies
   const DmaOperand oa{g.A + b * g.sA, g.a_i, g.a_k, g.M, g.K};
   const DmaOperand ob{g.B + b * g.sB, g.b_j, g.b_k, g.N, g.K};
+  // ADDA: A's second term, staged like A (a third tile per stage)
+  const DmaOperand oa2{ADDA ? g.A2 + b * g.sA2 : nullptr, g.a_i, g.a_k, g.M, g.K};
+  constexpr int kTiles = ADDA ? 3 : 2;
   const int64_t ktiles = (g.K + kDK - 1) / kDK;
   const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
   const int nk = static_cast<int>(kt1 - kt0);
@@ -417,14 +432,20 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   const int zspread = static_cast<int>((T.x + 3 * T.y + 5 * T.z) & 63);
   auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
     const int64_t k0 = kt * kDK;
-    const uint32_t sa = lds0 + stage * 2 * kDmaTileBytes, sb = sa + kDmaTileBytes;
+    const uint32_t sa = lds0 + stage * kTiles * kDmaTileBytes, sb = sa + kDmaTileBytes;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int slot0 = 64 * (2 * wave + i);
       dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
       dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, zspread + 1), sb + 16 * slot0);
+      if constexpr (ADDA)
+        dion_dma16(oa2.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread + 2), sb + kDmaTileBytes + 16 * slot0);
     }
   };
+  // ADDA: the lane that reads an entry of A + A2 (one lane per entry: a wave
+  // owns its 16 rows, and k-slot q reads chunk 4 g + q) writes it to Aout
+  float* aout = ADDA ? g.Aout + b * g.sA + (i0 + arow) * g.a_i : nullptr;
+  const bool arow_in = i0 + arow < g.M;
   f32x4_t acc[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -433,20 +454,29 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
     if (s < nk) issue(s, kt0 + s);
   for (int it = 0; it < nk; ++it) {
     if (it + S - 1 < nk) {
-      dion_wait_vm_barrier<4 * (S - 2)>();
+      dion_wait_vm_barrier<2 * kTiles * (S - 2)>();
       issue((it + S - 1) % S, kt0 + it + S - 1);
     } else {
       dion_wait_vm_barrier<0>();
     }
-    const char* ta = dsm + (it % S) * 2 * kDmaTileBytes;
+    const char* ta = dsm + (it % S) * kTiles * kDmaTileBytes;
     const char* tb = ta + kDmaTileBytes;
 #pragma unroll
     for (int gk = 0; gk < 2; ++gk) {
       float av[4];
       if constexpr (ACK) {
         const int c = 4 * gk + q;
-        const float4 v = *reinterpret_cast<const float4*>(ta + arow * 128 + ((c ^ (arow & 7)) << 4));
+        const int o = arow * 128 + ((c ^ (arow & 7)) << 4);
+        const float4 v = *reinterpret_cast<const float4*>(ta + o);
         av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+        if constexpr (ADDA) {
+          const float4 w = *reinterpret_cast<const float4*>(tb + kDmaTileBytes + o);
+          av[0] = add_once(av[0], w.x); av[1] = add_once(av[1], w.y);
+          av[2] = add_once(av[2], w.z); av[3] = add_once(av[3], w.w);
+          const int64_t k = (kt0 + it) * kDK + 4 * c;
+          if (arow_in && k < g.K)
+            *reinterpret_cast<float4*>(aout + k) = make_float4(av[0], av[1], av[2], av[3]);
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -934,9 +964,6 @@ __global__ __launch_bounds__(256) void colscale_kernel(const float* __restrict__
 // M[b] <- round_fp32(M[b] + G[b]) (the exact sum of two fp32 values rounded
 // once), len entries per matrix; 4 entries per thread when len and the batch
 // strides are multiples of 4 (the bases are 16-byte aligned)
-__device__ __forceinline__ float add_once(float a, float b) {
-  return static_cast<float>(static_cast<double>(a) + static_cast<double>(b));
-}
 
 __global__ __launch_bounds__(256) void add_kernel(float* __restrict__ M, int64_t sM,
                                                  const float* __restrict__ G, int64_t sG, int64_t len, int vec) {
@@ -1008,19 +1035,24 @@ void launch_dma(const DGemm& g, dim3 grid, int splits, float* part, const float*
 int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, int64_t sB, int64_t b_k,
           int64_t b_j, const float* Z, int64_t sZ, int64_t ldz, float* C, int64_t sC, int64_t ldc,
           int64_t M, int64_t N, int64_t K, float alpha, float beta, int64_t batch, float* part,
-          const float* zero, hipStream_t st) {
-  DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta};
+          const float* zero, hipStream_t st, const float* A2 = nullptr, int64_t sA2 = 0, float* Aout = nullptr) {
+  DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta, A2, sA2, Aout};
   const bool dma = zero && dma_operand_ok(A, sA, a_i, a_k, M, K) && dma_operand_ok(B, sB, b_j, b_k, N, K);
+  // A + A2 written back to Aout: one 48-wide column tile (every entry of A
+  // read by one workgroup) and a k-contiguous A
+  if (A2 && !(dma && N == 48 && a_k == 1 && Aout && dma_operand_ok(A2, sA2, a_i, a_k, M, K))) return MUON_EINVAL;
   if (dma && use48(N)) {
     const int splits = gemm_splits(M, N, K, batch, true);
     const dim3 grid(N / 48, (M + kDT - 1) / kDT, batch * splits);
-    const uint32_t lds = kDionStages * 2 * kDmaTileBytes;
+    const uint32_t lds = kDionStages * (A2 ? 3 : 2) * kDmaTileBytes;
     auto go = [&](auto kern) { launch_kernel(kern, grid, dim3(256), lds, st, g, splits, part, zero); };
     const bool ack = a_k == 1, bck = b_k == 1;
-    if (ack && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true>);
-    else if (ack) go(dion_gemm_dma48_kernel<kDionStages, true, false>);
-    else if (bck) go(dion_gemm_dma48_kernel<kDionStages, false, true>);
-    else go(dion_gemm_dma48_kernel<kDionStages, false, false>);
+    if (A2 && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true, true>);
+    else if (A2) go(dion_gemm_dma48_kernel<kDionStages, true, false, true>);
+    else if (ack && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true, false>);
+    else if (ack) go(dion_gemm_dma48_kernel<kDionStages, true, false, false>);
+    else if (bck) go(dion_gemm_dma48_kernel<kDionStages, false, true, false>);
+    else go(dion_gemm_dma48_kernel<kDionStages, false, false, false>);
     if (splits > 1) {
       const int64_t n = batch * M * N;
       launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
@@ -1255,14 +1287,22 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
       const DRun& run = (*C.runs)[k];
       const muon_dion_problem& p = (*C.sorted)[run.first];
       float* M = static_cast<float*>(p.M);
+      const float* G = static_cast<const float*>(p.G);
+      const float* Q = static_cast<const float*>(p.Q);
       const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
-      const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
-      const int64_t threads = vec ? mn / 4 : mn;
-      launch_kernel(add_kernel, dim3((threads + 255) / 256, b), dim3(256), 0, st, M, run.sM,
-                    static_cast<const float*>(p.G), run.sG, mn, vec);
-      if ((status = launch_status()) != MUON_OK) return status;
-      status = dgemm(M, run.sM, n, 1, static_cast<const float*>(p.Q), run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0),
-                     m * r, r, m, r, n, 1.0f, 0.0f, b, part, zp, st);
+      // rank 48: B = M + G formed by B Q as it stages M and G, and written back
+      // to M there, instead of by a pass of its own (one 48-wide column tile
+      // reads each entry of M once)
+      const bool fused = zp != nullptr && r == 48 && dma_operand_ok(M, run.sM, n, 1, m, n) &&
+                         dma_operand_ok(G, run.sG, n, 1, m, n) && dma_operand_ok(Q, run.sQ, 1, r, r, n);
+      if (!fused) {
+        const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;
+        const int64_t threads = vec ? mn / 4 : mn;
+        launch_kernel(add_kernel, dim3((threads + 255) / 256, b), dim3(256), 0, st, M, run.sM, G, run.sG, mn, vec);
+        if ((status = launch_status()) != MUON_OK) return status;
+      }
+      status = dgemm(M, run.sM, n, 1, Q, run.sQ, r, 1, nullptr, 0, 0, Pbuf(k, 0), m * r, r, m, r, n, 1.0f, 0.0f, b,
+                     part, zp, st, fused ? G : nullptr, run.sG, fused ? M : nullptr);
       if (status != MUON_OK) return status;
     }
     return MUON_OK;
