@@ -398,24 +398,27 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
   }
 }
 
-// A 64 x 48 output tile, for an output width N that is a multiple of 48 but
-// not of 64 (rank 48 or 96, where 64-wide tiles would compute a quarter or a
-// third of padding).  Wave w owns rows 16 w .. 16 w + 15 and all 48 columns
-// as three 16 x 16 blocks on v_mfma_f32_16x16x4f32: lane l supplies A(16 w +
-// l % 16, k) and B(k, 16 j + l % 16) for the product's k-slot l / 16 and
-// holds rows 4 (l / 16) .. + 3 of column l % 16.  Operands are staged as in
-// dion_gemm_dma_kernel (the B tile keeps 64 output indices: the last 16 are
-// loaded, clamped at the edge, and not used).  In each 16-deep k group g,
+// A 64 x 16 NB output tile on 16 x 16 blocks: NB = 3 for output widths that
+// are multiples of 48 but not of 64 (rank 48 or 96, where 64-wide tiles would
+// compute a quarter or a third of padding), and one tile as wide as the output
+// (NB = r / 16) for B Q with B = M + G formed in the product.  Wave w owns rows
+// 16 w .. 16 w + 15 and all 16 NB columns as NB blocks on
+// v_mfma_f32_16x16x4f32: lane l supplies A(16 w + l % 16, k) and B(k, 16 j +
+// l % 16) for the product's k-slot l / 16 and holds rows 4 (l / 16) .. + 3 of
+// column l % 16.  Operands are staged as in dion_gemm_dma_kernel, B as
+// ceil(16 NB / 64) tiles of 64 output indices (indices past the tile's width
+// are loaded, clamped at the edge, and not used).  In each 16-deep k group g,
 // k-slot q of product t (t = 0..3) is k = 16 g + 4 q + t, so a k-contiguous
 // lane's 16-byte read feeds four products.
-template <int S, bool ACK, bool BCK, bool ADDA>
+template <int S, int NB, bool ACK, bool BCK, bool ADDA>
 __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int splits, float* part,
                                                               const float* zero) {
+  constexpr int kW = 16 * NB, kSub = (kW + kDT - 1) / kDT;   // tile width, B tiles per stage
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const DTile T = dion_tile();
   const int64_t b = T.z / splits;
   const int sp = static_cast<int>(T.z % splits);
-  const int64_t i0 = T.y * kDT, j0 = T.x * 48;
+  const int64_t i0 = T.y * kDT, j0 = T.x * kW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q = lane >> 4;
   const int arow = 16 * wave + li;   // the tile row this lane supplies
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   const DmaOperand ob{g.B + b * g.sB, g.b_j, g.b_k, g.N, g.K};
   // ADDA: A's second term, staged like A (a third tile per stage)
   const DmaOperand oa2{ADDA ? g.A2 + b * g.sA2 : nullptr, g.a_i, g.a_k, g.M, g.K};
-  constexpr int kTiles = ADDA ? 3 : 2;
+  constexpr int kTiles = 1 + kSub + (ADDA ? 1 : 0);   // A, the B tiles, A2
   const int64_t ktiles = (g.K + kDK - 1) / kDK;
   const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
   const int nk = static_cast<int>(kt1 - kt0);
@@ -437,18 +440,21 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
     for (int i = 0; i < 2; ++i) {
       const int slot0 = 64 * (2 * wave + i);
       dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
-      dion_dma16(ob.chunk<BCK>(slot0 + lane, j0, k0, zero, zspread + 1), sb + 16 * slot0);
+#pragma unroll
+      for (int t = 0; t < kSub; ++t)
+        dion_dma16(ob.chunk<BCK>(slot0 + lane, j0 + kDT * t, k0, zero, zspread + 1 + t),
+                   sb + t * kDmaTileBytes + 16 * slot0);
       if constexpr (ADDA)
-        dion_dma16(oa2.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread + 2), sb + kDmaTileBytes + 16 * slot0);
+        dion_dma16(oa2.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread + 5), sb + kSub * kDmaTileBytes + 16 * slot0);
     }
   };
   // ADDA: the lane that reads an entry of A + A2 (one lane per entry: a wave
   // owns its 16 rows, and k-slot q reads chunk 4 g + q) writes it to Aout
   float* aout = ADDA ? g.Aout + b * g.sA + (i0 + arow) * g.a_i : nullptr;
   const bool arow_in = i0 + arow < g.M;
-  f32x4_t acc[3];
+  f32x4_t acc[NB];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s, kt0 + s);
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
         const float4 v = *reinterpret_cast<const float4*>(ta + o);
         av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
         if constexpr (ADDA) {
-          const float4 w = *reinterpret_cast<const float4*>(tb + kDmaTileBytes + o);
+          const float4 w = *reinterpret_cast<const float4*>(tb + kSub * kDmaTileBytes + o);
           av[0] = add_once(av[0], w.x); av[1] = add_once(av[1], w.y);
           av[2] = add_once(av[2], w.z); av[3] = add_once(av[3], w.w);
           const int64_t k = (kt0 + it) * kDK + 4 * c;
@@ -483,17 +489,18 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
           av[t] = *reinterpret_cast<const float*>(ta + ((16 * gk + 4 * q + t) * kDT + arow) * 4);
       }
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int bcol = 16 * j + li;
+      for (int j = 0; j < NB; ++j) {
+        const int bcol = (16 * j) % kDT + li;                     // index within its B tile
+        const char* tbj = tb + (16 * j / kDT) * kDmaTileBytes;   // the B tile holding block j
         float bv[4];
         if constexpr (BCK) {
           const int c = 4 * gk + q;
-          const float4 v = *reinterpret_cast<const float4*>(tb + bcol * 128 + ((c ^ (bcol & 7)) << 4));
+          const float4 v = *reinterpret_cast<const float4*>(tbj + bcol * 128 + ((c ^ (bcol & 7)) << 4));
           bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
         } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            bv[t] = *reinterpret_cast<const float*>(tb + ((16 * gk + 4 * q + t) * kDT + bcol) * 4);
+            bv[t] = *reinterpret_cast<const float*>(tbj + ((16 * gk + 4 * q + t) * kDT + bcol) * 4);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc[j], 0, 0, 0);
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   float* C = g.C + b * g.sC;
   const float* Z = g.Z ? g.Z + b * g.sZ : nullptr;
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < NB; ++j) {
     const int64_t col = j0 + 16 * j + li;
     if (col >= g.N) continue;
 #pragma unroll
@@ -989,6 +996,13 @@ __global__ __launch_bounds__(256) void add_kernel(float* __restrict__ M, int64_t
 // of 48 but not of 64, when the operands can be staged by DMA
 bool use48(int64_t N) { return N % 48 == 0 && N % kDT != 0; }
 
+// output widths one fused-add workgroup spans (16 x 16 blocks per wave row)
+bool fused_width(int64_t N) { return N == 48 || N == 64 || N == 96 || N == 128 || N == 192; }
+#ifndef MUON_DION_FUSED_ADD_MAX_RANK
+#define MUON_DION_FUSED_ADD_MAX_RANK 192
+#endif
+constexpr int kFusedAddMaxRank = MUON_DION_FUSED_ADD_MAX_RANK;   // ranks whose B Q forms B = M + G
+
 int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch, bool w48 = false) {
   const int64_t blocks = (w48 ? N / 48 : (N + kDT - 1) / kDT) * ((M + kDT - 1) / kDT) * batch;
   int64_t s = (1024 + blocks - 1) / blocks;
@@ -1038,21 +1052,48 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
           const float* zero, hipStream_t st, const float* A2 = nullptr, int64_t sA2 = 0, float* Aout = nullptr) {
   DGemm g{A, sA, a_i, a_k, B, sB, b_k, b_j, Z, sZ, ldz, C, sC, ldc, M, N, K, alpha, beta, A2, sA2, Aout};
   const bool dma = zero && dma_operand_ok(A, sA, a_i, a_k, M, K) && dma_operand_ok(B, sB, b_j, b_k, N, K);
-  // A + A2 written back to Aout: one 48-wide column tile (every entry of A
-  // read by one workgroup) and a k-contiguous A
-  if (A2 && !(dma && N == 48 && a_k == 1 && Aout && dma_operand_ok(A2, sA2, a_i, a_k, M, K))) return MUON_EINVAL;
+  // A + A2 written back to Aout: one column tile as wide as the output (every
+  // entry of A read by one workgroup) and a k-contiguous A
+  if (A2 && !(dma && fused_width(N) && a_k == 1 && Aout && dma_operand_ok(A2, sA2, a_i, a_k, M, K)))
+    return MUON_EINVAL;
+  if (A2) {
+    // ranges per product as for 64-wide tiles, so that the split-k buffer
+    // sized for those holds these
+    const int splits = N == 48 ? gemm_splits(M, N, K, batch, true) : gemm_splits(M, N, K, batch);
+    const dim3 grid(1, (M + kDT - 1) / kDT, batch * splits);
+    const bool bck = b_k == 1;
+    auto go = [&](auto kern, int nb) {
+      const uint32_t lds = kDionStages * (2 + (16 * nb + kDT - 1) / kDT) * kDmaTileBytes;
+      launch_kernel(kern, grid, dim3(256), lds, st, g, splits, part, zero);
+    };
+    switch (N) {
+      case 48: bck ? go(dion_gemm_dma48_kernel<kDionStages, 3, true, true, true>, 3)
+                   : go(dion_gemm_dma48_kernel<kDionStages, 3, true, false, true>, 3); break;
+      case 64: bck ? go(dion_gemm_dma48_kernel<kDionStages, 4, true, true, true>, 4)
+                   : go(dion_gemm_dma48_kernel<kDionStages, 4, true, false, true>, 4); break;
+      case 96: bck ? go(dion_gemm_dma48_kernel<kDionStages, 6, true, true, true>, 6)
+                   : go(dion_gemm_dma48_kernel<kDionStages, 6, true, false, true>, 6); break;
+      case 128: bck ? go(dion_gemm_dma48_kernel<kDionStages, 8, true, true, true>, 8)
+                    : go(dion_gemm_dma48_kernel<kDionStages, 8, true, false, true>, 8); break;
+      default: bck ? go(dion_gemm_dma48_kernel<kDionStages, 12, true, true, true>, 12)
+                   : go(dion_gemm_dma48_kernel<kDionStages, 12, true, false, true>, 12); break;
+    }
+    if (splits > 1) {
+      const int64_t n = batch * M * N;
+      launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
+    }
+    return launch_status();
+  }
   if (dma && use48(N)) {
     const int splits = gemm_splits(M, N, K, batch, true);
     const dim3 grid(N / 48, (M + kDT - 1) / kDT, batch * splits);
-    const uint32_t lds = kDionStages * (A2 ? 3 : 2) * kDmaTileBytes;
+    const uint32_t lds = kDionStages * 2 * kDmaTileBytes;
     auto go = [&](auto kern) { launch_kernel(kern, grid, dim3(256), lds, st, g, splits, part, zero); };
     const bool ack = a_k == 1, bck = b_k == 1;
-    if (A2 && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true, true>);
-    else if (A2) go(dion_gemm_dma48_kernel<kDionStages, true, false, true>);
-    else if (ack && bck) go(dion_gemm_dma48_kernel<kDionStages, true, true, false>);
-    else if (ack) go(dion_gemm_dma48_kernel<kDionStages, true, false, false>);
-    else if (bck) go(dion_gemm_dma48_kernel<kDionStages, false, true, false>);
-    else go(dion_gemm_dma48_kernel<kDionStages, false, false, false>);
+    if (ack && bck) go(dion_gemm_dma48_kernel<kDionStages, 3, true, true, false>);
+    else if (ack) go(dion_gemm_dma48_kernel<kDionStages, 3, true, false, false>);
+    else if (bck) go(dion_gemm_dma48_kernel<kDionStages, 3, false, true, false>);
+    else go(dion_gemm_dma48_kernel<kDionStages, 3, false, false, false>);
     if (splits > 1) {
       const int64_t n = batch * M * N;
       launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
@@ -1290,10 +1331,11 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
       const float* G = static_cast<const float*>(p.G);
       const float* Q = static_cast<const float*>(p.Q);
       const int64_t m = run.m, n = run.n, b = run.count, mn = m * n;
-      // rank 48: B = M + G formed by B Q as it stages M and G, and written back
-      // to M there, instead of by a pass of its own (one 48-wide column tile
-      // reads each entry of M once)
-      const bool fused = zp != nullptr && r == 48 && dma_operand_ok(M, run.sM, n, 1, m, n) &&
+      // B = M + G formed by B Q as it stages M and G, and written back to M
+      // there, instead of by a pass of its own (one column tile as wide as the
+      // rank reads each entry of M once)
+      const bool fused = zp != nullptr && fused_width(r) && r <= kFusedAddMaxRank &&
+                         dma_operand_ok(M, run.sM, n, 1, m, n) &&
                          dma_operand_ok(G, run.sG, n, 1, m, n) && dma_operand_ok(Q, run.sQ, 1, r, r, n);
       if (!fused) {
         const int vec = mn % 4 == 0 && run.sM % 4 == 0 && run.sG % 4 == 0;

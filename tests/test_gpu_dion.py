@@ -42,6 +42,7 @@ def run_single(M0, G, X0, Q0, rank, mu, eta):
 
 @pytest.mark.parametrize("m,n,r", [(100, 70, 1), (100, 70, 5), (64, 64, 64), (300, 130, 48), (130, 300, 48),
                                    (768, 768, 192), (96, 1000, 17),
+                                   (200, 324, 96), (140, 260, 128),   # B = M + G in B Q: ragged rows, k tail
                                    (37, 91, 6),      # m n odd: element-wise B = M + G; rows of Q not 16-byte multiples
                                    (8, 5000, 4)])    # n >> m: the column-norm chunks number exactly m
 def test_dion_single_matrix(m, n, r):
