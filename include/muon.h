@@ -441,8 +441,12 @@ int apply_update_dense(void* W, int w_dtype, int64_t numel, const void* U, int u
  *     Q = ColumnNormalize(R)         (zero columns stay zero)
  *     X = X - eta P Q^T
  * orth: Cholesky-QR applied twice; a column whose residual is at most 1e-4
- * of its own norm counts as dependent and becomes zero.  The page does not
- * spell out the orthonormalisation; this is the thin QR factor.
+ * of its own norm counts as dependent and becomes zero, and so does every
+ * column after the first min(m, n) independent ones (B Q has rank at most
+ * min(m, n); an fp32 Gram cannot resolve a dependent column's residual below
+ * about sqrt(2^-24) = 2.4e-4 of its norm, so a rank above a side relies on
+ * this bound).  The
+ * page does not spell out the orthonormalisation; this is the thin QR factor.
  *
  * problem    M, G, X device fp32 m x n (M, X updated in place, G read);
  *            Q device fp32 n x rank (read as Q_{t-1}, written as Q_t).

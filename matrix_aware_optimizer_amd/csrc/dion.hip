@@ -15,7 +15,9 @@
 // P^T P is factored L L^T in LDS by one workgroup per matrix, L is inverted
 // in place, and P <- P L^-T; the second pass restores orthogonality lost to
 // fp32 rounding.  A column whose Gram-Schmidt residual (the Cholesky pivot)
-// is at most 1e-4 of its own norm counts as dependent and is zeroed.
+// is at most 1e-4 of its own norm counts as dependent and is zeroed, and so
+// is every column after the first min(m, n) independent ones (the rank bound
+// of B Q, which the fp32 Gram's rounding could not show at that tolerance).
 #include <algorithm>
 #include <vector>
 
@@ -676,7 +678,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const 
 // Linv[b] = L^-1 with G[b] = L L^T (r x r, lower triangle of G read).  One
 // workgroup per matrix, on 16 x 16 blocks in LDS (size padded to a multiple
 // of 16 with an identity block; row pitch rp + 1).  Dependent columns
-// (pivot^2 <= tol^2 * G_jj, G_jj the diagonal of G) get a zero column in L;
+// (pivot^2 <= tol^2 * G_jj, G_jj the diagonal of G, or a real column after
+// the first cap independent ones) get a zero column in L;
 // L^-1 is then the inverse over the independent indices, with zero rows and
 // columns at the dependent ones.
 //
@@ -701,7 +704,7 @@ __device__ __forceinline__ float from_lane(float v, int lane) {
 constexpr int kCholThreads = MUON_CHOL_THREADS;   // threads of the factorisation's workgroup
 constexpr int kCholWaves = kCholThreads / 64;
 __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __restrict__ G, int64_t sG,
-                                                      float* __restrict__ Linv, int64_t sL, int r) {
+                                                      float* __restrict__ Linv, int64_t sL, int r, int cap) {
   extern __shared__ float sm[];
   const int nb = (r + kCb - 1) / kCb, rp = nb * kCb, ld = rp + 1;
   float* S = sm;                 // rp x ld
@@ -760,6 +763,7 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
   __syncthreads();
   for (int i = tid; i < rp; i += kCholThreads) g0[i] = S[i * ld + i];   // read before the first factorisation
 
+  int kept = 0;   // the factoring wave's count of independent columns so far
   for (int J = 0; J < nb; ++J) {
     const int c0 = J * kCb;
     if (J > 0) {
@@ -802,7 +806,10 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
 #pragma unroll
       for (int k = 0; k < kCb; ++k) {
         const float d = from_lane(a[k], k);
-        const float piv = (d > 0.0f && d > kDependentTol * kDependentTol * from_lane(g, k)) ? sqrtf(d) : 0.0f;
+        const bool room = c0 + k >= r || kept < cap;   // a real column past the rank bound is dependent
+        const float piv =
+            (room && d > 0.0f && d > kDependentTol * kDependentTol * from_lane(g, k)) ? sqrtf(d) : 0.0f;
+        kept += piv > 0.0f ? 1 : 0;
         const float inv = piv > 0.0f ? 1.0f / piv : 0.0f;
         if (lane == k) {
           a[k] = piv;
@@ -1360,10 +1367,22 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
         if (status != MUON_OK) return status;
       }
     } else if (step == 1) {
-      if (nmat > 0) {
+      // P = B Q has rank at most min(m, n): a run whose side is below the rank
+      // factors on its own with that bound, the others in one launch
+      bool bounded = false;
+      for (int k : ids) bounded = bounded || std::min((*C.runs)[k].m, (*C.runs)[k].n) < r;
+      if (!bounded && nmat > 0) {
         launch_kernel(chol_inv_kernel, dim3(nmat), dim3(kCholThreads), C.chol_lds, st, Gm + slot0 * r * r, r * r,
-                      Li + slot0 * r * r, r * r, C.rank);
+                      Li + slot0 * r * r, r * r, C.rank, C.rank);
         status = launch_status();
+      }
+      for (int k : ids) {
+        if (!bounded) break;
+        const DRun& run = (*C.runs)[k];
+        const int cap = static_cast<int>(std::min<int64_t>({run.m, run.n, r}));
+        launch_kernel(chol_inv_kernel, dim3(run.count), dim3(kCholThreads), C.chol_lds, st, Gm + L.slot[k] * r * r,
+                      r * r, Li + L.slot[k] * r * r, r * r, C.rank, cap);
+        if ((status = launch_status()) != MUON_OK) return status;
       }
     } else {
       for (int k : ids) {

@@ -43,6 +43,7 @@ def run_single(M0, G, X0, Q0, rank, mu, eta):
 @pytest.mark.parametrize("m,n,r", [(100, 70, 1), (100, 70, 5), (64, 64, 64), (300, 130, 48), (130, 300, 48),
                                    (768, 768, 192), (96, 1000, 17),
                                    (200, 324, 96), (140, 260, 128),   # B = M + G in B Q: ragged rows, k tail
+                                   (70, 260, 128), (200, 60, 96),    # rank above a side: P of rank min(m, n)
                                    (37, 91, 6),      # m n odd: element-wise B = M + G; rows of Q not 16-byte multiples
                                    (8, 5000, 4)])    # n >> m: the column-norm chunks number exactly m
 def test_dion_single_matrix(m, n, r):
@@ -52,8 +53,11 @@ def test_dion_single_matrix(m, n, r):
     Q0 = random_matrix((n, r), [603, r]).astype(np.float32)
     out = run_single(M0, G, X0, Q0, r, 0.95, 0.02)
     check_against_oracle(M0, G, X0, Q0, out, 0.95, 0.02)
-    # the new right factor has unit columns
-    assert np.allclose(np.linalg.norm(out[1].astype(np.float64), axis=0), 1.0, atol=1e-5)
+    # the new right factor has unit columns, min(m, n, r) of them (the rest zero:
+    # B Q has rank at most min(m, n))
+    nrm = np.linalg.norm(out[1].astype(np.float64), axis=0)
+    unit = np.isclose(nrm, 1.0, atol=1e-5)
+    assert np.all(unit | (nrm == 0.0)) and unit.sum() == min(m, n, r)
 
 
 def test_dion_closed_form_rank_r():
