@@ -674,6 +674,28 @@ __global__ __launch_bounds__(256) void reduce_kernel(DGemm g, int splits, const 
   g.C[b * g.sC + i * g.ldc + j] = v;
 }
 
+// reduce_kernel on four consecutive entries of a row per thread (N, the
+// leading dimensions and batch strides multiples of 4, 16-byte aligned bases):
+// each entry summed and scaled as there
+__global__ __launch_bounds__(256) void reduce4_kernel(DGemm g, int splits, const float* __restrict__ part,
+                                                     int64_t batch) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per = g.M * g.N;
+  if (4 * t >= batch * per) return;
+  const int64_t b = 4 * t / per, e = 4 * t % per, i = e / g.N, j = e % g.N;
+  float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < splits; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t(s) * batch + b) * per + e);
+    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+  }
+  float4 o = make_float4(g.alpha * sum.x, g.alpha * sum.y, g.alpha * sum.z, g.alpha * sum.w);
+  if (g.beta != 0.0f) {
+    const float4 z = *reinterpret_cast<const float4*>(g.Z + b * g.sZ + i * g.ldz + j);
+    o = make_float4(fmaf(g.beta, z.x, o.x), fmaf(g.beta, z.y, o.y), fmaf(g.beta, z.z, o.z), fmaf(g.beta, z.w, o.w));
+  }
+  *reinterpret_cast<float4*>(g.C + b * g.sC + i * g.ldc + j) = o;
+}
+
 // ---------------------------------------------------------------------------
 // Linv[b] = L^-1 with G[b] = L L^T (r x r, lower triangle of G read).  One
 // workgroup per matrix, on 16 x 16 blocks in LDS (size padded to a multiple
@@ -917,29 +939,40 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
 // Q[b] = R[b] with every column divided by its norm (zero columns stay zero);
 // R and Q row-major n x r.  Two passes over chunks of `rows_per` rows, one
 // workgroup per (chunk, matrix): colsq_kernel writes each chunk's column sums
-// of squares (thread c owns column c, four interleaved partial sums), and
+// of squares (four interleaved partial sums per column: sum k takes the rows
+// i0 + k, i0 + k + 4, ... of the chunk's whole groups of four, sum 0 also the
+// rows after them; the chunk's sum is (s0 + s1) + (s2 + s3)), and
 // colscale_kernel adds the chunks' sums in chunk order -- the same order in
 // every workgroup -- and scales its chunk.
 __global__ __launch_bounds__(256) void colsq_kernel(const float* __restrict__ R, int64_t sR,
                                                    float* __restrict__ part, int64_t n, int r,
                                                    int64_t rows_per, int64_t nch) {
+  __shared__ float sums[4][kDionMaxRank];
   const int64_t b = blockIdx.y, ch = blockIdx.x;
   const int64_t i0 = ch * rows_per, i1 = min(n, i0 + rows_per);
+  const int64_t whole = i0 + (i1 - i0) / 4 * 4;   // end of the whole groups of four rows
   const float* Rb = R + b * sR;
-  for (int c = threadIdx.x; c < r; c += 256) {
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    int64_t i = i0;
-    for (; i + 4 <= i1; i += 4) {
-      const float v0 = Rb[i * r + c], v1 = Rb[(i + 1) * r + c];
-      const float v2 = Rb[(i + 2) * r + c], v3 = Rb[(i + 3) * r + c];
-      s0 = fmaf(v0, v0, s0);
-      s1 = fmaf(v1, v1, s1);
-      s2 = fmaf(v2, v2, s2);
-      s3 = fmaf(v3, v3, s3);
+  // thread (k, c), k = e / r: partial sum k of column c (4 r threads' work)
+  for (int e = threadIdx.x; e < 4 * r; e += 256) {
+    const int k = e / r, c = e % r;
+    float acc = 0.0f;
+    int64_t i = i0 + k;
+    for (; i + 12 < whole; i += 16) {   // four rows of this sum in flight
+      const float v0 = Rb[i * r + c], v1 = Rb[(i + 4) * r + c];
+      const float v2 = Rb[(i + 8) * r + c], v3 = Rb[(i + 12) * r + c];
+      acc = fmaf(v0, v0, acc);
+      acc = fmaf(v1, v1, acc);
+      acc = fmaf(v2, v2, acc);
+      acc = fmaf(v3, v3, acc);
     }
-    for (; i < i1; ++i) s0 = fmaf(Rb[i * r + c], Rb[i * r + c], s0);
-    part[(b * nch + ch) * r + c] = (s0 + s1) + (s2 + s3);
+    for (; i < whole; i += 4) acc = fmaf(Rb[i * r + c], Rb[i * r + c], acc);
+    if (k == 0)
+      for (i = whole; i < i1; ++i) acc = fmaf(Rb[i * r + c], Rb[i * r + c], acc);
+    sums[k][c] = acc;
   }
+  __syncthreads();
+  for (int c = threadIdx.x; c < r; c += 256)
+    part[(b * nch + ch) * r + c] = (sums[0][c] + sums[1][c]) + (sums[2][c] + sums[3][c]);
 }
 
 __global__ __launch_bounds__(256) void colscale_kernel(const float* __restrict__ R, int64_t sR,
@@ -949,8 +982,18 @@ __global__ __launch_bounds__(256) void colscale_kernel(const float* __restrict__
   __shared__ float inv[kDionMaxRank];
   const int64_t b = blockIdx.y, ch = blockIdx.x;
   for (int c = threadIdx.x; c < r; c += 256) {
+    // the chunks' sums added in chunk order, eight loads in flight at a time
     float t = 0.0f;
-    for (int64_t q = 0; q < nch; ++q) t += part[(b * nch + q) * r + c];
+    const float* pc = part + b * nch * r + c;
+    int64_t q = 0;
+    for (; q + 8 <= nch; q += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pc[(q + u) * r];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += v[u];
+    }
+    for (; q < nch; ++q) t += pc[q * r];
     const float nrm = sqrtf(t);
     inv[c] = nrm > 0.0f ? 1.0f / nrm : 0.0f;
   }
@@ -1051,6 +1094,17 @@ void launch_dma(const DGemm& g, dim3 grid, int splits, float* part, const float*
   launch_kernel(dion_gemm_dma_kernel<kDionStages, ACK, BCK, false>, grid, dim3(256), lds, st, g, splits, part, zero);
 }
 
+// the sum of a product's k ranges (part: splits x batch x M x N)
+void launch_reduce(const DGemm& g, int splits, const float* part, int64_t batch, hipStream_t st) {
+  const int64_t n = batch * g.M * g.N;
+  const bool vec = g.N % 4 == 0 && g.ldc % 4 == 0 && g.sC % 4 == 0 && aligned16(g.C) && aligned16(part) &&
+                   (g.beta == 0.0f || (g.ldz % 4 == 0 && g.sZ % 4 == 0 && aligned16(g.Z)));
+  if (vec)
+    launch_kernel(reduce4_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
+  else
+    launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
+}
+
 // zero: the workspace's zero page (NULL keeps every product on the
 // register-staged kernel)
 int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, int64_t sB, int64_t b_k,
@@ -1085,10 +1139,7 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
       default: bck ? go(dion_gemm_dma48_kernel<kDionStages, 12, true, true, true>, 12)
                    : go(dion_gemm_dma48_kernel<kDionStages, 12, true, false, true>, 12); break;
     }
-    if (splits > 1) {
-      const int64_t n = batch * M * N;
-      launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
-    }
+    if (splits > 1) launch_reduce(g, splits, part, batch, st);
     return launch_status();
   }
   if (dma && use48(N)) {
@@ -1101,10 +1152,7 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
     else if (ack) go(dion_gemm_dma48_kernel<kDionStages, 3, true, false, false>);
     else if (bck) go(dion_gemm_dma48_kernel<kDionStages, 3, false, true, false>);
     else go(dion_gemm_dma48_kernel<kDionStages, 3, false, false, false>);
-    if (splits > 1) {
-      const int64_t n = batch * M * N;
-      launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
-    }
+    if (splits > 1) launch_reduce(g, splits, part, batch, st);
     return launch_status();
   }
   const int splits = gemm_splits(M, N, K, batch);
@@ -1124,10 +1172,7 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
     const int a_vec = vec_ok(A, sA, a_i, a_k), b_vec = vec_ok(B, sB, b_k, b_j);
     launch_kernel(dion_gemm_kernel, grid, dim3(256), 0, st, g, splits, part, a_vec, b_vec);
   }
-  if (splits > 1) {
-    const int64_t n = batch * M * N;
-    launch_kernel(reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, g, splits, part, batch);
-  }
+  if (splits > 1) launch_reduce(g, splits, part, batch, st);
   return launch_status();
 }
 
