@@ -283,6 +283,17 @@ struct DmaOperand {
     // land on the same few cache lines
     return k < K ? base + o * s_out + k * s_k : zero + 4 * ((p + 67 * zspread) & (kZeroPageFloats / 4 - 1));
   }
+  // a half tile of a k-contiguous operand: 16 k-values (64 bytes) per output
+  // index, chunk c of index o at slot c ^ ((o + o / 4) % 4), so that the eight
+  // rows one 16-byte read phase touches fall in distinct banks
+  __device__ __forceinline__ const float* chunk16(int p, int64_t o0, int64_t k0, const float* zero,
+                                                  int zspread) const {
+    const int row = p >> 2, c = (p & 3) ^ ((row + (row >> 2)) & 3);
+    int64_t o = o0 + row;
+    if (o >= n_out) o = n_out - 1;
+    const int64_t k = k0 + 4 * c;
+    return k < K ? base + o * s_out + k * s_k : zero + 4 * ((p + 67 * zspread) & (kZeroPageFloats / 4 - 1));
+  }
 };
 
 template <int S, bool ACK, bool BCK, bool ZPRE>
@@ -557,7 +568,11 @@ struct DUpdate2 {
                 // alpha * acc and its sum with the addend round as they do there
 };
 
-template <int S, bool TAIL16>
+// HALF (r = 16 or 48: one whole k-tile at most, then the 16-deep tail): the
+// whole tile in one 24 KB stage and the tail in a 12 KB half stage of 64-byte
+// rows, both issued at once; 36 KB of LDS, so four workgroups share a CU.
+// The addends are read once the whole tile has landed, under its products.
+template <int S, bool TAIL16, bool HALF>
 __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const DTile T = dion_tile();
@@ -586,23 +601,43 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
       dion_dma16(oq.chunk<true>(slot0 + lane, j0, k0, zero, zspread + 2), sa + 2 * kDmaTileBytes + 16 * slot0);
     }
   };
+  constexpr int kHalfBytes = kDmaTileBytes / 2;
+  // the half stage after the whole one: P's, R's and Q's 4 KB (3 DMA
+  // instructions per wave)
+  auto issue_half = [&](int64_t kt) __attribute__((always_inline)) {
+    const int64_t k0 = kt * kDK;
+    const uint32_t sa = lds0 + 3 * kDmaTileBytes + 16 * 64 * wave;
+    dion_dma16(op.chunk16(64 * wave + lane, i0, k0, zero, zspread), sa);
+    dion_dma16(orr.chunk16(64 * wave + lane, j0, k0, zero, zspread + 1), sa + kHalfBytes);
+    dion_dma16(oq.chunk16(64 * wave + lane, j0, k0, zero, zspread + 2), sa + 2 * kHalfBytes);
+  };
   f32x16_t am, ax;
 #pragma unroll
   for (int v = 0; v < 16; ++v) am[v] = ax[v] = 0.0f;
+  if constexpr (HALF) {
+    if (nk == 2) issue(0, 0);
+    issue_half(nk - 1);
+    if (nk == 2) dion_wait_vm_barrier<3>();   // the whole tile has landed; the half stage may be in flight
+  } else {
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s);
-  // the addends (this lane's entries of M and X) before the contraction
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s, s);
+  }
+  // the addends (this lane's entries of M and X), read before the products
   const int64_t col = j0 + wj + l32;
   float* Mb = u.M + b * u.sM;
   float* Xb = u.X + b * u.sX;
   float zm[16], zx[16];
+  // this lane's first row of M and X; its other rows at uniform offsets
+  const int64_t row0 = i0 + wi + 4 * half;
+  const float* mrow = Mb + row0 * u.ldm + col;
+  const float* xrow = Xb + row0 * u.ldx + col;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
-    const bool in = row < u.m && col < u.n;
-    zm[v] = in ? Mb[row * u.ldm + col] : 0.0f;
-    zx[v] = in ? Xb[row * u.ldx + col] : 0.0f;
+    const int dr = 8 * (v >> 2) + (v & 3);
+    const bool in = row0 + dr < u.m && col < u.n;
+    zm[v] = in ? mrow[dr * u.ldm] : 0.0f;
+    zx[v] = in ? xrow[dr * u.ldx] : 0.0f;
   }
   // the products of k-tile `it` over its first G 8-deep groups
   auto mma = [&](int it, auto groups) __attribute__((always_inline)) {
@@ -627,9 +662,32 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
     }
   };
+  if constexpr (HALF) {
+    if (nk == 2) mma(0, std::integral_constant<int, 4>{});
+    dion_wait_vm_barrier<0>();
+    const char* ta = dsm + 3 * kDmaTileBytes;
+    const char* tr = ta + kHalfBytes;
+    const char* tq = tr + kHalfBytes;
+    const int ra = wi + l32, rb = wj + l32;
+#pragma unroll
+    for (int gk = 0; gk < 2; ++gk) {
+      const int c = 2 * gk + half;
+      const float4 a = *reinterpret_cast<const float4*>(ta + ra * 64 + ((c ^ ((ra + (ra >> 2)) & 3)) << 4));
+      const float4 br = *reinterpret_cast<const float4*>(tr + rb * 64 + ((c ^ ((rb + (rb >> 2)) & 3)) << 4));
+      const float4 bq = *reinterpret_cast<const float4*>(tq + rb * 64 + ((c ^ ((rb + (rb >> 2)) & 3)) << 4));
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, br.x, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, br.y, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, br.z, am, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, br.w, am, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bq.x, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bq.y, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bq.z, ax, 0, 0, 0);
+      ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
+    }
+  }
   // TAIL16: the contraction ends 16 into its last k-tile (r = 48, 80, ...),
   // whose last two 8-deep groups hold only the zero page's zeros
-  const int full = TAIL16 ? nk - 1 : nk;
+  const int full = HALF ? 0 : TAIL16 ? nk - 1 : nk;
   for (int it = 0; it < full; ++it) {
     if (it + S - 1 < nk) {
       dion_wait_vm_barrier<6 * (S - 2)>();
@@ -639,7 +697,7 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     }
     mma(it, std::integral_constant<int, 4>{});
   }
-  if constexpr (TAIL16) {
+  if constexpr (TAIL16 && !HALF) {
     if (full >= 0) {
       dion_wait_vm_barrier<0>();
       mma(full, std::integral_constant<int, 2>{});
@@ -647,12 +705,14 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every stage has landed
   if (col < u.n) {
+    float* mw = Mb + row0 * u.ldm + col;
+    float* xw = Xb + row0 * u.ldx + col;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t row = i0 + wi + 8 * (v >> 2) + 4 * half + (v & 3);
-      if (row >= u.m) continue;
-      Mb[row * u.ldm + col] = fmaf(u.beta, zm[v], u.alpha_m * am[v]);
-      Xb[row * u.ldx + col] = fmaf(u.beta, zx[v], u.alpha_x * ax[v]);
+      const int dr = 8 * (v >> 2) + (v & 3);
+      if (row0 + dr >= u.m) continue;
+      mw[dr * u.ldm] = fmaf(u.beta, zm[v], u.alpha_m * am[v]);
+      xw[dr * u.ldx] = fmaf(u.beta, zx[v], u.alpha_x * ax[v]);
     }
   }
 }
@@ -1071,6 +1131,10 @@ size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
 #define MUON_DION_STAGES 2
 #endif
 constexpr int kDionStages = MUON_DION_STAGES;   // DMA ring depth (16 KB per stage)
+#ifndef MUON_DION_UPDATE2_HALF
+#define MUON_DION_UPDATE2_HALF 1
+#endif
+constexpr bool kUpdate2Half = MUON_DION_UPDATE2_HALF;   // r = 16, 48: the tail in a half stage
 
 // an operand the DMA kernel can stage: 16-byte chunks along its contiguous
 // dimension (k when s_k == 1, else the output dimension), whole chunks only
@@ -1477,8 +1541,12 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
                        -(1.0f - C.mu), -C.eta, 1.0f};
       const dim3 grid((n + kDT - 1) / kDT, (m + kDT - 1) / kDT, b);
       const uint32_t lds = kDionStages * 3 * kDmaTileBytes;
-      if (r % kDK == 16) launch_kernel(dion_update2_kernel<kDionStages, true>, grid, dim3(256), lds, st, u, zp);
-      else launch_kernel(dion_update2_kernel<kDionStages, false>, grid, dim3(256), lds, st, u, zp);
+      if (r % kDK == 16 && r <= kDK + 16 && kUpdate2Half)
+        launch_kernel(dion_update2_kernel<kDionStages, true, true>, grid, dim3(256), 9 * kDmaTileBytes / 2, st, u,
+                      zp);
+      else if (r % kDK == 16)
+        launch_kernel(dion_update2_kernel<kDionStages, true, false>, grid, dim3(256), lds, st, u, zp);
+      else launch_kernel(dion_update2_kernel<kDionStages, false, false>, grid, dim3(256), lds, st, u, zp);
       status = launch_status();
     } else {
       status = dgemm(Pf, m * r, r, 1, Q, run.sQ, 1, r, X, run.sX, n, X, run.sX, n, m, n, r, -C.eta, 1.0f, b, part,
