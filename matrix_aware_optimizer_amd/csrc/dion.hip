@@ -260,6 +260,9 @@ __device__ __forceinline__ void dion_wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// the slot of chunk c in row o of a half tile is c ^ half_swizzle(o)
+__device__ __forceinline__ int half_swizzle(int o) { return (o + (o >> 2)) & 3; }
+
 struct DmaOperand {
   const float* base;     // this batch entry
   int64_t s_out, s_k;    // element strides along the output dimension and along k
@@ -288,7 +291,7 @@ struct DmaOperand {
   // rows one 16-byte read phase touches fall in distinct banks
   __device__ __forceinline__ const float* chunk16(int p, int64_t o0, int64_t k0, const float* zero,
                                                   int zspread) const {
-    const int row = p >> 2, c = (p & 3) ^ ((row + (row >> 2)) & 3);
+    const int row = p >> 2, c = (p & 3) ^ half_swizzle(row);
     int64_t o = o0 + row;
     if (o >= n_out) o = n_out - 1;
     const int64_t k = k0 + 4 * c;
@@ -423,10 +426,18 @@ __global__ __launch_bounds__(256) void dion_gemm_dma_kernel(DGemm g, int splits,
 // are loaded, clamped at the edge, and not used).  In each 16-deep k group g,
 // k-slot q of product t (t = 0..3) is k = 16 g + 4 q + t, so a k-contiguous
 // lane's 16-byte read feeds four products.
-template <int S, int NB, bool ACK, bool BCK, bool ADDA>
+//
+// KD16: stages of 16 k-values (half tiles, 4 KB per operand: k-contiguous ones
+// in 64-byte rows, see DmaOperand::chunk16; the others as the first 16 k-rows
+// of the 32-deep layout), for a ring of more, smaller stages.  The k ranges
+// and the order of the products over k are those of 32-deep stages.
+template <int S, int NB, bool ACK, bool BCK, bool ADDA, bool KD16 = false>
 __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int splits, float* part,
                                                               const float* zero) {
   constexpr int kW = 16 * NB, kSub = (kW + kDT - 1) / kDT;   // tile width, B tiles per stage
+  constexpr int KD = KD16 ? 16 : kDK;                          // k-values per stage
+  constexpr int kTB = KD16 ? kDmaTileBytes / 2 : kDmaTileBytes;   // bytes per operand tile
+  constexpr int kSlots = KD16 ? 1 : 2;                         // DMA instructions per operand tile and wave
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const DTile T = dion_tile();
   const int64_t b = T.z / splits;
@@ -442,23 +453,32 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   constexpr int kTiles = 1 + kSub + (ADDA ? 1 : 0);   // A, the B tiles, A2
   const int64_t ktiles = (g.K + kDK - 1) / kDK;
   const int64_t kt0 = ktiles * sp / splits, kt1 = ktiles * (sp + 1) / splits;
-  const int nk = static_cast<int>(kt1 - kt0);
+  const int nk = static_cast<int>(kt1 - kt0) * (kDK / KD);   // stages of this range
+  const int64_t kbase = kt0 * kDK;                           // its first k
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)dsm));
   const int zspread = static_cast<int>((T.x + 3 * T.y + 5 * T.z) & 63);
-  auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
-    const int64_t k0 = kt * kDK;
-    const uint32_t sa = lds0 + stage * kTiles * kDmaTileBytes, sb = sa + kDmaTileBytes;
+  // a k-contiguous operand's chunk in a half tile, else the 32-deep layout's
+  auto chunk_of = [&](const DmaOperand& o, auto ck, int p, int64_t o0, int64_t k0, int zs)
+      __attribute__((always_inline)) {
+    constexpr bool CK = decltype(ck)::value;
+    if constexpr (KD16 && CK) return o.chunk16(p, o0, k0, zero, zs);
+    else return o.template chunk<CK>(p, o0, k0, zero, zs);
+  };
+  auto issue = [&](int stage, int it) __attribute__((always_inline)) {
+    const int64_t k0 = kbase + int64_t(it) * KD;
+    const uint32_t sa = lds0 + stage * kTiles * kTB, sb = sa + kTB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int slot0 = 64 * (2 * wave + i);
-      dion_dma16(oa.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread), sa + 16 * slot0);
+    for (int i = 0; i < kSlots; ++i) {
+      const int slot0 = 64 * (kSlots * wave + i);
+      dion_dma16(chunk_of(oa, std::integral_constant<bool, ACK>{}, slot0 + lane, i0, k0, zspread), sa + 16 * slot0);
 #pragma unroll
       for (int t = 0; t < kSub; ++t)
-        dion_dma16(ob.chunk<BCK>(slot0 + lane, j0 + kDT * t, k0, zero, zspread + 1 + t),
-                   sb + t * kDmaTileBytes + 16 * slot0);
+        dion_dma16(chunk_of(ob, std::integral_constant<bool, BCK>{}, slot0 + lane, j0 + kDT * t, k0, zspread + 1 + t),
+                   sb + t * kTB + 16 * slot0);
       if constexpr (ADDA)
-        dion_dma16(oa2.chunk<ACK>(slot0 + lane, i0, k0, zero, zspread + 5), sb + kSub * kDmaTileBytes + 16 * slot0);
+        dion_dma16(chunk_of(oa2, std::integral_constant<bool, ACK>{}, slot0 + lane, i0, k0, zspread + 5),
+                   sb + kSub * kTB + 16 * slot0);
     }
   };
   // ADDA: the lane that reads an entry of A + A2 (one lane per entry: a wave
@@ -470,29 +490,29 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
   for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, kt0 + s);
+    if (s < nk) issue(s, s);
   for (int it = 0; it < nk; ++it) {
     if (it + S - 1 < nk) {
-      dion_wait_vm_barrier<2 * kTiles * (S - 2)>();
-      issue((it + S - 1) % S, kt0 + it + S - 1);
+      dion_wait_vm_barrier<kSlots * kTiles * (S - 2)>();
+      issue((it + S - 1) % S, it + S - 1);
     } else {
       dion_wait_vm_barrier<0>();
     }
-    const char* ta = dsm + (it % S) * kTiles * kDmaTileBytes;
-    const char* tb = ta + kDmaTileBytes;
+    const char* ta = dsm + (it % S) * kTiles * kTB;
+    const char* tb = ta + kTB;
 #pragma unroll
-    for (int gk = 0; gk < 2; ++gk) {
+    for (int gk = 0; gk < KD / 16; ++gk) {
       float av[4];
       if constexpr (ACK) {
         const int c = 4 * gk + q;
-        const int o = arow * 128 + ((c ^ (arow & 7)) << 4);
+        const int o = KD16 ? arow * 64 + ((c ^ half_swizzle(arow)) << 4) : arow * 128 + ((c ^ (arow & 7)) << 4);
         const float4 v = *reinterpret_cast<const float4*>(ta + o);
         av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
         if constexpr (ADDA) {
-          const float4 w = *reinterpret_cast<const float4*>(tb + kSub * kDmaTileBytes + o);
+          const float4 w = *reinterpret_cast<const float4*>(tb + kSub * kTB + o);
           av[0] = add_once(av[0], w.x); av[1] = add_once(av[1], w.y);
           av[2] = add_once(av[2], w.z); av[3] = add_once(av[3], w.w);
-          const int64_t k = (kt0 + it) * kDK + 4 * c;
+          const int64_t k = kbase + int64_t(it) * KD + 4 * c;
           if (arow_in && k < g.K)
             *reinterpret_cast<float4*>(aout + k) = make_float4(av[0], av[1], av[2], av[3]);
         }
@@ -503,12 +523,13 @@ __global__ __launch_bounds__(256) void dion_gemm_dma48_kernel(DGemm g, int split
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int bcol = (16 * j) % kDT + li;                     // index within its B tile
-        const char* tbj = tb + (16 * j / kDT) * kDmaTileBytes;   // the B tile holding block j
+        const int bcol = (16 * j) % kDT + li;        // index within its B tile
+        const char* tbj = tb + (16 * j / kDT) * kTB;   // the B tile holding block j
         float bv[4];
         if constexpr (BCK) {
           const int c = 4 * gk + q;
-          const float4 v = *reinterpret_cast<const float4*>(tbj + bcol * 128 + ((c ^ (bcol & 7)) << 4));
+          const int o = KD16 ? bcol * 64 + ((c ^ half_swizzle(bcol)) << 4) : bcol * 128 + ((c ^ (bcol & 7)) << 4);
+          const float4 v = *reinterpret_cast<const float4*>(tbj + o);
           bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
         } else {
 #pragma unroll
@@ -1135,6 +1156,16 @@ constexpr int kDionStages = MUON_DION_STAGES;   // DMA ring depth (16 KB per sta
 #define MUON_DION_UPDATE2_HALF 1
 #endif
 constexpr bool kUpdate2Half = MUON_DION_UPDATE2_HALF;   // r = 16, 48: the tail in a half stage
+// B Q with B = M + G formed in it at rank 192: 16-deep stages, kAddStages of
+// them (2% faster there; 1-4% slower at ranks 48 and 96, which keep 32)
+#ifndef MUON_DION_ADD_KD16
+#define MUON_DION_ADD_KD16 1
+#endif
+#ifndef MUON_DION_ADD_STAGES
+#define MUON_DION_ADD_STAGES 3
+#endif
+constexpr bool kAddKD16 = MUON_DION_ADD_KD16;
+constexpr int kAddStages = MUON_DION_ADD_STAGES;
 
 // an operand the DMA kernel can stage: 16-byte chunks along its contiguous
 // dimension (k when s_k == 1, else the output dimension), whole chunks only
@@ -1187,21 +1218,26 @@ int dgemm(const float* A, int64_t sA, int64_t a_i, int64_t a_k, const float* B, 
     const int splits = N == 48 ? gemm_splits(M, N, K, batch, true) : gemm_splits(M, N, K, batch);
     const dim3 grid(1, (M + kDT - 1) / kDT, batch * splits);
     const bool bck = b_k == 1;
-    auto go = [&](auto kern, int nb) {
-      const uint32_t lds = kDionStages * (2 + (16 * nb + kDT - 1) / kDT) * kDmaTileBytes;
+    // the 192-wide tile on 16-deep stages (kAddStages half stages), the
+    // others on the 32-deep ring
+    auto go = [&](auto kern, int nb, bool kd16) {
+      const uint32_t stages = kd16 ? kAddStages : kDionStages;
+      const uint32_t lds = stages * (2 + (16 * nb + kDT - 1) / kDT) * (kDmaTileBytes / (kd16 ? 2 : 1));
       launch_kernel(kern, grid, dim3(256), lds, st, g, splits, part, zero);
     };
+    constexpr int S = kDionStages, SA = kAddStages;
+    constexpr bool H = kAddKD16;
     switch (N) {
-      case 48: bck ? go(dion_gemm_dma48_kernel<kDionStages, 3, true, true, true>, 3)
-                   : go(dion_gemm_dma48_kernel<kDionStages, 3, true, false, true>, 3); break;
-      case 64: bck ? go(dion_gemm_dma48_kernel<kDionStages, 4, true, true, true>, 4)
-                   : go(dion_gemm_dma48_kernel<kDionStages, 4, true, false, true>, 4); break;
-      case 96: bck ? go(dion_gemm_dma48_kernel<kDionStages, 6, true, true, true>, 6)
-                   : go(dion_gemm_dma48_kernel<kDionStages, 6, true, false, true>, 6); break;
-      case 128: bck ? go(dion_gemm_dma48_kernel<kDionStages, 8, true, true, true>, 8)
-                    : go(dion_gemm_dma48_kernel<kDionStages, 8, true, false, true>, 8); break;
-      default: bck ? go(dion_gemm_dma48_kernel<kDionStages, 12, true, true, true>, 12)
-                   : go(dion_gemm_dma48_kernel<kDionStages, 12, true, false, true>, 12); break;
+      case 48: bck ? go(dion_gemm_dma48_kernel<S, 3, true, true, true>, 3, false)
+                   : go(dion_gemm_dma48_kernel<S, 3, true, false, true>, 3, false); break;
+      case 64: bck ? go(dion_gemm_dma48_kernel<S, 4, true, true, true>, 4, false)
+                   : go(dion_gemm_dma48_kernel<S, 4, true, false, true>, 4, false); break;
+      case 96: bck ? go(dion_gemm_dma48_kernel<S, 6, true, true, true>, 6, false)
+                   : go(dion_gemm_dma48_kernel<S, 6, true, false, true>, 6, false); break;
+      case 128: bck ? go(dion_gemm_dma48_kernel<S, 8, true, true, true>, 8, false)
+                    : go(dion_gemm_dma48_kernel<S, 8, true, false, true>, 8, false); break;
+      default: bck ? go(dion_gemm_dma48_kernel<H ? SA : S, 12, true, true, true, H>, 12, H)
+                   : go(dion_gemm_dma48_kernel<H ? SA : S, 12, true, false, true, H>, 12, H); break;
     }
     if (splits > 1) launch_reduce(g, splits, part, batch, st);
     return launch_status();
