@@ -593,7 +593,12 @@ struct DUpdate2 {
 // whole tile in one 24 KB stage and the tail in a 12 KB half stage of 64-byte
 // rows, both issued at once; 36 KB of LDS, so four workgroups share a CU.
 // The addends are read once the whole tile has landed, under its products.
-template <int S, bool TAIL16, bool HALF>
+//
+// KD16: every stage 16 k-values deep (half tiles, 12 KB a stage), S of them,
+// for the ranks HALF does not take; the addends are read first, so every wait
+// counts only the stages' copies.  The order of the products over k is that
+// of 32-deep stages.
+template <int S, bool TAIL16, bool HALF, bool KD16 = false>
 __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const float* zero) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const DTile T = dion_tile();
@@ -632,6 +637,15 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     dion_dma16(orr.chunk16(64 * wave + lane, j0, k0, zero, zspread + 1), sa + kHalfBytes);
     dion_dma16(oq.chunk16(64 * wave + lane, j0, k0, zero, zspread + 2), sa + 2 * kHalfBytes);
   };
+  // KD16: stage s of the ring holds P's, R's and Q's half tiles of 16-deep
+  // step `it` (3 DMA instructions per wave)
+  auto issue16 = [&](int stage, int it) __attribute__((always_inline)) {
+    const int64_t k0 = int64_t(it) * 16;
+    const uint32_t sa = lds0 + stage * 3 * kHalfBytes + 16 * 64 * wave;
+    dion_dma16(op.chunk16(64 * wave + lane, i0, k0, zero, zspread), sa);
+    dion_dma16(orr.chunk16(64 * wave + lane, j0, k0, zero, zspread + 1), sa + kHalfBytes);
+    dion_dma16(oq.chunk16(64 * wave + lane, j0, k0, zero, zspread + 2), sa + 2 * kHalfBytes);
+  };
   f32x16_t am, ax;
 #pragma unroll
   for (int v = 0; v < 16; ++v) am[v] = ax[v] = 0.0f;
@@ -639,7 +653,7 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     if (nk == 2) issue(0, 0);
     issue_half(nk - 1);
     if (nk == 2) dion_wait_vm_barrier<3>();   // the whole tile has landed; the half stage may be in flight
-  } else {
+  } else if constexpr (!KD16) {
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < nk) issue(s, s);
@@ -659,6 +673,12 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     const bool in = row0 + dr < u.m && col < u.n;
     zm[v] = in ? mrow[dr * u.ldm] : 0.0f;
     zx[v] = in ? xrow[dr * u.ldx] : 0.0f;
+  }
+  const int nk16 = static_cast<int>((u.r + 15) / 16);
+  if constexpr (KD16) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk16) issue16(s, s);
   }
   // the products of k-tile `it` over its first G 8-deep groups
   auto mma = [&](int it, auto groups) __attribute__((always_inline)) {
@@ -683,10 +703,8 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
     }
   };
-  if constexpr (HALF) {
-    if (nk == 2) mma(0, std::integral_constant<int, 4>{});
-    dion_wait_vm_barrier<0>();
-    const char* ta = dsm + 3 * kDmaTileBytes;
+  // the products of one half tile (16 k-values in 64-byte rows) at ta
+  auto mma_half = [&](const char* ta) __attribute__((always_inline)) {
     const char* tr = ta + kHalfBytes;
     const char* tq = tr + kHalfBytes;
     const int ra = wi + l32, rb = wj + l32;
@@ -705,10 +723,26 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bq.z, ax, 0, 0, 0);
       ax = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bq.w, ax, 0, 0, 0);
     }
+  };
+  if constexpr (HALF) {
+    if (nk == 2) mma(0, std::integral_constant<int, 4>{});
+    dion_wait_vm_barrier<0>();
+    mma_half(dsm + 3 * kDmaTileBytes);
+  }
+  if constexpr (KD16) {
+    for (int it = 0; it < nk16; ++it) {
+      if (it + S - 1 < nk16) {
+        dion_wait_vm_barrier<3 * (S - 2)>();
+        issue16((it + S - 1) % S, it + S - 1);
+      } else {
+        dion_wait_vm_barrier<0>();
+      }
+      mma_half(dsm + (it % S) * 3 * kHalfBytes);
+    }
   }
   // TAIL16: the contraction ends 16 into its last k-tile (r = 48, 80, ...),
   // whose last two 8-deep groups hold only the zero page's zeros
-  const int full = HALF ? 0 : TAIL16 ? nk - 1 : nk;
+  const int full = HALF || KD16 ? 0 : TAIL16 ? nk - 1 : nk;
   for (int it = 0; it < full; ++it) {
     if (it + S - 1 < nk) {
       dion_wait_vm_barrier<6 * (S - 2)>();
@@ -718,7 +752,7 @@ __global__ __launch_bounds__(256) void dion_update2_kernel(DUpdate2 u, const flo
     }
     mma(it, std::integral_constant<int, 4>{});
   }
-  if constexpr (TAIL16 && !HALF) {
+  if constexpr (TAIL16 && !HALF && !KD16) {
     if (full >= 0) {
       dion_wait_vm_barrier<0>();
       mma(full, std::integral_constant<int, 2>{});
@@ -1156,6 +1190,15 @@ constexpr int kDionStages = MUON_DION_STAGES;   // DMA ring depth (16 KB per sta
 #define MUON_DION_UPDATE2_HALF 1
 #endif
 constexpr bool kUpdate2Half = MUON_DION_UPDATE2_HALF;   // r = 16, 48: the tail in a half stage
+// the other ranks' fused updates on 16-deep stages, kUpdate2Stages16 of them
+#ifndef MUON_DION_UPDATE2_KD16
+#define MUON_DION_UPDATE2_KD16 1
+#endif
+#ifndef MUON_DION_UPDATE2_STAGES16
+#define MUON_DION_UPDATE2_STAGES16 3
+#endif
+constexpr bool kUpdate2KD16 = MUON_DION_UPDATE2_KD16;
+constexpr int kUpdate2Stages16 = MUON_DION_UPDATE2_STAGES16;
 // B Q with B = M + G formed in it at rank 192: 16-deep stages, kAddStages of
 // them (2% faster there; 1-4% slower at ranks 48 and 96, which keep 32)
 #ifndef MUON_DION_ADD_KD16
@@ -1580,6 +1623,9 @@ int dion_stage(const DionCall& C, int stage, const std::vector<int>& ids, float*
       if (r % kDK == 16 && r <= kDK + 16 && kUpdate2Half)
         launch_kernel(dion_update2_kernel<kDionStages, true, true>, grid, dim3(256), 9 * kDmaTileBytes / 2, st, u,
                       zp);
+      else if (kUpdate2KD16)
+        launch_kernel(dion_update2_kernel<kUpdate2Stages16, false, false, true>, grid, dim3(256),
+                      kUpdate2Stages16 * 3 * kDmaTileBytes / 2, st, u, zp);
       else if (r % kDK == 16)
         launch_kernel(dion_update2_kernel<kDionStages, true, false>, grid, dim3(256), lds, st, u, zp);
       else launch_kernel(dion_update2_kernel<kDionStages, false, false>, grid, dim3(256), lds, st, u, zp);
