@@ -344,12 +344,12 @@ def test_dion_validation(L):
     # P twice (m x r) and R (n x r) per run, the Grams and their inverse factors
     # (r x r per matrix), one split-k partial buffer, and the 16 KB page of zeros
     # the DMA-staged products read past the contraction: ranges per product =
-    # ceil(1024 / output tiles of 64 x 64), at most K / 256 and 16, at least 1
+    # ceil(512 / output tiles of 64 x 64), at most K / 256 and 16, at least 1
     up = lambda x: -(-x // 256) * 256
 
     def part(M, N, K, b=1):
         blocks = -(-N // 64) * -(-M // 64) * b
-        sp = max(1, min(-(-1024 // blocks), max(1, K // 256), 16))
+        sp = max(1, min(-(-512 // blocks), max(1, K // 256), 16))
         return sp * b * M * N * 4 if sp > 1 else 0
 
     m, n, r = 768, 3072, 192
