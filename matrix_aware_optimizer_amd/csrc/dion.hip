@@ -944,16 +944,18 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
       for (int k = 0; k < kCb; ++k) {
         const float d = from_lane(a[k], k);
         const bool room = c0 + k >= r || kept < cap;   // a real column past the rank bound is dependent
-        const float piv =
-            (room && d > 0.0f && d > kDependentTol * kDependentTol * from_lane(g, k)) ? sqrtf(d) : 0.0f;
+        const bool ok = room && d > 0.0f && d > kDependentTol * kDependentTol * from_lane(g, k);
+        // the hardware square root and reciprocal (1 ulp each), computed
+        // unconditionally: this chain of uniform operations is the factor's
+        // critical path, and the correctly rounded forms take several times
+        // as many dependent instructions
+        const float sq = __builtin_amdgcn_sqrtf(fmaxf(d, 0.0f));
+        const float piv = ok ? sq : 0.0f;
+        const float inv = ok ? __builtin_amdgcn_rcpf(sq) : 0.0f;
         kept += piv > 0.0f ? 1 : 0;
-        const float inv = piv > 0.0f ? 1.0f / piv : 0.0f;
-        if (lane == k) {
-          a[k] = piv;
-          own_inv = inv;
-        } else {
-          a[k] *= inv;
-        }
+        // selects, not branches: lane k keeps the pivot, the others scale
+        own_inv = lane == k ? inv : own_inv;
+        a[k] = lane == k ? piv : a[k] * inv;
 #pragma unroll
         for (int m = k + 1; m < kCb; ++m) a[m] = fmaf(-a[k], from_lane(a[k], m), a[m]);
       }
@@ -962,10 +964,8 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
       for (int c = 0; c < kCb; ++c) x[c] = acc[c] = 0.0f;
 #pragma unroll
       for (int k = 0; k < kCb; ++k) {
-        if (lane == k) {
 #pragma unroll
-          for (int c = 0; c <= k; ++c) x[c] = ((c == k ? 1.0f : 0.0f) - acc[c]) * own_inv;
-        }
+        for (int c = 0; c <= k; ++c) x[c] = lane == k ? ((c == k ? 1.0f : 0.0f) - acc[c]) * own_inv : x[c];
 #pragma unroll
         for (int c = 0; c <= k; ++c) acc[c] = fmaf(a[k], from_lane(x[c], k), acc[c]);
       }
