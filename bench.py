@@ -646,6 +646,30 @@ def cold_elementwise(mao, torch, wl, objs, dev, reps=5):
     return out
 
 
+def kernel_and_call_ms(mao, torch, fn, reps):
+    """(median kernel ms, ms per call) of a call that launches one kernel: the
+    kernel's own start and end events (muon_time_next_launch) for each of `reps`
+    calls, and HIP events around the `reps` calls back to back (launch gaps
+    included)."""
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()            # creates the HIP events; the launch records them again
+        mao.time_next_launch(e0, e1)
+        fn()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    kernel = float(np.median([a.elapsed_time(b) for a, b in pairs]))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return kernel, start.elapsed_time(end) / reps
+
+
 def int8_exchange(mao, torch, U, wl, n, nwords, dev, reps=10):
     """The int8 exchange format next to the 1-bit one: sign_int8 of one direction,
     sum_int8 over the M resident int8 buffers, threshold_pack of the sum; each
@@ -665,15 +689,9 @@ def int8_exchange(mao, torch, U, wl, n, nwords, dev, reps=10):
     out = {}
     for name, (fn, nbytes) in calls.items():
         fn()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(reps):
-            fn()
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / reps
+        ms, call_ms = kernel_and_call_ms(mao, torch, fn, reps)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        out[name] = {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "call_ms": call_ms}
     out["payload_bytes_per_worker"] = {"fp32": 4 * n, "int8": n, "packed_bits": nwords * 8}
     return out
 
@@ -702,13 +720,14 @@ def reorth_update(mao, torch, wl, W, vote, dev, reps=3):
     es_u = step.U.element_size()
     es_w = W.element_size()
     whole = timed(lambda: step.reorthogonalized_update(Wc, vote))
-    unpack = timed(lambda: mao.unpack_signs(vote, step._sbar))
-    dense = timed(lambda: mao.apply_update_dense(Wc, step.U, wl.eta))
+    unpack, unpack_call = kernel_and_call_ms(mao, torch, lambda: mao.unpack_signs(vote, step._sbar), 10)
+    dense, dense_call = kernel_and_call_ms(mao, torch, lambda: mao.apply_update_dense(Wc, step.U, wl.eta), 10)
     gbs_u = (n * es_u + n / 8) / (unpack * 1e-3) / 1e9
     gbs_d = (n * (2 * es_w + es_u)) / (dense * 1e-3) / 1e9
     return {"ms": whole,
-            "unpack_signs": {"ms": unpack, "GB/s": gbs_u, "frac_hbm": gbs_u / PEAK_HBM_GBS},
-            "apply_update_dense": {"ms": dense, "GB/s": gbs_d, "frac_hbm": gbs_d / PEAK_HBM_GBS}}
+            "unpack_signs": {"ms": unpack, "GB/s": gbs_u, "frac_hbm": gbs_u / PEAK_HBM_GBS, "call_ms": unpack_call},
+            "apply_update_dense": {"ms": dense, "GB/s": gbs_d, "frac_hbm": gbs_d / PEAK_HBM_GBS,
+                                   "call_ms": dense_call}}
 
 
 def dion_bench(mao, torch, dev, reps=5):
