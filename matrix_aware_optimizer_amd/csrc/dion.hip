@@ -939,7 +939,13 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
 #pragma unroll
       for (int c = 0; c < kCb; ++c) a[c] = S[row * ld + c0 + c];
       const float g = g0[row];
+      // the factor's step k and row k of D = L_JJ^-1 in one pass: row k of D
+      // needs only columns <= k of L, final after step k, so the two chains
+      // are independent from there and interleave:
+      // D(k, c) = (delta_kc - sum_{m<k} L(k, m) D(m, c)) / l_kk
       float own_inv = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kCb; ++c) x[c] = acc[c] = 0.0f;
 #pragma unroll
       for (int k = 0; k < kCb; ++k) {
         const float d = from_lane(a[k], k);
@@ -958,12 +964,6 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv_kernel(const float* __r
         a[k] = lane == k ? piv : a[k] * inv;
 #pragma unroll
         for (int m = k + 1; m < kCb; ++m) a[m] = fmaf(-a[k], from_lane(a[k], m), a[m]);
-      }
-      // rows of D = L_JJ^-1 in order: D(k, c) = (delta_kc - sum_{m<k} L(k, m) D(m, c)) / l_kk
-#pragma unroll
-      for (int c = 0; c < kCb; ++c) x[c] = acc[c] = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kCb; ++k) {
 #pragma unroll
         for (int c = 0; c <= k; ++c) x[c] = lane == k ? ((c == k ? 1.0f : 0.0f) - acc[c]) * own_inv : x[c];
 #pragma unroll
