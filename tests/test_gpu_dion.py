@@ -44,6 +44,7 @@ def run_single(M0, G, X0, Q0, rank, mu, eta):
                                    (768, 768, 192), (96, 1000, 17),
                                    (200, 324, 96), (140, 260, 128),   # B = M + G in B Q: ragged rows, k tail
                                    (70, 260, 128), (200, 60, 96),    # rank above a side: P of rank min(m, n)
+                                   (300, 260, 80), (200, 516, 160),  # fused update on 16-deep stages, 5 and 10 of them
                                    (37, 91, 6),      # m n odd: element-wise B = M + G; rows of Q not 16-byte multiples
                                    (8, 5000, 4)])    # n >> m: the column-norm chunks number exactly m
 def test_dion_single_matrix(m, n, r):
